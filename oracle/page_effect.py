@@ -1,0 +1,134 @@
+"""CommitKV page deletion effects and lifecycle decisions (test infrastructure).
+
+CommitKV §3.2: for one attention layer and query head, a query p pays
+attention a_pi to resident token i and produces o_p. Deleting an event page
+E (a contiguous span of at most G tokens) and renormalising the remaining
+weights gives o_p^{\\E}; Eq. 6 writes that renormalisation in closed form.
+This oracle uses the plain definition instead -- attention recomputed over
+the visible tokens not in E -- which Eq. 6 reaches exactly.
+
+    R_h(E; Q) = max_{p in Q} ||o_p - o_p^{\\E}||_2 / ||o_p||_2     (Eq. 7)
+    R(E; Q)   = max_h R_h(E; Q)
+
+Eq. 8 evaluates it on the pre-commit window Q^- and the post-commit window
+Q^+ (Eq. 5). Eq. 9 labels a page high (R >= tau_use and percentile >=
+rho_use) or low (R <= tau_dead and percentile <= rho_dead); Eq. 10 names the
+states; §3.3 (Eq. 11) retires completion candidates greedily, in the order
+(R^+ ascending, R^- descending), while the joint effect of the retired set
+stays within tau_joint. The page's setup section fixes tau_use = 0.05,
+rho_use = 0.75, rho_dead = 0.25 and a scan of at most 64 pages.
+
+Readings where the page is silent:
+* percentile rank = fraction of the other comparison pages with a strictly
+  smaller effect: #{E' : R(E') < R(E)} / (|E_c| - 1);
+* remaining ties in the greedy order go to the lower page index;
+* deleting every visible token leaves no output: the effect is +inf and such
+  a page is never accepted.
+
+Parity status: the effect itself is pinned (Eq. 6 identity, brute force,
+closed forms); the labels and the greedy loop are pinned only by invariants
+and hand-built cases -- the workload they run on in the benchmark is
+synthetic, so beyond those invariants they are "parity unpinned".
+"""
+import numpy as np
+
+STATES = ("uncertain", "completion_candidate", "dormant", "newly_active", "still_active")
+
+
+def head_outputs(K, V, Q, q_pos, k_pos=None, drop=None):
+    """Attention outputs of one query head over one KV head.
+
+    K, V: [T, d]; Q: [P, d]; q_pos: [P]; k_pos: [T] (default 0..T-1);
+    drop: boolean [T] of tokens removed before the softmax (default none).
+    Returns [P, d] float64; rows with no remaining visible key are NaN.
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    Q = np.asarray(Q, np.float64)
+    T, d = K.shape
+    if k_pos is None:
+        k_pos = np.arange(T)
+    vis = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+    if drop is not None:
+        vis &= ~np.asarray(drop, bool)[None, :]
+    s = np.where(vis, (Q @ K.T) / np.sqrt(d), -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        e = np.exp(s - m)
+        e = np.where(vis, e, 0.0)
+        return (e @ V) / e.sum(axis=1, keepdims=True)
+
+
+def deletion_effect(K, V, Q, q_pos, tokens, k_pos=None):
+    """R(E; Q) and its absolute numerator for the token set ``tokens``.
+
+    K, V: [Hkv, T, d]; Q: [Hq, P, d] (Hq a multiple of Hkv, query head h reads
+    KV head h // (Hq/Hkv)); q_pos: [P]. Returns (R_rel, R_abs) with
+    R_rel = max_h max_p ||o - o^{\\E}|| / ||o|| and
+    R_abs = max_h max_p ||o - o^{\\E}||.
+    """
+    Hkv, T, _ = np.shape(K)
+    Hq = np.shape(Q)[0]
+    G = Hq // Hkv
+    drop = np.zeros(T, bool)
+    drop[np.asarray(tokens, dtype=np.int64)] = True
+    rel = 0.0
+    ab = 0.0
+    for h in range(Hq):
+        kv = h // G
+        o = head_outputs(K[kv], V[kv], Q[h], q_pos, k_pos)
+        o_del = head_outputs(K[kv], V[kv], Q[h], q_pos, k_pos, drop)
+        if np.isnan(o_del).any():
+            return np.inf, np.inf
+        diff = np.linalg.norm(o - o_del, axis=1)
+        rel = max(rel, float(np.max(diff / np.linalg.norm(o, axis=1))))
+        ab = max(ab, float(np.max(diff)))
+    return rel, ab
+
+
+def page_tokens(first, page_size):
+    return np.arange(first, first + page_size, dtype=np.int64)
+
+
+def percentile_ranks(R):
+    """P(E) = #{E' != E : R(E') < R(E)} / (n - 1)."""
+    R = np.asarray(R, np.float64)
+    n = R.size
+    if n <= 1:
+        return np.zeros(n)
+    less = (R[None, :] < R[:, None]).sum(axis=1)
+    return less / (n - 1)
+
+
+def lifecycle_states(R_minus, R_plus, tau_use, tau_dead, rho_use, rho_dead):
+    """Eq. 9-10 labels per page; returns an int array indexing STATES."""
+    Pm, Pp = percentile_ranks(R_minus), percentile_ranks(R_plus)
+    Rm, Rp = np.asarray(R_minus), np.asarray(R_plus)
+    Hm = (Rm >= tau_use) & (Pm >= rho_use)
+    Lm = (Rm <= tau_dead) & (Pm <= rho_dead)
+    Hp = (Rp >= tau_use) & (Pp >= rho_use)
+    Lp = (Rp <= tau_dead) & (Pp <= rho_dead)
+    st = np.zeros(Rm.size, np.int64)
+    st[Hm & Lp] = 1
+    st[Lm & Lp] = 2
+    st[Lm & Hp] = 3
+    st[Hm & Hp] = 4
+    return st
+
+
+def candidate_order(R_minus, R_plus, states):
+    """Completion candidates sorted by (R^+ asc, R^- desc, index asc)."""
+    idx = np.flatnonzero(np.asarray(states) == 1)
+    Rm, Rp = np.asarray(R_minus), np.asarray(R_plus)
+    order = np.lexsort((idx, -Rm[idx], Rp[idx]))
+    return idx[order]
+
+
+def greedy_retire(order, joint_effect, tau_joint, max_scan=64):
+    """Eq. 11: walk ``order`` (at most max_scan entries) and accept E iff
+    joint_effect(D + [E]) <= tau_joint. Returns the accepted page list D."""
+    D = []
+    for E in list(order)[:max_scan]:
+        if joint_effect(D + [int(E)]) <= tau_joint:
+            D.append(int(E))
+    return D

@@ -1,0 +1,144 @@
+"""Pins for the oracle's compaction/re-rotation, int8 codes and decode attention (CPU only)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import compact, decode, numfmt, quant, rope
+
+
+def _bf16(x):
+    return numfmt.f64_to_bf16_bits(x)
+
+
+def test_rerotation_matches_direct_rotation_prop1():
+    # PACE Prop. 1: R_{p'-p} (R_p k) = R_{p'} k. Both sides pass through one bf16
+    # rounding of the cached key, so they agree within about two bf16 roundings.
+    rng = np.random.default_rng(11)
+    T, d, base = 3000, 128, 1e6
+    k = rng.standard_normal((T, d))
+    pos = np.arange(T) * 333 + 17                      # positions up to ~1e6
+    cached = _bf16(rope.rotate(k, pos, base))
+    kept = np.sort(rng.choice(T, 256, replace=False))
+    Kn, _, pn = compact.compact_row(cached, cached, pos, kept, 0, base)
+    np.testing.assert_array_equal(pn, np.arange(256))
+    want = rope.rotate(k[kept], pn, base)
+    got = numfmt.bf16_bits_to_f64(Kn)
+    err = np.abs(got - want) / (np.abs(want).max(axis=1, keepdims=True))
+    assert err.max() < 2 * 2.0 ** -8
+
+
+def test_rerotation_zero_shift_and_no_renumber_are_bit_copies():
+    rng = np.random.default_rng(12)
+    T, d = 100, 64
+    K = _bf16(rng.standard_normal((T, d)))
+    V = _bf16(rng.standard_normal((T, d)))
+    kept = np.arange(10, 30)
+    Kn, Vn, pn = compact.compact_row(K, V, np.arange(T), kept, 10, 1e4)   # p' = p
+    np.testing.assert_array_equal(Kn, K[kept])
+    np.testing.assert_array_equal(Vn, V[kept])
+    Kn, Vn, pn = compact.compact_row(K, V, np.arange(T) + 5, kept, -1, 1e4)
+    np.testing.assert_array_equal(Kn, K[kept])
+    np.testing.assert_array_equal(pn, kept + 5)
+
+
+def test_rerotation_round_trip():
+    rng = np.random.default_rng(13)
+    T, d, base = 64, 128, 1e6
+    K = _bf16(rng.standard_normal((T, d)))
+    kept = np.arange(T)
+    far = np.arange(T) + 700000
+    K1, _, p1 = compact.compact_row(K, K, far, kept, 0, base)      # rotate by -700000
+    K2, _, _ = compact.compact_row(K1, K1, p1, kept, 700000, base)  # and back
+    a, b = numfmt.bf16_bits_to_f64(K2), numfmt.bf16_bits_to_f64(K)
+    assert np.max(np.abs(a - b) / np.abs(b).max(axis=1, keepdims=True)) < 2 * 2.0 ** -8
+
+
+def test_renumbered_suffix_decodes_like_original_positions():
+    # Shift invariance: keep the last B tokens, renumber them to 0..B-1 and place the
+    # query at m_hat = m - (T - B); attention equals that at the original positions.
+    rng = np.random.default_rng(14)
+    T, B, d, base = 5000, 512, 64, 1e4
+    k = rng.standard_normal((T, d))
+    v = _bf16(rng.standard_normal((T, d)))
+    q = rng.standard_normal(d)
+    m = T
+    K = _bf16(rope.rotate(k, np.arange(T), base))
+    kept = np.arange(T - B, T)
+    Kn, Vn, pn = compact.compact_row(K, v, np.arange(T), kept, 0, base)
+    o_new, _ = decode.decode_head(rope.rotate(q, m - (T - B), base),
+                                  numfmt.bf16_bits_to_f64(Kn), numfmt.bf16_bits_to_f64(Vn))
+    o_old, _ = decode.decode_head(rope.rotate(q, m, base),
+                                  numfmt.bf16_bits_to_f64(K[kept]), numfmt.bf16_bits_to_f64(v[kept]))
+    np.testing.assert_allclose(o_new, o_old, atol=5e-3)
+
+
+def _argmin_code(x, s, qmax):
+    # independent definition: the integer in [-qmax, qmax] closest to x/s (ties to even)
+    c = np.arange(-qmax, qmax + 1)
+    err = np.abs(x - c * s)
+    best = err.min()
+    cand = c[np.isclose(err, best, rtol=0, atol=0)]
+    return cand[0] if cand.size == 1 else cand[cand % 2 == 0][0]
+
+
+def test_int8_codes_brute_force_and_bounds():
+    rng = np.random.default_rng(15)
+    X = numfmt.round_bf16(rng.standard_normal((40, 16)) * rng.uniform(0.01, 10, (40, 1)))
+    codes, sb = quant.quantize_rows(X)
+    for t in range(X.shape[0]):
+        s = numfmt.fp16_bits_to_f64(sb[t])
+        amax = np.abs(X[t]).max()
+        assert sb[t] == numfmt.f64_to_fp16_bits(amax / 127)
+        for i in range(X.shape[1]):
+            assert codes[t, i] == _argmin_code(X[t, i], s, 127)
+        unclipped = np.abs(X[t]) <= 127 * s
+        assert np.all(np.abs(X[t] - codes[t] * s)[unclipped] <= s / 2 + 1e-300)
+        i = np.argmax(np.abs(X[t]))
+        assert abs(int(codes[t, i])) in (126, 127)
+
+
+def test_int8_zero_row_and_tiny_scale():
+    codes, s = quant.quantize_row(np.zeros(8))
+    assert np.all(codes == 0) and numfmt.fp16_bits_to_f64(s) == 1.0
+    x = np.zeros(8)
+    x[3] = 2.0 ** -40                                  # scale would underflow fp16
+    codes, s = quant.quantize_row(x)
+    assert numfmt.fp16_bits_to_f64(s) == 2.0 ** -24
+    assert codes[3] == 0
+
+
+def test_decode_full_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(16)
+    n, d = 300, 64
+    q, K, V = rng.standard_normal(d), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    o, _ = decode.decode_head(q, K, V)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None], torch.from_numpy(K)[None, None],
+        torch.from_numpy(V)[None, None])[0, 0, 0].numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_partition_merge_eq15_and_empty_partition():
+    rng = np.random.default_rng(17)
+    d = 32
+    q = rng.standard_normal(d)
+    parts = [(rng.standard_normal((n, d)), rng.standard_normal((n, d))) for n in (5, 0, 40, 1)]
+    o_union, _ = decode.decode_partitions(q, parts)
+    stats = []
+    for K, V in parts:
+        if len(K) == 0:
+            continue
+        s = K @ q / np.sqrt(d)
+        vj = s.max()
+        e = np.exp(s - vj)
+        stats.append((vj, e.sum(), e @ V))
+    np.testing.assert_allclose(decode.merge_partitions(stats), o_union, rtol=1e-12)
+    o_noempty, _ = decode.decode_partitions(q, [p for p in parts if len(p[0])])
+    np.testing.assert_array_equal(o_union, o_noempty)
+
+
+def test_decode_single_token_returns_value():
+    v = np.array([[0.5, -2.0, 3.25]])
+    o, lse = decode.decode_head(np.array([1.0, 2.0, 3.0]), np.array([[1.0, 1.0, 1.0]]), v)
+    np.testing.assert_array_equal(o, v[0])
+    assert lse == pytest.approx(6.0 / np.sqrt(3))

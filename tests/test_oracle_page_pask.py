@@ -1,0 +1,166 @@
+"""Pins for the oracle's CommitKV page effects and PASK controller (CPU only)."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import page_effect as pe
+from oracle import pask
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_deletion_effect_equals_eq6_renormalisation():
+    # CommitKV Eq. 6: o^{\E} = (o - sum_{i in E} a_i v_i) / (1 - sum_{i in E} a_i).
+    rng = np.random.default_rng(20)
+    Hkv, Hq, T, P, d = 2, 6, 96, 5, 16
+    K = rng.standard_normal((Hkv, T, d))
+    V = rng.standard_normal((Hkv, T, d))
+    Q = rng.standard_normal((Hq, P, d))
+    q_pos = np.arange(T - P, T)
+    E = np.arange(32, 48)
+    rel, ab = pe.deletion_effect(K, V, Q, q_pos, E)
+    best_rel, best_abs = 0.0, 0.0
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        s = Q[h] @ K[kv].T / np.sqrt(d)
+        s = np.where(np.arange(T)[None, :] <= q_pos[:, None], s, -np.inf)
+        a = np.exp(s - s.max(1, keepdims=True))
+        a /= a.sum(1, keepdims=True)
+        o = a @ V[kv]
+        aE = a[:, E]
+        o_del = (o - aE @ V[kv][E]) / (1 - aE.sum(1, keepdims=True))
+        diff = np.linalg.norm(o - o_del, axis=1)
+        best_rel = max(best_rel, np.max(diff / np.linalg.norm(o, axis=1)))
+        best_abs = max(best_abs, np.max(diff))
+    assert rel == pytest.approx(best_rel, rel=1e-10)
+    assert ab == pytest.approx(best_abs, rel=1e-10)
+
+
+def test_deletion_effect_uniform_attention_closed_form():
+    # q = 0: uniform attention, so o is the mean of visible values and o^{\E} the mean of
+    # the rest.
+    rng = np.random.default_rng(21)
+    T, d = 64, 8
+    K = rng.standard_normal((1, T, d))
+    V = rng.standard_normal((1, T, d))
+    Q = np.zeros((1, 1, d))
+    E = np.arange(16, 32)
+    rel, ab = pe.deletion_effect(K, V, Q, np.array([T - 1]), E)
+    keep = np.setdiff1d(np.arange(T), E)
+    o, o_del = V[0].mean(0), V[0][keep].mean(0)
+    assert ab == pytest.approx(np.linalg.norm(o - o_del), rel=1e-12)
+    assert rel == pytest.approx(np.linalg.norm(o - o_del) / np.linalg.norm(o), rel=1e-12)
+
+
+def test_deletion_effect_empty_set_and_everything():
+    rng = np.random.default_rng(22)
+    K = rng.standard_normal((1, 20, 4))
+    V = rng.standard_normal((1, 20, 4))
+    Q = rng.standard_normal((2, 3, 4))
+    assert pe.deletion_effect(K, V, Q, np.array([17, 18, 19]), []) == (0.0, 0.0)
+    assert pe.deletion_effect(K, V, Q, np.array([17, 18, 19]), np.arange(20))[0] == np.inf
+
+
+def test_deletion_effect_invisible_page_is_zero():
+    rng = np.random.default_rng(23)
+    K = rng.standard_normal((1, 40, 4))
+    V = rng.standard_normal((1, 40, 4))
+    Q = rng.standard_normal((1, 2, 4))
+    # queries at positions 10, 11 never see tokens 20..35
+    assert pe.deletion_effect(K, V, Q, np.array([10, 11]), np.arange(20, 36)) == (0.0, 0.0)
+
+
+def test_percentiles_and_states():
+    R = np.array([0.5, 0.1, 0.1, 0.9, 0.0])
+    np.testing.assert_allclose(pe.percentile_ranks(R), [3 / 4, 1 / 4, 1 / 4, 4 / 4, 0])
+    c = json.load(open(os.path.join(GOLDEN, "commitkv_constants.json")))
+    # 5 pages: before/after effects chosen to land in each state of Eq. 10
+    Rm = np.array([0.30, 0.001, 0.0005, 0.40, 0.02])
+    Rp = np.array([0.0008, 0.0009, 0.50, 0.60, 0.02])
+    st = pe.lifecycle_states(Rm, Rp, c["tau_use"], c["tau_dead"], c["rho_use"], c["rho_dead"])
+    names = [pe.STATES[s] for s in st]
+    assert names == ["completion_candidate", "dormant", "newly_active", "still_active", "uncertain"]
+
+
+def test_candidate_order_and_greedy():
+    Rm = np.array([0.5, 0.9, 0.9, 0.2])
+    Rp = np.array([0.001, 0.001, 0.001, 0.0001])
+    st = np.array([1, 1, 1, 0])
+    assert list(pe.candidate_order(Rm, Rp, st)) == [1, 2, 0]
+    # additive joint effect: accept while the running sum stays within tau
+    w = {0: 0.5, 1: 0.5, 2: 0.25, 3: 0.25}          # exact binary fractions
+    D = pe.greedy_retire([1, 2, 0, 3], lambda S: sum(w[e] for e in S), 1.0)
+    assert D == [1, 2, 3]
+    assert pe.greedy_retire(list(range(100)), lambda S: 0.0, 1.0) == list(range(64))
+
+
+# ---------------------------------------------------------------- PASK controller
+
+def _rand_table(rng, n_tags, C):
+    a0 = rng.integers(0, 3, (n_tags, C))
+    amin = np.minimum(a0, rng.integers(0, 3, (n_tags, C)))
+    prio = rng.random((n_tags, C, 2))
+    crit = rng.random(n_tags) < 0.3
+    return a0, amin, prio, crit
+
+
+def test_payload_costs_eq13_14():
+    c = pask.group_costs([8, 8, 8, 8], 8, 128)
+    assert c[0][2] == 16 * 2 * 8 * 8 * 128          # m(H) = 16 n_c
+    assert c[0][1] == 8 * 2 * 8 * 8 * 128 + 16 * 2 * 8 * 8
+    assert c[0][0] == 0
+    c4 = pask.group_costs([1], 1, 6, low_bits=4)    # PASK's INT4 form
+    assert c4[0][1] == 4 * 12 + 16 * 2
+
+
+def test_controller_floors_ledger_and_fallback():
+    rng = np.random.default_rng(30)
+    costs = pask.group_costs([8, 8, 8, 8], 8, 128)
+    a0, amin, prio, crit = _rand_table(rng, 8, 4)
+    tags = rng.integers(0, 8, 500)
+    acts, ledger = pask.control_sequence(tags, a0, amin, prio, crit, costs, 1 / 3)
+    assert np.all(acts >= amin[tags])                           # floors never violated
+    b = costs[:, 2].sum() / 3
+    M = np.array([pask.cost(a, costs) for a in acts])
+    t = np.arange(1, len(tags) + 2)
+    np.testing.assert_allclose(ledger, t * b - np.concatenate([[0], np.cumsum(M)]), rtol=1e-12)
+    # all-high fallback: B_D = 1 and base actions all H keep every token H
+    allH = np.full_like(a0, 2)
+    acts2, _ = pask.control_sequence(tags, allH, np.zeros_like(amin), prio, crit, costs, 1.0)
+    assert np.all(acts2 == 2)
+
+
+def test_controller_step_brute_force_properties():
+    rng = np.random.default_rng(31)
+    costs = pask.group_costs([3, 2, 4], 2, 16)
+    for trial in range(300):
+        a0 = rng.integers(0, 3, 3)
+        amin = np.minimum(a0, rng.integers(0, 3, 3))
+        prio = rng.random((3, 2))
+        crit = bool(rng.random() < 0.5)
+        R_t = rng.uniform(-0.2, 1.2) * costs[:, 2].sum()
+        a, M = pask.control_token(a0, amin, prio, crit, R_t, costs)
+        B_t = max(R_t, 0.0)
+        start = np.maximum(a0, amin)
+        assert np.all(np.array(a) >= amin)
+        if not crit:
+            assert np.all(np.array(a) <= start)
+            if M > B_t:
+                assert list(a) == list(amin)              # only floors remain
+            # demotion stops as soon as the cost fits: undoing the last step (one of
+            # the demoted groups) no longer fits
+            undo = []
+            for c in range(3):
+                if a[c] < start[c]:
+                    up = list(a)
+                    up[c] += 1
+                    undo.append(pask.cost(up, costs) > B_t)
+            assert not undo or any(undo)
+        # brute force over all 3^3 action vectors: the result is one of the vectors
+        # between the floor and H; with non-critical tags it never exceeds the start
+        space = [v for v in itertools.product(range(3), repeat=3)
+                 if all(v[c] >= amin[c] for c in range(3))]
+        assert tuple(a) in space
