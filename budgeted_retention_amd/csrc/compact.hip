@@ -1,0 +1,333 @@
+// kvc_compact_rerotate: gather the kept tokens of every row into contiguous
+// pools, renumber them to bounded positions and re-rotate their keys exactly.
+//
+// PACE §3.2: kept tokens are renumbered in logical order to p' = base + rank
+// and every kept key is rotated by R_{p'-p}; by Proposition 1 that is the key
+// the engine would have cached at p'. The angle (p'-p)*theta_i is formed in
+// fp64 from the integer position difference and reduced modulo 2*pi in fp64
+// (Cody-Waite with a two-term 2*pi), so positions up to 2^31 stay exact to
+// well below a bf16 ulp; the reduced angle's sine/cosine and the rotation run
+// in fp32 and the result is rounded once to bf16. Values are bit copies
+// (CommitKV §3.1 Eq. 4 applies the same index set to K, V and positions).
+//
+// Work split: a group of D/4 threads owns one token. Thread `sub` of the group
+// rotates the frequency pairs (2sub, 2sub+D/2) and (2sub+1, 2sub+1+D/2) --
+// one 4-byte load from each half of the key -- and copies 8 bytes of the
+// value row, so a group's loads cover the key and value rows contiguously.
+//
+// With an action array the kept entries are routed, in rank order, to the
+// bf16 tier, the int8 tier (PASK Appendix B.5 symmetric per-token-per-head
+// rule with 7 -> 127, separately for K and V) or dropped; one workgroup per
+// row scans the actions to give every entry its slot in its tier.
+#include <cmath>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+static constexpr int CMP_THREADS = 256;
+
+__device__ __forceinline__ void reduced_sincos(double ang, float *s, float *c) {
+    const double INV_2PI = 0.15915494309189535;
+    const double TWO_PI_HI = 6.283185307179586;       // nearest double to 2*pi
+    const double TWO_PI_LO = 2.4492935982947064e-16;  // 2*pi - TWO_PI_HI
+    const double k = rint(ang * INV_2PI);
+    double r = fma(-k, TWO_PI_HI, ang);
+    r = fma(-k, TWO_PI_LO, r);
+    sincosf((float)r, s, c);
+}
+
+// Rotates the two bf16 pairs packed in (lo, hi): lo holds x_i, x_{i+1} of the
+// first half, hi the partners x_{i+D/2}, x_{i+1+D/2}.
+__device__ __forceinline__ void rotate_pairs(uint32_t &lo, uint32_t &hi, double delta, double th0,
+                                             double th1) {
+    float s0, c0, s1, c1;
+    reduced_sincos(delta * th0, &s0, &c0);
+    reduced_sincos(delta * th1, &s1, &c1);
+    const float x0 = bf16_to_f32((uint16_t)(lo & 0xFFFF)), x1 = bf16_to_f32((uint16_t)(lo >> 16));
+    const float y0 = bf16_to_f32((uint16_t)(hi & 0xFFFF)), y1 = bf16_to_f32((uint16_t)(hi >> 16));
+    const float nx0 = x0 * c0 - y0 * s0, ny0 = y0 * c0 + x0 * s0;
+    const float nx1 = x1 * c1 - y1 * s1, ny1 = y1 * c1 + x1 * s1;
+    lo = (uint32_t)f32_to_bf16(nx0) | ((uint32_t)f32_to_bf16(nx1) << 16);
+    hi = (uint32_t)f32_to_bf16(ny0) | ((uint32_t)f32_to_bf16(ny1) << 16);
+}
+
+// Non-negative double -> IEEE half bits, round-to-nearest-even, from the
+// exact double (no intermediate float rounding).
+__device__ uint16_t f64_to_f16_rne(double x) {
+    if (!(x > 0.0)) return 0;
+    int e;
+    const double m = frexp(x, &e);  // x = m * 2^e, m in [0.5, 1)
+    if (e - 1 < -14) {               // below the smallest normal: grid 2^-24
+        return (uint16_t)rint(ldexp(x, 24));  // 1024 lands exactly on 2^-14's encoding
+    }
+    double mant = rint(ldexp(m, 11));  // 11 significant bits, in [1024, 2048]
+    if (mant == 2048.0) {
+        mant = 1024.0;
+        ++e;
+    }
+    const int field = e - 1 + 15;
+    if (field >= 31) return 0x7C00;
+    return (uint16_t)((field << 10) | ((int)mant - 1024));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    const int ex = (h >> 10) & 31, mt = h & 1023;
+    const float v = ex == 0 ? ldexpf((float)mt, -24) : ldexpf((float)(1024 + mt), ex - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+template <int TPT>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int m = TPT / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ int8_t quant_code(float x, float s) {
+    float q = rintf(__fdiv_rn(x, s));
+    q = fminf(fmaxf(q, -127.f), 127.f);
+    return (int8_t)(int)q;
+}
+
+// Scale bits for a row whose max |x| is amax: max(fp16(amax/127), 2^-24); zero row -> 1.0.
+__device__ __forceinline__ uint16_t int8_scale_bits(float amax) {
+    if (!(amax > 0.f)) return 0x3C00;
+    uint16_t b = f64_to_f16_rne((double)amax / 127.0);
+    return b == 0 ? (uint16_t)1 : b;
+}
+
+struct CompactArgs {
+    const uint16_t *K, *V;
+    const int32_t *pos_in, *kept, *n_kept;
+    const uint8_t *action;
+    int64_t T;
+    int kept_stride, out_stride, renumber_base;
+    double rope_base;
+    uint16_t *Ko, *Vo;
+    int32_t *po, *nh;
+    int8_t *Kq, *Vq;
+    uint16_t *Ks, *Vs;
+    int32_t *pq, *nl;
+};
+
+template <int D>
+__global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int blocks_per_row) {
+    constexpr int TPT = D / 4;
+    constexpr int TOK = CMP_THREADS / TPT;
+    const int64_t r = blockIdx.x / blocks_per_row;
+    const int cb = blockIdx.x % blocks_per_row;
+    int n = a.n_kept[r];
+    if (n > a.kept_stride) n = a.kept_stride;
+    if (n > a.out_stride) n = a.out_stride;
+    if (n < 0) n = 0;
+    if (cb == 0 && threadIdx.x == 0 && a.nh) a.nh[r] = n;
+    const int sub = threadIdx.x % TPT, tin = threadIdx.x / TPT;
+    const bool rot = a.renumber_base >= 0;
+    double th0 = 0.0, th1 = 0.0;
+    if (rot) {
+        th0 = pow(a.rope_base, -2.0 * (2 * sub) / D);
+        th1 = pow(a.rope_base, -2.0 * (2 * sub + 1) / D);
+    }
+    for (int rho = cb * TOK + tin; rho < n; rho += blocks_per_row * TOK) {
+        const int64_t j = a.kept[(size_t)r * a.kept_stride + rho];
+        if (j < 0 || j >= a.T) continue;
+        const size_t src = ((size_t)r * a.T + j) * D;
+        const size_t dst = ((size_t)r * a.out_stride + rho) * D;
+        uint32_t lo = *reinterpret_cast<const uint32_t *>(a.K + src + 2 * sub);
+        uint32_t hi = *reinterpret_cast<const uint32_t *>(a.K + src + D / 2 + 2 * sub);
+        const uint2 v = *reinterpret_cast<const uint2 *>(a.V + src + 4 * sub);
+        const int64_t p = a.pos_in ? (int64_t)a.pos_in[(size_t)r * a.T + j] : j;
+        int64_t pn = p;
+        if (rot) {
+            pn = (int64_t)a.renumber_base + rho;
+            rotate_pairs(lo, hi, (double)(pn - p), th0, th1);
+        }
+        *reinterpret_cast<uint32_t *>(a.Ko + dst + 2 * sub) = lo;
+        *reinterpret_cast<uint32_t *>(a.Ko + dst + D / 2 + 2 * sub) = hi;
+        *reinterpret_cast<uint2 *>(a.Vo + dst + 4 * sub) = v;
+        if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + rho] = (int32_t)pn;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
+    constexpr int TPT = D / 4;
+    constexpr int TOK = CMP_THREADS / TPT;
+    constexpr int NW = CMP_THREADS / 64;
+    __shared__ int32_t s_j[CMP_THREADS], s_slot[CMP_THREADS];
+    __shared__ uint8_t s_tier[CMP_THREADS];
+    __shared__ uint32_t s_wave[NW + 1];
+
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int n = a.n_kept[r];
+    if (n > a.kept_stride) n = a.kept_stride;
+    if (n < 0) n = 0;
+    const int sub = tid % TPT, tin = tid / TPT;
+    const bool rot = a.renumber_base >= 0;
+    double th0 = 0.0, th1 = 0.0;
+    if (rot) {
+        th0 = pow(a.rope_base, -2.0 * (2 * sub) / D);
+        th1 = pow(a.rope_base, -2.0 * (2 * sub + 1) / D);
+    }
+    int carry_h = 0, carry_l = 0;
+    for (int base = 0; base < n; base += CMP_THREADS) {
+        const int rho = base + tid;
+        const int act = rho < n ? a.action[(size_t)r * a.kept_stride + rho] : 0;
+        const uint32_t v = (uint32_t)(act == 2) | ((uint32_t)(act == 1) << 16);
+        // exclusive scan of (H, L) counts over the block
+        uint32_t x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) s_wave[wave] = x;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t c = 0;
+            for (int w = 0; w < NW; ++w) {
+                const uint32_t t = s_wave[w];
+                s_wave[w] = c;
+                c += t;
+            }
+            s_wave[NW] = c;
+        }
+        __syncthreads();
+        const uint32_t ex = s_wave[wave] + x - v;
+        const uint32_t tot = s_wave[NW];
+        int slot = -1;
+        if (act == 2) slot = carry_h + (int)(ex & 0xFFFFu);
+        if (act == 1) slot = carry_l + (int)(ex >> 16);
+        if (slot >= a.out_stride) slot = -1;
+        s_j[tid] = rho < n ? a.kept[(size_t)r * a.kept_stride + rho] : -1;
+        s_slot[tid] = slot;
+        s_tier[tid] = (uint8_t)act;
+        __syncthreads();
+        for (int e = tin; e < CMP_THREADS; e += TOK) {
+            const int64_t j = s_j[e];
+            const int sl = s_slot[e];
+            const int tier = s_tier[e];
+            // Uniform across the TPT-thread group: all of it reads the same entry.
+            if (sl < 0 || j < 0 || j >= a.T || (tier != 1 && tier != 2)) continue;
+            const int rho_e = base + e;
+            const size_t src = ((size_t)r * a.T + j) * D;
+            uint32_t lo = *reinterpret_cast<const uint32_t *>(a.K + src + 2 * sub);
+            uint32_t hi = *reinterpret_cast<const uint32_t *>(a.K + src + D / 2 + 2 * sub);
+            const uint2 vv = *reinterpret_cast<const uint2 *>(a.V + src + 4 * sub);
+            const int64_t p = a.pos_in ? (int64_t)a.pos_in[(size_t)r * a.T + j] : j;
+            int64_t pn = p;
+            if (rot) {
+                pn = (int64_t)a.renumber_base + rho_e;
+                rotate_pairs(lo, hi, (double)(pn - p), th0, th1);
+            }
+            const size_t dst = ((size_t)r * a.out_stride + sl) * D;
+            if (tier == 2) {
+                *reinterpret_cast<uint32_t *>(a.Ko + dst + 2 * sub) = lo;
+                *reinterpret_cast<uint32_t *>(a.Ko + dst + D / 2 + 2 * sub) = hi;
+                *reinterpret_cast<uint2 *>(a.Vo + dst + 4 * sub) = vv;
+                if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + sl] = (int32_t)pn;
+            } else {
+                const float k0 = bf16_to_f32((uint16_t)(lo & 0xFFFF)), k1 = bf16_to_f32((uint16_t)(lo >> 16));
+                const float k2 = bf16_to_f32((uint16_t)(hi & 0xFFFF)), k3 = bf16_to_f32((uint16_t)(hi >> 16));
+                const float v0 = bf16_to_f32((uint16_t)(vv.x & 0xFFFF)), v1 = bf16_to_f32((uint16_t)(vv.x >> 16));
+                const float v2 = bf16_to_f32((uint16_t)(vv.y & 0xFFFF)), v3 = bf16_to_f32((uint16_t)(vv.y >> 16));
+                const float kmax = group_max<TPT>(fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3))));
+                const float vmax = group_max<TPT>(fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3))));
+                const uint16_t ksb = int8_scale_bits(kmax), vsb = int8_scale_bits(vmax);
+                const float ks = f16_to_f32(ksb), vs = f16_to_f32(vsb);
+                int8_t *kq = a.Kq + dst;
+                int8_t *vq = a.Vq + dst;
+                const uint16_t klo = (uint16_t)(uint8_t)quant_code(k0, ks) | ((uint16_t)(uint8_t)quant_code(k1, ks) << 8);
+                const uint16_t khi = (uint16_t)(uint8_t)quant_code(k2, ks) | ((uint16_t)(uint8_t)quant_code(k3, ks) << 8);
+                *reinterpret_cast<uint16_t *>(kq + 2 * sub) = klo;
+                *reinterpret_cast<uint16_t *>(kq + D / 2 + 2 * sub) = khi;
+                const uint32_t vc = (uint32_t)(uint8_t)quant_code(v0, vs) | ((uint32_t)(uint8_t)quant_code(v1, vs) << 8) |
+                                    ((uint32_t)(uint8_t)quant_code(v2, vs) << 16) |
+                                    ((uint32_t)(uint8_t)quant_code(v3, vs) << 24);
+                *reinterpret_cast<uint32_t *>(vq + 4 * sub) = vc;
+                if (sub == 0) {
+                    a.Ks[(size_t)r * a.out_stride + sl] = ksb;
+                    a.Vs[(size_t)r * a.out_stride + sl] = vsb;
+                    if (a.pq) a.pq[(size_t)r * a.out_stride + sl] = (int32_t)pn;
+                }
+            }
+        }
+        carry_h += (int)(tot & 0xFFFFu);
+        carry_l += (int)(tot >> 16);
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (a.nh) a.nh[r] = carry_h < a.out_stride ? carry_h : a.out_stride;
+        if (a.nl) a.nl[r] = carry_l < a.out_stride ? carry_l : a.out_stride;
+    }
+}
+
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, const uint16_t *V,
+                                    const int32_t *pos_in, const int32_t *kept_idx,
+                                    int32_t kept_stride, const int32_t *n_kept, int32_t renumber_base,
+                                    double rope_base, const kvc_compact_out *out, void *stream) {
+    int st = check_dims(dims, "kvc_compact_rerotate");
+    if (st != KVC_OK) return st;
+    if (!K || !V || !kept_idx || !n_kept || !out)
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: NULL pointer");
+    if (kept_stride <= 0 || out->out_stride <= 0 || out->reserved != 0)
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: strides must be positive (kept %d, out %d)",
+                    kept_stride, out->out_stride);
+    if (renumber_base >= 0 && !(rope_base > 1.0))
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: rope_base %g must exceed 1", rope_base);
+    if (renumber_base >= 0 && (int64_t)renumber_base + kept_stride > (int64_t)INT32_MAX)
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: renumbered positions overflow int32");
+    if (out->action) {
+        if (!out->Kq || !out->Vq || !out->Ks || !out->Vs || !out->K_out || !out->V_out)
+            return fail(KVC_ERR_ARG, "kvc_compact_rerotate: tiered output needs bf16 and int8 pools");
+    } else if (!out->K_out || !out->V_out) {
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: K_out/V_out are NULL");
+    }
+    CompactArgs a;
+    a.K = K;
+    a.V = V;
+    a.pos_in = pos_in;
+    a.kept = kept_idx;
+    a.n_kept = n_kept;
+    a.action = out->action;
+    a.T = dims->n_tokens;
+    a.kept_stride = kept_stride;
+    a.out_stride = out->out_stride;
+    a.renumber_base = renumber_base;
+    a.rope_base = rope_base;
+    a.Ko = out->K_out;
+    a.Vo = out->V_out;
+    a.po = out->pos_out;
+    a.nh = out->n_h;
+    a.Kq = out->Kq;
+    a.Vq = out->Vq;
+    a.Ks = out->Ks;
+    a.Vs = out->Vs;
+    a.pq = out->pos_q;
+    a.nl = out->n_l;
+    const int64_t rows = n_rows(dims);
+    hipStream_t s = as_stream(stream);
+    if (!out->action) {
+        const int tok = CMP_THREADS / (dims->head_dim / 4);
+        const int cap = kept_stride < out->out_stride ? kept_stride : out->out_stride;
+        int bpr = (cap + 4 * tok - 1) / (4 * tok);  // about 4 tokens per group
+        if (bpr < 1) bpr = 1;
+        if (rows * bpr > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_compact_rerotate: grid too large");
+        if (dims->head_dim == 128)
+            compact_plain<128><<<dim3((unsigned)(rows * bpr)), dim3(CMP_THREADS), 0, s>>>(a, bpr);
+        else
+            compact_plain<64><<<dim3((unsigned)(rows * bpr)), dim3(CMP_THREADS), 0, s>>>(a, bpr);
+    } else {
+        if (dims->head_dim == 128)
+            compact_tiered<128><<<dim3((unsigned)rows), dim3(CMP_THREADS), 0, s>>>(a);
+        else
+            compact_tiered<64><<<dim3((unsigned)rows), dim3(CMP_THREADS), 0, s>>>(a);
+    }
+    return check_launch("kvc_compact_rerotate");
+}

@@ -1,0 +1,60 @@
+// Internal helpers shared by the kvc HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+// ---------------------------------------------------------------- host side
+
+// Records the message for kvc_last_error() and returns `status`.
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Checks the launch just enqueued; returns KVC_OK or KVC_ERR_HIP.
+int check_launch(const char *what);
+
+// Validates a kvc_dims for the kernels' shape limits.
+int check_dims(const kvc_dims *d, const char *who);
+
+inline int64_t n_rows(const kvc_dims *d) {
+    return (int64_t)d->n_seq * d->n_layers * d->n_kv_heads;
+}
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------- device side
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// float -> bf16 with round-to-nearest-even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Row r = (n*L + l)*Hkv + h  ->  (n, l, h).
+struct RowIdx {
+    int n, l, h;
+};
+__device__ __forceinline__ RowIdx split_row(int64_t r, int L, int Hkv) {
+    RowIdx o;
+    o.h = (int)(r % Hkv);
+    int64_t nl = r / Hkv;
+    o.l = (int)(nl % L);
+    o.n = (int)(nl / L);
+    return o;
+}
+
+}  // namespace kvc

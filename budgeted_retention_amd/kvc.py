@@ -1,0 +1,149 @@
+"""Thin Python binding of libkvc.so with the C ABI's names.
+
+Only argument marshalling happens here: torch tensors (device memory) are
+checked for device, dtype and contiguity and turned into raw pointers, and
+the call's status is turned into an exception. Every step of the path runs in
+the HIP kernels behind the ABI; there is no fallback implementation.
+"""
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+KvcDims = _lib.KvcDims
+KVC_OP_SCORE = _lib.KVC_OP_SCORE
+KVC_OP_SELECT = _lib.KVC_OP_SELECT
+KVC_OK = _lib.KVC_OK
+KVC_WARN_FLOOR_EXCESS = _lib.KVC_WARN_FLOOR_EXCESS
+KvcError = _lib.KvcError
+
+
+def make_dims(n_seq, n_layers, n_kv_heads, n_q_heads, head_dim, n_tokens):
+    return KvcDims(n_seq, n_layers, n_kv_heads, n_q_heads, head_dim, 0, n_tokens)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must live in GPU memory (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def kvc_version():
+    return _lib.load().kvc_version()
+
+
+def kvc_layer_group(layer, n_layers, n_groups):
+    return _lib.load().kvc_layer_group(layer, n_layers, n_groups)
+
+
+def kvc_foresight_bonus(sigma, lam, steps_ahead):
+    return _lib.load().kvc_foresight_bonus(sigma, lam, steps_ahead)
+
+
+def kvc_workspace_bytes(op, dims, W=0, B=0):
+    lib = _lib.load()
+    n = lib.kvc_workspace_bytes(op, ctypes.byref(dims), W, B)
+    if n == 0 and lib.kvc_last_error():
+        msg = lib.kvc_last_error().decode()
+        if msg.startswith("kvc_workspace_bytes"):
+            raise KvcError(_lib.KVC_ERR_ARG, msg)
+    return n
+
+
+def workspace(op, dims, W=0, B=0, device="cuda"):
+    """Allocate (through torch) the workspace an operation needs."""
+    n = kvc_workspace_bytes(op, dims, W, B)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def kvc_score(dims, K, Q_obs, W, scores, ws, stream=None):
+    st = _lib.load().kvc_score(
+        ctypes.byref(dims), _ptr(K, torch.bfloat16, "K"), _ptr(Q_obs, torch.bfloat16, "Q_obs"), W,
+        _ptr(scores, torch.float32, "scores"), _ptr(ws, None, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    return _lib.check(st)
+
+
+@dataclass
+class Policy:
+    n_sink: int
+    n_recent: int
+    budget: int
+    n_tags: int = 1
+    n_groups: int = 1
+    layer_base: int = 0
+    n_layers_model: int = 1
+    tags: Optional[torch.Tensor] = None        # uint8 [N][T]
+    tag_bonus: Optional[torch.Tensor] = None   # float32 [n_tags][n_groups]
+    tag_floor: Optional[torch.Tensor] = None   # uint8 [n_tags][n_groups]
+
+    def to_c(self):
+        return _lib.KvcPolicy(
+            self.n_sink, self.n_recent, self.budget, self.n_tags, self.n_groups, self.layer_base,
+            self.n_layers_model, 0, _ptr(self.tags, torch.uint8, "tags"),
+            _ptr(self.tag_bonus, torch.float32, "tag_bonus"),
+            _ptr(self.tag_floor, torch.uint8, "tag_floor"))
+
+
+def kvc_select(dims, scores, policy: Policy, kept_idx, kept_stride, n_kept, ws=None, stream=None):
+    pol = policy.to_c()
+    st = _lib.load().kvc_select(
+        ctypes.byref(dims), _ptr(scores, torch.float32, "scores"), ctypes.byref(pol),
+        _ptr(kept_idx, torch.int32, "kept_idx"), kept_stride, _ptr(n_kept, torch.int32, "n_kept"),
+        _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    return _lib.check(st)
+
+
+@dataclass
+class CompactOut:
+    out_stride: int
+    K_out: torch.Tensor
+    V_out: torch.Tensor
+    pos_out: Optional[torch.Tensor] = None
+    n_h: Optional[torch.Tensor] = None
+    action: Optional[torch.Tensor] = None      # uint8 [rows][kept_stride]
+    Kq: Optional[torch.Tensor] = None
+    Vq: Optional[torch.Tensor] = None
+    Ks: Optional[torch.Tensor] = None          # fp16 scales stored as int16 bits
+    Vs: Optional[torch.Tensor] = None
+    pos_q: Optional[torch.Tensor] = None
+    n_l: Optional[torch.Tensor] = None
+
+    def to_c(self):
+        return _lib.KvcCompactOut(
+            _ptr(self.action, torch.uint8, "action"), self.out_stride, 0,
+            _ptr(self.K_out, torch.bfloat16, "K_out"), _ptr(self.V_out, torch.bfloat16, "V_out"),
+            _ptr(self.pos_out, torch.int32, "pos_out"), _ptr(self.n_h, torch.int32, "n_h"),
+            _ptr(self.Kq, torch.int8, "Kq"), _ptr(self.Vq, torch.int8, "Vq"),
+            _ptr(self.Ks, torch.int16, "Ks"), _ptr(self.Vs, torch.int16, "Vs"),
+            _ptr(self.pos_q, torch.int32, "pos_q"), _ptr(self.n_l, torch.int32, "n_l"))
+
+
+def kvc_compact_rerotate(dims, K, V, pos_in, kept_idx, kept_stride, n_kept, renumber_base, rope_base,
+                         out: CompactOut, stream=None):
+    o = out.to_c()
+    st = _lib.load().kvc_compact_rerotate(
+        ctypes.byref(dims), _ptr(K, torch.bfloat16, "K"), _ptr(V, torch.bfloat16, "V"),
+        _ptr(pos_in, torch.int32, "pos_in"), _ptr(kept_idx, torch.int32, "kept_idx"), kept_stride,
+        _ptr(n_kept, torch.int32, "n_kept"), renumber_base, float(rope_base), ctypes.byref(o),
+        _stream(stream))
+    return _lib.check(st)

@@ -1,0 +1,201 @@
+/*
+ * kvc -- budgeted KV-cache compaction on AMD MI355X (gfx950).
+ *
+ * C ABI of libkvc.so. The operations follow three pages on budgeted KV
+ * retention:
+ *   PASK     -- "Parser Transitions Already Reveal Structural Responsibility:
+ *               KV Persistence for Structured Generation"
+ *   PACE     -- "PACE: Keeping the Right Tokens in the KV Cache Is Not Enough
+ *               for Long-Horizon LLM Agents"
+ *   CommitKV -- "CommitKV: Lifecycle-Aware KV Cache Compression via Commit
+ *               Transitions for Multi-Turn Agents"
+ *
+ * Conventions shared by every call:
+ *  - Tensor arguments are DEVICE pointers to contiguous, row-major buffers
+ *    that the caller owns; the library never allocates or frees device
+ *    memory. bf16 tensors are passed as uint16_t bit patterns, fp16 scales
+ *    likewise.
+ *  - A "row" is one (sequence, layer, KV head) triple, r = (n*L + l)*Hkv + h.
+ *    Query head g of a row's GQA group is absolute head h*G + g, G = Hq/Hkv.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call checks
+ *    its arguments on the host, then only enqueues work on `stream`: it does
+ *    not synchronise, so results are valid once the stream reaches them.
+ *  - Argument errors return before anything is enqueued. KVC_ERR_HIP reports
+ *    a failed launch. kvc_last_error() returns a thread-local description of
+ *    the last non-OK status.
+ *  - The library keeps no state between calls; calls on different streams
+ *    may run concurrently if their buffers do not overlap.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_WARN_FLOOR_EXCESS = 1,  /* sink + recent alone exceed the budget: all protected tokens kept */
+    KVC_ERR_ARG = -1,           /* NULL pointer, negative size, inconsistent shape */
+    KVC_ERR_UNSUPPORTED = -2,   /* shape outside what the kernels handle (head_dim, W*G, ...) */
+    KVC_ERR_WORKSPACE = -3,     /* workspace missing or smaller than kvc_workspace_bytes() */
+    KVC_ERR_HIP = -4            /* the HIP runtime rejected a launch */
+} kvc_status;
+
+/* Shape of the cache buffers handed to a call. */
+typedef struct kvc_dims {
+    int32_t n_seq;       /* N */
+    int32_t n_layers;    /* L: layers present in the buffers of this call */
+    int32_t n_kv_heads;  /* Hkv */
+    int32_t n_q_heads;   /* Hq, a multiple of Hkv */
+    int32_t head_dim;    /* d: 64 or 128 */
+    int32_t reserved;    /* must be 0 */
+    int64_t n_tokens;    /* T: cached tokens per row */
+} kvc_dims;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int kvc_version(void);
+
+/* Thread-local text for the last non-OK status returned on this thread. */
+const char *kvc_last_error(void);
+
+/* Operation ids for kvc_workspace_bytes(). */
+enum { KVC_OP_SCORE = 1, KVC_OP_SELECT = 2 };
+
+/* Device workspace (bytes) that operation `op` needs for these dims, window W
+ * and budget B; 0 if it needs none. Returns 0 and sets the error on bad args. */
+size_t kvc_workspace_bytes(int op, const kvc_dims *dims, int32_t W, int32_t B);
+
+/*
+ * Observation-window attention score (PASK §3.1 Eq. 1 attention; the
+ * SnapKV-style window of PASK Appendix C and CommitKV's pre-commit window,
+ * CommitKV §3.1 Eq. 5; causal rule of CommitKV Eq. 6).
+ *
+ * For every row and every cached token j < T:
+ *   scores[r][j] = sum_{g<G} sum_{w<W} softmax_j( q_{g,w} . k_j / sqrt(d) )
+ * where query (g, w) sits at position T-W+w and sees keys j <= T-W+w.
+ *
+ *   K       bf16 [N][L][Hkv][T][d]  cached (already rotated) keys
+ *   Q_obs   bf16 [N][L][Hq][W][d]   rotated queries of the last W positions
+ *   W       1 <= W <= T, W*G <= 256
+ *   scores  fp32 [N][L][Hkv][T]     output, sums to W*G per row
+ *   ws      device workspace of kvc_workspace_bytes(KVC_OP_SCORE, dims, W, 0) bytes
+ * Supported: d in {64, 128}. Deterministic (no float atomics).
+ */
+int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
+              float *scores, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Retention policy for kvc_select: bonus and protection floor per
+ * (tag, layer group) from a frozen table (PASK §3.5 Eq. 11 lookup, PASK
+ * Appendix A.2 layer groups; PACE §3.1 Eq. 2 foresight bonus, precomputed per
+ * span tag), plus sink and recent-window protection (PASK Appendix B.2;
+ * PACE Table 1 counts them inside the budget).
+ */
+typedef struct kvc_policy {
+    int32_t n_sink;             /* tokens j < n_sink are protected */
+    int32_t n_recent;           /* tokens j >= T - n_recent are protected */
+    int32_t budget;             /* B: tokens kept per row, protected ones included */
+    int32_t n_tags;             /* rows of the tables (>= 1); tag values >= n_tags read as 0 */
+    int32_t n_groups;           /* columns of the tables (>= 1) */
+    int32_t layer_base;         /* model index of the first layer in this call */
+    int32_t n_layers_model;     /* model depth used for the group rule */
+    int32_t reserved;           /* must be 0 */
+    const uint8_t *tags;        /* device u8 [N][T] tag per token, or NULL (all tag 0) */
+    const float *tag_bonus;     /* device fp32 [n_tags][n_groups], or NULL (no bonus) */
+    const uint8_t *tag_floor;   /* device u8 [n_tags][n_groups] 1 = protected, or NULL */
+} kvc_policy;
+
+/* Layer group of model layer `layer` among `n_groups` groups of an
+ * n_layers-deep model: #{c in 1..n_groups-1 : layer >= ceil(c*n_layers/n_groups)}
+ * (PASK Appendix A.2 generalised). Returns -1 on bad arguments. */
+int32_t kvc_layer_group(int32_t layer, int32_t n_layers, int32_t n_groups);
+
+/* PACE §3.1 Eq. 2 foresight bonus sigma*(1/2 + 1/2*exp(-lambda*steps_ahead))
+ * for a span whose next reader is steps_ahead >= 0 steps away. Host helper
+ * for filling tag_bonus. */
+double kvc_foresight_bonus(double sigma, double lambda, double steps_ahead);
+
+/*
+ * Top-B selection under the budget (PACE §2 problem statement and §3.1
+ * "keep the top-B by the sum"; PASK Appendix B.4 tie rule and floor excess;
+ * CommitKV §3.1 Eq. 4 index set).
+ *
+ * Per row: total[j] = scores[j] + tag_bonus[tag_j][group(layer)];
+ * protected[j] = j < n_sink || j >= T - n_recent || tag_floor[tag_j][group].
+ * Kept set = every protected token plus the best unprotected tokens by
+ * (total descending, index ascending) until `budget` tokens are kept; all T
+ * if T <= budget; only the protected ones if they alone reach the budget.
+ *
+ *   scores     fp32 [N][L][Hkv][T]   (NaN totals rank lowest)
+ *   kept_idx   int32 [N][L][Hkv][kept_stride]  ascending kept token indices;
+ *              only the first min(n_kept, kept_stride) entries are written
+ *   kept_stride  >= min(budget, T)
+ *   n_kept     int32 [N][L][Hkv]  number of kept tokens; n_kept > budget
+ *              reports floor excess (the device-side count is the authority)
+ *   ws         kvc_workspace_bytes(KVC_OP_SELECT, ...) bytes (may be 0/NULL)
+ * Returns KVC_WARN_FLOOR_EXCESS (after enqueueing) when n_sink + n_recent
+ * alone exceed the budget and T > budget.
+ */
+int kvc_select(const kvc_dims *dims, const float *scores, const kvc_policy *policy,
+               int32_t *kept_idx, int32_t kept_stride, int32_t *n_kept,
+               void *ws, size_t ws_bytes, void *stream);
+
+/* Outputs of kvc_compact_rerotate. Strides are in tokens per row. */
+typedef struct kvc_compact_out {
+    /* Per kept entry action, device u8 [N][L][Hkv][kept_stride]:
+     * 0 = release, 1 = int8 tier, 2 = bf16 tier (PASK §3.2 {R, L, H}).
+     * NULL = every kept token goes to the bf16 tier. */
+    const uint8_t *action;
+    int32_t out_stride;   /* capacity per row of every output pool below */
+    int32_t reserved;     /* must be 0 */
+    /* bf16 tier */
+    uint16_t *K_out;      /* bf16 [N][L][Hkv][out_stride][d] */
+    uint16_t *V_out;      /* bf16 [N][L][Hkv][out_stride][d] */
+    int32_t *pos_out;     /* int32 [N][L][Hkv][out_stride], may be NULL */
+    int32_t *n_h;         /* int32 [N][L][Hkv] rows written to the bf16 tier, may be NULL */
+    /* int8 tier (required only when `action` is given) */
+    int8_t *Kq;           /* int8 [N][L][Hkv][out_stride][d] */
+    int8_t *Vq;           /* int8 [N][L][Hkv][out_stride][d] */
+    uint16_t *Ks;         /* fp16 [N][L][Hkv][out_stride] per-token K scale */
+    uint16_t *Vs;         /* fp16 [N][L][Hkv][out_stride] per-token V scale */
+    int32_t *pos_q;       /* int32 [N][L][Hkv][out_stride], may be NULL */
+    int32_t *n_l;         /* int32 [N][L][Hkv] rows written to the int8 tier, may be NULL */
+} kvc_compact_out;
+
+/*
+ * Gather, renumber and exact re-rotation (PACE §3.2 "Bounded positions",
+ * Proposition 1; CommitKV §3.1 Eq. 4 for the shared index set; PASK
+ * Appendix B.5 for the int8 tier with 7 -> 127).
+ *
+ * For the rank rho-th kept token j = kept_idx[r][rho] (rho < n_kept[r]):
+ *   p  = pos_in ? pos_in[r][j] : j
+ *   p' = renumber_base + rho            (renumber_base >= 0)
+ *   K' = bf16_rne( R_{p'-p} K[j] )      split-half RoPE, theta_i = rope_base^(-2i/d),
+ *                                       angle (p'-p)*theta_i formed in fp64
+ *   V' = V[j] (bit copy),  pos' = p'
+ * With renumber_base < 0 positions are kept (p' = p) and K' = K[j] bit-exact.
+ * The kept entries are then routed by `action` in rank order (stable):
+ * bf16 tier rows are written as above; int8 tier rows get, separately for K'
+ * and V', scale s = max(fp16_rne(max|x|/127), 2^-24) (a zero row: s = 1,
+ * codes 0) and codes clamp(rne(x/s), -127, 127); released rows are dropped.
+ *
+ *   K, V      bf16 [N][L][Hkv][T][d]
+ *   pos_in    int32 [N][L][Hkv][T] physical positions, or NULL (position = index)
+ *   kept_idx  int32 [N][L][Hkv][kept_stride], n_kept int32 [N][L][Hkv] (from kvc_select)
+ *   Entries beyond min(n_kept, kept_stride, out_stride) are ignored; indices
+ *   outside [0, T) are skipped.
+ */
+int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, const uint16_t *V,
+                         const int32_t *pos_in, const int32_t *kept_idx, int32_t kept_stride,
+                         const int32_t *n_kept, int32_t renumber_base, double rope_base,
+                         const kvc_compact_out *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

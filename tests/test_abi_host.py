@@ -1,0 +1,134 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before enqueueing anything (these
+calls return before any HIP runtime call, so no GPU is needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from budgeted_retention_amd import _lib
+from oracle import policy as o_policy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(kvc_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    declared = _declared_functions()
+    assert {"kvc_score", "kvc_select", "kvc_compact_rerotate"} <= declared
+    missing = [n for n in sorted(declared) if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding knows a prototype for each
+    assert declared <= set(_lib.PROTOTYPES), declared - set(_lib.PROTOTYPES)
+
+
+def test_version_and_helpers_match_oracle():
+    lib = _lib.load()
+    assert lib.kvc_version() >= 100
+    for L, n in [(36, 3), (40, 3), (32, 3), (32, 4), (28, 1), (7, 5)]:
+        for l in range(L):
+            assert lib.kvc_layer_group(l, L, n) == o_policy.layer_group(l, L, n)
+    assert lib.kvc_layer_group(5, 4, 2) == -1
+    for k in [0, 1, 3, 7, 50]:
+        assert lib.kvc_foresight_bonus(1e3, 0.35, k) == pytest.approx(
+            o_policy.foresight_bonus(1e3, 0.35, k), rel=1e-14)
+
+
+def _dims(**kw):
+    d = dict(n_seq=1, n_layers=1, n_kv_heads=2, n_q_heads=8, head_dim=64, n_tokens=4096)
+    d.update(kw)
+    return _lib.KvcDims(d["n_seq"], d["n_layers"], d["n_kv_heads"], d["n_q_heads"],
+                        d["head_dim"], 0, d["n_tokens"])
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), _lib.KVC_ERR_UNSUPPORTED),
+    (dict(n_q_heads=7), _lib.KVC_ERR_ARG),
+    (dict(n_tokens=0), _lib.KVC_ERR_ARG),
+    (dict(n_seq=-1), _lib.KVC_ERR_ARG),
+])
+def test_score_rejects_bad_dims(kw, code):
+    lib = _lib.load()
+    d = _dims(**kw)
+    st = lib.kvc_score(ctypes.byref(d), FAKE, FAKE, 16, FAKE, FAKE, 1 << 30, None)
+    assert st == code
+    assert lib.kvc_last_error().decode().startswith("kvc_score")
+
+
+def test_score_rejects_window_workspace_and_nulls():
+    lib = _lib.load()
+    d = _dims()
+    ws = lib.kvc_workspace_bytes(_lib.KVC_OP_SCORE, ctypes.byref(d), 16, 0)
+    assert ws > 0
+    assert lib.kvc_score(ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE, ws, None) == _lib.KVC_ERR_ARG
+    assert lib.kvc_score(ctypes.byref(d), FAKE, FAKE, 4097, FAKE, FAKE, ws, None) == _lib.KVC_ERR_ARG
+    assert lib.kvc_score(ctypes.byref(d), FAKE, FAKE, 16, FAKE, FAKE, ws - 1, None) == _lib.KVC_ERR_WORKSPACE
+    assert lib.kvc_score(ctypes.byref(d), FAKE, FAKE, 16, FAKE, None, ws, None) == _lib.KVC_ERR_WORKSPACE
+    assert lib.kvc_score(ctypes.byref(d), None, FAKE, 16, FAKE, FAKE, ws, None) == _lib.KVC_ERR_ARG
+    d2 = _dims(n_q_heads=64, n_kv_heads=2)     # G = 32, W*G = 512 > 256
+    ws2 = lib.kvc_workspace_bytes(_lib.KVC_OP_SCORE, ctypes.byref(d2), 16, 0)
+    assert lib.kvc_score(ctypes.byref(d2), FAKE, FAKE, 16, FAKE, FAKE, ws2, None) == _lib.KVC_ERR_UNSUPPORTED
+    assert lib.kvc_workspace_bytes(99, ctypes.byref(d), 16, 0) == 0
+
+
+def _policy(**kw):
+    p = dict(n_sink=4, n_recent=64, budget=512, n_tags=1, n_groups=1, layer_base=0, n_layers_model=1)
+    p.update(kw)
+    return _lib.KvcPolicy(p["n_sink"], p["n_recent"], p["budget"], p["n_tags"], p["n_groups"],
+                          p["layer_base"], p["n_layers_model"], 0, None, None, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(budget=0), dict(n_sink=-1), dict(n_tags=0), dict(n_tags=300), dict(n_groups=0),
+    dict(layer_base=1), dict(n_layers_model=0),
+])
+def test_select_rejects_bad_policy(kw):
+    lib = _lib.load()
+    d = _dims()
+    p = _policy(**kw)
+    assert lib.kvc_select(ctypes.byref(d), FAKE, ctypes.byref(p), FAKE, 512, FAKE, None, 0, None) == _lib.KVC_ERR_ARG
+
+
+def test_select_rejects_small_kept_stride():
+    lib = _lib.load()
+    d = _dims()
+    p = _policy()
+    assert lib.kvc_select(ctypes.byref(d), FAKE, ctypes.byref(p), FAKE, 511, FAKE, None, 0, None) == _lib.KVC_ERR_ARG
+
+
+def test_compact_rejects_bad_outputs():
+    lib = _lib.load()
+    d = _dims()
+    out = _lib.KvcCompactOut()
+    out.out_stride = 512
+    st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 512, FAKE, 0, 1e4,
+                                  ctypes.byref(out), None)
+    assert st == _lib.KVC_ERR_ARG                                # K_out / V_out missing
+    out.K_out = out.V_out = FAKE
+    st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 512, FAKE, 0, 1.0,
+                                  ctypes.byref(out), None)
+    assert st == _lib.KVC_ERR_ARG                                # rope base must exceed 1
+    out.action = FAKE
+    st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 512, FAKE, -1, 1e4,
+                                  ctypes.byref(out), None)
+    assert st == _lib.KVC_ERR_ARG                                # int8 pools missing
+    out.action = None
+    out.out_stride = 0
+    st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 512, FAKE, -1, 1e4,
+                                  ctypes.byref(out), None)
+    assert st == _lib.KVC_ERR_ARG

@@ -1,0 +1,145 @@
+"""GPU parity: kvc_score -> kvc_select -> kvc_compact_rerotate against the
+float64 oracle on the same seeded inputs, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from budgeted_retention_amd import synth
+from oracle import numfmt
+import kvc_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+SIGMA, LAMBDA = 1e3, 0.35
+
+
+def _gpu_policy(w, sp, tags_dev, n_groups=1, floor=None):
+    from budgeted_retention_amd import kvc
+    vals = [0.0] + [0.0 if s is None else kvc.kvc_foresight_bonus(SIGMA, LAMBDA, s)
+                    for s in sp.steps_ahead]
+    bonus = torch.tensor(vals, dtype=torch.float32).reshape(-1, 1).repeat(1, n_groups)
+    fl = None if floor is None else torch.from_numpy(np.asarray(floor, np.uint8)).cuda()
+    return kvc.Policy(w.n_sink, w.n_recent, w.budget, len(vals), n_groups, 0, w.n_layers,
+                      tags_dev, bonus.cuda(), fl)
+
+
+def _check_rows(w, inp, res, rows, floor=None, n_groups=1, layer_base=0, n_layers_model=None):
+    N, L, Hkv, Hq, d, T, W = (w.n_seq, inp.K.shape[1], w.n_kv_heads, w.n_q_heads, w.head_dim,
+                              w.n_tokens, w.window)
+    G = Hq // Hkv
+    bonus = tl.oracle_bonus_table(inp.spans.steps_ahead, SIGMA, LAMBDA)
+    bonus = np.repeat(bonus, n_groups, axis=1)
+    fl = np.zeros_like(bonus, dtype=np.uint8) if floor is None else np.asarray(floor)
+    from oracle import policy as o_policy
+    swaps = 0
+    for r in rows:
+        n, l, h = r // (L * Hkv), (r // Hkv) % L, r % Hkv
+        K_bits = tl.bits(inp.K[n, l, h])
+        V_bits = tl.bits(inp.V[n, l, h])
+        Qg = tl.f64(inp.Q_obs[n, l, h * G:(h + 1) * G])
+        grp = o_policy.layer_group(layer_base + l, n_layers_model or L, n_groups)
+        s, tot, prot, kept, _ = tl.oracle_row(numfmt.bf16_bits_to_f64(K_bits), Qg, W,
+                                              inp.spans.tags, bonus, fl, grp, w.n_sink,
+                                              w.n_recent, w.budget)
+        tl.check_scores(res["scores"][r], s)
+        swaps += tl.check_kept(res["kept"][r], res["n_kept"][r], kept, tot, prot, w.budget)
+        gk = res["kept"][r][: res["n_kept"][r]].astype(np.int64)
+        tl.check_compaction(res["K"][r], res["V"][r], res["pos"][r], K_bits, V_bits,
+                            np.arange(T), gk, w.renumber_base, w.rope_base)
+        assert res["n_h"][r] == gk.size
+    return swaps
+
+
+def _run(w, inp, **kw):
+    dev = inp.K.device
+    pol = _gpu_policy(w, inp.spans, inp.tags.to(dev), **kw)
+    dims = (w.n_seq, inp.K.shape[1], w.n_kv_heads, w.n_q_heads, w.head_dim, w.n_tokens)
+    # room for every protected token when floors exceed the budget
+    ks = w.n_tokens if w.n_sink + w.n_recent > w.budget else None
+    return tl.gpu_path(dims, inp.K, inp.V, inp.Q_obs, w.window, pol, w.renumber_base, w.rope_base,
+                       kept_stride=ks)
+
+
+def test_tiny_workload_all_rows():
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_compaction_inputs(w, "cpu")
+    inp.K, inp.V, inp.Q_obs = inp.K.cuda(), inp.V.cuda(), inp.Q_obs.cuda()
+    res = _run(w, inp)
+    assert (res["n_kept"] == w.budget).all()
+    _check_rows(w, inp, res, range(w.rows))
+    # spans carry +1e3, far above any score: all 4*32 span tokens are kept
+    for s, ln in inp.spans.spans:
+        for r in range(w.rows):
+            assert set(range(s, s + ln)) <= set(res["kept"][r].tolist())
+
+
+def test_tiny_workload_is_deterministic():
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_compaction_inputs(w, "cpu")
+    inp.K, inp.V, inp.Q_obs = inp.K.cuda(), inp.V.cuda(), inp.Q_obs.cuda()
+    a, b = _run(w, inp), _run(w, inp)
+    for k in ("scores", "kept", "K", "V", "pos"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("T,Hkv,Hq,d,W,B,sink,recent", [
+    (3001, 2, 14, 128, 5, 300, 4, 32),     # G = 7, ragged T, W*G = 35 (two waves, one partial)
+    (777, 1, 4, 64, 16, 100, 0, 16),       # no sinks, d = 64
+    (2049, 4, 16, 128, 32, 1500, 4, 128),  # W*G = 128, one key past a chunk boundary
+    (64, 2, 2, 64, 8, 100, 4, 8),          # T <= B: keep everything
+    (500, 1, 8, 128, 32, 40, 8, 64),       # sink + recent exceed B: floor excess
+    (1031, 1, 32, 64, 8, 64, 1, 8),        # W*G = 256, eight waves
+])
+def test_ragged_shapes_and_edges(T, Hkv, Hq, d, W, B, sink, recent):
+    w = synth.Workload("sweep", 1, 2, Hkv, Hq, d, T, W, sink, recent, B, 1e4, 0,
+                       3, (4, 12), 2, seed=31 + T)
+    inp = synth.make_compaction_inputs(w, "cpu")
+    inp.K, inp.V, inp.Q_obs = inp.K.cuda(), inp.V.cuda(), inp.Q_obs.cuda()
+    res = _run(w, inp)
+    if sink + recent > B and T > B:
+        assert res["status"] == 1      # KVC_WARN_FLOOR_EXCESS
+        assert (res["n_kept"] == min(sink + recent, T)).all()
+    _check_rows(w, inp, res, range(w.rows))
+
+
+def test_tag_floors_and_layer_groups():
+    # a floor table protecting span tag 2 in group 1 only: rows of layer 1 keep it all
+    T, B = 2000, 128
+    w = synth.Workload("floors", 1, 2, 2, 8, 64, T, 16, 4, 16, B, 1e4, 0, 3, (40, 40), 0, seed=5)
+    inp = synth.make_compaction_inputs(w, "cpu")
+    inp.K, inp.V, inp.Q_obs = inp.K.cuda(), inp.V.cuda(), inp.Q_obs.cuda()
+    floor = np.zeros((4, 2), np.uint8)
+    floor[2, 1] = 1
+    res = _run(w, inp, n_groups=2, floor=floor)
+    _check_rows(w, inp, res, range(w.rows), floor=floor, n_groups=2)
+    s, ln = inp.spans.spans[1]
+    for r in range(w.rows):
+        kept = set(res["kept"][r][: res["n_kept"][r]].tolist())
+        layer = (r // 2) % 2
+        assert set(range(s, s + ln)) <= kept if layer == 1 else True
+
+
+def test_qwen3_8b_100k_sampled_rows():
+    w = synth.WORKLOADS["qwen3_8b_100k"]
+    inp = synth.make_compaction_inputs(w, "cuda")
+    res = _run(w, inp)
+    assert (res["n_kept"] == w.budget).all()
+    swaps = _check_rows(w, inp, res, [0, 137, w.rows - 1])
+    assert swaps <= 4
+
+
+def test_qwen3_8b_1m_one_layer_sampled_row():
+    # one layer of the 1,048,576-token session (the per-layer call of the long workload)
+    w = synth.WORKLOADS["qwen3_8b_1m"]
+    inp = synth.make_compaction_inputs(w, "cuda", layers=1)
+    res = _run(w, inp)
+    assert (res["n_kept"] == w.budget).all()
+    _check_rows(w, inp, res, [5], n_layers_model=w.n_layers)
+    # the definition span (rank 0, 900,000 tokens back) survives and is renumbered into
+    # the bounded range: its rotary distance to the next query (at B) is below B
+    s, ln = inp.spans.spans[0]
+    for r in range(w.n_kv_heads):
+        kept = res["kept"][r][: res["n_kept"][r]]
+        where = np.flatnonzero((kept >= s) & (kept < s + ln))
+        assert where.size == ln
+        assert res["pos"][r][where].max() < w.budget
