@@ -63,6 +63,11 @@ PROTOTYPES = {
     "kvc_compact_rerotate": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_void_p,
                                             c_void_p, c_int32, c_void_p, c_int32, c_double,
                                             ctypes.POINTER(KvcCompactOut), c_void_p]),
+    "kvc_decode_workspace_bytes": (c_size_t, [ctypes.POINTER(KvcDims), c_int64, c_int64]),
+    "kvc_decode_attn": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int64, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None

@@ -147,3 +147,21 @@ def kvc_compact_rerotate(dims, K, V, pos_in, kept_idx, kept_stride, n_kept, renu
         _ptr(n_kept, torch.int32, "n_kept"), renumber_base, float(rope_base), ctypes.byref(o),
         _stream(stream))
     return _lib.check(st)
+
+
+def kvc_decode_workspace_bytes(dims, max_h, stride_l=0):
+    return _lib.load().kvc_decode_workspace_bytes(ctypes.byref(dims), max_h, stride_l)
+
+
+def kvc_decode_attn(dims, q, K, V, n_h, stride_h, o, ws, lse=None, block_table=None, page_size=0,
+                    blocks_per_seq=0, Kq=None, Vq=None, Ks=None, Vs=None, n_l=None, stride_l=0,
+                    stream=None):
+    st = _lib.load().kvc_decode_attn(
+        ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"), _ptr(K, torch.bfloat16, "K"),
+        _ptr(V, torch.bfloat16, "V"), _ptr(n_h, torch.int32, "n_h"), stride_h,
+        _ptr(block_table, torch.int32, "block_table"), page_size, blocks_per_seq,
+        _ptr(Kq, torch.int8, "Kq"), _ptr(Vq, torch.int8, "Vq"), _ptr(Ks, torch.int16, "Ks"),
+        _ptr(Vs, torch.int16, "Vs"), _ptr(n_l, torch.int32, "n_l"), stride_l,
+        _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    return _lib.check(st)

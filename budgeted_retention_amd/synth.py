@@ -185,3 +185,51 @@ def small_case(T, Hkv=2, Hq=8, d=64, W=16, L=1, N=1, seed=7, device="cpu"):
     V = normal_bf16((N, L, Hkv, T, d), seed * 16 + 2, device)
     Q = normal_bf16((N, L, Hq, W, d), seed * 16 + 3, device)
     return K, V, Q
+
+
+def decode_pools(N, L, Hkv, Hq, d, stride_h, stride_l=0, seed=11, device="cpu"):
+    """Random decode inputs: queries, a bf16 pool with per-row token counts in
+    [0, stride_h] (the first rows pinned to 0, 1 and stride_h), and optionally an
+    int8 pool (codes uniform in [-127, 127], fp16 scales uniform in [1e-3, 3e-2])
+    with counts in [0, stride_l]."""
+    rows = N * L * Hkv
+    rng = np.random.default_rng(seed)
+    q = normal_bf16((N, L, Hq, d), seed * 16 + 5, device)
+    K = normal_bf16((rows, stride_h, d), seed * 16 + 6, device)
+    V = normal_bf16((rows, stride_h, d), seed * 16 + 7, device)
+    n_h = rng.integers(0, stride_h + 1, rows)
+    n_h[: min(3, rows)] = [0, 1, stride_h][: min(3, rows)]
+    out = dict(q=q, K=K, V=V, n_h=torch.from_numpy(n_h.astype(np.int32)).to(device))
+    if stride_l:
+        n_l = rng.integers(0, stride_l + 1, rows)
+        if rows > 3:
+            n_l[0] = stride_l          # a row with only int8 tokens
+            n_l[3] = 0
+        codes = rng.integers(-127, 128, (2, rows, stride_l, d)).astype(np.int8)
+        scales = rng.uniform(1e-3, 3e-2, (2, rows, stride_l)).astype(np.float16).view(np.int16)
+        out.update(Kq=torch.from_numpy(codes[0]).to(device), Vq=torch.from_numpy(codes[1]).to(device),
+                   Ks=torch.from_numpy(scales[0].copy()).to(device),
+                   Vs=torch.from_numpy(scales[1].copy()).to(device),
+                   n_l=torch.from_numpy(n_l.astype(np.int32)).to(device))
+    return out
+
+
+def page_table(N, n_pages_storage, blocks_per_seq, seed=13):
+    """Per sequence, `blocks_per_seq` distinct page ids drawn from the row
+    storage's pages, in random order (a paged view of a cache)."""
+    rng = np.random.default_rng(seed)
+    tbl = np.stack([rng.permutation(n_pages_storage)[:blocks_per_seq] for _ in range(N)])
+    return torch.from_numpy(tbl.astype(np.int32))
+
+
+def kept_and_actions(rows, T, n_keep, seed=17, with_actions=True):
+    """Ascending random kept-index lists (n_keep per row, the last row keeping
+    fewer) and per-entry actions uniform over {0: release, 1: int8, 2: bf16}."""
+    rng = np.random.default_rng(seed)
+    kept = np.full((rows, n_keep), -1, np.int32)
+    n = np.full(rows, n_keep, np.int32)
+    n[-1] = n_keep // 2
+    for r in range(rows):
+        kept[r, : n[r]] = np.sort(rng.choice(T, n[r], replace=False))
+    act = rng.integers(0, 3, (rows, n_keep)).astype(np.uint8) if with_actions else None
+    return kept, n, act

@@ -194,6 +194,41 @@ int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, const uint16_t
                          const int32_t *n_kept, int32_t renumber_base, double rope_base,
                          const kvc_compact_out *out, void *stream);
 
+/* Device workspace (bytes) kvc_decode_attn needs: `max_h` is the number of
+ * bf16-partition tokens a row can address (stride_h, or blocks_per_seq *
+ * page_size for a paged layout), `stride_l` the int8 capacity (0 if none). */
+size_t kvc_decode_workspace_bytes(const kvc_dims *dims, int64_t max_h, int64_t stride_l);
+
+/*
+ * Decode attention over a compacted cache (PASK §3.1 Eq. 1 attention; PASK
+ * Appendix B.5 disjoint bf16/low-precision partitions with fp32 statistics,
+ * bf16 output and the Eq. 15 merge; grouped-query heads).
+ *
+ * For every row r and query head g of its group (absolute head h*G + g):
+ *   o = sum_t softmax_t(q . k_t / sqrt(d)) v_t
+ * over the union of the row's bf16 tokens (n_h[r] of them) and int8 tokens
+ * (n_l[r], dequantised as code * fp16 scale); every cached token is visible.
+ *
+ *   q            bf16 [N][L][Hq][d] (already rotated to the query position)
+ *   K, V         bf16 [N][L][Hkv][stride_h][d]
+ *   n_h          int32 [N][L][Hkv], clamped to the addressable tokens
+ *   block_table  int32 [N][blocks_per_seq] or NULL. When given, token t of row
+ *                (n, l, h) lives in slot block_table[n][t / page_size] *
+ *                page_size + t % page_size of that row's storage (paged
+ *                layout); slots outside [0, stride_h) are skipped.
+ *   Kq, Vq       int8 [N][L][Hkv][stride_l][d]; Ks, Vs fp16 [N][L][Hkv][stride_l];
+ *   n_l          int32 [N][L][Hkv], or NULL for no int8 partition
+ *   o            bf16 [N][L][Hq][d] output; a row with no tokens gives o = 0
+ *   lse          fp32 [N][L][Hq] natural-log normaliser (max + log sum), or NULL
+ *   ws           kvc_decode_workspace_bytes(dims, max_h, stride_l) bytes
+ * Supported: d in {64, 128}, G = Hq/Hkv <= 16.
+ */
+int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                    const int32_t *n_h, int64_t stride_h, const int32_t *block_table,
+                    int32_t page_size, int32_t blocks_per_seq, const int8_t *Kq, const int8_t *Vq,
+                    const uint16_t *Ks, const uint16_t *Vs, const int32_t *n_l, int64_t stride_l,
+                    uint16_t *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,3 +132,20 @@ def test_compact_rejects_bad_outputs():
     st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 512, FAKE, -1, 1e4,
                                   ctypes.byref(out), None)
     assert st == _lib.KVC_ERR_ARG
+
+
+def test_decode_rejects_bad_arguments():
+    lib = _lib.load()
+    d = _dims()
+    ws = lib.kvc_decode_workspace_bytes(ctypes.byref(d), 512, 0)
+    assert ws > 0
+    call = lambda **k: lib.kvc_decode_attn(
+        ctypes.byref(k.get("dims", d)), FAKE, FAKE, FAKE, FAKE, k.get("stride_h", 512),
+        k.get("bt", None), k.get("ps", 0), k.get("bps", 0), k.get("Kq", None), None, None, None,
+        k.get("n_l", None), k.get("stride_l", 0), FAKE, None, FAKE, k.get("ws", ws), None)
+    assert call(stride_h=0) == _lib.KVC_ERR_ARG
+    assert call(ws=ws - 1) == _lib.KVC_ERR_WORKSPACE
+    assert call(bt=FAKE, ps=0, bps=4) == _lib.KVC_ERR_ARG            # paged needs a page size
+    assert call(n_l=FAKE, stride_l=64) == _lib.KVC_ERR_ARG            # int8 pools missing
+    big = _dims(n_q_heads=64, n_kv_heads=2)                             # G = 32 > 16
+    assert call(dims=big, ws=1 << 40) == _lib.KVC_ERR_UNSUPPORTED

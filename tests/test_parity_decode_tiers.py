@@ -1,0 +1,146 @@
+"""GPU parity: kvc_decode_attn (bf16 pool, int8 pool, paged layout) and the
+int8/bf16/release tiers of kvc_compact_rerotate, against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from budgeted_retention_amd import synth
+from oracle import compact as o_compact, decode as o_decode, numfmt, quant as o_quant
+import kvc_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_decode(dims_t, p, stride_h, stride_l=0, block_table=None, page_size=0, bps=0):
+    from budgeted_retention_amd import kvc
+    N, L, Hkv, Hq, d = dims_t
+    dims = kvc.make_dims(N, L, Hkv, Hq, d, stride_h)
+    max_h = bps * page_size if block_table is not None else stride_h
+    ws = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims, max_h, stride_l)), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, L, Hq), dtype=torch.float32, device="cuda")
+    c = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    kvc.kvc_decode_attn(dims, c["q"], c["K"], c["V"], c["n_h"], stride_h, o, ws, lse,
+                        None if block_table is None else block_table.cuda(), page_size, bps,
+                        c.get("Kq"), c.get("Vq"), c.get("Ks"), c.get("Vs"), c.get("n_l"), stride_l)
+    torch.cuda.synchronize()
+    return tl.f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def _check_decode(g_o, g_lse, q, parts_per_row, dims_t):
+    N, L, Hkv, Hq, d = dims_t
+    G = Hq // Hkv
+    for n in range(N):
+        for l in range(L):
+            for hq in range(Hq):
+                r = (n * L + l) * Hkv + hq // G
+                parts = parts_per_row[r]
+                if sum(len(k) for k, _ in parts) == 0:
+                    assert np.all(g_o[n, l, hq] == 0) and g_lse[n, l, hq] == -np.inf
+                    continue
+                o, lse = o_decode.decode_partitions(q[n, l, hq], parts)
+                ob = numfmt.round_bf16(o)
+                np.testing.assert_allclose(g_o[n, l, hq], ob, rtol=1e-2, atol=2e-2)   # the bar
+                np.testing.assert_allclose(g_o[n, l, hq], o, rtol=8e-3, atol=1e-3)    # fp32 path
+                assert g_lse[n, l, hq] == pytest.approx(lse, rel=1e-5, abs=1e-5)
+
+
+@pytest.mark.parametrize("d,Hkv,Hq,stride", [(128, 2, 8, 700), (64, 1, 2, 300), (128, 4, 28, 513)])
+def test_decode_bf16_pool(d, Hkv, Hq, stride):
+    dims_t = (2, 2, Hkv, Hq, d)
+    p = synth.decode_pools(*dims_t, stride, seed=d + stride)
+    g_o, g_lse = _gpu_decode(dims_t, p, stride)
+    K, V, n_h = tl.f64(p["K"]), tl.f64(p["V"]), p["n_h"].numpy()
+    parts = [[(K[r, : n_h[r]], V[r, : n_h[r]])] for r in range(K.shape[0])]
+    _check_decode(g_o, g_lse, tl.f64(p["q"]), parts, dims_t)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_with_int8_partition(d):
+    dims_t = (2, 3, 2, 8, d)
+    p = synth.decode_pools(*dims_t, 400, stride_l=300, seed=3 + d)
+    g_o, g_lse = _gpu_decode(dims_t, p, 400, stride_l=300)
+    K, V, n_h = tl.f64(p["K"]), tl.f64(p["V"]), p["n_h"].numpy()
+    n_l = p["n_l"].numpy()
+    Kq, Vq = p["Kq"].numpy(), p["Vq"].numpy()
+    Ks, Vs = p["Ks"].numpy().view(np.uint16), p["Vs"].numpy().view(np.uint16)
+    parts = []
+    for r in range(K.shape[0]):
+        kl = o_quant.dequantize_rows(Kq[r, : n_l[r]], Ks[r, : n_l[r]])
+        vl = o_quant.dequantize_rows(Vq[r, : n_l[r]], Vs[r, : n_l[r]])
+        parts.append([(K[r, : n_h[r]], V[r, : n_h[r]]), (kl, vl)])
+    _check_decode(g_o, g_lse, tl.f64(p["q"]), parts, dims_t)
+
+
+def test_decode_paged_layout():
+    N, L, Hkv, Hq, d, ps = 3, 2, 2, 8, 128, 16
+    T_store, bps = 1024, 25                       # 64 stored pages, 25 referenced per sequence
+    dims_t = (N, L, Hkv, Hq, d)
+    p = synth.decode_pools(*dims_t, T_store, seed=21)
+    rows = N * L * Hkv
+    p["n_h"] = torch.full((rows,), bps * ps - 7, dtype=torch.int32)     # ragged last page
+    tbl = synth.page_table(N, T_store // ps, bps)
+    g_o, g_lse = _gpu_decode(dims_t, p, T_store, block_table=tbl, page_size=ps, bps=bps)
+    K, V = tl.f64(p["K"]), tl.f64(p["V"])
+    parts = []
+    for r in range(rows):
+        n = r // (L * Hkv)
+        t = np.arange(bps * ps - 7)
+        slot = tbl[n].numpy()[t // ps] * ps + t % ps
+        parts.append([(K[r, slot], V[r, slot])])
+    _check_decode(g_o, g_lse, tl.f64(p["q"]), parts, dims_t)
+
+
+@pytest.mark.parametrize("renumber_base,d", [(-1, 128), (0, 128), (100, 64)])
+def test_tiered_compaction(renumber_base, d):
+    from budgeted_retention_amd import kvc
+    N, L, Hkv, Hq, T, n_keep = 1, 2, 2, 8, 2000, 700
+    rows = N * L * Hkv
+    K, V, _ = synth.small_case(T, Hkv, Hq, d, 8, L, N, seed=40 + d)
+    kept, n, act = synth.kept_and_actions(rows, T, n_keep)
+    pos = np.tile(np.arange(T, dtype=np.int32) * 3 + 5, (rows, 1))      # non-trivial positions
+    dims = kvc.make_dims(N, L, Hkv, Hq, d, T)
+    cap = n_keep
+    dev = "cuda"
+    Ko = torch.zeros((rows, cap, d), dtype=torch.bfloat16, device=dev)
+    Vo = torch.zeros_like(Ko)
+    Kq = torch.zeros((rows, cap, d), dtype=torch.int8, device=dev)
+    Vq = torch.zeros_like(Kq)
+    Ks = torch.zeros((rows, cap), dtype=torch.int16, device=dev)
+    Vs = torch.zeros_like(Ks)
+    po = torch.full((rows, cap), -1, dtype=torch.int32, device=dev)
+    pq = torch.full((rows, cap), -1, dtype=torch.int32, device=dev)
+    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
+    nl = torch.zeros(rows, dtype=torch.int32, device=dev)
+    out = kvc.CompactOut(cap, Ko, Vo, po, nh, torch.from_numpy(act).to(dev), Kq, Vq, Ks, Vs, pq, nl)
+    kvc.kvc_compact_rerotate(dims, K.to(dev), V.to(dev), torch.from_numpy(pos).to(dev),
+                             torch.from_numpy(kept).to(dev), n_keep, torch.from_numpy(n).to(dev),
+                             renumber_base, 1e4, out)
+    torch.cuda.synchronize()
+    Kb, Vb = tl.bits(K).reshape(rows, T, d), tl.bits(V).reshape(rows, T, d)
+    for r in range(rows):
+        k = kept[r, : n[r]].astype(np.int64)
+        a = act[r, : n[r]]
+        oK, oV, op = o_compact.compact_row(Kb[r], Vb[r], pos[r], k, renumber_base, 1e4)
+        H, Lw = np.flatnonzero(a == 2), np.flatnonzero(a == 1)
+        assert nh[r].item() == H.size and nl[r].item() == Lw.size
+        gK = tl.bits(Ko[r])[: H.size]
+        np.testing.assert_array_equal(tl.bits(Vo[r])[: H.size], oV[H])
+        np.testing.assert_array_equal(po[r].cpu().numpy()[: H.size], op[H])
+        np.testing.assert_allclose(numfmt.bf16_bits_to_f64(gK), numfmt.bf16_bits_to_f64(oK[H]),
+                                   rtol=1e-2, atol=2e-2)
+        if renumber_base < 0:
+            np.testing.assert_array_equal(gK, oK[H])
+        # int8 tier: codes within +-1 and fp16 scales of the oracle's quantisation of
+        # the same (re-rotated) bf16 key and the value
+        if renumber_base < 0:
+            ck, sk = o_quant.quantize_rows(numfmt.bf16_bits_to_f64(oK[Lw]))
+            gck = Kq[r].cpu().numpy()[: Lw.size]
+            assert np.abs(gck.astype(int) - ck.astype(int)).max() <= 1
+            np.testing.assert_array_equal(Ks[r].cpu().numpy().view(np.uint16)[: Lw.size], sk)
+        cv, sv = o_quant.quantize_rows(numfmt.bf16_bits_to_f64(oV[Lw]))
+        gcv = Vq[r].cpu().numpy()[: Lw.size]
+        assert np.abs(gcv.astype(int) - cv.astype(int)).max() <= 1
+        np.testing.assert_array_equal(Vs[r].cpu().numpy().view(np.uint16)[: Lw.size], sv)
+        np.testing.assert_array_equal(pq[r].cpu().numpy()[: Lw.size], op[Lw])
