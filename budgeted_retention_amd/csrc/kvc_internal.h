@@ -57,4 +57,36 @@ __device__ __forceinline__ RowIdx split_row(int64_t r, int L, int Hkv) {
     return o;
 }
 
+// Where the window sits: query w is at position qbase + w and sees keys
+// j <= qbase + w; keys at or beyond kend are never read. lsel >= 0 restricts a
+// launch to one layer: local row rr = n*Hkv + h maps to global row
+// (n*L + lsel)*Hkv + h.
+struct WindowGeom {
+    int64_t qbase, kend;
+    int lsel;
+    __device__ __forceinline__ int64_t global_row(int64_t rr, int L, int Hkv) const {
+        if (lsel < 0) return rr;
+        return ((rr / Hkv) * L + lsel) * Hkv + rr % Hkv;
+    }
+};
+
+// Row of the 32x32 MFMA accumulator held in register i by a lane in half `hf`
+// (lanes 32..63 are half 1); the column is lane & 31.
+__device__ __forceinline__ int acc_row(int i, int hf) { return (i >> 2) * 8 + hf * 4 + (i & 3); }
+
+__device__ __forceinline__ bf16x8 load8(const uint16_t *p) {
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+
+// Enqueues the softmax statistics of a query window (score pass 1 + merge):
+// mm[rr][qr] = max + log2(sum) of the log2-domain logits of query row qr of
+// local row rr. `part` holds rows_local * window_chunks(kend) * QRP float2.
+int launch_window_stats(const kvc_dims *d, const uint16_t *K, const uint16_t *Q, int W, WindowGeom wg,
+                        int64_t rows_local, float2 *part, float *mm, hipStream_t s);
+int64_t window_chunks(int64_t kend);
+
 }  // namespace kvc

@@ -1,0 +1,525 @@
+// kvc_page_effect / kvc_page_retire: CommitKV page deletion effects.
+//
+// CommitKV §3.2: for one attention layer, query p of a window pays weight a_pi
+// to token i and outputs o_p. Deleting a page E and renormalising gives, by
+// Eq. 6, o_p^{\E} = (o_p - S_E) / (1 - alpha_E) with alpha_E = sum_{i in E} a_pi
+// and S_E = sum_{i in E} a_pi v_i, so
+//   o_p - o_p^{\E} = (S_E - alpha_E o_p) / (1 - alpha_E)
+//                  = sum_{i in E} a_pi (v_i - o_p) / (1 - alpha_E).
+// Eq. 7 takes ||.|| / ||o_p||, the max over the window's queries and over the
+// layer's query heads. The deletion vector is formed directly as
+// sum a_pi (v_i - o_p), never as a difference of two large norms.
+//
+// Stages, all for the chosen layer:
+//   1. window statistics (the score kernels' pass 1 + merge): per query row
+//      the log2-domain max and normaliser, so a_pi = exp2(logit*c - mm);
+//   2. pe_out: o_p for every query row (MFMA logits, a_pi staged in LDS,
+//      thread <-> (dimension pair, query stripe) accumulation over V in LDS);
+//   3. pe_effect: for every page, alpha and ||sum a (v - o)|| per query row,
+//      reduced to the max over rows and heads with an atomic max on the
+//      non-negative float bit pattern (order-independent, so deterministic);
+//   4. pe_retire (kvc_page_retire): CommitKV §3.3 Eq. 11 greedy joint test in
+//      the caller's candidate order, one workgroup per sequence; a candidate is
+//      accepted iff the effect of deleting it together with the pages already
+//      accepted stays within tau_joint.
+#include <cmath>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+static constexpr int PE_TILE = 64;      // keys per tile
+static constexpr int PE_THREADS = 128;  // two waves: 32 query rows x 64 keys of logits
+static constexpr int PE_PAGE_CHUNK = 4096;  // keys per pe_effect workgroup
+static constexpr int PR_THREADS = 256;
+static constexpr int PR_PMAX = 16;      // largest page the retire kernel takes
+
+struct PageGeom {
+    int64_t rows_local, n_chunks;
+    int G, QR, nb, QRP;
+};
+
+static PageGeom page_geom(const kvc_dims *d, int W, int64_t kend) {
+    PageGeom g;
+    g.G = d->n_q_heads / d->n_kv_heads;
+    g.rows_local = (int64_t)d->n_seq * d->n_kv_heads;
+    g.n_chunks = window_chunks(kend);
+    g.QR = g.G * W;
+    g.nb = (g.QR + 31) / 32;
+    g.QRP = g.nb * 32;
+    return g;
+}
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct PageWs {
+    float2 *part;
+    float *mm, *o, *accD, *alphaD;
+};
+
+static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base, PageWs *w) {
+    const PageGeom g = page_geom(d, W, kend);
+    const size_t s_part = al256((size_t)g.rows_local * g.n_chunks * g.QRP * sizeof(float2));
+    const size_t s_mm = al256((size_t)g.rows_local * g.QRP * sizeof(float));
+    const size_t s_o = al256((size_t)g.rows_local * g.QRP * d->head_dim * sizeof(float));
+    const size_t s_a = al256((size_t)g.rows_local * g.QRP * sizeof(float));
+    if (w) {
+        char *p = reinterpret_cast<char *>(base);
+        w->part = reinterpret_cast<float2 *>(p);
+        w->mm = reinterpret_cast<float *>(p + s_part);
+        w->o = reinterpret_cast<float *>(p + s_part + s_mm);
+        w->accD = reinterpret_cast<float *>(p + s_part + s_mm + s_o);
+        w->alphaD = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o);
+    }
+    return s_part + s_mm + 2 * s_o + s_a;
+}
+
+struct PeArgs {
+    const uint16_t *K, *V, *Q;
+    int64_t T;
+    int W, G, L, Hkv, Hq, lsel;
+    int64_t qbase, kend;
+    float c2;
+    const float *mm;
+    float *o;
+    int page_size, n_pages;
+    float *eff_rel, *eff_abs;
+};
+
+// Stages one 64-key tile: a_pi for the block's 32 query rows into sp[32][64]
+// (0 for invisible keys and padding rows) and V into sv[64][D] as fp32.
+template <int D>
+__device__ void pe_stage_tile(const PeArgs &a, const uint16_t *Kr, const uint16_t *Vr, const bf16x8 *qf,
+                              const float *mmq, const int64_t *qposq, int64_t j0, float (*sp)[PE_TILE + 1],
+                              float (*sv)[D]) {
+    constexpr int S = D / 16;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 31, hf = lane >> 5;
+    const int64_t jb = j0 + 32 * wave;
+    const int64_t key = jb + col;
+    bf16x8 kf[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) kf[s] = key < a.kend ? load8(Kr + (size_t)key * D + 16 * s + 8 * hf) : zero8();
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
+    // acc[i]: key jb + acc_row(i, hf), query row `col` of the block
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t k = jb + acc_row(i, hf);
+        const float p = (k <= qposq[0]) ? __builtin_amdgcn_exp2f(fmaf(acc[i], a.c2, -mmq[0])) : 0.f;
+        sp[col][32 * wave + acc_row(i, hf)] = p;
+    }
+    for (int e = tid; e < PE_TILE * D / 2; e += PE_THREADS) {
+        const int k = e / (D / 2), c = 2 * (e % (D / 2));
+        float v0 = 0.f, v1 = 0.f;
+        if (j0 + k < a.kend) {
+            const uint32_t u = *reinterpret_cast<const uint32_t *>(Vr + (size_t)(j0 + k) * D + c);
+            v0 = bf16_to_f32((uint16_t)(u & 0xFFFF));
+            v1 = bf16_to_f32((uint16_t)(u >> 16));
+        }
+        sv[k][c] = v0;
+        sv[k][c + 1] = v1;
+    }
+}
+
+// Per-lane window data of query row `col` of block `b`: Q fragments, mm, position.
+template <int D>
+__device__ void pe_load_queries(const PeArgs &a, int64_t rr, int b, bf16x8 *qf, float *mmq, int64_t *qposq,
+                                const uint16_t **Kr, const uint16_t **Vr) {
+    constexpr int S = D / 16;
+    const int lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+    const int64_t gr = ((rr / a.Hkv) * a.L + a.lsel) * a.Hkv + rr % a.Hkv;
+    const RowIdx ri = split_row(gr, a.L, a.Hkv);
+    *Kr = a.K + (size_t)gr * a.T * D;
+    *Vr = a.V + (size_t)gr * a.T * D;
+    const uint16_t *Qg = a.Q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * a.G) * a.W * D;
+    const int qrow = b * 32 + col;
+    const int QR = a.G * a.W;
+#pragma unroll
+    for (int s = 0; s < S; ++s) qf[s] = qrow < QR ? load8(Qg + (size_t)qrow * D + 16 * s + 8 * hf) : zero8();
+    const int QRP = ((QR + 31) / 32) * 32;
+    mmq[0] = a.mm[rr * QRP + qrow];
+    qposq[0] = qrow < QR ? a.qbase + qrow % a.W : -1;
+}
+
+template <int D>
+__global__ void __launch_bounds__(PE_THREADS) pe_out(PeArgs a) {
+    constexpr int DP = D / 2, STRIPES = PE_THREADS / DP, QPS = 32 / STRIPES;
+    __shared__ float sp[32][PE_TILE + 1];
+    __shared__ float sv[PE_TILE][D];
+    const int nb = (a.G * a.W + 31) / 32;
+    const int64_t rr = blockIdx.x / nb;
+    const int b = blockIdx.x % nb;
+    bf16x8 qf[D / 16];
+    float mmq[1];
+    int64_t qposq[1];
+    const uint16_t *Kr, *Vr;
+    pe_load_queries<D>(a, rr, b, qf, mmq, qposq, &Kr, &Vr);
+    const int tid = threadIdx.x, dp = tid % DP, stripe = tid / DP;
+    float acc0[QPS], acc1[QPS];
+#pragma unroll
+    for (int q = 0; q < QPS; ++q) acc0[q] = acc1[q] = 0.f;
+    for (int64_t j0 = 0; j0 < a.kend; j0 += PE_TILE) {
+        pe_stage_tile<D>(a, Kr, Vr, qf, mmq, qposq, j0, sp, sv);
+        __syncthreads();
+        for (int k = 0; k < PE_TILE; ++k) {
+            const float v0 = sv[k][2 * dp], v1 = sv[k][2 * dp + 1];
+#pragma unroll
+            for (int q = 0; q < QPS; ++q) {
+                const float p = sp[stripe * QPS + q][k];
+                acc0[q] = fmaf(p, v0, acc0[q]);
+                acc1[q] = fmaf(p, v1, acc1[q]);
+            }
+        }
+        __syncthreads();
+    }
+    const int QRP = nb * 32;
+#pragma unroll
+    for (int q = 0; q < QPS; ++q) {
+        float *o = a.o + ((size_t)rr * QRP + b * 32 + stripe * QPS + q) * D;
+        o[2 * dp] = acc0[q];
+        o[2 * dp + 1] = acc1[q];
+    }
+}
+
+__device__ __forceinline__ void atomic_max_nonneg(float *addr, float v) {
+    atomicMax(reinterpret_cast<unsigned int *>(addr), __float_as_uint(v));
+}
+
+template <int D>
+__global__ void __launch_bounds__(PE_THREADS) pe_effect(PeArgs a, int chunks_per_row) {
+    constexpr int DP = D / 2, STRIPES = PE_THREADS / DP, QPS = 32 / STRIPES;
+    __shared__ float sp[32][PE_TILE + 1];
+    __shared__ float sv[PE_TILE][D];
+    __shared__ float s_alpha[32][PE_TILE];   // per query row and page of the tile (<= 64 pages)
+    __shared__ float s_best[2][STRIPES][PE_TILE];
+    const int nb = (a.G * a.W + 31) / 32;
+    const int64_t rr = blockIdx.x / (nb * chunks_per_row);
+    const int b = (int)((blockIdx.x / chunks_per_row) % nb);
+    const int pc = (int)(blockIdx.x % chunks_per_row);
+    bf16x8 qf[D / 16];
+    float mmq[1];
+    int64_t qposq[1];
+    const uint16_t *Kr, *Vr;
+    pe_load_queries<D>(a, rr, b, qf, mmq, qposq, &Kr, &Vr);
+    const int tid = threadIdx.x, dp = tid % DP, stripe = tid / DP;
+    const int QR = a.G * a.W, QRP = nb * 32;
+    const int ps = a.page_size, ppt = PE_TILE / ps;  // pages per tile
+    const int64_t n_tok = (int64_t)a.n_pages * ps;
+    const int n_seq_idx = (int)(rr / a.Hkv);
+
+    // o and ||o|| for this thread's query rows
+    float o0[QPS], o1[QPS], onorm[QPS];
+#pragma unroll
+    for (int q = 0; q < QPS; ++q) {
+        const float *o = a.o + ((size_t)rr * QRP + b * 32 + stripe * QPS + q) * D;
+        o0[q] = o[2 * dp];
+        o1[q] = o[2 * dp + 1];
+        float n2 = o0[q] * o0[q] + o1[q] * o1[q];
+        for (int m = DP / 2; m >= 1; m >>= 1) n2 += __shfl_xor(n2, m);
+        onorm[q] = sqrtf(n2);
+    }
+    const int64_t t_begin = (int64_t)pc * PE_PAGE_CHUNK;
+    const int64_t t_end = t_begin + PE_PAGE_CHUNK < n_tok ? t_begin + PE_PAGE_CHUNK : n_tok;
+    for (int64_t j0 = t_begin; j0 < t_end; j0 += PE_TILE) {
+        pe_stage_tile<D>(a, Kr, Vr, qf, mmq, qposq, j0, sp, sv);
+        __syncthreads();
+        for (int e = tid; e < 32 * ppt; e += PE_THREADS) {
+            const int q = e / ppt, pg = e % ppt;
+            float al = 0.f;
+            for (int k = 0; k < ps; ++k) al += sp[q][pg * ps + k];
+            s_alpha[q][pg] = al;
+        }
+        __syncthreads();
+        for (int pg = 0; pg < ppt; ++pg) {
+            float best_rel = 0.f, best_abs = 0.f;
+#pragma unroll
+            for (int q = 0; q < QPS; ++q) {
+                const int ql = stripe * QPS + q;
+                float t0 = 0.f, t1 = 0.f;
+                for (int k = 0; k < ps; ++k) {
+                    const float p = sp[ql][pg * ps + k];
+                    t0 = fmaf(p, sv[pg * ps + k][2 * dp] - o0[q], t0);
+                    t1 = fmaf(p, sv[pg * ps + k][2 * dp + 1] - o1[q], t1);
+                }
+                float n2 = t0 * t0 + t1 * t1;
+                for (int m = DP / 2; m >= 1; m >>= 1) n2 += __shfl_xor(n2, m);
+                if (b * 32 + ql < QR) {
+                    const float al = s_alpha[ql][pg];
+                    const float num = sqrtf(n2);
+                    const float den = 1.f - al;
+                    float ab = den > 0.f ? num / den : INFINITY;
+                    float rel = onorm[q] > 0.f ? ab / onorm[q] : (num > 0.f ? INFINITY : 0.f);
+                    if (!(num > 0.f)) ab = rel = 0.f;
+                    best_rel = fmaxf(best_rel, rel);
+                    best_abs = fmaxf(best_abs, ab);
+                }
+            }
+            if (dp == 0) {
+                s_best[0][stripe][pg] = best_rel;
+                s_best[1][stripe][pg] = best_abs;
+            }
+        }
+        __syncthreads();
+        for (int pg = tid; pg < ppt; pg += PE_THREADS) {
+            const int64_t page = (j0 / ps) + pg;
+            if (page >= a.n_pages) continue;
+            float br = 0.f, ba = 0.f;
+            for (int s = 0; s < STRIPES; ++s) {
+                br = fmaxf(br, s_best[0][s][pg]);
+                ba = fmaxf(ba, s_best[1][s][pg]);
+            }
+            atomic_max_nonneg(a.eff_rel + (size_t)n_seq_idx * a.n_pages + page, br);
+            if (a.eff_abs) atomic_max_nonneg(a.eff_abs + (size_t)n_seq_idx * a.n_pages + page, ba);
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void fill_f32(float *p, int64_t n, float v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// Greedy joint retirement, one workgroup per sequence. Thread <-> query row of
+// one KV head at a time. accD[rr][q][d] holds sum over accepted pages of
+// sum a (v - o); alphaD[rr][q] the accepted pages' summed weight.
+template <int D>
+__global__ void __launch_bounds__(PR_THREADS) pe_retire(PeArgs a, const int32_t *order, int n_cand,
+                                                        float tau_joint, float *accD, float *alphaD,
+                                                        uint8_t *accepted, float *joint_rel) {
+    __shared__ float s_k[PR_PMAX][D];
+    __shared__ float s_v[PR_PMAX][D];
+    __shared__ float s_red[PR_THREADS / 64];
+    __shared__ int s_accept;
+    const int n = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
+    const int ps = a.page_size;
+    // clear the running sums of this sequence's rows
+    for (int h = 0; h < a.Hkv; ++h) {
+        const int64_t rr = (int64_t)n * a.Hkv + h;
+        for (int i = tid; i < QRP * D; i += PR_THREADS) accD[(size_t)rr * QRP * D + i] = 0.f;
+        for (int i = tid; i < QRP; i += PR_THREADS) alphaD[(size_t)rr * QRP + i] = 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < n_cand; ++c) {
+        const int page = order[(size_t)n * n_cand + c];
+        if (page < 0 || page >= a.n_pages) {
+            if (tid == 0) {
+                accepted[(size_t)n * n_cand + c] = 0;
+                if (joint_rel) joint_rel[(size_t)n * n_cand + c] = -1.f;
+            }
+            continue;
+        }
+        float worst = 0.f;
+        for (int pass = 0; pass < 2; ++pass) {  // pass 0: evaluate; pass 1: commit if accepted
+            if (pass == 1 && !s_accept) break;
+            for (int h = 0; h < a.Hkv; ++h) {
+                const int64_t rr = (int64_t)n * a.Hkv + h;
+                const int64_t gr = ((int64_t)n * a.L + a.lsel) * a.Hkv + h;
+                const uint16_t *Kr = a.K + (size_t)gr * a.T * D;
+                const uint16_t *Vr = a.V + (size_t)gr * a.T * D;
+                __syncthreads();
+                for (int e = tid; e < ps * D; e += PR_THREADS) {
+                    const int k = e / D, cc = e % D;
+                    const int64_t t = (int64_t)page * ps + k;
+                    s_k[k][cc] = bf16_to_f32(Kr[(size_t)t * D + cc]);
+                    s_v[k][cc] = bf16_to_f32(Vr[(size_t)t * D + cc]);
+                }
+                __syncthreads();
+                const RowIdx ri = split_row(gr, a.L, a.Hkv);
+                const uint16_t *Qg = a.Q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * a.G) * a.W * D;
+                for (int q = tid; q < QR; q += PR_THREADS) {
+                    const int64_t qpos = a.qbase + q % a.W;
+                    const float mq = a.mm[rr * QRP + q];
+                    float p[PR_PMAX];
+#pragma unroll
+                    for (int k = 0; k < PR_PMAX; ++k) p[k] = 0.f;
+                    for (int cc = 0; cc < D; ++cc) {
+                        const float qv = bf16_to_f32(Qg[(size_t)q * D + cc]);
+#pragma unroll
+                        for (int k = 0; k < PR_PMAX; ++k)
+                            if (k < ps) p[k] = fmaf(qv, s_k[k][cc], p[k]);
+                    }
+                    float al = 0.f;
+#pragma unroll
+                    for (int k = 0; k < PR_PMAX; ++k) {
+                        const int64_t t = (int64_t)page * ps + k;
+                        p[k] = (k < ps && t <= qpos) ? __builtin_amdgcn_exp2f(fmaf(p[k], a.c2, -mq)) : 0.f;
+                        al += p[k];
+                    }
+                    const float *o = a.o + ((size_t)rr * QRP + q) * D;
+                    float *acc = accD + ((size_t)rr * QRP + q) * D;
+                    float n2 = 0.f, o2 = 0.f;
+                    for (int cc = 0; cc < D; ++cc) {
+                        float t = 0.f;
+#pragma unroll
+                        for (int k = 0; k < PR_PMAX; ++k)
+                            if (k < ps) t = fmaf(p[k], s_v[k][cc] - o[cc], t);
+                        const float j = acc[cc] + t;
+                        if (pass == 1) acc[cc] = j;
+                        n2 = fmaf(j, j, n2);
+                        o2 = fmaf(o[cc], o[cc], o2);
+                    }
+                    const float alj = alphaD[rr * QRP + q] + al;
+                    if (pass == 1) alphaD[rr * QRP + q] = alj;
+                    const float num = sqrtf(n2), onorm = sqrtf(o2);
+                    float rel = 0.f;
+                    if (num > 0.f) rel = (1.f - alj > 0.f && onorm > 0.f) ? num / ((1.f - alj) * onorm) : INFINITY;
+                    worst = fmaxf(worst, rel);
+                }
+            }
+            if (pass == 0) {
+                // block max of `worst`
+                float v = worst;
+                for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+                if ((tid & 63) == 0) s_red[tid >> 6] = v;
+                __syncthreads();
+                if (tid == 0) {
+                    float m = s_red[0];
+                    for (int w = 1; w < PR_THREADS / 64; ++w) m = fmaxf(m, s_red[w]);
+                    s_accept = m <= tau_joint;
+                    accepted[(size_t)n * n_cand + c] = (uint8_t)s_accept;
+                    if (joint_rel) joint_rel[(size_t)n * n_cand + c] = m;
+                }
+                __syncthreads();
+            }
+        }
+        __syncthreads();
+    }
+}
+
+static int pe_common_checks(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
+                            const uint16_t *Q, int32_t W, int64_t q_first, int32_t page_size,
+                            int32_t n_pages, const char *who) {
+    int st = check_dims(dims, who);
+    if (st != KVC_OK) return st;
+    if (!K || !V || !Q) return fail(KVC_ERR_ARG, "%s: NULL tensor pointer", who);
+    if (layer < 0 || layer >= dims->n_layers)
+        return fail(KVC_ERR_ARG, "%s: layer %d outside [0, %d)", who, layer, dims->n_layers);
+    if (W <= 0 || q_first < 0 || q_first + W > dims->n_tokens)
+        return fail(KVC_ERR_ARG, "%s: window [%lld, %lld) outside the %lld cached tokens", who,
+                    (long long)q_first, (long long)(q_first + W), (long long)dims->n_tokens);
+    const int G = dims->n_q_heads / dims->n_kv_heads;
+    if (G * W > 256) return fail(KVC_ERR_UNSUPPORTED, "%s: W*G = %d exceeds 256", who, G * W);
+    if (page_size <= 0 || PE_TILE % page_size)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: page_size %d must divide %d", who, page_size, PE_TILE);
+    if (n_pages <= 0 || (int64_t)n_pages * page_size > dims->n_tokens)
+        return fail(KVC_ERR_ARG, "%s: %d pages of %d tokens exceed the cache", who, n_pages, page_size);
+    return KVC_OK;
+}
+
+static PeArgs pe_args(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
+                      const uint16_t *Q, int32_t W, int64_t q_first, int32_t page_size, int32_t n_pages,
+                      const PageWs &w) {
+    PeArgs a;
+    a.K = K;
+    a.V = V;
+    a.Q = Q;
+    a.T = dims->n_tokens;
+    a.W = W;
+    a.G = dims->n_q_heads / dims->n_kv_heads;
+    a.L = dims->n_layers;
+    a.Hkv = dims->n_kv_heads;
+    a.Hq = dims->n_q_heads;
+    a.lsel = layer;
+    a.qbase = q_first;
+    a.kend = q_first + W;
+    a.c2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
+    a.mm = w.mm;
+    a.o = w.o;
+    a.page_size = page_size;
+    a.n_pages = n_pages;
+    a.eff_rel = a.eff_abs = nullptr;
+    return a;
+}
+
+// Stages 1 and 2 (statistics and outputs), shared by both entry points.
+static int pe_prepare(const kvc_dims *dims, const PeArgs &a, const PageWs &w, hipStream_t s) {
+    const PageGeom g = page_geom(dims, a.W, a.kend);
+    WindowGeom wg{a.qbase, a.kend, a.lsel};
+    int st = launch_window_stats(dims, a.K, a.Q, a.W, wg, g.rows_local, w.part, w.mm, s);
+    if (st != KVC_OK) return st;
+    const int64_t blocks = g.rows_local * g.nb;
+    if (dims->head_dim == 128)
+        pe_out<128><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a);
+    else
+        pe_out<64><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a);
+    return check_launch("page effect outputs");
+}
+
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int64_t q_first) {
+    if (check_dims(dims, "kvc_page_workspace_bytes") != KVC_OK) return 0;
+    if (W <= 0 || q_first < 0) {
+        fail(KVC_ERR_ARG, "kvc_page_workspace_bytes: bad window");
+        return 0;
+    }
+    return page_ws_layout(dims, W, q_first + W, nullptr, nullptr);
+}
+
+extern "C" int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
+                               const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
+                               int32_t n_pages, float *effect_rel, float *effect_abs, void *ws,
+                               size_t ws_bytes, void *stream) {
+    int st = pe_common_checks(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, "kvc_page_effect");
+    if (st != KVC_OK) return st;
+    if (!effect_rel) return fail(KVC_ERR_ARG, "kvc_page_effect: effect_rel is NULL");
+    const size_t need = page_ws_layout(dims, W, q_first + W, nullptr, nullptr);
+    if (!ws || ws_bytes < need)
+        return fail(KVC_ERR_WORKSPACE, "kvc_page_effect: workspace %zu < %zu bytes", ws_bytes, need);
+    PageWs w;
+    page_ws_layout(dims, W, q_first + W, ws, &w);
+    PeArgs a = pe_args(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, w);
+    a.eff_rel = effect_rel;
+    a.eff_abs = effect_abs;
+    hipStream_t s = as_stream(stream);
+    const int64_t n_out = (int64_t)dims->n_seq * n_pages;
+    fill_f32<<<dim3(256), dim3(256), 0, s>>>(effect_rel, n_out, 0.f);
+    if (effect_abs) fill_f32<<<dim3(256), dim3(256), 0, s>>>(effect_abs, n_out, 0.f);
+    if ((st = check_launch("kvc_page_effect clear")) != KVC_OK) return st;
+    if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
+    const PageGeom g = page_geom(dims, W, q_first + W);
+    const int64_t n_tok = (int64_t)n_pages * page_size;
+    const int cpr = (int)((n_tok + PE_PAGE_CHUNK - 1) / PE_PAGE_CHUNK);
+    const int64_t blocks = g.rows_local * g.nb * cpr;
+    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_effect: grid too large");
+    if (dims->head_dim == 128)
+        pe_effect<128><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a, cpr);
+    else
+        pe_effect<64><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a, cpr);
+    return check_launch("kvc_page_effect");
+}
+
+extern "C" int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
+                               const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
+                               int32_t n_pages, const int32_t *order, int32_t n_cand, float tau_joint,
+                               uint8_t *accepted, float *joint_rel, void *ws, size_t ws_bytes,
+                               void *stream) {
+    int st = pe_common_checks(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, "kvc_page_retire");
+    if (st != KVC_OK) return st;
+    if (!order || !accepted || n_cand <= 0)
+        return fail(KVC_ERR_ARG, "kvc_page_retire: order/accepted missing or n_cand <= 0");
+    if (page_size > PR_PMAX)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_page_retire: page_size %d above %d", page_size, PR_PMAX);
+    const size_t need = page_ws_layout(dims, W, q_first + W, nullptr, nullptr);
+    if (!ws || ws_bytes < need)
+        return fail(KVC_ERR_WORKSPACE, "kvc_page_retire: workspace %zu < %zu bytes", ws_bytes, need);
+    PageWs w;
+    page_ws_layout(dims, W, q_first + W, ws, &w);
+    PeArgs a = pe_args(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, w);
+    hipStream_t s = as_stream(stream);
+    if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
+    if (dims->head_dim == 128)
+        pe_retire<128><<<dim3(dims->n_seq), dim3(PR_THREADS), 0, s>>>(a, order, n_cand, tau_joint, w.accD,
+                                                                       w.alphaD, accepted, joint_rel);
+    else
+        pe_retire<64><<<dim3(dims->n_seq), dim3(PR_THREADS), 0, s>>>(a, order, n_cand, tau_joint, w.accD,
+                                                                      w.alphaD, accepted, joint_rel);
+    return check_launch("kvc_page_retire");
+}

@@ -57,42 +57,33 @@ size_t score_workspace_bytes(const kvc_dims *d, int32_t W) {
     return align256(part) + align256(mm);
 }
 
-// Row of the 32x32 MFMA accumulator held in register i by a lane in half `hf`
-// (lanes 32..63 are half 1); the column is lane & 31.
-__device__ __forceinline__ int acc_row(int i, int hf) { return (i >> 2) * 8 + hf * 4 + (i & 3); }
-
-__device__ __forceinline__ bf16x8 load8(const uint16_t *p) {
-    uint4 u = *reinterpret_cast<const uint4 *>(p);
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
-
 template <int D>
 __global__ void __launch_bounds__(512) score_pass1(const uint16_t *__restrict__ K,
                                                    const uint16_t *__restrict__ Q, int64_t T, int W,
                                                    int G, int L, int Hkv, int Hq, int64_t n_chunks,
-                                                   float c2, float2 *__restrict__ part) {
+                                                   float c2, WindowGeom wg, float2 *__restrict__ part) {
     constexpr int S = D / 16;
     const int QR = G * W;
     const int QRP = (blockDim.x >> 6) * 32;
-    const int64_t r = blockIdx.x / n_chunks;
+    const int64_t r = blockIdx.x / n_chunks;  // local row
     const int64_t chunk = blockIdx.x % n_chunks;
-    const RowIdx ri = split_row(r, L, Hkv);
-    const uint16_t *Kr = K + (size_t)r * T * D;
+    const int64_t gr = wg.global_row(r, L, Hkv);
+    const RowIdx ri = split_row(gr, L, Hkv);
+    const uint16_t *Kr = K + (size_t)gr * T * D;
     const uint16_t *Qg = Q + ((size_t)(ri.n * L + ri.l) * Hq + (size_t)ri.h * G) * W * D;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 31, hf = lane >> 5;
+    const int64_t qbase = wg.qbase;
 
     const int qrow = wave * 32 + col;
     bf16x8 qf[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) qf[s] = qrow < QR ? load8(Qg + (size_t)qrow * D + 16 * s + 8 * hf) : zero8();
-    const int64_t qpos = qrow < QR ? T - W + qrow % W : -1;
+    const int64_t qpos = qrow < QR ? qbase + qrow % W : -1;
 
     float m = -INFINITY, l = 0.f;
     const int64_t k0 = chunk * SCORE_CHUNK;
-    const int64_t k1 = k0 + SCORE_CHUNK < T ? k0 + SCORE_CHUNK : T;
+    const int64_t k1 = k0 + SCORE_CHUNK < wg.kend ? k0 + SCORE_CHUNK : wg.kend;
     for (int64_t j0 = k0; j0 < k1; j0 += 32) {
         const int64_t key = j0 + col;
         bf16x8 kf[S];
@@ -102,7 +93,7 @@ __global__ void __launch_bounds__(512) score_pass1(const uint16_t *__restrict__ 
 #pragma unroll
         for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
         // acc[i] = logit of key j0 + acc_row(i, hf) for query row `qrow`
-        const bool all_vis = j0 + 31 <= T - W;  // every key of the tile is visible to every query
+        const bool all_vis = j0 + 31 <= qbase;  // every key of the tile is visible to every query
         float tmax = -INFINITY;
         if (all_vis) {
 #pragma unroll
@@ -163,6 +154,7 @@ __global__ void __launch_bounds__(512) score_pass2(const uint16_t *__restrict__ 
                                                    int G, int L, int Hkv, int Hq, int64_t n_chunks,
                                                    float c2, const float *__restrict__ mm,
                                                    float *__restrict__ scores) {
+    const WindowGeom wg{T - W, T, -1};
     constexpr int S = D / 16;
     extern __shared__ float red[];  // [nb][SCORE_CHUNK]
     const int QR = G * W;
@@ -170,7 +162,7 @@ __global__ void __launch_bounds__(512) score_pass2(const uint16_t *__restrict__ 
     const int QRP = nb * 32;
     const int64_t r = blockIdx.x / n_chunks;
     const int64_t chunk = blockIdx.x % n_chunks;
-    const RowIdx ri = split_row(r, L, Hkv);
+    const RowIdx ri = split_row(wg.global_row(r, L, Hkv), L, Hkv);
     const uint16_t *Kr = K + (size_t)r * T * D;
     const uint16_t *Qg = Q + ((size_t)(ri.n * L + ri.l) * Hq + (size_t)ri.h * G) * W * D;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -190,7 +182,7 @@ __global__ void __launch_bounds__(512) score_pass2(const uint16_t *__restrict__ 
     for (int i = 0; i < 16; ++i) {
         const int qr = wave * 32 + acc_row(i, hf);
         mmi[i] = mm[r * QRP + qr];
-        qpos[i] = qr < QR ? T - W + qr % W : -1;
+        qpos[i] = qr < QR ? wg.qbase + qr % W : -1;
     }
 
     const int64_t k0 = chunk * SCORE_CHUNK;
@@ -205,7 +197,7 @@ __global__ void __launch_bounds__(512) score_pass2(const uint16_t *__restrict__ 
         for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
         // acc[i] = logit of query row wave*32 + acc_row(i, hf) for key `key`
         float p = 0.f;
-        if (j0 + 31 <= T - W) {
+        if (j0 + 31 <= wg.qbase) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) p += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mmi[i]));
         } else {
@@ -223,6 +215,30 @@ __global__ void __launch_bounds__(512) score_pass2(const uint16_t *__restrict__ 
         scores[(size_t)r * T + k0 + t] = s;
     }
 }
+
+int launch_window_stats(const kvc_dims *d, const uint16_t *K, const uint16_t *Q, int W, WindowGeom wg,
+                        int64_t rows_local, float2 *part, float *mm, hipStream_t s) {
+    const int G = d->n_q_heads / d->n_kv_heads;
+    const int QR = G * W, nb = (QR + 31) / 32, QRP = nb * 32;
+    const int64_t n_chunks = window_chunks(wg.kend);
+    const int64_t blocks = rows_local * n_chunks;
+    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "window stats: grid too large");
+    const float c2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
+    const int L = d->n_layers, Hkv = d->n_kv_heads, Hq = d->n_q_heads;
+    const int64_t T = d->n_tokens;
+    if (d->head_dim == 128)
+        score_pass1<128><<<dim3((unsigned)blocks), dim3(nb * 64), 0, s>>>(K, Q, T, W, G, L, Hkv, Hq, n_chunks,
+                                                                        c2, wg, part);
+    else
+        score_pass1<64><<<dim3((unsigned)blocks), dim3(nb * 64), 0, s>>>(K, Q, T, W, G, L, Hkv, Hq, n_chunks,
+                                                                       c2, wg, part);
+    int st = check_launch("window stats pass 1");
+    if (st != KVC_OK) return st;
+    score_merge<<<dim3((unsigned)rows_local), dim3(QRP), 0, s>>>(part, n_chunks, QR, QRP, mm);
+    return check_launch("window stats merge");
+}
+
+int64_t window_chunks(int64_t kend) { return (kend + SCORE_CHUNK - 1) / SCORE_CHUNK; }
 
 }  // namespace kvc
 
@@ -254,12 +270,13 @@ extern "C" int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t
     const size_t red_bytes = (size_t)g.nb * SCORE_CHUNK * sizeof(float);
     const int L = dims->n_layers, Hkv = dims->n_kv_heads, Hq = dims->n_q_heads;
     const int64_t T = dims->n_tokens;
+    const WindowGeom wgeo{T - W, T, -1};
     if (dims->head_dim == 128) {
         score_pass1<128><<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(K, Q_obs, T, W, G, L, Hkv, Hq,
-                                                                          g.n_chunks, c2, part);
+                                                                          g.n_chunks, c2, wgeo, part);
     } else {
         score_pass1<64><<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(K, Q_obs, T, W, G, L, Hkv, Hq,
-                                                                         g.n_chunks, c2, part);
+                                                                         g.n_chunks, c2, wgeo, part);
     }
     if ((st = check_launch("kvc_score pass 1")) != KVC_OK) return st;
     score_merge<<<dim3((unsigned)g.rows), dim3(g.QRP), 0, s>>>(part, g.n_chunks, g.QR, g.QRP, mm);

@@ -165,3 +165,34 @@ def kvc_decode_attn(dims, q, K, V, n_h, stride_h, o, ws, lse=None, block_table=N
         _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     return _lib.check(st)
+
+
+def kvc_page_workspace_bytes(dims, W, q_first):
+    return _lib.load().kvc_page_workspace_bytes(ctypes.byref(dims), W, q_first)
+
+
+def page_workspace(dims, W, q_first, device="cuda"):
+    return torch.empty(max(1, kvc_page_workspace_bytes(dims, W, q_first)), dtype=torch.uint8,
+                       device=device)
+
+
+def kvc_page_effect(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, effect_rel, ws,
+                    effect_abs=None, stream=None):
+    st = _lib.load().kvc_page_effect(
+        ctypes.byref(dims), layer, _ptr(K, torch.bfloat16, "K"), _ptr(V, torch.bfloat16, "V"),
+        _ptr(Q_win, torch.bfloat16, "Q_win"), W, q_first, page_size, n_pages,
+        _ptr(effect_rel, torch.float32, "effect_rel"), _ptr(effect_abs, torch.float32, "effect_abs"),
+        _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    return _lib.check(st)
+
+
+def kvc_page_retire(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, order, tau_joint,
+                    accepted, ws, joint_rel=None, stream=None):
+    n_cand = order.shape[-1]
+    st = _lib.load().kvc_page_retire(
+        ctypes.byref(dims), layer, _ptr(K, torch.bfloat16, "K"), _ptr(V, torch.bfloat16, "V"),
+        _ptr(Q_win, torch.bfloat16, "Q_win"), W, q_first, page_size, n_pages,
+        _ptr(order, torch.int32, "order"), n_cand, float(tau_joint), _ptr(accepted, torch.uint8, "accepted"),
+        _ptr(joint_rel, torch.float32, "joint_rel"), _ptr(ws, None, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    return _lib.check(st)

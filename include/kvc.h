@@ -229,6 +229,52 @@ int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const uint16_t *K, 
                     const uint16_t *Ks, const uint16_t *Vs, const int32_t *n_l, int64_t stride_l,
                     uint16_t *o, float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/* Device workspace (bytes) of kvc_page_effect / kvc_page_retire for a window
+ * of W queries starting at position q_first. */
+size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int64_t q_first);
+
+/*
+ * CommitKV page deletion effect (CommitKV §3.2, Eq. 6 renormalisation and
+ * Eq. 7 relative change; the window of Eq. 5).
+ *
+ * For the chosen layer, window query w of query head hq sits at position
+ * q_first + w and attends to the cached tokens j <= q_first + w (attention
+ * weights a_j, output o). For every page E = tokens [e*page_size,
+ * (e+1)*page_size), e < n_pages, and every sequence n:
+ *   effect_rel[n][e] = max over the layer's query heads and window queries of
+ *                      ||o - o^{\E}|| / ||o||,  o - o^{\E} = sum_{j in E} a_j (v_j - o) / (1 - alpha_E)
+ *   effect_abs[n][e] = the same maximum of ||o - o^{\E}||
+ * A page whose deletion leaves nothing visible (alpha_E = 1) gets +inf; a
+ * page no query sees gets 0.
+ *
+ *   K, V      bf16 [N][L][Hkv][T][d];  Q_win bf16 [N][L][Hq][W][d] (rotated)
+ *   layer     0 <= layer < L;  q_first + W <= T;  W*G <= 256
+ *   page_size divides 64;  n_pages*page_size <= T
+ *   effect_rel fp32 [N][n_pages];  effect_abs fp32 [N][n_pages] or NULL
+ *   ws        kvc_page_workspace_bytes(dims, W, q_first) bytes
+ */
+int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
+                    const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
+                    int32_t n_pages, float *effect_rel, float *effect_abs, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/*
+ * CommitKV greedy joint retirement (CommitKV §3.3, Eq. 11). Per sequence n,
+ * candidates order[n][0..n_cand) (page indices; -1 = no candidate) are
+ * examined in that order; candidate E is accepted iff the effect, in the
+ * sense of kvc_page_effect, of deleting E together with every page accepted
+ * before it is <= tau_joint. The joint deletion treats all their tokens as
+ * one set (Eq. 6 with the combined weights).
+ *
+ *   accepted   u8 [N][n_cand] 1 = retired;  joint_rel fp32 [N][n_cand] or NULL
+ *              (the joint effect tested for each candidate, -1 for none)
+ *   Other arguments as kvc_page_effect; page_size <= 16.
+ */
+int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
+                    const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
+                    int32_t n_pages, const int32_t *order, int32_t n_cand, float tau_joint,
+                    uint8_t *accepted, float *joint_rel, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
