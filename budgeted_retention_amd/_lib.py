@@ -43,10 +43,16 @@ class KvcPolicy(ctypes.Structure):
 class KvcCompactOut(ctypes.Structure):
     _fields_ = [
         ("action", c_void_p), ("out_stride", c_int32), ("reserved", c_int32),
+        ("h_base", c_void_p), ("l_base", c_void_p),
         ("K_out", c_void_p), ("V_out", c_void_p), ("pos_out", c_void_p), ("n_h", c_void_p),
         ("Kq", c_void_p), ("Vq", c_void_p), ("Ks", c_void_p), ("Vs", c_void_p),
         ("pos_q", c_void_p), ("n_l", c_void_p),
     ]
+
+
+class KvcPaskTable(ctypes.Structure):
+    _fields_ = [("n_tags", c_int32), ("n_groups", c_int32), ("a0", c_void_p), ("amin", c_void_p),
+                ("prio", c_void_p), ("critical", c_void_p)]
 
 
 # name -> (restype, argtypes); mirrors include/kvc.h
@@ -76,6 +82,12 @@ PROTOTYPES = {
                                        c_int32, c_int64, c_int32, c_int32, c_void_p, c_int32,
                                        ctypes.c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
+    "kvc_host_pask_costs": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p]),
+    "kvc_host_pask_control": (ctypes.c_int, [ctypes.POINTER(KvcPaskTable), c_void_p, c_double, c_double,
+                                             c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "kvc_host_commit_candidates": (ctypes.c_int, [c_void_p, c_void_p, c_int32, ctypes.c_float,
+                                                  ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                                  c_int32, c_void_p, c_void_p, c_void_p]),
 }
 
 _lib = None

@@ -1,6 +1,6 @@
 """Builds libkvc.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-Every HIP source under csrc/ is compiled with hipcc for gfx950 and linked
+Every source under csrc/ (HIP kernels and host C++) is compiled with hipcc for gfx950 and linked
 into budgeted_retention_amd/libkvc.so. Packed-FP32 instructions are disabled
 for all device code.
 """
@@ -46,8 +46,8 @@ def _compile(src, obj, verbose):
 def build(verbose=False, jobs=8):
     """Compile every csrc/*.hip and link libkvc.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s).replace(".hip", ".o")) for s in srcs]
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
     tmp = LIB_PATH + ".tmp"

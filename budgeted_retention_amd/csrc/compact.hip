@@ -109,6 +109,7 @@ struct CompactArgs {
     int8_t *Kq, *Vq;
     uint16_t *Ks, *Vs;
     int32_t *pq, *nl;
+    const int32_t *h_base, *l_base;
 };
 
 template <int D>
@@ -119,9 +120,12 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
     const int cb = blockIdx.x % blocks_per_row;
     int n = a.n_kept[r];
     if (n > a.kept_stride) n = a.kept_stride;
-    if (n > a.out_stride) n = a.out_stride;
     if (n < 0) n = 0;
-    if (cb == 0 && threadIdx.x == 0 && a.nh) a.nh[r] = n;
+    int base = a.h_base ? a.h_base[r] : 0;
+    if (base < 0) base = 0;
+    const int room = a.out_stride - base > 0 ? a.out_stride - base : 0;
+    if (n > room) n = room;
+    if (cb == 0 && threadIdx.x == 0 && a.nh) a.nh[r] = base + n;
     const int sub = threadIdx.x % TPT, tin = threadIdx.x / TPT;
     const bool rot = a.renumber_base >= 0;
     double th0 = 0.0, th1 = 0.0;
@@ -133,7 +137,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         const int64_t j = a.kept[(size_t)r * a.kept_stride + rho];
         if (j < 0 || j >= a.T) continue;
         const size_t src = ((size_t)r * a.T + j) * D;
-        const size_t dst = ((size_t)r * a.out_stride + rho) * D;
+        const size_t dst = ((size_t)r * a.out_stride + base + rho) * D;
         uint32_t lo = *reinterpret_cast<const uint32_t *>(a.K + src + 2 * sub);
         uint32_t hi = *reinterpret_cast<const uint32_t *>(a.K + src + D / 2 + 2 * sub);
         const uint2 v = *reinterpret_cast<const uint2 *>(a.V + src + 4 * sub);
@@ -146,7 +150,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         *reinterpret_cast<uint32_t *>(a.Ko + dst + 2 * sub) = lo;
         *reinterpret_cast<uint32_t *>(a.Ko + dst + D / 2 + 2 * sub) = hi;
         *reinterpret_cast<uint2 *>(a.Vo + dst + 4 * sub) = v;
-        if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + rho] = (int32_t)pn;
+        if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + base + rho] = (int32_t)pn;
     }
 }
 
@@ -171,7 +175,9 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
         th0 = pow(a.rope_base, -2.0 * (2 * sub) / D);
         th1 = pow(a.rope_base, -2.0 * (2 * sub + 1) / D);
     }
-    int carry_h = 0, carry_l = 0;
+    int carry_h = a.h_base ? a.h_base[r] : 0, carry_l = a.l_base ? a.l_base[r] : 0;
+    if (carry_h < 0) carry_h = 0;
+    if (carry_l < 0) carry_l = 0;
     for (int base = 0; base < n; base += CMP_THREADS) {
         const int rho = base + tid;
         const int act = rho < n ? a.action[(size_t)r * a.kept_stride + rho] : 0;
@@ -311,6 +317,8 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     a.Vs = out->Vs;
     a.pq = out->pos_q;
     a.nl = out->n_l;
+    a.h_base = out->h_base;
+    a.l_base = out->l_base;
     const int64_t rows = n_rows(dims);
     hipStream_t s = as_stream(stream);
     if (!out->action) {

@@ -127,10 +127,13 @@ class CompactOut:
     Vs: Optional[torch.Tensor] = None
     pos_q: Optional[torch.Tensor] = None
     n_l: Optional[torch.Tensor] = None
+    h_base: Optional[torch.Tensor] = None      # int32 [rows] first bf16 slot (append)
+    l_base: Optional[torch.Tensor] = None      # int32 [rows] first int8 slot (append)
 
     def to_c(self):
         return _lib.KvcCompactOut(
             _ptr(self.action, torch.uint8, "action"), self.out_stride, 0,
+            _ptr(self.h_base, torch.int32, "h_base"), _ptr(self.l_base, torch.int32, "l_base"),
             _ptr(self.K_out, torch.bfloat16, "K_out"), _ptr(self.V_out, torch.bfloat16, "V_out"),
             _ptr(self.pos_out, torch.int32, "pos_out"), _ptr(self.n_h, torch.int32, "n_h"),
             _ptr(self.Kq, torch.int8, "Kq"), _ptr(self.Vq, torch.int8, "Vq"),
@@ -196,3 +199,56 @@ def kvc_page_retire(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, or
         _ptr(joint_rel, torch.float32, "joint_rel"), _ptr(ws, None, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     return _lib.check(st)
+
+
+# ---------------------------------------------------------------- host control (numpy in/out)
+
+def _np_ptr(a, dtype):
+    import numpy as np
+    if a.dtype != dtype or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"expected a contiguous {dtype} array")
+    return a.ctypes.data
+
+
+def kvc_host_pask_costs(layers_per_group, n_kv_heads, head_dim, low_bits=8):
+    import numpy as np
+    lpg = np.ascontiguousarray(layers_per_group, dtype=np.int32)
+    out = np.zeros((lpg.size, 3), dtype=np.float64)
+    _lib.check(_lib.load().kvc_host_pask_costs(_np_ptr(lpg, np.int32), lpg.size, n_kv_heads, head_dim,
+                                               low_bits, _np_ptr(out, np.float64)))
+    return out
+
+
+def kvc_host_pask_control(a0, amin, prio, critical, costs, budget_fraction, tags, reserve=0.0):
+    """tags: uint8 [n_seq][n_tok]. Returns (actions uint8 [n_seq][n_tok][C], ledger [n_seq][n_tok+1])."""
+    import numpy as np
+    a0 = np.ascontiguousarray(a0, np.uint8)
+    amin = np.ascontiguousarray(amin, np.uint8)
+    prio = np.ascontiguousarray(prio, np.float32)
+    crit = np.ascontiguousarray(critical, np.uint8)
+    costs = np.ascontiguousarray(costs, np.float64)
+    tags = np.ascontiguousarray(tags, np.uint8)
+    n_seq, n_tok = tags.shape
+    C = a0.shape[1]
+    tbl = _lib.KvcPaskTable(a0.shape[0], C, _np_ptr(a0, np.uint8), _np_ptr(amin, np.uint8),
+                            _np_ptr(prio, np.float32), _np_ptr(crit, np.uint8))
+    acts = np.zeros((n_seq, n_tok, C), np.uint8)
+    ledger = np.zeros((n_seq, n_tok + 1), np.float64)
+    _lib.check(_lib.load().kvc_host_pask_control(
+        ctypes.byref(tbl), _np_ptr(costs, np.float64), float(budget_fraction), float(reserve),
+        _np_ptr(tags, np.uint8), n_seq, n_tok, _np_ptr(acts, np.uint8), _np_ptr(ledger, np.float64)))
+    return acts, ledger
+
+
+def kvc_host_commit_candidates(R_minus, R_plus, tau_use, tau_dead, rho_use, rho_dead, max_scan=64):
+    """Returns (state uint8 [n_pages], order int32 [max_scan] padded with -1, n_order)."""
+    import numpy as np
+    Rm = np.ascontiguousarray(R_minus, np.float32)
+    Rp = np.ascontiguousarray(R_plus, np.float32)
+    state = np.zeros(Rm.size, np.uint8)
+    order = np.zeros(max_scan, np.int32)
+    n = ctypes.c_int32(0)
+    _lib.check(_lib.load().kvc_host_commit_candidates(
+        _np_ptr(Rm, np.float32), _np_ptr(Rp, np.float32), Rm.size, tau_use, tau_dead, rho_use, rho_dead,
+        max_scan, _np_ptr(state, np.uint8), _np_ptr(order, np.int32), ctypes.addressof(n)))
+    return state, order, n.value

@@ -152,6 +152,11 @@ typedef struct kvc_compact_out {
     const uint8_t *action;
     int32_t out_stride;   /* capacity per row of every output pool below */
     int32_t reserved;     /* must be 0 */
+    /* Per-row first slot of this call's writes, device int32 [N][L][Hkv] or
+     * NULL (= 0): appends after what an earlier call wrote (pass that call's
+     * n_h / n_l). Must not alias the n_h / n_l outputs. */
+    const int32_t *h_base;
+    const int32_t *l_base;
     /* bf16 tier */
     uint16_t *K_out;      /* bf16 [N][L][Hkv][out_stride][d] */
     uint16_t *V_out;      /* bf16 [N][L][Hkv][out_stride][d] */
@@ -186,8 +191,8 @@ typedef struct kvc_compact_out {
  *   K, V      bf16 [N][L][Hkv][T][d]
  *   pos_in    int32 [N][L][Hkv][T] physical positions, or NULL (position = index)
  *   kept_idx  int32 [N][L][Hkv][kept_stride], n_kept int32 [N][L][Hkv] (from kvc_select)
- *   Entries beyond min(n_kept, kept_stride, out_stride) are ignored; indices
- *   outside [0, T) are skipped.
+ *   Entries beyond min(n_kept, kept_stride) or past out_stride are ignored;
+ *   indices outside [0, T) are skipped. n_h / n_l report base + rows written.
  */
 int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, const uint16_t *V,
                          const int32_t *pos_in, const int32_t *kept_idx, int32_t kept_stride,
@@ -274,6 +279,68 @@ int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16_t *K, cons
                     const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
                     int32_t n_pages, const int32_t *order, int32_t n_cand, float tau_joint,
                     uint8_t *accepted, float *joint_rel, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Host-side serial control (plain C on host memory; no GPU work). Their
+ * outputs feed the `action` argument of kvc_compact_rerotate and the `order`
+ * argument of kvc_page_retire.
+ * ---------------------------------------------------------------------- */
+
+/* PASK Appendix B.3 payload costs (Eq. 13-14) per layer group, in bits:
+ * costs[c][0..2] = m(R), m(L), m(H) with n_c = 2*layers*Hkv*d and
+ * k_c = 2*layers*Hkv, m(H) = 16 n_c, m(L) = low_bits*n_c + 16 k_c, m(R) = 0.
+ * costs is host double [n_groups][3]. */
+int kvc_host_pask_costs(const int32_t *layers_per_group, int32_t n_groups, int32_t n_kv_heads,
+                        int32_t head_dim, int32_t low_bits, double *costs);
+
+/* Frozen PASK policy table (PASK §3.5 lookup), host memory. Actions are
+ * 0 = release (R), 1 = low precision (L), 2 = bf16 (H). */
+typedef struct kvc_pask_table {
+    int32_t n_tags, n_groups;
+    const uint8_t *a0;        /* [n_tags][n_groups] base action */
+    const uint8_t *amin;      /* [n_tags][n_groups] floor action */
+    const float *prio;        /* [n_tags][n_groups][2] stored priority of the upgrades R->L, L->H */
+    const uint8_t *critical;  /* [n_tags] 1 = critical tag (promotions allowed) */
+} kvc_pask_table;
+
+/*
+ * PASK online structural control, Algorithm 2 (§3.5, Eq. 11) per generated
+ * token: a = max(a0, amin); B_t = [R_t - reserve]_+; demote the eligible
+ * adjacent step with the smallest stored priority (never below the floor)
+ * until M(a) <= B_t or only floors remain; for critical tags promote in
+ * descending priority while the cost still fits (stopping at the first that
+ * does not); R_{t+1} = R_t - M(a) + b with b = budget_fraction * C_full and
+ * R_1 = b. The priority of a demotion is that of the upgrade it undoes;
+ * priority ties go to the lower group.
+ *   tags     host u8 [n_seq][n_tok];  actions host u8 [n_seq][n_tok][n_groups]
+ *   ledger   host double [n_seq][n_tok + 1] (R_1 .. R_{n_tok+1}) or NULL
+ */
+int kvc_host_pask_control(const kvc_pask_table *tbl, const double *costs, double budget_fraction,
+                          double reserve, const uint8_t *tags, int32_t n_seq, int32_t n_tok,
+                          uint8_t *actions, double *ledger);
+
+/* CommitKV lifecycle states (CommitKV §3.2 Eq. 10). */
+enum {
+    KVC_LIFE_UNCERTAIN = 0,
+    KVC_LIFE_COMPLETION = 1,
+    KVC_LIFE_DORMANT = 2,
+    KVC_LIFE_NEWLY_ACTIVE = 3,
+    KVC_LIFE_STILL_ACTIVE = 4
+};
+
+/*
+ * CommitKV lifecycle classification and candidate order (CommitKV §3.2
+ * Eq. 9-10, §3.3). Percentile rank P(E) = #{E' : R(E') < R(E)} / (n_pages-1);
+ * high: R >= tau_use and P >= rho_use; low: R <= tau_dead and P <= rho_dead.
+ * Completion candidates (high before, low after) are ordered by R_plus
+ * ascending, then R_minus descending, then page index; the first max_scan
+ * go to `order` (padded with -1), their count to *n_order.
+ *   R_minus, R_plus host fp32 [n_pages]; state host u8 [n_pages];
+ *   order host int32 [max_scan].
+ */
+int kvc_host_commit_candidates(const float *R_minus, const float *R_plus, int32_t n_pages, float tau_use,
+                               float tau_dead, float rho_use, float rho_dead, int32_t max_scan,
+                               uint8_t *state, int32_t *order, int32_t *n_order);
 
 #ifdef __cplusplus
 }

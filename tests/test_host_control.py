@@ -1,0 +1,61 @@
+"""Host-side serial control in libkvc (PASK controller, CommitKV candidate
+order) against the oracle. Plain host code: runs without a GPU."""
+import numpy as np
+import pytest
+
+from budgeted_retention_amd import kvc
+from oracle import page_effect as o_pe
+from oracle import pask as o_pask
+
+
+def test_pask_costs_match_oracle():
+    got = kvc.kvc_host_pask_costs([8, 8, 8, 8], 8, 128, 8)
+    np.testing.assert_array_equal(got, o_pask.group_costs([8, 8, 8, 8], 8, 128))
+    got4 = kvc.kvc_host_pask_costs([12, 12, 12], 8, 128, 4)
+    np.testing.assert_array_equal(got4, o_pask.group_costs([12, 12, 12], 8, 128, low_bits=4))
+
+
+@pytest.mark.parametrize("seed,B_D", [(1, 1 / 3), (2, 0.5), (3, 0.1), (4, 1.0)])
+def test_pask_control_matches_oracle(seed, B_D):
+    rng = np.random.default_rng(seed)
+    n_tags, C, n_seq, n_tok = 8, 4, 3, 700
+    a0 = rng.integers(0, 3, (n_tags, C)).astype(np.uint8)
+    amin = np.minimum(a0, rng.integers(0, 3, (n_tags, C))).astype(np.uint8)
+    prio = rng.random((n_tags, C, 2)).astype(np.float32)
+    crit = (rng.random(n_tags) < 0.3).astype(np.uint8)
+    costs = o_pask.group_costs([8, 8, 8, 8], 8, 128)
+    tags = rng.integers(0, n_tags, (n_seq, n_tok)).astype(np.uint8)
+    acts, ledger = kvc.kvc_host_pask_control(a0, amin, prio, crit, costs, B_D, tags)
+    for n in range(n_seq):
+        o_acts, o_ledger = o_pask.control_sequence(tags[n], a0.astype(np.int64), amin.astype(np.int64),
+                                                   prio.astype(np.float64), crit, costs, B_D)
+        np.testing.assert_array_equal(acts[n], o_acts)
+        np.testing.assert_allclose(ledger[n], o_ledger, rtol=1e-12, atol=1e-6)
+
+
+def test_commit_candidates_match_oracle():
+    rng = np.random.default_rng(5)
+    n = 500
+    Rm = (10.0 ** rng.uniform(-5, 0, n)).astype(np.float32)
+    Rp = (10.0 ** rng.uniform(-5, 0, n)).astype(np.float32)
+    Rp[:40] = Rp[0]                       # ties in R+ exercise the secondary key
+    c = dict(tau_use=0.05, tau_dead=1e-3, rho_use=0.75, rho_dead=0.25)
+    state, order, n_order = kvc.kvc_host_commit_candidates(Rm, Rp, max_scan=64, **c)
+    o_state = o_pe.lifecycle_states(Rm.astype(np.float64), Rp.astype(np.float64), c["tau_use"],
+                                    np.float32(c["tau_dead"]), c["rho_use"], c["rho_dead"])
+    np.testing.assert_array_equal(state, o_state)
+    o_order = o_pe.candidate_order(Rm.astype(np.float64), Rp.astype(np.float64), o_state)[:64]
+    assert n_order == o_order.size
+    np.testing.assert_array_equal(order[:n_order], o_order)
+    assert np.all(order[n_order:] == -1)
+
+
+def test_host_helpers_reject_bad_arguments():
+    from budgeted_retention_amd import _lib
+    with pytest.raises(_lib.KvcError):
+        kvc.kvc_host_pask_costs([8, -1], 8, 128)
+    with pytest.raises(_lib.KvcError):
+        tags = np.full((1, 4), 9, np.uint8)        # tag outside the 8-row table
+        z = np.zeros((8, 2), np.uint8)
+        kvc.kvc_host_pask_control(z, z, np.zeros((8, 2, 2), np.float32), np.zeros(8, np.uint8),
+                                  np.zeros((2, 3)), 0.5, tags)
