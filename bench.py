@@ -30,6 +30,9 @@ def parse():
     ap.add_argument("--workload", default="qwen3_8b_100k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (three times), so that HBM "
+                         "counters can be scaled against a transfer of known size")
     return ap.parse_args()
 
 
@@ -142,6 +145,14 @@ def main():
         if ev:
             ev[3].record()
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
