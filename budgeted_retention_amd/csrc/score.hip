@@ -1,220 +1,373 @@
 // kvc_score: observation-window attention score.
 //
 // Per row (sequence, layer, KV head) the G*W window queries of the GQA group
-// (query row qr = g*W + w at position T-W+w) attend causally to the T cached
-// keys; the score of key j is the sum over query rows of its softmax weight
-// (PASK §3.1 Eq. 1 attention, window queries as in CommitKV §3.1 Eq. 5,
+// (query row qr = g*W + w at position qbase+w, qbase = T-W) attend causally to
+// the cached keys; the score of key j is the sum over query rows of its softmax
+// weight (PASK §3.1 Eq. 1 attention, window queries as in CommitKV §3.1 Eq. 5,
 // causal rule of CommitKV Eq. 6).
 //
-// A softmax weight needs its query row's normaliser over all T keys, so the
-// keys are streamed twice:
-//   pass 1  each workgroup takes CHUNK keys of one row and produces, per
-//           query row, the running max and exp-sum of its logits (log2 domain);
-//   merge   one workgroup per row folds the chunk partials into
-//           mm[qr] = max + log2(sum) for every query row;
-//   pass 2  each workgroup recomputes its chunk's logits and writes
-//           score[j] = sum_qr exp2(logit*c - mm[qr]).
+// A softmax weight needs its query row's normaliser over all keys, so the keys
+// are read twice: pass 1 gives every query row its max and exp-sum (log2
+// domain) chunk by chunk, a merge folds the chunks into mm[qr] = max +
+// log2(sum), and pass 2 recomputes the logits and writes
+// score[j] = sum_qr exp2(logit*c - mm[qr]).
 //
-// Logits come from MFMA v_mfma_f32_32x32x16_bf16 tiles. A 32-key x 16-dim slice of
-// K is loaded so that lane l holds key (l & 31), dims 8*(l>>5)..+8 of the
-// slice; that register layout serves as the A operand (rows = keys) in pass 1
-// and as the B operand (columns = keys) in pass 2, so one load feeds both
-// orientations. Pass 1 computes C[key][qrow] (a lane owns one query row, so the
-// max/sum over keys stay in-lane); pass 2 computes C[qrow][key] (a lane owns
-// one key, so the sum over query rows stays in-lane). Each wave owns 32 query
-// rows; a workgroup has ceil(G*W/32) waves.
+// kvc_score launches pass 1 (one workgroup per row and STATS_CHUNK keys), the
+// merge (one workgroup per row) and pass 2 (same grid as pass 1).
+//
+// Tiles. A workgroup has four waves; each wave owns whole 32-key tiles of the
+// chunk (tiles w, w+4, ...), so each key is loaded once, straight into MFMA operand registers. The
+// row's window queries are staged in LDS in MFMA fragment order (entry
+// (b*S + s)*64 + lane is the 16-byte slice lane `lane` feeds for query block
+// b, k-step s) and read back with conflict-free 16-byte loads.
+//
+// Logits come from v_mfma_f32_32x32x16_bf16. Lane l holds key (l & 31), dims
+// 8*(l>>5)..+8 of each 16-dim slice; that layout is the A operand (rows = keys)
+// in pass 1 and the B operand (columns = keys) in pass 2. Pass 1 computes
+// C[key][qrow] (a lane owns one query row: max/sum over keys stay in-lane);
+// pass 2 computes C[qrow][key] (a lane owns one key: the sum over query rows
+// stays in-lane).
 #include <cmath>
 
 #include "kvc_internal.h"
 
 namespace kvc {
 
-static constexpr int SCORE_CHUNK = 1024;  // keys per workgroup
-static constexpr int SCORE_MAX_QR = 256;  // query rows per row (8 waves)
-
-struct ScoreGeom {
-    int64_t rows, n_chunks;
-    int QR, QRP, nb;
-};
-
-static ScoreGeom score_geom(const kvc_dims *d, int32_t W) {
-    ScoreGeom g;
-    int G = d->n_q_heads / d->n_kv_heads;
-    g.rows = n_rows(d);
-    g.n_chunks = (d->n_tokens + SCORE_CHUNK - 1) / SCORE_CHUNK;
-    g.QR = G * W;
-    g.nb = (g.QR + 31) / 32;
-    g.QRP = g.nb * 32;
-    return g;
-}
+static constexpr int SCORE_WAVES = 4;  // waves per workgroup
+static constexpr int SCORE_THREADS = SCORE_WAVES * 64;
+static constexpr int SCORE_MAX_QR = 256;  // query rows per row (8 blocks of 32)
+static constexpr int STATS_CHUNK = 2048;  // keys per workgroup of both passes
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int64_t window_chunks(int64_t kend) { return (kend + STATS_CHUNK - 1) / STATS_CHUNK; }
+
+// kvc_score workspace: chunk partials [rows][QRP][n_chunks] then the merged
+// normalisers [rows][QRP].
 size_t score_workspace_bytes(const kvc_dims *d, int32_t W) {
-    ScoreGeom g = score_geom(d, W);
-    size_t part = (size_t)g.rows * g.n_chunks * g.QRP * sizeof(float2);
-    size_t mm = (size_t)g.rows * g.QRP * sizeof(float);
-    return align256(part) + align256(mm);
+    const int G = d->n_q_heads / d->n_kv_heads;
+    const int QRP = ((G * W + 31) / 32) * 32;
+    const int64_t rows = n_rows(d);
+    const int64_t nch = window_chunks(d->n_tokens);
+    return align256((size_t)rows * nch * QRP * sizeof(float2)) + align256((size_t)rows * QRP * sizeof(float));
 }
 
-template <int D>
-__global__ void __launch_bounds__(512) score_pass1(const uint16_t *__restrict__ K,
-                                                   const uint16_t *__restrict__ Q, int64_t T, int W,
-                                                   int G, int L, int Hkv, int Hq, int64_t n_chunks,
-                                                   float c2, WindowGeom wg, float2 *__restrict__ part) {
+// Stage the row's queries in fragment order (zero rows beyond QR).
+template <int D, int NB>
+__device__ __forceinline__ void stage_queries(const uint16_t *Qg, int QR, uint4 *sq) {
     constexpr int S = D / 16;
-    const int QR = G * W;
-    const int QRP = (blockDim.x >> 6) * 32;
-    const int64_t r = blockIdx.x / n_chunks;  // local row
+    for (int e = threadIdx.x; e < NB * S * 64; e += SCORE_THREADS) {
+        const int lane = e & 63, bs = e >> 6, s = bs % S, b = bs / S;
+        const int qr = b * 32 + (lane & 31);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (qr < QR) v = *reinterpret_cast<const uint4 *>(Qg + (size_t)qr * D + 16 * s + 8 * (lane >> 5));
+        sq[e] = v;
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void load_key_tile(const uint16_t *Kr, int64_t key, int64_t kend, int hf, bf16x8 *kf) {
+    constexpr int D = S * 16;
+#pragma unroll
+    for (int s = 0; s < S; ++s) kf[s] = key < kend ? load8(Kr + (size_t)key * D + 16 * s + 8 * hf) : zero8();
+}
+
+// Number of tiles of [k0, k0 + 32*ntiles) whose last key is <= qbase (visible
+// to every query row).
+__device__ __forceinline__ int visible_tiles(int64_t k0, int64_t qbase, int ntiles) {
+    const int64_t v = qbase + 1 - k0 >= 0 ? (qbase + 1 - k0) / 32 : 0;
+    return v < ntiles ? (int)v : ntiles;
+}
+
+// ---------------------------------------------------------------- pass 1
+
+// One 32-key tile for every query block: running max/exp-sum per query row
+// (this lane's query row is b*32 + col of block b).
+template <int D, int NB, bool MASKED>
+__device__ __forceinline__ void p1_tile(const uint16_t *Kr, int64_t j0, int64_t kend, int lane, const uint4 *sq,
+                                        const int64_t *qpos, float c2, float *m, float *l) {
+    constexpr int S = D / 16;
+    const int col = lane & 31, hf = lane >> 5;
+    bf16x8 kf[S];
+    load_key_tile<S>(Kr, j0 + col, kend, hf, kf);
+    // Re-read the queries from LDS every tile (an opaque lane offset keeps the
+    // loads in the loop): holding all of them in registers would cost occupancy.
+    int qoff = lane;
+    asm volatile("" : "+v"(qoff));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const bf16x8 qf = __builtin_bit_cast(bf16x8, sq[(b * S + s) * 64 + qoff]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf, acc, 0, 0, 0);
+        }
+        // acc[i] = logit of key j0 + acc_row(i, hf) for query row b*32 + col
+        if (MASKED) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (j0 + acc_row(i, hf) > qpos[b]) acc[i] = -INFINITY;
+        }
+        float tmax = acc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[i]);
+        tmax *= c2;
+        if (tmax > m[b]) {
+            l[b] *= __builtin_amdgcn_exp2f(m[b] - tmax);
+            m[b] = tmax;
+        }
+        // A row with no visible key yet keeps m = -inf; its exponents are all -inf.
+        const float mb = (MASKED && m[b] == -INFINITY) ? 0.f : m[b];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mb));
+        l[b] += sum;
+    }
+}
+
+// Pass 1 over keys [k0, k1): (max, exp-sum) of every query row q -> out[q * out_stride].
+// Uses s_m/s_l (SCORE_WAVES x QRP floats each) and ends with a barrier.
+template <int D, int NB>
+__device__ __forceinline__ void p1_chunk(const uint16_t *Kr, int64_t k0, int64_t k1, int64_t qbase, int W, int QR,
+                                         float c2, const uint4 *sq, float *s_m, float *s_l, float2 *out,
+                                         int64_t out_stride) {
+    constexpr int QRP = NB * 32;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 31, hf = lane >> 5;
+    float m[NB], l[NB];
+    int64_t qpos[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        m[b] = -INFINITY;
+        l[b] = 0.f;
+        const int qr = b * 32 + col;
+        qpos[b] = qr < QR ? qbase + qr % W : -1;
+    }
+    const int ntiles = (int)((k1 - k0 + 31) / 32);
+    const int nvis = visible_tiles(k0, qbase, ntiles);
+    int t = wave;
+    for (; t < nvis; t += SCORE_WAVES) p1_tile<D, NB, false>(Kr, k0 + 32 * t, k1, lane, sq, qpos, c2, m, l);
+    for (; t < ntiles; t += SCORE_WAVES) p1_tile<D, NB, true>(Kr, k0 + 32 * t, k1, lane, sq, qpos, c2, m, l);
+    // Lanes l and l^32 hold the same query row over different keys; then the
+    // waves of the workgroup hold it over different tiles.
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const float mo = __shfl_xor(m[b], 32);
+        const float lo = __shfl_xor(l[b], 32);
+        const float M = fmaxf(m[b], mo);
+        float Ls = 0.f;
+        if (M > -INFINITY) Ls = l[b] * __builtin_amdgcn_exp2f(m[b] - M) + lo * __builtin_amdgcn_exp2f(mo - M);
+        if (hf == 0) {
+            s_m[wave * QRP + b * 32 + col] = M;
+            s_l[wave * QRP + b * 32 + col] = Ls;
+        }
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < QRP; q += SCORE_THREADS) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < SCORE_WAVES; ++w) M = fmaxf(M, s_m[w * QRP + q]);
+        float Ls = 0.f;
+        if (M > -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < SCORE_WAVES; ++w)
+                if (s_l[w * QRP + q] > 0.f) Ls += s_l[w * QRP + q] * __builtin_amdgcn_exp2f(s_m[w * QRP + q] - M);
+        }
+        out[q * out_stride] = make_float2(M, Ls);
+    }
+    __syncthreads();
+}
+
+// mm[q] = max + log2(sum) over a row's chunk partials part[q][0..nch); padding
+// rows get +inf (their weights exp2(x - inf) are 0). All threads of the
+// workgroup take part: query row q is folded by blockDim/QRP threads, each over
+// a contiguous range of chunks in one online (max, sum) pass; the ranges are
+// then combined in a fixed order, so the result does not depend on timing.
+__device__ __forceinline__ void fold(float &M, float &S, float m, float l) {
+    if (!(l > 0.f)) return;
+    if (m > M) {
+        S = S * __builtin_amdgcn_exp2f(M - m) + l;
+        M = m;
+    } else {
+        S += l * __builtin_amdgcn_exp2f(m - M);
+    }
+}
+
+__device__ void merge_row(const float2 *part, int64_t nch, int QR, int QRP, float *mm, float2 *s_tmp) {
+    const int groups = (int)blockDim.x / QRP;  // >= 1 (QRP <= 256 = blockDim)
+    const int q = threadIdx.x % QRP, g = threadIdx.x / QRP;
+    if (g < groups) {
+        const int64_t per = (nch + groups - 1) / groups;
+        const int64_t c0 = g * per, c1 = c0 + per < nch ? c0 + per : nch;
+        const float2 *pq = part + (size_t)q * nch;
+        float M = -INFINITY, S = 0.f;
+        int64_t c = c0;
+        for (; c + 8 <= c1; c += 8) {
+            float2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = pq[c + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) fold(M, S, v[u].x, v[u].y);
+        }
+        for (; c < c1; ++c) fold(M, S, pq[c].x, pq[c].y);
+        s_tmp[g * QRP + q] = make_float2(M, S);
+    }
+    __syncthreads();
+    if (threadIdx.x < QRP) {
+        float M = -INFINITY, S = 0.f;
+        for (int gg = 0; gg < groups; ++gg) fold(M, S, s_tmp[gg * QRP + q].x, s_tmp[gg * QRP + q].y);
+        mm[q] = q < QR ? M + log2f(S) : INFINITY;
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------- pass 2
+
+// One 32-key tile: softmax weights of every query row for this lane's key,
+// summed; one query block at a time (interleaving blocks would hold several
+// accumulators and fragment sets live and cost occupancy).
+template <int D, int NB, bool MASKED>
+__device__ __forceinline__ void p2_tile(const uint16_t *Kr, int64_t j0, int64_t kend, int lane, const uint4 *sq,
+                                        const float4 *s_mm, float c2, int64_t qbase, int W, float *out) {
+    constexpr int S = D / 16;
+    const int col = lane & 31, hf = lane >> 5;
+    const int64_t key = j0 + col;
+    bf16x8 kf[S];
+    load_key_tile<S>(Kr, key, kend, hf, kf);
+    int qoff = lane, moff = hf;  // opaque offsets keep the LDS reads inside the loop
+    asm volatile("" : "+v"(qoff), "+v"(moff));
+    float p = 0.f;
+#pragma unroll 1
+    for (int b = 0; b < NB; ++b) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const bf16x8 qf = __builtin_bit_cast(bf16x8, sq[(b * S + s) * 64 + qoff]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf[s], acc, 0, 0, 0);
+        }
+        // acc[i] = logit of query row b*32 + acc_row(i, hf) for key `key`; rows
+        // acc_row(4k..4k+3, hf) are 8k + 4hf .. +3: one float4 of normalisers each.
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const float4 mv = s_mm[b * 8 + 2 * k4 + moff];
+            const float mvs[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * k4 + e;
+                float x = fmaf(acc[i], c2, -mvs[e]);
+                if (MASKED) {
+                    const int qr = b * 32 + acc_row(i, hf);
+                    if (key > qbase + qr % W) x = -INFINITY;
+                }
+                p += __builtin_amdgcn_exp2f(x);
+            }
+        }
+    }
+    p += __shfl_xor(p, 32);
+    if (hf == 0 && key < kend) out[key] = p;
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void p2_chunk(const uint16_t *Kr, int64_t k0, int64_t k1, int64_t qbase, int W,
+                                         float c2, const uint4 *sq, const float4 *s_mm, float *out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ntiles = (int)((k1 - k0 + 31) / 32);
+    const int nvis = visible_tiles(k0, qbase, ntiles);
+    int t = wave;
+    for (; t < nvis; t += SCORE_WAVES) p2_tile<D, NB, false>(Kr, k0 + 32 * t, k1, lane, sq, s_mm, c2, qbase, W, out);
+    for (; t < ntiles; t += SCORE_WAVES) p2_tile<D, NB, true>(Kr, k0 + 32 * t, k1, lane, sq, s_mm, c2, qbase, W, out);
+}
+
+// ---------------------------------------------------------------- kernels
+
+// Pass 1: one workgroup per (local row, STATS_CHUNK keys); also used for
+// windows inside the cache (page effects).
+template <int D, int NB>
+__global__ void __launch_bounds__(SCORE_THREADS) score_pass1(const uint16_t *__restrict__ K,
+                                                             const uint16_t *__restrict__ Q, int64_t T, int W,
+                                                             int G, int L, int Hkv, int Hq, int64_t n_chunks,
+                                                             float c2, WindowGeom wg, float2 *__restrict__ part) {
+    constexpr int QRP = NB * 32;
+    extern __shared__ uint4 sq[];
+    __shared__ float s_m[SCORE_WAVES * QRP], s_l[SCORE_WAVES * QRP];
+    const int64_t r = blockIdx.x / n_chunks;
     const int64_t chunk = blockIdx.x % n_chunks;
     const int64_t gr = wg.global_row(r, L, Hkv);
     const RowIdx ri = split_row(gr, L, Hkv);
     const uint16_t *Kr = K + (size_t)gr * T * D;
     const uint16_t *Qg = Q + ((size_t)(ri.n * L + ri.l) * Hq + (size_t)ri.h * G) * W * D;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int col = lane & 31, hf = lane >> 5;
-    const int64_t qbase = wg.qbase;
-
-    const int qrow = wave * 32 + col;
-    bf16x8 qf[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) qf[s] = qrow < QR ? load8(Qg + (size_t)qrow * D + 16 * s + 8 * hf) : zero8();
-    const int64_t qpos = qrow < QR ? qbase + qrow % W : -1;
-
-    float m = -INFINITY, l = 0.f;
-    const int64_t k0 = chunk * SCORE_CHUNK;
-    const int64_t k1 = k0 + SCORE_CHUNK < wg.kend ? k0 + SCORE_CHUNK : wg.kend;
-    for (int64_t j0 = k0; j0 < k1; j0 += 32) {
-        const int64_t key = j0 + col;
-        bf16x8 kf[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) kf[s] = key < T ? load8(Kr + (size_t)key * D + 16 * s + 8 * hf) : zero8();
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
-        // acc[i] = logit of key j0 + acc_row(i, hf) for query row `qrow`
-        const bool all_vis = j0 + 31 <= qbase;  // every key of the tile is visible to every query
-        float tmax = -INFINITY;
-        if (all_vis) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (j0 + acc_row(i, hf) <= qpos) tmax = fmaxf(tmax, acc[i]);
-        }
-        tmax *= c2;
-        if (tmax > m) {
-            l *= __builtin_amdgcn_exp2f(m - tmax);
-            m = tmax;
-        }
-        float sum = 0.f;
-        if (all_vis) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -m));
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (j0 + acc_row(i, hf) <= qpos) sum += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -m));
-        }
-        l += sum;
-    }
-    // Lanes l and l^32 hold the same query row over different keys.
-    const float mo = __shfl_xor(m, 32);
-    const float lo = __shfl_xor(l, 32);
-    const float M = fmaxf(m, mo);
-    float Ls = 0.f;
-    if (M > -INFINITY) Ls = l * __builtin_amdgcn_exp2f(m - M) + lo * __builtin_amdgcn_exp2f(mo - M);
-    if (hf == 0) part[((size_t)r * n_chunks + chunk) * QRP + qrow] = make_float2(M, Ls);
+    stage_queries<D, NB>(Qg, G * W, sq);
+    __syncthreads();
+    const int64_t k0 = chunk * STATS_CHUNK;
+    const int64_t k1 = k0 + STATS_CHUNK < wg.kend ? k0 + STATS_CHUNK : wg.kend;
+    p1_chunk<D, NB>(Kr, k0, k1, wg.qbase, W, G * W, c2, sq, s_m, s_l, part + ((size_t)r * QRP) * n_chunks + chunk,
+                    n_chunks);
 }
 
-__global__ void score_merge(const float2 *__restrict__ part, int64_t n_chunks, int QR, int QRP,
-                            float *__restrict__ mm) {
+__global__ void __launch_bounds__(SCORE_THREADS) score_merge(const float2 *__restrict__ part, int64_t n_chunks,
+                                                              int QR, int QRP, float *__restrict__ mm) {
+    __shared__ float2 s_tmp[SCORE_THREADS];
     const int64_t r = blockIdx.x;
-    const int q = threadIdx.x;
-    if (q >= QRP) return;
-    if (q >= QR) {
-        mm[r * QRP + q] = INFINITY;  // padding rows contribute exp2(-inf) = 0
-        return;
-    }
-    const float2 *p = part + (size_t)r * n_chunks * QRP + q;
-    float M = -INFINITY;
-    for (int64_t c = 0; c < n_chunks; ++c) M = fmaxf(M, p[c * QRP].x);
-    float S = 0.f;
-    for (int64_t c = 0; c < n_chunks; ++c) {
-        float2 v = p[c * QRP];
-        if (v.y > 0.f) S += v.y * exp2f(v.x - M);
-    }
-    mm[r * QRP + q] = M + log2f(S);
+    merge_row(part + (size_t)r * n_chunks * QRP, n_chunks, QR, QRP, mm + r * QRP, s_tmp);
 }
 
-template <int D>
-__global__ void __launch_bounds__(512) score_pass2(const uint16_t *__restrict__ K,
-                                                   const uint16_t *__restrict__ Q, int64_t T, int W,
-                                                   int G, int L, int Hkv, int Hq, int64_t n_chunks,
-                                                   float c2, const float *__restrict__ mm,
-                                                   float *__restrict__ scores) {
-    const WindowGeom wg{T - W, T, -1};
-    constexpr int S = D / 16;
-    extern __shared__ float red[];  // [nb][SCORE_CHUNK]
-    const int QR = G * W;
-    const int nb = blockDim.x >> 6;
-    const int QRP = nb * 32;
+// Pass 2: one workgroup per (row, STATS_CHUNK keys), with the row's merged
+// normalisers mm[row][QRP].
+template <int D, int NB>
+__global__ void __launch_bounds__(SCORE_THREADS) score_pass2(const uint16_t *__restrict__ K,
+                                                             const uint16_t *__restrict__ Q, int64_t T, int W,
+                                                             int G, int L, int Hkv, int Hq, int64_t n_chunks,
+                                                             float c2, const float *__restrict__ mm,
+                                                             float *__restrict__ scores) {
+    constexpr int QRP = NB * 32;
+    extern __shared__ uint4 sq[];
+    __shared__ float4 s_mm[QRP / 4];
     const int64_t r = blockIdx.x / n_chunks;
     const int64_t chunk = blockIdx.x % n_chunks;
-    const RowIdx ri = split_row(wg.global_row(r, L, Hkv), L, Hkv);
+    const RowIdx ri = split_row(r, L, Hkv);
     const uint16_t *Kr = K + (size_t)r * T * D;
     const uint16_t *Qg = Q + ((size_t)(ri.n * L + ri.l) * Hq + (size_t)ri.h * G) * W * D;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int col = lane & 31, hf = lane >> 5;
-
-    bf16x8 qf[S];
-    {
-        const int qrow = wave * 32 + col;
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-            qf[s] = qrow < QR ? load8(Qg + (size_t)qrow * D + 16 * s + 8 * hf) : zero8();
-    }
-    // This lane's 16 accumulator rows.
-    float mmi[16];
-    int64_t qpos[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int qr = wave * 32 + acc_row(i, hf);
-        mmi[i] = mm[r * QRP + qr];
-        qpos[i] = qr < QR ? wg.qbase + qr % W : -1;
-    }
-
-    const int64_t k0 = chunk * SCORE_CHUNK;
-    const int64_t k1 = k0 + SCORE_CHUNK < T ? k0 + SCORE_CHUNK : T;
-    for (int64_t j0 = k0; j0 < k1; j0 += 32) {
-        const int64_t key = j0 + col;
-        bf16x8 kf[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) kf[s] = key < T ? load8(Kr + (size_t)key * D + 16 * s + 8 * hf) : zero8();
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf[s], acc, 0, 0, 0);
-        // acc[i] = logit of query row wave*32 + acc_row(i, hf) for key `key`
-        float p = 0.f;
-        if (j0 + 31 <= wg.qbase) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) p += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mmi[i]));
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (key <= qpos[i]) p += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mmi[i]));
-        }
-        p += __shfl_xor(p, 32);
-        if (hf == 0) red[wave * SCORE_CHUNK + (j0 - k0) + col] = p;
-    }
+    stage_queries<D, NB>(Qg, G * W, sq);
+    for (int q = threadIdx.x; q < QRP / 4; q += SCORE_THREADS)
+        s_mm[q] = *reinterpret_cast<const float4 *>(mm + r * QRP + 4 * q);
     __syncthreads();
-    for (int64_t t = threadIdx.x; t < k1 - k0; t += blockDim.x) {
-        float s = 0.f;
-        for (int b = 0; b < nb; ++b) s += red[b * SCORE_CHUNK + t];
-        scores[(size_t)r * T + k0 + t] = s;
-    }
+    const int64_t k0 = chunk * STATS_CHUNK;
+    const int64_t k1 = k0 + STATS_CHUNK < T ? k0 + STATS_CHUNK : T;
+    p2_chunk<D, NB>(Kr, k0, k1, T - W, W, c2, sq, s_mm, scores + (size_t)r * T);
 }
+
+// ---------------------------------------------------------------- launches
+
+template <int D, int NB>
+static int launch_pass1(int64_t blocks, hipStream_t s, const uint16_t *K, const uint16_t *Q, int64_t T, int W,
+                        int G, int L, int Hkv, int Hq, int64_t n_chunks, float c2, WindowGeom wg, float2 *part) {
+    const size_t lds = (size_t)NB * (D / 16) * 64 * sizeof(uint4);
+    score_pass1<D, NB><<<dim3((unsigned)blocks), dim3(SCORE_THREADS), lds, s>>>(K, Q, T, W, G, L, Hkv, Hq,
+                                                                               n_chunks, c2, wg, part);
+    return check_launch("score pass 1");
+}
+
+template <int D, int NB>
+static int launch_pass2(int64_t blocks, hipStream_t s, const uint16_t *K, const uint16_t *Q, int64_t T, int W,
+                        int G, int L, int Hkv, int Hq, int64_t n_chunks, float c2, const float *mm,
+                        float *scores) {
+    const size_t lds = (size_t)NB * (D / 16) * 64 * sizeof(uint4);
+    score_pass2<D, NB><<<dim3((unsigned)blocks), dim3(SCORE_THREADS), lds, s>>>(K, Q, T, W, G, L, Hkv, Hq,
+                                                                               n_chunks, c2, mm, scores);
+    return check_launch("kvc_score pass 2");
+}
+
+#define KVC_NB_SWITCH(nb, D, CALL) \
+    switch (nb) {                  \
+    case 1: return CALL(D, 1);     \
+    case 2: return CALL(D, 2);     \
+    case 3: return CALL(D, 3);     \
+    case 4: return CALL(D, 4);     \
+    case 5: return CALL(D, 5);     \
+    case 6: return CALL(D, 6);     \
+    case 7: return CALL(D, 7);     \
+    default: return CALL(D, 8);    \
+    }
 
 int launch_window_stats(const kvc_dims *d, const uint16_t *K, const uint16_t *Q, int W, WindowGeom wg,
                         int64_t rows_local, float2 *part, float *mm, hipStream_t s) {
@@ -224,21 +377,22 @@ int launch_window_stats(const kvc_dims *d, const uint16_t *K, const uint16_t *Q,
     const int64_t blocks = rows_local * n_chunks;
     if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "window stats: grid too large");
     const float c2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
-    const int L = d->n_layers, Hkv = d->n_kv_heads, Hq = d->n_q_heads;
     const int64_t T = d->n_tokens;
-    if (d->head_dim == 128)
-        score_pass1<128><<<dim3((unsigned)blocks), dim3(nb * 64), 0, s>>>(K, Q, T, W, G, L, Hkv, Hq, n_chunks,
-                                                                        c2, wg, part);
-    else
-        score_pass1<64><<<dim3((unsigned)blocks), dim3(nb * 64), 0, s>>>(K, Q, T, W, G, L, Hkv, Hq, n_chunks,
-                                                                       c2, wg, part);
-    int st = check_launch("window stats pass 1");
+    const int L = d->n_layers, Hkv = d->n_kv_heads, Hq = d->n_q_heads;
+    auto p1 = [&]() -> int {
+#define P1(DD, NN) launch_pass1<DD, NN>(blocks, s, K, Q, T, W, G, L, Hkv, Hq, n_chunks, c2, wg, part)
+        if (d->head_dim == 128) {
+            KVC_NB_SWITCH(nb, 128, P1)
+        } else {
+            KVC_NB_SWITCH(nb, 64, P1)
+        }
+#undef P1
+    };
+    int st = p1();
     if (st != KVC_OK) return st;
-    score_merge<<<dim3((unsigned)rows_local), dim3(QRP), 0, s>>>(part, n_chunks, QR, QRP, mm);
+    score_merge<<<dim3((unsigned)rows_local), dim3(SCORE_THREADS), 0, s>>>(part, n_chunks, QR, QRP, mm);
     return check_launch("window stats merge");
 }
-
-int64_t window_chunks(int64_t kend) { return (kend + SCORE_CHUNK - 1) / SCORE_CHUNK; }
 
 }  // namespace kvc
 
@@ -257,36 +411,24 @@ extern "C" int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t
     const size_t need = score_workspace_bytes(dims, W);
     if (!ws || ws_bytes < need)
         return fail(KVC_ERR_WORKSPACE, "kvc_score: workspace %zu < %zu bytes", ws_bytes, need);
-
-    const ScoreGeom g = score_geom(dims, W);
-    const int64_t blocks = g.rows * g.n_chunks;
-    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_score: grid too large");
     float2 *part = reinterpret_cast<float2 *>(ws);
+    const int64_t rows = n_rows(dims), T = dims->n_tokens;
+    const int64_t n_chunks = window_chunks(T);
+    const int nb = (G * W + 31) / 32, QRP = nb * 32;
     float *mm = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
-                                          align256((size_t)g.rows * g.n_chunks * g.QRP * sizeof(float2)));
-    const float c2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
+                                          align256((size_t)rows * n_chunks * QRP * sizeof(float2)));
     hipStream_t s = as_stream(stream);
-    const int threads = g.nb * 64;
-    const size_t red_bytes = (size_t)g.nb * SCORE_CHUNK * sizeof(float);
+    st = launch_window_stats(dims, K, Q_obs, W, WindowGeom{T - W, T, -1}, rows, part, mm, s);
+    if (st != KVC_OK) return st;
+    const int64_t blocks = rows * n_chunks;
+    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_score: grid too large");
+    const float c2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
     const int L = dims->n_layers, Hkv = dims->n_kv_heads, Hq = dims->n_q_heads;
-    const int64_t T = dims->n_tokens;
-    const WindowGeom wgeo{T - W, T, -1};
+#define P2(DD, NN) launch_pass2<DD, NN>(blocks, s, K, Q_obs, T, W, G, L, Hkv, Hq, n_chunks, c2, mm, scores)
     if (dims->head_dim == 128) {
-        score_pass1<128><<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(K, Q_obs, T, W, G, L, Hkv, Hq,
-                                                                          g.n_chunks, c2, wgeo, part);
+        KVC_NB_SWITCH(nb, 128, P2)
     } else {
-        score_pass1<64><<<dim3((unsigned)blocks), dim3(threads), 0, s>>>(K, Q_obs, T, W, G, L, Hkv, Hq,
-                                                                         g.n_chunks, c2, wgeo, part);
+        KVC_NB_SWITCH(nb, 64, P2)
     }
-    if ((st = check_launch("kvc_score pass 1")) != KVC_OK) return st;
-    score_merge<<<dim3((unsigned)g.rows), dim3(g.QRP), 0, s>>>(part, g.n_chunks, g.QR, g.QRP, mm);
-    if ((st = check_launch("kvc_score merge")) != KVC_OK) return st;
-    if (dims->head_dim == 128) {
-        score_pass2<128><<<dim3((unsigned)blocks), dim3(threads), red_bytes, s>>>(
-            K, Q_obs, T, W, G, L, Hkv, Hq, g.n_chunks, c2, mm, scores);
-    } else {
-        score_pass2<64><<<dim3((unsigned)blocks), dim3(threads), red_bytes, s>>>(
-            K, Q_obs, T, W, G, L, Hkv, Hq, g.n_chunks, c2, mm, scores);
-    }
-    return check_launch("kvc_score pass 2");
+#undef P2
 }
