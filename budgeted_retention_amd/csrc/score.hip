@@ -72,6 +72,21 @@ __device__ __forceinline__ void load_key_tile(const uint16_t *Kr, int64_t key, i
     for (int s = 0; s < S; ++s) kf[s] = key < kend ? load8(Kr + (size_t)key * D + 16 * s + 8 * hf) : zero8();
 }
 
+// Loads the tile of keys [j0, j0 + 32) into registers; keys at or past kend
+// read the chunk's last key instead (the tile's consumer ignores them), so
+// every call issues the same loads and the next tile's loads can stay in
+// flight while this one is consumed.
+template <int S>
+__device__ __forceinline__ void load_tile_clamped(const uint16_t *Kr, int64_t j0, int64_t kend, int lane,
+                                                  bf16x8 (&kf)[S]) {
+    constexpr int D = S * 16;
+    int64_t key = j0 + (lane & 31);
+    if (key >= kend) key = kend - 1;
+    const uint16_t *p = Kr + (size_t)key * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < S; ++s) kf[s] = load8(p + 16 * s);
+}
+
 // Number of tiles of [k0, k0 + 32*ntiles) whose last key is <= qbase (visible
 // to every query row).
 __device__ __forceinline__ int visible_tiles(int64_t k0, int64_t qbase, int ntiles) {
@@ -81,20 +96,22 @@ __device__ __forceinline__ int visible_tiles(int64_t k0, int64_t qbase, int ntil
 
 // ---------------------------------------------------------------- pass 1
 
-// One 32-key tile for every query block: running max/exp-sum per query row
-// (this lane's query row is b*32 + col of block b).
+// One 32-key tile (in registers) for every query block: running max/exp-sum
+// per query row (this lane's query row is b*32 + col of block b). The blocks
+// go through a rolled loop to keep one accumulator live; the per-block state
+// m[], l[] rotates by one each iteration, so block b's state is always at
+// index 0 (static register indices) and the arrays are back in order after
+// NB iterations.
 template <int D, int NB, bool MASKED>
-__device__ __forceinline__ void p1_tile(const uint16_t *Kr, int64_t j0, int64_t kend, int lane, const uint4 *sq,
-                                        const int64_t *qpos, float c2, float *m, float *l) {
+__device__ __forceinline__ void p1_tile(const bf16x8 (&kf)[D / 16], int64_t j0, int lane, const uint4 *sq,
+                                        int64_t qbase, int W, int QR, float c2, float (&m)[NB], float (&l)[NB]) {
     constexpr int S = D / 16;
     const int col = lane & 31, hf = lane >> 5;
-    bf16x8 kf[S];
-    load_key_tile<S>(Kr, j0 + col, kend, hf, kf);
     // Re-read the queries from LDS every tile (an opaque lane offset keeps the
     // loads in the loop): holding all of them in registers would cost occupancy.
     int qoff = lane;
     asm volatile("" : "+v"(qoff));
-#pragma unroll
+#pragma unroll 1
     for (int b = 0; b < NB; ++b) {
         f32x16 acc = {};
 #pragma unroll
@@ -104,24 +121,37 @@ __device__ __forceinline__ void p1_tile(const uint16_t *Kr, int64_t j0, int64_t 
         }
         // acc[i] = logit of key j0 + acc_row(i, hf) for query row b*32 + col
         if (MASKED) {
+            // positions relative to qbase (masked tiles lie within W + 32 keys of it);
+            // padding query rows see no key
+            const int qr = b * 32 + col;
+            const int lim = qr < QR ? qr % W : -(1 << 30);
+            const int rel0 = (int)(j0 - qbase);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (j0 + acc_row(i, hf) > qpos[b]) acc[i] = -INFINITY;
+                if (rel0 + acc_row(i, hf) > lim) acc[i] = -INFINITY;
         }
         float tmax = acc[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[i]);
         tmax *= c2;
-        if (tmax > m[b]) {
-            l[b] *= __builtin_amdgcn_exp2f(m[b] - tmax);
-            m[b] = tmax;
+        float mc = m[0], lc = l[0];
+        if (tmax > mc) {
+            lc *= __builtin_amdgcn_exp2f(mc - tmax);
+            mc = tmax;
         }
         // A row with no visible key yet keeps m = -inf; its exponents are all -inf.
-        const float mb = (MASKED && m[b] == -INFINITY) ? 0.f : m[b];
+        const float mb = (MASKED && mc == -INFINITY) ? 0.f : mc;
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mb));
-        l[b] += sum;
+        lc += sum;
+#pragma unroll
+        for (int k = 0; k + 1 < NB; ++k) {
+            m[k] = m[k + 1];
+            l[k] = l[k + 1];
+        }
+        m[NB - 1] = mc;
+        l[NB - 1] = lc;
     }
 }
 
@@ -135,19 +165,39 @@ __device__ __forceinline__ void p1_chunk(const uint16_t *Kr, int64_t k0, int64_t
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 31, hf = lane >> 5;
     float m[NB], l[NB];
-    int64_t qpos[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         m[b] = -INFINITY;
         l[b] = 0.f;
-        const int qr = b * 32 + col;
-        qpos[b] = qr < QR ? qbase + qr % W : -1;
     }
     const int ntiles = (int)((k1 - k0 + 31) / 32);
     const int nvis = visible_tiles(k0, qbase, ntiles);
+    // tiles wave, wave+4, ...; the next tile's loads are in flight while the
+    // current one is computed (keys past k1 are masked out)
     int t = wave;
-    for (; t < nvis; t += SCORE_WAVES) p1_tile<D, NB, false>(Kr, k0 + 32 * t, k1, lane, sq, qpos, c2, m, l);
-    for (; t < ntiles; t += SCORE_WAVES) p1_tile<D, NB, true>(Kr, k0 + 32 * t, k1, lane, sq, qpos, c2, m, l);
+    if (t < ntiles) {
+        constexpr int S = D / 16;
+        auto tile = [&](const bf16x8(&kf)[S], int tt) {
+            if (tt < nvis)
+                p1_tile<D, NB, false>(kf, k0 + 32 * tt, lane, sq, qbase, W, QR, c2, m, l);
+            else
+                p1_tile<D, NB, true>(kf, k0 + 32 * tt, lane, sq, qbase, W, QR, c2, m, l);
+        };
+        const int last = ntiles - 1;
+        bf16x8 ka[S], kb[S];
+        load_tile_clamped<S>(Kr, k0 + 32 * t, k1, lane, ka);
+        for (;;) {
+            const int t1 = t + SCORE_WAVES;
+            load_tile_clamped<S>(Kr, k0 + 32 * (t1 < last ? t1 : last), k1, lane, kb);
+            tile(ka, t);
+            if (t1 > last) break;
+            const int t2 = t1 + SCORE_WAVES;
+            load_tile_clamped<S>(Kr, k0 + 32 * (t2 < last ? t2 : last), k1, lane, ka);
+            tile(kb, t1);
+            if (t2 > last) break;
+            t = t2;
+        }
+    }
     // Lanes l and l^32 hold the same query row over different keys; then the
     // waves of the workgroup hold it over different tiles.
 #pragma unroll
@@ -223,17 +273,16 @@ __device__ void merge_row(const float2 *part, int64_t nch, int QR, int QRP, floa
 
 // ---------------------------------------------------------------- pass 2
 
-// One 32-key tile: softmax weights of every query row for this lane's key,
-// summed; one query block at a time (interleaving blocks would hold several
-// accumulators and fragment sets live and cost occupancy).
+// One 32-key tile already in registers: softmax weights of every query row
+// for this lane's key, summed; one query block at a time (interleaving blocks
+// would hold several accumulators and fragment sets live and cost occupancy).
 template <int D, int NB, bool MASKED>
-__device__ __forceinline__ void p2_tile(const uint16_t *Kr, int64_t j0, int64_t kend, int lane, const uint4 *sq,
-                                        const float4 *s_mm, float c2, int64_t qbase, int W, float *out) {
+__device__ __forceinline__ void p2_tile(const bf16x8 (&kf)[D / 16], int64_t j0, int64_t kend, int lane,
+                                        const uint4 *sq, const float4 *s_mm, float c2, int64_t qbase, int W,
+                                        float *out) {
     constexpr int S = D / 16;
     const int col = lane & 31, hf = lane >> 5;
     const int64_t key = j0 + col;
-    bf16x8 kf[S];
-    load_key_tile<S>(Kr, key, kend, hf, kf);
     int qoff = lane, moff = hf;  // opaque offsets keep the LDS reads inside the loop
     asm volatile("" : "+v"(qoff), "+v"(moff));
     float p = 0.f;
@@ -257,7 +306,7 @@ __device__ __forceinline__ void p2_tile(const uint16_t *Kr, int64_t j0, int64_t 
                 float x = fmaf(acc[i], c2, -mvs[e]);
                 if (MASKED) {
                     const int qr = b * 32 + acc_row(i, hf);
-                    if (key > qbase + qr % W) x = -INFINITY;
+                    if ((int)(key - qbase) > qr % W) x = -INFINITY;
                 }
                 p += __builtin_amdgcn_exp2f(x);
             }
@@ -267,15 +316,37 @@ __device__ __forceinline__ void p2_tile(const uint16_t *Kr, int64_t j0, int64_t 
     if (hf == 0 && key < kend) out[key] = p;
 }
 
+// Pass 2 over keys [k0, k1): each wave walks its tiles (wave, wave+4, ...)
+// with the next tile's loads issued before the current tile is computed.
 template <int D, int NB>
 __device__ __forceinline__ void p2_chunk(const uint16_t *Kr, int64_t k0, int64_t k1, int64_t qbase, int W,
                                          float c2, const uint4 *sq, const float4 *s_mm, float *out) {
+    constexpr int S = D / 16;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ntiles = (int)((k1 - k0 + 31) / 32);
     const int nvis = visible_tiles(k0, qbase, ntiles);
     int t = wave;
-    for (; t < nvis; t += SCORE_WAVES) p2_tile<D, NB, false>(Kr, k0 + 32 * t, k1, lane, sq, s_mm, c2, qbase, W, out);
-    for (; t < ntiles; t += SCORE_WAVES) p2_tile<D, NB, true>(Kr, k0 + 32 * t, k1, lane, sq, s_mm, c2, qbase, W, out);
+    if (t >= ntiles) return;
+    auto tile = [&](const bf16x8(&kf)[S], int tt) {
+        if (tt < nvis)
+            p2_tile<D, NB, false>(kf, k0 + 32 * tt, k1, lane, sq, s_mm, c2, qbase, W, out);
+        else
+            p2_tile<D, NB, true>(kf, k0 + 32 * tt, k1, lane, sq, s_mm, c2, qbase, W, out);
+    };
+    const int last = ntiles - 1;
+    bf16x8 ka[S], kb[S];
+    load_tile_clamped<S>(Kr, k0 + 32 * t, k1, lane, ka);
+    for (;;) {
+        const int t1 = t + SCORE_WAVES;
+        load_tile_clamped<S>(Kr, k0 + 32 * (t1 < last ? t1 : last), k1, lane, kb);
+        tile(ka, t);
+        if (t1 > last) break;
+        const int t2 = t1 + SCORE_WAVES;
+        load_tile_clamped<S>(Kr, k0 + 32 * (t2 < last ? t2 : last), k1, lane, ka);
+        tile(kb, t1);
+        if (t2 > last) break;
+        t = t2;
+    }
 }
 
 // ---------------------------------------------------------------- kernels
