@@ -19,6 +19,8 @@
 // and four tag bytes when the row is 4-aligned); histogram increments are
 // aggregated per wave over equal digits, since the leading digits of a row's
 // scores fall into a handful of bins.
+#include <type_traits>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -42,25 +44,38 @@ __device__ int32_t device_layer_group(int32_t layer, int32_t n_layers, int32_t n
     return g;
 }
 
+// Cross-lane moves through DPP (VALU, no LDS round trip). Lanes whose source
+// falls outside the row read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, true);
+}
+static constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+static constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+static constexpr int DPP_HALF_MIRROR = 0x141;
+static constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118;
+static constexpr int DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143;
+
+// Inclusive scan of x over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += dpp<DPP_SHR1>(x);
+    x += dpp<DPP_SHR2>(x);
+    x += dpp<DPP_SHR4>(x);
+    x += dpp<DPP_SHR8>(x);
+    x += dpp<DPP_BCAST15, 0xA>(x);  // row r-1's last lane into rows 1 and 3
+    x += dpp<DPP_BCAST31, 0xC>(x);  // lane 31 into rows 2 and 3
+    return x;
+}
+
 // Exclusive block scan over SEL_THREADS threads; *total receives the sum.
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t *total, uint32_t *s_wave) {
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *total, uint32_t *s_wave) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) s_wave[wave] = x;
     __syncthreads();
     if (wave == 0) {
         const uint32_t w = lane < SEL_WAVES ? s_wave[lane] : 0u;
-        uint32_t c = w;
-#pragma unroll
-        for (int off = 1; off < SEL_WAVES; off <<= 1) {
-            const uint32_t y = __shfl_up(c, off);
-            if (lane >= off) c += y;
-        }
+        const uint32_t c = wave_incl_scan(w);
         if (lane < SEL_WAVES) s_wave[lane] = c - w;
         if (lane == SEL_WAVES - 1) s_wave[SEL_WAVES] = c;
     }
@@ -246,6 +261,453 @@ __global__ void __launch_bounds__(SEL_THREADS)
     if (tid == 0) n_kept[r] = (int32_t)(carry_gt + (carry_eq < need ? carry_eq : need));
 }
 
+// Candidate variant for rows whose decision bitmaps fit in LDS (T a multiple
+// of 4, 16-byte aligned rows). Every kept token is found among a short
+// candidate list, so the row's scores are streamed once instead of once per
+// radix digit:
+//   S. a sample (one 128-byte line in eight) places a lower-bound top digit
+//      d_lo whose tokens should number about 1.5 B;
+//   F. one pass over the row: the tokens with top digit >= d_lo are counted
+//      in the exact top-digit histogram and appended to an LDS candidate list;
+//   R. if they are at least B and fit the list, the histogram gives the bin of
+//      the budget-th key and the two low digits are resolved on the
+//      candidates alone; the kept candidates get bits in two LDS bitmaps
+//      ("above" tau, "equal" to tau);
+//   X. otherwise (a misleading sample, many equal scores) the exact path runs:
+//      a full histogram pass, the threshold bin's tokens as candidates (or
+//      streaming passes when they overflow), "above" bits written for whole
+//      words;
+//   D. each wave scans its contiguous bitmap words and expands the non-zero
+//      ones with 32 lanes per word: every "above" token and the first `need`
+//      "equal" tokens in index order, ascending.
+static constexpr int SEL_CAND = 8192;
+static constexpr int SEL_U = 4;  // float4 loads per thread per trip (two trips in flight)
+
+// ORs this lane's 4-bit nibble (tokens 4*lane .. 4*lane+3 of the wave's 256)
+// with those of its 8-lane group; lane 8g ends with the group's 32-bit word.
+__device__ __forceinline__ uint32_t group8_word(uint32_t nib, int lane) {
+    uint32_t w = nib << (4 * (lane & 7));
+    w |= dpp<DPP_XOR1>(w);
+    w |= dpp<DPP_XOR2>(w);
+    w |= dpp<DPP_HALF_MIRROR>(w);  // lane i <-> 7 - i: the other quad of the group
+    return w;
+}
+
+// Finds the bin where the count of keys from the top reaches `krank` (block-wide,
+// nbins <= 2*SEL_THREADS bins of hist); returns the bin and the rank within it.
+__device__ __forceinline__ void pick_bin(const uint32_t *hist, int nbins, uint32_t krank, uint32_t *s_wave,
+                                         uint32_t *s_pick, uint32_t &bin, uint32_t &rank) {
+    const int tid = threadIdx.x;
+    uint32_t cnt[2];
+    cnt[0] = 2 * tid < nbins ? hist[nbins - 1 - 2 * tid] : 0u;
+    cnt[1] = 2 * tid + 1 < nbins ? hist[nbins - 2 - 2 * tid] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(cnt[0] + cnt[1], &tot, s_wave);
+    if (tid == 0) {
+        s_pick[0] = 0u;  // not reached: bin 0
+        s_pick[1] = krank;
+    }
+    __syncthreads();
+    if (ex < krank && krank <= ex + cnt[0]) {
+        s_pick[0] = (uint32_t)(nbins - 1 - 2 * tid);
+        s_pick[1] = krank - ex;
+    } else if (ex + cnt[0] < krank && krank <= ex + cnt[0] + cnt[1]) {
+        s_pick[0] = (uint32_t)(nbins - 2 - 2 * tid);
+        s_pick[1] = krank - ex - cnt[0];
+    }
+    __syncthreads();
+    bin = s_pick[0];
+    rank = s_pick[1];
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(SEL_THREADS)
+    select_cand(const float *__restrict__ scores, const uint8_t *__restrict__ tags,
+                const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int64_t T, int L, int Hkv,
+                int n_groups, int layer_base, int n_layers_model, int n_tags, int n_sink, int n_recent, int B,
+                int32_t *__restrict__ kept, int kept_stride, int32_t *__restrict__ n_kept) {
+    __shared__ uint32_t hist[SEL_BINS];
+    __shared__ uint32_t s_wave[SEL_WAVES + 1];
+    __shared__ uint32_t s_wave2[SEL_WAVES + 1];
+    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_ncand;
+    __shared__ uint32_t s_tab[256];  // per tag: all ones = protected, else the bonus's float bits
+    extern __shared__ uint32_t s_dyn[];
+    const int Ti = (int)T, mwords = (Ti + 31) >> 5;
+    uint32_t *c_key = s_dyn;                    // [SEL_CAND]
+    uint32_t *c_idx = s_dyn + SEL_CAND;         // [SEL_CAND]
+    uint32_t *m_gt = s_dyn + 2 * SEL_CAND;      // [mwords] kept: above tau
+    uint32_t *m_eq = m_gt + mwords;             // [mwords] tie: equal to tau
+
+    const int64_t r = blockIdx.x;
+    const RowIdx ri = split_row(r, L, Hkv);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = device_layer_group(layer_base + ri.l, n_layers_model, n_groups);
+    for (int t = tid; t < 256; t += SEL_THREADS) {
+        const bool fl = floor_tbl && t < n_tags && floor_tbl[t * n_groups + grp];
+        const float bo = (bonus && t < n_tags) ? bonus[t * n_groups + grp] : 0.f;
+        s_tab[t] = fl ? KEY_PROTECTED : __float_as_uint(bo);
+    }
+    for (int t = tid; t < SEL_BINS; t += SEL_THREADS) hist[t] = 0u;
+    for (int t = tid; t < mwords; t += SEL_THREADS) {
+        m_gt[t] = 0u;
+        m_eq[t] = 0u;
+    }
+    if (tid == 0) s_ncand = 0u;
+    __syncthreads();
+    const float *sr = scores + (size_t)r * T;
+    const uint8_t *tr = tags ? tags + (size_t)ri.n * T : nullptr;
+    const int lo_prot = n_sink, hi_prot = Ti - n_recent;
+    // Keys of n groups of four tokens: all table lookups first (no branches
+    // between them), then the keys.
+    auto keys_of = [&](auto Nc, const float4 *sv, const uint32_t *tv, const int *base, uint32_t (*k)[SEL_VEC]) {
+        constexpr int N = decltype(Nc)::value;
+        uint32_t tab[N][SEL_VEC];
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) {
+                uint32_t tg = (tv[u] >> (8 * e)) & 0xFFu;
+                tg = tg < (uint32_t)n_tags ? tg : 0u;
+                tab[u][e] = s_tab[tg];
+            }
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const float x[SEL_VEC] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) {
+                const int j = base[u] + e;
+                const bool prot = j < lo_prot || j >= hi_prot || tab[u][e] == KEY_PROTECTED;
+                k[u][e] = prot ? KEY_PROTECTED : order_key(x[e] + __uint_as_float(tab[u][e]));
+            }
+        }
+    };
+    const int stride = SEL_THREADS * SEL_VEC;  // tokens per block step
+    // Streams the row: fn(base[SEL_U], keys[SEL_U][4]) once per trip of SEL_U
+    // 4-token groups per thread (groups with base >= T are padding); the next trip's scores and tags are loaded
+    // before this trip is processed (always issued, re-reading the last group
+    // past the end, so the loads in flight per wait are the same on every path).
+    // Every lane of a wave runs the same number of trips (fn may use wave-wide
+    // operations).
+    const int trips = (Ti + SEL_U * stride - 1) / (SEL_U * stride);
+    auto stream = [&](auto fn) {
+        float4 sa[SEL_U], sb[SEL_U];
+        uint32_t ta[SEL_U], tb[SEL_U];
+        auto fetch = [&](int it, float4 (&sv)[SEL_U], uint32_t (&tv)[SEL_U]) {
+#pragma unroll
+            for (int u = 0; u < SEL_U; ++u) {
+                int b = it * SEL_U * stride + u * stride + tid * SEL_VEC;
+                if (b >= Ti) b = Ti - SEL_VEC;
+                sv[u] = *reinterpret_cast<const float4 *>(sr + b);
+                tv[u] = tr ? *reinterpret_cast<const uint32_t *>(tr + b) : 0u;
+            }
+        };
+        auto consume = [&](int it, const float4 (&sv)[SEL_U], const uint32_t (&tv)[SEL_U]) {
+            int base[SEL_U];
+#pragma unroll
+            for (int u = 0; u < SEL_U; ++u) base[u] = it * SEL_U * stride + u * stride + tid * SEL_VEC;
+            uint32_t k[SEL_U][SEL_VEC];
+            keys_of(std::integral_constant<int, SEL_U>(), sv, tv, base, k);
+            fn(base, k);
+        };
+        fetch(0, sa, ta);
+        for (int it = 0; it < trips; it += 2) {
+            fetch(it + 1, sb, tb);
+            consume(it, sa, ta);
+            if (it + 1 >= trips) break;
+            fetch(it + 2, sa, ta);
+            consume(it + 1, sb, tb);
+        }
+    };
+    // per-group view of a trip: fn(base, ok, keys[4])
+    auto per_group = [&](auto fn) {
+        return [=](const int *base, uint32_t (*k)[SEL_VEC]) {
+#pragma unroll
+            for (int u = 0; u < SEL_U; ++u) fn(base[u], base[u] < Ti, k[u]);
+        };
+    };
+    // Appends a trip's flagged tokens (bit 4u+e of cmask) to the candidate
+    // list: a wave prefix sum over the lanes' counts and one LDS atomic per wave.
+    auto append = [&](const int *base, uint32_t cmask, uint32_t (*k)[SEL_VEC]) {
+        const uint32_t n = (uint32_t)__popc(cmask);
+        const uint64_t any = __ballot(n != 0u);
+        if (!any) return;
+        const uint32_t incl = wave_incl_scan(n);
+        uint32_t slot0 = 0;
+        if (lane == 63) slot0 = atomicAdd(&s_ncand, incl);
+        slot0 = __builtin_amdgcn_readlane(slot0, 63);
+        uint32_t slot = slot0 + incl - n;
+#pragma unroll
+        for (int u = 0; u < SEL_U; ++u)
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e)
+                if ((cmask >> (SEL_VEC * u + e)) & 1u) {
+                    if (slot < SEL_CAND) {
+                        c_key[slot] = k[u][e];
+                        c_idx[slot] = (uint32_t)(base[u] + e);
+                    }
+                    ++slot;
+                }
+    };
+    // Resolves digits [20:10] and [9:0] below the top digit pick0 and returns
+    // tau and the number of tau-valued tokens to keep; over the candidates, or
+    // over the stream when they overflowed.
+    auto low_digits = [&](uint32_t pick0, uint32_t krank, bool from_cands, uint32_t ncand, uint32_t &tau_out,
+                          int &need_out) {
+        uint32_t prefix = pick0;
+        for (int pass = 1; pass < 3; ++pass) {
+            const int shift = pass == 1 ? 10 : 0;
+            const int width = pass == 1 ? 11 : 10;
+            const uint32_t mask = (1u << width) - 1u;
+            for (int t = tid; t < SEL_BINS; t += SEL_THREADS) hist[t] = 0u;
+            __syncthreads();
+            if (from_cands) {
+                for (uint32_t c = tid; c < ncand; c += SEL_THREADS) {
+                    const uint32_t kv = c_key[c];
+                    if ((kv >> (shift + width)) == prefix) atomicAdd(&hist[(kv >> shift) & mask], 1u);
+                }
+            } else {
+                stream(per_group([&](int, bool ok, const uint32_t *k) {
+#pragma unroll
+                    for (int e = 0; e < SEL_VEC; ++e)
+                        if (ok && (k[e] >> (shift + width)) == prefix) atomicAdd(&hist[(k[e] >> shift) & mask], 1u);
+                }));
+            }
+            __syncthreads();
+            uint32_t bin;
+            pick_bin(hist, 1 << width, krank, s_wave, s_pick, bin, krank);
+            prefix = (prefix << width) | bin;
+        }
+        tau_out = prefix;
+        need_out = (int)krank;
+    };
+
+    uint32_t tau = 0u;
+    int need = Ti;
+    if (T <= B) {
+        // every token is kept
+        for (int w = tid; w < mwords; w += SEL_THREADS) {
+            const int left = Ti - 32 * w;
+            m_gt[w] = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+        }
+        __syncthreads();
+    } else {
+        // S: sample one 128-byte line (32 tokens) in eight into the histogram
+        bool fast = false;
+        uint32_t d_lo = 0u;
+        {
+            const int lines = (Ti + 255) / 256;  // sampled lines start at 256*i
+            for (int g0 = 0; g0 < lines * 8; g0 += SEL_U * SEL_THREADS) {
+                float4 sv[SEL_U];
+                uint32_t tv[SEL_U];
+                int base[SEL_U];
+#pragma unroll
+                for (int u = 0; u < SEL_U; ++u) {
+                    const int g = g0 + u * SEL_THREADS + tid;
+                    base[u] = (g >> 3) * 256 + (g & 7) * SEL_VEC;
+                    const int b = base[u] < Ti ? base[u] : Ti - SEL_VEC;
+                    sv[u] = *reinterpret_cast<const float4 *>(sr + b);
+                    tv[u] = tr ? *reinterpret_cast<const uint32_t *>(tr + b) : 0u;
+                }
+                uint32_t k[SEL_U][SEL_VEC];
+                keys_of(std::integral_constant<int, SEL_U>(), sv, tv, base, k);
+#pragma unroll
+                for (int u = 0; u < SEL_U; ++u) {
+                    if (base[u] >= Ti) continue;
+                    uint32_t c0 = 1;
+#pragma unroll
+                    for (int e = 1; e < SEL_VEC; ++e) c0 += (k[u][e] >> 21) == (k[u][0] >> 21);
+                    atomicAdd(&hist[k[u][0] >> 21], c0);
+#pragma unroll
+                    for (int e = 1; e < SEL_VEC; ++e)
+                        if ((k[u][e] >> 21) != (k[u][0] >> 21)) atomicAdd(&hist[k[u][e] >> 21], 1u);
+                }
+            }
+            __syncthreads();
+            // aim at about 1.5 B tokens at or above d_lo (the sample holds one in eight)
+            const uint32_t target = (uint32_t)((3 * (int64_t)B + 15) / 16) + 8;
+            uint32_t rank;
+            pick_bin(hist, SEL_BINS, target, s_wave, s_pick, d_lo, rank);
+            for (int t = tid; t < SEL_BINS; t += SEL_THREADS) hist[t] = 0u;
+            __syncthreads();
+        }
+        // F: exact histogram of the tokens at or above d_lo, appended as candidates
+        stream([&](const int *base, uint32_t (*k)[SEL_VEC]) {
+            uint32_t cmask = 0;
+#pragma unroll
+            for (int u = 0; u < SEL_U; ++u)
+#pragma unroll
+                for (int e = 0; e < SEL_VEC; ++e) {
+                    const uint32_t d = k[u][e] >> 21;
+                    if (base[u] < Ti && d >= d_lo) {
+                        atomicAdd(&hist[d], 1u);
+                        cmask |= 1u << (SEL_VEC * u + e);
+                    }
+                }
+            append(base, cmask, k);
+        });
+        __syncthreads();
+        const uint32_t ncand = s_ncand;
+        fast = ncand >= (uint32_t)B && ncand <= (uint32_t)SEL_CAND;
+        if (fast) {
+            // R: every kept token is a candidate
+            const bool all_protected = hist[SEL_BINS - 1] >= (uint32_t)B;
+            uint32_t pick0 = 0u, krank = (uint32_t)B;
+            if (all_protected) {
+                tau = KEY_PROTECTED;
+            } else {
+                pick_bin(hist, SEL_BINS, (uint32_t)B, s_wave, s_pick, pick0, krank);
+                low_digits(pick0, krank, true, ncand, tau, need);
+            }
+            for (uint32_t c = tid; c < ncand; c += SEL_THREADS) {
+                const uint32_t kv = c_key[c], j = c_idx[c];
+                if (all_protected) {
+                    if (kv == KEY_PROTECTED) atomicOr(&m_gt[j >> 5], 1u << (j & 31));
+                } else if (kv > tau) {
+                    atomicOr(&m_gt[j >> 5], 1u << (j & 31));
+                } else if (kv == tau) {
+                    atomicOr(&m_eq[j >> 5], 1u << (j & 31));
+                }
+            }
+            __syncthreads();
+        } else {
+            // X: the exact path over the whole row
+            for (int t = tid; t < SEL_BINS; t += SEL_THREADS) hist[t] = 0u;
+            if (tid == 0) s_ncand = 0u;
+            __syncthreads();
+            stream(per_group([&](int, bool ok, const uint32_t *k) {
+                if (!ok) return;
+                uint32_t d[SEL_VEC];
+#pragma unroll
+                for (int e = 0; e < SEL_VEC; ++e) d[e] = k[e] >> 21;
+                uint32_t c0 = 1;
+#pragma unroll
+                for (int e = 1; e < SEL_VEC; ++e) c0 += d[e] == d[0];
+                atomicAdd(&hist[d[0]], c0);
+#pragma unroll
+                for (int e = 1; e < SEL_VEC; ++e)
+                    if (d[e] != d[0]) atomicAdd(&hist[d[e]], 1u);
+            }));
+            __syncthreads();
+            const bool all_protected = hist[SEL_BINS - 1] >= (uint32_t)B;
+            uint32_t pick0 = 0u, krank = (uint32_t)B;
+            if (!all_protected) pick_bin(hist, SEL_BINS, (uint32_t)B, s_wave, s_pick, pick0, krank);
+            // "above" bits for whole words, the threshold bin's tokens as candidates
+            stream([&](const int *base, uint32_t (*k)[SEL_VEC]) {
+                uint32_t cmask = 0;
+#pragma unroll
+                for (int u = 0; u < SEL_U; ++u) {
+                    const bool ok = base[u] < Ti;
+                    uint32_t nib = 0;
+                    if (ok) {
+#pragma unroll
+                        for (int e = 0; e < SEL_VEC; ++e) {
+                            bool f;
+                            if (all_protected)
+                                f = k[u][e] == KEY_PROTECTED;
+                            else {
+                                const uint32_t d0 = k[u][e] >> 21;
+                                f = d0 > pick0;
+                                cmask |= (uint32_t)(d0 == pick0) << (SEL_VEC * u + e);
+                            }
+                            nib |= (uint32_t)f << e;
+                        }
+                    }
+                    // the wave's 256 tokens of group u are 8 consecutive words; past T nothing is written
+                    const uint32_t w = group8_word(nib, lane);
+                    if ((lane & 7) == 0 && ok) m_gt[base[u] >> 5] = w;
+                }
+                append(base, cmask, k);
+            });
+            __syncthreads();
+            if (all_protected) {
+                tau = KEY_PROTECTED;
+            } else {
+                const uint32_t nc = s_ncand;
+                const bool fits = nc <= (uint32_t)SEL_CAND;
+                low_digits(pick0, krank, fits, nc, tau, need);
+                if (fits) {
+                    for (uint32_t c = tid; c < nc; c += SEL_THREADS) {
+                        const uint32_t kv = c_key[c], j = c_idx[c];
+                        if (kv > tau) atomicOr(&m_gt[j >> 5], 1u << (j & 31));
+                        else if (kv == tau) atomicOr(&m_eq[j >> 5], 1u << (j & 31));
+                    }
+                } else {
+                    stream(per_group([&](int base, bool ok, const uint32_t *k) {
+#pragma unroll
+                        for (int e = 0; e < SEL_VEC; ++e) {
+                            const int j = base + e;
+                            if (ok && (k[e] >> 21) == pick0) {
+                                if (k[e] > tau) atomicOr(&m_gt[j >> 5], 1u << (j & 31));
+                                else if (k[e] == tau) atomicOr(&m_eq[j >> 5], 1u << (j & 31));
+                            }
+                        }
+                    }));
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // D: wave w owns the contiguous words [w*WPW, (w+1)*WPW), taken 64 at a time
+    const int WPW = (mwords + SEL_WAVES - 1) / SEL_WAVES;
+    const int wbeg = wave * WPW, wend = wbeg + WPW < mwords ? wbeg + WPW : mwords;
+    const int rounds = (WPW + 63) / 64;
+    uint32_t cg = 0, ce = 0;
+    for (int rr = 0; rr < rounds; ++rr) {
+        const int w = wbeg + rr * 64 + lane;
+        if (w < wend) {
+            cg += __popc(m_gt[w]);
+            ce += __popc(m_eq[w]);
+        }
+    }
+    const uint32_t wsum_g = __builtin_amdgcn_readlane(wave_incl_scan(cg), 63);
+    const uint32_t wsum_e = __builtin_amdgcn_readlane(wave_incl_scan(ce), 63);
+    if (lane == 0) {
+        s_wave[wave] = wsum_g;
+        s_wave2[wave] = wsum_e;
+    }
+    __syncthreads();
+    uint32_t base_g = 0, base_e = 0, tot_g = 0, tot_e = 0;
+    for (int v = 0; v < SEL_WAVES; ++v) {
+        if (v < wave) {
+            base_g += s_wave[v];
+            base_e += s_wave2[v];
+        }
+        tot_g += s_wave[v];
+        tot_e += s_wave2[v];
+    }
+    int32_t *kr = kept + (size_t)r * kept_stride;
+    for (int rr = 0; rr < rounds; ++rr) {
+        const int w = wbeg + rr * 64 + lane;
+        const uint32_t g = w < wend ? m_gt[w] : 0u, q = w < wend ? m_eq[w] : 0u;
+        const uint32_t ig = wave_incl_scan((uint32_t)__popc(g)), ie = wave_incl_scan((uint32_t)__popc(q));
+        const uint32_t gb = base_g + ig - __popc(g), eb = base_e + ie - __popc(q);  // before this word
+        uint64_t live = __ballot((g | q) != 0u);
+        while (live) {
+            const int src = __ffsll((unsigned long long)live) - 1;
+            live &= live - 1ull;
+            const uint32_t G = __builtin_amdgcn_readlane(g, src), E = __builtin_amdgcn_readlane(q, src);
+            const int GB = (int)__builtin_amdgcn_readlane(gb, src), EB = (int)__builtin_amdgcn_readlane(eb, src);
+            const int W = __builtin_amdgcn_readlane(w, src);
+            if (lane < 32) {
+                const uint32_t bit = 1u << lane, below = bit - 1u;
+                const int gpos = GB + __popc(G & below), erank = EB + __popc(E & below);
+                if (G & bit) {
+                    const int pos = gpos + (erank < need ? erank : need);
+                    if (pos < kept_stride) kr[pos] = 32 * W + lane;
+                } else if ((E & bit) && erank < need) {
+                    const int pos = gpos + erank;
+                    if (pos < kept_stride) kr[pos] = 32 * W + lane;
+                }
+            }
+        }
+        base_g += __builtin_amdgcn_readlane(ig, 63);
+        base_e += __builtin_amdgcn_readlane(ie, 63);
+    }
+    if (tid == 0) n_kept[r] = (int32_t)(tot_g + (tot_e < (uint32_t)need ? tot_e : (uint32_t)need));
+}
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -277,7 +739,21 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
                      (!p->tags || reinterpret_cast<uintptr_t>(p->tags) % 4 == 0);
     const dim3 grid((unsigned)n_rows(dims)), block(SEL_THREADS);
     hipStream_t s = as_stream(stream);
-    if (vec)
+    // rows whose decision map fits in LDS next to the candidate list
+    const size_t cand_lds = (size_t)2 * SEL_CAND * sizeof(uint32_t) + (size_t)2 * ((T + 31) / 32) * sizeof(uint32_t);
+    if (vec && cand_lds <= 144 * 1024) {
+        static bool lds_set = false;
+        if (!lds_set) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(&select_cand),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 144 * 1024) != hipSuccess)
+                return fail(KVC_ERR_HIP, "kvc_select: cannot raise the LDS limit");
+            lds_set = true;
+        }
+        select_cand<<<grid, block, cand_lds, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
+                                                  dims->n_kv_heads, p->n_groups, p->layer_base, p->n_layers_model,
+                                                  p->n_tags, p->n_sink, p->n_recent, p->budget, kept_idx,
+                                                  kept_stride, n_kept);
+    } else if (vec)
         select_kernel<true><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                     dims->n_kv_heads, p->n_groups, p->layer_base,
                                                     p->n_layers_model, p->n_tags, p->n_sink, p->n_recent,
