@@ -36,7 +36,10 @@ namespace kvc {
 static constexpr int SCORE_WAVES = 4;  // waves per workgroup
 static constexpr int SCORE_THREADS = SCORE_WAVES * 64;
 static constexpr int SCORE_MAX_QR = 256;  // query rows per row (8 blocks of 32)
-static constexpr int STATS_CHUNK = 2048;  // keys per workgroup of both passes
+#ifndef KVC_STATS_CHUNK
+#define KVC_STATS_CHUNK 4096
+#endif
+static constexpr int STATS_CHUNK = KVC_STATS_CHUNK;  // keys per workgroup of both passes
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
