@@ -42,7 +42,7 @@ class KvcPolicy(ctypes.Structure):
 
 class KvcCompactOut(ctypes.Structure):
     _fields_ = [
-        ("action", c_void_p), ("out_stride", c_int32), ("reserved", c_int32),
+        ("action", c_void_p), ("out_stride", c_int32), ("kept_page", c_int32),
         ("h_base", c_void_p), ("l_base", c_void_p),
         ("K_out", c_void_p), ("V_out", c_void_p), ("pos_out", c_void_p), ("n_h", c_void_p),
         ("Kq", c_void_p), ("Vq", c_void_p), ("Ks", c_void_p), ("Vs", c_void_p),
@@ -82,6 +82,8 @@ PROTOTYPES = {
                                        c_int32, c_int64, c_int32, c_int32, c_void_p, c_int32,
                                        ctypes.c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
+    "kvc_page_scores": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_int32, c_void_p,
+                                       c_void_p, c_int32, c_void_p, c_void_p]),
     "kvc_host_pask_costs": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "kvc_host_pask_control": (ctypes.c_int, [ctypes.POINTER(KvcPaskTable), c_void_p, c_double, c_double,
                                              c_void_p, c_int32, c_int32, c_void_p, c_void_p]),

@@ -101,8 +101,8 @@ struct CompactArgs {
     const uint16_t *K, *V;
     const int32_t *pos_in, *kept, *n_kept;
     const uint8_t *action;
-    int64_t T;
-    int kept_stride, out_stride, renumber_base;
+    int64_t T, rows_per_seq;
+    int kept_stride, out_stride, renumber_base, kept_page;
     double rope_base;
     uint16_t *Ko, *Vo;
     int32_t *po, *nh;
@@ -118,9 +118,12 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
     constexpr int TOK = CMP_THREADS / TPT;
     const int64_t r = blockIdx.x / blocks_per_row;
     const int cb = blockIdx.x % blocks_per_row;
-    int n = a.n_kept[r];
+    const int kp = a.kept_page;
+    const int64_t kr = kp ? r / a.rows_per_seq : r;  // row of the kept list
+    int n = a.n_kept[kr];
     if (n > a.kept_stride) n = a.kept_stride;
     if (n < 0) n = 0;
+    if (kp) n *= kp;
     int base = a.h_base ? a.h_base[r] : 0;
     if (base < 0) base = 0;
     const int room = a.out_stride - base > 0 ? a.out_stride - base : 0;
@@ -134,7 +137,13 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         th1 = pow(a.rope_base, -2.0 * (2 * sub + 1) / D);
     }
     for (int rho = cb * TOK + tin; rho < n; rho += blocks_per_row * TOK) {
-        const int64_t j = a.kept[(size_t)r * a.kept_stride + rho];
+        int64_t j;
+        if (kp) {
+            const int64_t e = a.kept[(size_t)kr * a.kept_stride + rho / kp];
+            j = e < 0 ? -1 : e * kp + rho % kp;
+        } else {
+            j = a.kept[(size_t)kr * a.kept_stride + rho];
+        }
         if (j < 0 || j >= a.T) continue;
         const size_t src = ((size_t)r * a.T + j) * D;
         const size_t dst = ((size_t)r * a.out_stride + base + rho) * D;
@@ -282,12 +291,18 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     if (st != KVC_OK) return st;
     if (!K || !V || !kept_idx || !n_kept || !out)
         return fail(KVC_ERR_ARG, "kvc_compact_rerotate: NULL pointer");
-    if (kept_stride <= 0 || out->out_stride <= 0 || out->reserved != 0)
-        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: strides must be positive (kept %d, out %d)",
-                    kept_stride, out->out_stride);
+    if (kept_stride <= 0 || out->out_stride <= 0 || out->kept_page < 0)
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: strides must be positive (kept %d, out %d, page %d)",
+                    kept_stride, out->out_stride, out->kept_page);
+    if (out->kept_page > 0 && out->action)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_compact_rerotate: shared page lists take no action array");
+    if ((int64_t)kept_stride * (out->kept_page > 0 ? out->kept_page : 1) > (int64_t)INT32_MAX)
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: kept tokens overflow int32");
     if (renumber_base >= 0 && !(rope_base > 1.0))
         return fail(KVC_ERR_ARG, "kvc_compact_rerotate: rope_base %g must exceed 1", rope_base);
-    if (renumber_base >= 0 && (int64_t)renumber_base + kept_stride > (int64_t)INT32_MAX)
+    if (renumber_base >= 0 &&
+        (int64_t)renumber_base + (int64_t)kept_stride * (out->kept_page > 0 ? out->kept_page : 1) >
+            (int64_t)INT32_MAX)
         return fail(KVC_ERR_ARG, "kvc_compact_rerotate: renumbered positions overflow int32");
     if (out->action) {
         if (!out->Kq || !out->Vq || !out->Ks || !out->Vs || !out->K_out || !out->V_out)
@@ -303,6 +318,8 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     a.n_kept = n_kept;
     a.action = out->action;
     a.T = dims->n_tokens;
+    a.rows_per_seq = (int64_t)dims->n_layers * dims->n_kv_heads;
+    a.kept_page = out->kept_page;
     a.kept_stride = kept_stride;
     a.out_stride = out->out_stride;
     a.renumber_base = renumber_base;
@@ -323,7 +340,8 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     hipStream_t s = as_stream(stream);
     if (!out->action) {
         const int tok = CMP_THREADS / (dims->head_dim / 4);
-        const int cap = kept_stride < out->out_stride ? kept_stride : out->out_stride;
+        const int64_t listed = (int64_t)kept_stride * (out->kept_page > 0 ? out->kept_page : 1);
+        const int cap = (int)(listed < out->out_stride ? listed : out->out_stride);
         int bpr = (cap + 4 * tok - 1) / (4 * tok);  // about 4 tokens per group
         if (bpr < 1) bpr = 1;
         if (rows * bpr > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_compact_rerotate: grid too large");

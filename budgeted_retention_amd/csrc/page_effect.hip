@@ -22,6 +22,12 @@
 //      the caller's candidate order, one workgroup per sequence; a candidate is
 //      accepted iff the effect of deleting it together with the pages already
 //      accepted stays within tau_joint.
+//
+// kvc_page_scores serves the compression checkpoint that follows (CommitKV
+// §3.3, Eq. 13 with Eq. 4): one page score per sequence, the window score of
+// every token summed over the page's tokens and over all layers and KV heads,
+// so that one page set can be kept for the whole sequence; pages accepted for
+// retirement are scored -inf.
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -454,6 +460,57 @@ static int pe_prepare(const kvc_dims *dims, const PeArgs &a, const PageWs &w, hi
 
 using namespace kvc;
 
+// One workgroup per (sequence, run of whole pages of at most PS_TOK tokens):
+// every thread sums its tokens over the sequence's L*Hkv score rows (rows in
+// order, coalesced across the workgroup), then one thread per page sums the
+// page's tokens in order. Fixed summation order: the result is deterministic.
+static constexpr int PS_THREADS = 256;
+static constexpr int PS_TOK = 1024;
+
+__global__ void __launch_bounds__(PS_THREADS)
+page_score_kernel(const float *scores, int64_t T, int64_t rows_per_seq, int page_size, int n_pages,
+                  int pages_per_block, int blocks_per_seq, const int32_t *order,
+                  const uint8_t *accepted, int n_cand, float *page_score) {
+    __shared__ float s_tok[PS_TOK];
+    __shared__ uint8_t s_ret[PS_TOK];
+    const int n = blockIdx.x / blocks_per_seq;
+    const int p0 = (blockIdx.x % blocks_per_seq) * pages_per_block;
+    const int np = min(pages_per_block, n_pages - p0);
+    const int64_t t0 = (int64_t)p0 * page_size;
+    const int ntok = np * page_size;
+    const int tid = threadIdx.x;
+    const float *base = scores + (int64_t)n * rows_per_seq * T + t0;
+    constexpr int PER = PS_TOK / PS_THREADS;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+#pragma unroll 4
+    for (int64_t r = 0; r < rows_per_seq; ++r) {
+        const float *row = base + r * T;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int t = tid + k * PS_THREADS;
+            if (t < ntok) acc[k] += row[t];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) s_tok[tid + k * PS_THREADS] = acc[k];
+    for (int e = tid; e < PS_TOK; e += PS_THREADS) s_ret[e] = 0;
+    __syncthreads();
+    if (order && accepted) {
+        for (int c = tid; c < n_cand; c += PS_THREADS) {
+            const int e = order[(int64_t)n * n_cand + c];
+            if (accepted[(int64_t)n * n_cand + c] && e >= p0 && e < p0 + np) s_ret[e - p0] = 1;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < np; e += PS_THREADS) {
+        float sum = 0.f;
+        for (int i = 0; i < page_size; ++i) sum += s_tok[e * page_size + i];
+        page_score[(int64_t)n * n_pages + p0 + e] = s_ret[e] ? -INFINITY : sum;
+    }
+}
+
 extern "C" size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int64_t q_first) {
     if (check_dims(dims, "kvc_page_workspace_bytes") != KVC_OK) return 0;
     if (W <= 0 || q_first < 0) {
@@ -522,4 +579,27 @@ extern "C" int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16
         pe_retire<64><<<dim3(dims->n_seq), dim3(PR_THREADS), 0, s>>>(a, order, n_cand, tau_joint, w.accD,
                                                                       w.alphaD, accepted, joint_rel);
     return check_launch("kvc_page_retire");
+}
+
+extern "C" int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_t page_size,
+                               int32_t n_pages, const int32_t *order, const uint8_t *accepted,
+                               int32_t n_cand, float *page_score, void *stream) {
+    int st = check_dims(dims, "kvc_page_scores");
+    if (st != KVC_OK) return st;
+    if (!scores || !page_score) return fail(KVC_ERR_ARG, "kvc_page_scores: NULL tensor pointer");
+    if (page_size <= 0 || page_size > PS_TOK)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_page_scores: page_size %d outside [1, %d]", page_size, PS_TOK);
+    if (n_pages <= 0 || (int64_t)n_pages * page_size > dims->n_tokens)
+        return fail(KVC_ERR_ARG, "kvc_page_scores: %d pages of %d tokens exceed the cache", n_pages, page_size);
+    if ((order == nullptr) != (accepted == nullptr) || (order && n_cand <= 0))
+        return fail(KVC_ERR_ARG, "kvc_page_scores: order and accepted go together, with n_cand > 0");
+    const int ppb = PS_TOK / page_size;
+    const int bps = (n_pages + ppb - 1) / ppb;
+    const int64_t blocks = (int64_t)dims->n_seq * bps;
+    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_scores: grid too large");
+    const int64_t rows_per_seq = (int64_t)dims->n_layers * dims->n_kv_heads;
+    page_score_kernel<<<dim3((unsigned)blocks), dim3(PS_THREADS), 0, as_stream(stream)>>>(
+        scores, dims->n_tokens, rows_per_seq, page_size, n_pages, ppb, bps, order, accepted,
+        order ? n_cand : 0, page_score);
+    return check_launch("kvc_page_scores");
 }

@@ -129,10 +129,11 @@ class CompactOut:
     n_l: Optional[torch.Tensor] = None
     h_base: Optional[torch.Tensor] = None      # int32 [rows] first bf16 slot (append)
     l_base: Optional[torch.Tensor] = None      # int32 [rows] first int8 slot (append)
+    kept_page: int = 0                         # > 0: kept lists are per-sequence page indices
 
     def to_c(self):
         return _lib.KvcCompactOut(
-            _ptr(self.action, torch.uint8, "action"), self.out_stride, 0,
+            _ptr(self.action, torch.uint8, "action"), self.out_stride, self.kept_page,
             _ptr(self.h_base, torch.int32, "h_base"), _ptr(self.l_base, torch.int32, "l_base"),
             _ptr(self.K_out, torch.bfloat16, "K_out"), _ptr(self.V_out, torch.bfloat16, "V_out"),
             _ptr(self.pos_out, torch.int32, "pos_out"), _ptr(self.n_h, torch.int32, "n_h"),
@@ -198,6 +199,15 @@ def kvc_page_retire(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, or
         _ptr(order, torch.int32, "order"), n_cand, float(tau_joint), _ptr(accepted, torch.uint8, "accepted"),
         _ptr(joint_rel, torch.float32, "joint_rel"), _ptr(ws, None, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    return _lib.check(st)
+
+
+def kvc_page_scores(dims, scores, page_size, n_pages, page_score, order=None, accepted=None, stream=None):
+    n_cand = 0 if order is None else order.shape[-1]
+    st = _lib.load().kvc_page_scores(
+        ctypes.byref(dims), _ptr(scores, torch.float32, "scores"), page_size, n_pages,
+        _ptr(order, torch.int32, "order"), _ptr(accepted, torch.uint8, "accepted"), n_cand,
+        _ptr(page_score, torch.float32, "page_score"), _stream(stream))
     return _lib.check(st)
 
 

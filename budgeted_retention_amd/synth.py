@@ -233,3 +233,207 @@ def kept_and_actions(rows, T, n_keep, seed=17, with_actions=True):
         kept[r, : n[r]] = np.sort(rng.choice(T, n[r], replace=False))
     act = rng.integers(0, 3, (rows, n_keep)).astype(np.uint8) if with_actions else None
     return kept, n, act
+
+
+# ---------------------------------------------------------------- PASK-style mixed precision
+
+@dataclass(frozen=True)
+class PaskWorkload:
+    """Batch of structured-generation requests: a prompt compacted by window
+    scoring, then generated tokens whose structural tags drive per-layer-group
+    release / int8 / bf16 actions."""
+    name: str = "pask_llama3_8b"
+    n_seq: int = 64
+    n_layers: int = 32
+    n_groups: int = 4
+    n_kv_heads: int = 8
+    n_q_heads: int = 32
+    head_dim: int = 128
+    n_prompt: int = 4096
+    n_gen: int = 1024
+    window: int = 32
+    n_sink: int = 4
+    n_recent: int = 128          # prompt tokens protected at the end of the prompt
+    budget: int = 1365           # prompt tokens kept per row
+    gen_recent: int = 128        # last generated tokens held in bf16 whatever their action
+    n_tags: int = 8
+    stay: float = 5.0 / 6.0      # Markov chain: P(next tag = current tag); mean run 6
+    n_critical: int = 2
+    budget_fraction: float = 1.0 / 3.0
+    rope_base: float = 5e5
+    seed: int = 20261204
+
+    @property
+    def rows(self):
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+
+PASK_WORKLOADS = {
+    "pask_llama3_8b": PaskWorkload(),
+    # same structure at a size the float64 oracle checks row by row in seconds
+    "pask_small": PaskWorkload("pask_small", n_seq=3, n_layers=4, n_groups=4, n_kv_heads=2, n_q_heads=8,
+                               head_dim=128, n_prompt=640, n_gen=300, window=16, n_recent=32,
+                               budget=213, gen_recent=32, seed=20261214),
+}
+
+
+def tag_chain(rng, n_seq, n_tok, n_tags, stay):
+    """Per sequence an n_tags-state Markov chain: the first tag uniform, then the
+    same tag with probability `stay`, else uniform over the other tags."""
+    tags = np.zeros((n_seq, n_tok), np.uint8)
+    for n in range(n_seq):
+        z = int(rng.integers(0, n_tags))
+        moves = rng.random(n_tok) >= stay
+        jumps = rng.integers(1, n_tags, n_tok)
+        for t in range(n_tok):
+            if t and moves[t]:
+                z = (z + int(jumps[t])) % n_tags
+            tags[n, t] = z
+    return tags
+
+
+def pask_table(rng, n_tags, n_groups, n_critical):
+    """Frozen [tag x layer group] table: base action a0 uniform over {R, L, H},
+    floor amin <= a0, upgrade priorities U(0,1) for R->L and L->H, and
+    `n_critical` critical tags."""
+    a0 = rng.integers(0, 3, (n_tags, n_groups)).astype(np.uint8)
+    amin = np.minimum(a0, rng.integers(0, 3, (n_tags, n_groups))).astype(np.uint8)
+    prio = rng.random((n_tags, n_groups, 2)).astype(np.float32)
+    crit = np.zeros(n_tags, np.uint8)
+    crit[rng.choice(n_tags, n_critical, replace=False)] = 1
+    return a0, amin, prio, crit
+
+
+@dataclass
+class PaskInputs:
+    w: PaskWorkload
+    K: torch.Tensor       # bf16 [N][L][Hkv][n_prompt][d] prompt keys
+    V: torch.Tensor
+    Q_obs: torch.Tensor   # bf16 [N][L][Hq][W][d] last W prompt queries
+    K_gen: torch.Tensor   # bf16 [N][L][Hkv][n_gen][d] generated tokens' keys
+    V_gen: torch.Tensor
+    q_dec: torch.Tensor   # bf16 [N][L][Hq][d] query at position n_prompt + n_gen
+    tags: np.ndarray      # uint8 [N][n_gen]
+    a0: np.ndarray
+    amin: np.ndarray
+    prio: np.ndarray
+    critical: np.ndarray
+
+
+def make_pask_inputs(w: PaskWorkload, device="cpu") -> PaskInputs:
+    N, L, Hkv, Hq, d = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
+    s = w.seed * 16
+    K = normal_bf16((N, L, Hkv, w.n_prompt, d), s + 1, device)
+    V = normal_bf16((N, L, Hkv, w.n_prompt, d), s + 2, device)
+    Q = normal_bf16((N, L, Hq, w.window, d), s + 3, device)
+    Kg = normal_bf16((N, L, Hkv, w.n_gen, d), s + 4, device)
+    Vg = normal_bf16((N, L, Hkv, w.n_gen, d), s + 5, device)
+    qd = normal_bf16((N, L, Hq, d), s + 6, device)
+    rng = np.random.default_rng(w.seed + 29)
+    tags = tag_chain(rng, N, w.n_gen, w.n_tags, w.stay)
+    a0, amin, prio, crit = pask_table(rng, w.n_tags, w.n_groups, w.n_critical)
+    return PaskInputs(w, K, V, Q, Kg, Vg, qd, tags, a0, amin, prio, crit)
+
+
+# ---------------------------------------------------------------- CommitKV-style page lifecycle
+
+@dataclass(frozen=True)
+class CommitWorkload:
+    """Agent trajectories at a tool-call commit: T_pre cached tokens in pages,
+    a pre-commit query window at the end of the tool call, an appended
+    observation, and a post-commit window. Planted "completion" pages have
+    keys aligned with the pre-commit queries and opposed to the post-commit
+    ones (logit shift +-plant_logit)."""
+    name: str = "commitkv_28l"
+    n_seq: int = 16
+    n_layers: int = 28
+    n_kv_heads: int = 4
+    n_q_heads: int = 28
+    head_dim: int = 128
+    n_pre: int = 32_768          # tokens before the commit (tool call ends at n_pre - 1)
+    n_obs: int = 512             # appended observation
+    window: int = 32             # W of both windows; the post-commit window is cached too
+    page_size: int = 16
+    n_planted: int = 64
+    plant_logit: float = 9.0     # c^2 / sqrt(d): c = sqrt(plant_logit * sqrt(d))
+    budget: int = 4096           # tokens retained at the checkpoint
+    layer: int = 27              # the attention layer whose effects decide
+    tau_use: float = 0.05
+    tau_dead: float = 1e-3
+    rho_use: float = 0.75
+    rho_dead: float = 0.25
+    tau_joint: float = 1e-2
+    max_scan: int = 64
+    seed: int = 20261205
+
+    @property
+    def n_tokens(self):
+        return self.n_pre + self.n_obs + self.window
+
+    @property
+    def q_first_pre(self):
+        return self.n_pre - self.window
+
+    @property
+    def q_first_post(self):
+        return self.n_pre + self.n_obs
+
+    @property
+    def n_eligible(self):
+        """Complete pages lying wholly before the pre-commit window."""
+        return self.q_first_pre // self.page_size
+
+    @property
+    def n_pages_all(self):
+        return self.n_tokens // self.page_size
+
+    @property
+    def rows(self):
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+
+COMMIT_WORKLOADS = {
+    "commitkv_28l": CommitWorkload(),
+    "commitkv_small": CommitWorkload("commitkv_small", n_seq=2, n_layers=3, n_kv_heads=2, n_q_heads=6,
+                                     n_pre=1024, n_obs=96, window=16, n_planted=6, budget=320, layer=2,
+                                     max_scan=8, seed=20261215),
+}
+
+
+@dataclass
+class CommitInputs:
+    w: CommitWorkload
+    K: torch.Tensor        # bf16 [N][L][Hkv][T][d], T = n_pre + n_obs + W
+    V: torch.Tensor
+    Q_pre: torch.Tensor    # bf16 [N][L][Hq][W][d] at positions n_pre-W .. n_pre-1
+    Q_post: torch.Tensor   # bf16 [N][L][Hq][W][d] at positions n_pre+n_obs .. T-1
+    q_dec: torch.Tensor    # bf16 [N][L][Hq][d] at position T
+    planted: np.ndarray    # int64 [N][n_planted] ascending page indices
+
+
+def make_commit_inputs(w: CommitWorkload, device="cpu") -> CommitInputs:
+    N, L, Hkv, Hq, d, T, W = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
+                              w.n_tokens, w.window)
+    G = Hq // Hkv
+    s = w.seed * 16
+    K = normal_bf16((N, L, Hkv, T, d), s + 1, device)
+    V = normal_bf16((N, L, Hkv, T, d), s + 2, device)
+    Qm = normal_bf16((N, L, Hq, W, d), s + 3, device)
+    Qp = normal_bf16((N, L, Hq, W, d), s + 4, device)
+    qd = normal_bf16((N, L, Hq, d), s + 5, device)
+    rng = np.random.default_rng(w.seed + 31)
+    planted = np.stack([np.sort(rng.choice(w.n_eligible, w.n_planted, replace=False)) for _ in range(N)])
+    u = rng.standard_normal((N, L, Hkv, d))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    c = float(np.sqrt(w.plant_logit * np.sqrt(d)))
+    cu = torch.from_numpy(c * u).to(device=device, dtype=torch.float32)        # [N][L][Hkv][d]
+    ps = w.page_size
+    for n in range(N):
+        Kn = K[n].view(L, Hkv, T // ps, ps, d)
+        idx = torch.from_numpy(planted[n]).to(device)
+        sel = Kn.index_select(2, idx).float() + cu[n][:, :, None, None, :]
+        Kn.index_copy_(2, idx, sel.to(torch.bfloat16))
+    cq = cu.repeat_interleave(G, dim=2)[:, :, :, None, :]                        # [N][L][Hq][1][d]
+    Qm = (Qm.float() + cq).to(torch.bfloat16)
+    Qp = (Qp.float() - cq).to(torch.bfloat16)
+    return CommitInputs(w, K, V, Qm, Qp, qd, planted)

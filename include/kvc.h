@@ -151,7 +151,13 @@ typedef struct kvc_compact_out {
      * NULL = every kept token goes to the bf16 tier. */
     const uint8_t *action;
     int32_t out_stride;   /* capacity per row of every output pool below */
-    int32_t reserved;     /* must be 0 */
+    /* 0: kept_idx / n_kept are per row ([N][L][Hkv][kept_stride] token
+     * indices, [N][L][Hkv] counts). p > 0: they are per sequence
+     * ([N][kept_stride] page indices, [N] page counts) and every layer and
+     * head of sequence n keeps the tokens e*p .. e*p+p-1 of each listed page
+     * e, in list order (CommitKV §3.1 Eq. 4: one index set for the token
+     * axis). p > 0 requires action == NULL. */
+    int32_t kept_page;
     /* Per-row first slot of this call's writes, device int32 [N][L][Hkv] or
      * NULL (= 0): appends after what an earlier call wrote (pass that call's
      * n_h / n_l). Must not alias the n_h / n_l outputs. */
@@ -190,7 +196,10 @@ typedef struct kvc_compact_out {
  *
  *   K, V      bf16 [N][L][Hkv][T][d]
  *   pos_in    int32 [N][L][Hkv][T] physical positions, or NULL (position = index)
- *   kept_idx  int32 [N][L][Hkv][kept_stride], n_kept int32 [N][L][Hkv] (from kvc_select)
+ *   kept_idx  int32 [N][L][Hkv][kept_stride], n_kept int32 [N][L][Hkv] (from kvc_select);
+ *             with out->kept_page = p > 0, [N][kept_stride] page indices and
+ *             [N] page counts shared by the sequence's rows: rank rho is token
+ *             kept_idx[n][rho / p] * p + rho % p
  *   Entries beyond min(n_kept, kept_stride) or past out_stride are ignored;
  *   indices outside [0, T) are skipped. n_h / n_l report base + rows written.
  */
@@ -279,6 +288,28 @@ int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16_t *K, cons
                     const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
                     int32_t n_pages, const int32_t *order, int32_t n_cand, float tau_joint,
                     uint8_t *accepted, float *joint_rel, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Page scores for the compression checkpoint (CommitKV §3.3: pages accepted
+ * for retirement are excluded and the retained index set, Eq. 13, is applied
+ * to keys, values and positions alike, Eq. 4, so one page set serves every
+ * layer and head of a sequence). For every sequence n and page
+ * e < n_pages (tokens [e*page_size, (e+1)*page_size)):
+ *   page_score[n][e] = sum over layers l, KV heads h and tokens j of page e
+ *                      of scores[n][l][h][j]            (fp32, fixed order)
+ * and -inf for every page order[n][c] with accepted[n][c] != 0 (the outputs
+ * of kvc_page_retire; entries outside [0, n_pages) are ignored). Ranking the
+ * page scores with kvc_select (dims with T = n_pages, one layer, one head)
+ * then keeps the best non-retired pages.
+ *
+ *   scores      fp32 [N][L][Hkv][T] (from kvc_score)
+ *   page_size   1..1024;  n_pages*page_size <= T
+ *   order, accepted  int32 / u8 [N][n_cand], both NULL for no exclusion
+ *   page_score  fp32 [N][n_pages]
+ */
+int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_t page_size, int32_t n_pages,
+                    const int32_t *order, const uint8_t *accepted, int32_t n_cand, float *page_score,
+                    void *stream);
 
 /* ------------------------------------------------------------------------
  * Host-side serial control (plain C on host memory; no GPU work). Their

@@ -25,10 +25,15 @@ Readings where the page is silent:
 * deleting every visible token leaves no output: the effect is +inf and such
   a page is never accepted.
 
+Checkpoint retention (§3.3, Eq. 13, with Eq. 4's single index set): a page's
+score pools the window score of its tokens over every layer and KV head of
+the sequence; retired pages are excluded; the best n_keep pages are kept.
+
 Parity status: the effect itself is pinned (Eq. 6 identity, brute force,
-closed forms); the labels and the greedy loop are pinned only by invariants
-and hand-built cases -- the workload they run on in the benchmark is
-synthetic, so beyond those invariants they are "parity unpinned".
+closed forms); the page score and the retained set by hand-built cases and
+brute force; the labels and the greedy loop only by invariants and
+hand-built cases -- the workload they run on in the benchmark is synthetic,
+so beyond those invariants they are "parity unpinned".
 """
 import numpy as np
 
@@ -122,6 +127,35 @@ def candidate_order(R_minus, R_plus, states):
     Rm, Rp = np.asarray(R_minus), np.asarray(R_plus)
     order = np.lexsort((idx, -Rm[idx], Rp[idx]))
     return idx[order]
+
+
+def page_scores(row_scores, page_size, n_pages):
+    """Checkpoint page score of one sequence (CommitKV §3.3 with Eq. 4: one
+    index set for every layer and head, so the score is pooled over them):
+    the window score of every token, summed over the sequence's rows
+    (layers x KV heads) and over the page's tokens.
+
+    row_scores: [R, T] float64 (R = layers x KV heads). Returns [n_pages].
+    """
+    S = np.asarray(row_scores, np.float64)
+    per_token = S.sum(axis=0)
+    return np.array([per_token[e * page_size:(e + 1) * page_size].sum() for e in range(n_pages)])
+
+
+def retained_pages(score, retired, n_keep):
+    """Pages kept at the checkpoint (CommitKV §3.3, Eq. 13 with an empty
+    pending set): retired pages are excluded (scored -inf), the rest ranked
+    by (score descending, page index ascending), the first n_keep kept and
+    returned in ascending order. Retired pages are used only when fewer than
+    n_keep others exist.
+    """
+    score = np.asarray(score, np.float64).copy()
+    score[np.asarray(list(retired), dtype=np.int64)] = -np.inf
+    if score.size <= n_keep:
+        return np.arange(score.size, dtype=np.int64)
+    idx = np.arange(score.size)
+    order = np.lexsort((idx, -score))
+    return np.sort(order[:n_keep]).astype(np.int64)
 
 
 def greedy_retire(order, joint_effect, tau_joint, max_scan=64):

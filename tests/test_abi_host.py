@@ -149,3 +149,40 @@ def test_decode_rejects_bad_arguments():
     assert call(n_l=FAKE, stride_l=64) == _lib.KVC_ERR_ARG            # int8 pools missing
     big = _dims(n_q_heads=64, n_kv_heads=2)                             # G = 32 > 16
     assert call(dims=big, ws=1 << 40) == _lib.KVC_ERR_UNSUPPORTED
+
+
+def test_compact_page_lists_reject_actions_and_negative_page():
+    lib = _lib.load()
+    d = _dims()
+    out = _lib.KvcCompactOut()
+    out.out_stride = 512
+    out.K_out = out.V_out = FAKE
+    out.kept_page = -1
+    st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 32, FAKE, -1, 1e4,
+                                  ctypes.byref(out), None)
+    assert st == _lib.KVC_ERR_ARG
+    out.kept_page = 16
+    out.action = FAKE
+    out.Kq = out.Vq = out.Ks = out.Vs = FAKE
+    st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 32, FAKE, -1, 1e4,
+                                  ctypes.byref(out), None)
+    assert st == _lib.KVC_ERR_UNSUPPORTED                        # shared page lists are bf16 only
+    out.action = None
+    out.kept_page = 1 << 20
+    st = lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 1 << 12, FAKE, -1, 1e4,
+                                  ctypes.byref(out), None)
+    assert st == _lib.KVC_ERR_ARG                                # listed tokens overflow int32
+
+
+def test_page_scores_reject_bad_arguments():
+    lib = _lib.load()
+    d = _dims(n_tokens=1000)
+    call = lambda ps=16, n=62, order=None, acc=None, n_cand=0, sc=FAKE: lib.kvc_page_scores(
+        ctypes.byref(d), sc, ps, n, order, acc, n_cand, FAKE, None)
+    assert call(sc=None) == _lib.KVC_ERR_ARG
+    assert call(ps=0) == _lib.KVC_ERR_UNSUPPORTED
+    assert call(ps=2048) == _lib.KVC_ERR_UNSUPPORTED
+    assert call(n=63) == _lib.KVC_ERR_ARG                        # 63 * 16 > 1000 tokens
+    assert call(order=FAKE) == _lib.KVC_ERR_ARG                  # order without accepted
+    assert call(order=FAKE, acc=FAKE, n_cand=0) == _lib.KVC_ERR_ARG
+    assert lib.kvc_last_error().decode().startswith("kvc_page_scores")

@@ -97,6 +97,46 @@ def test_candidate_order_and_greedy():
     assert pe.greedy_retire(list(range(100)), lambda S: 0.0, 1.0) == list(range(64))
 
 
+def test_page_scores_hand_built():
+    # 3 rows (layers x heads), T = 10, pages of 4: the tail tokens 8, 9 lie outside both pages
+    rows = np.array([[1, 0, 0, 0, 2, 0, 0, 0, 9, 9],
+                     [0, 1, 0, 0, 0, 0, 3, 0, 9, 9],
+                     [0, 0, 0, 1, 0, 0, 0, 4, 9, 9]], dtype=float)
+    np.testing.assert_array_equal(pe.page_scores(rows, 4, 2), [3.0, 9.0])
+
+
+def test_page_scores_pool_every_row_closed_form():
+    # window scores of a row sum to G*W (each query's weights sum to 1); pooled over
+    # R rows and pages that tile the cache, the page scores sum to R*G*W
+    from oracle import score as o_score
+    rng = np.random.default_rng(3)
+    R, T, d, G, W = 5, 96, 16, 3, 4
+    rows = [o_score.obs_window_score(rng.standard_normal((T, d)), rng.standard_normal((G, W, d)), W)
+            for _ in range(R)]
+    ps = pe.page_scores(np.stack(rows), 8, T // 8)
+    assert ps.sum() == pytest.approx(R * G * W, rel=1e-12)
+    assert np.all(ps > 0)
+
+
+def test_retained_pages_hand_built_and_brute_force():
+    assert list(pe.retained_pages([5, 1, 5, 3, 7], {4}, 2)) == [0, 2]     # 7 retired; tie to the lower index
+    assert list(pe.retained_pages([5, 1, 5, 3, 7], {4}, 4)) == [0, 1, 2, 3]
+    assert list(pe.retained_pages([5, 1, 5, 3, 7], set(), 1)) == [4]
+    assert list(pe.retained_pages([1, 2, 3], {2}, 3)) == [0, 1, 2]       # no more pages than the budget
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        n = int(rng.integers(2, 12))
+        sc = rng.integers(0, 4, n).astype(float)                          # many ties
+        ret = set(rng.choice(n, int(rng.integers(0, n)), replace=False).tolist())
+        k = int(rng.integers(1, n))
+        kept = set(pe.retained_pages(sc, ret, k).tolist())
+        assert len(kept) == k
+        eff = np.where(np.isin(np.arange(n), list(ret)), -np.inf, sc)
+        for a in kept:                                                    # every kept page outranks every dropped one
+            for b in set(range(n)) - kept:
+                assert (eff[a], -a) > (eff[b], -b)
+
+
 # ---------------------------------------------------------------- PASK controller
 
 def _rand_table(rng, n_tags, C):

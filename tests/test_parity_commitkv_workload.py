@@ -1,0 +1,314 @@
+"""GPU parity of the CommitKV-style page lifecycle workload, through the C ABI.
+
+The GPU runs the whole commit: page deletion effects in the pre- and
+post-commit windows (kvc_page_effect), lifecycle labels and candidate order
+(kvc_host_commit_candidates), greedy joint retirement (kvc_page_retire),
+checkpoint page scores from the post-commit window (kvc_score +
+kvc_page_scores), the retained page set (kvc_select over page scores), the
+compaction of keys, values and positions by that one page set
+(kvc_compact_rerotate with shared page lists) and decode attention at the next
+position, both over the compacted pool and as a paged view of the original
+storage (kvc_decode_attn with a block table).
+
+At the small shape the float64 oracle runs the same commit on its own, for
+every page and row. At the full shape (16 x 28 x 4 rows, 33,312 tokens) it
+checks sampled outputs one by one and the properties the planted pages fix.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from budgeted_retention_amd import synth
+from oracle import decode as o_decode, numfmt, page_effect as o_pe, score as o_score
+import kvc_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+EFF_RTOL, EFF_ATOL = 1e-2, 1e-7
+
+
+def run_commit(w, inp, taus):
+    """The commit on the GPU. `taus`: joint bounds to run the retirement with
+    (the first one feeds the checkpoint). Returns host arrays."""
+    from budgeted_retention_amd import kvc
+    N, L, Hkv, Hq, d, T, W, ps = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
+                                  w.n_tokens, w.window, w.page_size)
+    dev = inp.K.device
+    dims = kvc.make_dims(N, L, Hkv, Hq, d, T)
+    ws = kvc.page_workspace(dims, W, w.q_first_post, dev)
+    Rm = torch.empty((N, w.n_eligible), dtype=torch.float32, device=dev)
+    Rp = torch.empty_like(Rm)
+    kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_pre, W, w.q_first_pre, ps, w.n_eligible, Rm, ws)
+    kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible, Rp, ws)
+    Rm_h, Rp_h = Rm.cpu().numpy(), Rp.cpu().numpy()
+    states, orders, n_orders = [], [], []
+    for n in range(N):
+        st, od, no = kvc.kvc_host_commit_candidates(Rm_h[n], Rp_h[n], w.tau_use, w.tau_dead, w.rho_use,
+                                                     w.rho_dead, w.max_scan)
+        states.append(st)
+        orders.append(od)
+        n_orders.append(no)
+    order = torch.from_numpy(np.stack(orders)).to(dev)
+    retire = []
+    for tau in taus:
+        acc = torch.zeros((N, w.max_scan), dtype=torch.uint8, device=dev)
+        jr = torch.zeros((N, w.max_scan), dtype=torch.float32, device=dev)
+        kvc.kvc_page_retire(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible,
+                            order, tau, acc, ws, jr)
+        retire.append((acc, jr))
+    acc = retire[0][0]
+    # checkpoint: page scores from the post-commit window, best pages kept for every row
+    scores = torch.empty((N, L, Hkv, T), dtype=torch.float32, device=dev)
+    kvc.kvc_score(dims, inp.K, inp.Q_post, W, scores, kvc.workspace(kvc.KVC_OP_SCORE, dims, W, 0, dev))
+    P, Bp, B = w.n_pages_all, w.budget // ps, w.budget
+    pscore = torch.empty((N, P), dtype=torch.float32, device=dev)
+    kvc.kvc_page_scores(dims, scores, ps, P, pscore, order, acc)
+    pol = kvc.Policy(0, 0, Bp, 1, 1, 0, 1, None, torch.zeros((1, 1), dtype=torch.float32, device=dev))
+    kept = torch.full((N, Bp), -1, dtype=torch.int32, device=dev)
+    nk = torch.zeros(N, dtype=torch.int32, device=dev)
+    kvc.kvc_select(kvc.make_dims(N, 1, 1, 1, 64, P), pscore, pol, kept, Bp, nk)
+    rows = N * L * Hkv
+    Ko = torch.zeros((rows, B, d), dtype=torch.bfloat16, device=dev)
+    Vo = torch.zeros_like(Ko)
+    po = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
+    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
+    kvc.kvc_compact_rerotate(dims, inp.K, inp.V, None, kept, Bp, nk, -1, 1e6,
+                             kvc.CompactOut(B, Ko, Vo, po, nh, kept_page=ps))
+    # decode at position T: over the compacted pool, and through a block table of the kept pages
+    dims_c = kvc.make_dims(N, L, Hkv, Hq, d, B)
+    o1 = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
+    o2 = torch.empty_like(o1)
+    lse1 = torch.empty((N, L, Hq), dtype=torch.float32, device=dev)
+    lse2 = torch.empty_like(lse1)
+    ws1 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_c, B, 0)), dtype=torch.uint8, device=dev)
+    kvc.kvc_decode_attn(dims_c, inp.q_dec, Ko, Vo, nh, B, o1, ws1, lse1)
+    ws2 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims, Bp * ps, 0)), dtype=torch.uint8, device=dev)
+    n_all = torch.full((rows,), B, dtype=torch.int32, device=dev)
+    kvc.kvc_decode_attn(dims, inp.q_dec, inp.K, inp.V, n_all, T, o2, ws2, lse2, kept, ps, Bp)
+    torch.cuda.synchronize()
+    return dict(Rm=Rm_h, Rp=Rp_h, states=np.stack(states), order=np.stack(orders), n_order=np.array(n_orders),
+                retire=[(a.cpu().numpy(), j.cpu().numpy()) for a, j in retire],
+                scores=scores, pscore=pscore.cpu().numpy(), kept=kept.cpu().numpy(), n_kept=nk.cpu().numpy(),
+                Ko=Ko, Vo=Vo, pos=po, n_h=nh.cpu().numpy(), o1=tl.f64(o1), o2=tl.f64(o2),
+                lse1=lse1.cpu().numpy(), lse2=lse2.cpu().numpy())
+
+
+def _layer_f64(inp, n, layer):
+    return (tl.f64(inp.K[n, layer]), tl.f64(inp.V[n, layer]), tl.f64(inp.Q_pre[n, layer]),
+            tl.f64(inp.Q_post[n, layer]))
+
+
+def _effects(K, V, Q, q_first, W, pages, ps, mapper):
+    q_pos = q_first + np.arange(W)
+    return np.array(list(mapper(
+        lambda e: o_pe.deletion_effect(K, V, Q, q_pos, o_pe.page_tokens(e * ps, ps))[0], pages)))
+
+
+def _joint(K, V, Q, q_first, W, pages, ps):
+    toks = np.concatenate([o_pe.page_tokens(e * ps, ps) for e in pages])
+    return o_pe.deletion_effect(K, V, Q, q_first + np.arange(W), toks)[0]
+
+
+def _oracle_page_scores(inp, n, W, P, ps, mapper):
+    """Oracle window scores of every row of sequence n from the post-commit
+    window, and the pooled page scores."""
+    L, Hkv = inp.K.shape[1], inp.K.shape[2]
+    G = inp.Q_post.shape[2] // Hkv
+
+    def row(lh):
+        l, h = lh
+        return o_score.obs_window_score(tl.f64(inp.K[n, l, h]), tl.f64(inp.Q_post[n, l, h * G:(h + 1) * G]), W)
+    rows = np.stack(list(mapper(row, [(l, h) for l in range(L) for h in range(Hkv)])))
+    return rows, o_pe.page_scores(rows, ps, P)
+
+
+def _check_kept_pages(g_kept, g_n, o_kept, o_score_, retired, Bp):
+    """Kept page sets equal except swaps among pages whose oracle score lies
+    within 1e-3 relative of the Bp-th kept score; never a retired page."""
+    g = g_kept[:g_n].astype(np.int64)
+    assert g_n == Bp and np.all(np.diff(g) > 0)
+    assert not set(g.tolist()) & set(retired)
+    diff = np.setxor1d(g, o_kept)
+    if diff.size:
+        thr = o_score_[o_kept].min()
+        assert np.all(np.abs(o_score_[diff] - thr) <= 1e-3 * abs(thr)), (diff, o_score_[diff], thr)
+    return diff.size
+
+
+def _check_compaction_rows(res, inp, w, rows_sel):
+    ps = w.page_size
+    L, Hkv = w.n_layers, w.n_kv_heads
+    for r in rows_sel:
+        n, l, h = r // (L * Hkv), (r // Hkv) % L, r % Hkv
+        pages = res["kept"][n][: res["n_kept"][n]].astype(np.int64)
+        toks = (pages[:, None] * ps + np.arange(ps)[None, :]).reshape(-1)
+        assert res["n_h"][r] == toks.size
+        tl.check_compaction(tl.bits(res["Ko"][r]), tl.bits(res["Vo"][r]), res["pos"][r].cpu().numpy(),
+                            tl.bits(inp.K[n, l, h]), tl.bits(inp.V[n, l, h]), np.arange(w.n_tokens), toks,
+                            -1, 1e6)
+
+
+def _check_decode(res, inp, w, n, heads, o_pages, exact_set):
+    ps = w.page_size
+    G = w.n_q_heads // w.n_kv_heads
+    toks = (np.asarray(o_pages)[:, None] * ps + np.arange(ps)[None, :]).reshape(-1)
+    for l, hq in heads:
+        h = hq // G
+        K, V = tl.f64(inp.K[n, l, h])[toks], tl.f64(inp.V[n, l, h])[toks]
+        o, lse = o_decode.decode_partitions(tl.f64(inp.q_dec[n, l, hq]), [(K, V)])
+        for g_o, g_lse in ((res["o1"], res["lse1"]), (res["o2"], res["lse2"])):
+            np.testing.assert_allclose(g_o[n, l, hq], numfmt.round_bf16(o), rtol=1e-2, atol=2e-2)
+            if exact_set:
+                np.testing.assert_allclose(g_o[n, l, hq], o, rtol=8e-3, atol=1e-3)
+                assert g_lse[n, l, hq] == pytest.approx(lse, rel=1e-5, abs=1e-5)
+
+
+@pytest.mark.parametrize("bind", [False, True])
+def test_commitkv_small_end_to_end(bind):
+    """Every page and row against the oracle's own run of the commit."""
+    w = synth.COMMIT_WORKLOADS["commitkv_small"]
+    inp = synth.make_commit_inputs(w, "cpu")
+    W, ps, P, Bp = w.window, w.page_size, w.n_pages_all, w.budget // w.page_size
+    pool = map      # small products: threads would only contend for the BLAS threads
+    # the oracle's commit, per sequence
+    oracle = []
+    for n in range(w.n_seq):
+        K, V, Qm, Qp = _layer_f64(inp, n, w.layer)
+        Rm = _effects(K, V, Qm, w.q_first_pre, W, range(w.n_eligible), ps, pool)
+        Rp = _effects(K, V, Qp, w.q_first_post, W, range(w.n_eligible), ps, pool)
+        st = o_pe.lifecycle_states(Rm, Rp, w.tau_use, np.float32(w.tau_dead), w.rho_use, w.rho_dead)
+        order = o_pe.candidate_order(Rm, Rp, st)[: w.max_scan]
+        oracle.append(dict(K=K, V=V, Qp=Qp, Rm=Rm, Rp=Rp, st=st, order=order))
+    assert all(set(o["order"].tolist()) == set(inp.planted[n].tolist()) for n, o in enumerate(oracle))
+    taus = [w.tau_joint]
+    if bind:
+        # a bound between the joint effects of the first two and first three candidates
+        o = oracle[0]
+        j2 = _joint(o["K"], o["V"], o["Qp"], w.q_first_post, W, o["order"][:2], ps)
+        j3 = _joint(o["K"], o["V"], o["Qp"], w.q_first_post, W, o["order"][:3], ps)
+        assert j3 > 1.05 * j2
+        taus = [float(np.sqrt(j2 * j3))]
+    inp.K, inp.V, inp.Q_pre, inp.Q_post, inp.q_dec = (t.cuda() for t in (inp.K, inp.V, inp.Q_pre, inp.Q_post,
+                                                                         inp.q_dec))
+    res = run_commit(w, inp, taus)
+    acc, jr = res["retire"][0]
+    for n, o in enumerate(oracle):
+        np.testing.assert_allclose(res["Rm"][n], o["Rm"], rtol=EFF_RTOL, atol=EFF_ATOL)
+        np.testing.assert_allclose(res["Rp"][n], o["Rp"], rtol=EFF_RTOL, atol=EFF_ATOL)
+        np.testing.assert_array_equal(res["states"][n], o["st"])
+        assert res["n_order"][n] == o["order"].size
+        np.testing.assert_array_equal(res["order"][n][: o["order"].size], o["order"])
+        # the oracle's greedy walk over the same order; a joint effect within 1e-3 of
+        # the bound may be decided either way, and ends the comparison
+        D = []
+        for c, e in enumerate(o["order"].tolist()):
+            j = _joint(o["K"], o["V"], o["Qp"], w.q_first_post, W, D + [e], ps)
+            assert jr[n, c] == pytest.approx(j, rel=EFF_RTOL, abs=EFF_ATOL)
+            if abs(j - taus[0]) <= 1e-3 * taus[0]:
+                break
+            assert bool(acc[n, c]) == (j <= taus[0]), (n, c, j, taus[0])
+            if j <= taus[0]:
+                D.append(e)
+        if bind and n == 0:
+            assert 0 < acc[n].sum() < o["order"].size
+        retired = [int(res["order"][n][c]) for c in range(w.max_scan) if acc[n, c]]
+        rows, o_ps = _oracle_page_scores(inp, n, W, P, ps, pool)
+        g_rows = res["scores"][n].reshape(-1, w.n_tokens).cpu().numpy()
+        for r in range(rows.shape[0]):
+            tl.check_scores(g_rows[r], rows[r])
+        keep_mask = np.ones(P, bool)
+        keep_mask[retired] = False
+        tl.check_scores(res["pscore"][n][keep_mask], o_ps[keep_mask])
+        assert np.all(np.isneginf(res["pscore"][n][~keep_mask]))
+        o_kept = o_pe.retained_pages(o_ps, retired, Bp)
+        swaps = _check_kept_pages(res["kept"][n], res["n_kept"][n], o_kept, o_ps, retired, Bp)
+        G = w.n_q_heads // w.n_kv_heads
+        _check_decode(res, inp, w, n, [(l, hq) for l in range(w.n_layers) for hq in range(w.n_q_heads)],
+                      o_kept, swaps == 0)
+    _check_compaction_rows(res, inp, w, range(w.rows))
+
+
+def test_commitkv_full_size_sampled():
+    """16 trajectories x 28 layers x 4 KV heads, 33,312 tokens in 16-token pages."""
+    w = synth.COMMIT_WORKLOADS["commitkv_28l"]
+    inp = synth.make_commit_inputs(w, "cuda")
+    W, ps, P, Bp = w.window, w.page_size, w.n_pages_all, w.budget // w.page_size
+    executor = ThreadPoolExecutor(8)     # whole-row products: one row per thread pays off
+    pool = executor.map
+    K, V, Qm, Qp = _layer_f64(inp, 0, w.layer)
+    planted0 = inp.planted[0]
+    # the full-set joint effect of the planted pages, then a bound that binds inside the walk
+    j_all = _joint(K, V, Qp, w.q_first_post, W, planted0, ps)
+    res = run_commit(w, inp, [w.tau_joint, 0.5 * j_all])
+    # effects at sampled pages: planted ones (high before, low after) and others
+    rng = np.random.default_rng(1)
+    others = rng.choice(np.setdiff1d(np.arange(w.n_eligible), planted0), 3, replace=False)
+    sample = np.concatenate([planted0[[0, 31, 63]], others])
+    np.testing.assert_allclose(res["Rm"][0][sample], _effects(K, V, Qm, w.q_first_pre, W, sample, ps, pool),
+                               rtol=EFF_RTOL, atol=EFF_ATOL)
+    np.testing.assert_allclose(res["Rp"][0][sample], _effects(K, V, Qp, w.q_first_post, W, sample, ps, pool),
+                               rtol=EFF_RTOL, atol=EFF_ATOL)
+    # every sequence: the completion candidates are exactly the planted pages, each effect
+    # further from its threshold than twice the effect tolerance (so the float64 values
+    # fall on the same side); the order follows the oracle's rule on these effects
+    lo, hi = 1 - 2 * EFF_RTOL, 1 + 2 * EFF_RTOL
+    for n in range(w.n_seq):
+        pl = inp.planted[n]
+        assert res["Rm"][n][pl].min() > hi * w.tau_use and res["Rp"][n][pl].max() < lo * w.tau_dead
+        mask = np.ones(w.n_eligible, bool)
+        mask[pl] = False
+        assert res["Rp"][n][mask].min() > hi * w.tau_dead
+        o_st = o_pe.lifecycle_states(res["Rm"][n].astype(np.float64), res["Rp"][n].astype(np.float64),
+                                     w.tau_use, np.float32(w.tau_dead), w.rho_use, w.rho_dead)
+        np.testing.assert_array_equal(res["states"][n], o_st)
+        o_order = o_pe.candidate_order(res["Rm"][n].astype(np.float64), res["Rp"][n].astype(np.float64), o_st)
+        assert set(o_order.tolist()) == set(pl.tolist()) and res["n_order"][n] == w.n_planted
+        np.testing.assert_array_equal(res["order"][n], o_order[: w.max_scan])
+    # the configured bound retires every candidate; the joint effect of all of them
+    acc, jr = res["retire"][0]
+    assert acc.all()
+    assert jr[0, -1] == pytest.approx(j_all, rel=EFF_RTOL, abs=EFF_ATOL)
+    order0 = res["order"][0].tolist()
+    assert jr[0, 0] == pytest.approx(_joint(K, V, Qp, w.q_first_post, W, order0[:1], ps), rel=EFF_RTOL,
+                                     abs=EFF_ATOL)
+    # half the full-set effect binds inside the walk: each decision matches the joint
+    # effect of the set accepted before it, recomputed by the oracle at sampled steps
+    acc2, jr2 = res["retire"][1]
+    tau2 = 0.5 * j_all
+    valid = res["order"] >= 0
+    assert np.array_equal((acc2 != 0)[valid], (jr2 <= np.float32(tau2))[valid])
+    first_rej = int(np.flatnonzero(acc2[0] == 0)[0])
+    for c in sorted({0, 1, first_rej, first_rej + 1, w.max_scan - 1}):
+        D = [order0[i] for i in range(c) if acc2[0, i]]
+        j = _joint(K, V, Qp, w.q_first_post, W, D + [order0[c]], ps)
+        assert jr2[0, c] == pytest.approx(j, rel=EFF_RTOL, abs=EFF_ATOL), c
+        if abs(j - tau2) > 1e-3 * tau2:
+            assert bool(acc2[0, c]) == (j <= tau2), (c, j, tau2)
+    # checkpoint of sequence 0: every row's window score, the pooled page scores and the
+    # kept pages; the planted pages score far below the kept ones, so which of them are
+    # retired does not change the kept set
+    rows, o_ps = _oracle_page_scores(inp, 0, W, P, ps, pool)
+    g_rows = res["scores"][0].reshape(-1, w.n_tokens).cpu().numpy()
+    for r in range(rows.shape[0]):
+        tl.check_scores(g_rows[r], rows[r])
+    keep_mask = np.ones(P, bool)
+    keep_mask[planted0] = False
+    tl.check_scores(res["pscore"][0][keep_mask], o_ps[keep_mask])
+    assert np.all(np.isneginf(res["pscore"][0][planted0]))
+    o_kept = o_pe.retained_pages(o_ps, planted0, Bp)
+    assert not set(o_pe.retained_pages(o_ps, [], Bp).tolist()) & set(planted0.tolist())
+    swaps = _check_kept_pages(res["kept"][0], res["n_kept"][0], o_kept, o_ps, planted0, Bp)
+    assert swaps <= 2
+    for n in range(1, w.n_seq):
+        g = res["kept"][n][: res["n_kept"][n]]
+        assert res["n_kept"][n] == Bp and np.all(np.diff(g) > 0)
+        assert not set(g.tolist()) & set(inp.planted[n].tolist())
+    L, Hkv = w.n_layers, w.n_kv_heads
+    _check_compaction_rows(res, inp, w, [0, (0 * L + 27) * Hkv + 3, (0 * L + 13) * Hkv + 1,
+                                         (15 * L + 20) * Hkv + 2, w.rows - 1])
+    _check_decode(res, inp, w, 0, [(0, 0), (13, 9), (27, 27), (27, 6)], o_kept, swaps == 0)
+    # the compacted pool and the paged view of the original storage decode alike
+    np.testing.assert_allclose(res["o1"], res["o2"], rtol=8e-3, atol=1e-3)
+    executor.shutdown()

@@ -73,6 +73,42 @@ def test_tiny_workload_all_rows():
             assert set(range(s, s + ln)) <= set(res["kept"][r].tolist())
 
 
+def test_tiny_workload_decode_over_compacted_cache():
+    """One decode query per head at position B over the renumbered, re-rotated
+    cache, against the oracle's decode over its own compaction."""
+    from budgeted_retention_amd import kvc
+    from oracle import compact as o_compact, decode as o_decode
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_compaction_inputs(w, "cpu")
+    inp.K, inp.V, inp.Q_obs = inp.K.cuda(), inp.V.cuda(), inp.Q_obs.cuda()
+    res = _run(w, inp)
+    N, L, Hkv, Hq, d, B = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.budget
+    G = Hq // Hkv
+    dims = kvc.make_dims(N, L, Hkv, Hq, d, B)
+    Ko = torch.from_numpy(res["K"].view(np.int16)).view(torch.bfloat16).reshape(w.rows, B, d).cuda()
+    Vo = torch.from_numpy(res["V"].view(np.int16)).view(torch.bfloat16).reshape(w.rows, B, d).cuda()
+    o = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims, B, 0)), dtype=torch.uint8, device="cuda")
+    kvc.kvc_decode_attn(dims, inp.q_dec.cuda(), Ko, Vo, torch.from_numpy(res["n_h"]).cuda(), B, o, ws)
+    torch.cuda.synchronize()
+    g_o = tl.f64(o)
+    bonus = tl.oracle_bonus_table(inp.spans.steps_ahead, SIGMA, LAMBDA)
+    for r in range(w.rows):
+        n, l, h = r // (L * Hkv), (r // Hkv) % L, r % Hkv
+        K_bits, V_bits = tl.bits(inp.K[n, l, h]), tl.bits(inp.V[n, l, h])
+        _, _, _, kept, _ = tl.oracle_row(numfmt.bf16_bits_to_f64(K_bits), tl.f64(inp.Q_obs[n, l, h * G:(h + 1) * G]),
+                                         w.window, inp.spans.tags, bonus, np.zeros_like(bonus, np.uint8), 0,
+                                         w.n_sink, w.n_recent, B)
+        oK, oV, _ = o_compact.compact_row(K_bits, V_bits, np.arange(w.n_tokens), kept, w.renumber_base, w.rope_base)
+        for g in range(G):
+            hq = h * G + g
+            ref, _ = o_decode.decode_partitions(tl.f64(inp.q_dec[n, l, hq]),
+                                                [(numfmt.bf16_bits_to_f64(oK), numfmt.bf16_bits_to_f64(oV))])
+            np.testing.assert_allclose(g_o[n, l, hq], numfmt.round_bf16(ref), rtol=1e-2, atol=2e-2)
+            if np.array_equal(res["kept"][r][: res["n_kept"][r]], kept):
+                np.testing.assert_allclose(g_o[n, l, hq], ref, rtol=8e-3, atol=1e-3)
+
+
 def test_tiny_workload_is_deterministic():
     w = synth.WORKLOADS["tiny"]
     inp = synth.make_compaction_inputs(w, "cpu")

@@ -106,3 +106,100 @@ def test_page_retire_greedy_matches_oracle():
             if j <= tau:
                 D.append(e)
         assert acc[n].sum() >= 1
+
+
+@pytest.mark.parametrize("N,L,Hkv,T,ps,n_pages", [
+    (2, 3, 2, 2000, 16, 125),     # pages tile the rows exactly
+    (3, 2, 4, 1500, 24, 60),      # a page size that does not divide the workgroup's 1024 tokens
+    (1, 1, 1, 5000, 1000, 4),     # one page per workgroup, tail tokens outside every page
+    (2, 5, 1, 777, 1, 700),       # one-token pages
+])
+def test_page_scores_pool_rows_and_exclude_retired(N, L, Hkv, T, ps, n_pages):
+    from budgeted_retention_amd import kvc
+    from oracle import page_effect as o_pe2
+    rng = np.random.default_rng(T + ps)
+    scores = rng.gamma(0.5, 1.0, (N, L, Hkv, T)).astype(np.float32)
+    n_cand = min(6, n_pages)
+    order = np.stack([rng.choice(n_pages, n_cand, replace=False) for _ in range(N)]).astype(np.int32)
+    order[0, 1] = -1                       # an empty slot
+    order[-1, 2] = n_pages + 3             # outside the pages: ignored
+    acc = rng.integers(0, 2, (N, n_cand)).astype(np.uint8)
+    acc[:, 0] = 1
+    acc[0, 1] = acc[-1, 2] = 1
+    # the best page of every sequence is retired: it must drop to the end of the ranking
+    dims = kvc.make_dims(N, L, Hkv, 8, 64, T)
+    out = torch.empty((N, n_pages), dtype=torch.float32, device="cuda")
+    kvc.kvc_page_scores(dims, torch.from_numpy(scores).cuda(), ps, n_pages, out,
+                        torch.from_numpy(order).cuda(), torch.from_numpy(acc).cuda())
+    plain = torch.empty_like(out)
+    kvc.kvc_page_scores(dims, torch.from_numpy(scores).cuda(), ps, n_pages, plain)
+    torch.cuda.synchronize()
+    out, plain = out.cpu().numpy(), plain.cpu().numpy()
+    for n in range(N):
+        ref = o_pe2.page_scores(scores[n].reshape(L * Hkv, T).astype(np.float64), ps, n_pages)
+        np.testing.assert_allclose(plain[n], ref, rtol=1e-5, atol=1e-5)
+        retired = {int(e) for e, a in zip(order[n], acc[n]) if a and 0 <= e < n_pages}
+        mask = np.zeros(n_pages, bool)
+        mask[list(retired)] = True
+        assert np.all(np.isneginf(out[n][mask]))
+        np.testing.assert_array_equal(out[n][~mask], plain[n][~mask])
+
+
+def test_select_over_page_scores_keeps_best_unretired_pages():
+    from budgeted_retention_amd import kvc
+    from oracle import page_effect as o_pe2
+    rng = np.random.default_rng(4)
+    N, P, Bp = 3, 2082, 256
+    ps_ = rng.gamma(2.0, 1.0, (N, P)).astype(np.float32)
+    ps_[:, ::97] = 50.0                                   # ties at the top, broken by page index
+    retired = [rng.choice(np.flatnonzero(ps_[n] == 50.0), 5, replace=False) for n in range(N)]
+    for n in range(N):
+        ps_[n, retired[n]] = -np.inf
+    pol = kvc.Policy(0, 0, Bp, 1, 1, 0, 1, None, torch.zeros((1, 1), dtype=torch.float32, device="cuda"))
+    kept = torch.full((N, Bp), -1, dtype=torch.int32, device="cuda")
+    nk = torch.zeros(N, dtype=torch.int32, device="cuda")
+    kvc.kvc_select(kvc.make_dims(N, 1, 1, 1, 64, P), torch.from_numpy(ps_).cuda(), pol, kept, Bp, nk)
+    torch.cuda.synchronize()
+    for n in range(N):
+        ref = o_pe2.retained_pages(np.where(np.isneginf(ps_[n]), 0.0, ps_[n]).astype(np.float64), retired[n], Bp)
+        assert nk[n].item() == Bp
+        np.testing.assert_array_equal(kept[n].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("out_stride", [4096, 1000])
+def test_compact_shared_page_lists(out_stride):
+    """One page list per sequence applied to every layer and head; -1 entries and
+    entries past the cache are skipped; the pool capacity truncates."""
+    from budgeted_retention_amd import kvc
+    N, L, Hkv, d, T, ps, Bp = 2, 3, 2, 128, 5000, 16, 256
+    rows = N * L * Hkv
+    K, V, _ = synth.small_case(T, Hkv, 2 * Hkv, d, 4, L, N, seed=77)
+    rng = np.random.default_rng(6)
+    n_pages = T // ps + 1                                  # the last page runs past the cache
+    pages = np.stack([np.sort(rng.choice(n_pages, Bp, replace=False)) for _ in range(N)]).astype(np.int32)
+    pages[0, -1] = n_pages - 1
+    nk = np.array([Bp, Bp - 9], np.int32)
+    pages[1, 3] = -1
+    pos = np.tile((np.arange(T, dtype=np.int32) * 2 + 7), (rows, 1))
+    dims = kvc.make_dims(N, L, Hkv, 2 * Hkv, d, T)
+    Ko = torch.zeros((rows, out_stride, d), dtype=torch.bfloat16, device="cuda")
+    Vo = torch.zeros_like(Ko)
+    po = torch.full((rows, out_stride), -1, dtype=torch.int32, device="cuda")
+    nh = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    kvc.kvc_compact_rerotate(dims, K.cuda(), V.cuda(), torch.from_numpy(pos).cuda(), torch.from_numpy(pages).cuda(),
+                             Bp, torch.from_numpy(nk).cuda(), -1, 1e6,
+                             kvc.CompactOut(out_stride, Ko, Vo, po, nh, kept_page=ps))
+    torch.cuda.synchronize()
+    Kb, Vb = tl.bits(K).reshape(rows, T, d), tl.bits(V).reshape(rows, T, d)
+    gK, gV, gpos = tl.bits(Ko), tl.bits(Vo), po.cpu().numpy()
+    for r in range(rows):
+        n = r // (L * Hkv)
+        ranks = np.arange(min(int(nk[n]) * ps, out_stride))
+        entry = pages[n][ranks // ps].astype(np.int64)
+        tok = entry * ps + ranks % ps
+        ok = (entry >= 0) & (tok < T)
+        assert nh[r].item() == ranks.size
+        np.testing.assert_array_equal(gK[r][ranks[ok]], Kb[r][tok[ok]])
+        np.testing.assert_array_equal(gV[r][ranks[ok]], Vb[r][tok[ok]])
+        np.testing.assert_array_equal(gpos[r][ranks[ok]], pos[r][tok[ok]])
+        assert np.all(gpos[r][ranks[~ok]] == -1) and np.all(gK[r][ranks[~ok]] == 0)
