@@ -33,8 +33,17 @@ def _hipcc():
     return exe
 
 
+# Per-source extra flags. The score and page-effect kernels consume every MFMA
+# result on the VALU; keeping the accumulators in VGPRs (instead of AGPRs)
+# saves one v_accvgpr_read per logit.
+EXTRA_FLAGS = {
+    "score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "page_effect.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src, obj, verbose):
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,10 +10,10 @@
 // in fp32 and the result is rounded once to bf16. Values are bit copies
 // (CommitKV §3.1 Eq. 4 applies the same index set to K, V and positions).
 //
-// Work split: a group of D/4 threads owns one token. Thread `sub` of the group
-// rotates the frequency pairs (2sub, 2sub+D/2) and (2sub+1, 2sub+1+D/2) --
-// one 4-byte load from each half of the key -- and copies 8 bytes of the
-// value row, so a group's loads cover the key and value rows contiguously.
+// Work split (plain path): a group of D/8 threads owns one token; thread `sub`
+// rotates the frequency pairs 4sub..4sub+3 and their partners D/2 further on,
+// so a group's loads cover the key and value rows contiguously. The tiered
+// path keeps groups of D/4 threads with two pairs each.
 //
 // With an action array the kept entries are routed, in rank order, to the
 // bf16 tier, the int8 tier (PASK Appendix B.5 symmetric per-token-per-head
@@ -112,10 +112,39 @@ struct CompactArgs {
     const int32_t *h_base, *l_base;
 };
 
+// Rotates four frequency pairs: lo holds x_i..x_{i+3} of the first half, hi
+// their partners x_{i+D/2}..x_{i+3+D/2}; th[e] is the frequency of pair i+e.
+__device__ __forceinline__ void rotate_quad(uint2 &lo, uint2 &hi, double delta, const double (&th)[4]) {
+    uint32_t l[2] = {lo.x, lo.y}, h[2] = {hi.x, hi.y};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        float s0, c0, s1, c1;
+        reduced_sincos(delta * th[2 * w], &s0, &c0);
+        reduced_sincos(delta * th[2 * w + 1], &s1, &c1);
+        const float x0 = bf16_to_f32((uint16_t)(l[w] & 0xFFFF)), x1 = bf16_to_f32((uint16_t)(l[w] >> 16));
+        const float y0 = bf16_to_f32((uint16_t)(h[w] & 0xFFFF)), y1 = bf16_to_f32((uint16_t)(h[w] >> 16));
+        const float nx0 = x0 * c0 - y0 * s0, ny0 = y0 * c0 + x0 * s0;
+        const float nx1 = x1 * c1 - y1 * s1, ny1 = y1 * c1 + x1 * s1;
+        l[w] = (uint32_t)f32_to_bf16(nx0) | ((uint32_t)f32_to_bf16(nx1) << 16);
+        h[w] = (uint32_t)f32_to_bf16(ny0) | ((uint32_t)f32_to_bf16(ny1) << 16);
+    }
+    lo = make_uint2(l[0], l[1]);
+    hi = make_uint2(h[0], h[1]);
+}
+
+// Plain compaction. A group of D/8 threads owns one token; thread `sub`
+// rotates the frequency pairs 4sub..4sub+3 (an 8-byte load from each half of
+// the key) and copies 16 bytes of the value row. A workgroup takes CMP_UNROLL
+// consecutive groups of ranks of one row: every thread first reads the kept
+// indices of its CMP_UNROLL tokens, then issues all of their key and value
+// loads, so each workgroup waits for two memory latencies in all.
+static constexpr int CMP_UNROLL = 4;
+
 template <int D>
 __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int blocks_per_row) {
-    constexpr int TPT = D / 4;
+    constexpr int TPT = D / 8;
     constexpr int TOK = CMP_THREADS / TPT;
+    constexpr int U = CMP_UNROLL;
     const int64_t r = blockIdx.x / blocks_per_row;
     const int cb = blockIdx.x % blocks_per_row;
     const int kp = a.kept_page;
@@ -131,12 +160,22 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
     if (cb == 0 && threadIdx.x == 0 && a.nh) a.nh[r] = base + n;
     const int sub = threadIdx.x % TPT, tin = threadIdx.x / TPT;
     const bool rot = a.renumber_base >= 0;
-    double th0 = 0.0, th1 = 0.0;
+    double th[4] = {0.0, 0.0, 0.0, 0.0};
     if (rot) {
-        th0 = pow(a.rope_base, -2.0 * (2 * sub) / D);
-        th1 = pow(a.rope_base, -2.0 * (2 * sub + 1) / D);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) th[e] = pow(a.rope_base, -2.0 * (4 * sub + e) / D);
     }
-    for (int rho = cb * TOK + tin; rho < n; rho += blocks_per_row * TOK) {
+    const int rho0 = cb * (TOK * U) + tin;
+    // Each token lives in its own struct value (no per-thread arrays, which
+    // the compiler would place in LDS).
+    struct Tok {
+        int64_t j, p;
+        uint2 lo, hi;
+        uint4 v;
+    };
+    auto index = [&](int u) -> int64_t {
+        const int rho = rho0 + u * TOK;
+        if (rho >= n) return -1;
         int64_t j;
         if (kp) {
             const int64_t e = a.kept[(size_t)kr * a.kept_stride + rho / kp];
@@ -144,23 +183,41 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         } else {
             j = a.kept[(size_t)kr * a.kept_stride + rho];
         }
-        if (j < 0 || j >= a.T) continue;
-        const size_t src = ((size_t)r * a.T + j) * D;
-        const size_t dst = ((size_t)r * a.out_stride + base + rho) * D;
-        uint32_t lo = *reinterpret_cast<const uint32_t *>(a.K + src + 2 * sub);
-        uint32_t hi = *reinterpret_cast<const uint32_t *>(a.K + src + D / 2 + 2 * sub);
-        const uint2 v = *reinterpret_cast<const uint2 *>(a.V + src + 4 * sub);
-        const int64_t p = a.pos_in ? (int64_t)a.pos_in[(size_t)r * a.T + j] : j;
-        int64_t pn = p;
+        return j < a.T ? j : -1;
+    };
+    // entries past the kept count read token 0 of the row (always present) and are not stored
+    auto fetch = [&](int64_t j) -> Tok {
+        Tok t;
+        t.j = j;
+        const int64_t jj = j < 0 ? 0 : j;
+        const size_t src = ((size_t)r * a.T + jj) * D;
+        t.lo = *reinterpret_cast<const uint2 *>(a.K + src + 4 * sub);
+        t.hi = *reinterpret_cast<const uint2 *>(a.K + src + D / 2 + 4 * sub);
+        t.v = *reinterpret_cast<const uint4 *>(a.V + src + 8 * sub);
+        t.p = a.pos_in ? (int64_t)a.pos_in[(size_t)r * a.T + jj] : jj;
+        return t;
+    };
+    auto put = [&](Tok &t, int u) {
+        if (t.j < 0) return;
+        const int rho = rho0 + u * TOK;
+        int64_t pn = t.p;
         if (rot) {
             pn = (int64_t)a.renumber_base + rho;
-            rotate_pairs(lo, hi, (double)(pn - p), th0, th1);
+            rotate_quad(t.lo, t.hi, (double)(pn - t.p), th);
         }
-        *reinterpret_cast<uint32_t *>(a.Ko + dst + 2 * sub) = lo;
-        *reinterpret_cast<uint32_t *>(a.Ko + dst + D / 2 + 2 * sub) = hi;
-        *reinterpret_cast<uint2 *>(a.Vo + dst + 4 * sub) = v;
+        const size_t dst = ((size_t)r * a.out_stride + base + rho) * D;
+        *reinterpret_cast<uint2 *>(a.Ko + dst + 4 * sub) = t.lo;
+        *reinterpret_cast<uint2 *>(a.Ko + dst + D / 2 + 4 * sub) = t.hi;
+        *reinterpret_cast<uint4 *>(a.Vo + dst + 8 * sub) = t.v;
         if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + base + rho] = (int32_t)pn;
-    }
+    };
+    static_assert(U == 4, "the token batch below is written out for four tokens");
+    const int64_t j0 = index(0), j1 = index(1), j2 = index(2), j3 = index(3);
+    Tok t0 = fetch(j0), t1 = fetch(j1), t2 = fetch(j2), t3 = fetch(j3);
+    put(t0, 0);
+    put(t1, 1);
+    put(t2, 2);
+    put(t3, 3);
 }
 
 template <int D>
@@ -339,10 +396,10 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     const int64_t rows = n_rows(dims);
     hipStream_t s = as_stream(stream);
     if (!out->action) {
-        const int tok = CMP_THREADS / (dims->head_dim / 4);
+        const int tok = CMP_THREADS / (dims->head_dim / 8);
         const int64_t listed = (int64_t)kept_stride * (out->kept_page > 0 ? out->kept_page : 1);
         const int cap = (int)(listed < out->out_stride ? listed : out->out_stride);
-        int bpr = (cap + 4 * tok - 1) / (4 * tok);  // about 4 tokens per group
+        int bpr = (cap + CMP_UNROLL * tok - 1) / (CMP_UNROLL * tok);  // CMP_UNROLL tokens per group
         if (bpr < 1) bpr = 1;
         if (rows * bpr > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_compact_rerotate: grid too large");
         if (dims->head_dim == 128)
