@@ -1,11 +1,21 @@
 """Benchmark: KV tokens compacted per second (score + select + gather +
-re-rotate) on one MI355X, with the dominant kernel's HBM roofline and the CPU
+re-rotate) on one MI355X, with the dominant call's HBM roofline and the CPU
 oracle's rate on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one compaction of a whole session: kvc_score, kvc_select and
+Default workload: the Qwen3-8B-shaped 100,000-token session. One step is one
+compaction of the whole session: kvc_score, kvc_select and
 kvc_compact_rerotate over every (layer, KV head) row, inputs resident in HBM.
+Decode attention over the compacted cache is timed beside the step (not in
+`value`).
+
+Other workloads (parity cases, measured the same way call by call):
+  tiny            1 layer, T=4096, B=512, renumbered
+  qwen3_8b_1m     T=1,048,576, one layer per call (154.6 GB of K+V resident)
+  pask_llama3_8b  64 x 32 layers: prompt compaction, int8/bf16/release tiers, decode
+  commitkv_28l    16 x 28 layers: page effects, retirement, checkpoint, paged decode
+
 Prints one JSON line.
 """
 import argparse
@@ -20,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+METRIC = "KV tokens compacted/sec (score+select+gather+rerotate), % of HBM peak, 1 GPU"
 
 
 def parse():
@@ -47,57 +58,298 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w):
-    """Bytes the path must move at least once, per row and per call (the design doc
-    gives the derivation): score reads K once and Q once and writes the fp32
-    scores; select reads scores (and tags) and writes B indices; compaction
-    reads and writes B keys and values plus positions."""
-    G = w.group
-    T, d, W, B = w.n_tokens, w.head_dim, w.window, w.budget
+def cpu_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+
+def compaction_bytes(rows, T, d, G, W, B):
+    """Bytes each call must move at least once (the design doc gives the derivation):
+    score reads K and Q once and writes fp32 scores; select reads the scores
+    and tags and writes B indices; compaction reads and writes B keys and
+    values plus positions."""
     score = T * d * 2 + G * W * d * 2 + T * 4
     select = T * 4 + T + B * 4 + 4
     compact = 2 * B * d * 2 + 2 * B * d * 2 + B * 4 * 2
     path = T * d * 2 + G * W * d * 2 + 4 * B * d * 2 + 16 * B   # the whole path, scores kept on chip
-    return dict(score=score * w.rows, select=select * w.rows, compact=compact * w.rows,
-                path=path * w.rows)
+    decode = 2 * B * d * 2 + 2 * G * d * 2
+    return dict(kvc_score=score * rows, kvc_select=select * rows, kvc_compact_rerotate=compact * rows,
+                path=path * rows, kvc_decode_attn=decode * rows)
 
 
-def cpu_baseline(w, inp, budget_s):
-    """Time the float64 oracle over a prefix of the session's rows (D2H copies of
-    the exact input bytes), until about `budget_s` seconds of oracle work."""
+def roofline(bytes_per_call, ms, counters_name, workload):
+    achieved = bytes_per_call / (ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        c = json.load(open(COUNTERS_FILE))
+        ent = c.get("calls", {}).get(counters_name)
+        if ent and c.get("source_hash") == kernel_source_hash() and c.get("workload") == workload:
+            traffic = ent["hbm_bytes_per_call"]
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": counters_name,
+            "algorithmic_bytes": bytes_per_call}
+
+
+def per_call_rates(bytes_by_call, ms_by_call):
+    return {k: {"ms": round(ms_by_call[k], 4),
+                "GB_s": round(bytes_by_call[k] / (ms_by_call[k] * 1e-3) / 1e9, 1),
+                "hbm_frac": round(bytes_by_call[k] / (ms_by_call[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            for k in ms_by_call if k in bytes_by_call and ms_by_call[k] > 0}
+
+
+# ---------------------------------------------------------------- CPU oracle baselines
+
+def cpu_compaction_rows(K, V, Q, G, W, T, B, tags, bonus_tbl, n_sink, n_recent, renumber_base, rope_base,
+                        rows, budget_s, L, Hkv):
+    """Time the float64 oracle (score + select + gather/re-rotate) over a prefix
+    of `rows` (D2H copies of the exact input bytes) until about `budget_s`
+    seconds of oracle work. Returns (rows done, seconds)."""
     import numpy as np
     import torch
     from oracle import compact as o_compact, numfmt, policy as o_policy, score as o_score
     from oracle import select as o_select
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    G, W, T, B = w.group, w.window, w.n_tokens, w.budget
-    tbl = np.array([[0.0]] + [[0.0 if s is None else o_policy.foresight_bonus(1e3, 0.35, s)]
-                              for s in inp.spans.steps_ahead])
-    fl = np.zeros_like(tbl, dtype=np.uint8)
-    L, Hkv = w.n_layers, w.n_kv_heads
+    fl = np.zeros_like(bonus_tbl, dtype=np.uint8)
     done, spent = 0, 0.0
-    while spent < budget_s and done < w.rows:
+    while spent < budget_s and done < rows:
         r = done
         n, l, h = r // (L * Hkv), (r // Hkv) % L, r % Hkv
-        Kb = inp.K[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16)
-        Vb = inp.V[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16)
-        Qb = inp.Q_obs[n, l, h * G:(h + 1) * G].cpu().view(torch.int16).numpy().view(np.uint16)
+        Kb = K[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16)
+        Vb = V[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16)
+        Qb = Q[n, l, h * G:(h + 1) * G].cpu().view(torch.int16).numpy().view(np.uint16)
+        tg = tags[n].cpu().numpy() if tags is not None else np.zeros(T, np.uint8)
         t0 = time.perf_counter()
         s = o_score.obs_window_score(numfmt.bf16_bits_to_f64(Kb), numfmt.bf16_bits_to_f64(Qb), W)
-        tot, prot = o_policy.totals_and_protection(s, inp.spans.tags, tbl, fl, 0, w.n_sink, w.n_recent)
+        tot, prot = o_policy.totals_and_protection(s, tg, bonus_tbl, fl, 0, n_sink, n_recent)
         kept, _ = o_select.select_top_b(tot, prot, B)
-        o_compact.compact_row(Kb, Vb, np.arange(T), kept, w.renumber_base, w.rope_base)
+        o_compact.compact_row(Kb, Vb, np.arange(T), kept, renumber_base, rope_base)
         spent += time.perf_counter() - t0
         done += 1
-    rate = T * (done / w.rows) / spent
-    return {"value": rate, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {w.rows} (layer, KV head) rows of one {T}-token session, "
-                      f"float64 numpy oracle (score+select+gather/re-rotate), "
-                      f"{spent:.1f} s of oracle time scaled to the whole session"}
+    return done, spent
+
+
+def oracle_bonus(steps_ahead):
+    import numpy as np
+    from oracle import policy as o_policy
+    return np.array([[0.0]] + [[0.0 if s is None else o_policy.foresight_bonus(1e3, 0.35, s)]
+                               for s in steps_ahead])
+
+
+# ---------------------------------------------------------------- workloads
+
+def bench_compaction(args, w, dev):
+    """score -> select -> compact over every row (one layer per call for the
+    1M-token session), then decode over the compacted cache."""
+    import torch
+    from budgeted_retention_amd import kvc, synth
+    inp = synth.make_compaction_inputs(w, dev)
+    N, L, Hkv, Hq, d, T, W, B = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
+                                 w.n_tokens, w.window, w.budget)
+    per_layer = w.n_tokens > (1 << 20) - 1
+    chunks = [(l, l + 1) for l in range(L)] if per_layer else [(0, L)]
+    Lc = chunks[0][1] - chunks[0][0]
+    rows_c = N * Lc * Hkv
+    dims = kvc.make_dims(N, Lc, Hkv, Hq, d, T)
+    vals = [0.0] + [0.0 if s is None else kvc.kvc_foresight_bonus(1e3, 0.35, s) for s in inp.spans.steps_ahead]
+    bonus = torch.tensor(vals, dtype=torch.float32, device=dev).reshape(-1, 1)
+    pols = [kvc.Policy(w.n_sink, w.n_recent, B, len(vals), 1, l0, L, inp.tags, bonus) for l0, _ in chunks]
+    ws = kvc.workspace(kvc.KVC_OP_SCORE, dims, W, 0, dev)
+    scores = torch.empty((rows_c, T), dtype=torch.float32, device=dev)
+    kept = torch.empty((rows_c, B), dtype=torch.int32, device=dev)
+    n_kept = torch.empty(rows_c, dtype=torch.int32, device=dev)
+    Ko = torch.empty((rows_c, B, d), dtype=torch.bfloat16, device=dev)
+    Vo = torch.empty_like(Ko)
+    po = torch.empty((rows_c, B), dtype=torch.int32, device=dev)
+    nh = torch.empty(rows_c, dtype=torch.int32, device=dev)
+    out = kvc.CompactOut(B, Ko, Vo, po, nh)
+    dims_d = kvc.make_dims(N, Lc, Hkv, Hq, d, B)
+    wsd = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_d, B, 0)), dtype=torch.uint8, device=dev)
+    o = torch.empty((N, Lc, Hq, d), dtype=torch.bfloat16, device=dev)
+    views = []
+    for l0, l1 in chunks:
+        Kc, Vc, Qc, qc = inp.K[:, l0:l1], inp.V[:, l0:l1], inp.Q_obs[:, l0:l1], inp.q_dec[:, l0:l1]
+        assert all(t.is_contiguous() for t in (Kc, Vc, Qc, qc))
+        views.append((Kc, Vc, Qc, qc))
+    names = ["kvc_score", "kvc_select", "kvc_compact_rerotate", "kvc_decode_attn"]
+
+    def step(ev=None):
+        for (Kc, Vc, Qc, qc), pol in zip(views, pols):
+            if ev is not None:
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record()
+            kvc.kvc_score(dims, Kc, Qc, W, scores, ws)
+            if ev is not None:
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record()
+            kvc.kvc_select(dims, scores, pol, kept, B, n_kept)
+            if ev is not None:
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record()
+            kvc.kvc_compact_rerotate(dims, Kc, Vc, None, kept, B, n_kept, w.renumber_base, w.rope_base, out)
+            if ev is not None:
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record()
+            kvc.kvc_decode_attn(dims_d, qc, Ko, Vo, nh, B, o, wsd)
+            if ev is not None:
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record()
+
+    calibrate_copy(args, dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part = {n: 0.0 for n in names}
+    for ev in evs:
+        for c in range(len(chunks)):
+            for i, n in enumerate(names):
+                part[n] += ev[5 * c + i].elapsed_time(ev[5 * c + i + 1])
+    part = {n: v / args.steps for n, v in part.items()}
+    if not (n_kept == B).all():
+        raise SystemExit("bench: a row kept a number of tokens other than the budget")
+    ms = part["kvc_score"] + part["kvc_select"] + part["kvc_compact_rerotate"]
+    ab = compaction_bytes(w.rows, T, d, w.group, W, B)
+    path_calls = names[:3]
+    dom = max(path_calls, key=lambda n: part[n])
+    roof = roofline(ab[dom], part[dom], dom, w.name)
+    cpu = None
+    if args.cpu_seconds > 0:
+        done, spent = cpu_compaction_rows(inp.K, inp.V, inp.Q_obs, w.group, W, T, B, inp.tags,
+                                          oracle_bonus(inp.spans.steps_ahead), w.n_sink, w.n_recent,
+                                          w.renumber_base, w.rope_base, w.rows, args.cpu_seconds, L, Hkv)
+        cpu = {"value": T * N * (done / w.rows) / spent, "unit": "tokens/s", "cores": cpu_cores(),
+               "kind": "oracle",
+               "sample": f"{done} of {w.rows} (layer, KV head) rows of one {T}-token session, float64 numpy "
+                         f"oracle (score+select+gather/re-rotate), {spent:.1f} s of oracle time scaled to "
+                         f"the whole session"}
+    value = N * T / (ms * 1e-3)
+    config = {"workload": w.name, "n_seq": N, "layers": L, "kv_heads": Hkv, "q_heads": Hq, "head_dim": d,
+              "tokens": T, "window": W, "budget": B, "sink": w.n_sink, "recent": w.n_recent,
+              "rope_base": w.rope_base, "layers_per_call": Lc, "parallelism": "none"}
+    extra = {"hbm_frac_path": round(ab["path"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "breakdown_ms": {n: round(part[n], 4) for n in path_calls},
+             "decode_ms": round(part["kvc_decode_attn"], 4),
+             "calls": per_call_rates(ab, part),
+             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}
+    return value, ms, config, roof, cpu, extra
+
+
+def bench_pipeline(args, w, dev, kind):
+    """The mixed-precision or page-lifecycle workload, every call timed."""
+    import numpy as np
+    import torch
+    from budgeted_retention_amd import pipelines, synth
+    if kind == "pask":
+        inp = synth.make_pask_inputs(w, dev)
+        run = lambda timer=None: pipelines.run_pask(w, inp, timer)   # noqa: E731
+        tokens = w.n_seq * (w.n_prompt + w.n_gen)
+    else:
+        inp = synth.make_commit_inputs(w, dev)
+        run = lambda timer=None: pipelines.run_commit(w, inp, [w.tau_joint], timer)   # noqa: E731
+        tokens = w.n_seq * w.n_tokens
+    calibrate_copy(args, dev)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    timer = pipelines.CallTimer()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = run(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part = {k: v / args.steps for k, v in timer.totals_ms().items()}
+    host = {k: round(v * 1e3 / args.steps, 3) for k, v in timer.host.items()}
+    d, Hkv, G, W = w.head_dim, w.n_kv_heads, w.n_q_heads // w.n_kv_heads, w.window
+    rows = w.rows
+    if kind == "pask":
+        Tp, Tg, B = w.n_prompt, w.n_gen, w.budget
+        n_h = int(res["n_h"].sum().item())                  # bf16 pool tokens (kept prompt + bf16 tier)
+        n_l = int(res["n_l"].sum().item())                  # int8 pool tokens
+        n_hg = n_h - rows * B                               # generated tokens routed to bf16
+        ab = {"kvc_score": rows * (Tp * d * 2 + G * W * d * 2 + Tp * 4),
+              "kvc_select": rows * (Tp * 4 + B * 4),
+              "kvc_compact_rerotate:prompt": rows * (2 * B * d * 2 * 2 + B * 4),
+              # every generated token's K, V, action, index and position read; the bf16
+              # tier written with positions, the int8 tier as codes, fp16 scales, positions
+              "kvc_compact_rerotate:tiered": rows * Tg * (2 * d * 2 + 1 + 4 + 4) + n_hg * (2 * d * 2 + 4)
+                                             + n_l * (2 * d + 2 * 2 + 4),
+              # both pools read once, queries read and outputs written
+              "kvc_decode_attn": n_h * 2 * d * 2 + n_l * (2 * d + 2 * 2)
+                                 + w.n_seq * w.n_layers * w.n_q_heads * d * 2 * 2}
+        path_calls = ["kvc_score", "kvc_select", "kvc_compact_rerotate:prompt", "kvc_compact_rerotate:tiered"]
+    else:
+        T, B, P, ps = w.n_tokens, w.budget, w.n_pages_all, w.page_size
+        lrows = w.n_seq * Hkv          # rows of the deciding layer
+        ab = {"kvc_page_effect:pre": lrows * (2 * T * d * 2 + G * W * d * 2),
+              "kvc_page_effect:post": lrows * (2 * T * d * 2 + G * W * d * 2),
+              "kvc_page_retire": lrows * (2 * T * d * 2 + G * W * d * 2),
+              "kvc_score": rows * (T * d * 2 + G * W * d * 2 + T * 4),
+              "kvc_page_scores": rows * T * 4 + w.n_seq * P * 4,
+              "kvc_select": w.n_seq * (P * 4 + (B // ps) * 4),
+              "kvc_compact_rerotate": rows * (2 * B * d * 2 * 2 + B * 4),
+              "kvc_decode_attn:pool": rows * 2 * B * d * 2,
+              "kvc_decode_attn:paged": rows * 2 * B * d * 2}
+        path_calls = ["kvc_page_effect:pre", "kvc_page_effect:post", "kvc_page_retire", "kvc_score",
+                      "kvc_page_scores", "kvc_select", "kvc_compact_rerotate"]
+    ms = sum(part[k] for k in path_calls)
+    dom = max(path_calls, key=lambda k: part[k])
+    roof = roofline(ab[dom], part[dom], dom, w.name)
+    cpu = None
+    if args.cpu_seconds > 0:
+        if kind == "pask":
+            done, spent = cpu_compaction_rows(inp.K, inp.V, inp.Q_obs, G, W, w.n_prompt, w.budget, None,
+                                              np.zeros((1, 1)), w.n_sink, w.n_recent, -1, w.rope_base, rows,
+                                              args.cpu_seconds, w.n_layers, Hkv)
+            cpu = {"value": w.n_seq * w.n_prompt * (done / rows) / spent, "unit": "tokens/s",
+                   "cores": cpu_cores(), "kind": "oracle",
+                   "sample": f"{done} of {rows} prompt rows (score+select+gather), float64 numpy oracle, "
+                             f"{spent:.1f} s scaled to all prompt tokens"}
+        else:
+            done, spent = cpu_compaction_rows(inp.K, inp.V, inp.Q_post, G, W, w.n_tokens, w.budget, None,
+                                              np.zeros((1, 1)), 0, 0, -1, 1e6, rows, args.cpu_seconds,
+                                              w.n_layers, Hkv)
+            cpu = {"value": w.n_seq * w.n_tokens * (done / rows) / spent, "unit": "tokens/s",
+                   "cores": cpu_cores(), "kind": "oracle",
+                   "sample": f"{done} of {rows} rows: post-commit window score + per-row top-B and gather "
+                             f"(float64 numpy oracle), {spent:.1f} s scaled to all rows; the page effects "
+                             f"are not in the sample"}
+    value = tokens / (ms * 1e-3)
+    if kind == "pask":
+        config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "layer_groups": w.n_groups,
+                  "kv_heads": Hkv, "q_heads": w.n_q_heads, "head_dim": d, "prompt": w.n_prompt,
+                  "generated": w.n_gen, "window": W, "budget": w.budget, "byte_budget": w.budget_fraction,
+                  "parallelism": "none"}
+    else:
+        config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "kv_heads": Hkv,
+                  "q_heads": w.n_q_heads, "head_dim": d, "tokens": w.n_tokens, "page": w.page_size,
+                  "window": W, "budget": w.budget, "decision_layer": w.layer, "parallelism": "none"}
+    extra = {"breakdown_ms": {k: round(part[k], 4) for k in path_calls},
+             "other_ms": {k: round(v, 4) for k, v in part.items() if k not in path_calls},
+             "host_ms": host, "calls": per_call_rates(ab, part),
+             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}
+    return value, ms, config, roof, cpu, extra
+
+
+def calibrate_copy(args, dev):
+    import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
 
 def main():
@@ -107,102 +359,26 @@ def main():
               "needs no communication, so N GPUs would each run their own rows.", file=sys.stderr)
         sys.exit(2)
     import torch
-    from budgeted_retention_amd import kvc, synth
+    from budgeted_retention_amd import synth
 
-    w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = synth.make_compaction_inputs(w, dev)
-    N, L, Hkv, Hq, d, T, W, B = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
-                                 w.n_tokens, w.window, w.budget)
-    rows = w.rows
-    dims = kvc.make_dims(N, L, Hkv, Hq, d, T)
-    vals = [0.0] + [0.0 if s is None else kvc.kvc_foresight_bonus(1e3, 0.35, s)
-                    for s in inp.spans.steps_ahead]
-    bonus = torch.tensor(vals, dtype=torch.float32, device=dev).reshape(-1, 1)
-    pol = kvc.Policy(w.n_sink, w.n_recent, B, len(vals), 1, 0, L, inp.tags, bonus)
-    ws = kvc.workspace(kvc.KVC_OP_SCORE, dims, W, 0, dev)
-    scores = torch.empty((rows, T), dtype=torch.float32, device=dev)
-    kept = torch.empty((rows, B), dtype=torch.int32, device=dev)
-    n_kept = torch.empty(rows, dtype=torch.int32, device=dev)
-    Ko = torch.empty((rows, B, d), dtype=torch.bfloat16, device=dev)
-    Vo = torch.empty_like(Ko)
-    po = torch.empty((rows, B), dtype=torch.int32, device=dev)
-    nh = torch.empty(rows, dtype=torch.int32, device=dev)
-    out = kvc.CompactOut(B, Ko, Vo, po, nh)
-
-    def step(ev=None):
-        if ev:
-            ev[0].record()
-        kvc.kvc_score(dims, inp.K, inp.Q_obs, W, scores, ws)
-        if ev:
-            ev[1].record()
-        kvc.kvc_select(dims, scores, pol, kept, B, n_kept)
-        if ev:
-            ev[2].record()
-        kvc.kvc_compact_rerotate(dims, inp.K, inp.V, None, kept, B, n_kept, w.renumber_base,
-                                 w.rope_base, out)
-        if ev:
-            ev[3].record()
-
-    if args.calibrate_copy:
-        n = args.calibrate_copy * (1 << 20) // 2
-        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs]
-    step_ms = [sum(p) for p in per]
-    ms = sum(step_ms) / len(step_ms)
-    part_ms = [sum(p[i] for p in per) / len(per) for i in range(3)]
-    if not (n_kept == B).all():
-        raise SystemExit("bench: a row kept a number of tokens other than the budget")
-
-    ab = algorithmic_bytes(w)
-    names = ["kvc_score", "kvc_select", "kvc_compact_rerotate"]
-    keys = ["score", "select", "compact"]
-    dom = max(range(3), key=lambda i: part_ms[i])
-    achieved = ab[keys[dom]] / (part_ms[dom] * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(COUNTERS_FILE):
-        c = json.load(open(COUNTERS_FILE))
-        ent = c.get("calls", {}).get(names[dom])
-        if ent and c.get("source_hash") == kernel_source_hash() and c.get("workload") == w.name:
-            traffic = ent["hbm_bytes_per_call"]
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": names[dom],
-            "algorithmic_bytes": ab[keys[dom]]}
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, inp, args.cpu_seconds)
-
-    value = N * T / (ms * 1e-3)
+    if args.workload in synth.WORKLOADS:
+        w = synth.WORKLOADS[args.workload]
+        value, ms, config, roof, cpu, extra = bench_compaction(args, w, dev)
+    elif args.workload in synth.PASK_WORKLOADS:
+        w = synth.PASK_WORKLOADS[args.workload]
+        value, ms, config, roof, cpu, extra = bench_pipeline(args, w, dev, "pask")
+    elif args.workload in synth.COMMIT_WORKLOADS:
+        w = synth.COMMIT_WORKLOADS[args.workload]
+        value, ms, config, roof, cpu, extra = bench_pipeline(args, w, dev, "commit")
+    else:
+        raise SystemExit(f"unknown workload {args.workload}")
     line = {
-        "metric": "KV tokens compacted/sec (score+select+gather+rerotate), % of HBM peak, 1 GPU",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "n_seq": N, "layers": L, "kv_heads": Hkv, "q_heads": Hq,
-                   "head_dim": d, "tokens": T, "window": W, "budget": B, "sink": w.n_sink,
-                   "recent": w.n_recent, "rope_base": w.rope_base, "parallelism": "none"},
-        "hbm_frac_path": round(ab["path"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "breakdown_ms": {n: round(t, 4) for n, t in zip(names, part_ms)},
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
+        **extra, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

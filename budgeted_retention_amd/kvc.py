@@ -18,6 +18,8 @@ KVC_OP_SCORE = _lib.KVC_OP_SCORE
 KVC_OP_SELECT = _lib.KVC_OP_SELECT
 KVC_OK = _lib.KVC_OK
 KVC_WARN_FLOOR_EXCESS = _lib.KVC_WARN_FLOOR_EXCESS
+# kvc_compact_out.action codes (PASK {R, L, H}): release, int8 tier, bf16 tier
+ACT_RELEASE, ACT_INT8, ACT_BF16 = 0, 1, 2
 KvcError = _lib.KvcError
 
 

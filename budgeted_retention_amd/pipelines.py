@@ -1,0 +1,194 @@
+"""Whole-workload runs through the C ABI: the mixed-precision (PASK-style) and
+page-lifecycle (CommitKV-style) workloads, call by call.
+
+Each run takes an optional `timer`: a callable returning a context manager per
+call name. bench.py passes one that brackets every GPU call with HIP events on
+the current stream and every host step with the wall clock; the parity tests
+pass none. Argument marshalling only: every step runs in libkvc.
+"""
+import contextlib
+import time
+
+import numpy as np
+import torch
+
+from . import kvc
+
+
+def _null_timer(name):
+    return contextlib.nullcontext()
+
+
+class CallTimer:
+    """Per-call timing: HIP events around GPU calls (on the current stream),
+    wall clock around host steps (names starting with 'host:')."""
+
+    def __init__(self):
+        self.events = []     # (name, start event, end event)
+        self.host = {}       # name -> seconds
+
+    @contextlib.contextmanager
+    def __call__(self, name):
+        if name.startswith("host:"):
+            t0 = time.perf_counter()
+            yield
+            self.host[name] = self.host.get(name, 0.0) + time.perf_counter() - t0
+            return
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        yield
+        b.record()
+        self.events.append((name, a, b))
+
+    def totals_ms(self):
+        """Sum of event-timed milliseconds per call name (synchronises)."""
+        torch.cuda.synchronize()
+        out = {}
+        for name, a, b in self.events:
+            out[name] = out.get(name, 0.0) + a.elapsed_time(b)
+        return out
+
+
+def run_pask(w, inp, timer=None):
+    """The mixed-precision workload: the prompt of every row scored by its
+    observation window, compacted to B tokens with positions kept; the
+    generated tokens' tags drive the per-token controller, each row takes its
+    layer group's action (the last gen_recent tokens stay bf16) and its tokens
+    are appended to the bf16 pool, quantised into the int8 pool or released;
+    decode attention at the next position runs over both pools."""
+    t = timer or _null_timer
+    N, L, Hkv, Hq, d, Tp, Tg, W, B = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
+                                      w.n_prompt, w.n_gen, w.window, w.budget)
+    dev = inp.K.device
+    rows = N * L * Hkv
+    S = B + Tg                                         # pool capacity: kept prompt + every generated token
+    dims_p = kvc.make_dims(N, L, Hkv, Hq, d, Tp)
+    scores = torch.empty((N, L, Hkv, Tp), dtype=torch.float32, device=dev)
+    ws = kvc.workspace(kvc.KVC_OP_SCORE, dims_p, W, 0, dev)
+    with t("kvc_score"):
+        kvc.kvc_score(dims_p, inp.K, inp.Q_obs, W, scores, ws)
+    pol = kvc.Policy(w.n_sink, w.n_recent, B, 1, 1, 0, L, None,
+                     torch.zeros((1, 1), dtype=torch.float32, device=dev))
+    kept = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
+    nk = torch.zeros(rows, dtype=torch.int32, device=dev)
+    with t("kvc_select"):
+        st = kvc.kvc_select(dims_p, scores, pol, kept, B, nk)
+    Ko = torch.zeros((rows, S, d), dtype=torch.bfloat16, device=dev)
+    Vo = torch.zeros_like(Ko)
+    po = torch.full((rows, S), -1, dtype=torch.int32, device=dev)
+    nh0 = torch.zeros(rows, dtype=torch.int32, device=dev)
+    with t("kvc_compact_rerotate:prompt"):
+        kvc.kvc_compact_rerotate(dims_p, inp.K, inp.V, None, kept, B, nk, -1, w.rope_base,
+                                 kvc.CompactOut(S, Ko, Vo, po, nh0))
+    # controller per generated token, then each row's action from its layer group
+    with t("host:kvc_host_pask_control"):
+        grp = np.array([kvc.kvc_layer_group(l, L, w.n_groups) for l in range(L)])
+        costs = kvc.kvc_host_pask_costs(np.bincount(grp, minlength=w.n_groups), Hkv, d, 8)
+        acts, ledger = kvc.kvc_host_pask_control(inp.a0, inp.amin, inp.prio, inp.critical, costs,
+                                                 w.budget_fraction, inp.tags)
+    act_rows = np.ascontiguousarray(np.broadcast_to(
+        acts[:, :, grp].transpose(0, 2, 1)[:, :, None, :], (N, L, Hkv, Tg)))
+    act_rows[..., Tg - w.gen_recent:] = kvc.ACT_BF16      # the recent window stays bf16
+    action = torch.from_numpy(act_rows.reshape(rows, Tg)).to(dev)
+    kept_g = torch.arange(Tg, dtype=torch.int32, device=dev).expand(rows, Tg).contiguous()
+    pos_g = (Tp + kept_g).contiguous()
+    nk_g = torch.full((rows,), Tg, dtype=torch.int32, device=dev)
+    Kq = torch.zeros((rows, S, d), dtype=torch.int8, device=dev)
+    Vq = torch.zeros_like(Kq)
+    Ks = torch.zeros((rows, S), dtype=torch.int16, device=dev)
+    Vs = torch.zeros_like(Ks)
+    pq = torch.full((rows, S), -1, dtype=torch.int32, device=dev)
+    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
+    nl = torch.zeros(rows, dtype=torch.int32, device=dev)
+    dims_g = kvc.make_dims(N, L, Hkv, Hq, d, Tg)
+    with t("kvc_compact_rerotate:tiered"):
+        kvc.kvc_compact_rerotate(dims_g, inp.K_gen, inp.V_gen, pos_g, kept_g, Tg, nk_g, -1, w.rope_base,
+                                 kvc.CompactOut(S, Ko, Vo, po, nh, action, Kq, Vq, Ks, Vs, pq, nl, h_base=nh0))
+    dims_d = kvc.make_dims(N, L, Hkv, Hq, d, S)
+    wsd = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_d, S, S)), dtype=torch.uint8, device=dev)
+    o = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((N, L, Hq), dtype=torch.float32, device=dev)
+    with t("kvc_decode_attn"):
+        kvc.kvc_decode_attn(dims_d, inp.q_dec, Ko, Vo, nh, S, o, wsd, lse, None, 0, 0, Kq, Vq, Ks, Vs, nl, S)
+    return dict(status=st, scores=scores, kept=kept, n_kept=nk, acts=acts, ledger=ledger, Ko=Ko, Vo=Vo,
+                pos=po, n_h=nh, Kq=Kq, Vq=Vq, Ks=Ks, Vs=Vs, pos_q=pq, n_l=nl, o=o, lse=lse)
+
+
+def run_commit(w, inp, taus, timer=None):
+    """The page-lifecycle workload at one commit: page deletion effects in the
+    pre- and post-commit windows, lifecycle labels and candidate order (host),
+    greedy joint retirement for every bound in `taus` (the first feeds the
+    checkpoint), checkpoint page scores from the post-commit window, the
+    retained page set, the compaction of keys, values and positions by that
+    one page set, and decode attention at the next position over the
+    compacted pool and over a paged view of the original storage."""
+    t = timer or _null_timer
+    N, L, Hkv, Hq, d, T, W, ps = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
+                                  w.n_tokens, w.window, w.page_size)
+    dev = inp.K.device
+    dims = kvc.make_dims(N, L, Hkv, Hq, d, T)
+    ws = kvc.page_workspace(dims, W, w.q_first_post, dev)
+    Rm = torch.empty((N, w.n_eligible), dtype=torch.float32, device=dev)
+    Rp = torch.empty_like(Rm)
+    with t("kvc_page_effect:pre"):
+        kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_pre, W, w.q_first_pre, ps, w.n_eligible, Rm, ws)
+    with t("kvc_page_effect:post"):
+        kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible, Rp, ws)
+    with t("host:kvc_host_commit_candidates"):
+        Rm_h, Rp_h = Rm.cpu().numpy(), Rp.cpu().numpy()
+        states, orders, n_orders = [], [], []
+        for n in range(N):
+            st, od, no = kvc.kvc_host_commit_candidates(Rm_h[n], Rp_h[n], w.tau_use, w.tau_dead, w.rho_use,
+                                                         w.rho_dead, w.max_scan)
+            states.append(st)
+            orders.append(od)
+            n_orders.append(no)
+        order = torch.from_numpy(np.stack(orders)).to(dev)
+    retire = []
+    for k, tau in enumerate(taus):
+        acc = torch.zeros((N, w.max_scan), dtype=torch.uint8, device=dev)
+        jr = torch.zeros((N, w.max_scan), dtype=torch.float32, device=dev)
+        with t("kvc_page_retire" if k == 0 else f"kvc_page_retire:{k}"):
+            kvc.kvc_page_retire(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible,
+                                order, tau, acc, ws, jr)
+        retire.append((acc, jr))
+    acc = retire[0][0]
+    # checkpoint: page scores from the post-commit window, best pages kept for every row
+    scores = torch.empty((N, L, Hkv, T), dtype=torch.float32, device=dev)
+    wss = kvc.workspace(kvc.KVC_OP_SCORE, dims, W, 0, dev)
+    with t("kvc_score"):
+        kvc.kvc_score(dims, inp.K, inp.Q_post, W, scores, wss)
+    P, Bp, B = w.n_pages_all, w.budget // ps, w.budget
+    pscore = torch.empty((N, P), dtype=torch.float32, device=dev)
+    with t("kvc_page_scores"):
+        kvc.kvc_page_scores(dims, scores, ps, P, pscore, order, acc)
+    pol = kvc.Policy(0, 0, Bp, 1, 1, 0, 1, None, torch.zeros((1, 1), dtype=torch.float32, device=dev))
+    kept = torch.full((N, Bp), -1, dtype=torch.int32, device=dev)
+    nk = torch.zeros(N, dtype=torch.int32, device=dev)
+    with t("kvc_select"):
+        kvc.kvc_select(kvc.make_dims(N, 1, 1, 1, 64, P), pscore, pol, kept, Bp, nk)
+    rows = N * L * Hkv
+    Ko = torch.zeros((rows, B, d), dtype=torch.bfloat16, device=dev)
+    Vo = torch.zeros_like(Ko)
+    po = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
+    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
+    with t("kvc_compact_rerotate"):
+        kvc.kvc_compact_rerotate(dims, inp.K, inp.V, None, kept, Bp, nk, -1, 1e6,
+                                 kvc.CompactOut(B, Ko, Vo, po, nh, kept_page=ps))
+    # decode at position T: over the compacted pool, and through a block table of the kept pages
+    dims_c = kvc.make_dims(N, L, Hkv, Hq, d, B)
+    o1 = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
+    o2 = torch.empty_like(o1)
+    lse1 = torch.empty((N, L, Hq), dtype=torch.float32, device=dev)
+    lse2 = torch.empty_like(lse1)
+    ws1 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_c, B, 0)), dtype=torch.uint8, device=dev)
+    with t("kvc_decode_attn:pool"):
+        kvc.kvc_decode_attn(dims_c, inp.q_dec, Ko, Vo, nh, B, o1, ws1, lse1)
+    ws2 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims, Bp * ps, 0)), dtype=torch.uint8, device=dev)
+    n_all = torch.full((rows,), B, dtype=torch.int32, device=dev)
+    with t("kvc_decode_attn:paged"):
+        kvc.kvc_decode_attn(dims, inp.q_dec, inp.K, inp.V, n_all, T, o2, ws2, lse2, kept, ps, Bp)
+    return dict(Rm=Rm, Rp=Rp, states=np.stack(states), order=np.stack(orders), n_order=np.array(n_orders),
+                retire=retire, scores=scores, pscore=pscore, kept=kept, n_kept=nk, Ko=Ko, Vo=Vo, pos=po, n_h=nh,
+                o1=o1, o2=o2, lse1=lse1, lse2=lse2)

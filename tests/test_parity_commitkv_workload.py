@@ -30,69 +30,17 @@ EFF_RTOL, EFF_ATOL = 1e-2, 1e-7
 
 
 def run_commit(w, inp, taus):
-    """The commit on the GPU. `taus`: joint bounds to run the retirement with
-    (the first one feeds the checkpoint). Returns host arrays."""
-    from budgeted_retention_amd import kvc
-    N, L, Hkv, Hq, d, T, W, ps = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
-                                  w.n_tokens, w.window, w.page_size)
-    dev = inp.K.device
-    dims = kvc.make_dims(N, L, Hkv, Hq, d, T)
-    ws = kvc.page_workspace(dims, W, w.q_first_post, dev)
-    Rm = torch.empty((N, w.n_eligible), dtype=torch.float32, device=dev)
-    Rp = torch.empty_like(Rm)
-    kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_pre, W, w.q_first_pre, ps, w.n_eligible, Rm, ws)
-    kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible, Rp, ws)
-    Rm_h, Rp_h = Rm.cpu().numpy(), Rp.cpu().numpy()
-    states, orders, n_orders = [], [], []
-    for n in range(N):
-        st, od, no = kvc.kvc_host_commit_candidates(Rm_h[n], Rp_h[n], w.tau_use, w.tau_dead, w.rho_use,
-                                                     w.rho_dead, w.max_scan)
-        states.append(st)
-        orders.append(od)
-        n_orders.append(no)
-    order = torch.from_numpy(np.stack(orders)).to(dev)
-    retire = []
-    for tau in taus:
-        acc = torch.zeros((N, w.max_scan), dtype=torch.uint8, device=dev)
-        jr = torch.zeros((N, w.max_scan), dtype=torch.float32, device=dev)
-        kvc.kvc_page_retire(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible,
-                            order, tau, acc, ws, jr)
-        retire.append((acc, jr))
-    acc = retire[0][0]
-    # checkpoint: page scores from the post-commit window, best pages kept for every row
-    scores = torch.empty((N, L, Hkv, T), dtype=torch.float32, device=dev)
-    kvc.kvc_score(dims, inp.K, inp.Q_post, W, scores, kvc.workspace(kvc.KVC_OP_SCORE, dims, W, 0, dev))
-    P, Bp, B = w.n_pages_all, w.budget // ps, w.budget
-    pscore = torch.empty((N, P), dtype=torch.float32, device=dev)
-    kvc.kvc_page_scores(dims, scores, ps, P, pscore, order, acc)
-    pol = kvc.Policy(0, 0, Bp, 1, 1, 0, 1, None, torch.zeros((1, 1), dtype=torch.float32, device=dev))
-    kept = torch.full((N, Bp), -1, dtype=torch.int32, device=dev)
-    nk = torch.zeros(N, dtype=torch.int32, device=dev)
-    kvc.kvc_select(kvc.make_dims(N, 1, 1, 1, 64, P), pscore, pol, kept, Bp, nk)
-    rows = N * L * Hkv
-    Ko = torch.zeros((rows, B, d), dtype=torch.bfloat16, device=dev)
-    Vo = torch.zeros_like(Ko)
-    po = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
-    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
-    kvc.kvc_compact_rerotate(dims, inp.K, inp.V, None, kept, Bp, nk, -1, 1e6,
-                             kvc.CompactOut(B, Ko, Vo, po, nh, kept_page=ps))
-    # decode at position T: over the compacted pool, and through a block table of the kept pages
-    dims_c = kvc.make_dims(N, L, Hkv, Hq, d, B)
-    o1 = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
-    o2 = torch.empty_like(o1)
-    lse1 = torch.empty((N, L, Hq), dtype=torch.float32, device=dev)
-    lse2 = torch.empty_like(lse1)
-    ws1 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_c, B, 0)), dtype=torch.uint8, device=dev)
-    kvc.kvc_decode_attn(dims_c, inp.q_dec, Ko, Vo, nh, B, o1, ws1, lse1)
-    ws2 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims, Bp * ps, 0)), dtype=torch.uint8, device=dev)
-    n_all = torch.full((rows,), B, dtype=torch.int32, device=dev)
-    kvc.kvc_decode_attn(dims, inp.q_dec, inp.K, inp.V, n_all, T, o2, ws2, lse2, kept, ps, Bp)
+    """The commit on the GPU (budgeted_retention_amd.pipelines.run_commit).
+    `taus`: joint bounds to run the retirement with (the first one feeds the
+    checkpoint). Host copies of the small outputs."""
+    from budgeted_retention_amd import pipelines
+    res = pipelines.run_commit(w, inp, taus)
     torch.cuda.synchronize()
-    return dict(Rm=Rm_h, Rp=Rp_h, states=np.stack(states), order=np.stack(orders), n_order=np.array(n_orders),
-                retire=[(a.cpu().numpy(), j.cpu().numpy()) for a, j in retire],
-                scores=scores, pscore=pscore.cpu().numpy(), kept=kept.cpu().numpy(), n_kept=nk.cpu().numpy(),
-                Ko=Ko, Vo=Vo, pos=po, n_h=nh.cpu().numpy(), o1=tl.f64(o1), o2=tl.f64(o2),
-                lse1=lse1.cpu().numpy(), lse2=lse2.cpu().numpy())
+    for k in ("Rm", "Rp", "pscore", "kept", "n_kept", "n_h", "lse1", "lse2"):
+        res[k] = res[k].cpu().numpy()
+    res["retire"] = [(a.cpu().numpy(), j.cpu().numpy()) for a, j in res["retire"]]
+    res["o1"], res["o2"] = tl.f64(res["o1"]), tl.f64(res["o2"])
+    return res
 
 
 def _layer_f64(inp, n, layer):

@@ -25,58 +25,15 @@ pytestmark = pytest.mark.gpu
 
 
 def run_pask(w, inp):
-    """The workload on the GPU. Returns host arrays (pools stay on the device)."""
-    from budgeted_retention_amd import kvc
-    N, L, Hkv, Hq, d, Tp, Tg, W, B = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
-                                      w.n_prompt, w.n_gen, w.window, w.budget)
-    dev = inp.K.device
-    rows = N * L * Hkv
-    S = B + Tg                                         # pool capacity: kept prompt + every generated token
-    dims_p = kvc.make_dims(N, L, Hkv, Hq, d, Tp)
-    scores = torch.empty((N, L, Hkv, Tp), dtype=torch.float32, device=dev)
-    kvc.kvc_score(dims_p, inp.K, inp.Q_obs, W, scores, kvc.workspace(kvc.KVC_OP_SCORE, dims_p, W, 0, dev))
-    pol = kvc.Policy(w.n_sink, w.n_recent, B, 1, 1, 0, L, None,
-                     torch.zeros((1, 1), dtype=torch.float32, device=dev))
-    kept = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
-    nk = torch.zeros(rows, dtype=torch.int32, device=dev)
-    st = kvc.kvc_select(dims_p, scores, pol, kept, B, nk)
-    Ko = torch.zeros((rows, S, d), dtype=torch.bfloat16, device=dev)
-    Vo = torch.zeros_like(Ko)
-    po = torch.full((rows, S), -1, dtype=torch.int32, device=dev)
-    nh0 = torch.zeros(rows, dtype=torch.int32, device=dev)
-    kvc.kvc_compact_rerotate(dims_p, inp.K, inp.V, None, kept, B, nk, -1, w.rope_base,
-                             kvc.CompactOut(S, Ko, Vo, po, nh0))
-    # controller per generated token, then each row's action from its layer group
-    grp = np.array([kvc.kvc_layer_group(l, L, w.n_groups) for l in range(L)])
-    costs = kvc.kvc_host_pask_costs(np.bincount(grp, minlength=w.n_groups), Hkv, d, 8)
-    acts, ledger = kvc.kvc_host_pask_control(inp.a0, inp.amin, inp.prio, inp.critical, costs,
-                                             w.budget_fraction, inp.tags)
-    act_rows = np.ascontiguousarray(np.broadcast_to(
-        acts[:, :, grp].transpose(0, 2, 1)[:, :, None, :], (N, L, Hkv, Tg)))
-    act_rows[..., Tg - w.gen_recent:] = o_pask.H_ACT
-    action = torch.from_numpy(act_rows.reshape(rows, Tg)).to(dev)
-    kept_g = torch.arange(Tg, dtype=torch.int32, device=dev).expand(rows, Tg).contiguous()
-    pos_g = (Tp + kept_g).contiguous()
-    nk_g = torch.full((rows,), Tg, dtype=torch.int32, device=dev)
-    Kq = torch.zeros((rows, S, d), dtype=torch.int8, device=dev)
-    Vq = torch.zeros_like(Kq)
-    Ks = torch.zeros((rows, S), dtype=torch.int16, device=dev)
-    Vs = torch.zeros_like(Ks)
-    pq = torch.full((rows, S), -1, dtype=torch.int32, device=dev)
-    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
-    nl = torch.zeros(rows, dtype=torch.int32, device=dev)
-    dims_g = kvc.make_dims(N, L, Hkv, Hq, d, Tg)
-    kvc.kvc_compact_rerotate(dims_g, inp.K_gen, inp.V_gen, pos_g, kept_g, Tg, nk_g, -1, w.rope_base,
-                             kvc.CompactOut(S, Ko, Vo, po, nh, action, Kq, Vq, Ks, Vs, pq, nl, h_base=nh0))
-    dims_d = kvc.make_dims(N, L, Hkv, Hq, d, S)
-    ws = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_d, S, S)), dtype=torch.uint8, device=dev)
-    o = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((N, L, Hq), dtype=torch.float32, device=dev)
-    kvc.kvc_decode_attn(dims_d, inp.q_dec, Ko, Vo, nh, S, o, ws, lse, None, 0, 0, Kq, Vq, Ks, Vs, nl, S)
+    """The workload on the GPU (budgeted_retention_amd.pipelines.run_pask); host
+    copies of the small outputs, the pools stay on the device."""
+    from budgeted_retention_amd import pipelines
+    res = pipelines.run_pask(w, inp)
     torch.cuda.synchronize()
-    return dict(status=st, scores=scores, kept=kept.cpu().numpy(), n_kept=nk.cpu().numpy(),
-                acts=acts, ledger=ledger, Ko=Ko, Vo=Vo, pos=po, n_h=nh.cpu().numpy(), Kq=Kq, Vq=Vq,
-                Ks=Ks, Vs=Vs, pos_q=pq, n_l=nl.cpu().numpy(), o=tl.f64(o), lse=lse.cpu().numpy())
+    for k in ("kept", "n_kept", "n_h", "n_l", "lse"):
+        res[k] = res[k].cpu().numpy()
+    res["o"] = tl.f64(res["o"])
+    return res
 
 
 def _oracle_actions(w, inp):
