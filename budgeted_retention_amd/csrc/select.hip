@@ -708,6 +708,320 @@ __global__ void __launch_bounds__(SEL_THREADS)
     if (tid == 0) n_kept[r] = (int32_t)(tot_g + (tot_e < (uint32_t)need ? tot_e : (uint32_t)need));
 }
 
+
+// ---------------------------------------------------------------- long rows
+//
+// Rows too long for one workgroup (a million-token session compacts a few
+// rows per call) are split into chunks of SPLIT_CHUNK tokens, each its own
+// workgroup. The same three radix digits are resolved in turn: every chunk
+// adds its digit histogram into the row's histogram in the workspace, and one
+// workgroup per row picks the bin where the budget-th key lies. With tau and
+// `need` fixed, every chunk counts its keys above and equal to tau, one
+// workgroup per row turns the counts into each chunk's first output slot and
+// first tie rank, and every chunk writes its kept indices in index order.
+// The decisions are those of the one-workgroup kernels (same keys, ties to the
+// lower index, floors before the budget).
+static constexpr int SPLIT_CHUNK = SEL_THREADS * SEL_VEC * 4;   // 16384 tokens per workgroup
+
+struct SplitState {
+    uint32_t prefix;   // digits resolved so far; after the last pick: tau
+    uint32_t k;        // rank of the budget-th key among keys with that prefix
+    uint32_t done;     // 1: tau/need final (every token, or every protected one)
+    uint32_t pad;
+    int64_t need;      // tau-valued tokens to keep (lowest indices first)
+};
+
+struct SplitWs {
+    uint32_t *hist;      // [rows][3][SEL_BINS]
+    SplitState *state;   // [rows]
+    uint32_t *cnt;       // [rows][chunks][2]  keys above / equal to tau
+    int64_t *base;       // [rows][chunks][2]  first output slot, tau-valued tokens before the chunk
+};
+
+static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool select_use_split(const kvc_dims *d) {
+    const int64_t T = d->n_tokens, rows = n_rows(d);
+    return T >= 262144 || (rows < 128 && T >= 32768);
+}
+
+static size_t split_bytes(int64_t rows, int64_t chunks) {
+    return align256s((size_t)rows * 3 * SEL_BINS * sizeof(uint32_t)) + align256s((size_t)rows * sizeof(SplitState)) +
+           align256s((size_t)rows * chunks * 2 * sizeof(uint32_t)) + align256s((size_t)rows * chunks * 2 * sizeof(int64_t));
+}
+
+static SplitWs split_layout(void *ws, int64_t rows, int64_t chunks) {
+    char *p = reinterpret_cast<char *>(ws);
+    SplitWs w;
+    w.hist = reinterpret_cast<uint32_t *>(p);
+    p += align256s((size_t)rows * 3 * SEL_BINS * sizeof(uint32_t));
+    w.state = reinterpret_cast<SplitState *>(p);
+    p += align256s((size_t)rows * sizeof(SplitState));
+    w.cnt = reinterpret_cast<uint32_t *>(p);
+    p += align256s((size_t)rows * chunks * 2 * sizeof(uint32_t));
+    w.base = reinterpret_cast<int64_t *>(p);
+    return w;
+}
+
+struct SplitArgs {
+    const float *scores;
+    const uint8_t *tags;
+    const float *bonus;
+    const uint8_t *floor_tbl;
+    int64_t T;
+    int L, Hkv, n_groups, layer_base, n_layers_model, n_tags, n_sink, n_recent, B;
+    int32_t *kept;
+    int kept_stride;
+    int32_t *n_kept;
+    int64_t chunks;
+};
+
+// Per-workgroup bonus/floor table of the row's layer group, and the row view.
+__device__ __forceinline__ SelRow split_row_view(const SplitArgs &a, int64_t r, float *s_bonus, uint8_t *s_floor) {
+    const RowIdx ri = split_row(r, a.L, a.Hkv);
+    const int grp = device_layer_group(a.layer_base + ri.l, a.n_layers_model, a.n_groups);
+    for (int t = threadIdx.x; t < 256; t += SEL_THREADS) {
+        s_bonus[t] = (a.bonus && t < a.n_tags) ? a.bonus[t * a.n_groups + grp] : 0.f;
+        s_floor[t] = (a.floor_tbl && t < a.n_tags) ? a.floor_tbl[t * a.n_groups + grp] : 0;
+    }
+    __syncthreads();
+    return SelRow{a.scores + (size_t)r * a.T, a.tags ? a.tags + (size_t)ri.n * a.T : nullptr, a.T, a.n_sink,
+                  a.n_recent, a.n_tags, s_bonus, s_floor};
+}
+
+__global__ void __launch_bounds__(SEL_THREADS) split_init(SplitWs w, int64_t rows) {
+    const int64_t n = rows * 3 * SEL_BINS;
+    for (int64_t i = (int64_t)blockIdx.x * SEL_THREADS + threadIdx.x; i < n; i += (int64_t)gridDim.x * SEL_THREADS)
+        w.hist[i] = 0u;
+    for (int64_t i = (int64_t)blockIdx.x * SEL_THREADS + threadIdx.x; i < rows; i += (int64_t)gridDim.x * SEL_THREADS)
+        w.state[i] = SplitState{0u, 0u, 0u, 0u, 0};
+}
+
+// Histogram of digit `pass` over one chunk, for the keys whose higher digits
+// equal the row's prefix.
+template <bool VEC>
+__global__ void __launch_bounds__(SEL_THREADS) split_hist(SplitArgs a, SplitWs w, int pass) {
+    __shared__ float s_bonus[256];
+    __shared__ uint8_t s_floor[256];
+    __shared__ uint32_t hist[SEL_BINS];
+    const int64_t r = blockIdx.x / a.chunks, c = blockIdx.x % a.chunks;
+    const SplitState st = w.state[r];
+    if (st.done) return;
+    const SelRow row = split_row_view(a, r, s_bonus, s_floor);
+    for (int t = threadIdx.x; t < SEL_BINS; t += SEL_THREADS) hist[t] = 0u;
+    __syncthreads();
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int width = pass == 2 ? 10 : 11;
+    const uint32_t mask = (1u << width) - 1u;
+    const int64_t c0 = c * SPLIT_CHUNK, c1 = c0 + SPLIT_CHUNK < a.T ? c0 + SPLIT_CHUNK : a.T;
+    for (int64_t base = c0 + (int64_t)threadIdx.x * SEL_VEC; base < c0 + SPLIT_CHUNK;
+         base += (int64_t)SEL_THREADS * SEL_VEC) {
+        uint32_t kk[SEL_VEC];
+        bool valid[SEL_VEC];
+        if (base < c1) {
+            row.keys4<VEC>(base, kk, valid);
+        } else {
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) valid[e] = false, kk[e] = 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < SEL_VEC; ++e) {
+            const bool active = valid[e] && (pass == 0 || (kk[e] >> (shift + width)) == st.prefix);
+            const uint32_t digit = (kk[e] >> shift) & mask;
+            if (pass == 0)
+                wave_hist_add(hist, active, digit);  // leading digits cluster in a few bins
+            else if (active)
+                atomicAdd(&hist[digit], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t *g = w.hist + ((size_t)r * 3 + pass) * SEL_BINS;
+    for (int t = threadIdx.x; t < (1 << width); t += SEL_THREADS)
+        if (hist[t]) atomicAdd(&g[t], hist[t]);
+}
+
+// One workgroup per row: the bin of digit `pass` holding the budget-th key.
+__global__ void __launch_bounds__(SEL_THREADS) split_pick(SplitArgs a, SplitWs w, int pass) {
+    __shared__ uint32_t hist[SEL_BINS];
+    __shared__ uint32_t s_wave[SEL_WAVES + 1];
+    __shared__ uint32_t s_pick[2];
+    const int64_t r = blockIdx.x;
+    SplitState st = w.state[r];
+    if (st.done) return;
+    const uint32_t *g = w.hist + ((size_t)r * 3 + pass) * SEL_BINS;
+    for (int t = threadIdx.x; t < SEL_BINS; t += SEL_THREADS) hist[t] = g[t];
+    __syncthreads();
+    if (pass == 0) {
+        if (a.T <= a.B) {  // every token is kept
+            st = SplitState{0u, 0u, 1u, 0u, a.T};
+        } else if (hist[SEL_BINS - 1] >= (uint32_t)a.B) {  // protected tokens fill the budget: keep them all
+            st = SplitState{KEY_PROTECTED, 0u, 1u, 0u, a.T};
+        }
+        if (st.done) {
+            if (threadIdx.x == 0) w.state[r] = st;
+            return;
+        }
+        st.k = (uint32_t)a.B;
+    }
+    const int width = pass == 2 ? 10 : 11;
+    uint32_t bin, rank;
+    pick_bin(hist, 1 << width, st.k, s_wave, s_pick, bin, rank);
+    st.prefix = (st.prefix << width) | bin;
+    st.k = rank;
+    if (pass == 2) {
+        st.done = 1u;
+        st.need = rank;
+    }
+    if (threadIdx.x == 0) w.state[r] = st;
+}
+
+// Keys above and equal to tau in one chunk.
+template <bool VEC>
+__global__ void __launch_bounds__(SEL_THREADS) split_count(SplitArgs a, SplitWs w) {
+    __shared__ float s_bonus[256];
+    __shared__ uint8_t s_floor[256];
+    __shared__ uint32_t s_wave[SEL_WAVES + 1];
+    const int64_t r = blockIdx.x / a.chunks, c = blockIdx.x % a.chunks;
+    const SplitState st = w.state[r];
+    const uint32_t tau = st.prefix;
+    const SelRow row = split_row_view(a, r, s_bonus, s_floor);
+    const int64_t c0 = c * SPLIT_CHUNK, c1 = c0 + SPLIT_CHUNK < a.T ? c0 + SPLIT_CHUNK : a.T;
+    uint32_t ngt = 0, neq = 0;
+    for (int64_t base = c0 + (int64_t)threadIdx.x * SEL_VEC; base < c1; base += (int64_t)SEL_THREADS * SEL_VEC) {
+        uint32_t kk[SEL_VEC];
+        bool valid[SEL_VEC];
+        row.keys4<VEC>(base, kk, valid);
+#pragma unroll
+        for (int e = 0; e < SEL_VEC; ++e) {
+            ngt += valid[e] && kk[e] > tau;
+            neq += valid[e] && kk[e] == tau;
+        }
+    }
+    uint32_t tg, te;
+    block_excl_scan(ngt, &tg, s_wave);
+    block_excl_scan(neq, &te, s_wave);
+    if (threadIdx.x == 0) {
+        w.cnt[((size_t)r * a.chunks + c) * 2] = tg;
+        w.cnt[((size_t)r * a.chunks + c) * 2 + 1] = te;
+    }
+}
+
+// One workgroup per row: each chunk's first output slot and the number of
+// tau-valued tokens before it; the row's kept count.
+__global__ void __launch_bounds__(SEL_THREADS) split_scan(SplitArgs a, SplitWs w) {
+    __shared__ uint32_t s_wave[SEL_WAVES + 1];
+    const int64_t r = blockIdx.x;
+    const int64_t need = w.state[r].need;
+    int64_t carry_g = 0, carry_e = 0;
+    for (int64_t c0 = 0; c0 < a.chunks; c0 += SEL_THREADS) {
+        const int64_t c = c0 + threadIdx.x;
+        const uint32_t g = c < a.chunks ? w.cnt[((size_t)r * a.chunks + c) * 2] : 0u;
+        const uint32_t e = c < a.chunks ? w.cnt[((size_t)r * a.chunks + c) * 2 + 1] : 0u;
+        // counts per chunk are at most SPLIT_CHUNK, so 1024 of them sum below 2^32
+        uint32_t tg, te;
+        const uint32_t eg = block_excl_scan(g, &tg, s_wave);
+        const uint32_t ee = block_excl_scan(e, &te, s_wave);
+        if (c < a.chunks) {
+            const int64_t eq_before = carry_e + ee;
+            w.base[((size_t)r * a.chunks + c) * 2] = carry_g + eg + (eq_before < need ? eq_before : need);
+            w.base[((size_t)r * a.chunks + c) * 2 + 1] = eq_before;
+        }
+        carry_g += tg;
+        carry_e += te;
+    }
+    if (threadIdx.x == 0) a.n_kept[r] = (int32_t)(carry_g + (carry_e < need ? carry_e : need));
+}
+
+// Every chunk writes its kept indices in index order from its first slot.
+template <bool VEC>
+__global__ void __launch_bounds__(SEL_THREADS) split_write(SplitArgs a, SplitWs w) {
+    __shared__ float s_bonus[256];
+    __shared__ uint8_t s_floor[256];
+    __shared__ uint32_t s_wave[SEL_WAVES + 1];
+    const int64_t r = blockIdx.x / a.chunks, c = blockIdx.x % a.chunks;
+    const SplitState st = w.state[r];
+    const uint32_t tau = st.prefix;
+    const int64_t need = st.need;
+    const SelRow row = split_row_view(a, r, s_bonus, s_floor);
+    const int64_t c0 = c * SPLIT_CHUNK, c1 = c0 + SPLIT_CHUNK < a.T ? c0 + SPLIT_CHUNK : a.T;
+    const int64_t slot0 = w.base[((size_t)r * a.chunks + c) * 2];
+    const int64_t eq0 = w.base[((size_t)r * a.chunks + c) * 2 + 1];
+    int32_t *kr = a.kept + (size_t)r * a.kept_stride;
+    // running counts from the chunk start: slot = slot0 + gt_seen + taken ties seen
+    int64_t carry_gt = 0, carry_eq = 0;
+    for (int64_t it = c0; it < c1; it += (int64_t)SEL_THREADS * SEL_VEC) {
+        const int64_t base = it + (int64_t)threadIdx.x * SEL_VEC;
+        uint32_t kk[SEL_VEC];
+        bool valid[SEL_VEC];
+        if (base < c1) {
+            row.keys4<VEC>(base, kk, valid);
+        } else {
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) valid[e] = false, kk[e] = 0u;
+        }
+        uint32_t ngt = 0, neq = 0;
+#pragma unroll
+        for (int e = 0; e < SEL_VEC; ++e) {
+            ngt += valid[e] && kk[e] > tau;
+            neq += valid[e] && kk[e] == tau;
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(ngt | (neq << 16), &tot, s_wave);
+        int64_t gt_before = carry_gt + (ex & 0xFFFFu);
+        int64_t eq_before = eq0 + carry_eq + (ex >> 16);
+#pragma unroll
+        for (int e = 0; e < SEL_VEC; ++e) {
+            const bool gt = valid[e] && kk[e] > tau;
+            const bool eq = valid[e] && kk[e] == tau;
+            if (gt || (eq && eq_before < need)) {
+                // slot0 already counts the ties taken before the chunk
+                const int64_t taken = (eq_before < need ? eq_before : need) - (eq0 < need ? eq0 : need);
+                const int64_t pos = slot0 + gt_before + taken;
+                if (pos < a.kept_stride) kr[pos] = (int32_t)(base + e);
+            }
+            gt_before += gt;
+            eq_before += eq;
+        }
+        carry_gt += tot & 0xFFFFu;
+        carry_eq += tot >> 16;
+    }
+}
+
+static int launch_select_split(const SplitArgs &a, int64_t rows, void *ws, bool vec, hipStream_t s) {
+    const SplitWs w = split_layout(ws, rows, a.chunks);
+    const int64_t grid_c = rows * a.chunks;
+    if (grid_c > (int64_t)INT32_MAX || rows > (int64_t)INT32_MAX)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_select: grid too large");
+    const dim3 block(SEL_THREADS);
+    const int64_t init_blocks = (rows * 3 * SEL_BINS + SEL_THREADS - 1) / SEL_THREADS;
+    split_init<<<dim3((unsigned)(init_blocks < 1024 ? init_blocks : 1024)), block, 0, s>>>(w, rows);
+    for (int pass = 0; pass < 3; ++pass) {
+        if (vec)
+            split_hist<true><<<dim3((unsigned)grid_c), block, 0, s>>>(a, w, pass);
+        else
+            split_hist<false><<<dim3((unsigned)grid_c), block, 0, s>>>(a, w, pass);
+        split_pick<<<dim3((unsigned)rows), block, 0, s>>>(a, w, pass);
+    }
+    if (vec)
+        split_count<true><<<dim3((unsigned)grid_c), block, 0, s>>>(a, w);
+    else
+        split_count<false><<<dim3((unsigned)grid_c), block, 0, s>>>(a, w);
+    split_scan<<<dim3((unsigned)rows), block, 0, s>>>(a, w);
+    if (vec)
+        split_write<true><<<dim3((unsigned)grid_c), block, 0, s>>>(a, w);
+    else
+        split_write<false><<<dim3((unsigned)grid_c), block, 0, s>>>(a, w);
+    return check_launch("kvc_select (long rows)");
+}
+
+// Workspace of kvc_select: the long-row path's histograms, per-row state and
+// per-chunk counts; 0 when the rows take the one-workgroup kernels.
+size_t select_workspace_bytes(const kvc_dims *d) {
+    if (!select_use_split(d)) return 0;
+    const int64_t chunks = (d->n_tokens + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
+    return split_bytes(n_rows(d), chunks);
+}
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -715,8 +1029,6 @@ using namespace kvc;
 extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_policy *p,
                           int32_t *kept_idx, int32_t kept_stride, int32_t *n_kept, void *ws,
                           size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     int st = check_dims(dims, "kvc_select");
     if (st != KVC_OK) return st;
     if (!scores || !p || !kept_idx || !n_kept) return fail(KVC_ERR_ARG, "kvc_select: NULL pointer");
@@ -741,7 +1053,15 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
     hipStream_t s = as_stream(stream);
     // rows whose decision map fits in LDS next to the candidate list
     const size_t cand_lds = (size_t)2 * SEL_CAND * sizeof(uint32_t) + (size_t)2 * ((T + 31) / 32) * sizeof(uint32_t);
-    if (vec && cand_lds <= 144 * 1024) {
+    if (select_use_split(dims)) {
+        const size_t need = select_workspace_bytes(dims);
+        if (!ws || ws_bytes < need)
+            return fail(KVC_ERR_WORKSPACE, "kvc_select: workspace %zu < %zu bytes (long rows)", ws_bytes, need);
+        SplitArgs a{scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers, dims->n_kv_heads, p->n_groups,
+                    p->layer_base, p->n_layers_model, p->n_tags, p->n_sink, p->n_recent, p->budget, kept_idx,
+                    kept_stride, n_kept, (T + SPLIT_CHUNK - 1) / SPLIT_CHUNK};
+        if ((st = launch_select_split(a, n_rows(dims), ws, vec, s)) != KVC_OK) return st;
+    } else if (vec && cand_lds <= 144 * 1024) {
         static bool lds_set = false;
         if (!lds_set) {
             if (hipFuncSetAttribute(reinterpret_cast<const void *>(&select_cand),
@@ -753,16 +1073,17 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
                                                   dims->n_kv_heads, p->n_groups, p->layer_base, p->n_layers_model,
                                                   p->n_tags, p->n_sink, p->n_recent, p->budget, kept_idx,
                                                   kept_stride, n_kept);
-    } else if (vec)
+    } else if (vec) {
         select_kernel<true><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                     dims->n_kv_heads, p->n_groups, p->layer_base,
                                                     p->n_layers_model, p->n_tags, p->n_sink, p->n_recent,
                                                     p->budget, kept_idx, kept_stride, n_kept);
-    else
+    } else {
         select_kernel<false><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                      dims->n_kv_heads, p->n_groups, p->layer_base,
                                                      p->n_layers_model, p->n_tags, p->n_sink, p->n_recent,
                                                      p->budget, kept_idx, kept_stride, n_kept);
+    }
     if ((st = check_launch("kvc_select")) != KVC_OK) return st;
     const int64_t sink_recent = (int64_t)p->n_sink + p->n_recent;
     if (T > p->budget && (sink_recent < T ? sink_recent : T) > p->budget) {

@@ -107,6 +107,12 @@ class Policy:
 
 
 def kvc_select(dims, scores, policy: Policy, kept_idx, kept_stride, n_kept, ws=None, stream=None):
+    """ws=None: a workspace of kvc_workspace_bytes(KVC_OP_SELECT) bytes is
+    allocated here when the rows need one (long rows), else none is passed."""
+    if ws is None:
+        n = kvc_workspace_bytes(KVC_OP_SELECT, dims, 0, policy.budget)
+        if n:
+            ws = torch.empty(n, dtype=torch.uint8, device=scores.device)
     pol = policy.to_c()
     st = _lib.load().kvc_select(
         ctypes.byref(dims), _ptr(scores, torch.float32, "scores"), ctypes.byref(pol),

@@ -136,7 +136,13 @@ double kvc_foresight_bonus(double sigma, double lambda, double steps_ahead);
  *   kept_stride  >= min(budget, T)
  *   n_kept     int32 [N][L][Hkv]  number of kept tokens; n_kept > budget
  *              reports floor excess (the device-side count is the authority)
- *   ws         kvc_workspace_bytes(KVC_OP_SELECT, ...) bytes (may be 0/NULL)
+ *   ws         device workspace of kvc_workspace_bytes(KVC_OP_SELECT, dims, 0, B)
+ *              bytes. It is 0 (ws may be NULL) unless the rows are long: T >=
+ *              262144, or fewer than 128 rows of T >= 32768. Such rows are
+ *              split over several workgroups whose histograms and counts meet
+ *              in the workspace; the call returns KVC_ERR_WORKSPACE before
+ *              enqueueing anything if it is missing or too small. The
+ *              workspace is overwritten; calls sharing one must not overlap.
  * Returns KVC_WARN_FLOOR_EXCESS (after enqueueing) when n_sink + n_recent
  * alone exceed the budget and T > budget.
  */

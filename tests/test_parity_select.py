@@ -4,7 +4,11 @@ The rows exercise what the kernels' selection paths branch on: many tied
 scores (the budget-th key inside a run of equal keys), a threshold bin larger
 than the on-chip candidate list (all scores equal), protection beyond the
 budget, rows no longer than the budget, rows whose length is not a multiple
-of four, and the long-row streaming path. Totals are formed as float32
+of four, and the long-row streaming path. Calls with at least 128 rows of up
+to 262,143 tokens take the one-workgroup-per-row kernels; fewer rows of at
+least 32,768 tokens, or any rows of 262,144 tokens and more, take the split
+path (several workgroups per row meeting in a workspace); the tests run both.
+Totals are formed as float32
 (score + bonus) on both sides, the kernel's precision, and the float64
 oracle selects on those values, so kept sets must match exactly.
 """
@@ -48,30 +52,32 @@ def _oracle(score_row, tags, bonus, floor, n_sink, n_recent, B):
     return kept
 
 
-def _check(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=None):
+def _check(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=None, check_rows=None):
     st, kept, n_kept = _run_select(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride)
-    for r in range(scores.shape[0]):
+    for r in (range(scores.shape[0]) if check_rows is None else check_rows):
         ref = _oracle(scores[r], tags, bonus, floor, n_sink, n_recent, B)
         assert n_kept[r] == ref.size, (r, n_kept[r], ref.size)
         np.testing.assert_array_equal(kept[r][: ref.size], ref.astype(np.int32))
     return st
 
 
+@pytest.mark.parametrize("rows", [3, 128])
 @pytest.mark.parametrize("T,B,levels", [(100_000, 2048, 16), (100_000, 2048, 3), (33_312, 4096, 64),
                                         (4096, 512, 5), (100_000, 2048, 0)])
-def test_ties_and_candidate_paths(T, B, levels):
+def test_ties_and_candidate_paths(T, B, levels, rows):
     """Quantised scores put the budget-th key inside a run of equal keys;
     levels == 0 makes every score equal, so the threshold bin overflows the
-    candidate list and the streaming fallback resolves it."""
+    candidate list and the streaming fallback resolves it. 3 rows of >= 32,768
+    tokens take the split path, 128 rows the one-workgroup kernels (a sample of
+    them is checked)."""
     rng = np.random.default_rng(T + B + levels)
-    rows = 3
     if levels:
         scores = (rng.integers(0, levels, (rows, T)) / levels).astype(np.float32)
     else:
         scores = np.full((rows, T), 0.25, np.float32)
     tags = rng.integers(0, 4, T).astype(np.uint8)
     bonus = np.array([[0.0], [0.5], [0.0], [0.125]])
-    _check(scores, tags, bonus, None, 4, 128, B)
+    _check(scores, tags, bonus, None, 4, 128, B, check_rows=[0, 1, 2, rows - 1] if rows > 3 else None)
 
 
 def test_continuous_scores_with_bonus_spans():
@@ -105,3 +111,44 @@ def test_short_ragged_and_long_rows(T, B):
     tags = rng.integers(0, 3, T).astype(np.uint8)
     bonus = np.array([[0.0], [0.25], [2.0]])
     _check(scores, tags, bonus, None, 4, 64, B, kept_stride=max(B, 1))
+
+
+@pytest.mark.parametrize("T,rows", [(300_000, 2), (262_147, 3), (1_048_576, 1), (65_537, 5)])
+def test_split_path_long_rows(T, rows):
+    """Rows split over several workgroups: continuous scores with bonus spans,
+    exact ties at the threshold, NaN totals (lowest), ragged lengths (scalar
+    loads) and a kept list shorter than the row's kept count never overrun."""
+    rng = np.random.default_rng(T + rows)
+    B = 2048
+    scores = rng.gamma(0.5, 1.0 / T, (rows, T)).astype(np.float32)
+    scores[:, 5000:5600] = np.float32(np.sort(scores[0])[-B // 2])   # a run of equal keys near the threshold
+    scores[:, 100:110] = np.nan
+    tags = np.zeros(T, np.uint8)
+    for k, start in enumerate(rng.choice(np.arange(200, T - 1000, 997), 6, replace=False)):
+        tags[start:start + int(rng.integers(16, 300))] = k + 1
+    bonus = np.array([[0.0]] + [[1000.0 - 50.0 * k] for k in range(6)])
+    _check(scores, tags, bonus, None, 4, 128, B)
+
+
+def test_split_path_floors_beyond_budget_and_short_kept_list():
+    """Long rows whose protected tokens exceed the budget keep all of them
+    (n_kept reports the count; only kept_stride entries are written); a row
+    no longer than the budget keeps everything."""
+    rng = np.random.default_rng(21)
+    T, B = 300_000, 1024
+    scores = rng.random((2, T)).astype(np.float32)
+    tags = np.zeros(T, np.uint8)
+    tags[50_000:52_000] = 1
+    floor = np.array([[0], [1]], np.uint8)
+    bonus = np.zeros((2, 1))
+    st, kept, n_kept = _run_select(scores, tags, bonus, floor, 4, 16, B, kept_stride=B)
+    ref = _oracle(scores[0], tags, bonus, floor, 4, 16, B)
+    assert ref.size == 4 + 16 + 2000 and np.all(n_kept == ref.size)
+    for r in range(2):
+        np.testing.assert_array_equal(kept[r], ref[:B].astype(np.int32))
+    _check(scores, tags, bonus, floor, 4, 16, B, kept_stride=T)
+    # T <= budget on the split path: every token, in order
+    small = rng.random((3, 40_000)).astype(np.float32)
+    st, kept, n_kept = _run_select(small, None, np.zeros((1, 1)), None, 4, 16, 50_000, kept_stride=50_000)
+    assert np.all(n_kept == 40_000)
+    np.testing.assert_array_equal(kept[:, :40_000], np.tile(np.arange(40_000, dtype=np.int32), (3, 1)))
