@@ -11,9 +11,7 @@
 // Split-KV: every workgroup takes one chunk of DEC_CHUNK keys of one row (from
 // either partition) for all G query heads of the row and writes its (v, l, u)
 // partial to the workspace; a merge kernel applies Eq. 15 across the chunks of
-// both partitions. Phase A: thread <-> key, dot products against the G queries
-// (staged in LDS as fp32). Phase B: per-head chunk max and exp-sum. Phase C:
-// thread <-> (dimension pair, key stripe) accumulation of sum_j p_j v_j.
+// both partitions.
 // The bf16 partition may be paged: token t of a row then lives in slot
 // block_table[n][t / page_size] * page_size + t % page_size of the row's storage.
 #include <cmath>
@@ -75,24 +73,36 @@ __device__ __forceinline__ int64_t bf16_slot(const DecodeArgs &a, int n, int t) 
     return (blk < 0 || s >= a.stride_h) ? -1 : s;
 }
 
-template <int D>
-__global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
-    constexpr int DP = D / 2;
-    constexpr int STRIPES = DEC_THREADS / DP;
-    __shared__ float s_q[DEC_MAX_G][D];
-    __shared__ float s_p[DEC_MAX_G][DEC_CHUNK];
-    __shared__ float s_red[DEC_THREADS / 64];
-    __shared__ float s_acc[STRIPES][DEC_MAX_G][D];
-    __shared__ int64_t s_slot[DEC_CHUNK];
+// One chunk of DEC_CHUNK keys of one row (either partition) for the GM >= G
+// query heads of the row's group. A key is owned by TPK = D/8 threads, each
+// holding 8 consecutive dimensions: every thread issues the loads of all its
+// keys (16 bytes each) before using any, partial dot products are summed
+// across the key's threads with shuffles, and the softmax statistics need
+// three barriers for all heads together.
+static_assert(DEC_CHUNK == DEC_THREADS, "the statistics map one thread to one key");
 
+template <int D, int GM, bool LOW>
+__global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
+    constexpr int TPK = D / 8;                  // threads per key
+    constexpr int KPI = DEC_THREADS / TPK;      // keys per pass over the block
+    constexpr int ITER = DEC_CHUNK / KPI;       // passes per chunk
+    constexpr int NW = DEC_THREADS / 64;
+    __shared__ float s_q[GM][D];
+    __shared__ float s_p[GM][DEC_CHUNK];        // logits, then weights
+    __shared__ float s_w[NW][GM];
+    __shared__ float s_acc[NW][GM][D];
+
+    // the bf16 partition's chunks come first in a row's partial slots
     const int slots = a.chunks_h + a.chunks_l;
-    const int64_t r = blockIdx.x / slots;
-    const int slot = blockIdx.x % slots;
-    const bool low = slot >= a.chunks_h;
-    const int chunk = low ? slot - a.chunks_h : slot;
+    const int own = LOW ? a.chunks_l : a.chunks_h;
+    const int64_t r = blockIdx.x / own;
+    const int chunk = blockIdx.x % own;
+    const int slot = LOW ? a.chunks_h + chunk : chunk;
+    constexpr bool low = LOW;
     const RowIdx ri = split_row(r, a.L, a.Hkv);
     const int G = a.G;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = tid % TPK, kin = tid / TPK;  // dimension group, key within a pass
     float *out = a.part + ((size_t)r * slots + slot) * G * (D + 2);
 
     int64_t n = low ? (a.n_l ? a.n_l[r] : 0) : a.n_h[r];
@@ -106,117 +116,184 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         return;
     }
     const uint16_t *qrow = a.q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * G) * D;
-    for (int i = tid; i < G * D; i += DEC_THREADS) s_q[i / D][i % D] = bf16_to_f32(qrow[i]);
-    __syncthreads();
+    for (int i = tid; i < GM * D; i += DEC_THREADS) s_q[i / D][i % D] = i / D < G ? bf16_to_f32(qrow[i]) : 0.f;
 
-    // Phase A: thread <-> key.
-    float sc[DEC_MAX_G];
+    // Storage row of every key this thread touches (-1: none), then all loads.
+    int32_t srow[ITER];   // storage slots fit int32: the caller checks the strides
 #pragma unroll
-    for (int g = 0; g < DEC_MAX_G; ++g) sc[g] = 0.f;
-    bool valid = tid < cnt;
-    if (valid) {
-        const int t = (int)(k0 + tid);
+    for (int it = 0; it < ITER; ++it) {
+        const int e = it * KPI + kin;
+        int64_t sl = -1;
+        if (e < cnt) sl = low ? k0 + e : bf16_slot(a, ri.n, (int)(k0 + e));
+        srow[it] = (int32_t)sl;
+    }
+    uint4 kv[ITER];   // bf16: 8 values; int8: codes in .x/.y
+    float ks[LOW ? ITER : 1];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        kv[it] = make_uint4(0, 0, 0, 0);
+        if (LOW) ks[LOW ? it : 0] = 0.f;
+        if (srow[it] < 0) continue;
         if (!low) {
-            const int64_t sl = bf16_slot(a, ri.n, t);
-            s_slot[tid] = sl;
-            valid = sl >= 0;
-            if (valid) {
-                const uint16_t *kr = a.K + ((size_t)r * a.stride_h + sl) * D;
-                for (int c = 0; c < D; c += 8) {
-                    const uint4 u = *reinterpret_cast<const uint4 *>(kr + c);
-                    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float ka = bf16_to_f32((uint16_t)(w[e] & 0xFFFF));
-                        const float kb = bf16_to_f32((uint16_t)(w[e] >> 16));
-#pragma unroll
-                        for (int g = 0; g < DEC_MAX_G; ++g)
-                            if (g < G) sc[g] = fmaf(kb, s_q[g][c + 2 * e + 1], fmaf(ka, s_q[g][c + 2 * e], sc[g]));
-                    }
-                }
-            }
+            kv[it] = *reinterpret_cast<const uint4 *>(a.K + ((size_t)r * a.stride_h + srow[it]) * D + 8 * sub);
         } else {
-            s_slot[tid] = t;
-            const int8_t *kr = a.Kq + ((size_t)r * a.stride_l + t) * D;
-            const float ks = half_bits_to_f32(a.Ks[(size_t)r * a.stride_l + t]);
-            for (int c = 0; c < D; c += 16) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(kr + c);
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const float kf = (float)(int8_t)((w[e] >> (8 * b)) & 0xFF) * ks;
-#pragma unroll
-                        for (int g = 0; g < DEC_MAX_G; ++g)
-                            if (g < G) sc[g] = fmaf(kf, s_q[g][c + 4 * e + b], sc[g]);
-                    }
-                }
-            }
+            const uint2 c = *reinterpret_cast<const uint2 *>(a.Kq + ((size_t)r * a.stride_l + srow[it]) * D + 8 * sub);
+            kv[it] = make_uint4(c.x, c.y, 0, 0);
+            ks[LOW ? it : 0] = half_bits_to_f32(a.Ks[(size_t)r * a.stride_l + srow[it]]);
         }
     }
-    // Phase B: per-head chunk max and exp-sum (log2 domain).
-    float mg[DEC_MAX_G], lg[DEC_MAX_G];
+    __syncthreads();  // s_q ready
+    float q[GM][8];
 #pragma unroll
-    for (int g = 0; g < DEC_MAX_G; ++g) {
-        mg[g] = -INFINITY;
-        lg[g] = 0.f;
-        if (g < G) {
-            const float v = valid ? sc[g] * a.c2 : -INFINITY;
-            mg[g] = block_reduce(v, true, s_red);
-            const float p = valid ? __builtin_amdgcn_exp2f(v - mg[g]) : 0.f;
-            s_p[g][tid] = p;
-            lg[g] = block_reduce(p, false, s_red);
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) q[g][c] = s_q[g][8 * sub + c];
+
+    // Logits: partial dot products over this thread's 8 dimensions, summed
+    // over the key's TPK threads (lanes kin*TPK .. kin*TPK + TPK-1 of the wave).
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        float x[8];
+        if (!low) {
+            const uint32_t w[4] = {kv[it].x, kv[it].y, kv[it].z, kv[it].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xFFFF));
+                x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+            }
+        } else {
+            const uint32_t w[2] = {kv[it].x, kv[it].y};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFF) * ks[LOW ? it : 0];
         }
+        float dot[GM];
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc = fmaf(x[c], q[g][c], acc);
+            dot[g] = acc;
+        }
+#pragma unroll
+        for (int off = 1; off < TPK; off <<= 1)
+#pragma unroll
+            for (int g = 0; g < GM; ++g) dot[g] += __shfl_xor(dot[g], off);
+        const int e = it * KPI + kin;
+        if (sub == 0) {
+#pragma unroll
+            for (int g = 0; g < GM; ++g) s_p[g][e] = srow[it] >= 0 ? dot[g] * a.c2 : -INFINITY;
+        }
+    }
+    // Value loads now, so they are in flight during the statistics.
+    uint4 vv[ITER];
+    float vs[LOW ? ITER : 1];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        vv[it] = make_uint4(0, 0, 0, 0);
+        if (LOW) vs[LOW ? it : 0] = 0.f;
+        if (srow[it] < 0) continue;
+        if (!low) {
+            vv[it] = *reinterpret_cast<const uint4 *>(a.V + ((size_t)r * a.stride_h + srow[it]) * D + 8 * sub);
+        } else {
+            const uint2 c = *reinterpret_cast<const uint2 *>(a.Vq + ((size_t)r * a.stride_l + srow[it]) * D + 8 * sub);
+            vv[it] = make_uint4(c.x, c.y, 0, 0);
+            vs[LOW ? it : 0] = half_bits_to_f32(a.Vs[(size_t)r * a.stride_l + srow[it]]);
+        }
+    }
+    __syncthreads();  // logits ready
+    // Per-head chunk max and exp-sum (log2 domain): thread <-> key (DEC_CHUNK == DEC_THREADS).
+    float v[GM], m[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        v[g] = tid < cnt ? s_p[g][tid] : -INFINITY;
+        float x = v[g];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+        if (lane == 0) s_w[wave][g] = x;
     }
     __syncthreads();
-    // Phase C: thread <-> (dimension pair dp, key stripe).
-    const int dp = tid % DP, stripe = tid / DP;
-    float acc0[DEC_MAX_G], acc1[DEC_MAX_G];
 #pragma unroll
-    for (int g = 0; g < DEC_MAX_G; ++g) acc0[g] = acc1[g] = 0.f;
-    for (int e = stripe; e < cnt; e += STRIPES) {
-        const int64_t sl = s_slot[e];
-        if (sl < 0) continue;
-        float v0, v1;
+    for (int g = 0; g < GM; ++g) {
+        float x = s_w[0][g];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) x = fmaxf(x, s_w[w][g]);
+        m[g] = x;
+    }
+    __syncthreads();  // every thread has read the maxima
+    float l[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        const float pv = (v[g] > -INFINITY) ? __builtin_amdgcn_exp2f(v[g] - m[g]) : 0.f;
+        s_p[g][tid] = pv;
+        float x = pv;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+        if (lane == 0) s_w[wave][g] = x;
+    }
+    __syncthreads();  // weights and partial sums ready
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x += s_w[w][g];
+        l[g] = x;
+    }
+    // Weighted values: this thread's 8 dimensions over its keys.
+    float acc[GM][8];
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        if (srow[it] < 0) continue;
+        const int e = it * KPI + kin;
+        float x[8];
         if (!low) {
-            const uint32_t u = *reinterpret_cast<const uint32_t *>(a.V + ((size_t)r * a.stride_h + sl) * D + 2 * dp);
-            v0 = bf16_to_f32((uint16_t)(u & 0xFFFF));
-            v1 = bf16_to_f32((uint16_t)(u >> 16));
+            const uint32_t w[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                x[2 * c] = bf16_to_f32((uint16_t)(w[c] & 0xFFFF));
+                x[2 * c + 1] = bf16_to_f32((uint16_t)(w[c] >> 16));
+            }
         } else {
-            const float vs = half_bits_to_f32(a.Vs[(size_t)r * a.stride_l + sl]);
-            const uint16_t u = *reinterpret_cast<const uint16_t *>(a.Vq + ((size_t)r * a.stride_l + sl) * D + 2 * dp);
-            v0 = (float)(int8_t)(u & 0xFF) * vs;
-            v1 = (float)(int8_t)(u >> 8) * vs;
+            const uint32_t w[2] = {vv[it].x, vv[it].y};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = (float)(int8_t)((w[c >> 2] >> (8 * (c & 3))) & 0xFF) * vs[LOW ? it : 0];
         }
 #pragma unroll
-        for (int g = 0; g < DEC_MAX_G; ++g) {
-            if (g < G) {
-                const float p = s_p[g][e];
-                acc0[g] = fmaf(p, v0, acc0[g]);
-                acc1[g] = fmaf(p, v1, acc1[g]);
-            }
+        for (int g = 0; g < GM; ++g) {
+            const float pw = s_p[g][e];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(pw, x[c], acc[g][c]);
         }
     }
+    // Sum over the wave's keys (lanes differing in the key bits), then over waves.
 #pragma unroll
-    for (int g = 0; g < DEC_MAX_G; ++g) {
-        if (g < G) {
-            s_acc[stripe][g][2 * dp] = acc0[g];
-            s_acc[stripe][g][2 * dp + 1] = acc1[g];
-        }
+    for (int off = TPK; off < 64; off <<= 1)
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[g][c] += __shfl_xor(acc[g][c], off);
+    if (lane < TPK) {
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s_acc[wave][g][8 * sub + c] = acc[g][c];
     }
     __syncthreads();
     for (int i = tid; i < G * D; i += DEC_THREADS) {
         const int g = i / D, c = i % D;
         float u = 0.f;
-        for (int s = 0; s < STRIPES; ++s) u += s_acc[s][g][c];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) u += s_acc[w][g][c];
         out[g * (D + 2) + 2 + c] = u;
     }
 #pragma unroll
-    for (int g = 0; g < DEC_MAX_G; ++g) {
+    for (int g = 0; g < GM; ++g) {
         if (g < G && tid == 0) {
-            out[g * (D + 2) + 0] = mg[g];
-            out[g * (D + 2) + 1] = lg[g];
+            out[g * (D + 2) + 0] = m[g];
+            out[g * (D + 2) + 1] = l[g];
         }
     }
 }
@@ -268,6 +345,8 @@ extern "C" int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const ui
     if (st != KVC_OK) return st;
     if (!q || !K || !V || !n_h || !o) return fail(KVC_ERR_ARG, "kvc_decode_attn: NULL pointer");
     if (stride_h <= 0) return fail(KVC_ERR_ARG, "kvc_decode_attn: stride_h must be positive");
+    if (stride_h > (int64_t)INT32_MAX || stride_l > (int64_t)INT32_MAX)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_attn: pool strides must fit int32");
     const int G = dims->n_q_heads / dims->n_kv_heads;
     if (G > DEC_MAX_G)
         return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_attn: GQA group %d exceeds %d", G, DEC_MAX_G);
@@ -310,15 +389,32 @@ extern "C" int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const ui
     const int64_t blocks = rows * (a.chunks_h + a.chunks_l);
     if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_attn: grid too large");
     hipStream_t s = as_stream(stream);
+    const dim3 grid_h((unsigned)(rows * a.chunks_h)), grid_l((unsigned)(rows * a.chunks_l)), block(DEC_THREADS);
+#define DEC_PARTIAL_G(DD, GG)                                                              \
+    do {                                                                                   \
+        decode_partial<DD, GG, false><<<grid_h, block, 0, s>>>(a);                         \
+        if (a.chunks_l) decode_partial<DD, GG, true><<<grid_l, block, 0, s>>>(a);          \
+    } while (0)
+#define DEC_PARTIAL(DD)                                                                    \
+    do {                                                                                   \
+        if (G <= 4)                                                                        \
+            DEC_PARTIAL_G(DD, 4);                                                          \
+        else if (G <= 8)                                                                   \
+            DEC_PARTIAL_G(DD, 8);                                                          \
+        else                                                                               \
+            DEC_PARTIAL_G(DD, 16);                                                         \
+    } while (0)
     if (dims->head_dim == 128) {
-        decode_partial<128><<<dim3((unsigned)blocks), dim3(DEC_THREADS), 0, s>>>(a);
+        DEC_PARTIAL(128);
         if ((st = check_launch("kvc_decode_attn partial")) != KVC_OK) return st;
         decode_merge<128><<<dim3((unsigned)(rows * G)), dim3(128), 0, s>>>(a);
     } else {
-        decode_partial<64><<<dim3((unsigned)blocks), dim3(DEC_THREADS), 0, s>>>(a);
+        DEC_PARTIAL(64);
         if ((st = check_launch("kvc_decode_attn partial")) != KVC_OK) return st;
         decode_merge<64><<<dim3((unsigned)(rows * G)), dim3(64), 0, s>>>(a);
     }
+#undef DEC_PARTIAL
+#undef DEC_PARTIAL_G
     return check_launch("kvc_decode_attn merge");
 }
 
