@@ -39,6 +39,8 @@ static constexpr int PE_THREADS = 128;  // two waves: 32 query rows x 64 keys of
 static constexpr int PE_PAGE_CHUNK = 4096;  // keys per pe_effect workgroup
 static constexpr int PR_THREADS = 256;
 static constexpr int PR_PMAX = 16;      // largest page the retire kernel takes
+static constexpr int PR_BATCH = 8;      // candidates whose deletion terms are formed per launch
+static constexpr int PG_THREADS = 1024; // greedy walk: one workgroup per sequence
 
 struct PageGeom {
     int64_t rows_local, n_chunks;
@@ -61,6 +63,7 @@ static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct PageWs {
     float2 *part;
     float *mm, *o, *accD, *alphaD;
+    float *tD, *tA;   // [PR_BATCH][rows][QRP][D] and [PR_BATCH][rows][QRP]: one batch's deletion terms
 };
 
 static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base, PageWs *w) {
@@ -69,6 +72,8 @@ static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base,
     const size_t s_mm = al256((size_t)g.rows_local * g.QRP * sizeof(float));
     const size_t s_o = al256((size_t)g.rows_local * g.QRP * d->head_dim * sizeof(float));
     const size_t s_a = al256((size_t)g.rows_local * g.QRP * sizeof(float));
+    const size_t s_tD = al256((size_t)PR_BATCH * g.rows_local * g.QRP * d->head_dim * sizeof(float));
+    const size_t s_tA = al256((size_t)PR_BATCH * g.rows_local * g.QRP * sizeof(float));
     if (w) {
         char *p = reinterpret_cast<char *>(base);
         w->part = reinterpret_cast<float2 *>(p);
@@ -76,8 +81,10 @@ static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base,
         w->o = reinterpret_cast<float *>(p + s_part + s_mm);
         w->accD = reinterpret_cast<float *>(p + s_part + s_mm + s_o);
         w->alphaD = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o);
+        w->tD = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a);
+        w->tA = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a + s_tD);
     }
-    return s_part + s_mm + 2 * s_o + s_a;
+    return s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA;
 }
 
 struct PeArgs {
@@ -288,29 +295,122 @@ __global__ void fill_f32(float *p, int64_t n, float v) {
         p[i] = v;
 }
 
-// Greedy joint retirement, one workgroup per sequence. Thread <-> query row of
-// one KV head at a time. accD[rr][q][d] holds sum over accepted pages of
-// sum a (v - o); alphaD[rr][q] the accepted pages' summed weight.
+// Greedy joint retirement (CommitKV §3.3 Eq. 11), in two kernels per batch of
+// PR_BATCH candidates.
+//
+// pr_terms, one workgroup per (sequence, KV head, candidate): for every query
+// row q of the window, the page's weights a_qi, their sum alpha_q and the
+// deletion term t_q = sum_{i in page} a_qi (v_i - o_q), written to the
+// workspace. The terms do not depend on the decisions, so all candidates of a
+// batch are formed in parallel.
+//
+// pr_greedy, one workgroup per sequence: walks the batch in order. The joint
+// deletion of the accepted set D plus candidate E has, per query row, the
+// vector accD_q + t_q(E) and weight alphaD_q + alpha_q(E) (Eq. 6 over the
+// union, summed page by page); its relative effect is maximised over the rows
+// of every KV head and compared with tau_joint; an accepted candidate is
+// added to accD / alphaD. D/8 threads own one query row, 8 dimensions each.
 template <int D>
-__global__ void __launch_bounds__(PR_THREADS) pe_retire(PeArgs a, const int32_t *order, int n_cand,
-                                                        float tau_joint, float *accD, float *alphaD,
-                                                        uint8_t *accepted, float *joint_rel) {
+__global__ void __launch_bounds__(PR_THREADS) pr_terms(PeArgs a, const int32_t *order, int n_cand, int c0, int nc,
+                                                       float *tD, float *tA) {
     __shared__ float s_k[PR_PMAX][D];
     __shared__ float s_v[PR_PMAX][D];
-    __shared__ float s_red[PR_THREADS / 64];
-    __shared__ int s_accept;
-    const int n = blockIdx.x;
+    const int j = blockIdx.x % nc;
+    const int64_t nh = blockIdx.x / nc;
+    const int n = (int)(nh / a.Hkv), h = (int)(nh % a.Hkv);
+    const int page = order[(size_t)n * n_cand + c0 + j];
+    if (page < 0 || page >= a.n_pages) return;  // skipped by the walk
     const int tid = threadIdx.x;
     const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
     const int ps = a.page_size;
-    // clear the running sums of this sequence's rows
-    for (int h = 0; h < a.Hkv; ++h) {
-        const int64_t rr = (int64_t)n * a.Hkv + h;
-        for (int i = tid; i < QRP * D; i += PR_THREADS) accD[(size_t)rr * QRP * D + i] = 0.f;
-        for (int i = tid; i < QRP; i += PR_THREADS) alphaD[(size_t)rr * QRP + i] = 0.f;
+    const int64_t rows_local = (int64_t)gridDim.x / nc;
+    const int64_t rr = (int64_t)n * a.Hkv + h;
+    const int64_t gr = ((int64_t)n * a.L + a.lsel) * a.Hkv + h;
+    const uint16_t *Kr = a.K + (size_t)gr * a.T * D;
+    const uint16_t *Vr = a.V + (size_t)gr * a.T * D;
+    for (int e = tid; e < ps * D; e += PR_THREADS) {
+        const int k = e / D, cc = e % D;
+        const int64_t t = (int64_t)page * ps + k;
+        s_k[k][cc] = bf16_to_f32(Kr[(size_t)t * D + cc]);
+        s_v[k][cc] = bf16_to_f32(Vr[(size_t)t * D + cc]);
     }
     __syncthreads();
-    for (int c = 0; c < n_cand; ++c) {
+    const RowIdx ri = split_row(gr, a.L, a.Hkv);
+    const uint16_t *Qg = a.Q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * a.G) * a.W * D;
+    float *t_out = tD + ((size_t)j * rows_local + rr) * QRP * D;
+    float *a_out = tA + ((size_t)j * rows_local + rr) * QRP;
+    for (int q = tid; q < QR; q += PR_THREADS) {
+        const int64_t qpos = a.qbase + q % a.W;
+        const float mq = a.mm[rr * QRP + q];
+        float p[PR_PMAX];
+#pragma unroll
+        for (int k = 0; k < PR_PMAX; ++k) p[k] = 0.f;
+        for (int cc = 0; cc < D; cc += 8) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(Qg + (size_t)q * D + cc);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float q0 = bf16_to_f32((uint16_t)(w4[e] & 0xFFFF)), q1 = bf16_to_f32((uint16_t)(w4[e] >> 16));
+#pragma unroll
+                for (int k = 0; k < PR_PMAX; ++k)
+                    if (k < ps) p[k] = fmaf(q1, s_k[k][cc + 2 * e + 1], fmaf(q0, s_k[k][cc + 2 * e], p[k]));
+            }
+        }
+        float al = 0.f;
+#pragma unroll
+        for (int k = 0; k < PR_PMAX; ++k) {
+            const int64_t t = (int64_t)page * ps + k;
+            p[k] = (k < ps && t <= qpos) ? __builtin_amdgcn_exp2f(fmaf(p[k], a.c2, -mq)) : 0.f;
+            al += p[k];
+        }
+        const float *o = a.o + ((size_t)rr * QRP + q) * D;
+        for (int cc = 0; cc < D; cc += 4) {
+            const float4 o4 = *reinterpret_cast<const float4 *>(o + cc);
+            float4 t4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int k = 0; k < PR_PMAX; ++k) {
+                if (k < ps) {
+                    t4.x = fmaf(p[k], s_v[k][cc] - o4.x, t4.x);
+                    t4.y = fmaf(p[k], s_v[k][cc + 1] - o4.y, t4.y);
+                    t4.z = fmaf(p[k], s_v[k][cc + 2] - o4.z, t4.z);
+                    t4.w = fmaf(p[k], s_v[k][cc + 3] - o4.w, t4.w);
+                }
+            }
+            *reinterpret_cast<float4 *>(t_out + (size_t)q * D + cc) = t4;
+        }
+        a_out[q] = al;
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(PG_THREADS) pr_greedy(PeArgs a, const int32_t *order, int n_cand, int c0, int nc,
+                                                        int first, float tau_joint, const float *tD, const float *tA,
+                                                        float *accD, float *alphaD, uint8_t *accepted,
+                                                        float *joint_rel, int64_t rows_local) {
+    constexpr int TPP = D / 8;                 // threads per query row
+    constexpr int PPI = PG_THREADS / TPP;      // query rows per pass
+    extern __shared__ float s_onorm[];         // [Hkv * QR]
+    __shared__ float s_red[PG_THREADS / 64];
+    __shared__ int s_accept;
+    const int n = blockIdx.x;
+    const int tid = threadIdx.x, sub = tid % TPP;
+    const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
+    const int P = a.Hkv * QR;
+    for (int pq = tid; pq < P; pq += PG_THREADS) {
+        const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
+        const float *o = a.o + ((size_t)rr * QRP + pq % QR) * D;
+        float o2 = 0.f;
+        for (int cc = 0; cc < D; ++cc) o2 = fmaf(o[cc], o[cc], o2);
+        s_onorm[pq] = sqrtf(o2);
+    }
+    if (first) {  // clear the running sums of this sequence's rows
+        for (int64_t i = tid; i < (int64_t)a.Hkv * QRP * D; i += PG_THREADS)
+            accD[(size_t)n * a.Hkv * QRP * D + i] = 0.f;
+        for (int i = tid; i < a.Hkv * QRP; i += PG_THREADS) alphaD[(size_t)n * a.Hkv * QRP + i] = 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < nc; ++j) {
+        const int c = c0 + j;
         const int page = order[(size_t)n * n_cand + c];
         if (page < 0 || page >= a.n_pages) {
             if (tid == 0) {
@@ -320,77 +420,54 @@ __global__ void __launch_bounds__(PR_THREADS) pe_retire(PeArgs a, const int32_t 
             continue;
         }
         float worst = 0.f;
-        for (int pass = 0; pass < 2; ++pass) {  // pass 0: evaluate; pass 1: commit if accepted
-            if (pass == 1 && !s_accept) break;
-            for (int h = 0; h < a.Hkv; ++h) {
-                const int64_t rr = (int64_t)n * a.Hkv + h;
-                const int64_t gr = ((int64_t)n * a.L + a.lsel) * a.Hkv + h;
-                const uint16_t *Kr = a.K + (size_t)gr * a.T * D;
-                const uint16_t *Vr = a.V + (size_t)gr * a.T * D;
-                __syncthreads();
-                for (int e = tid; e < ps * D; e += PR_THREADS) {
-                    const int k = e / D, cc = e % D;
-                    const int64_t t = (int64_t)page * ps + k;
-                    s_k[k][cc] = bf16_to_f32(Kr[(size_t)t * D + cc]);
-                    s_v[k][cc] = bf16_to_f32(Vr[(size_t)t * D + cc]);
-                }
-                __syncthreads();
-                const RowIdx ri = split_row(gr, a.L, a.Hkv);
-                const uint16_t *Qg = a.Q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * a.G) * a.W * D;
-                for (int q = tid; q < QR; q += PR_THREADS) {
-                    const int64_t qpos = a.qbase + q % a.W;
-                    const float mq = a.mm[rr * QRP + q];
-                    float p[PR_PMAX];
+        for (int p0 = 0; p0 < P; p0 += PPI) {
+            const int pq = p0 + tid / TPP;
+            float n2 = 0.f, alj = 0.f;
+            if (pq < P) {
+                const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
+                const int q = pq % QR;
+                const float *t = tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub;
+                const float *acc = accD + ((size_t)rr * QRP + q) * D + 8 * sub;
+                const float4 t0 = *reinterpret_cast<const float4 *>(t), t1 = *reinterpret_cast<const float4 *>(t + 4);
+                const float4 a0 = *reinterpret_cast<const float4 *>(acc), a1 = *reinterpret_cast<const float4 *>(acc + 4);
+                const float jv[8] = {a0.x + t0.x, a0.y + t0.y, a0.z + t0.z, a0.w + t0.w,
+                                     a1.x + t1.x, a1.y + t1.y, a1.z + t1.z, a1.w + t1.w};
 #pragma unroll
-                    for (int k = 0; k < PR_PMAX; ++k) p[k] = 0.f;
-                    for (int cc = 0; cc < D; ++cc) {
-                        const float qv = bf16_to_f32(Qg[(size_t)q * D + cc]);
-#pragma unroll
-                        for (int k = 0; k < PR_PMAX; ++k)
-                            if (k < ps) p[k] = fmaf(qv, s_k[k][cc], p[k]);
-                    }
-                    float al = 0.f;
-#pragma unroll
-                    for (int k = 0; k < PR_PMAX; ++k) {
-                        const int64_t t = (int64_t)page * ps + k;
-                        p[k] = (k < ps && t <= qpos) ? __builtin_amdgcn_exp2f(fmaf(p[k], a.c2, -mq)) : 0.f;
-                        al += p[k];
-                    }
-                    const float *o = a.o + ((size_t)rr * QRP + q) * D;
-                    float *acc = accD + ((size_t)rr * QRP + q) * D;
-                    float n2 = 0.f, o2 = 0.f;
-                    for (int cc = 0; cc < D; ++cc) {
-                        float t = 0.f;
-#pragma unroll
-                        for (int k = 0; k < PR_PMAX; ++k)
-                            if (k < ps) t = fmaf(p[k], s_v[k][cc] - o[cc], t);
-                        const float j = acc[cc] + t;
-                        if (pass == 1) acc[cc] = j;
-                        n2 = fmaf(j, j, n2);
-                        o2 = fmaf(o[cc], o[cc], o2);
-                    }
-                    const float alj = alphaD[rr * QRP + q] + al;
-                    if (pass == 1) alphaD[rr * QRP + q] = alj;
-                    const float num = sqrtf(n2), onorm = sqrtf(o2);
-                    float rel = 0.f;
-                    if (num > 0.f) rel = (1.f - alj > 0.f && onorm > 0.f) ? num / ((1.f - alj) * onorm) : INFINITY;
-                    worst = fmaxf(worst, rel);
-                }
+                for (int e = 0; e < 8; ++e) n2 = fmaf(jv[e], jv[e], n2);
+                alj = alphaD[rr * QRP + q] + tA[((size_t)j * rows_local + rr) * QRP + q];
             }
-            if (pass == 0) {
-                // block max of `worst`
-                float v = worst;
-                for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-                if ((tid & 63) == 0) s_red[tid >> 6] = v;
-                __syncthreads();
-                if (tid == 0) {
-                    float m = s_red[0];
-                    for (int w = 1; w < PR_THREADS / 64; ++w) m = fmaxf(m, s_red[w]);
-                    s_accept = m <= tau_joint;
-                    accepted[(size_t)n * n_cand + c] = (uint8_t)s_accept;
-                    if (joint_rel) joint_rel[(size_t)n * n_cand + c] = m;
-                }
-                __syncthreads();
+#pragma unroll
+            for (int off = 1; off < TPP; off <<= 1) n2 += __shfl_xor(n2, off);
+            if (pq < P) {
+                const float num = sqrtf(n2), onorm = s_onorm[pq];
+                float rel = 0.f;
+                if (num > 0.f) rel = (1.f - alj > 0.f && onorm > 0.f) ? num / ((1.f - alj) * onorm) : INFINITY;
+                worst = fmaxf(worst, rel);
+            }
+        }
+        float v = worst;
+        for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+        if ((tid & 63) == 0) s_red[tid >> 6] = v;
+        __syncthreads();
+        if (tid == 0) {
+            float m = s_red[0];
+            for (int w = 1; w < PG_THREADS / 64; ++w) m = fmaxf(m, s_red[w]);
+            s_accept = m <= tau_joint;
+            accepted[(size_t)n * n_cand + c] = (uint8_t)s_accept;
+            if (joint_rel) joint_rel[(size_t)n * n_cand + c] = m;
+        }
+        __syncthreads();
+        if (s_accept) {
+            for (int p0 = 0; p0 < P; p0 += PPI) {
+                const int pq = p0 + tid / TPP;
+                if (pq >= P) continue;
+                const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
+                const int q = pq % QR;
+                const float *t = tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub;
+                float *acc = accD + ((size_t)rr * QRP + q) * D + 8 * sub;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += t[e];
+                if (sub == 0) alphaD[rr * QRP + q] += tA[((size_t)j * rows_local + rr) * QRP + q];
             }
         }
         __syncthreads();
@@ -572,13 +649,26 @@ extern "C" int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16
     PeArgs a = pe_args(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, w);
     hipStream_t s = as_stream(stream);
     if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
-    if (dims->head_dim == 128)
-        pe_retire<128><<<dim3(dims->n_seq), dim3(PR_THREADS), 0, s>>>(a, order, n_cand, tau_joint, w.accD,
-                                                                       w.alphaD, accepted, joint_rel);
-    else
-        pe_retire<64><<<dim3(dims->n_seq), dim3(PR_THREADS), 0, s>>>(a, order, n_cand, tau_joint, w.accD,
-                                                                      w.alphaD, accepted, joint_rel);
-    return check_launch("kvc_page_retire");
+    const PageGeom g = page_geom(dims, W, q_first + W);
+    const size_t lds = (size_t)dims->n_kv_heads * g.QR * sizeof(float);
+    if (lds > 64 * 1024) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_retire: %d KV heads x %d rows too many", dims->n_kv_heads, g.QR);
+    for (int c0 = 0; c0 < n_cand; c0 += PR_BATCH) {
+        const int nc = n_cand - c0 < PR_BATCH ? n_cand - c0 : PR_BATCH;
+        const dim3 tgrid((unsigned)(g.rows_local * nc));
+        if (dims->head_dim == 128) {
+            pr_terms<128><<<tgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, w.tD, w.tA);
+            pr_greedy<128><<<dim3(dims->n_seq), dim3(PG_THREADS), lds, s>>>(
+                a, order, n_cand, c0, nc, c0 == 0, tau_joint, w.tD, w.tA, w.accD, w.alphaD, accepted, joint_rel,
+                g.rows_local);
+        } else {
+            pr_terms<64><<<tgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, w.tD, w.tA);
+            pr_greedy<64><<<dim3(dims->n_seq), dim3(PG_THREADS), lds, s>>>(
+                a, order, n_cand, c0, nc, c0 == 0, tau_joint, w.tD, w.tA, w.accD, w.alphaD, accepted, joint_rel,
+                g.rows_local);
+        }
+        if ((st = check_launch("kvc_page_retire")) != KVC_OK) return st;
+    }
+    return KVC_OK;
 }
 
 extern "C" int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_t page_size,

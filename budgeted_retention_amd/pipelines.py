@@ -30,6 +30,7 @@ class CallTimer:
     @contextlib.contextmanager
     def __call__(self, name):
         if name.startswith("host:"):
+            torch.cuda.synchronize()   # time the host step alone, not the GPU work queued before it
             t0 = time.perf_counter()
             yield
             self.host[name] = self.host.get(name, 0.0) + time.perf_counter() - t0
