@@ -47,12 +47,18 @@ def parse():
     return ap.parse_args()
 
 
+# Sources (and build flags) of the calls whose HBM counters profiles/ holds:
+# the counters stay valid until one of these changes.
+COUNTED_SOURCES = ["budgeted_retention_amd/csrc/" + n for n in
+                   ("kvc_internal.h", "common.hip", "score.hip", "select.hip", "compact.hip")] + [
+                   "budgeted_retention_amd/build.py"]
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources the counters were taken on."""
+    """Hash of the sources the counters were taken on."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "budgeted_retention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in COUNTED_SOURCES:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
