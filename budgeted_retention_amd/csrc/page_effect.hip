@@ -41,6 +41,8 @@ static constexpr int PR_THREADS = 256;
 static constexpr int PR_PMAX = 16;      // largest page the retire kernel takes
 static constexpr int PR_BATCH = 8;      // candidates whose deletion terms are formed per launch
 static constexpr int PG_THREADS = 1024; // greedy walk: one workgroup per sequence
+static constexpr int PO_CHUNK = 4096;   // keys per pe_out_mfma / pe_effect_mfma workgroup
+static constexpr int PM_THREADS = 256;  // four waves, each on its own 32-key tiles
 
 struct PageGeom {
     int64_t rows_local, n_chunks;
@@ -64,6 +66,7 @@ struct PageWs {
     float2 *part;
     float *mm, *o, *accD, *alphaD;
     float *tD, *tA;   // [PR_BATCH][rows][QRP][D] and [PR_BATCH][rows][QRP]: one batch's deletion terms
+    float *opart;     // [chunks][rows][QRP][D]: per-chunk partial window outputs
 };
 
 static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base, PageWs *w) {
@@ -74,6 +77,8 @@ static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base,
     const size_t s_a = al256((size_t)g.rows_local * g.QRP * sizeof(float));
     const size_t s_tD = al256((size_t)PR_BATCH * g.rows_local * g.QRP * d->head_dim * sizeof(float));
     const size_t s_tA = al256((size_t)PR_BATCH * g.rows_local * g.QRP * sizeof(float));
+    const int64_t och = (kend + PO_CHUNK - 1) / PO_CHUNK;
+    const size_t s_op = al256((size_t)och * g.rows_local * g.QRP * d->head_dim * sizeof(float));
     if (w) {
         char *p = reinterpret_cast<char *>(base);
         w->part = reinterpret_cast<float2 *>(p);
@@ -83,8 +88,9 @@ static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base,
         w->alphaD = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o);
         w->tD = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a);
         w->tA = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a + s_tD);
+        w->opart = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA);
     }
-    return s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA;
+    return s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA + s_op;
 }
 
 struct PeArgs {
@@ -97,6 +103,7 @@ struct PeArgs {
     float *o;
     int page_size, n_pages;
     float *eff_rel, *eff_abs;
+    float *opart;
 };
 
 // Stages one 64-key tile: a_pi for the block's 32 query rows into sp[32][64]
@@ -154,46 +161,6 @@ __device__ void pe_load_queries(const PeArgs &a, int64_t rr, int b, bf16x8 *qf, 
     const int QRP = ((QR + 31) / 32) * 32;
     mmq[0] = a.mm[rr * QRP + qrow];
     qposq[0] = qrow < QR ? a.qbase + qrow % a.W : -1;
-}
-
-template <int D>
-__global__ void __launch_bounds__(PE_THREADS) pe_out(PeArgs a) {
-    constexpr int DP = D / 2, STRIPES = PE_THREADS / DP, QPS = 32 / STRIPES;
-    __shared__ float sp[32][PE_TILE + 1];
-    __shared__ float sv[PE_TILE][D];
-    const int nb = (a.G * a.W + 31) / 32;
-    const int64_t rr = blockIdx.x / nb;
-    const int b = blockIdx.x % nb;
-    bf16x8 qf[D / 16];
-    float mmq[1];
-    int64_t qposq[1];
-    const uint16_t *Kr, *Vr;
-    pe_load_queries<D>(a, rr, b, qf, mmq, qposq, &Kr, &Vr);
-    const int tid = threadIdx.x, dp = tid % DP, stripe = tid / DP;
-    float acc0[QPS], acc1[QPS];
-#pragma unroll
-    for (int q = 0; q < QPS; ++q) acc0[q] = acc1[q] = 0.f;
-    for (int64_t j0 = 0; j0 < a.kend; j0 += PE_TILE) {
-        pe_stage_tile<D>(a, Kr, Vr, qf, mmq, qposq, j0, sp, sv);
-        __syncthreads();
-        for (int k = 0; k < PE_TILE; ++k) {
-            const float v0 = sv[k][2 * dp], v1 = sv[k][2 * dp + 1];
-#pragma unroll
-            for (int q = 0; q < QPS; ++q) {
-                const float p = sp[stripe * QPS + q][k];
-                acc0[q] = fmaf(p, v0, acc0[q]);
-                acc1[q] = fmaf(p, v1, acc1[q]);
-            }
-        }
-        __syncthreads();
-    }
-    const int QRP = nb * 32;
-#pragma unroll
-    for (int q = 0; q < QPS; ++q) {
-        float *o = a.o + ((size_t)rr * QRP + b * 32 + stripe * QPS + q) * D;
-        o[2 * dp] = acc0[q];
-        o[2 * dp + 1] = acc1[q];
-    }
 }
 
 __device__ __forceinline__ void atomic_max_nonneg(float *addr, float v) {
@@ -293,6 +260,216 @@ __global__ void __launch_bounds__(PE_THREADS) pe_effect(PeArgs a, int chunks_per
 __global__ void fill_f32(float *p, int64_t n, float v) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = v;
+}
+
+
+// ---------------------------------------------------------------- P·V on the matrix cores
+//
+// A wave owns one block of 32 query rows of one row and walks 32-key tiles.
+// Logits come from v_mfma_f32_32x32x16_bf16 as C[key][q] (lane (col, hf) holds
+// query row col and keys acc_row(i, hf)); the weights a = exp2(logit*c - mm)
+// stay in those registers. P·V is then formed as C[d][q] = sum_k V[k][d] P[q][k]
+// with v_mfma_f32_32x32x2_f32, two keys per instruction: in instruction j the
+// lane half hf contributes key acc_row(j, hf), the lane supplying V[that key][d]
+// (d = its column of the 32-dimension block, staged in LDS) and its own weight.
+// Every lane then holds query row col over 16 dimensions of each block, so a
+// row's squared norm is an in-lane sum plus one shuffle. fp32 operands: the
+// weights are not rounded.
+
+template <int D>
+__device__ __forceinline__ void pm_setup(const PeArgs &a, int64_t rr, int b, bf16x8 (&qf)[D / 16], float &mmq,
+                                         int64_t &qpos, bool &qvalid, const uint16_t **Kr, const uint16_t **Vr) {
+    float mm1[1];
+    int64_t qp1[1];
+    pe_load_queries<D>(a, rr, b, qf, mm1, qp1, Kr, Vr);
+    mmq = mm1[0];
+    qpos = qp1[0];
+    qvalid = b * 32 + (int)(threadIdx.x & 31) < a.G * a.W;
+}
+
+// One 32-key tile: the wave's V tile into its LDS slice (bf16 [32][D]), the
+// logits and the weights a[i] of keys j0 + acc_row(i, hf) (0 past kend or qpos).
+template <int D>
+__device__ __forceinline__ void pm_tile(const PeArgs &a, const uint16_t *Kr, const uint16_t *Vr, int64_t j0,
+                                        const bf16x8 (&qf)[D / 16], float mmq, int64_t qpos, uint16_t *sv,
+                                        float (&w)[16]) {
+    constexpr int S = D / 16;
+    constexpr int CPK = D / 8;  // 16-byte pieces per key
+    const int lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+    bf16x8 kf[S];
+    const int64_t key = j0 + col;
+#pragma unroll
+    for (int s = 0; s < S; ++s) kf[s] = key < a.kend ? load8(Kr + (size_t)key * D + 16 * s + 8 * hf) : zero8();
+    // the previous tile's reads of the wave's V slice come before this tile's writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int u = 0; u < 32 * CPK / 64; ++u) {
+        const int c = lane + 64 * u, k = c / CPK, part = c % CPK;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (j0 + k < a.kend) v = *reinterpret_cast<const uint4 *>(Vr + (size_t)(j0 + k) * D + 8 * part);
+        *reinterpret_cast<uint4 *>(sv + k * D + 8 * part) = v;
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t k = j0 + acc_row(i, hf);
+        w[i] = (k < a.kend && k <= qpos) ? __builtin_amdgcn_exp2f(fmaf(acc[i], a.c2, -mmq)) : 0.f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // the V tile is written before it is read
+}
+
+// C[d][q] of dimension block db over the tile's keys acc_row(j, hf), j in [j_lo, j_hi).
+template <int D>
+__device__ __forceinline__ void pm_pv(const uint16_t *sv, const float (&w)[16], int db, int j_lo, int j_hi,
+                                      f32x16 &c) {
+    const int lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j < j_lo || j >= j_hi) continue;
+        const float v = bf16_to_f32(sv[acc_row(j, hf) * D + db * 32 + col]);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(v, w[j], c, 0, 0, 0);
+    }
+}
+
+// Window outputs o_q = sum_k a_qk v_k: each workgroup covers PO_CHUNK keys for one
+// query block, its four waves summed in LDS, one partial per chunk.
+template <int D>
+__global__ void __launch_bounds__(PM_THREADS) pe_out_mfma(PeArgs a, int chunks) {
+    constexpr int NDB = D / 32;
+    __shared__ uint16_t s_v[PM_THREADS / 64][32 * D];
+    __shared__ float s_o[32][D];
+    const int nb = (a.G * a.W + 31) / 32;
+    const int64_t rr = blockIdx.x / (nb * chunks);
+    const int b = (int)((blockIdx.x / chunks) % nb);
+    const int ch = (int)(blockIdx.x % chunks);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+    bf16x8 qf[D / 16];
+    float mmq;
+    int64_t qpos;
+    bool qvalid;
+    const uint16_t *Kr, *Vr;
+    pm_setup<D>(a, rr, b, qf, mmq, qpos, qvalid, &Kr, &Vr);
+    f32x16 co[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) co[db] = f32x16{};
+    const int64_t c0 = (int64_t)ch * PO_CHUNK;
+    const int64_t c1 = c0 + PO_CHUNK < a.kend ? c0 + PO_CHUNK : a.kend;
+    for (int64_t j0 = c0 + 32 * wave; j0 < c1; j0 += 32 * (PM_THREADS / 64)) {
+        float w[16];
+        pm_tile<D>(a, Kr, Vr, j0, qf, mmq, qpos, s_v[wave], w);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) pm_pv<D>(s_v[wave], w, db, 0, 16, co[db]);
+    }
+    // waves in turn add their partial into s_o
+    for (int wv = 0; wv < PM_THREADS / 64; ++wv) {
+        if (wave == wv) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float &dst = s_o[col][db * 32 + acc_row(i, hf)];
+                    dst = (wv == 0 ? 0.f : dst) + co[db][i];
+                }
+        }
+        __syncthreads();
+    }
+    const int QRP = nb * 32;
+    float *out = a.opart + (((size_t)ch * (gridDim.x / (nb * chunks)) + rr) * QRP + b * 32) * D;
+    for (int e = threadIdx.x; e < 32 * D; e += PM_THREADS) out[e] = s_o[e / D][e % D];
+}
+
+// o[rr][q][:] = sum over chunks of the partials, in chunk order.
+__global__ void pe_out_reduce(const float *opart, float *o, int64_t n, int chunks) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        float acc = 0.f;
+        for (int c = 0; c < chunks; ++c) acc += opart[(size_t)c * n + i];
+        o[i] = acc;
+    }
+}
+
+// Page effects for pages of PS = 8, 16 or 32 tokens: per page and query row,
+// t = S - alpha o with S = sum_{k in page} a_qk v_k from the matrix cores, the
+// relative norm reduced to the max over the wave's query rows and then over
+// workgroups with an atomic max on the non-negative float bits.
+template <int D, int PS>
+__global__ void __launch_bounds__(PM_THREADS) pe_effect_mfma(PeArgs a, int chunks) {
+    constexpr int NDB = D / 32;
+    constexpr int JP = PS / 2;  // MFMA key pairs per page
+    __shared__ uint16_t s_v[PM_THREADS / 64][32 * D];
+    const int nb = (a.G * a.W + 31) / 32;
+    const int64_t rr = blockIdx.x / (nb * chunks);
+    const int b = (int)((blockIdx.x / chunks) % nb);
+    const int ch = (int)(blockIdx.x % chunks);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+    bf16x8 qf[D / 16];
+    float mmq;
+    int64_t qpos;
+    bool qvalid;
+    const uint16_t *Kr, *Vr;
+    pm_setup<D>(a, rr, b, qf, mmq, qpos, qvalid, &Kr, &Vr);
+    const int QRP = nb * 32;
+    // this lane's part of o_q in the C[d][q] layout, and ||o_q||
+    float ov[NDB][16];
+    float o2 = 0.f;
+    {
+        const float *o = a.o + ((size_t)rr * QRP + b * 32 + col) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                ov[db][i] = o[db * 32 + acc_row(i, hf)];
+                o2 = fmaf(ov[db][i], ov[db][i], o2);
+            }
+    }
+    o2 += __shfl_xor(o2, 32);
+    const float onorm = sqrtf(o2);
+    const int n_seq_idx = (int)(rr / a.Hkv);
+    const int64_t n_tok = (int64_t)a.n_pages * PS;
+    const int64_t c0 = (int64_t)ch * PO_CHUNK;
+    const int64_t c1 = c0 + PO_CHUNK < n_tok ? c0 + PO_CHUNK : n_tok;
+    for (int64_t j0 = c0 + 32 * wave; j0 < c1; j0 += 32 * (PM_THREADS / 64)) {
+        float w[16];
+        pm_tile<D>(a, Kr, Vr, j0, qf, mmq, qpos, s_v[wave], w);
+#pragma unroll
+        for (int pg = 0; pg < 32 / PS; ++pg) {
+            float al = 0.f;
+#pragma unroll
+            for (int j = pg * JP; j < (pg + 1) * JP; ++j) al += w[j];
+            al += __shfl_xor(al, 32);
+            float n2 = 0.f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                f32x16 c = {};
+                pm_pv<D>(s_v[wave], w, db, pg * JP, (pg + 1) * JP, c);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float t = fmaf(-al, ov[db][i], c[i]);
+                    n2 = fmaf(t, t, n2);
+                }
+            }
+            n2 += __shfl_xor(n2, 32);
+            float rel = 0.f, ab = 0.f;
+            if (qvalid) {
+                const float num = sqrtf(n2);
+                const float den = 1.f - al;
+                ab = den > 0.f ? num / den : INFINITY;
+                rel = onorm > 0.f ? ab / onorm : (num > 0.f ? INFINITY : 0.f);
+                if (!(num > 0.f)) ab = rel = 0.f;
+            }
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                rel = fmaxf(rel, __shfl_xor(rel, off));
+                ab = fmaxf(ab, __shfl_xor(ab, off));
+            }
+            const int64_t page = j0 / PS + pg;
+            if (lane == 0 && page < a.n_pages) {
+                atomic_max_nonneg(a.eff_rel + (size_t)n_seq_idx * a.n_pages + page, rel);
+                if (a.eff_abs) atomic_max_nonneg(a.eff_abs + (size_t)n_seq_idx * a.n_pages + page, ab);
+            }
+        }
+    }
 }
 
 // Greedy joint retirement (CommitKV §3.3 Eq. 11), in two kernels per batch of
@@ -396,12 +573,19 @@ __global__ void __launch_bounds__(PG_THREADS) pr_greedy(PeArgs a, const int32_t 
     const int tid = threadIdx.x, sub = tid % TPP;
     const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
     const int P = a.Hkv * QR;
-    for (int pq = tid; pq < P; pq += PG_THREADS) {
-        const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
-        const float *o = a.o + ((size_t)rr * QRP + pq % QR) * D;
+    // ||o_q|| of every query row of the sequence: D/8 threads per row, 16-byte loads
+    for (int p0 = 0; p0 < P; p0 += PPI) {
+        const int pq = p0 + tid / TPP;
         float o2 = 0.f;
-        for (int cc = 0; cc < D; ++cc) o2 = fmaf(o[cc], o[cc], o2);
-        s_onorm[pq] = sqrtf(o2);
+        if (pq < P) {
+            const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
+            const float *o = a.o + ((size_t)rr * QRP + pq % QR) * D + 8 * sub;
+            const float4 x = *reinterpret_cast<const float4 *>(o), y = *reinterpret_cast<const float4 *>(o + 4);
+            o2 = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w + y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+        }
+#pragma unroll
+        for (int off = 1; off < TPP; off <<= 1) o2 += __shfl_xor(o2, off);
+        if (pq < P && sub == 0) s_onorm[pq] = sqrtf(o2);
     }
     if (first) {  // clear the running sums of this sequence's rows
         for (int64_t i = tid; i < (int64_t)a.Hkv * QRP * D; i += PG_THREADS)
@@ -420,29 +604,40 @@ __global__ void __launch_bounds__(PG_THREADS) pr_greedy(PeArgs a, const int32_t 
             continue;
         }
         float worst = 0.f;
-        for (int p0 = 0; p0 < P; p0 += PPI) {
-            const int pq = p0 + tid / TPP;
-            float n2 = 0.f, alj = 0.f;
-            if (pq < P) {
-                const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
-                const int q = pq % QR;
-                const float *t = tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub;
-                const float *acc = accD + ((size_t)rr * QRP + q) * D + 8 * sub;
-                const float4 t0 = *reinterpret_cast<const float4 *>(t), t1 = *reinterpret_cast<const float4 *>(t + 4);
-                const float4 a0 = *reinterpret_cast<const float4 *>(acc), a1 = *reinterpret_cast<const float4 *>(acc + 4);
-                const float jv[8] = {a0.x + t0.x, a0.y + t0.y, a0.z + t0.z, a0.w + t0.w,
-                                     a1.x + t1.x, a1.y + t1.y, a1.z + t1.z, a1.w + t1.w};
+        constexpr int U = 4;  // passes whose loads are issued together
+        for (int p0 = 0; p0 < P; p0 += U * PPI) {
+            float n2[U], alj[U];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) n2 = fmaf(jv[e], jv[e], n2);
-                alj = alphaD[rr * QRP + q] + tA[((size_t)j * rows_local + rr) * QRP + q];
+            for (int u = 0; u < U; ++u) {
+                const int pq = p0 + u * PPI + tid / TPP;
+                n2[u] = 0.f;
+                alj[u] = 0.f;
+                if (pq < P) {
+                    const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
+                    const int q = pq % QR;
+                    const float *t = tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub;
+                    const float *acc = accD + ((size_t)rr * QRP + q) * D + 8 * sub;
+                    const float4 t0 = *reinterpret_cast<const float4 *>(t), t1 = *reinterpret_cast<const float4 *>(t + 4);
+                    const float4 a0 = *reinterpret_cast<const float4 *>(acc), a1 = *reinterpret_cast<const float4 *>(acc + 4);
+                    const float jv[8] = {a0.x + t0.x, a0.y + t0.y, a0.z + t0.z, a0.w + t0.w,
+                                         a1.x + t1.x, a1.y + t1.y, a1.z + t1.z, a1.w + t1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) n2[u] = fmaf(jv[e], jv[e], n2[u]);
+                    alj[u] = alphaD[rr * QRP + q] + tA[((size_t)j * rows_local + rr) * QRP + q];
+                }
             }
 #pragma unroll
-            for (int off = 1; off < TPP; off <<= 1) n2 += __shfl_xor(n2, off);
-            if (pq < P) {
-                const float num = sqrtf(n2), onorm = s_onorm[pq];
-                float rel = 0.f;
-                if (num > 0.f) rel = (1.f - alj > 0.f && onorm > 0.f) ? num / ((1.f - alj) * onorm) : INFINITY;
-                worst = fmaxf(worst, rel);
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int off = 1; off < TPP; off <<= 1) n2[u] += __shfl_xor(n2[u], off);
+                const int pq = p0 + u * PPI + tid / TPP;
+                if (pq < P) {
+                    const float num = sqrtf(n2[u]), onorm = s_onorm[pq];
+                    float rel = 0.f;
+                    if (num > 0.f)
+                        rel = (1.f - alj[u] > 0.f && onorm > 0.f) ? num / ((1.f - alj[u]) * onorm) : INFINITY;
+                    worst = fmaxf(worst, rel);
+                }
             }
         }
         float v = worst;
@@ -516,6 +711,7 @@ static PeArgs pe_args(const kvc_dims *dims, int32_t layer, const uint16_t *K, co
     a.page_size = page_size;
     a.n_pages = n_pages;
     a.eff_rel = a.eff_abs = nullptr;
+    a.opart = w.opart;
     return a;
 }
 
@@ -525,12 +721,17 @@ static int pe_prepare(const kvc_dims *dims, const PeArgs &a, const PageWs &w, hi
     WindowGeom wg{a.qbase, a.kend, a.lsel};
     int st = launch_window_stats(dims, a.K, a.Q, a.W, wg, g.rows_local, w.part, w.mm, s);
     if (st != KVC_OK) return st;
-    const int64_t blocks = g.rows_local * g.nb;
+    const int chunks = (int)((a.kend + PO_CHUNK - 1) / PO_CHUNK);
+    const int64_t blocks = g.rows_local * g.nb * chunks;
+    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "page effect outputs: grid too large");
     if (dims->head_dim == 128)
-        pe_out<128><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a);
+        pe_out_mfma<128><<<dim3((unsigned)blocks), dim3(PM_THREADS), 0, s>>>(a, chunks);
     else
-        pe_out<64><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a);
-    return check_launch("page effect outputs");
+        pe_out_mfma<64><<<dim3((unsigned)blocks), dim3(PM_THREADS), 0, s>>>(a, chunks);
+    if ((st = check_launch("page effect outputs")) != KVC_OK) return st;
+    const int64_t n_o = g.rows_local * g.QRP * dims->head_dim;
+    pe_out_reduce<<<dim3(1024), dim3(256), 0, s>>>(a.opart, w.o, n_o, chunks);
+    return check_launch("page effect outputs (sum)");
 }
 
 }  // namespace kvc
@@ -620,6 +821,24 @@ extern "C" int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16
     if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
     const PageGeom g = page_geom(dims, W, q_first + W);
     const int64_t n_tok = (int64_t)n_pages * page_size;
+    if (page_size == 8 || page_size == 16 || page_size == 32) {
+        const int chunks = (int)((n_tok + PO_CHUNK - 1) / PO_CHUNK);
+        const int64_t blocks = g.rows_local * g.nb * chunks;
+        if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_effect: grid too large");
+        const dim3 grid((unsigned)blocks), block(PM_THREADS);
+#define PEM(DD, PP) pe_effect_mfma<DD, PP><<<grid, block, 0, s>>>(a, chunks)
+        if (dims->head_dim == 128) {
+            if (page_size == 8) PEM(128, 8);
+            else if (page_size == 16) PEM(128, 16);
+            else PEM(128, 32);
+        } else {
+            if (page_size == 8) PEM(64, 8);
+            else if (page_size == 16) PEM(64, 16);
+            else PEM(64, 32);
+        }
+#undef PEM
+        return check_launch("kvc_page_effect");
+    }
     const int cpr = (int)((n_tok + PE_PAGE_CHUNK - 1) / PE_PAGE_CHUNK);
     const int64_t blocks = g.rows_local * g.nb * cpr;
     if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_effect: grid too large");
