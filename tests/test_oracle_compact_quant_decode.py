@@ -142,3 +142,79 @@ def test_decode_single_token_returns_value():
     o, lse = decode.decode_head(np.array([1.0, 2.0, 3.0]), np.array([[1.0, 1.0, 1.0]]), v)
     np.testing.assert_array_equal(o, v[0])
     assert lse == pytest.approx(6.0 / np.sqrt(3))
+
+
+# ---------------------------------------------------------------- reference store pins
+
+def _churn(k, p0, steps, base, rng, store):
+    """Renumber a set of keys `steps` times to fresh positions (eviction churn):
+    with the store every key is re-derived from its first cached copy,
+    without it the stored bf16 key is re-rotated each time."""
+    K = _bf16(rope.rotate(k, p0, base))
+    pos = p0.copy()
+    Kref, pref = (None, None) if store else (None, None)
+    for _ in range(steps):
+        kept = np.arange(k.shape[0])
+        rb = int(rng.integers(0, 6000))                        # new block of positions below L
+        if store:
+            K, _, pos, Kref, pref = compact.compact_row_ref(K, K, pos, kept, rb, base, Kref, pref)
+        else:
+            K, _, pos = compact.compact_row(K, K, pos, kept, rb, base)
+    want = rope.rotate(k, pos, base)
+    got = numfmt.bf16_bits_to_f64(K)
+    return np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
+
+
+def test_reference_store_stops_drift_like_pace_appendix_d():
+    # PACE Appendix D: naive re-rotation's mean relative key error grows with the
+    # number of renumbers (0.011 after 23, 0.019 after 71: ratio 1.73, about
+    # sqrt(71/23) = 1.76, one rounding per renumber adding up like a random walk);
+    # §3.2: with the reference store the error stays at about two roundings
+    # (max 0.003 after 60 renumbers, against 0.031 without).
+    rng = np.random.default_rng(31)
+    n, d, base = 200, 128, 1e6
+    k = rng.standard_normal((n, d))
+    p0 = rng.integers(0, 1_000_000, n)
+    e23 = _churn(k, p0, 23, base, np.random.default_rng(1), False).mean()
+    e71 = _churn(k, p0, 71, base, np.random.default_rng(2), False).mean()
+    assert 1.5 < e71 / e23 < 2.0                                  # ~ sqrt(71/23): compounding
+    naive60 = _churn(k, p0, 60, base, np.random.default_rng(3), False)
+    store60 = _churn(k, p0, 60, base, np.random.default_rng(3), True)
+    store1 = _churn(k, p0, 1, base, np.random.default_rng(3), True)
+    assert store60.max() < 3 * 2.0 ** -8                           # about two bf16 roundings
+    assert store60.max() < 1.5 * store1.max()                      # flat in the number of renumbers
+    assert naive60.max() > 4 * store60.max()
+
+
+def test_reference_store_first_renumber_and_checks():
+    rng = np.random.default_rng(32)
+    T, d, base = 300, 64, 1e4
+    K = _bf16(rng.standard_normal((T, d)))
+    V = _bf16(rng.standard_normal((T, d)))
+    pos = np.arange(T) + 5000
+    kept = np.sort(rng.choice(T, 40, replace=False))
+    # first renumber: the stored keys become the references, at their positions
+    K1, V1, p1, R1, q1 = compact.compact_row_ref(K, V, pos, kept, 0, base)
+    Kn, Vn, pn = compact.compact_row(K, V, pos, kept, 0, base)
+    np.testing.assert_array_equal(K1, Kn)
+    np.testing.assert_array_equal(V1, Vn)
+    np.testing.assert_array_equal(R1, K[kept])
+    np.testing.assert_array_equal(q1, pos[kept])
+    # second renumber from the references: one rotation from the original key
+    kept2 = np.arange(0, 40, 3)
+    K2, _, p2, R2, q2 = compact.compact_row_ref(K1, V1, p1, kept2, 100, base, R1, q1)
+    direct = _bf16(rope.rotate(numfmt.bf16_bits_to_f64(K[kept][kept2]), p2 - pos[kept][kept2], base))
+    np.testing.assert_array_equal(K2, direct)
+    np.testing.assert_array_equal(R2, K[kept][kept2])
+    # a stale reference (the slot was reused by another key) fails the check
+    bad = R1.copy()
+    bad[5] = _bf16(rng.standard_normal(d))
+    assert not compact.ref_matches(K1[5], bad[5], p1[5], q1[5], base)
+    assert compact.ref_matches(K1[6], R1[6], p1[6], q1[6], base)
+    K3, _, _, R3, q3 = compact.compact_row_ref(K1, V1, p1, np.array([5, 6]), 0, base, bad, q1)
+    np.testing.assert_array_equal(R3[0], K1[5])                    # the stored key is the new reference
+    assert q3[0] == p1[5] and q3[1] == q1[6]
+    # positions kept (no renumbering): keys copied, references carried
+    K4, _, p4, R4, q4 = compact.compact_row_ref(K1, V1, p1, kept2, -1, base, R1, q1)
+    np.testing.assert_array_equal(K4, K1[kept2])
+    np.testing.assert_array_equal(R4, R1[kept2])
