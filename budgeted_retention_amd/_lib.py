@@ -47,6 +47,7 @@ class KvcCompactOut(ctypes.Structure):
         ("K_out", c_void_p), ("V_out", c_void_p), ("pos_out", c_void_p), ("n_h", c_void_p),
         ("Kq", c_void_p), ("Vq", c_void_p), ("Ks", c_void_p), ("Vs", c_void_p),
         ("pos_q", c_void_p), ("n_l", c_void_p),
+        ("K_ref", c_void_p), ("p_ref", c_void_p), ("K_ref_out", c_void_p), ("p_ref_out", c_void_p),
     ]
 
 

@@ -110,6 +110,10 @@ struct CompactArgs {
     uint16_t *Ks, *Vs;
     int32_t *pq, *nl;
     const int32_t *h_base, *l_base;
+    const uint16_t *Kref;     // reference store of the current slots, or NULL
+    const int32_t *pref;
+    uint16_t *Kref_out;       // reference store of the kept slots (REF kernels)
+    int32_t *pref_out;
 };
 
 // Rotates four frequency pairs: lo holds x_i..x_{i+3} of the first half, hi
@@ -140,7 +144,38 @@ __device__ __forceinline__ void rotate_quad(uint2 &lo, uint2 &hi, double delta, 
 // loads, so each workgroup waits for two memory latencies in all.
 static constexpr int CMP_UNROLL = 4;
 
-template <int D>
+// True when bf16(R_delta ref) lies within one bf16 step (plus 1e-5 of the
+// reference row's largest magnitude, `refmax`) of the stored key, for the four
+// pairs this thread holds.
+__device__ __forceinline__ bool ref_pairs_match(uint2 rlo, uint2 rhi, uint2 klo, uint2 khi, double delta,
+                                                const double (&th)[4], float refmax) {
+    rotate_quad(rlo, rhi, delta, th);
+    const uint32_t g[4] = {rlo.x, rlo.y, rhi.x, rhi.y}, k[4] = {klo.x, klo.y, khi.x, khi.y};
+    bool ok = true;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float gv = bf16_to_f32((uint16_t)(g[w] >> (16 * h)));
+            const float kv = bf16_to_f32((uint16_t)(k[w] >> (16 * h)));
+            const float tol = fmaxf(fabsf(kv), 1.17549435e-38f) * 0.0078125f + 1e-5f * refmax;
+            ok = ok && fabsf(gv - kv) <= tol;
+        }
+    }
+    return ok;
+}
+
+__device__ __forceinline__ float bf16x4_maxabs(uint2 v) {
+    const float a0 = fabsf(bf16_to_f32((uint16_t)(v.x & 0xFFFF))), a1 = fabsf(bf16_to_f32((uint16_t)(v.x >> 16)));
+    const float a2 = fabsf(bf16_to_f32((uint16_t)(v.y & 0xFFFF))), a3 = fabsf(bf16_to_f32((uint16_t)(v.y >> 16)));
+    return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+}
+
+// REF adds PACE's reference store (non-compounding re-rotation): a kept token
+// whose slot holds a reference that passes the check is re-rotated from it
+// (angle p' - p_ref); any other from its stored key, which becomes its
+// reference at p. The kept slots' references are written beside the keys.
+template <int D, bool REF>
 __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int blocks_per_row) {
     constexpr int TPT = D / 8;
     constexpr int TOK = CMP_THREADS / TPT;
@@ -161,7 +196,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
     const int sub = threadIdx.x % TPT, tin = threadIdx.x / TPT;
     const bool rot = a.renumber_base >= 0;
     double th[4] = {0.0, 0.0, 0.0, 0.0};
-    if (rot) {
+    if (rot || REF) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) th[e] = pow(a.rope_base, -2.0 * (4 * sub + e) / D);
     }
@@ -172,6 +207,8 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         int64_t j, p;
         uint2 lo, hi;
         uint4 v;
+        uint2 rlo, rhi;  // the slot's reference (REF)
+        int64_t pr;
     };
     auto index = [&](int u) -> int64_t {
         const int rho = rho0 + u * TOK;
@@ -195,17 +232,50 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         t.hi = *reinterpret_cast<const uint2 *>(a.K + src + D / 2 + 4 * sub);
         t.v = *reinterpret_cast<const uint4 *>(a.V + src + 8 * sub);
         t.p = a.pos_in ? (int64_t)a.pos_in[(size_t)r * a.T + jj] : jj;
+        t.pr = -1;
+        if (REF && a.Kref) {
+            t.rlo = *reinterpret_cast<const uint2 *>(a.Kref + src + 4 * sub);
+            t.rhi = *reinterpret_cast<const uint2 *>(a.Kref + src + D / 2 + 4 * sub);
+            t.pr = (int64_t)a.pref[(size_t)r * a.T + jj];
+        }
         return t;
     };
     auto put = [&](Tok &t, int u) {
-        if (t.j < 0) return;
+        if (t.j < 0) return;  // the same for the token's TPT threads
         const int rho = rho0 + u * TOK;
+        const size_t dst = ((size_t)r * a.out_stride + base + rho) * D;
+        int64_t psrc = t.p;
+        if (REF) {
+            // the check before use; the token's TPT adjacent lanes agree on it
+            bool use = false;
+            if (t.pr >= 0) {
+                float rm = fmaxf(bf16x4_maxabs(t.rlo), bf16x4_maxabs(t.rhi));
+#pragma unroll
+                for (int m = 1; m < TPT; m <<= 1) rm = fmaxf(rm, __shfl_xor(rm, m));
+                int ok = ref_pairs_match(t.rlo, t.rhi, t.lo, t.hi, (double)(t.p - t.pr), th, rm) ? 1 : 0;
+#pragma unroll
+                for (int m = 1; m < TPT; m <<= 1) ok &= __shfl_xor(ok, m);
+                use = ok != 0;
+            }
+            if (use) {
+                psrc = t.pr;
+            } else {
+                t.rlo = t.lo;
+                t.rhi = t.hi;
+            }
+            *reinterpret_cast<uint2 *>(a.Kref_out + dst + 4 * sub) = t.rlo;
+            *reinterpret_cast<uint2 *>(a.Kref_out + dst + D / 2 + 4 * sub) = t.rhi;
+            if (sub == 0) a.pref_out[(size_t)r * a.out_stride + base + rho] = (int32_t)psrc;
+        }
         int64_t pn = t.p;
         if (rot) {
             pn = (int64_t)a.renumber_base + rho;
-            rotate_quad(t.lo, t.hi, (double)(pn - t.p), th);
+            if (REF) {
+                t.lo = t.rlo;
+                t.hi = t.rhi;
+            }
+            rotate_quad(t.lo, t.hi, (double)(pn - psrc), th);
         }
-        const size_t dst = ((size_t)r * a.out_stride + base + rho) * D;
         *reinterpret_cast<uint2 *>(a.Ko + dst + 4 * sub) = t.lo;
         *reinterpret_cast<uint2 *>(a.Ko + dst + D / 2 + 4 * sub) = t.hi;
         *reinterpret_cast<uint4 *>(a.Vo + dst + 8 * sub) = t.v;
@@ -367,6 +437,18 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     } else if (!out->K_out || !out->V_out) {
         return fail(KVC_ERR_ARG, "kvc_compact_rerotate: K_out/V_out are NULL");
     }
+    if (out->K_ref_out || out->p_ref_out || out->K_ref || out->p_ref) {
+        if (!out->K_ref_out || !out->p_ref_out)
+            return fail(KVC_ERR_ARG, "kvc_compact_rerotate: the reference store needs K_ref_out and p_ref_out");
+        if ((out->K_ref == nullptr) != (out->p_ref == nullptr))
+            return fail(KVC_ERR_ARG, "kvc_compact_rerotate: K_ref and p_ref go together");
+        if (out->action || out->kept_page > 0)
+            return fail(KVC_ERR_UNSUPPORTED,
+                        "kvc_compact_rerotate: the reference store takes neither actions nor page lists");
+        if (!(rope_base > 1.0))
+            return fail(KVC_ERR_ARG, "kvc_compact_rerotate: the reference check needs rope_base > 1 (got %g)",
+                        rope_base);
+    }
     CompactArgs a;
     a.K = K;
     a.V = V;
@@ -393,6 +475,10 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     a.nl = out->n_l;
     a.h_base = out->h_base;
     a.l_base = out->l_base;
+    a.Kref = out->K_ref;
+    a.pref = out->p_ref;
+    a.Kref_out = out->K_ref_out;
+    a.pref_out = out->p_ref_out;
     const int64_t rows = n_rows(dims);
     hipStream_t s = as_stream(stream);
     if (!out->action) {
@@ -402,10 +488,19 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
         int bpr = (cap + CMP_UNROLL * tok - 1) / (CMP_UNROLL * tok);  // CMP_UNROLL tokens per group
         if (bpr < 1) bpr = 1;
         if (rows * bpr > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_compact_rerotate: grid too large");
-        if (dims->head_dim == 128)
-            compact_plain<128><<<dim3((unsigned)(rows * bpr)), dim3(CMP_THREADS), 0, s>>>(a, bpr);
-        else
-            compact_plain<64><<<dim3((unsigned)(rows * bpr)), dim3(CMP_THREADS), 0, s>>>(a, bpr);
+        const dim3 grid((unsigned)(rows * bpr)), block(CMP_THREADS);
+        const bool ref = out->K_ref_out != nullptr;
+        if (dims->head_dim == 128) {
+            if (ref)
+                compact_plain<128, true><<<grid, block, 0, s>>>(a, bpr);
+            else
+                compact_plain<128, false><<<grid, block, 0, s>>>(a, bpr);
+        } else {
+            if (ref)
+                compact_plain<64, true><<<grid, block, 0, s>>>(a, bpr);
+            else
+                compact_plain<64, false><<<grid, block, 0, s>>>(a, bpr);
+        }
     } else {
         if (dims->head_dim == 128)
             compact_tiered<128><<<dim3((unsigned)rows), dim3(CMP_THREADS), 0, s>>>(a);

@@ -138,6 +138,10 @@ class CompactOut:
     h_base: Optional[torch.Tensor] = None      # int32 [rows] first bf16 slot (append)
     l_base: Optional[torch.Tensor] = None      # int32 [rows] first int8 slot (append)
     kept_page: int = 0                         # > 0: kept lists are per-sequence page indices
+    K_ref: Optional[torch.Tensor] = None       # reference store of the current slots (bf16)
+    p_ref: Optional[torch.Tensor] = None       # int32 positions of those references (< 0: none)
+    K_ref_out: Optional[torch.Tensor] = None   # reference store of the kept slots
+    p_ref_out: Optional[torch.Tensor] = None
 
     def to_c(self):
         return _lib.KvcCompactOut(
@@ -147,7 +151,9 @@ class CompactOut:
             _ptr(self.pos_out, torch.int32, "pos_out"), _ptr(self.n_h, torch.int32, "n_h"),
             _ptr(self.Kq, torch.int8, "Kq"), _ptr(self.Vq, torch.int8, "Vq"),
             _ptr(self.Ks, torch.int16, "Ks"), _ptr(self.Vs, torch.int16, "Vs"),
-            _ptr(self.pos_q, torch.int32, "pos_q"), _ptr(self.n_l, torch.int32, "n_l"))
+            _ptr(self.pos_q, torch.int32, "pos_q"), _ptr(self.n_l, torch.int32, "n_l"),
+            _ptr(self.K_ref, torch.bfloat16, "K_ref"), _ptr(self.p_ref, torch.int32, "p_ref"),
+            _ptr(self.K_ref_out, torch.bfloat16, "K_ref_out"), _ptr(self.p_ref_out, torch.int32, "p_ref_out"))
 
 
 def kvc_compact_rerotate(dims, K, V, pos_in, kept_idx, kept_stride, n_kept, renumber_base, rope_base,

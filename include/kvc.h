@@ -181,6 +181,24 @@ typedef struct kvc_compact_out {
     uint16_t *Vs;         /* fp16 [N][L][Hkv][out_stride] per-token V scale */
     int32_t *pos_q;       /* int32 [N][L][Hkv][out_stride], may be NULL */
     int32_t *n_l;         /* int32 [N][L][Hkv] rows written to the int8 tier, may be NULL */
+    /* Reference store (PACE §3.2, non-compounding re-rotation; Appendix D):
+     * per cache slot, the key that the slot's key was derived from and that
+     * key's position. K_ref_out != NULL turns it on; only the plain path takes
+     * it (action == NULL, kept_page == 0; else KVC_ERR_UNSUPPORTED), and
+     * rope_base must exceed 1 even when renumber_base < 0.
+     * Kept token j uses its reference when p_ref[j] >= 0 and the reference
+     * passes the check before use: every element of bf16(R_{p - p_ref[j]}
+     * K_ref[j]) within max(|K|, 2^-126) * 2^-7 + 1e-5 * max|K_ref[j]| of the
+     * stored K[j]. Then K' = bf16(R_{p' - p_ref[j]} K_ref[j]) and the
+     * reference is carried; otherwise K' = bf16(R_{p' - p} K[j]) and K[j] at
+     * p becomes the reference. With renumber_base < 0 keys are copied and
+     * only the store is rewritten. K_ref_out[rho] / p_ref_out[rho] follow the
+     * kept order like K_out (from h_base). K_ref / p_ref NULL: no references
+     * yet (each kept key starts one). Outputs must not alias the inputs. */
+    const uint16_t *K_ref;    /* bf16 [N][L][Hkv][T][d], NULL together with p_ref */
+    const int32_t *p_ref;     /* int32 [N][L][Hkv][T], < 0 = no reference */
+    uint16_t *K_ref_out;      /* bf16 [N][L][Hkv][out_stride][d], or NULL */
+    int32_t *p_ref_out;       /* int32 [N][L][Hkv][out_stride], with K_ref_out */
 } kvc_compact_out;
 
 /*

@@ -186,3 +186,26 @@ def test_page_scores_reject_bad_arguments():
     assert call(order=FAKE) == _lib.KVC_ERR_ARG                  # order without accepted
     assert call(order=FAKE, acc=FAKE, n_cand=0) == _lib.KVC_ERR_ARG
     assert lib.kvc_last_error().decode().startswith("kvc_page_scores")
+
+
+def test_compact_reference_store_rejects_bad_combinations():
+    lib = _lib.load()
+    d = _dims()
+    out = _lib.KvcCompactOut()
+    out.out_stride = 512
+    out.K_out = out.V_out = FAKE
+    call = lambda rb=0, base=1e4: lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 512, FAKE,
+                                                           rb, base, ctypes.byref(out), None)
+    out.K_ref_out = FAKE
+    assert call() == _lib.KVC_ERR_ARG                            # p_ref_out missing
+    out.p_ref_out = FAKE
+    out.K_ref = FAKE
+    assert call() == _lib.KVC_ERR_ARG                            # K_ref without p_ref
+    out.p_ref = FAKE
+    assert call(rb=-1, base=1.0) == _lib.KVC_ERR_ARG             # the check rotates: base must exceed 1
+    out.kept_page = 16
+    assert call() == _lib.KVC_ERR_UNSUPPORTED                    # plain per-row lists only
+    out.kept_page = 0
+    out.action = FAKE
+    out.Kq = out.Vq = out.Ks = out.Vs = FAKE
+    assert call() == _lib.KVC_ERR_UNSUPPORTED
