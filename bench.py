@@ -247,7 +247,51 @@ def bench_compaction(args, w, dev):
              "decode_ms": round(part["kvc_decode_attn"], 4),
              "calls": per_call_rates(ab, part),
              "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}
+    if not per_layer and w.renumber_base >= 0:
+        extra["ref_store"] = bench_ref_store(args, w, dims, views[0][0], views[0][1], kept, n_kept, Ko, Vo, po, dev)
     return value, ms, config, roof, cpu, extra
+
+
+def bench_ref_store(args, w, dims, K, V, kept, n_kept, Ko, Vo, po, dev):
+    """The next compaction of the resident set with the reference store on:
+    the B kept slots (with the references a first compaction started) plus B
+    newly appended tokens without references, of which every other slot is
+    kept. Timed on its own; not part of the step."""
+    import torch
+    from budgeted_retention_amd import kvc, synth
+    rows, B, d = Ko.shape
+    R1 = torch.empty_like(Ko)
+    q1 = torch.empty_like(po)
+    first = kvc.CompactOut(B, Ko, Vo, po, None, K_ref_out=R1, p_ref_out=q1)
+    kvc.kvc_compact_rerotate(dims, K, V, None, kept, B, n_kept, w.renumber_base, w.rope_base, first)
+    rK = torch.cat([Ko, synth.normal_bf16((rows, B, d), 71, dev)], dim=1)
+    rV = torch.cat([Vo, synth.normal_bf16((rows, B, d), 72, dev)], dim=1)
+    rp = torch.cat([po, torch.arange(B, 2 * B, dtype=torch.int32, device=dev).repeat(rows, 1)], dim=1)
+    rR = torch.cat([R1, torch.zeros_like(R1)], dim=1)
+    rq = torch.cat([q1, torch.full_like(q1, -1)], dim=1)
+    keep = torch.arange(0, 2 * B, 2, dtype=torch.int32, device=dev).repeat(rows, 1)
+    cnt = torch.full((rows,), B, dtype=torch.int32, device=dev)
+    outs = [torch.empty((rows, B, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    o2 = kvc.CompactOut(B, outs[0], outs[1], torch.empty_like(po), None, K_ref=rR, p_ref=rq,
+                        K_ref_out=outs[2], p_ref_out=torch.empty_like(po))
+    dims_r = kvc.make_dims(w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, d, 2 * B)
+    call = lambda: kvc.kvc_compact_rerotate(dims_r, rK, rV, rp, keep, B, cnt, 0, w.rope_base, o2)  # noqa: E731
+    for _ in range(max(1, args.warmup)):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    used = int((o2.p_ref_out[:, : B // 2] == q1[:, 0::2]).float().mean().item() * 100 + 0.5)
+    # kept K, V and references read and written, plus index, positions and reference positions
+    nbytes = rows * B * (12 * d + 20)
+    return {"ms": round(ms, 4), "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+            "resident_slots": 2 * B, "kept": B, "old_slots_from_reference_pct": used}
 
 
 def bench_pipeline(args, w, dev, kind):
