@@ -15,6 +15,10 @@ Other workloads (parity cases, measured the same way call by call):
   qwen3_8b_1m     T=1,048,576, one layer per call (154.6 GB of K+V resident)
   pask_llama3_8b  64 x 32 layers: prompt compaction, int8/bf16/release tiers, decode
   commitkv_28l    16 x 28 layers: page effects, retirement, checkpoint, paged decode
+  pace_h2o_decode 36 layers x 8 KV heads of 2048 + 32 resident slots: one step is one
+                  eviction cycle (32 decode steps adding H2O cumulative attention,
+                  then top-B by cumulative score + foresight bonus and compaction);
+                  value = resident tokens per second through the cycle
 
 Prints one JSON line.
 """
@@ -390,6 +394,86 @@ def bench_pipeline(args, w, dev, kind):
     return value, ms, config, roof, cpu, extra
 
 
+def cpu_h2o_rows(w, inp, budget_s):
+    """Time the float64 oracle's cycle (E decode steps of cumulative attention,
+    eviction, gather) over a prefix of rows. Returns (rows done, seconds)."""
+    import numpy as np
+    import torch
+    from oracle import h2o, numfmt, policy
+    B, E, G, L, Hkv = w.budget, w.interval, w.group, w.n_layers, w.n_kv_heads
+    bonus = np.array([0.0] + [policy.foresight_bonus(1e3, 0.35, s) for s in inp.steps_ahead]).reshape(-1, 1)
+    floor = np.zeros_like(bonus, np.uint8)
+    done, spent = 0, 0.0
+    while done < w.rows and spent < budget_s:
+        r = done
+        l, h = (r // Hkv) % L, r % Hkv
+        K = inp.K[r].cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        K[B:] = inp.K_new[0, r].cpu().view(torch.int16).numpy().view(np.uint16)
+        q = inp.q[0, :, 0, l, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
+        acc = inp.acc[r].cpu().numpy().astype(np.float64)
+        tags = inp.tags[r].cpu().numpy().astype(np.int64)
+        t0 = time.perf_counter()
+        Kf = numfmt.bf16_bits_to_f64(K)
+        for e in range(E):
+            acc[:B + e + 1] = h2o.accumulate(acc[:B + e + 1], q[e], Kf[:B + e + 1])
+        kept = h2o.evict(acc, tags, bonus, floor, 0, w.n_sink, w.n_recent, B)
+        _ = (K[kept], acc[kept], tags[kept])
+        spent += time.perf_counter() - t0
+        done += 1
+    return done, spent
+
+
+def bench_h2o(args, w, dev):
+    """PACE-style decode with H2O eviction: one step = one cycle."""
+    import torch
+    from budgeted_retention_amd import pipelines, synth
+    cycles = args.warmup + args.steps
+    inp = synth.make_h2o_inputs(w, max(cycles, 1), dev)
+    calibrate_copy(args, dev)
+    timer = pipelines.CallTimer()
+    # one run over warm-up + timed cycles; the warm-up cycles' events are dropped
+    marks = []
+
+    class Cut:
+        def __call__(self, name):
+            if name == "append":
+                marks.append(len(timer.events))
+            return timer(name)
+    res = pipelines.run_h2o(w, inp, cycles, Cut())
+    torch.cuda.synchronize()
+    first = marks[args.warmup] if args.warmup < len(marks) else len(timer.events)
+    timer.events = timer.events[first:]
+    part = {k: v / args.steps for k, v in timer.totals_ms().items()}
+    rows, S, B, E, d, G = w.rows, w.slots, w.budget, w.interval, w.head_dim, w.group
+    path_calls = ["kvc_decode_attn_h2o", "kvc_select", "kvc_compact_rerotate"]
+    ms = sum(part[k] for k in path_calls)
+    # decode: every resident key's K and V read once per step (B+1 .. B+E keys) and its score
+    # read and written; select: scores and tags read, B indices written; compaction: kept K, V,
+    # reference keys, positions, reference positions, scores and tags read and written, index read
+    keys = rows * sum(B + e + 1 for e in range(E))
+    ab = {"kvc_decode_attn_h2o": keys * (2 * d * 2 + 8) + E * w.n_seq * w.n_layers * w.n_q_heads * d * 2 * 2,
+          "kvc_select": rows * (S * 5 + B * 4),
+          "kvc_compact_rerotate": rows * B * (12 * d + 30)}
+    dom = max(path_calls, key=lambda k: part[k])
+    roof = roofline(ab[dom], part[dom], dom, w.name)
+    cpu = None
+    if args.cpu_seconds > 0:
+        done, spent = cpu_h2o_rows(w, inp, args.cpu_seconds)
+        cpu = {"value": w.n_seq * S * (done / rows) / spent, "unit": "tokens/s", "cores": cpu_cores(),
+               "kind": "oracle",
+               "sample": f"{done} of {rows} rows through one cycle ({E} decode steps of cumulative attention, "
+                         f"eviction, gather), float64 numpy oracle, {spent:.1f} s scaled to all rows"}
+    config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "kv_heads": w.n_kv_heads,
+              "q_heads": w.n_q_heads, "head_dim": d, "budget": B, "interval": E, "sink": w.n_sink,
+              "recent": w.n_recent, "parallelism": "none"}
+    extra = {"breakdown_ms": {k: round(part[k], 4) for k in path_calls},
+             "other_ms": {k: round(v, 4) for k, v in part.items() if k not in path_calls},
+             "decoded_tokens_per_s": round(w.n_seq * E / (ms * 1e-3), 1),
+             "calls": per_call_rates(ab, part)}
+    del res
+    return w.n_seq * S / (ms * 1e-3), ms, config, roof, cpu, extra
+
+
 def calibrate_copy(args, dev):
     import torch
     if args.calibrate_copy:
@@ -422,6 +506,9 @@ def main():
     elif args.workload in synth.COMMIT_WORKLOADS:
         w = synth.COMMIT_WORKLOADS[args.workload]
         value, ms, config, roof, cpu, extra = bench_pipeline(args, w, dev, "commit")
+    elif args.workload in synth.H2O_WORKLOADS:
+        w = synth.H2O_WORKLOADS[args.workload]
+        value, ms, config, roof, cpu, extra = bench_h2o(args, w, dev)
     else:
         raise SystemExit(f"unknown workload {args.workload}")
     line = {

@@ -35,7 +35,7 @@ class KvcPolicy(ctypes.Structure):
     _fields_ = [
         ("n_sink", c_int32), ("n_recent", c_int32), ("budget", c_int32),
         ("n_tags", c_int32), ("n_groups", c_int32), ("layer_base", c_int32),
-        ("n_layers_model", c_int32), ("reserved", c_int32),
+        ("n_layers_model", c_int32), ("tag_rows", c_int32),
         ("tags", c_void_p), ("tag_bonus", c_void_p), ("tag_floor", c_void_p),
     ]
 
@@ -48,6 +48,7 @@ class KvcCompactOut(ctypes.Structure):
         ("Kq", c_void_p), ("Vq", c_void_p), ("Ks", c_void_p), ("Vs", c_void_p),
         ("pos_q", c_void_p), ("n_l", c_void_p),
         ("K_ref", c_void_p), ("p_ref", c_void_p), ("K_ref_out", c_void_p), ("p_ref_out", c_void_p),
+        ("score_in", c_void_p), ("score_out", c_void_p), ("tag_in", c_void_p), ("tag_out", c_void_p),
     ]
 
 
@@ -75,6 +76,10 @@ PROTOTYPES = {
                                        c_int64, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_h2o_workspace_bytes": (c_size_t, [ctypes.POINTER(KvcDims), c_int64]),
+    "kvc_decode_attn_h2o": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                           c_void_p]),
     "kvc_page_workspace_bytes": (c_size_t, [ctypes.POINTER(KvcDims), c_int32, c_int64]),
     "kvc_page_effect": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_int32, c_void_p, c_void_p, c_void_p,
                                        c_int32, c_int64, c_int32, c_int32, c_void_p, c_void_p,

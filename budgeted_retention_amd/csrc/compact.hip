@@ -114,6 +114,10 @@ struct CompactArgs {
     const int32_t *pref;
     uint16_t *Kref_out;       // reference store of the kept slots (REF kernels)
     int32_t *pref_out;
+    const float *score_in;    // per-slot payloads carried with the tokens, or NULL
+    float *score_out;
+    const uint8_t *tag_in;
+    uint8_t *tag_out;
 };
 
 // Rotates four frequency pairs: lo holds x_i..x_{i+3} of the first half, hi
@@ -209,6 +213,8 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         uint4 v;
         uint2 rlo, rhi;  // the slot's reference (REF)
         int64_t pr;
+        float sc;        // carried score and tag (thread sub == 0)
+        uint32_t tg;
     };
     auto index = [&](int u) -> int64_t {
         const int rho = rho0 + u * TOK;
@@ -233,6 +239,10 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         t.v = *reinterpret_cast<const uint4 *>(a.V + src + 8 * sub);
         t.p = a.pos_in ? (int64_t)a.pos_in[(size_t)r * a.T + jj] : jj;
         t.pr = -1;
+        t.sc = 0.f;
+        t.tg = 0u;
+        if (sub == 0 && a.score_in) t.sc = a.score_in[(size_t)r * a.T + jj];
+        if (sub == 0 && a.tag_in) t.tg = a.tag_in[(size_t)r * a.T + jj];
         if (REF && a.Kref) {
             t.rlo = *reinterpret_cast<const uint2 *>(a.Kref + src + 4 * sub);
             t.rhi = *reinterpret_cast<const uint2 *>(a.Kref + src + D / 2 + 4 * sub);
@@ -280,6 +290,8 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         *reinterpret_cast<uint2 *>(a.Ko + dst + D / 2 + 4 * sub) = t.hi;
         *reinterpret_cast<uint4 *>(a.Vo + dst + 8 * sub) = t.v;
         if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + base + rho] = (int32_t)pn;
+        if (sub == 0 && a.score_out) a.score_out[(size_t)r * a.out_stride + base + rho] = t.sc;
+        if (sub == 0 && a.tag_out) a.tag_out[(size_t)r * a.out_stride + base + rho] = (uint8_t)t.tg;
     };
     static_assert(U == 4, "the token batch below is written out for four tokens");
     const int64_t j0 = index(0), j1 = index(1), j2 = index(2), j3 = index(3);
@@ -449,6 +461,10 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
             return fail(KVC_ERR_ARG, "kvc_compact_rerotate: the reference check needs rope_base > 1 (got %g)",
                         rope_base);
     }
+    if ((out->score_in == nullptr) != (out->score_out == nullptr) || (out->tag_in == nullptr) != (out->tag_out == nullptr))
+        return fail(KVC_ERR_ARG, "kvc_compact_rerotate: carried scores and tags need both in and out");
+    if (out->action && (out->score_out || out->tag_out))
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_compact_rerotate: the tiered path carries no scores or tags");
     CompactArgs a;
     a.K = K;
     a.V = V;
@@ -479,6 +495,10 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     a.pref = out->p_ref;
     a.Kref_out = out->K_ref_out;
     a.pref_out = out->p_ref_out;
+    a.score_in = out->score_in;
+    a.score_out = out->score_out;
+    a.tag_in = out->tag_in;
+    a.tag_out = out->tag_out;
     const int64_t rows = n_rows(dims);
     hipStream_t s = as_stream(stream);
     if (!out->action) {

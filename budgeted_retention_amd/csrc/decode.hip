@@ -14,6 +14,11 @@
 // both partitions.
 // The bf16 partition may be paged: token t of a row then lives in slot
 // block_table[n][t / page_size] * page_size + t % page_size of the row's storage.
+//
+// kvc_decode_attn_h2o adds H2O's cumulative attention (PACE §2 background,
+// §3.1 "cumulative attention score"): the partial kernel also writes every
+// key's scaled logit per head, the merge writes each head's log2 normaliser,
+// and a third kernel adds sum_g 2^(logit - lse2_g) to the key's running score.
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -41,6 +46,8 @@ struct DecodeArgs {
     float *part;             // [rows][chunks_h + chunks_l][G][D + 2]
     uint16_t *o;
     float *lse;
+    float *logit;            // H2O: [rows][G][chunks_h * DEC_CHUNK] log2-scaled logits, or NULL
+    float *lse2;             // H2O: [rows][G] log2 normalisers
 };
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
@@ -206,6 +213,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
         v[g] = tid < cnt ? s_p[g][tid] : -INFINITY;
+        if (!LOW && a.logit && g < G && tid < cnt)
+            a.logit[((size_t)r * G + g) * ((size_t)a.chunks_h * DEC_CHUNK) + k0 + tid] = v[g];
         float x = v[g];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -322,6 +331,23 @@ __global__ void __launch_bounds__(D) decode_merge(DecodeArgs a) {
     const size_t head = (size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * a.G + g;
     a.o[head * D + c] = f32_to_bf16(Lsum > 0.f ? U / Lsum : 0.f);
     if (c == 0 && a.lse) a.lse[head] = Lsum > 0.f ? (M + log2f(Lsum)) * 0.69314718055994531f : -INFINITY;
+    if (c == 0 && a.lse2) a.lse2[rg] = Lsum > 0.f ? M + log2f(Lsum) : INFINITY;
+}
+
+// H2O: acc[r][t] += sum over the group's heads of softmax weight 2^(logit - lse2)
+// for the row's n_h cached keys; one thread per key.
+__global__ void __launch_bounds__(DEC_THREADS) decode_mass(DecodeArgs a, float *acc) {
+    const int64_t r = blockIdx.x / a.chunks_h;
+    const int chunk = blockIdx.x % a.chunks_h;
+    int64_t n = a.n_h[r];
+    if (n > a.stride_h) n = a.stride_h;
+    const int64_t t = (int64_t)chunk * DEC_CHUNK + threadIdx.x;
+    if (t >= n) return;
+    const size_t lstride = (size_t)a.chunks_h * DEC_CHUNK;
+    float m = 0.f;
+    for (int g = 0; g < a.G; ++g)
+        m += __builtin_amdgcn_exp2f(a.logit[((size_t)r * a.G + g) * lstride + t] - a.lse2[(size_t)r * a.G + g]);
+    acc[(size_t)r * a.stride_h + t] += m;
 }
 
 size_t decode_workspace_bytes(const kvc_dims *d, int64_t stride_h, int64_t stride_l) {
@@ -330,6 +356,58 @@ size_t decode_workspace_bytes(const kvc_dims *d, int64_t stride_h, int64_t strid
     const int64_t cl = (stride_l + DEC_CHUNK - 1) / DEC_CHUNK;
     return (size_t)n_rows(d) * (ch + cl) * G * (d->head_dim + 2) * sizeof(float);
 }
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// H2O workspace: the partials, then the logits, then the normalisers.
+size_t decode_h2o_workspace_bytes(const kvc_dims *d, int64_t stride_h) {
+    const int G = d->n_q_heads / d->n_kv_heads;
+    const int64_t ch = (stride_h + DEC_CHUNK - 1) / DEC_CHUNK;
+    return align256(decode_workspace_bytes(d, stride_h, 0)) +
+           align256((size_t)n_rows(d) * G * ch * DEC_CHUNK * sizeof(float)) + (size_t)n_rows(d) * G * sizeof(float);
+}
+
+// Partials over both partitions, the Eq. 15 merge, and (acc != NULL) the H2O update.
+static int decode_launch(const kvc_dims *dims, DecodeArgs &a, float *acc, hipStream_t s, const char *who) {
+    int st;
+    const int G = a.G;
+    const int64_t rows = n_rows(dims);
+    const int64_t blocks = rows * (a.chunks_h + a.chunks_l);
+    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "%s: grid too large", who);
+    const dim3 grid_h((unsigned)(rows * a.chunks_h)), grid_l((unsigned)(rows * a.chunks_l)), block(DEC_THREADS);
+#define DEC_PARTIAL_G(DD, GG)                                                              \
+    do {                                                                                   \
+        decode_partial<DD, GG, false><<<grid_h, block, 0, s>>>(a);                         \
+        if (a.chunks_l) decode_partial<DD, GG, true><<<grid_l, block, 0, s>>>(a);          \
+    } while (0)
+#define DEC_PARTIAL(DD)                                                                    \
+    do {                                                                                   \
+        if (G <= 4)                                                                        \
+            DEC_PARTIAL_G(DD, 4);                                                          \
+        else if (G <= 8)                                                                   \
+            DEC_PARTIAL_G(DD, 8);                                                          \
+        else                                                                               \
+            DEC_PARTIAL_G(DD, 16);                                                         \
+    } while (0)
+    if (dims->head_dim == 128) {
+        DEC_PARTIAL(128);
+        if ((st = check_launch(who)) != KVC_OK) return st;
+        decode_merge<128><<<dim3((unsigned)(rows * G)), dim3(128), 0, s>>>(a);
+    } else {
+        DEC_PARTIAL(64);
+        if ((st = check_launch(who)) != KVC_OK) return st;
+        decode_merge<64><<<dim3((unsigned)(rows * G)), dim3(64), 0, s>>>(a);
+    }
+#undef DEC_PARTIAL
+#undef DEC_PARTIAL_G
+    if ((st = check_launch(who)) != KVC_OK) return st;
+    if (acc) {
+        decode_mass<<<grid_h, block, 0, s>>>(a, acc);
+        return check_launch(who);
+    }
+    return KVC_OK;
+}
+
 
 }  // namespace kvc
 
@@ -385,38 +463,67 @@ extern "C" int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const ui
     a.part = reinterpret_cast<float *>(ws);
     a.o = o;
     a.lse = lse;
-    const int64_t rows = n_rows(dims);
-    const int64_t blocks = rows * (a.chunks_h + a.chunks_l);
-    if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_attn: grid too large");
-    hipStream_t s = as_stream(stream);
-    const dim3 grid_h((unsigned)(rows * a.chunks_h)), grid_l((unsigned)(rows * a.chunks_l)), block(DEC_THREADS);
-#define DEC_PARTIAL_G(DD, GG)                                                              \
-    do {                                                                                   \
-        decode_partial<DD, GG, false><<<grid_h, block, 0, s>>>(a);                         \
-        if (a.chunks_l) decode_partial<DD, GG, true><<<grid_l, block, 0, s>>>(a);          \
-    } while (0)
-#define DEC_PARTIAL(DD)                                                                    \
-    do {                                                                                   \
-        if (G <= 4)                                                                        \
-            DEC_PARTIAL_G(DD, 4);                                                          \
-        else if (G <= 8)                                                                   \
-            DEC_PARTIAL_G(DD, 8);                                                          \
-        else                                                                               \
-            DEC_PARTIAL_G(DD, 16);                                                         \
-    } while (0)
-    if (dims->head_dim == 128) {
-        DEC_PARTIAL(128);
-        if ((st = check_launch("kvc_decode_attn partial")) != KVC_OK) return st;
-        decode_merge<128><<<dim3((unsigned)(rows * G)), dim3(128), 0, s>>>(a);
-    } else {
-        DEC_PARTIAL(64);
-        if ((st = check_launch("kvc_decode_attn partial")) != KVC_OK) return st;
-        decode_merge<64><<<dim3((unsigned)(rows * G)), dim3(64), 0, s>>>(a);
-    }
-#undef DEC_PARTIAL
-#undef DEC_PARTIAL_G
-    return check_launch("kvc_decode_attn merge");
+    a.logit = nullptr;
+    a.lse2 = nullptr;
+    return decode_launch(dims, a, nullptr, as_stream(stream), "kvc_decode_attn");
 }
+
+extern "C" size_t kvc_decode_h2o_workspace_bytes(const kvc_dims *dims, int64_t stride_h) {
+    if (check_dims(dims, "kvc_decode_h2o_workspace_bytes") != KVC_OK) return 0;
+    if (stride_h < 0) {
+        fail(KVC_ERR_ARG, "kvc_decode_h2o_workspace_bytes: negative capacity");
+        return 0;
+    }
+    return decode_h2o_workspace_bytes(dims, stride_h);
+}
+
+extern "C" int kvc_decode_attn_h2o(const kvc_dims *dims, const uint16_t *q, const uint16_t *K,
+                                   const uint16_t *V, const int32_t *n_h, int64_t stride_h, float *acc,
+                                   uint16_t *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_dims(dims, "kvc_decode_attn_h2o");
+    if (st != KVC_OK) return st;
+    if (!q || !K || !V || !n_h || !acc || !o) return fail(KVC_ERR_ARG, "kvc_decode_attn_h2o: NULL pointer");
+    if (stride_h <= 0) return fail(KVC_ERR_ARG, "kvc_decode_attn_h2o: stride_h must be positive");
+    if (stride_h > (int64_t)INT32_MAX)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_attn_h2o: pool stride must fit int32");
+    const int G = dims->n_q_heads / dims->n_kv_heads;
+    if (G > DEC_MAX_G)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_attn_h2o: GQA group %d exceeds %d", G, DEC_MAX_G);
+    const size_t need = decode_h2o_workspace_bytes(dims, stride_h);
+    if (!ws || ws_bytes < need)
+        return fail(KVC_ERR_WORKSPACE, "kvc_decode_attn_h2o: workspace %zu < %zu bytes", ws_bytes, need);
+    DecodeArgs a;
+    a.q = q;
+    a.K = K;
+    a.V = V;
+    a.n_h = n_h;
+    a.stride_h = stride_h;
+    a.block_table = nullptr;
+    a.page_size = 0;
+    a.blocks_per_seq = 0;
+    a.Kq = a.Vq = nullptr;
+    a.Ks = a.Vs = nullptr;
+    a.n_l = nullptr;
+    a.stride_l = 0;
+    a.L = dims->n_layers;
+    a.Hkv = dims->n_kv_heads;
+    a.Hq = dims->n_q_heads;
+    a.G = G;
+    a.chunks_h = (int)((stride_h + DEC_CHUNK - 1) / DEC_CHUNK);
+    a.chunks_l = 0;
+    a.c2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
+    char *w = reinterpret_cast<char *>(ws);
+    a.part = reinterpret_cast<float *>(w);
+    w += align256(decode_workspace_bytes(dims, stride_h, 0));
+    a.logit = reinterpret_cast<float *>(w);
+    w += align256((size_t)n_rows(dims) * G * a.chunks_h * DEC_CHUNK * sizeof(float));
+    a.lse2 = reinterpret_cast<float *>(w);
+    a.o = o;
+    a.lse = lse;
+    return decode_launch(dims, a, acc, as_stream(stream), "kvc_decode_attn_h2o");
+}
+
+
 
 extern "C" size_t kvc_decode_workspace_bytes(const kvc_dims *dims, int64_t max_h, int64_t stride_l) {
     if (check_dims(dims, "kvc_decode_workspace_bytes") != KVC_OK) return 0;

@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
     select_kernel(const float *__restrict__ scores, const uint8_t *__restrict__ tags,
                   const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int64_t T,
                   int L, int Hkv, int n_groups, int layer_base, int n_layers_model, int n_tags,
-                  int n_sink, int n_recent, int B, int32_t *__restrict__ kept, int kept_stride,
+                  int tag_rows, int n_sink, int n_recent, int B, int32_t *__restrict__ kept, int kept_stride,
                   int32_t *__restrict__ n_kept) {
     __shared__ float s_bonus[256];
     __shared__ uint8_t s_floor[256];
@@ -158,8 +158,8 @@ __global__ void __launch_bounds__(SEL_THREADS)
         s_floor[t] = (floor_tbl && t < n_tags) ? floor_tbl[t * n_groups + grp] : 0;
     }
     __syncthreads();
-    SelRow row{scores + (size_t)r * T, tags ? tags + (size_t)ri.n * T : nullptr, T, n_sink, n_recent, n_tags,
-               s_bonus, s_floor};
+    SelRow row{scores + (size_t)r * T, tags ? tags + (size_t)(tag_rows ? r : ri.n) * T : nullptr, T, n_sink,
+               n_recent, n_tags, s_bonus, s_floor};
     const int64_t step = (int64_t)SEL_THREADS * SEL_VEC;
     const int64_t trips = (T + step - 1) / step;
 
@@ -324,8 +324,8 @@ __device__ __forceinline__ void pick_bin(const uint32_t *hist, int nbins, uint32
 __global__ void __launch_bounds__(SEL_THREADS)
     select_cand(const float *__restrict__ scores, const uint8_t *__restrict__ tags,
                 const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int64_t T, int L, int Hkv,
-                int n_groups, int layer_base, int n_layers_model, int n_tags, int n_sink, int n_recent, int B,
-                int32_t *__restrict__ kept, int kept_stride, int32_t *__restrict__ n_kept) {
+                int n_groups, int layer_base, int n_layers_model, int n_tags, int tag_rows, int n_sink,
+                int n_recent, int B, int32_t *__restrict__ kept, int kept_stride, int32_t *__restrict__ n_kept) {
     __shared__ uint32_t hist[SEL_BINS];
     __shared__ uint32_t s_wave[SEL_WAVES + 1];
     __shared__ uint32_t s_wave2[SEL_WAVES + 1];
@@ -356,7 +356,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
     if (tid == 0) s_ncand = 0u;
     __syncthreads();
     const float *sr = scores + (size_t)r * T;
-    const uint8_t *tr = tags ? tags + (size_t)ri.n * T : nullptr;
+    const uint8_t *tr = tags ? tags + (size_t)(tag_rows ? r : ri.n) * T : nullptr;
     const int lo_prot = n_sink, hi_prot = Ti - n_recent;
     // Keys of n groups of four tokens: all table lookups first (no branches
     // between them), then the keys.
@@ -770,6 +770,7 @@ struct SplitArgs {
     const uint8_t *floor_tbl;
     int64_t T;
     int L, Hkv, n_groups, layer_base, n_layers_model, n_tags, n_sink, n_recent, B;
+    int tag_rows;
     int32_t *kept;
     int kept_stride;
     int32_t *n_kept;
@@ -785,8 +786,8 @@ __device__ __forceinline__ SelRow split_row_view(const SplitArgs &a, int64_t r, 
         s_floor[t] = (a.floor_tbl && t < a.n_tags) ? a.floor_tbl[t * a.n_groups + grp] : 0;
     }
     __syncthreads();
-    return SelRow{a.scores + (size_t)r * a.T, a.tags ? a.tags + (size_t)ri.n * a.T : nullptr, a.T, a.n_sink,
-                  a.n_recent, a.n_tags, s_bonus, s_floor};
+    return SelRow{a.scores + (size_t)r * a.T, a.tags ? a.tags + (size_t)(a.tag_rows ? r : ri.n) * a.T : nullptr,
+                  a.T, a.n_sink, a.n_recent, a.n_tags, s_bonus, s_floor};
 }
 
 __global__ void __launch_bounds__(SEL_THREADS) split_init(SplitWs w, int64_t rows) {
@@ -1038,7 +1039,8 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
     if (p->n_tags < 1 || p->n_tags > 256 || p->n_groups < 1 || p->n_tags * p->n_groups > 256 * 64)
         return fail(KVC_ERR_ARG, "kvc_select: table %d x %d out of range (tags 1..256)", p->n_tags,
                     p->n_groups);
-    if (p->reserved != 0) return fail(KVC_ERR_ARG, "kvc_select: reserved field must be 0");
+    if (p->tag_rows != 0 && p->tag_rows != 1)
+        return fail(KVC_ERR_ARG, "kvc_select: tag_rows must be 0 or 1 (got %d)", p->tag_rows);
     if (p->n_layers_model <= 0 || p->layer_base < 0 || p->layer_base + dims->n_layers > p->n_layers_model)
         return fail(KVC_ERR_ARG, "kvc_select: layers [%d, %d) outside a %d-layer model", p->layer_base,
                     p->layer_base + dims->n_layers, p->n_layers_model);
@@ -1058,8 +1060,8 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
         if (!ws || ws_bytes < need)
             return fail(KVC_ERR_WORKSPACE, "kvc_select: workspace %zu < %zu bytes (long rows)", ws_bytes, need);
         SplitArgs a{scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers, dims->n_kv_heads, p->n_groups,
-                    p->layer_base, p->n_layers_model, p->n_tags, p->n_sink, p->n_recent, p->budget, kept_idx,
-                    kept_stride, n_kept, (T + SPLIT_CHUNK - 1) / SPLIT_CHUNK};
+                    p->layer_base, p->n_layers_model, p->n_tags, p->n_sink, p->n_recent, p->budget, p->tag_rows,
+                    kept_idx, kept_stride, n_kept, (T + SPLIT_CHUNK - 1) / SPLIT_CHUNK};
         if ((st = launch_select_split(a, n_rows(dims), ws, vec, s)) != KVC_OK) return st;
     } else if (vec && cand_lds <= 144 * 1024) {
         static bool lds_set = false;
@@ -1071,18 +1073,18 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
         }
         select_cand<<<grid, block, cand_lds, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                   dims->n_kv_heads, p->n_groups, p->layer_base, p->n_layers_model,
-                                                  p->n_tags, p->n_sink, p->n_recent, p->budget, kept_idx,
-                                                  kept_stride, n_kept);
+                                                  p->n_tags, p->tag_rows, p->n_sink, p->n_recent, p->budget,
+                                                  kept_idx, kept_stride, n_kept);
     } else if (vec) {
         select_kernel<true><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                     dims->n_kv_heads, p->n_groups, p->layer_base,
-                                                    p->n_layers_model, p->n_tags, p->n_sink, p->n_recent,
-                                                    p->budget, kept_idx, kept_stride, n_kept);
+                                                    p->n_layers_model, p->n_tags, p->tag_rows, p->n_sink,
+                                                    p->n_recent, p->budget, kept_idx, kept_stride, n_kept);
     } else {
         select_kernel<false><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                      dims->n_kv_heads, p->n_groups, p->layer_base,
-                                                     p->n_layers_model, p->n_tags, p->n_sink, p->n_recent,
-                                                     p->budget, kept_idx, kept_stride, n_kept);
+                                                     p->n_layers_model, p->n_tags, p->tag_rows, p->n_sink,
+                                                     p->n_recent, p->budget, kept_idx, kept_stride, n_kept);
     }
     if ((st = check_launch("kvc_select")) != KVC_OK) return st;
     const int64_t sink_recent = (int64_t)p->n_sink + p->n_recent;

@@ -94,14 +94,15 @@ class Policy:
     n_groups: int = 1
     layer_base: int = 0
     n_layers_model: int = 1
-    tags: Optional[torch.Tensor] = None        # uint8 [N][T]
+    tags: Optional[torch.Tensor] = None        # uint8 [N][T] (or [N][L][Hkv][T], tag_rows=1)
     tag_bonus: Optional[torch.Tensor] = None   # float32 [n_tags][n_groups]
     tag_floor: Optional[torch.Tensor] = None   # uint8 [n_tags][n_groups]
+    tag_rows: int = 0                          # 1: tags are [N][L][Hkv][T], one per row
 
     def to_c(self):
         return _lib.KvcPolicy(
             self.n_sink, self.n_recent, self.budget, self.n_tags, self.n_groups, self.layer_base,
-            self.n_layers_model, 0, _ptr(self.tags, torch.uint8, "tags"),
+            self.n_layers_model, self.tag_rows, _ptr(self.tags, torch.uint8, "tags"),
             _ptr(self.tag_bonus, torch.float32, "tag_bonus"),
             _ptr(self.tag_floor, torch.uint8, "tag_floor"))
 
@@ -142,6 +143,10 @@ class CompactOut:
     p_ref: Optional[torch.Tensor] = None       # int32 positions of those references (< 0: none)
     K_ref_out: Optional[torch.Tensor] = None   # reference store of the kept slots
     p_ref_out: Optional[torch.Tensor] = None
+    score_in: Optional[torch.Tensor] = None    # fp32 per-slot running score carried with the tokens
+    score_out: Optional[torch.Tensor] = None
+    tag_in: Optional[torch.Tensor] = None      # uint8 per-slot tag carried with the tokens
+    tag_out: Optional[torch.Tensor] = None
 
     def to_c(self):
         return _lib.KvcCompactOut(
@@ -153,7 +158,9 @@ class CompactOut:
             _ptr(self.Ks, torch.int16, "Ks"), _ptr(self.Vs, torch.int16, "Vs"),
             _ptr(self.pos_q, torch.int32, "pos_q"), _ptr(self.n_l, torch.int32, "n_l"),
             _ptr(self.K_ref, torch.bfloat16, "K_ref"), _ptr(self.p_ref, torch.int32, "p_ref"),
-            _ptr(self.K_ref_out, torch.bfloat16, "K_ref_out"), _ptr(self.p_ref_out, torch.int32, "p_ref_out"))
+            _ptr(self.K_ref_out, torch.bfloat16, "K_ref_out"), _ptr(self.p_ref_out, torch.int32, "p_ref_out"),
+            _ptr(self.score_in, torch.float32, "score_in"), _ptr(self.score_out, torch.float32, "score_out"),
+            _ptr(self.tag_in, torch.uint8, "tag_in"), _ptr(self.tag_out, torch.uint8, "tag_out"))
 
 
 def kvc_compact_rerotate(dims, K, V, pos_in, kept_idx, kept_stride, n_kept, renumber_base, rope_base,
@@ -182,6 +189,19 @@ def kvc_decode_attn(dims, q, K, V, n_h, stride_h, o, ws, lse=None, block_table=N
         _ptr(Vs, torch.int16, "Vs"), _ptr(n_l, torch.int32, "n_l"), stride_l,
         _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    return _lib.check(st)
+
+
+def kvc_decode_h2o_workspace_bytes(dims, stride_h):
+    return _lib.load().kvc_decode_h2o_workspace_bytes(ctypes.byref(dims), stride_h)
+
+
+def kvc_decode_attn_h2o(dims, q, K, V, n_h, stride_h, acc, o, ws, lse=None, stream=None):
+    st = _lib.load().kvc_decode_attn_h2o(
+        ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"), _ptr(K, torch.bfloat16, "K"),
+        _ptr(V, torch.bfloat16, "V"), _ptr(n_h, torch.int32, "n_h"), stride_h,
+        _ptr(acc, torch.float32, "acc"), _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"),
+        _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     return _lib.check(st)
 
 

@@ -193,3 +193,65 @@ def run_commit(w, inp, taus, timer=None):
     return dict(Rm=Rm, Rp=Rp, states=np.stack(states), order=np.stack(orders), n_order=np.array(n_orders),
                 retire=retire, scores=scores, pscore=pscore, kept=kept, n_kept=nk, Ko=Ko, Vo=Vo, pos=po, n_h=nh,
                 o1=o1, o2=o2, lse1=lse1, lse2=lse2)
+
+
+def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
+    """PACE-style decode with H2O eviction over a resident cache of B + E
+    slots per row: each cycle the engine appends E new tokens (score 0, no
+    tag, no reference), E decode steps add their attention to the slots'
+    cumulative scores, then the rows are evicted back to B slots by cumulative
+    score + foresight bonus (per-slot tags) and compacted with positions kept;
+    scores, tags and the reference store move with the slots. Two slot pools
+    alternate. With `record`, returns per cycle the scores before eviction and
+    the kept lists, plus the final pool."""
+    t = timer or _null_timer
+    N, L, Hkv, Hq, d = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
+    rows, S, B, E = w.rows, w.slots, w.budget, w.interval
+    dev = inp.K.device
+    dims = kvc.make_dims(N, L, Hkv, Hq, d, S)
+
+    def pool():
+        return dict(K=torch.empty((rows, S, d), dtype=torch.bfloat16, device=dev), V=torch.empty((rows, S, d),
+                    dtype=torch.bfloat16, device=dev), pos=torch.empty((rows, S), dtype=torch.int32, device=dev),
+                    acc=torch.empty((rows, S), dtype=torch.float32, device=dev),
+                    tags=torch.empty((rows, S), dtype=torch.uint8, device=dev),
+                    Kr=torch.zeros((rows, S, d), dtype=torch.bfloat16, device=dev),
+                    pr=torch.full((rows, S), -1, dtype=torch.int32, device=dev))
+    cur, nxt = pool(), pool()
+    for k, src in (("K", inp.K), ("V", inp.V), ("pos", inp.pos), ("acc", inp.acc), ("tags", inp.tags)):
+        cur[k].copy_(src)
+    vals = [0.0] + [kvc.kvc_foresight_bonus(sigma, lam, s) for s in inp.steps_ahead]
+    bonus = torch.tensor(vals, dtype=torch.float32, device=dev).reshape(-1, 1)
+    nh = [torch.full((rows,), B + e + 1, dtype=torch.int32, device=dev) for e in range(E)]
+    new_pos = int(inp.pos[:, B:].min().item())
+    ar = torch.arange(E, dtype=torch.int32, device=dev)
+    o = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, kvc.kvc_decode_h2o_workspace_bytes(dims, S)), dtype=torch.uint8, device=dev)
+    kept = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
+    nk = torch.zeros(rows, dtype=torch.int32, device=dev)
+    rec = []
+    for c in range(cycles):
+        with t("append"):
+            cur["K"][:, B:] = inp.K_new[c]
+            cur["V"][:, B:] = inp.V_new[c]
+            cur["pos"][:, B:] = new_pos + c * E + ar
+            cur["acc"][:, B:] = 0.0
+            cur["tags"][:, B:] = 0
+            cur["pr"][:, B:] = -1
+        for e in range(E):
+            with t("kvc_decode_attn_h2o"):
+                kvc.kvc_decode_attn_h2o(dims, inp.q[c, e], cur["K"], cur["V"], nh[e], S, cur["acc"], o, ws)
+        if record:
+            rec.append({"acc": cur["acc"].clone(), "pos": cur["pos"].clone(), "tags": cur["tags"].clone()})
+        pol = kvc.Policy(w.n_sink, w.n_recent, B, len(vals), 1, 0, L, cur["tags"], bonus, None, tag_rows=1)
+        with t("kvc_select"):
+            kvc.kvc_select(dims, cur["acc"], pol, kept, B, nk)
+        out = kvc.CompactOut(S, nxt["K"], nxt["V"], nxt["pos"], None, K_ref=cur["Kr"], p_ref=cur["pr"],
+                             K_ref_out=nxt["Kr"], p_ref_out=nxt["pr"], score_in=cur["acc"],
+                             score_out=nxt["acc"], tag_in=cur["tags"], tag_out=nxt["tags"])
+        with t("kvc_compact_rerotate"):
+            kvc.kvc_compact_rerotate(dims, cur["K"], cur["V"], cur["pos"], kept, B, nk, -1, w.rope_base, out)
+        if record:
+            rec[-1].update(kept=kept.clone(), n_kept=nk.clone())
+        cur, nxt = nxt, cur
+    return {"cycles": rec, "final": cur, "o": o}

@@ -437,3 +437,91 @@ def make_commit_inputs(w: CommitWorkload, device="cpu") -> CommitInputs:
     Qm = (Qm.float() + cq).to(torch.bfloat16)
     Qp = (Qp.float() - cq).to(torch.bfloat16)
     return CommitInputs(w, K, V, Qm, Qp, qd, planted)
+
+
+# ---------------------------------------------------------------- PACE-style H2O decode with eviction
+
+@dataclass(frozen=True)
+class H2OWorkload:
+    """A resident cache of B + E slots per (layer, KV head) in decode: every
+    cycle decodes E tokens (each step's query attends to the resident slots
+    and the new tokens so far, adding its attention to the slots' cumulative
+    scores), then evicts back to B slots by cumulative score plus the
+    foresight bonus of the slot's span tag."""
+    name: str = "pace_h2o_decode"
+    n_seq: int = 1
+    n_layers: int = 36
+    n_kv_heads: int = 8
+    n_q_heads: int = 32
+    head_dim: int = 128
+    budget: int = 2048
+    interval: int = 32           # E: decoded tokens between evictions
+    n_sink: int = 4
+    n_recent: int = 128
+    n_spans: int = 8             # tagged span groups among the resident slots
+    span_slots: int = 24         # slots per tagged group per row
+    key_sigma: float = 0.5       # per-slot key scale ~ lognormal(0, key_sigma): uneven attention
+    rope_base: float = 1e6
+    seed: int = 20261206
+
+    @property
+    def rows(self):
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+    @property
+    def group(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def slots(self):
+        return self.budget + self.interval
+
+
+H2O_WORKLOADS = {
+    "pace_h2o_decode": H2OWorkload(),
+    "h2o_small": H2OWorkload("h2o_small", n_layers=2, n_kv_heads=2, n_q_heads=8, head_dim=64, budget=96,
+                             interval=8, n_recent=8, n_spans=3, span_slots=6, seed=20261216),
+}
+
+
+@dataclass
+class H2OInputs:
+    w: H2OWorkload
+    K: torch.Tensor        # bf16 [rows][B + E][d] resident keys (slots >= B: this cycle's new tokens)
+    V: torch.Tensor
+    pos: torch.Tensor      # int32 [rows][B + E] physical positions
+    acc: torch.Tensor      # fp32 [rows][B + E] cumulative scores of the resident slots (new: 0)
+    tags: torch.Tensor     # uint8 [rows][B + E] span tag per slot (0: none)
+    q: torch.Tensor        # bf16 [cycles][E][N][L][Hq][d] decode queries
+    K_new: torch.Tensor    # bf16 [cycles][rows][E][d] keys of the tokens decoded in each cycle
+    V_new: torch.Tensor
+    steps_ahead: tuple     # per tag 1..n_spans: steps until its next planned reader
+
+
+def make_h2o_inputs(w: H2OWorkload, cycles, device="cpu") -> H2OInputs:
+    rows, S, d, B, E = w.rows, w.slots, w.head_dim, w.budget, w.interval
+    s = w.seed * 16
+    g = _gen(s + 7, torch.device(device))
+    scale = torch.exp(w.key_sigma * torch.randn((rows, S, 1), generator=g, device=device))
+    K = (normal_bf16((rows, S, d), s + 1, device).float() * scale).to(torch.bfloat16)
+    V = normal_bf16((rows, S, d), s + 2, device)
+    q = normal_bf16((cycles, E, w.n_seq, w.n_layers, w.n_q_heads, d), s + 3, device)
+    gn = _gen(s + 8, torch.device(device))
+    sn = torch.exp(w.key_sigma * torch.randn((cycles, rows, E, 1), generator=gn, device=device))
+    K_new = (normal_bf16((cycles, rows, E, d), s + 4, device).float() * sn).to(torch.bfloat16)
+    V_new = normal_bf16((cycles, rows, E, d), s + 5, device)
+    rng = np.random.default_rng(w.seed + 37)
+    pos = np.stack([np.sort(rng.choice(8 * S, B, replace=False)) for _ in range(rows)]) + 16
+    pos = np.concatenate([pos, np.tile(np.arange(8 * S + 16, 8 * S + 16 + E), (rows, 1))], axis=1)
+    acc = rng.gamma(0.5, 4.0, (rows, S))
+    acc[:, B:] = 0.0
+    tags = np.zeros((rows, S), np.uint8)
+    lo, hi = w.n_sink, B - w.n_recent
+    for r in range(rows):
+        slots = rng.choice(np.arange(lo, hi), w.n_spans * w.span_slots, replace=False)
+        for k in range(w.n_spans):
+            tags[r, slots[k * w.span_slots:(k + 1) * w.span_slots]] = k + 1
+    steps = tuple(int(x) for x in rng.integers(0, 12, w.n_spans))
+    return H2OInputs(w, K, V, torch.from_numpy(pos.astype(np.int32)).to(device),
+                     torch.from_numpy(acc.astype(np.float32)).to(device), torch.from_numpy(tags).to(device),
+                     q, K_new, V_new, steps)

@@ -103,8 +103,10 @@ typedef struct kvc_policy {
     int32_t n_groups;           /* columns of the tables (>= 1) */
     int32_t layer_base;         /* model index of the first layer in this call */
     int32_t n_layers_model;     /* model depth used for the group rule */
-    int32_t reserved;           /* must be 0 */
-    const uint8_t *tags;        /* device u8 [N][T] tag per token, or NULL (all tag 0) */
+    int32_t tag_rows;           /* 0: tags [N][T], shared by a sequence's rows; 1: tags
+                                   [N][L][Hkv][T], one per row (a resident cache whose slots
+                                   hold different tokens in different rows) */
+    const uint8_t *tags;        /* device u8 tag per token (layout by tag_rows), or NULL (all tag 0) */
     const float *tag_bonus;     /* device fp32 [n_tags][n_groups], or NULL (no bonus) */
     const uint8_t *tag_floor;   /* device u8 [n_tags][n_groups] 1 = protected, or NULL */
 } kvc_policy;
@@ -199,6 +201,15 @@ typedef struct kvc_compact_out {
     const int32_t *p_ref;     /* int32 [N][L][Hkv][T], < 0 = no reference */
     uint16_t *K_ref_out;      /* bf16 [N][L][Hkv][out_stride][d], or NULL */
     int32_t *p_ref_out;       /* int32 [N][L][Hkv][out_stride], with K_ref_out */
+    /* Per-slot payloads that move with the kept tokens, in rank order like
+     * K_out (plain path only, else KVC_ERR_UNSUPPORTED): a running score, such
+     * as H2O's cumulative attention that PACE §3.1 adds the bonus to, and the
+     * slot's tag for per-row policies (kvc_policy.tag_rows = 1). In and out
+     * go together; NULL = not carried. */
+    const float *score_in;    /* fp32 [N][L][Hkv][T] */
+    float *score_out;         /* fp32 [N][L][Hkv][out_stride] */
+    const uint8_t *tag_in;    /* u8 [N][L][Hkv][T] */
+    uint8_t *tag_out;         /* u8 [N][L][Hkv][out_stride] */
 } kvc_compact_out;
 
 /*
@@ -266,6 +277,32 @@ int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const uint16_t *K, 
                     int32_t page_size, int32_t blocks_per_seq, const int8_t *Kq, const int8_t *Vq,
                     const uint16_t *Ks, const uint16_t *Vs, const int32_t *n_l, int64_t stride_l,
                     uint16_t *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* Device workspace (bytes) kvc_decode_attn_h2o needs for a pool of stride_h
+ * tokens per row. */
+size_t kvc_decode_h2o_workspace_bytes(const kvc_dims *dims, int64_t stride_h);
+
+/*
+ * Decode attention with H2O cumulative attention (PACE §2 background: H2O
+ * keeps the tokens with the largest attention received; PACE §3.1: the
+ * foresight bonus is added to that cumulative score).
+ *
+ * The same attention as kvc_decode_attn over one unpaged bf16 pool, and for
+ * every row r and cached token t < n_h[r]:
+ *   acc[r][t] += sum over the row's G query heads g of softmax_t(q_g . k_t / sqrt(d))
+ * (each call adds exactly G to a non-empty row). acc is read and written in
+ * place; the caller sets the score of a newly cached token to 0 before the
+ * step whose query attends to it. Softmax weights are formed in fp32 from the
+ * merged normaliser; the running sum is fp32.
+ *
+ *   q, K, V, n_h, stride_h, o, lse  as kvc_decode_attn
+ *   acc   fp32 [N][L][Hkv][stride_h]
+ *   ws    kvc_decode_h2o_workspace_bytes(dims, stride_h) bytes
+ * Supported: d in {64, 128}, G <= 16.
+ */
+int kvc_decode_attn_h2o(const kvc_dims *dims, const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                        const int32_t *n_h, int64_t stride_h, float *acc, uint16_t *o, float *lse,
+                        void *ws, size_t ws_bytes, void *stream);
 
 /* Device workspace (bytes) of kvc_page_effect / kvc_page_retire for a window
  * of W queries starting at position q_first. */

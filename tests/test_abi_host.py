@@ -209,3 +209,37 @@ def test_compact_reference_store_rejects_bad_combinations():
     out.action = FAKE
     out.Kq = out.Vq = out.Ks = out.Vs = FAKE
     assert call() == _lib.KVC_ERR_UNSUPPORTED
+
+
+def test_select_rejects_bad_tag_layout_and_decode_h2o_arguments():
+    lib = _lib.load()
+    d = _dims()
+    p = _policy()
+    p.tag_rows = 2
+    assert lib.kvc_select(ctypes.byref(d), FAKE, ctypes.byref(p), FAKE, 512, FAKE, None, 0, None) == _lib.KVC_ERR_ARG
+    ws = lib.kvc_decode_h2o_workspace_bytes(ctypes.byref(d), 512)
+    assert ws > lib.kvc_decode_workspace_bytes(ctypes.byref(d), 512, 0)
+    call = lambda **k: lib.kvc_decode_attn_h2o(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, k.get("stride", 512),
+                                               k.get("acc", FAKE), FAKE, None, FAKE, k.get("ws", ws), None)
+    assert call(acc=None) == _lib.KVC_ERR_ARG
+    assert call(stride=0) == _lib.KVC_ERR_ARG
+    assert call(ws=ws - 1) == _lib.KVC_ERR_WORKSPACE
+
+
+def test_compact_carry_rejects_half_pairs_and_tiered_path():
+    lib = _lib.load()
+    d = _dims()
+    out = _lib.KvcCompactOut()
+    out.out_stride = 512
+    out.K_out = out.V_out = FAKE
+    call = lambda: lib.kvc_compact_rerotate(ctypes.byref(d), FAKE, FAKE, None, FAKE, 512, FAKE, -1, 1e4,
+                                            ctypes.byref(out), None)
+    out.score_in = FAKE
+    assert call() == _lib.KVC_ERR_ARG                            # score_out missing
+    out.score_out = FAKE
+    out.tag_out = FAKE
+    assert call() == _lib.KVC_ERR_ARG                            # tag_in missing
+    out.tag_in = FAKE
+    out.action = FAKE
+    out.Kq = out.Vq = out.Ks = out.Vs = FAKE
+    assert call() == _lib.KVC_ERR_UNSUPPORTED

@@ -152,3 +152,33 @@ def test_split_path_floors_beyond_budget_and_short_kept_list():
     st, kept, n_kept = _run_select(small, None, np.zeros((1, 1)), None, 4, 16, 50_000, kept_stride=50_000)
     assert np.all(n_kept == 40_000)
     np.testing.assert_array_equal(kept[:, :40_000], np.tile(np.arange(40_000, dtype=np.int32), (3, 1)))
+
+
+@pytest.mark.parametrize("T,rows", [(4097, 3), (40_000, 3), (5000, 128)])
+def test_per_row_tags(T, rows):
+    """tag_rows = 1: every row reads its own tag array (a resident cache whose
+    slots hold different tokens per row), on the one-workgroup, candidate and
+    split paths."""
+    from budgeted_retention_amd import kvc
+    rng = np.random.default_rng(T + rows)
+    B = 700
+    scores = rng.random((rows, T)).astype(np.float32)
+    tags = rng.integers(0, 3, (rows, T)).astype(np.uint8)
+    for r in range(rows):                                   # a protected span at a different place per row
+        s0 = int(rng.integers(100, T - 400))
+        tags[r, s0:s0 + 300] = 3
+    bonus = np.array([[0.0], [0.5], [-0.25], [0.0]])
+    floor = np.array([[0], [0], [0], [1]], np.uint8)
+    dims = kvc.make_dims(1, 1, rows, rows, 64, T)
+    dev = torch.device("cuda")
+    pol = kvc.Policy(4, 16, B, 4, 1, 0, 1, torch.from_numpy(tags).to(dev),
+                     torch.from_numpy(bonus.astype(np.float32)).to(dev), torch.from_numpy(floor).to(dev), tag_rows=1)
+    kept = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
+    n_kept = torch.zeros(rows, dtype=torch.int32, device=dev)
+    kvc.kvc_select(dims, torch.from_numpy(scores).to(dev), pol, kept, B, n_kept)
+    torch.cuda.synchronize()
+    kept, n_kept = kept.cpu().numpy(), n_kept.cpu().numpy()
+    for r in sorted({0, 1, rows - 1}):
+        ref = _oracle(scores[r], tags[r], bonus, floor, 4, 16, B)
+        assert n_kept[r] == ref.size
+        np.testing.assert_array_equal(kept[r][: ref.size], ref.astype(np.int32))
