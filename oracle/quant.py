@@ -10,6 +10,11 @@ value = code * scale. The int8 tier here is the same rule with 7 -> 127.
 Readings where the page is silent: "smallest positive representable value"
 is the smallest FP16 subnormal, 2**-24; "rounded to the nearest integer"
 breaks ties to even.
+
+INT4 storage (PASK Appendix B.5): two signed nibbles per byte, an odd
+dimension padded with a zero code. Read here as: dimension 2i in the low
+nibble and 2i+1 in the high nibble of byte i, each nibble the code's 4-bit
+two's complement.
 """
 import numpy as np
 
@@ -43,3 +48,21 @@ def quantize_rows(X, qmax=127):
 
 def dequantize_rows(codes, scale_bits):
     return np.asarray(codes, np.float64) * numfmt.fp16_bits_to_f64(scale_bits)[:, None]
+
+
+def pack_nibbles(codes):
+    """codes: [..., d] ints in [-8, 7] -> uint8 [..., ceil(d/2)] (zero-padded)."""
+    c = np.asarray(codes, np.int64)
+    if c.shape[-1] % 2:
+        c = np.concatenate([c, np.zeros(c.shape[:-1] + (1,), np.int64)], axis=-1)
+    lo = c[..., 0::2] & 0xF
+    hi = c[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed, d):
+    """uint8 [..., ceil(d/2)] -> int8 codes [..., d]."""
+    b = np.asarray(packed, np.int64)
+    nib = np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    nib = np.where(nib >= 8, nib - 16, nib)
+    return nib[..., :d].astype(np.int8)

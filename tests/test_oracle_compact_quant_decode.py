@@ -218,3 +218,34 @@ def test_reference_store_first_renumber_and_checks():
     K4, _, p4, R4, q4 = compact.compact_row_ref(K1, V1, p1, kept2, -1, base, R1, q1)
     np.testing.assert_array_equal(K4, K1[kept2])
     np.testing.assert_array_equal(R4, R1[kept2])
+
+
+def test_int4_rule_on_a_hand_worked_row_pask_b5():
+    # PASK Appendix B.5 with 7: amax 0.7 -> scale fp16(0.1) = 0.0999755859375;
+    # 0.7/s = 7.0017 -> 7, -0.35/s = -3.5009 -> -4, 0 -> 0, 0.1/s = 1.0002 -> 1,
+    # -0.7/s -> -7; packed low nibble first: (7, -4) -> 0xC7, (0, 1) -> 0x10,
+    # (-7, pad 0) -> 0x09.
+    x = np.array([0.7, -0.35, 0.0, 0.1, -0.7])
+    codes, s_bits = quant.quantize_row(x, qmax=7)
+    assert numfmt.fp16_bits_to_f64(s_bits) == 0.0999755859375
+    np.testing.assert_array_equal(codes, [7, -4, 0, 1, -7])
+    packed = quant.pack_nibbles(codes)
+    np.testing.assert_array_equal(packed, np.array([0xC7, 0x10, 0x09], np.uint8))
+    np.testing.assert_array_equal(quant.unpack_nibbles(packed, 5), codes)
+    # zero row: zero codes, unit scale
+    c0, s0 = quant.quantize_row(np.zeros(6), qmax=7)
+    assert s0 == 0x3C00 and not c0.any() and not quant.pack_nibbles(c0).any()
+
+
+def test_int4_round_trip_and_bounds():
+    rng = np.random.default_rng(7)
+    X = numfmt.bf16_bits_to_f64(numfmt.f64_to_bf16_bits(rng.standard_normal((200, 128)) * 3))
+    codes, scales = quant.quantize_rows(X, qmax=7)
+    assert codes.min() >= -7 and codes.max() <= 7
+    s = numfmt.fp16_bits_to_f64(scales)
+    err = np.abs(quant.dequantize_rows(codes, scales) - X)
+    assert np.all(err <= s[:, None] * 0.5 + np.abs(X).max(axis=1, keepdims=True) * 2.0 ** -10)
+    assert np.all(np.abs(codes).max(axis=1) == 7)                  # the row maximum maps to +-7
+    allc = np.arange(-8, 8)
+    np.testing.assert_array_equal(quant.unpack_nibbles(quant.pack_nibbles(np.tile(allc, (3, 1))), 16),
+                                  np.tile(allc, (3, 1)))
