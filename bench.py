@@ -14,6 +14,7 @@ Other workloads (parity cases, measured the same way call by call):
   tiny            1 layer, T=4096, B=512, renumbered
   qwen3_8b_1m     T=1,048,576, one layer per call (154.6 GB of K+V resident)
   pask_llama3_8b  64 x 32 layers: prompt compaction, int8/bf16/release tiers, decode
+  pask_llama3_8b_int4  the same with the pages' INT4 low tier (two nibbles per byte)
   commitkv_28l    16 x 28 layers: page effects, retirement, checkpoint, paged decode
   pace_h2o_decode 36 layers x 8 KV heads of 2048 + 32 resident slots: one step is one
                   eviction cycle (32 decode steps adding H2O cumulative attention,
@@ -336,9 +337,9 @@ def bench_pipeline(args, w, dev, kind):
               # every generated token's K, V, action, index and position read; the bf16
               # tier written with positions, the int8 tier as codes, fp16 scales, positions
               "kvc_compact_rerotate:tiered": rows * Tg * (2 * d * 2 + 1 + 4 + 4) + n_hg * (2 * d * 2 + 4)
-                                             + n_l * (2 * d + 2 * 2 + 4),
+                                             + n_l * (2 * d * w.low_bits // 8 + 2 * 2 + 4),
               # both pools read once, queries read and outputs written
-              "kvc_decode_attn": n_h * 2 * d * 2 + n_l * (2 * d + 2 * 2)
+              "kvc_decode_attn": n_h * 2 * d * 2 + n_l * (2 * d * w.low_bits // 8 + 2 * 2)
                                  + w.n_seq * w.n_layers * w.n_q_heads * d * 2 * 2}
         path_calls = ["kvc_score", "kvc_select", "kvc_compact_rerotate:prompt", "kvc_compact_rerotate:tiered"]
     else:
@@ -381,7 +382,7 @@ def bench_pipeline(args, w, dev, kind):
     if kind == "pask":
         config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "layer_groups": w.n_groups,
                   "kv_heads": Hkv, "q_heads": w.n_q_heads, "head_dim": d, "prompt": w.n_prompt,
-                  "generated": w.n_gen, "window": W, "budget": w.budget, "byte_budget": w.budget_fraction,
+                  "generated": w.n_gen, "window": W, "budget": w.budget, "byte_budget": w.budget_fraction, "low_bits": w.low_bits,
                   "parallelism": "none"}
     else:
         config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "kv_heads": Hkv,

@@ -49,6 +49,7 @@ class KvcCompactOut(ctypes.Structure):
         ("pos_q", c_void_p), ("n_l", c_void_p),
         ("K_ref", c_void_p), ("p_ref", c_void_p), ("K_ref_out", c_void_p), ("p_ref_out", c_void_p),
         ("score_in", c_void_p), ("score_out", c_void_p), ("tag_in", c_void_p), ("tag_out", c_void_p),
+        ("low_bits", c_int32),
     ]
 
 
@@ -74,7 +75,7 @@ PROTOTYPES = {
     "kvc_decode_workspace_bytes": (c_size_t, [ctypes.POINTER(KvcDims), c_int64, c_int64]),
     "kvc_decode_attn": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_int64, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
-                                       c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
     "kvc_decode_h2o_workspace_bytes": (c_size_t, [ctypes.POINTER(KvcDims), c_int64]),
     "kvc_decode_attn_h2o": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_void_p, c_void_p,

@@ -84,17 +84,23 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
-__device__ __forceinline__ int8_t quant_code(float x, float s) {
+// Code of x under scale s: round to nearest even, clamp to [-qmax, qmax].
+__device__ __forceinline__ int8_t quant_code(float x, float s, float qmax) {
     float q = rintf(__fdiv_rn(x, s));
-    q = fminf(fmaxf(q, -127.f), 127.f);
+    q = fminf(fmaxf(q, -qmax), qmax);
     return (int8_t)(int)q;
 }
 
-// Scale bits for a row whose max |x| is amax: max(fp16(amax/127), 2^-24); zero row -> 1.0.
-__device__ __forceinline__ uint16_t int8_scale_bits(float amax) {
+// Scale bits for a row whose max |x| is amax: max(fp16(amax/qmax), 2^-24); zero row -> 1.0.
+__device__ __forceinline__ uint16_t low_scale_bits(float amax, double qmax) {
     if (!(amax > 0.f)) return 0x3C00;
-    uint16_t b = f64_to_f16_rne((double)amax / 127.0);
+    uint16_t b = f64_to_f16_rne((double)amax / qmax);
     return b == 0 ? (uint16_t)1 : b;
+}
+
+// Two codes as one byte: the first in the low nibble (4-bit two's complement).
+__device__ __forceinline__ uint32_t nibble_pair(int8_t c0, int8_t c1) {
+    return ((uint32_t)c0 & 0xFu) | (((uint32_t)c1 & 0xFu) << 4);
 }
 
 struct CompactArgs {
@@ -109,6 +115,7 @@ struct CompactArgs {
     int8_t *Kq, *Vq;
     uint16_t *Ks, *Vs;
     int32_t *pq, *nl;
+    int low_bits;             // 8: int8 codes; 4: INT4 nibble pairs
     const int32_t *h_base, *l_base;
     const uint16_t *Kref;     // reference store of the current slots, or NULL
     const int32_t *pref;
@@ -389,18 +396,34 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
                 const float v2 = bf16_to_f32((uint16_t)(vv.y & 0xFFFF)), v3 = bf16_to_f32((uint16_t)(vv.y >> 16));
                 const float kmax = group_max<TPT>(fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3))));
                 const float vmax = group_max<TPT>(fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3))));
-                const uint16_t ksb = int8_scale_bits(kmax), vsb = int8_scale_bits(vmax);
+                const bool q4 = a.low_bits == 4;
+                const float qm = q4 ? 7.f : 127.f;
+                const uint16_t ksb = low_scale_bits(kmax, qm), vsb = low_scale_bits(vmax, qm);
                 const float ks = f16_to_f32(ksb), vs = f16_to_f32(vsb);
-                int8_t *kq = a.Kq + dst;
-                int8_t *vq = a.Vq + dst;
-                const uint16_t klo = (uint16_t)(uint8_t)quant_code(k0, ks) | ((uint16_t)(uint8_t)quant_code(k1, ks) << 8);
-                const uint16_t khi = (uint16_t)(uint8_t)quant_code(k2, ks) | ((uint16_t)(uint8_t)quant_code(k3, ks) << 8);
-                *reinterpret_cast<uint16_t *>(kq + 2 * sub) = klo;
-                *reinterpret_cast<uint16_t *>(kq + D / 2 + 2 * sub) = khi;
-                const uint32_t vc = (uint32_t)(uint8_t)quant_code(v0, vs) | ((uint32_t)(uint8_t)quant_code(v1, vs) << 8) |
-                                    ((uint32_t)(uint8_t)quant_code(v2, vs) << 16) |
-                                    ((uint32_t)(uint8_t)quant_code(v3, vs) << 24);
-                *reinterpret_cast<uint32_t *>(vq + 4 * sub) = vc;
+                const int8_t c0 = quant_code(k0, ks, qm), c1 = quant_code(k1, ks, qm);
+                const int8_t c2 = quant_code(k2, ks, qm), c3 = quant_code(k3, ks, qm);
+                const int8_t w0 = quant_code(v0, vs, qm), w1 = quant_code(v1, vs, qm);
+                const int8_t w2 = quant_code(v2, vs, qm), w3 = quant_code(v3, vs, qm);
+                if (q4) {
+                    // dimensions 2sub, 2sub+1 -> byte sub; D/2+2sub, +1 -> byte D/4+sub;
+                    // values 4sub..4sub+3 -> bytes 2sub, 2sub+1
+                    const size_t dq = ((size_t)r * a.out_stride + sl) * (D / 2);
+                    uint8_t *kq = reinterpret_cast<uint8_t *>(a.Kq) + dq;
+                    uint8_t *vq = reinterpret_cast<uint8_t *>(a.Vq) + dq;
+                    kq[sub] = (uint8_t)nibble_pair(c0, c1);
+                    kq[D / 4 + sub] = (uint8_t)nibble_pair(c2, c3);
+                    *reinterpret_cast<uint16_t *>(vq + 2 * sub) =
+                        (uint16_t)(nibble_pair(w0, w1) | (nibble_pair(w2, w3) << 8));
+                } else {
+                    int8_t *kq = a.Kq + dst;
+                    int8_t *vq = a.Vq + dst;
+                    *reinterpret_cast<uint16_t *>(kq + 2 * sub) = (uint16_t)((uint8_t)c0 | ((uint32_t)(uint8_t)c1 << 8));
+                    *reinterpret_cast<uint16_t *>(kq + D / 2 + 2 * sub) =
+                        (uint16_t)((uint8_t)c2 | ((uint32_t)(uint8_t)c3 << 8));
+                    *reinterpret_cast<uint32_t *>(vq + 4 * sub) = (uint32_t)(uint8_t)w0 | ((uint32_t)(uint8_t)w1 << 8) |
+                                                                 ((uint32_t)(uint8_t)w2 << 16) |
+                                                                 ((uint32_t)(uint8_t)w3 << 24);
+                }
                 if (sub == 0) {
                     a.Ks[(size_t)r * a.out_stride + sl] = ksb;
                     a.Vs[(size_t)r * a.out_stride + sl] = vsb;
@@ -443,6 +466,8 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
         (int64_t)renumber_base + (int64_t)kept_stride * (out->kept_page > 0 ? out->kept_page : 1) >
             (int64_t)INT32_MAX)
         return fail(KVC_ERR_ARG, "kvc_compact_rerotate: renumbered positions overflow int32");
+    if (out->low_bits != 0 && out->low_bits != 8 && out->low_bits != 4)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_compact_rerotate: low_bits %d (0, 8 or 4)", out->low_bits);
     if (out->action) {
         if (!out->Kq || !out->Vq || !out->Ks || !out->Vs || !out->K_out || !out->V_out)
             return fail(KVC_ERR_ARG, "kvc_compact_rerotate: tiered output needs bf16 and int8 pools");
@@ -489,6 +514,7 @@ extern "C" int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, con
     a.Vs = out->Vs;
     a.pq = out->pos_q;
     a.nl = out->n_l;
+    a.low_bits = out->low_bits == 4 ? 4 : 8;
     a.h_base = out->h_base;
     a.l_base = out->l_base;
     a.Kref = out->K_ref;

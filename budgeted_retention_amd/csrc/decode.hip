@@ -36,10 +36,11 @@ struct DecodeArgs {
     int64_t stride_h;
     const int32_t *block_table;
     int32_t page_size, blocks_per_seq;
-    const int8_t *Kq, *Vq;
+    const int8_t *Kq, *Vq;    // int8 codes, or INT4 nibble pairs (low_bits 4)
     const uint16_t *Ks, *Vs;
     const int32_t *n_l;
     int64_t stride_l;
+    int low_bits;             // 8 or 4
     int L, Hkv, Hq, G;
     int chunks_h, chunks_l;  // chunk slots per row for each partition
     float c2;                // log2(e) / sqrt(d)
@@ -88,8 +89,12 @@ __device__ __forceinline__ int64_t bf16_slot(const DecodeArgs &a, int n, int t) 
 // three barriers for all heads together.
 static_assert(DEC_CHUNK == DEC_THREADS, "the statistics map one thread to one key");
 
-template <int D, int GM, bool LOW>
+// LOWB: 0 = the bf16 partition, 8 = int8 codes, 4 = INT4 codes (two signed
+// nibbles per byte, dimension 2i in the low nibble of byte i).
+template <int D, int GM, int LOWB>
 __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
+    constexpr bool LOW = LOWB != 0;
+    constexpr int CB = LOWB == 4 ? D / 2 : D;   // code bytes per low-precision row
     constexpr int TPK = D / 8;                  // threads per key
     constexpr int KPI = DEC_THREADS / TPK;      // keys per pass over the block
     constexpr int ITER = DEC_CHUNK / KPI;       // passes per chunk
@@ -143,8 +148,12 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         if (srow[it] < 0) continue;
         if (!low) {
             kv[it] = *reinterpret_cast<const uint4 *>(a.K + ((size_t)r * a.stride_h + srow[it]) * D + 8 * sub);
+        } else if (LOWB == 4) {
+            const uint32_t c = *reinterpret_cast<const uint32_t *>(a.Kq + ((size_t)r * a.stride_l + srow[it]) * CB + 4 * sub);
+            kv[it] = make_uint4(c, 0, 0, 0);
+            ks[LOW ? it : 0] = half_bits_to_f32(a.Ks[(size_t)r * a.stride_l + srow[it]]);
         } else {
-            const uint2 c = *reinterpret_cast<const uint2 *>(a.Kq + ((size_t)r * a.stride_l + srow[it]) * D + 8 * sub);
+            const uint2 c = *reinterpret_cast<const uint2 *>(a.Kq + ((size_t)r * a.stride_l + srow[it]) * CB + 8 * sub);
             kv[it] = make_uint4(c.x, c.y, 0, 0);
             ks[LOW ? it : 0] = half_bits_to_f32(a.Ks[(size_t)r * a.stride_l + srow[it]]);
         }
@@ -168,6 +177,9 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
                 x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xFFFF));
                 x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
             }
+        } else if (LOWB == 4) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)((int32_t)(kv[it].x << (28 - 4 * e)) >> 28) * ks[LOW ? it : 0];
         } else {
             const uint32_t w[2] = {kv[it].x, kv[it].y};
 #pragma unroll
@@ -201,8 +213,12 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         if (srow[it] < 0) continue;
         if (!low) {
             vv[it] = *reinterpret_cast<const uint4 *>(a.V + ((size_t)r * a.stride_h + srow[it]) * D + 8 * sub);
+        } else if (LOWB == 4) {
+            const uint32_t c = *reinterpret_cast<const uint32_t *>(a.Vq + ((size_t)r * a.stride_l + srow[it]) * CB + 4 * sub);
+            vv[it] = make_uint4(c, 0, 0, 0);
+            vs[LOW ? it : 0] = half_bits_to_f32(a.Vs[(size_t)r * a.stride_l + srow[it]]);
         } else {
-            const uint2 c = *reinterpret_cast<const uint2 *>(a.Vq + ((size_t)r * a.stride_l + srow[it]) * D + 8 * sub);
+            const uint2 c = *reinterpret_cast<const uint2 *>(a.Vq + ((size_t)r * a.stride_l + srow[it]) * CB + 8 * sub);
             vv[it] = make_uint4(c.x, c.y, 0, 0);
             vs[LOW ? it : 0] = half_bits_to_f32(a.Vs[(size_t)r * a.stride_l + srow[it]]);
         }
@@ -265,6 +281,9 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
                 x[2 * c] = bf16_to_f32((uint16_t)(w[c] & 0xFFFF));
                 x[2 * c + 1] = bf16_to_f32((uint16_t)(w[c] >> 16));
             }
+        } else if (LOWB == 4) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = (float)((int32_t)(vv[it].x << (28 - 4 * c)) >> 28) * vs[LOW ? it : 0];
         } else {
             const uint32_t w[2] = {vv[it].x, vv[it].y};
 #pragma unroll
@@ -377,8 +396,11 @@ static int decode_launch(const kvc_dims *dims, DecodeArgs &a, float *acc, hipStr
     const dim3 grid_h((unsigned)(rows * a.chunks_h)), grid_l((unsigned)(rows * a.chunks_l)), block(DEC_THREADS);
 #define DEC_PARTIAL_G(DD, GG)                                                              \
     do {                                                                                   \
-        decode_partial<DD, GG, false><<<grid_h, block, 0, s>>>(a);                         \
-        if (a.chunks_l) decode_partial<DD, GG, true><<<grid_l, block, 0, s>>>(a);          \
+        decode_partial<DD, GG, 0><<<grid_h, block, 0, s>>>(a);                             \
+        if (a.chunks_l && a.low_bits == 4)                                                 \
+            decode_partial<DD, GG, 4><<<grid_l, block, 0, s>>>(a);                         \
+        else if (a.chunks_l)                                                               \
+            decode_partial<DD, GG, 8><<<grid_l, block, 0, s>>>(a);                         \
     } while (0)
 #define DEC_PARTIAL(DD)                                                                    \
     do {                                                                                   \
@@ -417,7 +439,7 @@ extern "C" int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const ui
                                const uint16_t *V, const int32_t *n_h, int64_t stride_h,
                                const int32_t *block_table, int32_t page_size, int32_t blocks_per_seq,
                                const int8_t *Kq, const int8_t *Vq, const uint16_t *Ks,
-                               const uint16_t *Vs, const int32_t *n_l, int64_t stride_l,
+                               const uint16_t *Vs, const int32_t *n_l, int64_t stride_l, int32_t low_bits,
                                uint16_t *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
     int st = check_dims(dims, "kvc_decode_attn");
     if (st != KVC_OK) return st;
@@ -432,7 +454,9 @@ extern "C" int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const ui
         return fail(KVC_ERR_ARG, "kvc_decode_attn: paged layout needs page_size and blocks_per_seq");
     const bool has_low = n_l != nullptr;
     if (has_low && (!Kq || !Vq || !Ks || !Vs || stride_l <= 0))
-        return fail(KVC_ERR_ARG, "kvc_decode_attn: int8 partition needs Kq, Vq, Ks, Vs and stride_l");
+        return fail(KVC_ERR_ARG, "kvc_decode_attn: low-precision partition needs Kq, Vq, Ks, Vs and stride_l");
+    if (has_low && low_bits != 8 && low_bits != 4)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_attn: low_bits %d (8 or 4)", low_bits);
     // The bf16 partition's token count is bounded by what the layout can address.
     const int64_t max_h = block_table ? (int64_t)blocks_per_seq * page_size : stride_h;
     const size_t need = decode_workspace_bytes(dims, max_h, has_low ? stride_l : 0);
@@ -453,6 +477,7 @@ extern "C" int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const ui
     a.Vs = Vs;
     a.n_l = n_l;
     a.stride_l = has_low ? stride_l : 0;
+    a.low_bits = low_bits;
     a.L = dims->n_layers;
     a.Hkv = dims->n_kv_heads;
     a.Hq = dims->n_q_heads;
@@ -505,6 +530,7 @@ extern "C" int kvc_decode_attn_h2o(const kvc_dims *dims, const uint16_t *q, cons
     a.Ks = a.Vs = nullptr;
     a.n_l = nullptr;
     a.stride_l = 0;
+    a.low_bits = 8;
     a.L = dims->n_layers;
     a.Hkv = dims->n_kv_heads;
     a.Hq = dims->n_q_heads;

@@ -139,6 +139,7 @@ class CompactOut:
     h_base: Optional[torch.Tensor] = None      # int32 [rows] first bf16 slot (append)
     l_base: Optional[torch.Tensor] = None      # int32 [rows] first int8 slot (append)
     kept_page: int = 0                         # > 0: kept lists are per-sequence page indices
+    low_bits: int = 8                          # low tier codes: 8 (int8) or 4 (two nibbles per byte)
     K_ref: Optional[torch.Tensor] = None       # reference store of the current slots (bf16)
     p_ref: Optional[torch.Tensor] = None       # int32 positions of those references (< 0: none)
     K_ref_out: Optional[torch.Tensor] = None   # reference store of the kept slots
@@ -160,7 +161,7 @@ class CompactOut:
             _ptr(self.K_ref, torch.bfloat16, "K_ref"), _ptr(self.p_ref, torch.int32, "p_ref"),
             _ptr(self.K_ref_out, torch.bfloat16, "K_ref_out"), _ptr(self.p_ref_out, torch.int32, "p_ref_out"),
             _ptr(self.score_in, torch.float32, "score_in"), _ptr(self.score_out, torch.float32, "score_out"),
-            _ptr(self.tag_in, torch.uint8, "tag_in"), _ptr(self.tag_out, torch.uint8, "tag_out"))
+            _ptr(self.tag_in, torch.uint8, "tag_in"), _ptr(self.tag_out, torch.uint8, "tag_out"), self.low_bits)
 
 
 def kvc_compact_rerotate(dims, K, V, pos_in, kept_idx, kept_stride, n_kept, renumber_base, rope_base,
@@ -180,13 +181,13 @@ def kvc_decode_workspace_bytes(dims, max_h, stride_l=0):
 
 def kvc_decode_attn(dims, q, K, V, n_h, stride_h, o, ws, lse=None, block_table=None, page_size=0,
                     blocks_per_seq=0, Kq=None, Vq=None, Ks=None, Vs=None, n_l=None, stride_l=0,
-                    stream=None):
+                    low_bits=8, stream=None):
     st = _lib.load().kvc_decode_attn(
         ctypes.byref(dims), _ptr(q, torch.bfloat16, "q"), _ptr(K, torch.bfloat16, "K"),
         _ptr(V, torch.bfloat16, "V"), _ptr(n_h, torch.int32, "n_h"), stride_h,
         _ptr(block_table, torch.int32, "block_table"), page_size, blocks_per_seq,
         _ptr(Kq, torch.int8, "Kq"), _ptr(Vq, torch.int8, "Vq"), _ptr(Ks, torch.int16, "Ks"),
-        _ptr(Vs, torch.int16, "Vs"), _ptr(n_l, torch.int32, "n_l"), stride_l,
+        _ptr(Vs, torch.int16, "Vs"), _ptr(n_l, torch.int32, "n_l"), stride_l, low_bits,
         _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     return _lib.check(st)

@@ -85,7 +85,7 @@ def run_pask(w, inp, timer=None):
     # controller per generated token, then each row's action from its layer group
     with t("host:kvc_host_pask_control"):
         grp = np.array([kvc.kvc_layer_group(l, L, w.n_groups) for l in range(L)])
-        costs = kvc.kvc_host_pask_costs(np.bincount(grp, minlength=w.n_groups), Hkv, d, 8)
+        costs = kvc.kvc_host_pask_costs(np.bincount(grp, minlength=w.n_groups), Hkv, d, w.low_bits)
         acts, ledger = kvc.kvc_host_pask_control(inp.a0, inp.amin, inp.prio, inp.critical, costs,
                                                  w.budget_fraction, inp.tags)
     act_rows = np.ascontiguousarray(np.broadcast_to(
@@ -95,7 +95,7 @@ def run_pask(w, inp, timer=None):
     kept_g = torch.arange(Tg, dtype=torch.int32, device=dev).expand(rows, Tg).contiguous()
     pos_g = (Tp + kept_g).contiguous()
     nk_g = torch.full((rows,), Tg, dtype=torch.int32, device=dev)
-    Kq = torch.zeros((rows, S, d), dtype=torch.int8, device=dev)
+    Kq = torch.zeros((rows, S, d * w.low_bits // 8), dtype=torch.int8, device=dev)
     Vq = torch.zeros_like(Kq)
     Ks = torch.zeros((rows, S), dtype=torch.int16, device=dev)
     Vs = torch.zeros_like(Ks)
@@ -105,13 +105,15 @@ def run_pask(w, inp, timer=None):
     dims_g = kvc.make_dims(N, L, Hkv, Hq, d, Tg)
     with t("kvc_compact_rerotate:tiered"):
         kvc.kvc_compact_rerotate(dims_g, inp.K_gen, inp.V_gen, pos_g, kept_g, Tg, nk_g, -1, w.rope_base,
-                                 kvc.CompactOut(S, Ko, Vo, po, nh, action, Kq, Vq, Ks, Vs, pq, nl, h_base=nh0))
+                                 kvc.CompactOut(S, Ko, Vo, po, nh, action, Kq, Vq, Ks, Vs, pq, nl, h_base=nh0,
+                                                low_bits=w.low_bits))
     dims_d = kvc.make_dims(N, L, Hkv, Hq, d, S)
     wsd = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_d, S, S)), dtype=torch.uint8, device=dev)
     o = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((N, L, Hq), dtype=torch.float32, device=dev)
     with t("kvc_decode_attn"):
-        kvc.kvc_decode_attn(dims_d, inp.q_dec, Ko, Vo, nh, S, o, wsd, lse, None, 0, 0, Kq, Vq, Ks, Vs, nl, S)
+        kvc.kvc_decode_attn(dims_d, inp.q_dec, Ko, Vo, nh, S, o, wsd, lse, None, 0, 0, Kq, Vq, Ks, Vs, nl, S,
+                            w.low_bits)
     return dict(status=st, scores=scores, kept=kept, n_kept=nk, acts=acts, ledger=ledger, Ko=Ko, Vo=Vo,
                 pos=po, n_h=nh, Kq=Kq, Vq=Vq, Ks=Ks, Vs=Vs, pos_q=pq, n_l=nl, o=o, lse=lse)
 

@@ -262,6 +262,7 @@ class PaskWorkload:
     budget_fraction: float = 1.0 / 3.0
     rope_base: float = 5e5
     seed: int = 20261204
+    low_bits: int = 8            # low tier: 8 = int8, 4 = INT4 (two nibbles per byte)
 
     @property
     def rows(self):
@@ -274,6 +275,11 @@ PASK_WORKLOADS = {
     "pask_small": PaskWorkload("pask_small", n_seq=3, n_layers=4, n_groups=4, n_kv_heads=2, n_q_heads=8,
                                head_dim=128, n_prompt=640, n_gen=300, window=16, n_recent=32,
                                budget=213, gen_recent=32, seed=20261214),
+    # the pages' own low tier: INT4
+    "pask_llama3_8b_int4": PaskWorkload("pask_llama3_8b_int4", low_bits=4),
+    "pask_small_int4": PaskWorkload("pask_small_int4", n_seq=3, n_layers=4, n_groups=4, n_kv_heads=2,
+                                    n_q_heads=8, head_dim=128, n_prompt=640, n_gen=300, window=16,
+                                    n_recent=32, budget=213, gen_recent=32, seed=20261224, low_bits=4),
 }
 
 

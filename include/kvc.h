@@ -210,6 +210,11 @@ typedef struct kvc_compact_out {
     float *score_out;         /* fp32 [N][L][Hkv][out_stride] */
     const uint8_t *tag_in;    /* u8 [N][L][Hkv][T] */
     uint8_t *tag_out;         /* u8 [N][L][Hkv][out_stride] */
+    /* Low tier format (PASK Appendix B.5): 0 or 8 = int8 codes, Kq / Vq
+     * [..][out_stride][d] with 7 -> 127; 4 = INT4, codes in [-7, 7], two
+     * signed nibbles per byte (dimension 2i in the low nibble of byte i),
+     * Kq / Vq [..][out_stride][d/2]. Scales as for int8. */
+    int32_t low_bits;
 } kvc_compact_out;
 
 /*
@@ -255,7 +260,7 @@ size_t kvc_decode_workspace_bytes(const kvc_dims *dims, int64_t max_h, int64_t s
  *
  * For every row r and query head g of its group (absolute head h*G + g):
  *   o = sum_t softmax_t(q . k_t / sqrt(d)) v_t
- * over the union of the row's bf16 tokens (n_h[r] of them) and int8 tokens
+ * over the union of the row's bf16 tokens (n_h[r] of them) and low-precision tokens
  * (n_l[r], dequantised as code * fp16 scale); every cached token is visible.
  *
  *   q            bf16 [N][L][Hq][d] (already rotated to the query position)
@@ -265,8 +270,11 @@ size_t kvc_decode_workspace_bytes(const kvc_dims *dims, int64_t max_h, int64_t s
  *                (n, l, h) lives in slot block_table[n][t / page_size] *
  *                page_size + t % page_size of that row's storage (paged
  *                layout); slots outside [0, stride_h) are skipped.
- *   Kq, Vq       int8 [N][L][Hkv][stride_l][d]; Ks, Vs fp16 [N][L][Hkv][stride_l];
- *   n_l          int32 [N][L][Hkv], or NULL for no int8 partition
+ *   Kq, Vq       low-precision codes: low_bits 8 = int8 [N][L][Hkv][stride_l][d];
+ *                low_bits 4 = INT4 nibble pairs [N][L][Hkv][stride_l][d/2] (PASK
+ *                Appendix B.5, as kvc_compact_out.low_bits); Ks, Vs fp16 [N][L][Hkv][stride_l]
+ *   n_l          int32 [N][L][Hkv], or NULL for no low-precision partition
+ *   low_bits     8 or 4 (read only with n_l)
  *   o            bf16 [N][L][Hq][d] output; a row with no tokens gives o = 0
  *   lse          fp32 [N][L][Hq] natural-log normaliser (max + log sum), or NULL
  *   ws           kvc_decode_workspace_bytes(dims, max_h, stride_l) bytes
@@ -276,7 +284,7 @@ int kvc_decode_attn(const kvc_dims *dims, const uint16_t *q, const uint16_t *K, 
                     const int32_t *n_h, int64_t stride_h, const int32_t *block_table,
                     int32_t page_size, int32_t blocks_per_seq, const int8_t *Kq, const int8_t *Vq,
                     const uint16_t *Ks, const uint16_t *Vs, const int32_t *n_l, int64_t stride_l,
-                    uint16_t *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+                    int32_t low_bits, uint16_t *o, float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /* Device workspace (bytes) kvc_decode_attn_h2o needs for a pool of stride_h
  * tokens per row. */

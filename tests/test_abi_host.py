@@ -141,12 +141,13 @@ def test_decode_rejects_bad_arguments():
     assert ws > 0
     call = lambda **k: lib.kvc_decode_attn(
         ctypes.byref(k.get("dims", d)), FAKE, FAKE, FAKE, FAKE, k.get("stride_h", 512),
-        k.get("bt", None), k.get("ps", 0), k.get("bps", 0), k.get("Kq", None), None, None, None,
-        k.get("n_l", None), k.get("stride_l", 0), FAKE, None, FAKE, k.get("ws", ws), None)
+        k.get("bt", None), k.get("ps", 0), k.get("bps", 0), k.get("Kq"), k.get("Vq"), k.get("Ks"), k.get("Vs"),
+        k.get("n_l", None), k.get("stride_l", 0), k.get("bits", 8), FAKE, None, FAKE, k.get("ws", ws), None)
     assert call(stride_h=0) == _lib.KVC_ERR_ARG
     assert call(ws=ws - 1) == _lib.KVC_ERR_WORKSPACE
     assert call(bt=FAKE, ps=0, bps=4) == _lib.KVC_ERR_ARG            # paged needs a page size
     assert call(n_l=FAKE, stride_l=64) == _lib.KVC_ERR_ARG            # int8 pools missing
+    assert call(n_l=FAKE, stride_l=64, Kq=FAKE, Vq=FAKE, Ks=FAKE, Vs=FAKE, bits=2) == _lib.KVC_ERR_UNSUPPORTED
     big = _dims(n_q_heads=64, n_kv_heads=2)                             # G = 32 > 16
     assert call(dims=big, ws=1 << 40) == _lib.KVC_ERR_UNSUPPORTED
 

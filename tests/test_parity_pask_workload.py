@@ -39,7 +39,7 @@ def run_pask(w, inp):
 def _oracle_actions(w, inp):
     """PASK Algorithm 2 over every sequence, with the oracle's own costs."""
     layers = [last - first + 1 for first, last in o_policy.group_ranges(w.n_layers, w.n_groups)]
-    costs = o_pask.group_costs(layers, w.n_kv_heads, w.head_dim)
+    costs = o_pask.group_costs(layers, w.n_kv_heads, w.head_dim, low_bits=w.low_bits)
     out = [o_pask.control_sequence(inp.tags[n], inp.a0.astype(np.int64), inp.amin.astype(np.int64),
                                    inp.prio.astype(np.float64), inp.critical, costs, w.budget_fraction)
            for n in range(w.n_seq)]
@@ -78,10 +78,13 @@ def _check_row(w, inp, res, o_acts, r):
     np.testing.assert_array_equal(Vo_b[nk:nk + H.size], Vgb[H])
     np.testing.assert_array_equal(po[nk:nk + H.size], Tp + H)
     Kg, Vg = numfmt.bf16_bits_to_f64(Kgb), numfmt.bf16_bits_to_f64(Vgb)
-    ck, sk = o_quant.quantize_rows(Kg[Lw])
-    cv, sv = o_quant.quantize_rows(Vg[Lw])
-    gkq = res["Kq"][r][: Lw.size].cpu().numpy().astype(int)
-    gvq = res["Vq"][r][: Lw.size].cpu().numpy().astype(int)
+    qmax = 127 if w.low_bits == 8 else 7
+    ck, sk = o_quant.quantize_rows(Kg[Lw], qmax)
+    cv, sv = o_quant.quantize_rows(Vg[Lw], qmax)
+    codes = lambda x: (x.cpu().numpy() if w.low_bits == 8 else  # noqa: E731
+                       o_quant.unpack_nibbles(x.cpu().numpy().view(np.uint8), w.head_dim)).astype(int)
+    gkq = codes(res["Kq"][r][: Lw.size])
+    gvq = codes(res["Vq"][r][: Lw.size])
     assert Lw.size == 0 or (np.abs(gkq - ck).max() <= 1 and np.abs(gvq - cv).max() <= 1)
     np.testing.assert_array_equal(res["Ks"][r][: Lw.size].cpu().numpy().view(np.uint16), sk)
     np.testing.assert_array_equal(res["Vs"][r][: Lw.size].cpu().numpy().view(np.uint16), sv)
@@ -100,8 +103,9 @@ def _check_row(w, inp, res, o_acts, r):
     return swaps
 
 
-def test_pask_small_every_row():
-    w = synth.PASK_WORKLOADS["pask_small"]
+@pytest.mark.parametrize("name", ["pask_small", "pask_small_int4"])
+def test_pask_small_every_row(name):
+    w = synth.PASK_WORKLOADS[name]
     inp = synth.make_pask_inputs(w, "cuda")
     res = run_pask(w, inp)
     o_acts, o_ledger = _oracle_actions(w, inp)
@@ -113,9 +117,10 @@ def test_pask_small_every_row():
     assert (res["n_l"] > 0).any() and (res["n_h"] < w.budget + w.n_gen).any()
 
 
-def test_pask_full_size_sampled_rows():
+@pytest.mark.parametrize("name", ["pask_llama3_8b", "pask_llama3_8b_int4"])
+def test_pask_full_size_sampled_rows(name):
     """64 sequences x 32 layers (4 groups) x 8 KV heads: 4096 prompt + 1024 generated tokens."""
-    w = synth.PASK_WORKLOADS["pask_llama3_8b"]
+    w = synth.PASK_WORKLOADS[name]
     inp = synth.make_pask_inputs(w, "cuda")
     res = run_pask(w, inp)
     o_acts, o_ledger = _oracle_actions(w, inp)
