@@ -55,3 +55,22 @@ def obs_window_score(K, Qgrp, W):
     q_pos = np.tile(window_positions(T, W), G)          # row r = g*W + w
     a = attention_weights(K, Qgrp.reshape(G * W, d), q_pos)
     return a.sum(axis=0)
+
+
+def pool_scores(score, kernel, mode):
+    """Smoothing of a row's scores along the token axis before selection
+    (PASK Appendix C.3, Table 8: SnapKV's pooling, avg or max with an odd
+    kernel of 3, 5 or 7; the RocketKV baseline there scores the prefix with an
+    odd max-pool kernel of 63).
+
+    pooled[j] = max or mean of score[j'] over |j' - j| <= kernel // 2 with
+    0 <= j' < T. Reading: the window is cut at the row's ends (no padding
+    values enter the max or the mean). kernel 1 is the identity.
+    """
+    s = np.asarray(score, np.float64)
+    T, h = s.shape[0], kernel // 2
+    out = np.empty(T)
+    for j in range(T):
+        win = s[max(0, j - h):min(T, j + h + 1)]
+        out[j] = win.max() if mode == "max" else win.mean()
+    return out
