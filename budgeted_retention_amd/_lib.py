@@ -67,6 +67,7 @@ PROTOTYPES = {
     "kvc_foresight_bonus": (c_double, [c_double, c_double, c_double]),
     "kvc_score": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_int32,
                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kvc_pool_scores": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "kvc_select": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, ctypes.POINTER(KvcPolicy),
                                   c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "kvc_compact_rerotate": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_void_p,

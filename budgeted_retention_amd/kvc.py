@@ -85,6 +85,15 @@ def kvc_score(dims, K, Q_obs, W, scores, ws, stream=None):
     return _lib.check(st)
 
 
+
+KVC_POOL_MAX, KVC_POOL_AVG = 0, 1
+
+
+def kvc_pool_scores(dims, scores, kernel, mode, pooled, stream=None):
+    st = _lib.load().kvc_pool_scores(ctypes.byref(dims), _ptr(scores, torch.float32, "scores"), kernel, mode,
+                                     _ptr(pooled, torch.float32, "pooled"), _stream(stream))
+    return _lib.check(st)
+
 @dataclass
 class Policy:
     n_sink: int

@@ -88,6 +88,27 @@ size_t kvc_workspace_bytes(int op, const kvc_dims *dims, int32_t W, int32_t B);
 int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
               float *scores, void *ws, size_t ws_bytes, void *stream);
 
+/* Pooling modes of kvc_pool_scores. */
+enum { KVC_POOL_MAX = 0, KVC_POOL_AVG = 1 };
+
+/*
+ * Score pooling along the token axis (PASK Appendix C.3, Table 8: the SnapKV
+ * baseline smooths its window scores by average or max pooling with an odd
+ * kernel of 3, 5 or 7; the RocketKV baseline max-pools with a kernel of 63),
+ * applied between kvc_score and kvc_select.
+ *
+ *   pooled[r][j] = max (KVC_POOL_MAX) or mean (KVC_POOL_AVG) of scores[r][j']
+ *                  over |j' - j| <= kernel/2 and 0 <= j' < T
+ * The window is cut at the row's ends: no padding enters the max or the mean.
+ * The mean sums in token order in fp32 and divides once. Max ignores NaN
+ * unless every value is NaN.
+ *
+ *   scores, pooled  fp32 [N][L][Hkv][T]; pooled must not alias scores
+ *   kernel          odd, 1..255 (1 copies the scores)
+ */
+int kvc_pool_scores(const kvc_dims *dims, const float *scores, int32_t kernel, int32_t mode, float *pooled,
+                    void *stream);
+
 /*
  * Retention policy for kvc_select: bonus and protection floor per
  * (tag, layer group) from a frozen table (PASK §3.5 Eq. 11 lookup, PASK

@@ -244,3 +244,14 @@ def test_compact_carry_rejects_half_pairs_and_tiered_path():
     out.action = FAKE
     out.Kq = out.Vq = out.Ks = out.Vs = FAKE
     assert call() == _lib.KVC_ERR_UNSUPPORTED
+
+
+def test_pool_rejects_bad_kernel_mode_and_alias():
+    lib = _lib.load()
+    d = _dims()
+    other = FAKE + 64
+    assert lib.kvc_pool_scores(ctypes.byref(d), FAKE, 4, 0, other, None) == _lib.KVC_ERR_ARG     # even kernel
+    assert lib.kvc_pool_scores(ctypes.byref(d), FAKE, 257, 0, other, None) == _lib.KVC_ERR_ARG
+    assert lib.kvc_pool_scores(ctypes.byref(d), FAKE, 7, 2, other, None) == _lib.KVC_ERR_ARG     # mode
+    assert lib.kvc_pool_scores(ctypes.byref(d), FAKE, 7, 0, FAKE, None) == _lib.KVC_ERR_ARG      # alias
+    assert lib.kvc_pool_scores(ctypes.byref(d), FAKE, 7, 0, None, None) == _lib.KVC_ERR_ARG
