@@ -92,6 +92,8 @@ PROTOTYPES = {
                                        c_void_p]),
     "kvc_page_scores": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_int32, c_void_p,
                                        c_void_p, c_int32, c_void_p, c_void_p]),
+    "kvc_host_commit_protect": (ctypes.c_int, [c_void_p, c_void_p, c_int32, c_int32, c_double, c_int32,
+                                               c_void_p, c_void_p]),
     "kvc_host_pask_costs": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "kvc_host_pask_control": (ctypes.c_int, [ctypes.POINTER(KvcPaskTable), c_void_p, c_double, c_double,
                                              c_void_p, c_int32, c_int32, c_void_p, c_void_p]),

@@ -151,3 +151,32 @@ extern "C" int kvc_host_commit_candidates(const float *R_minus, const float *R_p
     *n_order = n;
     return KVC_OK;
 }
+
+extern "C" int kvc_host_commit_protect(const float *R_minus, const int32_t *page_tokens, int32_t n_pending,
+                                       int32_t budget, double eta, int32_t max_pages, uint8_t *protect,
+                                       int32_t *n_protected) {
+    if (!protect || !n_protected || n_pending < 0 || budget < 0 || max_pages < 0 || !(eta >= 0.0 && eta <= 1.0) ||
+        (n_pending > 0 && (!R_minus || !page_tokens)))
+        return fail(KVC_ERR_ARG, "kvc_host_commit_protect: bad arguments");
+    const int64_t B_N = (int64_t)std::floor(eta * (double)budget);
+    std::vector<int32_t> idx(n_pending);
+    for (int32_t e = 0; e < n_pending; ++e) {
+        idx[e] = e;
+        protect[e] = 0;
+        if (page_tokens[e] < 0) return fail(KVC_ERR_ARG, "kvc_host_commit_protect: negative page size");
+    }
+    std::sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+        if (R_minus[x] != R_minus[y]) return R_minus[x] > R_minus[y];
+        return x < y;
+    });
+    int64_t used = 0;
+    int32_t n = 0;
+    for (int32_t e : idx) {  // a prefix of the order: the first page that does not fit ends it
+        if (n >= max_pages || used + page_tokens[e] > B_N) break;
+        protect[e] = 1;
+        used += page_tokens[e];
+        ++n;
+    }
+    *n_protected = n;
+    return KVC_OK;
+}

@@ -306,3 +306,16 @@ def kvc_host_commit_candidates(R_minus, R_plus, tau_use, tau_dead, rho_use, rho_
         _np_ptr(Rm, np.float32), _np_ptr(Rp, np.float32), Rm.size, tau_use, tau_dead, rho_use, rho_dead,
         max_scan, _np_ptr(state, np.uint8), _np_ptr(order, np.int32), ctypes.addressof(n)))
     return state, order, n.value
+
+
+def kvc_host_commit_protect(R_minus, page_tokens, budget, eta, max_pages=16):
+    """Returns (protect uint8 [n_pending], n_protected)."""
+    import numpy as np
+    Rm = np.ascontiguousarray(R_minus, np.float32)
+    pt = np.ascontiguousarray(page_tokens, np.int32)
+    out = np.zeros(max(Rm.size, 1), np.uint8)
+    n = ctypes.c_int32(0)
+    _lib.check(_lib.load().kvc_host_commit_protect(
+        _np_ptr(Rm, np.float32), _np_ptr(pt, np.int32), Rm.size, budget, float(eta), max_pages,
+        _np_ptr(out, np.uint8), ctypes.addressof(n)))
+    return out[:Rm.size], n.value

@@ -463,6 +463,23 @@ int kvc_host_commit_candidates(const float *R_minus, const float *R_plus, int32_
                                float tau_dead, float rho_use, float rho_dead, int32_t max_scan,
                                uint8_t *state, int32_t *order, int32_t *n_order);
 
+/*
+ * Pending-page protection at a compression checkpoint (CommitKV §3.3
+ * "Protecting incomplete transitions", Eq. 12), on the host. Pages whose
+ * pre-commit effect R_minus is known but whose post-commit measurement is
+ * still to come are protected in order of decreasing R_minus (ties: lower
+ * index) while their tokens total at most B_N = floor(eta * budget) and at
+ * most max_pages pages are taken (the page's setup protects at most 16); the
+ * first page that does not fit ends the walk. The protected pages are then
+ * kept at the checkpoint (Eq. 13), e.g. as a floor tag in kvc_select.
+ *
+ *   R_minus, page_tokens  [n_pending] host arrays
+ *   protect               u8 [n_pending] output, 1 = protected; *n_protected their count
+ */
+int kvc_host_commit_protect(const float *R_minus, const int32_t *page_tokens, int32_t n_pending,
+                            int32_t budget, double eta, int32_t max_pages, uint8_t *protect,
+                            int32_t *n_protected);
+
 #ifdef __cplusplus
 }
 #endif

@@ -142,20 +142,46 @@ def page_scores(row_scores, page_size, n_pages):
     return np.array([per_token[e * page_size:(e + 1) * page_size].sum() for e in range(n_pages)])
 
 
-def retained_pages(score, retired, n_keep):
-    """Pages kept at the checkpoint (CommitKV §3.3, Eq. 13 with an empty
-    pending set): retired pages are excluded (scored -inf), the rest ranked
-    by (score descending, page index ascending), the first n_keep kept and
-    returned in ascending order. Retired pages are used only when fewer than
-    n_keep others exist.
+def retained_pages(score, retired, n_keep, protected=()):
+    """Pages kept at the checkpoint (CommitKV §3.3, Eq. 13): the protected
+    pending pages N are kept, retired pages are excluded (scored -inf), the
+    rest ranked by (score descending, page index ascending) fill the budget
+    to n_keep; returned in ascending order. Retired pages are used only when
+    fewer than n_keep others exist.
     """
     score = np.asarray(score, np.float64).copy()
     score[np.asarray(list(retired), dtype=np.int64)] = -np.inf
     if score.size <= n_keep:
         return np.arange(score.size, dtype=np.int64)
-    idx = np.arange(score.size)
-    order = np.lexsort((idx, -score))
-    return np.sort(order[:n_keep]).astype(np.int64)
+    prot = np.asarray(sorted(set(int(e) for e in protected)), dtype=np.int64)
+    if prot.size >= n_keep:
+        return prot
+    rest = np.setdiff1d(np.arange(score.size), prot)
+    order = rest[np.lexsort((rest, -score[rest]))]
+    return np.sort(np.concatenate([prot, order[: n_keep - prot.size]])).astype(np.int64)
+
+
+def protect_pending(R_minus, page_tokens, budget, eta, max_pages=16):
+    """Pending pages protected at a checkpoint (CommitKV §3.3 "Protecting
+    incomplete transitions", Eq. 12): pages awaiting their post-commit
+    measurement are protected in order of decreasing pre-commit effect
+    (ties: lower index) while their tokens total at most B_N = floor(eta * B)
+    and at most max_pages pages are protected (the setup section protects at
+    most 16). Reading: the protected set is a prefix of that order -- the
+    first page that does not fit ends it. Returns the protected indices
+    (positions in R_minus), ascending.
+    """
+    Rm = np.asarray(R_minus, np.float64)
+    tok = np.asarray(page_tokens, np.int64)
+    B_N = int(np.floor(eta * budget))
+    order = np.lexsort((np.arange(Rm.size), -Rm))
+    out, used = [], 0
+    for e in order:
+        if len(out) >= max_pages or used + tok[e] > B_N:
+            break
+        out.append(int(e))
+        used += int(tok[e])
+    return np.sort(np.asarray(out, np.int64))
 
 
 def greedy_retire(order, joint_effect, tau_joint, max_scan=64):

@@ -59,3 +59,20 @@ def test_host_helpers_reject_bad_arguments():
         z = np.zeros((8, 2), np.uint8)
         kvc.kvc_host_pask_control(z, z, np.zeros((8, 2, 2), np.float32), np.zeros(8, np.uint8),
                                   np.zeros((2, 3)), 0.5, tags)
+
+
+def test_commit_protection_matches_oracle_and_the_page_budget():
+    from oracle import page_effect as o_pe
+    rng = np.random.default_rng(3)
+    for trial in range(50):
+        n = int(rng.integers(0, 40))
+        Rm = rng.gamma(0.5, 0.05, n).astype(np.float32)
+        if n > 4:
+            Rm[1] = Rm[3]                                   # a tie: the lower index first
+        tok = np.where(rng.random(n) < 0.8, 16, rng.integers(1, 64, n)).astype(np.int32)
+        B = int(rng.integers(256, 8192))
+        eta = float(rng.choice([0.0, 0.0625, 0.125, 0.5, 1.0]))
+        got, k = kvc.kvc_host_commit_protect(Rm, tok, B, eta, 16)
+        want = o_pe.protect_pending(Rm.astype(np.float64), tok, B, eta, 16)
+        np.testing.assert_array_equal(np.flatnonzero(got), want)
+        assert k == want.size <= 16 and tok[want].sum() <= int(np.floor(eta * B))

@@ -204,3 +204,25 @@ def test_controller_step_brute_force_properties():
         space = [v for v in itertools.product(range(3), repeat=3)
                  if all(v[c] >= amin[c] for c in range(3))]
         assert tuple(a) in space
+
+
+def test_protection_budget_and_prefix_rule_commitkv_eq12():
+    # CommitKV §3.3 Eq. 12 with the setup's eta = 0.125 and at most 16 pages:
+    # B = 4096 gives B_N = 512 tokens; 16-token pages hit the 16-page cap first,
+    # 48-token pages the token bound after 10 pages.
+    Rm = np.linspace(1.0, 0.1, 30)
+    np.testing.assert_array_equal(pe.protect_pending(Rm, np.full(30, 16), 4096, 0.125), np.arange(16))
+    np.testing.assert_array_equal(pe.protect_pending(Rm, np.full(30, 48), 4096, 0.125), np.arange(10))
+    # the largest effect does not fit: nothing after it is taken either
+    tok = np.full(30, 16)
+    tok[0] = 600
+    assert pe.protect_pending(Rm, tok, 4096, 0.125).size == 0
+    assert pe.protect_pending(Rm, np.full(30, 16), 4096, 0.0).size == 0
+
+
+def test_retained_pages_keep_protected_and_drop_retired_eq13():
+    score = np.array([5.0, 1.0, 4.0, 3.0, 2.0, 0.5])
+    # keep 3: page 5 protected (lowest score), page 0 retired (highest)
+    np.testing.assert_array_equal(pe.retained_pages(score, [0], 3, protected=[5]), [2, 3, 5])
+    np.testing.assert_array_equal(pe.retained_pages(score, [], 3, protected=[]), [0, 2, 3])
+    np.testing.assert_array_equal(pe.retained_pages(score, [0, 2], 2, protected=[1]), [1, 3])
