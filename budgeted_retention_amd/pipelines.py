@@ -257,3 +257,118 @@ def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
             rec[-1].update(kept=kept.clone(), n_kept=nk.clone())
         cur, nxt = nxt, cur
     return {"cycles": rec, "final": cur, "o": o}
+
+
+def run_commit_multi(w, inp, timer=None, record=False):
+    """Successive commits of the CommitKV lifecycle (§3.2-3.4) for every
+    trajectory. Per commit c:
+
+    1. the engine appends turn c to the resident cache (t_pre tokens);
+    2. pre-commit deletion effects R^- of every page before the pre-commit
+       window, at the deciding layer (kvc_page_effect);
+    3. the turn's pages, pending their post-commit measurement, are protected
+       by decreasing R^- under B_N = floor(eta B), at most 16 pages
+       (kvc_host_commit_protect, Eq. 12);
+    4. checkpoint: window scores of the pre-commit queries, page scores with
+       the pages retired at the previous commit excluded, top pages to B
+       tokens with the protected pages floored (Eq. 13), compaction of keys,
+       values and positions by the one page set (Eq. 4);
+    5. the engine appends the observation and the post-commit window;
+    6. post-commit effects R^+ of the retained pages that carry an R^-,
+       lifecycle labels and candidate order (kvc_host_commit_candidates), and
+       greedy joint retirement (kvc_page_retire, Eq. 11), whose accepted
+       pages the next checkpoint excludes.
+    With `record`, returns the per-commit host arrays the parity tests use."""
+    t = timer or _null_timer
+    N, L, Hkv, Hq, d, W, ps = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.window, w.page_size
+    B, Ta, Tb = w.budget, w.t_pre, w.t_post
+    dev = inp.K0.device
+    Pa, Pb, n_keep = Ta // ps, Tb // ps, B // ps
+    n_el = (Ta - W) // ps                         # pages wholly before the pre-commit window
+    first_turn_page = Tb // ps
+    dims_a = kvc.make_dims(N, L, Hkv, Hq, d, Ta)
+    dims_b = kvc.make_dims(N, L, Hkv, Hq, d, Tb)
+    dims_p = kvc.make_dims(N, 1, 1, 1, 64, Pa)
+    ws_a = kvc.page_workspace(dims_a, W, Ta - W, dev)
+    ws_b = kvc.page_workspace(dims_b, W, Tb - W, dev)
+    ws_s = kvc.workspace(kvc.KVC_OP_SCORE, dims_a, W, 0, dev)
+    Ka = torch.empty((N, L, Hkv, Ta, d), dtype=torch.bfloat16, device=dev)
+    Va = torch.empty_like(Ka)
+    pa = torch.empty((N, L, Hkv, Ta), dtype=torch.int32, device=dev)
+    Kb = inp.K0.clone()
+    Vb = inp.V0.clone()
+    pb = torch.arange(Tb, dtype=torch.int32, device=dev).expand(N, L, Hkv, Tb).contiguous()
+    nh = torch.zeros(N * L * Hkv, dtype=torch.int32, device=dev)
+    Rm = torch.empty((N, n_el), dtype=torch.float32, device=dev)
+    Rp = torch.empty((N, n_keep), dtype=torch.float32, device=dev)
+    scores = torch.empty((N, L, Hkv, Ta), dtype=torch.float32, device=dev)
+    pscore = torch.empty((N, Pa), dtype=torch.float32, device=dev)
+    kept = torch.full((N, n_keep), -1, dtype=torch.int32, device=dev)
+    nk = torch.zeros(N, dtype=torch.int32, device=dev)
+    floor = torch.tensor([[0], [1]], dtype=torch.uint8, device=dev)
+    zero_bonus = torch.zeros((2, 1), dtype=torch.float32, device=dev)
+    order = torch.full((N, w.max_scan), -1, dtype=torch.int32, device=dev)   # cache_b page indices
+    accepted = torch.zeros((N, w.max_scan), dtype=torch.uint8, device=dev)
+    next_pos = Tb
+    rec = []
+    for c in range(w.commits):
+        with t("append"):
+            Ka[:, :, :, :Tb] = Kb
+            Va[:, :, :, :Tb] = Vb
+            pa[:, :, :, :Tb] = pb
+            Ka[:, :, :, Tb:] = inp.K_call[c]
+            Va[:, :, :, Tb:] = inp.V_call[c]
+            pa[:, :, :, Tb:] = torch.arange(next_pos, next_pos + w.n_call, dtype=torch.int32, device=dev)
+        next_pos += w.n_call
+        with t("kvc_page_effect:pre"):
+            kvc.kvc_page_effect(dims_a, w.layer, Ka, Va, inp.Q_pre[c], W, Ta - W, ps, n_el, Rm, ws_a)
+        with t("host:kvc_host_commit_protect"):
+            Rm_h = Rm.cpu().numpy()
+            tags = np.zeros((N, Pa), np.uint8)
+            for n in range(N):
+                pend = np.arange(first_turn_page, n_el)
+                prot, _ = kvc.kvc_host_commit_protect(Rm_h[n, pend], np.full(pend.size, ps, np.int32), B, w.eta,
+                                                      w.max_protect)
+                tags[n, pend[prot.astype(bool)]] = 1
+            tags_d = torch.from_numpy(tags).to(dev)
+        with t("kvc_score"):
+            kvc.kvc_score(dims_a, Ka, inp.Q_pre[c], W, scores, ws_s)
+        with t("kvc_page_scores"):
+            kvc.kvc_page_scores(dims_a, scores, ps, Pa, pscore, order if c else None, accepted if c else None)
+        pol = kvc.Policy(0, 0, n_keep, 2, 1, 0, 1, tags_d, zero_bonus, floor)
+        with t("kvc_select"):
+            kvc.kvc_select(dims_p, pscore, pol, kept, n_keep, nk)
+        with t("kvc_compact_rerotate"):
+            kvc.kvc_compact_rerotate(dims_a, Ka, Va, pa, kept, n_keep, nk, -1, 1e6,
+                                     kvc.CompactOut(Tb, Kb, Vb, pb, nh, kept_page=ps))
+        with t("append"):
+            Kb[:, :, :, B:] = inp.K_obs[c]
+            Vb[:, :, :, B:] = inp.V_obs[c]
+            pb[:, :, :, B:] = torch.arange(next_pos, next_pos + w.n_obs + W, dtype=torch.int32, device=dev)
+        next_pos += w.n_obs + W
+        with t("kvc_page_effect:post"):
+            kvc.kvc_page_effect(dims_b, w.layer, Kb, Vb, inp.Q_post[c], W, Tb - W, ps, n_keep, Rp, ws_b)
+        with t("host:kvc_host_commit_candidates"):
+            Rp_h, kept_h = Rp.cpu().numpy(), kept.cpu().numpy()
+            ord_h = np.full((N, w.max_scan), -1, np.int32)
+            ncand = np.zeros(N, np.int32)
+            events = []
+            for n in range(N):
+                ev = np.flatnonzero(kept_h[n] < n_el)            # retained pages with an R^-
+                events.append(ev)
+                if ev.size == 0:
+                    continue
+                _, od, no = kvc.kvc_host_commit_candidates(Rm_h[n, kept_h[n, ev]], Rp_h[n, ev], w.tau_use,
+                                                           w.tau_dead, w.rho_use, w.rho_dead, w.max_scan)
+                ord_h[n, :no] = ev[od[:no]]
+                ncand[n] = no
+            order = torch.from_numpy(ord_h).to(dev)
+        accepted = torch.zeros((N, w.max_scan), dtype=torch.uint8, device=dev)
+        with t("kvc_page_retire"):
+            kvc.kvc_page_retire(dims_b, w.layer, Kb, Vb, inp.Q_post[c], W, Tb - W, ps, n_keep, order,
+                                w.tau_joint, accepted, ws_b)
+        if record:
+            rec.append(dict(Rm=Rm_h.copy(), tags=tags, pscore=pscore.cpu().numpy(), kept=kept_h.copy(),
+                            n_kept=nk.cpu().numpy(), Rp=Rp_h.copy(), events=events, order=ord_h.copy(),
+                            n_order=ncand.copy(), accepted=accepted.cpu().numpy(), pos=pb.cpu().numpy()))
+    return dict(commits=rec, K=Kb, V=Vb, pos=pb)

@@ -531,3 +531,111 @@ def make_h2o_inputs(w: H2OWorkload, cycles, device="cpu") -> H2OInputs:
     return H2OInputs(w, K, V, torch.from_numpy(pos.astype(np.int32)).to(device),
                      torch.from_numpy(acc.astype(np.float32)).to(device), torch.from_numpy(tags).to(device),
                      q, K_new, V_new, steps)
+
+
+# ---------------------------------------------------------------- CommitKV-style successive commits
+
+@dataclass(frozen=True)
+class CommitMultiWorkload:
+    """Successive tool-call commits of agent trajectories. Before commit c the
+    resident cache (B retained tokens, the previous observation and its
+    window) grows by a new turn of n_call tokens whose last W tokens end the
+    tool call (the pre-commit window). The turn's pages are the newly
+    completed event pages: pending until their post-commit measurement. A
+    checkpoint keeps B tokens; then the observation (n_obs tokens) and the
+    post-commit window (W) are appended. In every turn n_plant pages have keys
+    aligned with that turn's pre-commit queries and opposed to its post-commit
+    ones (completion pages)."""
+    name: str = "commitkv_multi"
+    n_seq: int = 16
+    n_layers: int = 28
+    n_kv_heads: int = 4
+    n_q_heads: int = 28
+    head_dim: int = 128
+    page_size: int = 16
+    budget: int = 4096
+    n_call: int = 1024
+    n_obs: int = 512
+    window: int = 32
+    commits: int = 4
+    n_plant: int = 8
+    plant_logit: float = 9.0
+    eta: float = 0.125
+    max_protect: int = 16
+    layer: int = 27
+    tau_use: float = 0.05
+    tau_dead: float = 1e-3
+    rho_use: float = 0.75
+    rho_dead: float = 0.25
+    tau_joint: float = 1e-2
+    max_scan: int = 64
+    seed: int = 20261207
+
+    @property
+    def rows(self):
+        return self.n_seq * self.n_layers * self.n_kv_heads
+
+    @property
+    def t_post(self):
+        """Tokens after a checkpoint and its observation: B + n_obs + W."""
+        return self.budget + self.n_obs + self.window
+
+    @property
+    def t_pre(self):
+        """Tokens at a commit's pre-commit measurement: t_post + n_call."""
+        return self.t_post + self.n_call
+
+
+COMMIT_MULTI_WORKLOADS = {
+    "commitkv_multi": CommitMultiWorkload(),
+    "commitkv_multi_small": CommitMultiWorkload("commitkv_multi_small", n_seq=2, n_layers=3, n_kv_heads=2,
+                                                n_q_heads=6, budget=256, n_call=128, n_obs=64, window=16,
+                                                commits=3, n_plant=3, layer=2, max_scan=8, seed=20261217),
+}
+
+
+@dataclass
+class CommitMultiInputs:
+    w: CommitMultiWorkload
+    K0: torch.Tensor       # bf16 [N][L][Hkv][t_post][d] history before the first turn
+    V0: torch.Tensor
+    K_call: torch.Tensor   # bf16 [C][N][L][Hkv][n_call][d] each turn's tokens
+    V_call: torch.Tensor
+    K_obs: torch.Tensor    # bf16 [C][N][L][Hkv][n_obs + W][d] each observation and its window
+    V_obs: torch.Tensor
+    Q_pre: torch.Tensor    # bf16 [C][N][L][Hq][W][d] the last W tokens of each turn
+    Q_post: torch.Tensor   # bf16 [C][N][L][Hq][W][d] the last W tokens after each observation
+    planted: np.ndarray    # int64 [C][N][n_plant] page indices within each turn
+
+
+def make_commit_multi_inputs(w: CommitMultiWorkload, device="cpu") -> CommitMultiInputs:
+    N, L, Hkv, Hq, d, C, W = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.commits, w.window
+    G = Hq // Hkv
+    s = w.seed * 16
+    K0 = normal_bf16((N, L, Hkv, w.t_post, d), s + 1, device)
+    V0 = normal_bf16((N, L, Hkv, w.t_post, d), s + 2, device)
+    Kc = normal_bf16((C, N, L, Hkv, w.n_call, d), s + 3, device)
+    Vc = normal_bf16((C, N, L, Hkv, w.n_call, d), s + 4, device)
+    Ko = normal_bf16((C, N, L, Hkv, w.n_obs + W, d), s + 5, device)
+    Vo = normal_bf16((C, N, L, Hkv, w.n_obs + W, d), s + 6, device)
+    Qm = normal_bf16((C, N, L, Hq, W, d), s + 7, device)
+    Qp = normal_bf16((C, N, L, Hq, W, d), s + 8, device)
+    rng = np.random.default_rng(w.seed + 41)
+    ps = w.page_size
+    n_turn_pages = (w.n_call - W) // ps          # turn pages wholly before the pre-commit window
+    planted = np.stack([np.stack([np.sort(rng.choice(n_turn_pages, w.n_plant, replace=False)) for _ in range(N)])
+                        for _ in range(C)])
+    c_len = float(np.sqrt(w.plant_logit * np.sqrt(d)))
+    for c in range(C):
+        u = rng.standard_normal((N, L, Hkv, d))
+        u /= np.linalg.norm(u, axis=-1, keepdims=True)
+        cu = torch.from_numpy(c_len * u).to(device=device, dtype=torch.float32)
+        for n in range(N):
+            Kn = Kc[c, n].view(L, Hkv, w.n_call // ps, ps, d)
+            idx = torch.from_numpy(planted[c, n]).to(device)
+            sel = Kn.index_select(2, idx).float() + cu[n][:, :, None, None, :]
+            Kn.index_copy_(2, idx, sel.to(torch.bfloat16))
+        cq = cu.repeat_interleave(G, dim=2)[:, :, :, None, :]
+        Qm[c] = (Qm[c].float() + cq).to(torch.bfloat16)
+        Qp[c] = (Qp[c].float() - cq).to(torch.bfloat16)
+    return CommitMultiInputs(w, K0, V0, Kc, Vc, Ko, Vo, Qm, Qp, planted)
