@@ -16,6 +16,8 @@ Other workloads (parity cases, measured the same way call by call):
   pask_llama3_8b  64 x 32 layers: prompt compaction, int8/bf16/release tiers, decode
   pask_llama3_8b_int4  the same with the pages' INT4 low tier (two nibbles per byte)
   commitkv_28l    16 x 28 layers: page effects, retirement, checkpoint, paged decode
+  commitkv_multi  16 x 28 layers: four successive commits (pre/post effects, pending-page
+                  protection, checkpoint, retirement); one step = the four commits
   pace_h2o_decode 36 layers x 8 KV heads of 2048 + 32 resident slots: one step is one
                   eviction cycle (32 decode steps adding H2O cumulative attention,
                   then top-B by cumulative score + foresight bonus and compaction);
@@ -475,6 +477,51 @@ def bench_h2o(args, w, dev):
     return w.n_seq * S / (ms * 1e-3), ms, config, roof, cpu, extra
 
 
+def bench_commit_multi(args, w, dev):
+    """Successive CommitKV commits: one step = every commit of the workload."""
+    import torch
+    from budgeted_retention_amd import pipelines, synth
+    inp = synth.make_commit_multi_inputs(w, dev)
+    calibrate_copy(args, dev)
+    for _ in range(args.warmup):
+        pipelines.run_commit_multi(w, inp)
+    torch.cuda.synchronize()
+    timer = pipelines.CallTimer()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pipelines.run_commit_multi(w, inp, timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part = {k: v / args.steps for k, v in timer.totals_ms().items()}
+    host = {k: round(v * 1e3 / args.steps, 3) for k, v in timer.host.items()}
+    C, N, L, Hkv, d, W, ps = w.commits, w.n_seq, w.n_layers, w.n_kv_heads, w.head_dim, w.window, w.page_size
+    G = w.n_q_heads // Hkv
+    rows, Ta, Tb, B = w.rows, w.t_pre, w.t_post, w.budget
+    lrows = N * Hkv
+    # per step (all commits): the deciding layer's K and V read once per effect call, every row's K
+    # read by the window score, page scores, the page list, and the kept pages gathered and written
+    ab = {"kvc_page_effect:pre": C * lrows * (2 * Ta * d * 2 + G * W * d * 2),
+          "kvc_page_effect:post": C * lrows * (2 * Tb * d * 2 + G * W * d * 2),
+          "kvc_page_retire": C * lrows * (2 * Tb * d * 2 + G * W * d * 2),
+          "kvc_score": C * rows * (Ta * d * 2 + G * W * d * 2 + Ta * 4),
+          "kvc_page_scores": C * (rows * Ta * 4 + N * (Ta // ps) * 4),
+          "kvc_select": C * N * ((Ta // ps) * 5 + (B // ps) * 4),
+          "kvc_compact_rerotate": C * rows * (2 * B * d * 2 * 2 + B * 4 * 2)}
+    path_calls = list(ab)
+    ms = sum(part[k] for k in path_calls)
+    dom = max(path_calls, key=lambda k: part[k])
+    roof = roofline(ab[dom], part[dom], dom, w.name)
+    config = {"workload": w.name, "n_seq": N, "layers": L, "kv_heads": Hkv, "q_heads": w.n_q_heads,
+              "head_dim": d, "commits": C, "turn": w.n_call, "observation": w.n_obs, "window": W,
+              "page": ps, "budget": B, "eta": w.eta, "decision_layer": w.layer, "parallelism": "none"}
+    extra = {"breakdown_ms": {k: round(part[k], 4) for k in path_calls},
+             "other_ms": {k: round(v, 4) for k, v in part.items() if k not in path_calls},
+             "host_ms": host, "calls": per_call_rates(ab, part),
+             "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}
+    # tokens: every commit compacts the sequence's pre-commit cache
+    return C * N * Ta / (ms * 1e-3), ms, config, roof, None, extra
+
+
 def calibrate_copy(args, dev):
     import torch
     if args.calibrate_copy:
@@ -507,6 +554,9 @@ def main():
     elif args.workload in synth.COMMIT_WORKLOADS:
         w = synth.COMMIT_WORKLOADS[args.workload]
         value, ms, config, roof, cpu, extra = bench_pipeline(args, w, dev, "commit")
+    elif args.workload in synth.COMMIT_MULTI_WORKLOADS:
+        w = synth.COMMIT_MULTI_WORKLOADS[args.workload]
+        value, ms, config, roof, cpu, extra = bench_commit_multi(args, w, dev)
     elif args.workload in synth.H2O_WORKLOADS:
         w = synth.H2O_WORKLOADS[args.workload]
         value, ms, config, roof, cpu, extra = bench_h2o(args, w, dev)
