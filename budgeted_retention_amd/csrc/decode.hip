@@ -57,6 +57,54 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
     return (h & 0x8000) ? -v : v;
 }
 
+// Lane exchanges inside a row of 16 lanes through DPP (no LDS traffic):
+// quad_perm [1,0,3,2] and [2,3,0,1], then half-row and row mirrors. After the
+// steps for N lanes every lane of each aligned group of N holds the group's
+// total (N = 2, 4, 8, 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if (N >= 2) v += dpp_f<0xB1>(v);
+    if (N >= 4) v += dpp_f<0x4E>(v);
+    if (N >= 8) v += dpp_f<0x141>(v);
+    if (N >= 16) v += dpp_f<0x140>(v);
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    if (N >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+    if (N >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+    if (N >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+    if (N >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+    return v;
+}
+
+// Exchanges across rows with gfx950's lane swaps: permlane16_swap of a value
+// with itself gives, between its two results, the value of every lane and of
+// the lane 16 away (xor 16); permlane32_swap likewise for xor 32. All lanes
+// of the wave must be active.
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -194,9 +242,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
             dot[g] = acc;
         }
 #pragma unroll
-        for (int off = 1; off < TPK; off <<= 1)
-#pragma unroll
-            for (int g = 0; g < GM; ++g) dot[g] += __shfl_xor(dot[g], off);
+        for (int g = 0; g < GM; ++g) dot[g] = group_sum<TPK>(dot[g]);
         const int e = it * KPI + kin;
         if (sub == 0) {
 #pragma unroll
@@ -232,8 +278,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         if (!LOW && a.logit && g < G && tid < cnt)
             a.logit[((size_t)r * G + g) * ((size_t)a.chunks_h * DEC_CHUNK) + k0 + tid] = v[g];
         float x = v[g];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+        x = xor32_max(xor16_max(group_max<16>(x)));
         if (lane == 0) s_w[wave][g] = x;
     }
     __syncthreads();
@@ -251,8 +296,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         const float pv = (v[g] > -INFINITY) ? __builtin_amdgcn_exp2f(v[g] - m[g]) : 0.f;
         s_p[g][tid] = pv;
         float x = pv;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+        x = xor32_sum(xor16_sum(group_sum<16>(x)));
         if (lane == 0) s_w[wave][g] = x;
     }
     __syncthreads();  // weights and partial sums ready
@@ -297,12 +341,15 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         }
     }
     // Sum over the wave's keys (lanes differing in the key bits), then over waves.
+    static_assert(TPK == 8 || TPK == 16, "key groups of 8 or 16 lanes");
 #pragma unroll
-    for (int off = TPK; off < 64; off <<= 1)
+    for (int g = 0; g < GM; ++g)
 #pragma unroll
-        for (int g = 0; g < GM; ++g)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[g][c] += __shfl_xor(acc[g][c], off);
+        for (int c = 0; c < 8; ++c) {
+            float x = acc[g][c];
+            if (TPK == 8) x += dpp_f<0x128>(x);   // row_ror:8 pairs lane i with i ^ 8
+            acc[g][c] = xor32_sum(xor16_sum(x));
+        }
     if (lane < TPK) {
 #pragma unroll
         for (int g = 0; g < GM; ++g)
