@@ -77,8 +77,10 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return (h & 0x8000) ? -v : v;
 }
 
+// Maximum over the TPT adjacent lanes of a token (any TPT up to 64; some
+// lanes of the wave may be inactive).
 template <int TPT>
-__device__ __forceinline__ float group_max(float v) {
+__device__ __forceinline__ float token_max(float v) {
 #pragma unroll
     for (int m = TPT / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
     return v;
@@ -394,8 +396,8 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
                 const float k2 = bf16_to_f32((uint16_t)(hi & 0xFFFF)), k3 = bf16_to_f32((uint16_t)(hi >> 16));
                 const float v0 = bf16_to_f32((uint16_t)(vv.x & 0xFFFF)), v1 = bf16_to_f32((uint16_t)(vv.x >> 16));
                 const float v2 = bf16_to_f32((uint16_t)(vv.y & 0xFFFF)), v3 = bf16_to_f32((uint16_t)(vv.y >> 16));
-                const float kmax = group_max<TPT>(fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3))));
-                const float vmax = group_max<TPT>(fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3))));
+                const float kmax = token_max<TPT>(fmaxf(fmaxf(fabsf(k0), fabsf(k1)), fmaxf(fabsf(k2), fabsf(k3))));
+                const float vmax = token_max<TPT>(fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3))));
                 const bool q4 = a.low_bits == 4;
                 const float qm = q4 ? 7.f : 127.f;
                 const uint16_t ksb = low_scale_bits(kmax, qm), vsb = low_scale_bits(vmax, qm);

@@ -57,54 +57,6 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
     return (h & 0x8000) ? -v : v;
 }
 
-// Lane exchanges inside a row of 16 lanes through DPP (no LDS traffic):
-// quad_perm [1,0,3,2] and [2,3,0,1], then half-row and row mirrors. After the
-// steps for N lanes every lane of each aligned group of N holds the group's
-// total (N = 2, 4, 8, 16).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-    if (N >= 2) v += dpp_f<0xB1>(v);
-    if (N >= 4) v += dpp_f<0x4E>(v);
-    if (N >= 8) v += dpp_f<0x141>(v);
-    if (N >= 16) v += dpp_f<0x140>(v);
-    return v;
-}
-
-template <int N>
-__device__ __forceinline__ float group_max(float v) {
-    if (N >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
-    if (N >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
-    if (N >= 8) v = fmaxf(v, dpp_f<0x141>(v));
-    if (N >= 16) v = fmaxf(v, dpp_f<0x140>(v));
-    return v;
-}
-
-// Exchanges across rows with gfx950's lane swaps: permlane16_swap of a value
-// with itself gives, between its two results, the value of every lane and of
-// the lane 16 away (xor 16); permlane32_swap likewise for xor 32. All lanes
-// of the wave must be active.
-__device__ __forceinline__ float xor16_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor16_max(float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll

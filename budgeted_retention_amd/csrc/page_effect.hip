@@ -41,6 +41,8 @@ static constexpr int PR_THREADS = 256;
 static constexpr int PR_PMAX = 16;      // largest page the retire kernel takes
 static constexpr int PR_BATCH = 8;      // candidates whose deletion terms are formed per launch
 static constexpr int PG_THREADS = 1024; // greedy walk: one workgroup per sequence
+static constexpr int PG_RPT = 4;        // query rows per walk thread: Hkv * G * W <= 4096
+static constexpr int GR = 80;           // Gram record per query row (see pr_gram)
 static constexpr int PO_CHUNK = 4096;   // keys per pe_out_mfma / pe_effect_mfma workgroup
 static constexpr int PM_THREADS = 256;  // four waves, each on its own 32-key tiles
 
@@ -67,6 +69,7 @@ struct PageWs {
     float *mm, *o, *accD, *alphaD;
     float *tD, *tA;   // [PR_BATCH][rows][QRP][D] and [PR_BATCH][rows][QRP]: one batch's deletion terms
     float *opart;     // [chunks][rows][QRP][D]: per-chunk partial window outputs
+    float *gram;      // [rows][QRP][GR]: inner products of one batch (pr_gram)
 };
 
 static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base, PageWs *w) {
@@ -79,6 +82,7 @@ static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base,
     const size_t s_tA = al256((size_t)PR_BATCH * g.rows_local * g.QRP * sizeof(float));
     const int64_t och = (kend + PO_CHUNK - 1) / PO_CHUNK;
     const size_t s_op = al256((size_t)och * g.rows_local * g.QRP * d->head_dim * sizeof(float));
+    const size_t s_gr = al256((size_t)g.rows_local * g.QRP * GR * sizeof(float));
     if (w) {
         char *p = reinterpret_cast<char *>(base);
         w->part = reinterpret_cast<float2 *>(p);
@@ -89,8 +93,9 @@ static size_t page_ws_layout(const kvc_dims *d, int W, int64_t kend, void *base,
         w->tD = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a);
         w->tA = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a + s_tD);
         w->opart = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA);
+        w->gram = reinterpret_cast<float *>(p + s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA + s_op);
     }
-    return s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA + s_op;
+    return s_part + s_mm + 2 * s_o + s_a + s_tD + s_tA + s_op + s_gr;
 }
 
 struct PeArgs {
@@ -481,12 +486,16 @@ __global__ void __launch_bounds__(PM_THREADS) pe_effect_mfma(PeArgs a, int chunk
 // workspace. The terms do not depend on the decisions, so all candidates of a
 // batch are formed in parallel.
 //
-// pr_greedy, one workgroup per sequence: walks the batch in order. The joint
-// deletion of the accepted set D plus candidate E has, per query row, the
-// vector accD_q + t_q(E) and weight alphaD_q + alpha_q(E) (Eq. 6 over the
-// union, summed page by page); its relative effect is maximised over the rows
-// of every KV head and compared with tau_joint; an accepted candidate is
-// added to accD / alphaD. D/8 threads own one query row, 8 dimensions each.
+// The walk works on inner products. With a_q the running deletion vector of
+// the accepted set and t_q(j) the batch's terms, the joint vector of the set
+// plus candidate j has squared norm |a_q|^2 + 2<a_q, t_q(j)> + |t_q(j)|^2, and
+// accepting j adds t_q(j) to a_q. pr_gram forms, for every query row, |a_q|^2,
+// <a_q, t_q(k)>, <t_q(j), t_q(k)> and |o_q| in parallel; pr_walk, one
+// workgroup per sequence, then walks the batch on those scalars: the joint
+// relative effect is maximised over the rows of every KV head and compared
+// with tau_joint, and an accepted candidate updates each row's |a|^2, <a, t>
+// and alpha. pr_accum adds the accepted terms to a_q and alpha_q for the next
+// batch.
 template <int D>
 __global__ void __launch_bounds__(PR_THREADS) pr_terms(PeArgs a, const int32_t *order, int n_cand, int c0, int nc,
                                                        float *tD, float *tA) {
@@ -559,41 +568,100 @@ __global__ void __launch_bounds__(PR_THREADS) pr_terms(PeArgs a, const int32_t *
     }
 }
 
+// Gram record of query row q (GR floats): [0] |a|^2, [1 + k] <a, t(k)>,
+// [9 + 8j + k] <t(j), t(k)>, [73] |o|. D/8 threads per query row.
 template <int D>
-__global__ void __launch_bounds__(PG_THREADS) pr_greedy(PeArgs a, const int32_t *order, int n_cand, int c0, int nc,
-                                                        int first, float tau_joint, const float *tD, const float *tA,
-                                                        float *accD, float *alphaD, uint8_t *accepted,
-                                                        float *joint_rel, int64_t rows_local) {
-    constexpr int TPP = D / 8;                 // threads per query row
-    constexpr int PPI = PG_THREADS / TPP;      // query rows per pass
-    extern __shared__ float s_onorm[];         // [Hkv * QR]
+__global__ void __launch_bounds__(PR_THREADS) pr_gram(PeArgs a, const int32_t *order, int n_cand, int c0, int nc,
+                                                      int first, const float *tD, const float *accD, float *gram,
+                                                      int64_t rows_local) {
+    constexpr int TPP = D / 8;
+    const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
+    const int64_t nrows = rows_local * QR;
+    const int64_t p = (int64_t)blockIdx.x * (PR_THREADS / TPP) + threadIdx.x / TPP;
+    const int sub = threadIdx.x % TPP;
+    const bool valid = p < nrows;  // every lane takes part in the lane exchanges below
+    const int64_t rr = valid ? p / QR : 0;
+    const int q = valid ? (int)(p % QR) : 0;
+    const int n = (int)(rr / a.Hkv);
+    const size_t row = (size_t)rr * QRP + q;
+    auto load8 = [&](const float *src, float (&x)[8]) {
+        const float4 u = *reinterpret_cast<const float4 *>(src), v = *reinterpret_cast<const float4 *>(src + 4);
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    };
+    float acc[8], o[8], t[PR_BATCH][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = o[e] = 0.f;
+    if (valid && !first) load8(accD + row * D + 8 * sub, acc);
+    if (valid) load8(a.o + row * D + 8 * sub, o);
+#pragma unroll
+    for (int j = 0; j < PR_BATCH; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[j][e] = 0.f;
+        if (valid && j < nc) {
+            const int page = order[(size_t)n * n_cand + c0 + j];
+            if (page >= 0 && page < a.n_pages) load8(tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub, t[j]);
+        }
+    }
+    auto dot = [&](const float (&x)[8], const float (&y)[8]) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2 = fmaf(x[e], y[e], s2);
+        return group_sum<TPP>(s2);
+    };
+    float *g = gram + row * GR;
+    const float aa = dot(acc, acc), oo = dot(o, o);
+    if (valid && sub == 0) {
+        g[0] = aa;
+        g[73] = sqrtf(oo);
+    }
+#pragma unroll
+    for (int k = 0; k < PR_BATCH; ++k) {
+        const float at = dot(acc, t[k]);
+        if (valid && sub == 0) g[1 + k] = at;
+#pragma unroll
+        for (int j = 0; j <= k; ++j) {
+            const float tt = dot(t[j], t[k]);
+            if (valid && sub == 0) {
+                g[9 + 8 * j + k] = tt;
+                g[9 + 8 * k + j] = tt;
+            }
+        }
+    }
+}
+
+// One workgroup per sequence; PG_RPT query rows per thread, kept in registers.
+__global__ void __launch_bounds__(PG_THREADS) pr_walk(PeArgs a, const int32_t *order, int n_cand, int c0, int nc,
+                                                      int first, float tau_joint, const float *tA,
+                                                      const float *alphaD, const float *gram, uint8_t *accepted,
+                                                      float *joint_rel, int64_t rows_local) {
     __shared__ float s_red[PG_THREADS / 64];
     __shared__ int s_accept;
     const int n = blockIdx.x;
-    const int tid = threadIdx.x, sub = tid % TPP;
+    const int tid = threadIdx.x;
     const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
     const int P = a.Hkv * QR;
-    // ||o_q|| of every query row of the sequence: D/8 threads per row, 16-byte loads
-    for (int p0 = 0; p0 < P; p0 += PPI) {
-        const int pq = p0 + tid / TPP;
-        float o2 = 0.f;
-        if (pq < P) {
-            const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
-            const float *o = a.o + ((size_t)rr * QRP + pq % QR) * D + 8 * sub;
-            const float4 x = *reinterpret_cast<const float4 *>(o), y = *reinterpret_cast<const float4 *>(o + 4);
-            o2 = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w + y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
-        }
+    float base[PG_RPT], cross[PG_RPT][PR_BATCH], alpha[PG_RPT], onorm[PG_RPT];
+    size_t rowi[PG_RPT];
+    int64_t rri[PG_RPT];
+    int qi[PG_RPT];
 #pragma unroll
-        for (int off = 1; off < TPP; off <<= 1) o2 += __shfl_xor(o2, off);
-        if (pq < P && sub == 0) s_onorm[pq] = sqrtf(o2);
+    for (int i = 0; i < PG_RPT; ++i) {
+        const int pq = tid + i * PG_THREADS;
+        const bool ok = pq < P;
+        rri[i] = (int64_t)n * a.Hkv + (ok ? pq / QR : 0);
+        qi[i] = ok ? pq % QR : 0;
+        rowi[i] = (size_t)rri[i] * QRP + qi[i];
+        const float *g = gram + rowi[i] * GR;
+        base[i] = ok ? g[0] : 0.f;
+        onorm[i] = ok ? g[73] : 0.f;
+        alpha[i] = (ok && !first) ? alphaD[rowi[i]] : 0.f;
+#pragma unroll
+        for (int k = 0; k < PR_BATCH; ++k) cross[i][k] = (ok && k < nc) ? g[1 + k] : 0.f;
     }
-    if (first) {  // clear the running sums of this sequence's rows
-        for (int64_t i = tid; i < (int64_t)a.Hkv * QRP * D; i += PG_THREADS)
-            accD[(size_t)n * a.Hkv * QRP * D + i] = 0.f;
-        for (int i = tid; i < a.Hkv * QRP; i += PG_THREADS) alphaD[(size_t)n * a.Hkv * QRP + i] = 0.f;
-    }
-    __syncthreads();
-    for (int j = 0; j < nc; ++j) {
+#pragma unroll
+    for (int j = 0; j < PR_BATCH; ++j) {
+        if (j >= nc) break;
         const int c = c0 + j;
         const int page = order[(size_t)n * n_cand + c];
         if (page < 0 || page >= a.n_pages) {
@@ -603,45 +671,19 @@ __global__ void __launch_bounds__(PG_THREADS) pr_greedy(PeArgs a, const int32_t 
             }
             continue;
         }
-        float worst = 0.f;
-        constexpr int U = 4;  // passes whose loads are issued together
-        for (int p0 = 0; p0 < P; p0 += U * PPI) {
-            float n2[U], alj[U];
+        float worst = 0.f, tj[PG_RPT];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int pq = p0 + u * PPI + tid / TPP;
-                n2[u] = 0.f;
-                alj[u] = 0.f;
-                if (pq < P) {
-                    const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
-                    const int q = pq % QR;
-                    const float *t = tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub;
-                    const float *acc = accD + ((size_t)rr * QRP + q) * D + 8 * sub;
-                    const float4 t0 = *reinterpret_cast<const float4 *>(t), t1 = *reinterpret_cast<const float4 *>(t + 4);
-                    const float4 a0 = *reinterpret_cast<const float4 *>(acc), a1 = *reinterpret_cast<const float4 *>(acc + 4);
-                    const float jv[8] = {a0.x + t0.x, a0.y + t0.y, a0.z + t0.z, a0.w + t0.w,
-                                         a1.x + t1.x, a1.y + t1.y, a1.z + t1.z, a1.w + t1.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) n2[u] = fmaf(jv[e], jv[e], n2[u]);
-                    alj[u] = alphaD[rr * QRP + q] + tA[((size_t)j * rows_local + rr) * QRP + q];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int off = 1; off < TPP; off <<= 1) n2[u] += __shfl_xor(n2[u], off);
-                const int pq = p0 + u * PPI + tid / TPP;
-                if (pq < P) {
-                    const float num = sqrtf(n2[u]), onorm = s_onorm[pq];
-                    float rel = 0.f;
-                    if (num > 0.f)
-                        rel = (1.f - alj[u] > 0.f && onorm > 0.f) ? num / ((1.f - alj[u]) * onorm) : INFINITY;
-                    worst = fmaxf(worst, rel);
-                }
-            }
+        for (int i = 0; i < PG_RPT; ++i) {
+            tj[i] = 0.f;
+            if (tid + i * PG_THREADS >= P) continue;
+            tj[i] = tA[((size_t)j * rows_local + rri[i]) * QRP + qi[i]];
+            const float num2 = base[i] + 2.f * cross[i][j] + gram[rowi[i] * GR + 9 + 9 * j];
+            const float num = sqrtf(fmaxf(num2, 0.f)), alj = alpha[i] + tj[i];
+            float rel = 0.f;
+            if (num > 0.f) rel = (1.f - alj > 0.f && onorm[i] > 0.f) ? num / ((1.f - alj) * onorm[i]) : INFINITY;
+            worst = fmaxf(worst, rel);
         }
-        float v = worst;
-        for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+        float v = xor32_max(xor16_max(group_max<16>(worst)));
         if ((tid & 63) == 0) s_red[tid >> 6] = v;
         __syncthreads();
         if (tid == 0) {
@@ -653,20 +695,48 @@ __global__ void __launch_bounds__(PG_THREADS) pr_greedy(PeArgs a, const int32_t 
         }
         __syncthreads();
         if (s_accept) {
-            for (int p0 = 0; p0 < P; p0 += PPI) {
-                const int pq = p0 + tid / TPP;
-                if (pq >= P) continue;
-                const int64_t rr = (int64_t)n * a.Hkv + pq / QR;
-                const int q = pq % QR;
-                const float *t = tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub;
-                float *acc = accD + ((size_t)rr * QRP + q) * D + 8 * sub;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += t[e];
-                if (sub == 0) alphaD[rr * QRP + q] += tA[((size_t)j * rows_local + rr) * QRP + q];
+            for (int i = 0; i < PG_RPT; ++i) {
+                if (tid + i * PG_THREADS >= P) continue;
+                const float *gj = gram + rowi[i] * GR + 9 + 8 * j;
+                base[i] += 2.f * cross[i][j] + gj[j];
+                alpha[i] += tj[i];
+#pragma unroll
+                for (int k = 0; k < PR_BATCH; ++k) cross[i][k] += gj[k];
             }
         }
-        __syncthreads();
     }
+}
+
+// a_q += sum of the accepted candidates' t_q, alpha_q likewise (a_q = 0 first).
+template <int D>
+__global__ void __launch_bounds__(PR_THREADS) pr_accum(PeArgs a, const int32_t *order, int n_cand, int c0, int nc,
+                                                       int first, const uint8_t *accepted, const float *tD,
+                                                       const float *tA, float *accD, float *alphaD,
+                                                       int64_t rows_local) {
+    constexpr int TPP = D / 8;
+    const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
+    const int64_t p = (int64_t)blockIdx.x * (PR_THREADS / TPP) + threadIdx.x / TPP;
+    if (p >= rows_local * QR) return;
+    const int sub = threadIdx.x % TPP;
+    const int64_t rr = p / QR;
+    const int q = (int)(p % QR);
+    const int n = (int)(rr / a.Hkv);
+    const size_t row = (size_t)rr * QRP + q;
+    float x[8], al = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = first ? 0.f : accD[row * D + 8 * sub + e];
+    if (!first) al = alphaD[row];
+    for (int j = 0; j < nc; ++j) {
+        if (!accepted[(size_t)n * n_cand + c0 + j]) continue;
+        const float *t = tD + (((size_t)j * rows_local + rr) * QRP + q) * D + 8 * sub;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += t[e];
+        al += tA[((size_t)j * rows_local + rr) * QRP + q];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accD[row * D + 8 * sub + e] = x[e];
+    if (sub == 0) alphaD[row] = al;
 }
 
 static int pe_common_checks(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
@@ -869,21 +939,33 @@ extern "C" int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16
     hipStream_t s = as_stream(stream);
     if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
     const PageGeom g = page_geom(dims, W, q_first + W);
-    const size_t lds = (size_t)dims->n_kv_heads * g.QR * sizeof(float);
-    if (lds > 64 * 1024) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_retire: %d KV heads x %d rows too many", dims->n_kv_heads, g.QR);
+    if ((int64_t)dims->n_kv_heads * g.QR > (int64_t)PG_THREADS * PG_RPT)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_page_retire: %d KV heads x %d rows too many", dims->n_kv_heads, g.QR);
+    const int64_t rows_q = g.rows_local * g.QR;
+    const int64_t qblocks = (rows_q + PR_THREADS / (dims->head_dim / 8) - 1) / (PR_THREADS / (dims->head_dim / 8));
+    if (qblocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_retire: grid too large");
     for (int c0 = 0; c0 < n_cand; c0 += PR_BATCH) {
         const int nc = n_cand - c0 < PR_BATCH ? n_cand - c0 : PR_BATCH;
-        const dim3 tgrid((unsigned)(g.rows_local * nc));
+        const int first = c0 == 0, last = c0 + PR_BATCH >= n_cand;
+        const dim3 tgrid((unsigned)(g.rows_local * nc)), qgrid((unsigned)qblocks);
         if (dims->head_dim == 128) {
             pr_terms<128><<<tgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, w.tD, w.tA);
-            pr_greedy<128><<<dim3(dims->n_seq), dim3(PG_THREADS), lds, s>>>(
-                a, order, n_cand, c0, nc, c0 == 0, tau_joint, w.tD, w.tA, w.accD, w.alphaD, accepted, joint_rel,
-                g.rows_local);
+            pr_gram<128><<<qgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, first, w.tD, w.accD, w.gram,
+                                                             g.rows_local);
         } else {
             pr_terms<64><<<tgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, w.tD, w.tA);
-            pr_greedy<64><<<dim3(dims->n_seq), dim3(PG_THREADS), lds, s>>>(
-                a, order, n_cand, c0, nc, c0 == 0, tau_joint, w.tD, w.tA, w.accD, w.alphaD, accepted, joint_rel,
-                g.rows_local);
+            pr_gram<64><<<qgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, first, w.tD, w.accD, w.gram,
+                                                            g.rows_local);
+        }
+        pr_walk<<<dim3(dims->n_seq), dim3(PG_THREADS), 0, s>>>(a, order, n_cand, c0, nc, first, tau_joint, w.tA,
+                                                                w.alphaD, w.gram, accepted, joint_rel, g.rows_local);
+        if (!last) {  // the next batch starts from the accepted set
+            if (dims->head_dim == 128)
+                pr_accum<128><<<qgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, first, accepted, w.tD,
+                                                                  w.tA, w.accD, w.alphaD, g.rows_local);
+            else
+                pr_accum<64><<<qgrid, dim3(PR_THREADS), 0, s>>>(a, order, n_cand, c0, nc, first, accepted, w.tD,
+                                                                 w.tA, w.accD, w.alphaD, g.rows_local);
         }
         if ((st = check_launch("kvc_page_retire")) != KVC_OK) return st;
     }
