@@ -173,3 +173,48 @@ def test_tiered_compaction(renumber_base, d, low_bits):
         assert np.abs(gcv.astype(int) - cv.astype(int)).max() <= 1
         np.testing.assert_array_equal(Vs[r].cpu().numpy().view(np.uint16)[: Lw.size], sv)
         np.testing.assert_array_equal(pq[r].cpu().numpy()[: Lw.size], op[Lw])
+
+
+@pytest.mark.parametrize("low_bits", [8, 4])
+def test_tiered_compaction_zero_and_tiny_rows(low_bits):
+    """PASK Appendix B.5 edge cases: an all-zero row gets zero codes and unit
+    scale; a row whose largest magnitude is tiny gets the smallest positive
+    fp16 scale (2^-24) and codes clipped to the range."""
+    from budgeted_retention_amd import kvc
+    rows, T, d = 2, 64, 128
+    rng = np.random.default_rng(low_bits)
+    K = rng.standard_normal((rows, T, d))
+    V = rng.standard_normal((rows, T, d))
+    K[:, 5], V[:, 5] = 0.0, 0.0                     # zero rows
+    K[:, 9], V[:, 9] = 1e-9, -3e-9                  # far below 2^-24 * qmax
+    Kb, Vb = numfmt.f64_to_bf16_bits(K), numfmt.f64_to_bf16_bits(V)
+    kept = np.tile(np.arange(16, dtype=np.int32), (rows, 1))
+    n = np.full(rows, 16, np.int32)
+    act = np.ones((rows, 16), np.uint8)             # everything to the low tier
+    dims = kvc.make_dims(1, 1, rows, rows, d, T)
+    cb, qmax = (d, 127) if low_bits == 8 else (d // 2, 7)
+    dev = "cuda"
+    Ko = torch.zeros((rows, 16, d), dtype=torch.bfloat16, device=dev)
+    Kq = torch.zeros((rows, 16, cb), dtype=torch.int8, device=dev)
+    Vq = torch.zeros_like(Kq)
+    Ks = torch.zeros((rows, 16), dtype=torch.int16, device=dev)
+    Vs = torch.zeros_like(Ks)
+    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
+    nl = torch.zeros(rows, dtype=torch.int32, device=dev)
+    out = kvc.CompactOut(16, Ko, torch.zeros_like(Ko), None, nh, torch.from_numpy(act).to(dev), Kq, Vq, Ks, Vs,
+                         None, nl, low_bits=low_bits)
+    kvc.kvc_compact_rerotate(dims, torch.from_numpy(Kb.view(np.int16)).view(torch.bfloat16).to(dev),
+                             torch.from_numpy(Vb.view(np.int16)).view(torch.bfloat16).to(dev), None,
+                             torch.from_numpy(kept).to(dev), 16, torch.from_numpy(n).to(dev), -1, 1e4, out)
+    torch.cuda.synchronize()
+    unpack = (lambda x: x.astype(np.int8)) if low_bits == 8 else (lambda x: o_quant.unpack_nibbles(x.view(np.uint8), d))
+    for r in range(rows):
+        assert nl[r].item() == 16 and nh[r].item() == 0
+        for X, q, sc in ((Kb, Kq, Ks), (Vb, Vq, Vs)):
+            want_c, want_s = o_quant.quantize_rows(numfmt.bf16_bits_to_f64(X[r, :16]), qmax)
+            got_c = unpack(q[r].cpu().numpy())
+            got_s = sc[r].cpu().numpy().view(np.uint16)
+            np.testing.assert_array_equal(got_s, want_s)
+            assert np.abs(got_c.astype(int) - want_c.astype(int)).max() <= 1
+            assert got_s[5] == 0x3C00 and not got_c[5].any()
+            assert got_s[9] == 1 and np.abs(got_c[9]).max() <= qmax

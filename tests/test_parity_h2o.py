@@ -191,3 +191,20 @@ def test_pace_h2o_decode_shape_one_cycle_sampled_rows():
     import dataclasses
     ws = dataclasses.replace(w, n_layers=1, n_kv_heads=len(sample), n_q_heads=len(sample) * G)
     assert _oracle_cycles(ws, small, 1, rec_s, final_s) == 0
+
+
+def test_decode_h2o_counts_above_the_pool_are_clamped():
+    from budgeted_retention_amd import kvc
+    rows, S, d = 2, 300, 64
+    dims = kvc.make_dims(1, 1, rows, 2 * rows, d, S)
+    K = synth.normal_bf16((rows, S, d), 91, "cuda")
+    V = synth.normal_bf16((rows, S, d), 92, "cuda")
+    q = synth.normal_bf16((1, 1, 2 * rows, d), 93, "cuda")
+    acc = torch.zeros((rows, S), dtype=torch.float32, device="cuda")
+    n_h = torch.tensor([S + 77, S], dtype=torch.int32, device="cuda")
+    o, lse, o2, lse2 = _h2o_call(dims, q, K, V, n_h, S, acc)
+    a = acc.cpu().numpy()
+    assert np.isfinite(a).all()
+    for r in range(rows):
+        want = h2o.attention_mass(tl.f64(q)[0, 0, 2 * r:2 * r + 2], tl.f64(K)[r])
+        np.testing.assert_allclose(a[r], want, rtol=MASS_RTOL, atol=MASS_ATOL)

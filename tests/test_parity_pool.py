@@ -61,3 +61,14 @@ def test_pooled_selection_on_the_tiny_workload():
         tot, prot = o_policy.totals_and_protection(p, None, z, z.astype(np.uint8), 0, w.n_sink, w.n_recent)
         o_kept, _ = o_select.select_top_b(tot, prot, B)
         tl.check_kept(kept[r].cpu().numpy(), int(nk[r]), o_kept, tot, prot, B)
+
+
+def test_pool_single_token_rows():
+    from budgeted_retention_amd import kvc
+    s = torch.tensor([[3.5], [-1.0]], dtype=torch.float32, device="cuda")
+    dims = kvc.make_dims(1, 1, 2, 2, 64, 1)
+    for mode in (kvc.KVC_POOL_MAX, kvc.KVC_POOL_AVG):
+        out = torch.empty_like(s)
+        kvc.kvc_pool_scores(dims, s, 63, mode, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, s)

@@ -259,3 +259,20 @@ def test_qwen3_8b_100k_shape_two_compactions_sampled_rows():
         _close_keys(res2["K"][r], oK, oR)
         old = k2 < B
         assert np.all(oq[old] == o1[r][4][k2[old]]) and np.all(oq[~old] == p1[k2[~old]])
+
+
+def test_empty_rows_and_clamped_counts():
+    """A row that keeps nothing writes nothing; a kept count above the list or
+    the output room is clamped; references follow the same slots."""
+    rows, T, d = 3, 500, 64
+    K = tl.bits(synth.normal_bf16((rows, T, d), 81))
+    V = tl.bits(synth.normal_bf16((rows, T, d), 82))
+    pos = np.tile(np.arange(T), (rows, 1)) + 100
+    kept = np.tile(np.arange(0, 400, 2, dtype=np.int32), (rows, 1))      # 200 listed per row
+    n = np.array([0, 200, 10_000], np.int32)                              # empty, full, above the list
+    res = _gpu(K, V, pos, kept, n, 0, 1e4, out_stride=150, h_base=np.array([0, 0, 20], np.int32))
+    assert res["n_h"].tolist() == [0, 150, 150]
+    assert np.all(res["pref"][0] == -7)                                   # nothing written
+    _check_row(res, 1, K, V, pos, kept[1, :150].astype(np.int64), 0, 1e4, h0=0)
+    _check_row(res, 2, K, V, pos, kept[2, :130].astype(np.int64), 0, 1e4, h0=20)
+    assert np.all(res["pref"][2][:20] == -7)
