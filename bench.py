@@ -256,7 +256,30 @@ def bench_compaction(args, w, dev):
              "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}
     if not per_layer and w.renumber_base >= 0:
         extra["ref_store"] = bench_ref_store(args, w, dims, views[0][0], views[0][1], kept, n_kept, Ko, Vo, po, dev)
+        extra["pool"] = bench_pool(args, dims, scores)
     return value, ms, config, roof, cpu, extra
+
+
+def bench_pool(args, dims, scores):
+    """Max pooling (kernel 7) of the session's window scores, timed on its own:
+    the optional smoothing step between scoring and selection."""
+    import torch
+    from budgeted_retention_amd import kvc
+    pooled = torch.empty_like(scores)
+    for _ in range(max(1, args.warmup)):
+        kvc.kvc_pool_scores(dims, scores, 7, kvc.KVC_POOL_MAX, pooled)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        kvc.kvc_pool_scores(dims, scores, 7, kvc.KVC_POOL_MAX, pooled)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    nbytes = scores.numel() * 8   # each score read once and written once
+    return {"ms": round(ms, 4), "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes,
+            "kernel": 7, "mode": "max"}
 
 
 def bench_ref_store(args, w, dims, K, V, kept, n_kept, Ko, Vo, po, dev):
