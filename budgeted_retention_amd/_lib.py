@@ -94,6 +94,8 @@ PROTOTYPES = {
                                        c_void_p, c_int32, c_void_p, c_void_p]),
     "kvc_host_commit_protect": (ctypes.c_int, [c_void_p, c_void_p, c_int32, c_int32, c_double, c_int32,
                                                c_void_p, c_void_p]),
+    "kvc_host_pace_renumber": (ctypes.c_int, [c_int64, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                              c_void_p]),
     "kvc_host_pask_costs": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "kvc_host_pask_control": (ctypes.c_int, [ctypes.POINTER(KvcPaskTable), c_void_p, c_double, c_double,
                                              c_void_p, c_int32, c_int32, c_void_p, c_void_p]),

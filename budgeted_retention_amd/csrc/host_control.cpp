@@ -180,3 +180,21 @@ extern "C" int kvc_host_commit_protect(const float *R_minus, const int32_t *page
     *n_protected = n;
     return KVC_OK;
 }
+
+extern "C" int kvc_host_pace_renumber(int64_t m_next, int64_t shift, int32_t resident, int32_t limit,
+                                      int32_t headroom, int32_t b_max, int32_t *renumber, int64_t *new_shift) {
+    if (!renumber || !new_shift || resident < 0 || limit <= 0 || headroom < 0 || b_max < 0 || m_next < 0)
+        return fail(KVC_ERR_ARG, "kvc_host_pace_renumber: bad arguments");
+    if ((int64_t)limit <= (int64_t)b_max + headroom)
+        return fail(KVC_ERR_ARG, "kvc_host_pace_renumber: limit %d must exceed B_max %d + headroom %d", limit, b_max,
+                    headroom);
+    if (resident > b_max) return fail(KVC_ERR_ARG, "kvc_host_pace_renumber: %d resident > B_max %d", resident, b_max);
+    if (m_next - shift + headroom > (int64_t)limit) {
+        *renumber = 1;
+        *new_shift = m_next - resident;
+    } else {
+        *renumber = 0;
+        *new_shift = shift;
+    }
+    return KVC_OK;
+}

@@ -319,3 +319,12 @@ def kvc_host_commit_protect(R_minus, page_tokens, budget, eta, max_pages=16):
         _np_ptr(Rm, np.float32), _np_ptr(pt, np.int32), Rm.size, budget, float(eta), max_pages,
         _np_ptr(out, np.uint8), ctypes.addressof(n)))
     return out[:Rm.size], n.value
+
+
+def kvc_host_pace_renumber(m_next, shift, resident, limit, headroom, b_max):
+    """Returns (renumber bool, new_shift)."""
+    ren = ctypes.c_int32(0)
+    sh = ctypes.c_int64(0)
+    _lib.check(_lib.load().kvc_host_pace_renumber(m_next, shift, resident, limit, headroom, b_max,
+                                                   ctypes.addressof(ren), ctypes.addressof(sh)))
+    return bool(ren.value), sh.value

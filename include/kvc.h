@@ -480,6 +480,22 @@ int kvc_host_commit_protect(const float *R_minus, const int32_t *page_tokens, in
                             int32_t budget, double eta, int32_t max_pages, uint8_t *protect,
                             int32_t *n_protected);
 
+/*
+ * Bounded positions (PACE §3.2, Renumbering and "Choosing L"), on the host.
+ * Called after an eviction that leaves `resident` tokens per row, with
+ * m_next the logical position of the next token and `shift` the sequence's
+ * current shift (next physical position m_next - shift).
+ *   KVC_ERR_ARG unless limit > b_max + headroom (b_max: the largest resident
+ *   row, budget plus eviction interval; headroom: the most tokens appended
+ *   between two checks) and resident <= b_max.
+ *   *renumber = 1 when m_next - shift + headroom > limit: renumber the
+ *   resident rows to 0..resident-1 (kvc_compact_rerotate with renumber_base
+ *   0) and continue at physical position `resident`: *new_shift =
+ *   m_next - resident. Otherwise *renumber = 0, *new_shift = shift.
+ */
+int kvc_host_pace_renumber(int64_t m_next, int64_t shift, int32_t resident, int32_t limit, int32_t headroom,
+                           int32_t b_max, int32_t *renumber, int64_t *new_shift);
+
 #ifdef __cplusplus
 }
 #endif

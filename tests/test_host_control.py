@@ -76,3 +76,27 @@ def test_commit_protection_matches_oracle_and_the_page_budget():
         want = o_pe.protect_pending(Rm.astype(np.float64), tok, B, eta, 16)
         np.testing.assert_array_equal(np.flatnonzero(got), want)
         assert k == want.size <= 16 and tok[want].sum() <= int(np.floor(eta * B))
+
+
+def test_pace_renumber_matches_oracle_and_keeps_positions_below_the_limit():
+    from oracle import positions
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        L = int(rng.choice([4096, 8192, 16384]))
+        H = int(rng.integers(0, 4097))
+        bmax = int(rng.integers(1, max(2, L - H)))
+        if not positions.admissible(L, bmax, H):
+            with pytest.raises(RuntimeError):
+                kvc.kvc_host_pace_renumber(10, 0, 1, L, H, bmax)
+            continue
+        res = int(rng.integers(0, bmax + 1))
+        shift = int(rng.integers(0, 10 ** 6))
+        m = shift + int(rng.integers(res, L + 1))
+        assert kvc.kvc_host_pace_renumber(m, shift, res, L, H, bmax) == positions.after_eviction(m, shift, res, L, H)
+    # a session driven by the native rule never writes a position >= L
+    shift, m, top = 0, 0, -1
+    while m < 300_000:
+        top = max(top, m + 2000 - 1 - shift)
+        m += 2000
+        ren, shift = kvc.kvc_host_pace_renumber(m, shift, 2048, 8192, 4096, 2048 + 64)
+    assert top < 8192
