@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--workload", default="qwen3_8b_100k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="scratch written before every timed step so no step starts from cached data "
+                         "(the 256 MB memory-side cache); 0 disables it")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), so that HBM "
                          "counters can be scaled against a transfer of known size")
@@ -69,6 +72,35 @@ def kernel_source_hash():
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_bandwidth(dev, mib=2048):
+    """Device-to-device copy rate on this machine (bytes read + written per second)."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * n * 2 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return round(gbs, 1)
 
 
 def cpu_cores():
@@ -212,6 +244,7 @@ def bench_compaction(args, w, dev):
                 ev[-1].record()
 
     calibrate_copy(args, dev)
+    flush = torch.empty(max(1, args.flush_mb) * (1 << 18), dtype=torch.float32, device=dev) if args.flush_mb else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -219,18 +252,29 @@ def bench_compaction(args, w, dev):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(k))   # outside the step's events
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    per_step = []
     part = {n: 0.0 for n in names}
     for ev in evs:
+        one = {n: 0.0 for n in names}
         for c in range(len(chunks)):
             for i, n in enumerate(names):
-                part[n] += ev[5 * c + i].elapsed_time(ev[5 * c + i + 1])
+                one[n] += ev[5 * c + i].elapsed_time(ev[5 * c + i + 1])
+        per_step.append(one)
+        for n in names:
+            part[n] += one[n]
     part = {n: v / args.steps for n, v in part.items()}
+    path_sums = sorted(o["kvc_score"] + o["kvc_select"] + o["kvc_compact_rerotate"] for o in per_step)
+    median_ms = path_sums[len(path_sums) // 2] if len(path_sums) % 2 else \
+        0.5 * (path_sums[len(path_sums) // 2 - 1] + path_sums[len(path_sums) // 2])
     if not (n_kept == B).all():
         raise SystemExit("bench: a row kept a number of tokens other than the budget")
-    ms = part["kvc_score"] + part["kvc_select"] + part["kvc_compact_rerotate"]
+    mean_ms = part["kvc_score"] + part["kvc_select"] + part["kvc_compact_rerotate"]
+    ms = median_ms
     ab = compaction_bytes(w.rows, T, d, w.group, W, B)
     path_calls = names[:3]
     dom = max(path_calls, key=lambda n: part[n])
@@ -244,12 +288,26 @@ def bench_compaction(args, w, dev):
                "kind": "oracle",
                "sample": f"{done} of {w.rows} (layer, KV head) rows of one {T}-token session, float64 numpy "
                          f"oracle (score+select+gather/re-rotate), {spent:.1f} s of oracle time scaled to "
-                         f"the whole session"}
+                         f"the whole session",
+               "cpu_model": cpu_model()}
+        try:   # the same oracle on one core, on a smaller sample
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                d1, s1 = cpu_compaction_rows(inp.K, inp.V, inp.Q_obs, w.group, W, T, B, inp.tags,
+                                             oracle_bonus(inp.spans.steps_ahead), w.n_sink, w.n_recent,
+                                             w.renumber_base, w.rope_base, w.rows, args.cpu_seconds / 3, L, Hkv)
+            cpu["value_1core"] = T * N * (d1 / w.rows) / s1
+        except ImportError:
+            pass
     value = N * T / (ms * 1e-3)
     config = {"workload": w.name, "n_seq": N, "layers": L, "kv_heads": Hkv, "q_heads": Hq, "head_dim": d,
               "tokens": T, "window": W, "budget": B, "sink": w.n_sink, "recent": w.n_recent,
               "rope_base": w.rope_base, "layers_per_call": Lc, "parallelism": "none"}
+    copy_gbs = copy_bandwidth(dev)
     extra = {"hbm_frac_path": round(ab["path"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "ms_mean": round(mean_ms, 4), "timing": f"median of {args.steps} steps, each after writing "
+             f"{args.flush_mb} MiB of scratch",
+             "copy_GB_s": copy_gbs, "roofline_frac_of_copy": round(roof["achieved"] / copy_gbs, 4),
              "breakdown_ms": {n: round(part[n], 4) for n in path_calls},
              "decode_ms": round(part["kvc_decode_attn"], 4),
              "calls": per_call_rates(ab, part),
