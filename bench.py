@@ -177,6 +177,35 @@ def cpu_compaction_rows(K, V, Q, G, W, T, B, tags, bonus_tbl, n_sink, n_recent, 
     return done, spent
 
 
+def oracle_call_times(w, budget_s):
+    """The float64 oracle's time for the session's decode attention over the
+    compacted cache and for score pooling (kernel 7), measured on a prefix of
+    rows of seeded inputs of the same shapes and scaled to all rows (ms)."""
+    import numpy as np
+    from oracle import decode as o_decode, score as o_score
+    rng = np.random.default_rng(1)
+    G, d, B, T = w.group, w.head_dim, w.budget, w.n_tokens
+    out = {}
+    done, spent = 0, 0.0
+    while spent < budget_s and done < w.rows:
+        K, V, q = rng.standard_normal((B, d)), rng.standard_normal((B, d)), rng.standard_normal((G, d))
+        t0 = time.perf_counter()
+        for g in range(G):
+            o_decode.decode_head(q[g], K, V)
+        spent += time.perf_counter() - t0
+        done += 1
+    out["kvc_decode_attn"] = {"cpu_ms": round(spent / done * w.rows * 1e3, 2), "rows_sampled": done}
+    done, spent = 0, 0.0
+    while spent < budget_s and done < w.rows:
+        sc = rng.gamma(0.5, 1.0, T)
+        t0 = time.perf_counter()
+        o_score.pool_scores(sc, 7, "max")
+        spent += time.perf_counter() - t0
+        done += 1
+    out["kvc_pool_scores"] = {"cpu_ms": round(spent / done * w.rows * 1e3, 2), "rows_sampled": done}
+    return out
+
+
 def oracle_bonus(steps_ahead):
     import numpy as np
     from oracle import policy as o_policy
@@ -299,6 +328,7 @@ def bench_compaction(args, w, dev):
             cpu["value_1core"] = T * N * (d1 / w.rows) / s1
         except ImportError:
             pass
+        cpu["calls"] = oracle_call_times(w, args.cpu_seconds / 5)
     value = N * T / (ms * 1e-3)
     config = {"workload": w.name, "n_seq": N, "layers": L, "kv_heads": Hkv, "q_heads": Hq, "head_dim": d,
               "tokens": T, "window": W, "budget": B, "sink": w.n_sink, "recent": w.n_recent,
