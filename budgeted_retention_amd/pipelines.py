@@ -202,10 +202,15 @@ def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
     slots per row: each cycle the engine appends E new tokens (score 0, no
     tag, no reference), E decode steps add their attention to the slots'
     cumulative scores, then the rows are evicted back to B slots by cumulative
-    score + foresight bonus (per-slot tags) and compacted with positions kept;
-    scores, tags and the reference store move with the slots. Two slot pools
-    alternate. With `record`, returns per cycle the scores before eviction and
-    the kept lists, plus the final pool."""
+    score + foresight bonus (per-slot tags) and compacted; scores, tags and
+    the reference store move with the slots. Positions are kept unless the
+    workload bounds them (w.limit = L > 0, PACE §3.2): after each eviction the
+    host rule (kvc_host_pace_renumber, headroom E) decides whether this
+    compaction renumbers the resident rows to 0..B-1, re-deriving the keys
+    from the reference store, and the sequence's shift advances so new tokens
+    continue at B. Two slot pools alternate. With `record`, returns per cycle
+    the scores before eviction, the kept lists and the renumber decisions,
+    plus the final pool."""
     t = timer or _null_timer
     N, L, Hkv, Hq, d = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
     rows, S, B, E = w.rows, w.slots, w.budget, w.interval
@@ -225,7 +230,8 @@ def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
     vals = [0.0] + [kvc.kvc_foresight_bonus(sigma, lam, s) for s in inp.steps_ahead]
     bonus = torch.tensor(vals, dtype=torch.float32, device=dev).reshape(-1, 1)
     nh = [torch.full((rows,), B + e + 1, dtype=torch.int32, device=dev) for e in range(E)]
-    new_pos = int(inp.pos[:, B:].min().item())
+    new_pos = int(inp.pos[:, B:].min().item())   # logical position of the first appended token
+    shift = 0
     ar = torch.arange(E, dtype=torch.int32, device=dev)
     o = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(1, kvc.kvc_decode_h2o_workspace_bytes(dims, S)), dtype=torch.uint8, device=dev)
@@ -236,7 +242,7 @@ def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
         with t("append"):
             cur["K"][:, B:] = inp.K_new[c]
             cur["V"][:, B:] = inp.V_new[c]
-            cur["pos"][:, B:] = new_pos + c * E + ar
+            cur["pos"][:, B:] = new_pos + c * E - shift + ar
             cur["acc"][:, B:] = 0.0
             cur["tags"][:, B:] = 0
             cur["pr"][:, B:] = -1
@@ -251,10 +257,14 @@ def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
         out = kvc.CompactOut(S, nxt["K"], nxt["V"], nxt["pos"], None, K_ref=cur["Kr"], p_ref=cur["pr"],
                              K_ref_out=nxt["Kr"], p_ref_out=nxt["pr"], score_in=cur["acc"],
                              score_out=nxt["acc"], tag_in=cur["tags"], tag_out=nxt["tags"])
+        renumber = False
+        if w.limit:
+            renumber, shift = kvc.kvc_host_pace_renumber(new_pos + (c + 1) * E, shift, B, w.limit, E, B + E)
         with t("kvc_compact_rerotate"):
-            kvc.kvc_compact_rerotate(dims, cur["K"], cur["V"], cur["pos"], kept, B, nk, -1, w.rope_base, out)
+            kvc.kvc_compact_rerotate(dims, cur["K"], cur["V"], cur["pos"], kept, B, nk, 0 if renumber else -1,
+                                     w.rope_base, out)
         if record:
-            rec[-1].update(kept=kept.clone(), n_kept=nk.clone())
+            rec[-1].update(kept=kept.clone(), n_kept=nk.clone(), renumber=renumber)
         cur, nxt = nxt, cur
     return {"cycles": rec, "final": cur, "o": o}
 

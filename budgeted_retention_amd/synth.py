@@ -469,6 +469,7 @@ class H2OWorkload:
     key_sigma: float = 0.5       # per-slot key scale ~ lognormal(0, key_sigma): uneven attention
     rope_base: float = 1e6
     seed: int = 20261206
+    limit: int = 0               # bounded positions: physical positions stay below L (0: positions kept)
 
     @property
     def rows(self):
@@ -487,6 +488,11 @@ H2O_WORKLOADS = {
     "pace_h2o_decode": H2OWorkload(),
     "h2o_small": H2OWorkload("h2o_small", n_layers=2, n_kv_heads=2, n_q_heads=8, head_dim=64, budget=96,
                              interval=8, n_recent=8, n_spans=3, span_slots=6, seed=20261216),
+    # PACE's bounded positions on top: L = 8,192, renumbered with the reference store
+    "pace_h2o_bounded": H2OWorkload("pace_h2o_bounded", limit=8192),
+    "h2o_small_bounded": H2OWorkload("h2o_small_bounded", n_layers=2, n_kv_heads=2, n_q_heads=8, head_dim=64,
+                                     budget=96, interval=8, n_recent=8, n_spans=3, span_slots=6, seed=20261226,
+                                     limit=128),
 }
 
 
@@ -517,8 +523,9 @@ def make_h2o_inputs(w: H2OWorkload, cycles, device="cpu") -> H2OInputs:
     K_new = (normal_bf16((cycles, rows, E, d), s + 4, device).float() * sn).to(torch.bfloat16)
     V_new = normal_bf16((cycles, rows, E, d), s + 5, device)
     rng = np.random.default_rng(w.seed + 37)
-    pos = np.stack([np.sort(rng.choice(8 * S, B, replace=False)) for _ in range(rows)]) + 16
-    pos = np.concatenate([pos, np.tile(np.arange(8 * S + 16, 8 * S + 16 + E), (rows, 1))], axis=1)
+    span = w.limit - 2 * E - 16 if w.limit else 8 * S     # history positions below the limit when bounded
+    pos = np.stack([np.sort(rng.choice(span, B, replace=False)) for _ in range(rows)]) + 16
+    pos = np.concatenate([pos, np.tile(np.arange(span + 16, span + 16 + E), (rows, 1))], axis=1)
     acc = rng.gamma(0.5, 4.0, (rows, S))
     acc[:, B:] = 0.0
     tags = np.zeros((rows, S), np.uint8)

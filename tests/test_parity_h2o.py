@@ -135,8 +135,8 @@ def _oracle_cycles(w, inp, cycles, rec, final, sigma=1e3, lam=0.35):
 
 
 def _host(res):
-    rec = [{k: (tl.bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in c.items()}
-           for c in res["cycles"]]
+    conv = lambda v: v if not torch.is_tensor(v) else (tl.bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy())  # noqa: E731
+    rec = [{k: conv(v) for k, v in c.items()} for c in res["cycles"]]
     final = {k: (tl.bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in res["final"].items()}
     return rec, final
 
@@ -208,3 +208,93 @@ def test_decode_h2o_counts_above_the_pool_are_clamped():
     for r in range(rows):
         want = h2o.attention_mass(tl.f64(q)[0, 0, 2 * r:2 * r + 2], tl.f64(K)[r])
         np.testing.assert_allclose(a[r], want, rtol=MASS_RTOL, atol=MASS_ATOL)
+
+
+def _oracle_cycles_bounded(w, inp, cycles, rec, final, sigma=1e3, lam=0.35):
+    """As _oracle_cycles with PACE's bounded positions: the oracle's own
+    renumber decisions (oracle.positions), compaction with the reference store
+    (oracle.compact.compact_row_ref). After a renumber the kernel's keys differ
+    from the oracle's by one bf16 rounding, so later running scores are held
+    to the workload bar and kept sets to swaps within 1e-2 relative; a row
+    with a swap is not compared further. Returns (rows compared to the end,
+    number of renumbers)."""
+    from oracle import compact as o_compact, positions
+    N, L, Hkv, Hq, d = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
+    B, E, G = w.budget, w.interval, w.group
+    vals = [0.0] + [o_policy.foresight_bonus(sigma, lam, s) for s in inp.steps_ahead]
+    bonus = np.array(vals).reshape(-1, 1)
+    floor = np.zeros_like(bonus, np.uint8)
+    Kb, Vb = tl.bits(inp.K), tl.bits(inp.V)
+    Knb, Vnb = tl.bits(inp.K_new), tl.bits(inp.V_new)
+    qh = tl.f64(inp.q)
+    pos0, acc0, tags0 = inp.pos.cpu().numpy(), inp.acc.cpu().numpy(), inp.tags.cpu().numpy()
+    new_pos = int(pos0[:, B:].min())
+    full, renumbers = 0, 0
+    for r in range(w.rows):
+        n, l, h = r // (L * Hkv), (r // Hkv) % L, r % Hkv
+        K, V = Kb[r].copy(), Vb[r].copy()
+        pos, acc, tags = pos0[r].astype(np.int64), acc0[r].astype(np.float64), tags0[r].astype(np.int64)
+        Kref, pref = np.zeros_like(K), np.full(K.shape[0], -1, np.int64)
+        shift, renumbered, ok = 0, False, True
+        for c in range(cycles):
+            g = rec[c]
+            K[B:], V[B:] = Knb[c, r], Vnb[c, r]
+            pos[B:] = new_pos + c * E - shift + np.arange(E)
+            acc[B:], tags[B:], pref[B:] = 0.0, 0, -1
+            Kf = numfmt.bf16_bits_to_f64(K)
+            for e in range(E):
+                acc[:B + e + 1] = h2o.accumulate(acc[:B + e + 1], qh[c, e, n, l, h * G:(h + 1) * G], Kf[:B + e + 1])
+            np.testing.assert_array_equal(g["pos"][r], pos)
+            assert pos.max() < w.limit
+            if renumbered:
+                np.testing.assert_allclose(g["acc"][r], acc, rtol=1e-2, atol=2e-2)
+            else:
+                np.testing.assert_allclose(g["acc"][r], acc, rtol=MASS_RTOL, atol=MASS_ATOL)
+            kept = h2o.evict(acc, tags, bonus, floor, 0, w.n_sink, w.n_recent, B)
+            gk = g["kept"][r][: g["n_kept"][r]].astype(np.int64)
+            if not np.array_equal(gk, kept):
+                tot, _ = o_policy.totals_and_protection(acc, tags, bonus, floor, 0, w.n_sink, w.n_recent)
+                thr = tot[kept].min()
+                diff = np.setxor1d(gk, kept)
+                assert np.all(np.abs(tot[diff] - thr) <= (1e-2 if renumbered else 1e-3) * abs(thr))
+                ok = False
+                break
+            ren, shift = positions.after_eviction(new_pos + (c + 1) * E, shift, B, w.limit, E)
+            assert g["renumber"] == ren
+            renumbers += int(ren and r == 0)
+            K, V, pos, Kref, pref = o_compact.compact_row_ref(K, V, pos, kept, 0 if ren else -1, w.rope_base,
+                                                             Kref, pref)
+            acc, tags = acc[kept], tags[kept]
+            renumbered |= ren
+            pad = lambda a, v: np.concatenate([a, np.full((E,) + a.shape[1:], v, a.dtype)])  # noqa: E731
+            K, V, Kref = pad(K, 0), pad(V, 0), pad(Kref, 0)
+            pos, pref, acc, tags = pad(pos, 0), pad(pref, -1), pad(acc, 0.0), pad(tags, 0)
+        if not ok:
+            continue
+        full += 1
+        np.testing.assert_array_equal(final["pos"][r][:B], pos[:B])
+        np.testing.assert_array_equal(final["pr"][r][:B], pref[:B])
+        np.testing.assert_array_equal(final["Kr"][r][:B], Kref[:B])          # references are bit copies
+        np.testing.assert_array_equal(final["V"][r][:B], V[:B])
+        _close = numfmt.bf16_bits_to_f64
+        a, b = _close(final["K"][r][:B]), _close(K[:B])
+        np.testing.assert_allclose(a, b, rtol=1e-2, atol=2e-2)
+    return full, renumbers
+
+
+def test_h2o_small_bounded_positions_with_reference_store():
+    """PACE's decode loop with H2O eviction, bounded positions (L = 128 here,
+    headroom E) and renumbering through the reference store, against the
+    oracle's own loop."""
+    from budgeted_retention_amd import pipelines
+    w = synth.H2O_WORKLOADS["h2o_small_bounded"]
+    cycles = 10
+    inp = synth.make_h2o_inputs(w, cycles, "cuda")
+    res = pipelines.run_h2o(w, inp, cycles, record=True)
+    torch.cuda.synchronize()
+    rec, final = _host(res)
+    assert sum(c["renumber"] for c in rec) >= 2                   # the limit was reached more than once
+    assert all(c["pos"].max() < w.limit for c in rec)
+    full, renumbers = _oracle_cycles_bounded(w, inp, cycles, rec, final)
+    assert renumbers == sum(c["renumber"] for c in rec)
+    assert full >= w.rows // 2, full
