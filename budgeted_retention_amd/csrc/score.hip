@@ -99,12 +99,18 @@ __device__ __forceinline__ int visible_tiles(int64_t k0, int64_t qbase, int ntil
 
 // ---------------------------------------------------------------- pass 1
 
-// One 32-key tile (in registers) for every query block: running max/exp-sum
-// per query row (this lane's query row is b*32 + col of block b). The blocks
-// go through a rolled loop to keep one accumulator live; the per-block state
-// m[], l[] rotates by one each iteration, so block b's state is always at
-// index 0 (static register indices) and the arrays are back in order after
-// NB iterations.
+// One 32-key tile (in registers) for every query block: running (reference,
+// exp-sum) per query row (this lane's query row is b*32 + col of block b).
+// The reference m need not be the running max: any m with every term
+// exp2(x - m) finite gives the same normaliser m + log2(l). So a tile's terms
+// are summed against the current reference first, and only when that sum is
+// not below 2^64 (or is not finite: the row's first tile, or a logit well
+// above the reference) does the tile take its max and rescale. The per-block
+// state m[], l[] rotates by one each iteration, so block b's state is always
+// at index 0 and the arrays are back in order after NB iterations; up to 7
+// blocks the loop is unrolled (the rotation is then free), with 8 it stays
+// rolled (static register indices, one accumulator live) so that the kernel
+// fits 128 VGPRs.
 template <int D, int NB, bool MASKED>
 __device__ __forceinline__ void p1_tile(const bf16x8 (&kf)[D / 16], int64_t j0, int lane, const uint4 *sq,
                                         int64_t qbase, int W, int QR, float c2, float (&m)[NB], float (&l)[NB]) {
@@ -114,7 +120,8 @@ __device__ __forceinline__ void p1_tile(const bf16x8 (&kf)[D / 16], int64_t j0, 
     // loads in the loop): holding all of them in registers would cost occupancy.
     int qoff = lane;
     asm volatile("" : "+v"(qoff));
-#pragma unroll 1
+    constexpr int UNROLL = NB <= 7 ? NB : 1;
+#pragma unroll UNROLL
     for (int b = 0; b < NB; ++b) {
         f32x16 acc = {};
 #pragma unroll
@@ -124,29 +131,36 @@ __device__ __forceinline__ void p1_tile(const bf16x8 (&kf)[D / 16], int64_t j0, 
         }
         // acc[i] = logit of key j0 + acc_row(i, hf) for query row b*32 + col
         if (MASKED) {
-            // positions relative to qbase (masked tiles lie within W + 32 keys of it);
-            // padding query rows see no key
+            // key j0 + acc_row(i, hf) is visible to query row qr when its offset
+            // from qbase is at most qr % W (masked tiles lie within W + 32 keys
+            // of qbase); padding query rows see no key. Comparing acc_row(i, 0)
+            // against one per-lane bound keeps the offsets as inline constants.
             const int qr = b * 32 + col;
             const int lim = qr < QR ? qr % W : -(1 << 30);
-            const int rel0 = (int)(j0 - qbase);
+            const int bound = lim - (int)(j0 - qbase) - 4 * hf;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (rel0 + acc_row(i, hf) > lim) acc[i] = -INFINITY;
+                if (acc_row(i, 0) > bound) acc[i] = -INFINITY;
         }
-        float tmax = acc[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[i]);
-        tmax *= c2;
         float mc = m[0], lc = l[0];
-        if (tmax > mc) {
-            lc *= __builtin_amdgcn_exp2f(mc - tmax);
-            mc = tmax;
-        }
-        // A row with no visible key yet keeps m = -inf; its exponents are all -inf.
-        const float mb = (MASKED && mc == -INFINITY) ? 0.f : mc;
-        float sum = 0.f;
+        float sum = __builtin_amdgcn_exp2f(fmaf(acc[0], c2, -mc));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mb));
+        for (int i = 1; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mc));
+        if (!(sum <= 0x1p64f)) {
+            float tmax = acc[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, acc[i]);
+            tmax *= c2;
+            if (tmax > mc) {
+                lc *= __builtin_amdgcn_exp2f(mc - tmax);
+                mc = tmax;
+            }
+            // A row with no visible key yet keeps m = -inf; its exponents are all -inf.
+            const float mb = mc == -INFINITY ? 0.f : mc;
+            sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(fmaf(acc[i], c2, -mb));
+        }
         lc += sum;
 #pragma unroll
         for (int k = 0; k + 1 < NB; ++k) {
@@ -357,7 +371,7 @@ __device__ __forceinline__ void p2_chunk(const uint16_t *Kr, int64_t k0, int64_t
 // Pass 1: one workgroup per (local row, STATS_CHUNK keys); also used for
 // windows inside the cache (page effects).
 template <int D, int NB>
-__global__ void __launch_bounds__(SCORE_THREADS) score_pass1(const uint16_t *__restrict__ K,
+__global__ void __launch_bounds__(SCORE_THREADS) __attribute__((amdgpu_waves_per_eu(4))) score_pass1(const uint16_t *__restrict__ K,
                                                              const uint16_t *__restrict__ Q, int64_t T, int W,
                                                              int G, int L, int Hkv, int Hq, int64_t n_chunks,
                                                              float c2, WindowGeom wg, float2 *__restrict__ part) {

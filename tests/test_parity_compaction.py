@@ -138,6 +138,38 @@ def test_ragged_shapes_and_edges(T, Hkv, Hq, d, W, B, sink, recent):
     _check_rows(w, inp, res, range(w.rows))
 
 
+@pytest.mark.parametrize("profile", ["late_jump", "steady_growth"])
+def test_score_logit_ranges_beyond_the_first_tiles_reference(profile):
+    """Rows whose logits climb far above what the first key tiles show. Pass 1
+    sums each tile against its running reference and rescales only when a
+    tile's sum reaches 2^64, so these rows take that path repeatedly: keys
+    from 700 on scaled by 24 (a jump of about 100 log2 units), or keys scaled
+    by 2^(6 j / T) (a steady climb over hundreds of log2 units). Scores of
+    every row against the oracle."""
+    from budgeted_retention_amd import kvc
+    from oracle import score as o_score
+    w = synth.Workload("ranges", 1, 2, 2, 8, 64, 1031, 8, 4, 8, 64, 1e4, 0, 3, (4, 12), 2, seed=97)
+    inp = synth.make_compaction_inputs(w, "cpu")
+    T, G = w.n_tokens, w.n_q_heads // w.n_kv_heads
+    j = torch.arange(T, dtype=torch.float32)
+    scale = torch.where(j >= 700, 24.0, 1.0) if profile == "late_jump" else 2.0 ** (6.0 * j / T)
+    K = (inp.K.float() * scale[:, None]).to(torch.bfloat16)
+    dims = kvc.make_dims(1, 2, w.n_kv_heads, w.n_q_heads, w.head_dim, T)
+    Kd, Qd = K.cuda(), inp.Q_obs.cuda()
+    ws = kvc.workspace(kvc.KVC_OP_SCORE, dims, w.window, 0, Kd.device)
+    scores = torch.empty((1, 2, w.n_kv_heads, T), dtype=torch.float32, device=Kd.device)
+    kvc.kvc_score(dims, Kd, Qd, w.window, scores, ws)
+    torch.cuda.synchronize()
+    g = scores.cpu().numpy().reshape(-1, T)
+    for r in range(g.shape[0]):
+        l, h = r // w.n_kv_heads, r % w.n_kv_heads
+        o = o_score.obs_window_score(numfmt.bf16_bits_to_f64(tl.bits(K[0, l, h])),
+                                     tl.f64(inp.Q_obs[0, l, h * G:(h + 1) * G]), w.window)
+        tl.check_scores(g[r], o)
+        # the scaled keys hold the attention: the check is not vacuous
+        assert o[700:].sum() > 0.9 * o.sum()
+
+
 def test_tag_floors_and_layer_groups():
     # a floor table protecting span tag 2 in group 1 only: rows of layer 1 keep it all
     T, B = 2000, 128
