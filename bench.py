@@ -114,10 +114,12 @@ def cpu_cores():
 # ---------------------------------------------------------------- algorithmic bytes
 
 def compaction_bytes(rows, T, d, G, W, B):
-    """Bytes each call must move at least once (the design doc gives the derivation):
-    score reads K and Q once and writes fp32 scores; select reads the scores
-    and tags and writes B indices; compaction reads and writes B keys and
-    values plus positions."""
+    """Bytes each call must move at least once, per row: score reads K
+    (T*d bf16) and the group's window queries (G*W*d bf16) once and writes T
+    fp32 scores; select reads the scores and the row's tags (T bytes) and
+    writes B indices and the count; compaction reads and writes B keys and
+    values (bf16) plus B input and output positions; decode reads the B kept
+    keys and values and the group's queries and writes their outputs."""
     score = T * d * 2 + G * W * d * 2 + T * 4
     select = T * 4 + T + B * 4 + 4
     compact = 2 * B * d * 2 + 2 * B * d * 2 + B * 4 * 2
