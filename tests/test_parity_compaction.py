@@ -125,10 +125,13 @@ def test_tiny_workload_is_deterministic():
     (64, 2, 2, 64, 8, 100, 4, 8),          # T <= B: keep everything
     (500, 1, 8, 128, 32, 40, 8, 64),       # sink + recent exceed B: floor excess
     (1031, 1, 32, 64, 8, 64, 1, 8),        # W*G = 256, eight waves
+    (40, 2, 8, 128, 40, 24, 2, 8),         # T = W: every key inside the causal window
+    (1, 1, 4, 64, 1, 1, 0, 1),             # a one-token cache
 ])
 def test_ragged_shapes_and_edges(T, Hkv, Hq, d, W, B, sink, recent):
+    spans, referenced = (3, 2) if T >= 64 else (0, 0)   # no room for spans in the tiny caches
     w = synth.Workload("sweep", 1, 2, Hkv, Hq, d, T, W, sink, recent, B, 1e4, 0,
-                       3, (4, 12), 2, seed=31 + T)
+                       spans, (4, 12), referenced, seed=31 + T)
     inp = synth.make_compaction_inputs(w, "cpu")
     inp.K, inp.V, inp.Q_obs = inp.K.cuda(), inp.V.cuda(), inp.Q_obs.cuda()
     res = _run(w, inp)
