@@ -27,6 +27,7 @@ Prints one JSON line.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -64,13 +65,25 @@ COUNTED_SOURCES = ["budgeted_retention_amd/csrc/" + n for n in
                    "budgeted_retention_amd/build.py"]
 
 
+_C_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def _code_only(name, text):
+    """The source with C/C++ comments and blank space removed (string and
+    character literals kept), so that editing a comment leaves the hash alone."""
+    if not name.endswith((".hip", ".h", ".cpp")):
+        return text
+    text = _C_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
-    """Hash of the sources the counters were taken on."""
+    """Hash of the code (comments excluded) the counters were taken on."""
     h = hashlib.sha256()
     for name in COUNTED_SOURCES:
-        with open(os.path.join(ROOT, name), "rb") as f:
+        with open(os.path.join(ROOT, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(name, f.read()).encode())
     return h.hexdigest()[:16]
 
 

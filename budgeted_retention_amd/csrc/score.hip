@@ -7,10 +7,10 @@
 // causal rule of CommitKV Eq. 6).
 //
 // A softmax weight needs its query row's normaliser over all keys, so the keys
-// are read twice: pass 1 gives every query row its max and exp-sum (log2
-// domain) chunk by chunk, a merge folds the chunks into mm[qr] = max +
-// log2(sum), and pass 2 recomputes the logits and writes
-// score[j] = sum_qr exp2(logit*c - mm[qr]).
+// are read twice: pass 1 gives every query row a reference r and its exp-sum
+// sum_j exp2(logit*c - r) (log2 domain) chunk by chunk, a merge folds the
+// chunks into mm[qr] = r + log2(sum), and pass 2 recomputes the logits and
+// writes score[j] = sum_qr exp2(logit*c - mm[qr]).
 //
 // kvc_score launches pass 1 (one workgroup per row and STATS_CHUNK keys), the
 // merge (one workgroup per row) and pass 2 (same grid as pass 1).
@@ -24,7 +24,7 @@
 // Logits come from v_mfma_f32_32x32x16_bf16. Lane l holds key (l & 31), dims
 // 8*(l>>5)..+8 of each 16-dim slice; that layout is the A operand (rows = keys)
 // in pass 1 and the B operand (columns = keys) in pass 2. Pass 1 computes
-// C[key][qrow] (a lane owns one query row: max/sum over keys stay in-lane);
+// C[key][qrow] (a lane owns one query row: its reference and sum stay in-lane);
 // pass 2 computes C[qrow][key] (a lane owns one key: the sum over query rows
 // stays in-lane).
 #include <cmath>
@@ -172,7 +172,7 @@ __device__ __forceinline__ void p1_tile(const bf16x8 (&kf)[D / 16], int64_t j0, 
     }
 }
 
-// Pass 1 over keys [k0, k1): (max, exp-sum) of every query row q -> out[q * out_stride].
+// Pass 1 over keys [k0, k1): (reference, exp-sum) of every query row q -> out[q * out_stride].
 // Uses s_m/s_l (SCORE_WAVES x QRP floats each) and ends with a barrier.
 template <int D, int NB>
 __device__ __forceinline__ void p1_chunk(const uint16_t *Kr, int64_t k0, int64_t k1, int64_t qbase, int W, int QR,
@@ -245,8 +245,8 @@ __device__ __forceinline__ void p1_chunk(const uint16_t *Kr, int64_t k0, int64_t
     __syncthreads();
 }
 
-// mm[q] = max + log2(sum) over a row's chunk partials part[q][0..nch); padding
-// rows get +inf (their weights exp2(x - inf) are 0). All threads of the
+// mm[q] = M + log2(S), the fold of a row's chunk partials (reference, sum)
+// part[q][0..nch); padding rows get +inf (their weights exp2(x - inf) are 0). All threads of the
 // workgroup take part: query row q is folded by blockDim/QRP threads, each over
 // a contiguous range of chunks in one online (max, sum) pass; the ranges are
 // then combined in a fixed order, so the result does not depend on timing.
