@@ -1,0 +1,39 @@
+"""Host-side pieces of bench.py (no GPU): the refusal of more than one GPU,
+the algorithmic byte counts, and the counted-source hash that keys the stored
+HBM counters (bench.py reports no traffic once the counted code changes)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_source_hash_ignores_comments_and_layout_but_not_code():
+    src = 'int f(int a) {  // doubles\n  /* no side effects */ return 2 * a; }\nconst char *s = "// kept";\n'
+    base = bench._code_only("k.hip", src)
+    assert base == 'int f(int a) { return 2 * a; } const char *s = "// kept";'
+    assert bench._code_only("k.hip", src.replace("doubles", "twice")) == base
+    assert bench._code_only("k.hip", src.replace("  return", "\n\n    return")) == base
+    assert bench._code_only("k.hip", src.replace("2 * a", "3 * a")) != base
+    assert bench._code_only("k.hip", src.replace('"// kept"', '"// changed"')) != base
+    # other files are hashed as they are
+    assert bench._code_only("build.py", "x = 1  # note\n") == "x = 1  # note\n"
+
+
+def test_algorithmic_bytes_of_the_100k_session():
+    b = bench.compaction_bytes(288, 100000, 128, 4, 32, 2048)
+    # K (T*d bf16) + the group's window queries + fp32 scores, per row
+    assert b["kvc_score"] == 288 * (100000 * 128 * 2 + 4 * 32 * 128 * 2 + 100000 * 4)
+    # B keys and values read and written, input and output positions
+    assert b["kvc_compact_rerotate"] == 288 * (4 * 2048 * 128 * 2 + 2048 * 8)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
