@@ -329,7 +329,7 @@ __device__ __forceinline__ void p2_tile(const bf16x8 (&kf)[D / 16], int64_t j0, 
             }
         }
     }
-    p += __shfl_xor(p, 32);
+    p = xor32_sum(p);  // + the other half-wave's query rows (all lanes active here)
     if (hf == 0 && key < kend) out[key] = p;
 }
 
