@@ -72,3 +72,26 @@ def test_pool_single_token_rows():
         kvc.kvc_pool_scores(dims, s, 63, mode, out)
         torch.cuda.synchronize()
         assert torch.equal(out, s)
+
+
+@pytest.mark.parametrize("mode", ["max", "avg"])
+def test_pool_full_session_shape_sampled_rows(mode):
+    """The launch bench.py times: 36 layers x 8 KV heads of 100,000-token
+    score rows, kernel 7; three rows checked against the oracle entry by entry."""
+    from budgeted_retention_amd import kvc
+    L, Hkv, T, kernel = 36, 8, 100_000, 7
+    rows = L * Hkv
+    gen = torch.Generator(device="cuda").manual_seed(20261229)
+    s = torch.rand((rows, T), generator=gen, device="cuda", dtype=torch.float32) ** 4   # many small, few large
+    dims = kvc.make_dims(1, L, Hkv, 4 * Hkv, 128, T)
+    out = torch.full((rows, T), -7.0, dtype=torch.float32, device="cuda")
+    kvc.kvc_pool_scores(dims, s, kernel, kvc.KVC_POOL_MAX if mode == "max" else kvc.KVC_POOL_AVG, out)
+    torch.cuda.synchronize()
+    for r in (0, 143, rows - 1):
+        src = s[r].cpu().numpy()
+        want = o_score.pool_scores(src.astype(np.float64), kernel, mode)
+        got = out[r].cpu().numpy()
+        if mode == "max":
+            np.testing.assert_array_equal(got, want)
+        else:
+            np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-7)
