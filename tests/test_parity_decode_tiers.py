@@ -218,3 +218,24 @@ def test_tiered_compaction_zero_and_tiny_rows(low_bits):
             assert np.abs(got_c.astype(int) - want_c.astype(int)).max() <= 1
             assert got_s[5] == 0x3C00 and not got_c[5].any()
             assert got_s[9] == 1 and np.abs(got_c[9]).max() <= qmax
+
+
+def test_decode_full_session_shape_sampled_rows():
+    """The decode launch bench.py times: 36 layers x 8 KV heads (G = 4, d 128),
+    every row holding B = 2048 resident keys; the 4 query heads of sampled rows
+    against the oracle."""
+    dims_t = (1, 36, 8, 32, 128)
+    B = 2048
+    p = synth.decode_pools(*dims_t, B, seed=2048, device="cuda")
+    p["n_h"].fill_(B)
+    g_o, g_lse = _gpu_decode(dims_t, p, B)
+    L, Hkv, G = 36, 8, 4
+    for r in (0, 1, 143, L * Hkv - 1):
+        l, h = r // Hkv, r % Hkv
+        K, V = tl.f64(p["K"][r]), tl.f64(p["V"][r])
+        for g in range(G):
+            hq = h * G + g
+            o, lse = o_decode.decode_partitions(tl.f64(p["q"][0, l, hq]), [(K, V)])
+            np.testing.assert_allclose(g_o[0, l, hq], numfmt.round_bf16(o), rtol=1e-2, atol=2e-2)   # the bar
+            np.testing.assert_allclose(g_o[0, l, hq], o, rtol=8e-3, atol=1e-3)                      # fp32 path
+            assert g_lse[0, l, hq] == pytest.approx(lse, rel=1e-5, abs=1e-5)
