@@ -27,9 +27,13 @@ Appendix A.4); promotion stops at the first step that does not fit.
 
 Parity status: pinned by invariants (floors never violated, the ledger's
 closed form R_t = t*b - sum_{i<t} M(a_i) from Appendix B.6, the all-high
-fallback) and by brute force over all action vectors; the synthetic tag
-chain and table it runs on in the benchmark are "parity unpinned" beyond
-those.
+fallback), by hand-built steps whose outcome the order of §3.5 fixes (which
+group is demoted first, which priority a demotion carries, promotion in
+descending priority stopping at the first step that does not fit, ties to
+the lower group), and by a search over every order of the groups' step
+chains that picks the smallest (demotion) or largest (promotion) priorities
+first. The synthetic tag chain and table it runs on in the benchmark are
+"parity unpinned" beyond those.
 """
 import numpy as np
 

@@ -226,3 +226,127 @@ def test_retained_pages_keep_protected_and_drop_retired_eq13():
     np.testing.assert_array_equal(pe.retained_pages(score, [0], 3, protected=[5]), [2, 3, 5])
     np.testing.assert_array_equal(pe.retained_pages(score, [], 3, protected=[]), [0, 2, 3])
     np.testing.assert_array_equal(pe.retained_pages(score, [0, 2], 2, protected=[1]), [1, 3])
+
+
+# ---- PASK §3.5, Algorithm 2 (Demote, then Promote for critical tags): the order ----
+# Demotion takes eligible adjacent steps in ascending stored priority; promotion
+# takes them in descending priority and stops at the first step that does not fit.
+# Demoting H->L undoes the upgrade L->H, so it carries that upgrade's stored
+# priority (index 1); demoting L->R carries that of R->L (index 0).
+
+_FLAT = np.array([[0.0, 5.0, 10.0]] * 4)      # m(R), m(L), m(H) per group
+
+
+def test_demotion_takes_the_lowest_stored_priority_first():
+    # two groups at H, a budget that allows exactly one demotion
+    prio = [[0.5, 0.9], [0.5, 0.1]]            # group 1's L->H upgrade ranks lowest
+    a, M = pask.control_token([2, 2], [0, 0], prio, False, 15.0, _FLAT[:2])
+    assert a == [2, 1] and M == 15.0
+    prio = [[0.5, 0.1], [0.5, 0.9]]
+    a, _ = pask.control_token([2, 2], [0, 0], prio, False, 15.0, _FLAT[:2])
+    assert a == [1, 2]
+
+
+def test_demotion_uses_the_priority_of_the_upgrade_it_undoes():
+    # H->L is priced by the L->H priority, not by R->L's
+    prio = [[0.1, 0.9], [0.8, 0.2]]
+    a, _ = pask.control_token([2, 2], [0, 0], prio, False, 15.0, _FLAT[:2])
+    assert a == [2, 1]
+    # L->R is priced by the R->L priority, not by L->H's
+    prio = [[0.3, 0.9], [0.7, 0.1]]
+    a, _ = pask.control_token([1, 1], [0, 0], prio, False, 5.0, _FLAT[:2])
+    assert a == [0, 1]
+
+
+def test_demotion_sequence_over_several_steps():
+    # three groups at H, cost 30, budget 15: three demotions, each the cheapest
+    # eligible step at its turn. Step 1: H->L of group 1 (0.2); step 2: H->L of
+    # group 0 (0.5 < 0.8, group 1's L->R is 0.9); step 3: L->R of group 0 (0.3).
+    prio = [[0.3, 0.5], [0.9, 0.2], [0.1, 0.8]]
+    a, M = pask.control_token([2, 2, 2], [0, 0, 0], prio, False, 15.0, _FLAT[:3])
+    assert a == [0, 1, 2] and M == 15.0
+
+
+def test_demotion_skips_floored_groups_and_ties_go_to_the_lower_group():
+    prio = [[0.5, 0.9], [0.5, 0.1]]
+    # group 1 is floored at H: group 0 is demoted although its priority is higher
+    a, _ = pask.control_token([2, 2], [0, 2], prio, False, 15.0, _FLAT[:2])
+    assert a == [1, 2]
+    # equal priorities: the lower group index goes first
+    a, _ = pask.control_token([2, 2], [0, 0], [[0.4, 0.4], [0.4, 0.4]], False, 15.0, _FLAT[:2])
+    assert a == [1, 2]
+
+
+def test_promotion_takes_the_highest_priority_first_and_stops_at_the_first_misfit():
+    costs = np.array([[0.0, 1.0, 2.0], [0.0, 5.0, 10.0], [0.0, 5.0, 10.0]])
+    prio = [[0.4, 0.0], [0.6, 0.0], [0.0, 0.9]]
+    # start [R, R, L], cost 5, budget 12. Promote L->H of group 2 (0.9): cost 10.
+    # Next is R->L of group 1 (0.6): 15 > 12, so promotion stops there, although
+    # group 0's cheaper step (0.4, +1) would still fit.
+    a, M = pask.control_token([0, 0, 1], [0, 0, 0], prio, True, 12.0, costs)
+    assert a == [0, 0, 2] and M == 10.0
+    # the same table for a non-critical tag: no promotion at all
+    a, _ = pask.control_token([0, 0, 1], [0, 0, 0], prio, False, 12.0, costs)
+    assert a == [0, 0, 1]
+
+
+def _chain_walk(steps_per_group, key):
+    """Every interleaving of per-group step chains (each group's steps in their
+    fixed order); returns the interleaving whose sequence of keys is
+    lexicographically smallest, as a list of (group, step index)."""
+    best = None
+    counts = [len(s) for s in steps_per_group]
+    groups = [c for c in range(len(counts)) for _ in range(counts[c])]
+    for perm in set(itertools.permutations(groups)):
+        seen = [0] * len(counts)
+        seq = []
+        for c in perm:
+            seq.append((key(steps_per_group[c][seen[c]], c), c, seen[c]))
+            seen[c] += 1
+        cand = [k for k, _, _ in seq]
+        if best is None or cand < best[0]:
+            best = (cand, [(c, i) for _, c, i in seq])
+    return best[1]
+
+
+def _brute_force_token(a0, amin, prio, crit, R_t, costs):
+    """Algorithm 2 restated as a search over step orders: the demotion order is
+    the interleaving of the groups' demotion chains whose priorities read
+    smallest first (ties by group index), walked until the cost fits; the
+    promotion order is the interleaving whose priorities read largest first,
+    walked while the cost still fits."""
+    C = len(a0)
+    a = [max(int(a0[c]), int(amin[c])) for c in range(C)]
+    B = max(R_t, 0.0)
+    cost = lambda v: sum(costs[c][v[c]] for c in range(C))
+    # demotion chain of group c: a[c] -> a[c]-1 -> ... -> amin[c]; the step from
+    # level k to k-1 carries the priority of the upgrade k-1 -> k
+    chains = [[prio[c][k - 1] for k in range(a[c], int(amin[c]), -1)] for c in range(C)]
+    for c, _ in _chain_walk(chains, lambda p, c: (p, c)):
+        if cost(a) <= B:
+            break
+        a[c] -= 1
+    if crit:
+        chains = [[prio[c][k] for k in range(a[c], 2)] for c in range(C)]
+        for c, _ in _chain_walk(chains, lambda p, c: (-p, c)):
+            up = list(a)
+            up[c] += 1
+            if cost(up) > B:
+                break
+            a = up
+    return a
+
+
+def test_controller_matches_the_order_derived_by_search_over_all_step_orders():
+    rng = np.random.default_rng(32)
+    for trial in range(400):
+        C = int(rng.integers(2, 4))
+        costs = np.array([[0.0, float(rng.integers(1, 6)), 0.0] for _ in range(C)])
+        costs[:, 2] = costs[:, 1] + rng.integers(1, 6, C)
+        a0 = rng.integers(0, 3, C)
+        amin = np.minimum(a0, rng.integers(0, 3, C))
+        prio = rng.random((C, 2)).round(1)          # coarse values make ties common
+        crit = bool(rng.random() < 0.5)
+        R_t = float(rng.uniform(-0.1, 1.1) * costs[:, 2].sum())
+        a, _ = pask.control_token(a0, amin, prio, crit, R_t, costs)
+        assert a == _brute_force_token(a0, amin, prio, crit, R_t, costs), (trial, a0, amin, prio, crit, R_t)
