@@ -116,12 +116,40 @@ def copy_bandwidth(dev, mib=2048):
     return round(gbs, 1)
 
 
-def cpu_cores():
+def host_cores():
+    """Cores of this host (os.cpu_count) and the share a job may use: the
+    scheduler's thread limit when one is set (OMP_NUM_THREADS), else all."""
+    n = os.cpu_count() or 1
+    lim = os.environ.get("OMP_NUM_THREADS", "")
+    share = min(n, int(lim)) if lim.isdigit() and int(lim) > 0 else n
+    return n, share
+
+
+def run_metadata(dev):
+    """Where the line was measured: commit, ROCm and torch versions, GPU name,
+    and the GPU's current and maximum shader clock."""
+    import subprocess
+    import torch
+    meta = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
     try:
-        from threadpoolctl import threadpool_info
-        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        meta["git"] = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True,
+                                     text=True, timeout=10).stdout.strip() or None
     except Exception:
-        return 1
+        meta["git"] = None
+    try:
+        meta["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        meta["rocm"] = None
+    p = torch.cuda.get_device_properties(dev)
+    meta["gpu"] = f"{p.name} ({getattr(p, 'gcnArchName', '')}, {p.multi_processor_count} CUs)"
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        meta["sclk"] = card.get("sclk clock speed:")
+    except Exception:
+        meta["sclk"] = None
+    return meta
 
 
 # ---------------------------------------------------------------- algorithmic bytes
@@ -165,30 +193,43 @@ def per_call_rates(bytes_by_call, ms_by_call):
 # ---------------------------------------------------------------- CPU oracle baselines
 
 def cpu_compaction_rows(K, V, Q, G, W, T, B, tags, bonus_tbl, n_sink, n_recent, renumber_base, rope_base,
-                        rows, budget_s, L, Hkv):
-    """Time the float64 oracle (score + select + gather/re-rotate) over a prefix
-    of `rows` (D2H copies of the exact input bytes) until about `budget_s`
-    seconds of oracle work. Returns (rows done, seconds)."""
+                        rows, budget_s, L, Hkv, threads=1):
+    """Time the float64 oracle (score + select + gather/re-rotate) over the
+    rows in order (D2H copies of the exact input bytes, made before the timed
+    part) until all `rows` are done or about `budget_s` seconds have passed.
+    `threads` rows run at once, each on one BLAS thread (numpy releases the
+    interpreter lock inside its array operations); the time is the wall time
+    of those parallel batches. Returns (rows done, seconds)."""
+    import concurrent.futures
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_limits
     from oracle import compact as o_compact, numfmt, policy as o_policy, score as o_score
     from oracle import select as o_select
     fl = np.zeros_like(bonus_tbl, dtype=np.uint8)
-    done, spent = 0, 0.0
-    while spent < budget_s and done < rows:
-        r = done
+
+    def fetch(r):
         n, l, h = r // (L * Hkv), (r // Hkv) % L, r % Hkv
-        Kb = K[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16)
-        Vb = V[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16)
-        Qb = Q[n, l, h * G:(h + 1) * G].cpu().view(torch.int16).numpy().view(np.uint16)
-        tg = tags[n].cpu().numpy() if tags is not None else np.zeros(T, np.uint8)
-        t0 = time.perf_counter()
+        return (K[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16),
+                V[n, l, h].cpu().view(torch.int16).numpy().view(np.uint16),
+                Q[n, l, h * G:(h + 1) * G].cpu().view(torch.int16).numpy().view(np.uint16),
+                tags[n].cpu().numpy() if tags is not None else np.zeros(T, np.uint8))
+
+    def one(row):
+        Kb, Vb, Qb, tg = row
         s = o_score.obs_window_score(numfmt.bf16_bits_to_f64(Kb), numfmt.bf16_bits_to_f64(Qb), W)
         tot, prot = o_policy.totals_and_protection(s, tg, bonus_tbl, fl, 0, n_sink, n_recent)
         kept, _ = o_select.select_top_b(tot, prot, B)
         o_compact.compact_row(Kb, Vb, np.arange(T), kept, renumber_base, rope_base)
-        spent += time.perf_counter() - t0
-        done += 1
+
+    done, spent = 0, 0.0
+    with threadpool_limits(limits=1), concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        while spent < budget_s and done < rows:
+            batch = [fetch(r) for r in range(done, min(rows, done + threads))]
+            t0 = time.perf_counter()
+            list(ex.map(one, batch))
+            spent += time.perf_counter() - t0
+            done += len(batch)
     return done, spent
 
 
@@ -325,24 +366,21 @@ def bench_compaction(args, w, dev):
     roof = roofline(ab[dom], part[dom], dom, w.name)
     cpu = None
     if args.cpu_seconds > 0:
-        done, spent = cpu_compaction_rows(inp.K, inp.V, inp.Q_obs, w.group, W, T, B, inp.tags,
-                                          oracle_bonus(inp.spans.steps_ahead), w.n_sink, w.n_recent,
-                                          w.renumber_base, w.rope_base, w.rows, args.cpu_seconds, L, Hkv)
-        cpu = {"value": T * N * (done / w.rows) / spent, "unit": "tokens/s", "cores": cpu_cores(),
-               "kind": "oracle",
-               "sample": f"{done} of {w.rows} (layer, KV head) rows of one {T}-token session, float64 numpy "
-                         f"oracle (score+select+gather/re-rotate), {spent:.1f} s of oracle time scaled to "
-                         f"the whole session",
+        n_host, share = host_cores()
+        orc = (inp.K, inp.V, inp.Q_obs, w.group, W, T, B, inp.tags, oracle_bonus(inp.spans.steps_ahead),
+               w.n_sink, w.n_recent, w.renumber_base, w.rope_base, w.rows)
+        done, spent = cpu_compaction_rows(*orc, args.cpu_seconds, L, Hkv, threads=share)
+        limit = "all rows" if done == w.rows else f"the first {done} rows (the {args.cpu_seconds:.0f} s limit)"
+        cpu = {"value": T * N * (done / w.rows) / spent, "unit": "tokens/s", "cores": share,
+               "host_cores": n_host, "kind": "oracle",
+               "sample": f"{limit} of the {w.rows} (layer, KV head) rows of one {T}-token session: the float64 "
+                         f"numpy oracle (score+select+gather/re-rotate), {share} rows at a time on one BLAS "
+                         f"thread each, {spent:.1f} s of wall time, scaled to the whole session",
                "cpu_model": cpu_model()}
-        try:   # the same oracle on one core, on a smaller sample
-            from threadpoolctl import threadpool_limits
-            with threadpool_limits(limits=1):
-                d1, s1 = cpu_compaction_rows(inp.K, inp.V, inp.Q_obs, w.group, W, T, B, inp.tags,
-                                             oracle_bonus(inp.spans.steps_ahead), w.n_sink, w.n_recent,
-                                             w.renumber_base, w.rope_base, w.rows, args.cpu_seconds / 3, L, Hkv)
-            cpu["value_1core"] = T * N * (d1 / w.rows) / s1
-        except ImportError:
-            pass
+        # the same oracle on one core, on a smaller sample
+        d1, s1 = cpu_compaction_rows(*orc, args.cpu_seconds / 5, L, Hkv, threads=1)
+        cpu["value_1core"] = T * N * (d1 / w.rows) / s1
+        cpu["rows_1core"] = d1
         cpu["calls"] = oracle_call_times(w, args.cpu_seconds / 5)
     value = N * T / (ms * 1e-3)
     config = {"workload": w.name, "n_seq": N, "layers": L, "kv_heads": Hkv, "q_heads": Hq, "head_dim": d,
@@ -489,23 +527,26 @@ def bench_pipeline(args, w, dev, kind):
     roof = roofline(ab[dom], part[dom], dom, w.name)
     cpu = None
     if args.cpu_seconds > 0:
+        n_host, share = host_cores()
         if kind == "pask":
             done, spent = cpu_compaction_rows(inp.K, inp.V, inp.Q_obs, G, W, w.n_prompt, w.budget, None,
                                               np.zeros((1, 1)), w.n_sink, w.n_recent, -1, w.rope_base, rows,
-                                              args.cpu_seconds, w.n_layers, Hkv)
+                                              args.cpu_seconds, w.n_layers, Hkv, threads=share)
             cpu = {"value": w.n_seq * w.n_prompt * (done / rows) / spent, "unit": "tokens/s",
-                   "cores": cpu_cores(), "kind": "oracle",
+                   "cores": share, "host_cores": n_host, "kind": "oracle",
                    "sample": f"{done} of {rows} prompt rows (score+select+gather), float64 numpy oracle, "
-                             f"{spent:.1f} s scaled to all prompt tokens"}
+                             f"{share} rows at a time on one BLAS thread each, {spent:.1f} s of wall time "
+                             f"scaled to all prompt tokens"}
         else:
             done, spent = cpu_compaction_rows(inp.K, inp.V, inp.Q_post, G, W, w.n_tokens, w.budget, None,
                                               np.zeros((1, 1)), 0, 0, -1, 1e6, rows, args.cpu_seconds,
-                                              w.n_layers, Hkv)
+                                              w.n_layers, Hkv, threads=share)
             cpu = {"value": w.n_seq * w.n_tokens * (done / rows) / spent, "unit": "tokens/s",
-                   "cores": cpu_cores(), "kind": "oracle",
+                   "cores": share, "host_cores": n_host, "kind": "oracle",
                    "sample": f"{done} of {rows} rows: post-commit window score + per-row top-B and gather "
-                             f"(float64 numpy oracle), {spent:.1f} s scaled to all rows; the page effects "
-                             f"are not in the sample"}
+                             f"(float64 numpy oracle, {share} rows at a time on one BLAS thread each), "
+                             f"{spent:.1f} s of wall time scaled to all rows; the page effects are not in "
+                             f"the sample"}
     value = tokens / (ms * 1e-3)
     if kind == "pask":
         config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "layer_groups": w.n_groups,
@@ -530,7 +571,8 @@ def cpu_h2o_rows(w, inp, budget_s):
     import torch
     from oracle import h2o, numfmt, policy
     B, E, G, L, Hkv = w.budget, w.interval, w.group, w.n_layers, w.n_kv_heads
-    bonus = np.array([0.0] + [policy.foresight_bonus(1e3, 0.35, s) for s in inp.steps_ahead]).reshape(-1, 1)
+    from budgeted_retention_amd.pipelines import H2O_SIGMA
+    bonus = np.array([0.0] + [policy.foresight_bonus(H2O_SIGMA, 0.35, s) for s in inp.steps_ahead]).reshape(-1, 1)
     floor = np.zeros_like(bonus, np.uint8)
     done, spent = 0, 0.0
     while done < w.rows and spent < budget_s:
@@ -587,11 +629,14 @@ def bench_h2o(args, w, dev):
     roof = roofline(ab[dom], part[dom], dom, w.name)
     cpu = None
     if args.cpu_seconds > 0:
-        done, spent = cpu_h2o_rows(w, inp, args.cpu_seconds)
-        cpu = {"value": w.n_seq * S * (done / rows) / spent, "unit": "tokens/s", "cores": cpu_cores(),
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            done, spent = cpu_h2o_rows(w, inp, args.cpu_seconds)
+        cpu = {"value": w.n_seq * S * (done / rows) / spent, "unit": "tokens/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{done} of {rows} rows through one cycle ({E} decode steps of cumulative attention, "
-                         f"eviction, gather), float64 numpy oracle, {spent:.1f} s scaled to all rows"}
+                         f"eviction, gather), float64 numpy oracle on one BLAS thread, {spent:.1f} s scaled "
+                         f"to all rows"}
     config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "kv_heads": w.n_kv_heads,
               "q_heads": w.n_q_heads, "head_dim": d, "budget": B, "interval": E, "sink": w.n_sink,
               "recent": w.n_recent, "parallelism": "none"}
@@ -692,7 +737,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
-        **extra, "roofline": roof, "cpu_baseline": cpu,
+        **extra, "roofline": roof, "cpu_baseline": cpu, "run": run_metadata(dev),
     }
     print(json.dumps(line), flush=True)
 

@@ -1048,6 +1048,12 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
     if (kept_stride < want)
         return fail(KVC_ERR_ARG, "kvc_select: kept_stride %d < min(budget, T) = %lld", kept_stride,
                     (long long)want);
+    // Table floors may protect any token, and every protected token is kept
+    // (floors take precedence over the budget): only a full-length list is
+    // sure to hold them all.
+    if (p->tag_floor && T > p->budget && kept_stride < T)
+        return fail(KVC_ERR_ARG, "kvc_select: with a floor table kept_stride %d must be >= T = %lld", kept_stride,
+                    (long long)T);
     // float4 score loads and 4-byte tag loads need every row start 16-byte aligned.
     const bool vec = (T % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0) &&
                      (!p->tags || reinterpret_cast<uintptr_t>(p->tags) % 4 == 0);

@@ -197,7 +197,14 @@ def run_commit(w, inp, taus, timer=None):
                 o1=o1, o2=o2, lse1=lse1, lse2=lse2)
 
 
-def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
+# PACE §3.1: the foresight bonus scale. Its floor sigma/2 must stay above every
+# cumulative attention score a slot can reach, so that every referenced token
+# outranks every unreferenced one; a running H2O score grows without bound over
+# a session (the pages report scores near 25,000), hence the page's 1e5.
+H2O_SIGMA = 1e5
+
+
+def run_h2o(w, inp, cycles, timer=None, record=False, sigma=H2O_SIGMA, lam=0.35):
     """PACE-style decode with H2O eviction over a resident cache of B + E
     slots per row: each cycle the engine appends E new tokens (score 0, no
     tag, no reference), E decode steps add their attention to the slots'
@@ -209,8 +216,8 @@ def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
     compaction renumbers the resident rows to 0..B-1, re-deriving the keys
     from the reference store, and the sequence's shift advances so new tokens
     continue at B. Two slot pools alternate. With `record`, returns per cycle
-    the scores before eviction, the kept lists and the renumber decisions,
-    plus the final pool."""
+    the scores before eviction, the kept lists, the renumber decisions and the
+    resident state after compaction, plus the final pool."""
     t = timer or _null_timer
     N, L, Hkv, Hq, d = w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
     rows, S, B, E = w.rows, w.slots, w.budget, w.interval
@@ -264,7 +271,8 @@ def run_h2o(w, inp, cycles, timer=None, record=False, sigma=1e3, lam=0.35):
             kvc.kvc_compact_rerotate(dims, cur["K"], cur["V"], cur["pos"], kept, B, nk, 0 if renumber else -1,
                                      w.rope_base, out)
         if record:
-            rec[-1].update(kept=kept.clone(), n_kept=nk.clone(), renumber=renumber)
+            rec[-1].update(kept=kept.clone(), n_kept=nk.clone(), renumber=renumber,
+                           post={k: nxt[k][:, :B].clone() for k in ("K", "V", "pos", "acc", "tags", "Kr", "pr")})
         cur, nxt = nxt, cur
     return {"cycles": rec, "final": cur, "o": o}
 
@@ -313,7 +321,9 @@ def run_commit_multi(w, inp, timer=None, record=False):
     Rp = torch.empty((N, n_keep), dtype=torch.float32, device=dev)
     scores = torch.empty((N, L, Hkv, Ta), dtype=torch.float32, device=dev)
     pscore = torch.empty((N, Pa), dtype=torch.float32, device=dev)
-    kept = torch.full((N, n_keep), -1, dtype=torch.int32, device=dev)
+    # a floor table may protect any page, so selection gets a full-length list
+    kept_sel = torch.full((N, Pa), -1, dtype=torch.int32, device=dev)
+    kept = kept_sel[:, :n_keep]
     nk = torch.zeros(N, dtype=torch.int32, device=dev)
     floor = torch.tensor([[0], [1]], dtype=torch.uint8, device=dev)
     zero_bonus = torch.zeros((2, 1), dtype=torch.float32, device=dev)
@@ -347,9 +357,9 @@ def run_commit_multi(w, inp, timer=None, record=False):
             kvc.kvc_page_scores(dims_a, scores, ps, Pa, pscore, order if c else None, accepted if c else None)
         pol = kvc.Policy(0, 0, n_keep, 2, 1, 0, 1, tags_d, zero_bonus, floor)
         with t("kvc_select"):
-            kvc.kvc_select(dims_p, pscore, pol, kept, n_keep, nk)
+            kvc.kvc_select(dims_p, pscore, pol, kept_sel, Pa, nk)
         with t("kvc_compact_rerotate"):
-            kvc.kvc_compact_rerotate(dims_a, Ka, Va, pa, kept, n_keep, nk, -1, 1e6,
+            kvc.kvc_compact_rerotate(dims_a, Ka, Va, pa, kept_sel, Pa, nk, -1, 1e6,
                                      kvc.CompactOut(Tb, Kb, Vb, pb, nh, kept_page=ps))
         with t("append"):
             Kb[:, :, :, B:] = inp.K_obs[c]

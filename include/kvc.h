@@ -156,9 +156,14 @@ double kvc_foresight_bonus(double sigma, double lambda, double steps_ahead);
  *   scores     fp32 [N][L][Hkv][T]   (NaN totals rank lowest)
  *   kept_idx   int32 [N][L][Hkv][kept_stride]  ascending kept token indices;
  *              only the first min(n_kept, kept_stride) entries are written
- *   kept_stride  >= min(budget, T)
- *   n_kept     int32 [N][L][Hkv]  number of kept tokens; n_kept > budget
- *              reports floor excess (the device-side count is the authority)
+ *   kept_stride  >= min(budget, T); >= T when tag_floor is given and T >
+ *              budget (a floor can protect any token, and every protected
+ *              token is kept, so only a full-length list holds them all);
+ *              KVC_ERR_ARG otherwise
+ *   n_kept     int32 [N][L][Hkv]  number of kept tokens. Excess caused by
+ *              table floors is reported here only: n_kept > budget (the host
+ *              cannot see the tags without a copy, and the call does not
+ *              synchronise). Size the compaction's out_stride to hold n_kept.
  *   ws         device workspace of kvc_workspace_bytes(KVC_OP_SELECT, dims, 0, B)
  *              bytes. It is 0 (ws may be NULL) unless the rows are long: T >=
  *              262144, or fewer than 128 rows of T >= 32768. Such rows are
@@ -167,7 +172,7 @@ double kvc_foresight_bonus(double sigma, double lambda, double steps_ahead);
  *              enqueueing anything if it is missing or too small. The
  *              workspace is overwritten; calls sharing one must not overlap.
  * Returns KVC_WARN_FLOOR_EXCESS (after enqueueing) when n_sink + n_recent
- * alone exceed the budget and T > budget.
+ * alone exceed the budget and T > budget: the one excess the host can see.
  */
 int kvc_select(const kvc_dims *dims, const float *scores, const kvc_policy *policy,
                int32_t *kept_idx, int32_t kept_stride, int32_t *n_kept,

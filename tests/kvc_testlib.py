@@ -49,6 +49,27 @@ def gpu_path(dims_args, K, V, Q, W, policy, renumber_base, rope_base, kept_strid
                 n_h=nh.cpu().numpy())
 
 
+def assert_same_bits(a, b, path="out"):
+    """Two runs of the same GPU path on the same inputs produced identical bits
+    (dicts, lists, torch tensors on any device, numpy arrays, scalars)."""
+    if isinstance(a, dict):
+        assert a.keys() == b.keys(), path
+        for k in a:
+            assert_same_bits(a[k], b[k], f"{path}.{k}")
+    elif isinstance(a, (list, tuple)):
+        assert len(a) == len(b), path
+        for i, (x, y) in enumerate(zip(a, b)):
+            assert_same_bits(x, y, f"{path}[{i}]")
+    elif torch.is_tensor(a):
+        assert a.dtype == b.dtype and a.shape == b.shape, path
+        assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), path
+    elif isinstance(a, np.ndarray):
+        assert a.dtype == b.dtype and a.shape == b.shape, path
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8)), path
+    else:
+        assert a == b or (a != a and b != b), path
+
+
 def oracle_bonus_table(steps_ahead, sigma, lam):
     """[n_tags][1] float64 bonus table: tag 0 = no span, tag k+1 = span k (PACE Eq. 2)."""
     return np.array([[0.0]] + [[o_policy.foresight_bonus(sigma, lam, s)] for s in steps_ahead])

@@ -111,6 +111,21 @@ def test_select_rejects_small_kept_stride():
     assert lib.kvc_select(ctypes.byref(d), FAKE, ctypes.byref(p), FAKE, 511, FAKE, None, 0, None) == _lib.KVC_ERR_ARG
 
 
+def test_select_with_a_floor_table_needs_a_full_length_list():
+    # PASK §3.5: floors take precedence over the budget, so a floor table can
+    # make any token protected; the kept list must then hold all T entries.
+    lib = _lib.load()
+    d = _dims()
+    p = _policy()
+    p.tag_floor = FAKE
+    assert lib.kvc_select(ctypes.byref(d), FAKE, ctypes.byref(p), FAKE, 512, FAKE, None, 0, None) == _lib.KVC_ERR_ARG
+    assert lib.kvc_select(ctypes.byref(d), FAKE, ctypes.byref(p), FAKE, 4095, FAKE, None, 0, None) == _lib.KVC_ERR_ARG
+    # T <= budget keeps every token: the usual min(budget, T) suffices
+    d = _dims(n_tokens=300)
+    p.budget = 300
+    assert lib.kvc_select(ctypes.byref(d), FAKE, ctypes.byref(p), FAKE, 299, FAKE, None, 0, None) == _lib.KVC_ERR_ARG
+
+
 def test_compact_rejects_bad_outputs():
     lib = _lib.load()
     d = _dims()

@@ -179,7 +179,8 @@ def test_commitkv_small_end_to_end(bind):
 
 
 def test_commitkv_full_size_sampled():
-    """16 trajectories x 28 layers x 4 KV heads, 33,312 tokens in 16-token pages."""
+    """16 trajectories x 28 layers x 4 KV heads, 33,312 tokens in 16-token pages; a second run
+    is bit-identical."""
     w = synth.COMMIT_WORKLOADS["commitkv_28l"]
     inp = synth.make_commit_inputs(w, "cuda")
     W, ps, P, Bp = w.window, w.page_size, w.n_pages_all, w.budget // w.page_size
@@ -260,3 +261,5 @@ def test_commitkv_full_size_sampled():
     # the compacted pool and the paged view of the original storage decode alike
     np.testing.assert_allclose(res["o1"], res["o2"], rtol=8e-3, atol=1e-3)
     executor.shutdown()
+    # a second run of the whole commit gives the same bits
+    tl.assert_same_bits(res, run_commit(w, inp, [w.tau_joint, 0.5 * j_all]))

@@ -119,7 +119,8 @@ def test_pask_small_every_row(name):
 
 @pytest.mark.parametrize("name", ["pask_llama3_8b", "pask_llama3_8b_int4"])
 def test_pask_full_size_sampled_rows(name):
-    """64 sequences x 32 layers (4 groups) x 8 KV heads: 4096 prompt + 1024 generated tokens."""
+    """64 sequences x 32 layers (4 groups) x 8 KV heads: 4096 prompt + 1024 generated tokens;
+    a second run is bit-identical."""
     w = synth.PASK_WORKLOADS[name]
     inp = synth.make_pask_inputs(w, "cuda")
     res = run_pask(w, inp)
@@ -138,3 +139,5 @@ def test_pask_full_size_sampled_rows(name):
     n_L = np.repeat((a == o_pask.L_ACT).sum(-1)[:, :, None], Hkv, axis=2).reshape(-1)
     np.testing.assert_array_equal(res["n_h"], w.budget + n_H)
     np.testing.assert_array_equal(res["n_l"], n_L)
+    # a second run of the whole workload gives the same bits
+    tl.assert_same_bits(res, run_pask(w, inp))

@@ -103,6 +103,39 @@ def test_protection_beyond_budget_keeps_every_protected_token():
     assert st == 0  # floor excess that the host cannot see is reported through n_kept only
 
 
+def test_floor_excess_survives_compaction():
+    # PASK §3.5 "floors take precedence" and App. B.4 "floor excess is recorded":
+    # 400 floored tokens + 4 sinks + 16 recent exceed B = 256; with the full-length
+    # list the selection requires, compaction keeps every one of them, in order.
+    from budgeted_retention_amd import kvc
+    rng = np.random.default_rng(19)
+    rows, T, B, d = 2, 8192, 256, 64
+    dev = torch.device("cuda")
+    scores = torch.from_numpy(rng.random((rows, T)).astype(np.float32)).to(dev)
+    tags = np.zeros(T, np.uint8)
+    tags[1000:1400] = 1
+    pol = kvc.Policy(4, 16, B, 2, 1, 0, 1, torch.from_numpy(tags).to(dev),
+                     torch.zeros((2, 1), dtype=torch.float32, device=dev),
+                     torch.tensor([[0], [1]], dtype=torch.uint8, device=dev))
+    dims = kvc.make_dims(1, 1, rows, rows, d, T)
+    kept = torch.full((rows, T), -1, dtype=torch.int32, device=dev)
+    nk = torch.zeros(rows, dtype=torch.int32, device=dev)
+    assert kvc.kvc_select(dims, scores, pol, kept, T, nk) == 0
+    K = torch.randn((1, 1, rows, T, d), device=dev).to(torch.bfloat16)
+    V = torch.randn_like(K)
+    Ko = torch.zeros((rows, T, d), dtype=torch.bfloat16, device=dev)
+    Vo = torch.zeros_like(Ko)
+    po = torch.full((rows, T), -1, dtype=torch.int32, device=dev)
+    nh = torch.zeros(rows, dtype=torch.int32, device=dev)
+    kvc.kvc_compact_rerotate(dims, K, V, None, kept, T, nk, -1, 1e4, kvc.CompactOut(T, Ko, Vo, po, nh))
+    torch.cuda.synchronize()
+    want = np.concatenate([np.arange(4), np.arange(1000, 1400), np.arange(T - 16, T)])
+    for r in range(rows):
+        assert int(nk[r]) == want.size == int(nh[r])
+        np.testing.assert_array_equal(po[r, :want.size].cpu().numpy(), want)
+        assert torch.equal(Vo[r, :want.size], V[0, 0, r, torch.from_numpy(want).to(dev)])
+
+
 @pytest.mark.parametrize("T,B", [(300, 512), (512, 512), (4097, 700), (10_001, 1000), (131_075, 2048)])
 def test_short_ragged_and_long_rows(T, B):
     rng = np.random.default_rng(T)
