@@ -26,7 +26,7 @@ def _run_select(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=Non
     from budgeted_retention_amd import kvc
     rows, T = scores.shape
     dims = kvc.make_dims(1, 1, rows, rows, 64, T)
-    ks = kept_stride or min(B, T)
+    ks = kept_stride or (T if floor is not None and T > B else min(B, T))   # floors need the full list
     dev = torch.device("cuda")
     pol = kvc.Policy(n_sink, n_recent, B, bonus.shape[0], 1, 0, 1,
                      None if tags is None else torch.from_numpy(tags).to(dev),
@@ -164,9 +164,12 @@ def test_split_path_long_rows(T, rows):
 
 
 def test_split_path_floors_beyond_budget_and_short_kept_list():
-    """Long rows whose protected tokens exceed the budget keep all of them
-    (n_kept reports the count; only kept_stride entries are written); a row
-    no longer than the budget keeps everything."""
+    """Long rows whose protected tokens exceed the budget keep all of them. A
+    floor table needs a full-length list (a shorter one is refused before
+    anything runs); sink + recent alone beyond the budget report the count in
+    n_kept and write only kept_stride entries. A row no longer than the
+    budget keeps everything."""
+    from budgeted_retention_amd import _lib
     rng = np.random.default_rng(21)
     T, B = 300_000, 1024
     scores = rng.random((2, T)).astype(np.float32)
@@ -174,12 +177,16 @@ def test_split_path_floors_beyond_budget_and_short_kept_list():
     tags[50_000:52_000] = 1
     floor = np.array([[0], [1]], np.uint8)
     bonus = np.zeros((2, 1))
-    st, kept, n_kept = _run_select(scores, tags, bonus, floor, 4, 16, B, kept_stride=B)
-    ref = _oracle(scores[0], tags, bonus, floor, 4, 16, B)
-    assert ref.size == 4 + 16 + 2000 and np.all(n_kept == ref.size)
+    with pytest.raises(_lib.KvcError):
+        _run_select(scores, tags, bonus, floor, 4, 16, B, kept_stride=B)
+    _check(scores, tags, bonus, floor, 4, 16, B, kept_stride=T)
+    # 4 sinks + 1,100 recent > B, no table: the first B of the protected set are written
+    st, kept, n_kept = _run_select(scores, tags, bonus, None, 4, 1100, B, kept_stride=B)
+    ref = _oracle(scores[0], tags, bonus, None, 4, 1100, B)
+    assert st == _lib.KVC_WARN_FLOOR_EXCESS
+    assert ref.size == 4 + 1100 and np.all(n_kept == ref.size)
     for r in range(2):
         np.testing.assert_array_equal(kept[r], ref[:B].astype(np.int32))
-    _check(scores, tags, bonus, floor, 4, 16, B, kept_stride=T)
     # T <= budget on the split path: every token, in order
     small = rng.random((3, 40_000)).astype(np.float32)
     st, kept, n_kept = _run_select(small, None, np.zeros((1, 1)), None, 4, 16, 50_000, kept_stride=50_000)
@@ -206,9 +213,9 @@ def test_per_row_tags(T, rows):
     dev = torch.device("cuda")
     pol = kvc.Policy(4, 16, B, 4, 1, 0, 1, torch.from_numpy(tags).to(dev),
                      torch.from_numpy(bonus.astype(np.float32)).to(dev), torch.from_numpy(floor).to(dev), tag_rows=1)
-    kept = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
+    kept = torch.full((rows, T), -1, dtype=torch.int32, device=dev)      # a floor table: full-length lists
     n_kept = torch.zeros(rows, dtype=torch.int32, device=dev)
-    kvc.kvc_select(dims, torch.from_numpy(scores).to(dev), pol, kept, B, n_kept)
+    kvc.kvc_select(dims, torch.from_numpy(scores).to(dev), pol, kept, T, n_kept)
     torch.cuda.synchronize()
     kept, n_kept = kept.cpu().numpy(), n_kept.cpu().numpy()
     for r in sorted({0, 1, rows - 1}):
