@@ -67,6 +67,8 @@ PROTOTYPES = {
     "kvc_foresight_bonus": (c_double, [c_double, c_double, c_double]),
     "kvc_score": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_int32,
                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kvc_score_noalloc": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "kvc_score_noalloc_max_bytes": (c_size_t, []),
     "kvc_pool_scores": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "kvc_select": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, ctypes.POINTER(KvcPolicy),
                                   c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -28,6 +28,8 @@
 // pass 2 computes C[qrow][key] (a lane owns one key: the sum over query rows
 // stays in-lane).
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "kvc_internal.h"
 
@@ -484,28 +486,103 @@ int launch_window_stats(const kvc_dims *d, const uint16_t *K, const uint16_t *Q,
 
 }  // namespace kvc
 
+namespace kvc {
+
+// Argument checks shared by both score entry points; on success `need` holds
+// the workspace bytes the call uses.
+static int score_check(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
+                       const float *scores, const char *who, size_t *need) {
+    int st = check_dims(dims, who);
+    if (st != KVC_OK) return st;
+    if (!K || !Q_obs || !scores) return fail(KVC_ERR_ARG, "%s: NULL tensor pointer", who);
+    if (W <= 0 || W > dims->n_tokens)
+        return fail(KVC_ERR_ARG, "%s: W=%d must be in [1, T=%lld]", who, W, (long long)dims->n_tokens);
+    const int G = dims->n_q_heads / dims->n_kv_heads;
+    if ((int64_t)G * W > SCORE_MAX_QR)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: W*G=%d exceeds %d query rows", who, G * W, SCORE_MAX_QR);
+    *need = score_workspace_bytes(dims, W);
+    return KVC_OK;
+}
+
+// The score kernels over a checked call, with `ws` (>= the bytes score_check
+// reported) as their scratch.
+static int score_enqueue(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
+                         float *scores, void *ws, hipStream_t s);
+
+// ---------------------------------------------------------------- the no-allocation variant
+//
+// Scratch of kvc_score_noalloc: a file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends). Host code
+// never uses the array's name as an address: it takes each device's address
+// once, through hipGetSymbolAddress with that device current, and passes
+// that pointer to the kernels.
+static constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static std::vector<void *> g_scratch_ptr;   // per device ordinal; NULL until first looked up
+
+static int scratch_pointer(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(KVC_ERR_HIP, "kvc_score_noalloc: no current device");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KVC_ERR_HIP, "kvc_score_noalloc: hipGetSymbolAddress of the scratch array failed: %s",
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVC_OK;
+}
+
+}  // namespace kvc
+
 using namespace kvc;
+
+extern "C" size_t kvc_score_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+extern "C" int kvc_score_noalloc(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
+                                 float *scores, void *stream) {
+    size_t need = 0;
+    int st = score_check(dims, K, Q_obs, W, scores, "kvc_score_noalloc", &need);
+    if (st != KVC_OK) return st;
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(KVC_ERR_WORKSPACE,
+                    "kvc_score_noalloc: the call needs %zu bytes of scratch, above the library's static %zu "
+                    "(fewer rows or shorter rows per call, or kvc_score with a workspace)",
+                    need, NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((st = scratch_pointer(&ws)) != KVC_OK) return st;
+    return score_enqueue(dims, K, Q_obs, W, scores, ws, as_stream(stream));
+}
 
 extern "C" int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
                          float *scores, void *ws, size_t ws_bytes, void *stream) {
-    int st = check_dims(dims, "kvc_score");
+    size_t need = 0;
+    int st = score_check(dims, K, Q_obs, W, scores, "kvc_score", &need);
     if (st != KVC_OK) return st;
-    if (!K || !Q_obs || !scores) return fail(KVC_ERR_ARG, "kvc_score: NULL tensor pointer");
-    if (W <= 0 || W > dims->n_tokens)
-        return fail(KVC_ERR_ARG, "kvc_score: W=%d must be in [1, T=%lld]", W, (long long)dims->n_tokens);
-    const int G = dims->n_q_heads / dims->n_kv_heads;
-    if ((int64_t)G * W > SCORE_MAX_QR)
-        return fail(KVC_ERR_UNSUPPORTED, "kvc_score: W*G=%d exceeds %d query rows", G * W, SCORE_MAX_QR);
-    const size_t need = score_workspace_bytes(dims, W);
     if (!ws || ws_bytes < need)
         return fail(KVC_ERR_WORKSPACE, "kvc_score: workspace %zu < %zu bytes", ws_bytes, need);
+    return score_enqueue(dims, K, Q_obs, W, scores, ws, as_stream(stream));
+}
+
+namespace kvc {
+
+static int score_enqueue(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
+                         float *scores, void *ws, hipStream_t s) {
+    int st;
+    const int G = dims->n_q_heads / dims->n_kv_heads;
     float2 *part = reinterpret_cast<float2 *>(ws);
     const int64_t rows = n_rows(dims), T = dims->n_tokens;
     const int64_t n_chunks = window_chunks(T);
     const int nb = (G * W + 31) / 32, QRP = nb * 32;
     float *mm = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
                                           align256((size_t)rows * n_chunks * QRP * sizeof(float2)));
-    hipStream_t s = as_stream(stream);
     st = launch_window_stats(dims, K, Q_obs, W, WindowGeom{T - W, T, -1}, rows, part, mm, s);
     if (st != KVC_OK) return st;
     const int64_t blocks = rows * n_chunks;
@@ -520,3 +597,5 @@ extern "C" int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t
     }
 #undef P2
 }
+
+}  // namespace kvc

@@ -86,6 +86,14 @@ def kvc_score(dims, K, Q_obs, W, scores, ws, stream=None):
 
 
 
+def kvc_score_noalloc(dims, K, Q_obs, W, scores, stream=None):
+    """kvc_score without a workspace: the library's static scratch array."""
+    st = _lib.load().kvc_score_noalloc(
+        ctypes.byref(dims), _ptr(K, torch.bfloat16, "K"), _ptr(Q_obs, torch.bfloat16, "Q_obs"), W,
+        _ptr(scores, torch.float32, "scores"), _stream(stream))
+    return _lib.check(st)
+
+
 KVC_POOL_MAX, KVC_POOL_AVG = 0, 1
 
 

@@ -88,6 +88,22 @@ size_t kvc_workspace_bytes(int op, const kvc_dims *dims, int32_t W, int32_t B);
 int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
               float *scores, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * kvc_score for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It
+ * takes no workspace; its scratch is a static device array of the library,
+ * kvc_score_noalloc_max_bytes() bytes (16 MiB) on every GPU the library runs
+ * on, held until the process ends. Same arguments, kernels and results as
+ * kvc_score; calls whose workspace (kvc_workspace_bytes(KVC_OP_SCORE, ...))
+ * would exceed the array return KVC_ERR_WORKSPACE before touching the device.
+ * The call allocates nothing and enqueues on `stream` only.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialised by the caller.
+ */
+int kvc_score_noalloc(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
+                      float *scores, void *stream);
+size_t kvc_score_noalloc_max_bytes(void);
+
 /* Pooling modes of kvc_pool_scores. */
 enum { KVC_POOL_MAX = 0, KVC_POOL_AVG = 1 };
 
