@@ -69,6 +69,8 @@ PROTOTYPES = {
                                  c_void_p, c_void_p, c_size_t, c_void_p]),
     "kvc_score_noalloc": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "kvc_score_noalloc_max_bytes": (c_size_t, []),
+    "kvc_score_options": (ctypes.c_int, [c_int32, ctypes.c_int64, c_int32]),
+    "kvc_score_status": (ctypes.c_int, [c_void_p, c_void_p]),
     "kvc_pool_scores": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "kvc_select": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, ctypes.POINTER(KvcPolicy),
                                   c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),

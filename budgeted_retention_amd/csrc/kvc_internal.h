@@ -89,6 +89,15 @@ int launch_window_stats(const kvc_dims *d, const uint16_t *K, const uint16_t *Q,
                         int64_t rows_local, float2 *part, float *mm, hipStream_t s);
 int64_t window_chunks(int64_t kend);
 
+// The single-read score kernel (score_once.hip): the number of workgroups it
+// would run with for these dims on the current device (0: not applicable), and
+// its workspace bytes; its launch (after a 256-byte control block the kernel
+// clears); its wait bound and the diagnostic switch that stops the merges.
+int score_once_plan(const kvc_dims *d, int W, size_t *ws_bytes);
+int launch_score_once(const kvc_dims *d, const uint16_t *K, const uint16_t *Q, int W, float *scores, void *ws,
+                      int nwg, hipStream_t s);
+void set_score_wait(int64_t wait_us, bool no_merge);
+
 // Lane exchanges inside a row of 16 lanes through DPP (no LDS traffic):
 // quad_perm [1,0,3,2] and [2,3,0,1], then half-row and row mirrors. After the
 // steps for N lanes every lane of each aligned group of N holds the group's

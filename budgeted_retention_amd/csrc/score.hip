@@ -47,14 +47,25 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t window_chunks(int64_t kend) { return (kend + STATS_CHUNK - 1) / STATS_CHUNK; }
 
-// kvc_score workspace: chunk partials [rows][QRP][n_chunks] then the merged
-// normalisers [rows][QRP].
-size_t score_workspace_bytes(const kvc_dims *d, int32_t W) {
+// kvc_score workspace: a 256-byte control block (word 0: the call's status),
+// then either path's scratch: the two passes' chunk partials [rows][QRP][n_chunks]
+// and merged normalisers [rows][QRP], or the single-read kernel's exchange words.
+static size_t two_pass_bytes(const kvc_dims *d, int32_t W) {
     const int G = d->n_q_heads / d->n_kv_heads;
     const int QRP = ((G * W + 31) / 32) * 32;
     const int64_t rows = n_rows(d);
     const int64_t nch = window_chunks(d->n_tokens);
     return align256((size_t)rows * nch * QRP * sizeof(float2)) + align256((size_t)rows * QRP * sizeof(float));
+}
+
+static bool g_single_read = false;  // kvc_score_options (the single-read kernel measured slower)
+
+// Covers both paths (whichever kvc_score_options selects when the call runs).
+size_t score_workspace_bytes(const kvc_dims *d, int32_t W) {
+    size_t once_bytes = 0;
+    const size_t two = two_pass_bytes(d, W) + 256;
+    if (score_once_plan(d, W, &once_bytes) > 0 && once_bytes > two) return once_bytes;
+    return two;
 }
 
 // Stage the row's queries in fragment order (zero rows beyond QR).
@@ -408,8 +419,9 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_pass2(const uint16_t *__r
                                                              const uint16_t *__restrict__ Q, int64_t T, int W,
                                                              int G, int L, int Hkv, int Hq, int64_t n_chunks,
                                                              float c2, const float *__restrict__ mm,
-                                                             float *__restrict__ scores) {
+                                                             float *__restrict__ scores, unsigned *__restrict__ ctl) {
     constexpr int QRP = NB * 32;
+    if (blockIdx.x == 0 && threadIdx.x == 0) ctl[0] = 0u;   // the two passes never give up
     extern __shared__ uint4 sq[];
     __shared__ float4 s_mm[QRP / 4];
     const int64_t r = blockIdx.x / n_chunks;
@@ -440,10 +452,10 @@ static int launch_pass1(int64_t blocks, hipStream_t s, const uint16_t *K, const 
 template <int D, int NB>
 static int launch_pass2(int64_t blocks, hipStream_t s, const uint16_t *K, const uint16_t *Q, int64_t T, int W,
                         int G, int L, int Hkv, int Hq, int64_t n_chunks, float c2, const float *mm,
-                        float *scores) {
+                        float *scores, unsigned *ctl) {
     const size_t lds = (size_t)NB * (D / 16) * 64 * sizeof(uint4);
     score_pass2<D, NB><<<dim3((unsigned)blocks), dim3(SCORE_THREADS), lds, s>>>(K, Q, T, W, G, L, Hkv, Hq,
-                                                                               n_chunks, c2, mm, scores);
+                                                                               n_chunks, c2, mm, scores, ctl);
     return check_launch("kvc_score pass 2");
 }
 
@@ -546,6 +558,28 @@ using namespace kvc;
 
 extern "C" size_t kvc_score_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
+extern "C" int kvc_score_options(int32_t single_read, int64_t wait_us, int32_t diag_no_merge) {
+    if (single_read != 0 && single_read != 1) return fail(KVC_ERR_ARG, "kvc_score_options: single_read must be 0 or 1");
+    if (wait_us < 0) return fail(KVC_ERR_ARG, "kvc_score_options: wait_us must be >= 0");
+    g_single_read = single_read != 0;
+    set_score_wait(wait_us, diag_no_merge != 0);
+    return KVC_OK;
+}
+
+extern "C" int kvc_score_status(const void *ws, void *stream) {
+    void *p = const_cast<void *>(ws);
+    if (!p) {
+        const int st = scratch_pointer(&p);
+        if (st != KVC_OK) return st;
+    }
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return fail(KVC_ERR_HIP, "kvc_score_status: stream");
+    unsigned w = 0;
+    if (hipMemcpy(&w, p, sizeof(w), hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(KVC_ERR_HIP, "kvc_score_status: copy of the status word failed");
+    if (w != 0u) return fail(KVC_ERR_HIP, "kvc_score: the single-read kernel gave up waiting (status %u)", w);
+    return KVC_OK;
+}
+
 extern "C" int kvc_score_noalloc(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
                                  float *scores, void *stream) {
     size_t need = 0;
@@ -576,6 +610,11 @@ namespace kvc {
 static int score_enqueue(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
                          float *scores, void *ws, hipStream_t s) {
     int st;
+    size_t once_bytes = 0;
+    const int nwg = g_single_read ? score_once_plan(dims, W, &once_bytes) : 0;
+    if (nwg > 0) return launch_score_once(dims, K, Q_obs, W, scores, ws, nwg, s);
+    unsigned *ctl = reinterpret_cast<unsigned *>(ws);
+    ws = reinterpret_cast<char *>(ws) + 256;
     const int G = dims->n_q_heads / dims->n_kv_heads;
     float2 *part = reinterpret_cast<float2 *>(ws);
     const int64_t rows = n_rows(dims), T = dims->n_tokens;
@@ -589,7 +628,7 @@ static int score_enqueue(const kvc_dims *dims, const uint16_t *K, const uint16_t
     if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_score: grid too large");
     const float c2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
     const int L = dims->n_layers, Hkv = dims->n_kv_heads, Hq = dims->n_q_heads;
-#define P2(DD, NN) launch_pass2<DD, NN>(blocks, s, K, Q_obs, T, W, G, L, Hkv, Hq, n_chunks, c2, mm, scores)
+#define P2(DD, NN) launch_pass2<DD, NN>(blocks, s, K, Q_obs, T, W, G, L, Hkv, Hq, n_chunks, c2, mm, scores, ctl)
     if (dims->head_dim == 128) {
         KVC_NB_SWITCH(nb, 128, P2)
     } else {

@@ -94,6 +94,15 @@ def kvc_score_noalloc(dims, K, Q_obs, W, scores, stream=None):
     return _lib.check(st)
 
 
+def kvc_score_options(single_read=False, wait_us=200000, diag_no_merge=False):
+    return _lib.check(_lib.load().kvc_score_options(int(single_read), int(wait_us), int(diag_no_merge)))
+
+
+def kvc_score_status(ws=None, stream=None):
+    """Status of the last kvc_score call on `ws` (None: the last no-allocation call)."""
+    return _lib.check(_lib.load().kvc_score_status(_ptr(ws, None, "ws"), _stream(stream)))
+
+
 KVC_POOL_MAX, KVC_POOL_AVG = 0, 1
 
 

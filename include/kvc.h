@@ -82,11 +82,41 @@ size_t kvc_workspace_bytes(int op, const kvc_dims *dims, int32_t W, int32_t B);
  *   Q_obs   bf16 [N][L][Hq][W][d]   rotated queries of the last W positions
  *   W       1 <= W <= T, W*G <= 256
  *   scores  fp32 [N][L][Hkv][T]     output, sums to W*G per row
- *   ws      device workspace of kvc_workspace_bytes(KVC_OP_SCORE, dims, W, 0) bytes
+ *   ws      device workspace of kvc_workspace_bytes(KVC_OP_SCORE, dims, W, 0) bytes;
+ *           its first 32-bit word is the call's status once the stream has
+ *           reached the end of the call (kvc_score_status)
  * Supported: d in {64, 128}. Deterministic (no float atomics).
+ *
+ * K is read twice: a statistics pass, then the scores. With
+ * kvc_score_options(1, ...), rows of d = 128, W*G = 128 and 32,768 <= T <=
+ * about 106,000 (a 100K-token Qwen3-8B-shaped row) read K once instead: a
+ * persistent kernel, one workgroup per CU (a cooperative launch), keeps each
+ * row's exponentials on chip until the row's normalisers are merged across
+ * the chip. Every wait in it is bounded; a wait that runs out (only possible
+ * if the workgroups were not all resident) ends the kernel early and sets
+ * the status word. On MI355X it is measured slower than the two passes, so
+ * it is off by default.
  */
 int kvc_score(const kvc_dims *dims, const uint16_t *K, const uint16_t *Q_obs, int32_t W,
               float *scores, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Options of kvc_score (process-wide; set them while no kvc_score call is
+ * being enqueued): single_read = 1 uses the single-read kernel where it
+ * applies, 0 (default) always reads K twice; wait_us bounds every wait of the
+ * single-read kernel (default 200000); diag_no_merge = 1 stops the kernel's
+ * merges so that every wait for merged values runs out (a test of the
+ * give-up path; 0 in normal use). Returns KVC_ERR_ARG on bad values.
+ */
+int kvc_score_options(int32_t single_read, int64_t wait_us, int32_t diag_no_merge);
+
+/*
+ * Synchronises `stream` and reads the status word of the last kvc_score call
+ * on workspace `ws` (NULL: the last kvc_score_noalloc call on the current
+ * device). KVC_OK, or KVC_ERR_HIP when the single-read kernel gave up (the
+ * scores of the rows it did not finish are undefined).
+ */
+int kvc_score_status(const void *ws, void *stream);
 
 /*
  * kvc_score for callers that cannot allocate device memory: code under HIP
