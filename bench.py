@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="scratch written before every timed step so no step starts from cached data "
                          "(the 256 MB memory-side cache); 0 disables it")
+    ap.add_argument("--layers-per-call", type=int, default=36,
+                    help="layers per kvc_score / kvc_select / kvc_compact_rerotate call of the 100K "
+                         "session (a divisor of 36); one group is selected and compacted on a second "
+                         "stream while the next is scored")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), so that HBM "
                          "counters can be scaled against a transfer of known size")
@@ -272,93 +276,115 @@ def oracle_bonus(steps_ahead):
 # ---------------------------------------------------------------- workloads
 
 def bench_compaction(args, w, dev):
-    """score -> select -> compact over every row (one layer per call for the
-    1M-token session), then decode over the compacted cache."""
+    """score -> select -> compact over every row, then decode over the
+    compacted cache. The layers go in groups of --layers-per-call (all 36 in
+    one call by default for the 100K session, one layer per call for the
+    1M-token session). With several groups the scores of group g+1 are
+    computed on one stream while group g is selected and compacted on a
+    second stream (both at the default priority). The step is timed from the
+    first launch to the last compaction's end event."""
     import torch
     from budgeted_retention_amd import kvc, synth
     inp = synth.make_compaction_inputs(w, dev)
     N, L, Hkv, Hq, d, T, W, B = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
                                  w.n_tokens, w.window, w.budget)
     per_layer = w.n_tokens > (1 << 20) - 1
-    chunks = [(l, l + 1) for l in range(L)] if per_layer else [(0, L)]
-    Lc = chunks[0][1] - chunks[0][0]
+    Lc = 1 if per_layer else (args.layers_per_call or L)
+    if L % Lc:
+        raise SystemExit(f"--layers-per-call {Lc} must divide {L} layers")
+    chunks = [(l, l + Lc) for l in range(0, L, Lc)]
+    nc = len(chunks)
     rows_c = N * Lc * Hkv
     dims = kvc.make_dims(N, Lc, Hkv, Hq, d, T)
     vals = [0.0] + [0.0 if s is None else kvc.kvc_foresight_bonus(1e3, 0.35, s) for s in inp.spans.steps_ahead]
     bonus = torch.tensor(vals, dtype=torch.float32, device=dev).reshape(-1, 1)
     pols = [kvc.Policy(w.n_sink, w.n_recent, B, len(vals), 1, l0, L, inp.tags, bonus) for l0, _ in chunks]
     ws = kvc.workspace(kvc.KVC_OP_SCORE, dims, W, 0, dev)
-    scores = torch.empty((rows_c, T), dtype=torch.float32, device=dev)
-    kept = torch.empty((rows_c, B), dtype=torch.int32, device=dev)
-    n_kept = torch.empty(rows_c, dtype=torch.int32, device=dev)
-    Ko = torch.empty((rows_c, B, d), dtype=torch.bfloat16, device=dev)
+    n_sel = kvc.kvc_workspace_bytes(kvc.KVC_OP_SELECT, dims, 0, B)
+    ws_sel = torch.empty(n_sel, dtype=torch.uint8, device=dev) if n_sel else None
+    # every group its own buffers: the two streams never touch the same memory
+    scores = torch.empty((nc, rows_c, T), dtype=torch.float32, device=dev)
+    kept = torch.empty((nc, rows_c, B), dtype=torch.int32, device=dev)
+    n_kept = torch.empty((nc, rows_c), dtype=torch.int32, device=dev)
+    Ko = torch.empty((nc, rows_c, B, d), dtype=torch.bfloat16, device=dev)
     Vo = torch.empty_like(Ko)
-    po = torch.empty((rows_c, B), dtype=torch.int32, device=dev)
-    nh = torch.empty(rows_c, dtype=torch.int32, device=dev)
-    out = kvc.CompactOut(B, Ko, Vo, po, nh)
+    po = torch.empty((nc, rows_c, B), dtype=torch.int32, device=dev)
+    nh = torch.empty((nc, rows_c), dtype=torch.int32, device=dev)
+    outs = [kvc.CompactOut(B, Ko[c], Vo[c], po[c], nh[c]) for c in range(nc)]
     dims_d = kvc.make_dims(N, Lc, Hkv, Hq, d, B)
     wsd = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_d, B, 0)), dtype=torch.uint8, device=dev)
-    o = torch.empty((N, Lc, Hq, d), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((nc, N, Lc, Hq, d), dtype=torch.bfloat16, device=dev)
     views = []
     for l0, l1 in chunks:
         Kc, Vc, Qc, qc = inp.K[:, l0:l1], inp.V[:, l0:l1], inp.Q_obs[:, l0:l1], inp.q_dec[:, l0:l1]
         assert all(t.is_contiguous() for t in (Kc, Vc, Qc, qc))
         views.append((Kc, Vc, Qc, qc))
     names = ["kvc_score", "kvc_select", "kvc_compact_rerotate", "kvc_decode_attn"]
+    s_score = torch.cuda.current_stream()
+    s_comp = torch.cuda.Stream()              # default priority
+    last_comp = [torch.cuda.Event()]          # the previous step's last event on s_comp
 
-    def step(ev=None):
-        for (Kc, Vc, Qc, qc), pol in zip(views, pols):
-            if ev is not None:
-                ev.append(torch.cuda.Event(enable_timing=True))
-                ev[-1].record()
-            kvc.kvc_score(dims, Kc, Qc, W, scores, ws)
-            if ev is not None:
-                ev.append(torch.cuda.Event(enable_timing=True))
-                ev[-1].record()
-            kvc.kvc_select(dims, scores, pol, kept, B, n_kept)
-            if ev is not None:
-                ev.append(torch.cuda.Event(enable_timing=True))
-                ev[-1].record()
-            kvc.kvc_compact_rerotate(dims, Kc, Vc, None, kept, B, n_kept, w.renumber_base, w.rope_base, out)
-            if ev is not None:
-                ev.append(torch.cuda.Event(enable_timing=True))
-                ev[-1].record()
-            kvc.kvc_decode_attn(dims_d, qc, Ko, Vo, nh, B, o, wsd)
-            if ev is not None:
-                ev.append(torch.cuda.Event(enable_timing=True))
-                ev[-1].record()
+    def ev(stream):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(rec=None):
+        s_score.wait_event(last_comp[0])
+        t = {n: [] for n in names}
+        t["start"] = ev(s_score)
+        for c, ((Kc, Vc, Qc, qc), pol) in enumerate(zip(views, pols)):
+            a = ev(s_score)
+            kvc.kvc_score(dims, Kc, Qc, W, scores[c], ws, stream=s_score)
+            b = ev(s_score)
+            t["kvc_score"].append((a, b))
+            s_comp.wait_event(b)
+            a = ev(s_comp)
+            kvc.kvc_select(dims, scores[c], pol, kept[c], B, n_kept[c], ws_sel, stream=s_comp)
+            b = ev(s_comp)
+            t["kvc_select"].append((a, b))
+            kvc.kvc_compact_rerotate(dims, Kc, Vc, None, kept[c], B, n_kept[c], w.renumber_base, w.rope_base,
+                                     outs[c], stream=s_comp)
+            e = ev(s_comp)
+            t["kvc_compact_rerotate"].append((b, e))
+        t["end"] = e
+        for c, (_, _, _, qc) in enumerate(views):   # after the path, off its critical stream order
+            a = ev(s_comp)
+            kvc.kvc_decode_attn(dims_d, qc, Ko[c], Vo[c], nh[c], B, o[c], wsd, stream=s_comp)
+            t["kvc_decode_attn"].append((a, ev(s_comp)))
+        last_comp[0] = torch.cuda.Event()
+        last_comp[0].record(s_comp)
+        if rec is not None:
+            rec.append(t)
 
     calibrate_copy(args, dev)
     flush = torch.empty(max(1, args.flush_mb) * (1 << 18), dtype=torch.float32, device=dev) if args.flush_mb else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    recs = []
     t0 = time.perf_counter()
     for k in range(args.steps):
         if flush is not None:
+            s_score.wait_event(last_comp[0])
             flush.fill_(float(k))   # outside the step's events
-        step(evs[k])
+        step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_step = []
-    part = {n: 0.0 for n in names}
-    for ev in evs:
-        one = {n: 0.0 for n in names}
-        for c in range(len(chunks)):
-            for i, n in enumerate(names):
-                one[n] += ev[5 * c + i].elapsed_time(ev[5 * c + i + 1])
+    per_step, part = [], {n: 0.0 for n in names}
+    for t in recs:
+        one = {n: sum(a.elapsed_time(b) for a, b in t[n]) for n in names}
+        one["path"] = t["start"].elapsed_time(t["end"])
         per_step.append(one)
         for n in names:
             part[n] += one[n]
     part = {n: v / args.steps for n, v in part.items()}
-    path_sums = sorted(o["kvc_score"] + o["kvc_select"] + o["kvc_compact_rerotate"] for o in per_step)
-    median_ms = path_sums[len(path_sums) // 2] if len(path_sums) % 2 else \
-        0.5 * (path_sums[len(path_sums) // 2 - 1] + path_sums[len(path_sums) // 2])
+    path_ms = sorted(o_["path"] for o_ in per_step)
+    median_ms = path_ms[len(path_ms) // 2] if len(path_ms) % 2 else \
+        0.5 * (path_ms[len(path_ms) // 2 - 1] + path_ms[len(path_ms) // 2])
     if not (n_kept == B).all():
         raise SystemExit("bench: a row kept a number of tokens other than the budget")
-    mean_ms = part["kvc_score"] + part["kvc_select"] + part["kvc_compact_rerotate"]
+    mean_ms = sum(path_ms) / len(path_ms)
     ms = median_ms
     ab = compaction_bytes(w.rows, T, d, w.group, W, B)
     path_calls = names[:3]
@@ -389,15 +415,20 @@ def bench_compaction(args, w, dev):
     copy_gbs = copy_bandwidth(dev)
     extra = {"hbm_frac_path": round(ab["path"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "ms_mean": round(mean_ms, 4), "timing": f"median of {args.steps} steps, each after writing "
-             f"{args.flush_mb} MiB of scratch",
+             f"{args.flush_mb} MiB of scratch; a step runs from the first score launch to the last "
+             f"compaction's end event; {nc} group(s) of {Lc} layers"
+             + (", each group selected and compacted on a second stream while the next is scored"
+                if nc > 1 else ""),
              "copy_GB_s": copy_gbs, "roofline_frac_of_copy": round(roof["achieved"] / copy_gbs, 4),
              "breakdown_ms": {n: round(part[n], 4) for n in path_calls},
              "decode_ms": round(part["kvc_decode_attn"], 4),
              "calls": per_call_rates(ab, part),
              "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}
     if not per_layer and w.renumber_base >= 0:
-        extra["ref_store"] = bench_ref_store(args, w, dims, views[0][0], views[0][1], kept, n_kept, Ko, Vo, po, dev)
-        extra["pool"] = bench_pool(args, dims, scores)
+        dims_all = kvc.make_dims(N, L, Hkv, Hq, d, T)      # every group at once: the whole session
+        extra["ref_store"] = bench_ref_store(args, w, dims_all, inp.K, inp.V, kept.view(-1, B), n_kept.view(-1),
+                                             Ko.view(-1, B, d), Vo.view(-1, B, d), po.view(-1, B), dev)
+        extra["pool"] = bench_pool(args, dims_all, scores.view(-1, T))
     return value, ms, config, roof, cpu, extra
 
 
