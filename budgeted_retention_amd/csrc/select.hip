@@ -740,6 +740,293 @@ struct SplitWs {
 
 static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Short rows (T <= 8192): one wave per row, four rows per workgroup, no
+// workgroup barriers. Lane l holds the keys of tokens 256k + 4l .. 256k + 4l + 3
+// (k < NPL4) in registers; the budget-th key is found with the same three
+// radix digits (11, 11, 10 bits) over the wave's own LDS histogram, the
+// crossing bin by a wave scan of per-lane bin sums; the ordered write walks
+// the 256-token blocks in order with wave scans of the per-lane counts.
+// Each tag's bonus and floor are one 32-bit table entry: the bonus, or the
+// bit pattern SW_FLOOR for a floored tag (a NaN bonus is stored as the
+// canonical NaN, so it still ranks lowest).
+static constexpr int SW_WAVES = 4;
+static constexpr uint32_t SW_FLOOR = 0x7FFFFFFFu;
+
+// A wave's LDS operations execute in issue order; this keeps the compiler from
+// moving LDS accesses of one lane across accesses of the other lanes.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t sw_key(int j, float score, float bt, int lo, uint32_t span) {
+    if ((uint32_t)(j - lo) >= span || __float_as_uint(bt) == SW_FLOOR) return KEY_PROTECTED;
+    return order_key(score + bt);
+}
+
+template <int NPL4, bool VEC>
+__global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per_eu(NPL4 <= 16 ? 4 : 2)))
+    select_wave(const float *__restrict__ scores, const uint8_t *__restrict__ tags,
+                const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int Ti, int64_t rows,
+                int L, int Hkv, int n_groups, int layer_base, int n_layers_model, int n_tags, int tag_rows,
+                int n_sink, int n_recent, int B, int32_t *__restrict__ kept, int kept_stride,
+                int32_t *__restrict__ n_kept) {
+    __shared__ __align__(16) uint32_t s_hist[SW_WAVES][SEL_BINS];
+    __shared__ float s_tab[SW_WAVES][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r = (int64_t)blockIdx.x * SW_WAVES + wave;
+    if (r >= rows) return;
+    const RowIdx ri = split_row(r, L, Hkv);
+    const int grp = device_layer_group(layer_base + ri.l, n_layers_model, n_groups);
+    float *tab = s_tab[wave];
+    uint32_t *hist = s_hist[wave];
+    for (int t = lane; t < 256; t += 64) {
+        const int u = t < n_tags ? t : 0;   // tags beyond the table read tag 0
+        float b = 0.f;
+        if (u < n_tags) {
+            b = bonus ? bonus[u * n_groups + grp] : 0.f;
+            if (b != b) b = __uint_as_float(0x7FC00000u);
+            if (floor_tbl && floor_tbl[u * n_groups + grp]) b = __uint_as_float(SW_FLOOR);
+        }
+        tab[t] = b;
+    }
+    wave_lds_order();
+    const float *sr = scores + (size_t)r * Ti;
+    const uint8_t *tr = tags ? tags + (size_t)(tag_rows ? r : ri.n) * Ti : nullptr;
+    const int lo = n_sink;
+    const int hi = Ti - n_recent;
+    const uint32_t span = hi > lo ? (uint32_t)(hi - lo) : 0u;
+    const float b0 = tab[0];
+
+    // All loads first (score bits into key[][], four tags per word), then the
+    // keys in place. Tokens past T get key 0 (the key of a NaN total): they
+    // sit after every real token in index order, so the ordered write never
+    // reaches them, and `pads` of them are taken out of histogram bin 0.
+    uint32_t key[NPL4][SEL_VEC], tg[NPL4];
+#pragma unroll
+    for (int k = 0; k < NPL4; ++k) {
+        const int base = k * 256 + 4 * lane;
+        if (VEC && base + SEL_VEC <= Ti) {
+            const uint4 sv = *reinterpret_cast<const uint4 *>(sr + base);
+            key[k][0] = sv.x;
+            key[k][1] = sv.y;
+            key[k][2] = sv.z;
+            key[k][3] = sv.w;
+            tg[k] = tr ? *reinterpret_cast<const uint32_t *>(tr + base) : 0u;
+        } else {
+            tg[k] = 0u;
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) {
+                const int j = base + e;
+                key[k][e] = j < Ti ? __float_as_uint(sr[j]) : 0u;
+                if (tr && j < Ti) tg[k] |= (uint32_t)tr[j] << (8 * e);
+            }
+        }
+    }
+    // Protected tokens are kept whatever the budget; the histograms rank only
+    // the others ("real" tokens) by d = key - kmin, so that the first digit's
+    // 2048 bins span the range of real keys actually present (score totals sit
+    // within a few octaves, and a fixed top digit would put most of them in a
+    // handful of bins). kmax1 tracks max(key + 1): a protected key wraps to 0.
+    const bool b0_floor = __float_as_uint(b0) == SW_FLOOR;
+    auto inner = [&](int k) { return k * 256 >= lo && k * 256 + 256 <= hi; };
+    auto plain = [&](int k) { return inner(k) && !tr && !b0_floor; };
+    uint32_t nprot = 0u, kmin = 0xFFFFFFFFu, kmax1 = 0u;
+#pragma unroll
+    for (int k = 0; k < NPL4; ++k) {
+        if (plain(k)) {
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) {
+                const uint32_t kk = order_key(__uint_as_float(key[k][e]) + b0);
+                key[k][e] = kk;
+                kmin = min(kmin, kk);
+                kmax1 = max(kmax1, kk + 1u);
+            }
+        } else if (inner(k) && !tr) {   // a floored tag 0 protects every token
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) key[k][e] = KEY_PROTECTED;
+            nprot += SEL_VEC;
+        } else {
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) {
+                const int j = k * 256 + 4 * lane + e;
+                const float bt = tr ? tab[(tg[k] >> (8 * e)) & 0xFF] : b0;
+                const uint32_t kk = j < Ti ? sw_key(j, __uint_as_float(key[k][e]), bt, lo, span) : 0u;
+                key[k][e] = kk;
+                nprot += (j < Ti && kk == KEY_PROTECTED) ? 1u : 0u;
+                kmin = min(kmin, j < Ti ? kk : 0xFFFFFFFFu);
+                kmax1 = max(kmax1, j < Ti ? kk + 1u : 0u);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the live range to one block of keys
+    }
+    const uint32_t pads = (uint32_t)(NPL4 * 256 - Ti);
+
+    uint32_t tau = 0u;
+    int need;
+    if (Ti <= B) {
+        // keep every real token: all keys above 0, and the real tokens with key 0
+        uint32_t zeros = 0u;
+#pragma unroll
+        for (int k = 0; k < NPL4; ++k)
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) zeros += (uint32_t)__popcll(__ballot(key[k][e] == 0u));
+        need = (int)(zeros - pads);
+    } else {
+        nprot = __builtin_amdgcn_readlane(wave_incl_scan(nprot), 63);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+            kmax1 = max(kmax1, (uint32_t)__shfl_xor((int)kmax1, o));
+        }
+        if (nprot >= (uint32_t)B) {   // protected tokens fill the budget: keep them all
+            tau = KEY_PROTECTED;
+            need = Ti;
+        } else {
+            uint4 *h4 = reinterpret_cast<uint4 *>(hist);
+            auto clear = [&]() {
+#pragma unroll
+                for (int t = 0; t < SEL_BINS / 256; ++t) h4[t * 64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+                wave_lds_order();
+            };
+            // In the order from the top bin down, lane l owns the `per` bins
+            // l*per .. l*per + per - 1 (read four at a time, starting at a
+            // lane-rotated offset to spread the reads over the banks); the
+            // first lane whose running count reaches kr holds the wanted key,
+            // and its bins are then resolved one per lane.
+            auto pick = [&](int nbins, uint32_t kr, uint32_t &bin, uint32_t &rank) {
+                const int per = nbins / 64;
+                const uint4 *mine = reinterpret_cast<const uint4 *>(hist + nbins - (lane + 1) * per);
+                uint32_t sum = 0u;
+                for (int q = 0; q < per / 4; ++q) {
+                    const uint4 v = mine[(q + lane) & (per / 4 - 1)];
+                    sum += v.x + v.y + v.z + v.w;
+                }
+                const uint32_t incl = wave_incl_scan(sum);
+                const int src = __ffsll((unsigned long long)__ballot(incl >= kr)) - 1;
+                const uint32_t before = __shfl(incl - sum, src);
+                const uint32_t c = lane < per ? hist[nbins - 1 - src * per - lane] : 0u;
+                const uint32_t incl2 = before + wave_incl_scan(c);
+                const int at = __ffsll((unsigned long long)__ballot(incl2 >= kr)) - 1;
+                bin = (uint32_t)(nbins - 1 - src * per - at);
+                rank = kr - __shfl(incl2 - c, at);
+                wave_lds_order();
+            };
+            // adds one to hist[digit(d)] for every real key with match(d)
+            auto count = [&](auto match, auto digit) {
+                clear();
+#pragma unroll
+                for (int k = 0; k < NPL4; ++k) {
+                    if (plain(k)) {
+#pragma unroll
+                        for (int e = 0; e < SEL_VEC; ++e) {
+                            const uint32_t d = key[k][e] - kmin;
+                            if (match(d)) atomicAdd(&hist[digit(d)], 1u);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < SEL_VEC; ++e) {
+                            const uint32_t d = key[k][e] - kmin;
+                            const bool real = key[k][e] != KEY_PROTECTED && k * 256 + 4 * lane + e < Ti;
+                            if (real && match(d)) atomicAdd(&hist[digit(d)], 1u);
+                        }
+                    }
+                }
+                wave_lds_order();
+            };
+            const uint32_t range = kmax1 - 1u - kmin;
+            const int bl = range ? 32 - __clz(range) : 0;   // bits of d
+            const int s0 = bl > 11 ? bl - 11 : 0;           // first digit: d >> s0 (< 2048)
+            const int w1 = s0 < 11 ? s0 : 11, s1 = s0 - w1;  // then bits [s0-1 : s1], then [s1-1 : 0]
+            uint32_t kr = (uint32_t)B - nprot;
+            uint32_t dt;
+            count([](uint32_t) { return true; }, [&](uint32_t d) { return d >> s0; });
+            pick(SEL_BINS, kr, dt, kr);
+            if (w1) {
+                count([&](uint32_t d) { return (d >> s0) == dt; },
+                      [&](uint32_t d) { return (d >> s1) & ((1u << w1) - 1u); });
+                uint32_t b1;
+                pick(w1 >= 8 ? 1 << w1 : 256, kr, b1, kr);
+                dt = (dt << w1) | b1;
+            }
+            if (s1) {
+                count([&](uint32_t d) { return (d >> s1) == dt; },
+                      [&](uint32_t d) { return d & ((1u << s1) - 1u); });
+                uint32_t b2;
+                pick(s1 >= 8 ? 1 << s1 : 256, kr, b2, kr);
+                dt = (dt << s1) | b2;
+            }
+            tau = kmin + dt;
+            need = (int)kr;
+        }
+    }
+    // ordered write: key > tau, and the first `need` keys == tau by index
+    int32_t *out = kept + (size_t)r * kept_stride;
+    int gt_run = 0, eq_run = 0;
+    int lane4 = 4 * lane;
+    asm volatile("" : "+v"(lane4));   // token indices are recomputed here, not kept live from the loads
+#pragma unroll
+    for (int k = 0; k < NPL4; ++k) {
+        const int base = k * 256 + lane4;
+        uint32_t ngt = 0, neq = 0;
+#pragma unroll
+        for (int e = 0; e < SEL_VEC; ++e) {
+            ngt += key[k][e] > tau;
+            neq += key[k][e] == tau;
+        }
+        if (__ballot(neq != 0u) == 0ull) {
+            // no key of this block equals tau: keep exactly the keys above it
+            const uint32_t incl = wave_incl_scan(ngt);
+            const int tot = (int)__builtin_amdgcn_readlane(incl, 63);
+            int pos = gt_run + (eq_run < need ? eq_run : need) + (int)(incl - ngt);
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e)
+                if (key[k][e] > tau) {
+                    if (pos < kept_stride) out[pos] = base + e;
+                    ++pos;
+                }
+            gt_run += tot;
+        } else {
+            const uint32_t packed = ngt | (neq << 16);
+            const uint32_t incl = wave_incl_scan(packed);
+            const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+            int gt_before = gt_run + (int)((incl - packed) & 0xFFFFu);
+            int eq_before = eq_run + (int)((incl - packed) >> 16);
+#pragma unroll
+            for (int e = 0; e < SEL_VEC; ++e) {
+                const bool gt = key[k][e] > tau;
+                const bool eq = key[k][e] == tau;
+                if (gt || (eq && eq_before < need)) {
+                    const int pos = gt_before + (eq_before < need ? eq_before : need);
+                    if (pos < kept_stride) out[pos] = base + e;
+                }
+                gt_before += gt;
+                eq_before += eq;
+            }
+            gt_run += (int)(tot & 0xFFFFu);
+            eq_run += (int)(tot >> 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (lane == 0) n_kept[r] = gt_run + (eq_run < need ? eq_run : need);
+}
+
+template <int NPL4>
+static void launch_select_wave(bool vec, int64_t rows, hipStream_t s, const float *scores, const kvc_policy *p,
+                               const kvc_dims *dims, int32_t *kept, int kept_stride, int32_t *n_kept) {
+    const dim3 grid((unsigned)((rows + SW_WAVES - 1) / SW_WAVES)), block(SW_WAVES * 64);
+    if (vec)
+        select_wave<NPL4, true><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, (int)dims->n_tokens,
+                                                       rows, dims->n_layers, dims->n_kv_heads, p->n_groups,
+                                                       p->layer_base, p->n_layers_model, p->n_tags, p->tag_rows,
+                                                       p->n_sink, p->n_recent, p->budget, kept, kept_stride, n_kept);
+    else
+        select_wave<NPL4, false><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, (int)dims->n_tokens,
+                                                        rows, dims->n_layers, dims->n_kv_heads, p->n_groups,
+                                                        p->layer_base, p->n_layers_model, p->n_tags, p->tag_rows,
+                                                        p->n_sink, p->n_recent, p->budget, kept, kept_stride, n_kept);
+}
+
 static bool select_use_split(const kvc_dims *d) {
     const int64_t T = d->n_tokens, rows = n_rows(d);
     return T >= 262144 || (rows < 128 && T >= 32768);
@@ -1061,7 +1348,17 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
     hipStream_t s = as_stream(stream);
     // rows whose decision map fits in LDS next to the candidate list
     const size_t cand_lds = (size_t)2 * SEL_CAND * sizeof(uint32_t) + (size_t)2 * ((T + 31) / 32) * sizeof(uint32_t);
-    if (select_use_split(dims)) {
+    if (T <= 8192) {
+        const int64_t rows = n_rows(dims);
+        if (T <= 1024)
+            launch_select_wave<4>(vec, rows, s, scores, p, dims, kept_idx, kept_stride, n_kept);
+        else if (T <= 2048)
+            launch_select_wave<8>(vec, rows, s, scores, p, dims, kept_idx, kept_stride, n_kept);
+        else if (T <= 4096)
+            launch_select_wave<16>(vec, rows, s, scores, p, dims, kept_idx, kept_stride, n_kept);
+        else
+            launch_select_wave<32>(vec, rows, s, scores, p, dims, kept_idx, kept_stride, n_kept);
+    } else if (select_use_split(dims)) {
         const size_t need = select_workspace_bytes(dims);
         if (!ws || ws_bytes < need)
             return fail(KVC_ERR_WORKSPACE, "kvc_select: workspace %zu < %zu bytes (long rows)", ws_bytes, need);

@@ -222,3 +222,56 @@ def test_per_row_tags(T, rows):
         ref = _oracle(scores[r], tags[r], bonus, floor, 4, 16, B)
         assert n_kept[r] == ref.size
         np.testing.assert_array_equal(kept[r][: ref.size], ref.astype(np.int32))
+
+
+def _short_scores(rng, dist, rows, T):
+    if dist == "wide":      # both signs over 60 decades, NaNs, exact ties
+        s = np.sign(rng.random((rows, T)) - 0.3) * 10.0 ** rng.uniform(-30, 30, (rows, T))
+        s[:, ::97] = np.nan
+        s[:, ::13] = s[:, min(5, T - 1):min(5, T - 1) + 1]
+    elif dist == "narrow":  # every total within a few float32 steps of 1
+        s = 1.0 + rng.integers(0, 64, (rows, T)) * 2.0 ** -23
+    elif dist == "equal":
+        s = np.full((rows, T), 0.25)
+    else:                   # softmax-sum-like: a few heavy tokens over a small floor
+        s = rng.gamma(0.3, 1.0 / max(T, 1), (rows, T))
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("T", [1, 5, 63, 256, 257, 1000, 1024, 1025, 2047, 2048, 3001, 4096, 4099, 6000, 8192])
+@pytest.mark.parametrize("dist", ["wide", "narrow", "equal", "gamma"])
+def test_short_rows_one_wave_per_row(T, dist):
+    """Rows of at most 8192 tokens are selected one wave per row (four rows
+    per workgroup, six rows here so the last workgroup is partial): every
+    register-block count, ragged lengths (scalar loads), totals of both signs
+    with NaNs and ties, totals a few float32 steps apart, all-equal totals,
+    and per-token tags with a negative bonus and a floored tag."""
+    rng = np.random.default_rng(T * 7 + len(dist))
+    rows = 6
+    scores = _short_scores(rng, dist, rows, T)
+    B = max(1, T // 3)
+    # a full-length list: in the shortest rows the sinks and recent window alone exceed B
+    _check(scores, None, np.zeros((1, 1)), None, 4, 16, B, kept_stride=T)
+    tags = rng.integers(0, 4, T).astype(np.uint8)
+    bonus = np.array([[0.0], [0.5], [-3.0], [1e3]])
+    floor = np.array([[0], [0], [0], [1]], np.uint8)
+    tags[rng.random(T) < 0.9] = 0   # about 2.5% of tokens floored
+    _check(scores, tags, bonus, floor, 4, 16, B, kept_stride=T)
+    _check(scores, tags, bonus, None, 0, 0, B, kept_stride=T)
+
+
+@pytest.mark.parametrize("T,B,n_sink,n_recent,floored", [(4096, 100, 64, 64, 0), (3000, 200, 4, 16, 500),
+                                                          (2048, 20, 4, 16, 0), (1000, 1, 0, 0, 0),
+                                                          (8192, 8191, 4, 16, 0)])
+def test_short_rows_protection_at_and_beyond_the_budget(T, B, n_sink, n_recent, floored):
+    """Protected tokens (sinks, recent window, floored tags) ranked outside the
+    histograms: more of them than the budget keeps exactly them; fewer leaves
+    the rest of the budget to the highest real totals; B = 1 and B = T - 1."""
+    rng = np.random.default_rng(B)
+    scores = rng.random((5, T)).astype(np.float32)
+    tags = np.zeros(T, np.uint8)
+    if floored:
+        tags[rng.choice(T, floored, replace=False)] = 1
+    bonus = np.zeros((2, 1))
+    floor = np.array([[0], [1]], np.uint8)
+    _check(scores, tags, bonus, floor if floored else None, n_sink, n_recent, B, kept_stride=T)
