@@ -95,6 +95,39 @@ def page_tokens(first, page_size):
     return np.arange(first, first + page_size, dtype=np.int64)
 
 
+def event_pages(event_lengths, G, start=0):
+    """Event pages (CommitKV §3.1, "Agent events and commit transitions"):
+    every event is partitioned into contiguous pages of at most G tokens, so no
+    page spans two events. Reading: an event is cut from its first token into
+    pages of G tokens, the last one shorter. Events follow each other from
+    token ``start``. Returns (first, length), int64, in token order.
+    """
+    first, length = [], []
+    t = int(start)
+    for n_ev in event_lengths:
+        off = 0
+        while off < n_ev:
+            ln = min(int(G), int(n_ev) - off)
+            first.append(t + off)
+            length.append(ln)
+            off += ln
+        t += int(n_ev)
+    return np.asarray(first, np.int64), np.asarray(length, np.int64)
+
+
+def page_scores_spans(row_scores, first, length):
+    """page_scores for pages given as token spans [first[e], first[e] + length[e])."""
+    per_token = np.asarray(row_scores, np.float64).sum(axis=0)
+    return np.array([per_token[f:f + ln].sum() for f, ln in zip(np.asarray(first), np.asarray(length))])
+
+
+def retained_tokens(first, length, pages):
+    """The index set of the listed pages (Eq. 13 applied through Eq. 4's single
+    index set): each page's tokens in order, pages in list order."""
+    parts = [np.arange(first[e], first[e] + length[e], dtype=np.int64) for e in pages]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
 def percentile_ranks(R):
     """P(E) = #{E' != E : R(E') < R(E)} / (n - 1)."""
     R = np.asarray(R, np.float64)

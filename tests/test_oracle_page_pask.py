@@ -118,6 +118,42 @@ def test_page_scores_pool_every_row_closed_form():
     assert np.all(ps > 0)
 
 
+def test_event_pages_cut_every_event_into_pages_of_at_most_G():
+    # CommitKV §3.1: events of 37, 5, 16 and 17 tokens with G = 16
+    first, length = pe.event_pages([37, 5, 16, 17], 16)
+    np.testing.assert_array_equal(length, [16, 16, 5, 5, 16, 16, 1])
+    np.testing.assert_array_equal(first, [0, 16, 32, 37, 42, 58, 74])
+    # invariants on random events: the pages tile the events in order, none
+    # longer than G, none crossing an event boundary
+    rng = np.random.default_rng(3)
+    ev = rng.integers(1, 90, 40)
+    for G in (1, 7, 16, 64):
+        first, length = pe.event_pages(ev, G, start=11)
+        assert first[0] == 11 and first[-1] + length[-1] == 11 + ev.sum()
+        np.testing.assert_array_equal(first[1:], first[:-1] + length[:-1])
+        assert length.min() >= 1 and length.max() <= G
+        bounds = 11 + np.concatenate([[0], np.cumsum(ev)])
+        ev_of_first = np.searchsorted(bounds, first, side="right") - 1
+        ev_of_last = np.searchsorted(bounds, first + length - 1, side="right") - 1
+        np.testing.assert_array_equal(ev_of_first, ev_of_last)
+        assert len(first) == sum(-(-int(n) // G) for n in ev)
+
+
+def test_page_scores_spans_and_retained_tokens():
+    S = np.arange(2 * 12, dtype=np.float64).reshape(2, 12)   # per-token sums 12, 14, ..., 34
+    first, length = np.array([0, 3, 5, 10]), np.array([3, 2, 5, 2])
+    np.testing.assert_array_equal(pe.page_scores_spans(S, first, length),
+                                  [12 + 14 + 16, 18 + 20, 22 + 24 + 26 + 28 + 30, 32 + 34])
+    # uniform spans reduce to page_scores
+    rng = np.random.default_rng(4)
+    R = rng.random((5, 96))
+    np.testing.assert_allclose(pe.page_scores_spans(R, np.arange(6) * 16, np.full(6, 16)),
+                               pe.page_scores(R, 16, 6), rtol=1e-15)
+    np.testing.assert_array_equal(pe.retained_tokens(first, length, [3, 0, 2]),
+                                  [10, 11, 0, 1, 2, 5, 6, 7, 8, 9])
+    assert pe.retained_tokens(first, length, []).size == 0
+
+
 def test_retained_pages_hand_built_and_brute_force():
     assert list(pe.retained_pages([5, 1, 5, 3, 7], {4}, 2)) == [0, 2]     # 7 retired; tie to the lower index
     assert list(pe.retained_pages([5, 1, 5, 3, 7], {4}, 4)) == [0, 1, 2, 3]
