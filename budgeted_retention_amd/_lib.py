@@ -88,14 +88,16 @@ PROTOTYPES = {
                                            c_void_p]),
     "kvc_page_workspace_bytes": (c_size_t, [ctypes.POINTER(KvcDims), c_int32, c_int64]),
     "kvc_page_effect": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_int32, c_void_p, c_void_p, c_void_p,
-                                       c_int32, c_int64, c_int32, c_int32, c_void_p, c_void_p,
-                                       c_void_p, c_size_t, c_void_p]),
+                                       c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
+                                       c_void_p, c_void_p, c_size_t, c_void_p]),
     "kvc_page_retire": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_int32, c_void_p, c_void_p, c_void_p,
-                                       c_int32, c_int64, c_int32, c_int32, c_void_p, c_int32,
-                                       ctypes.c_float, c_void_p, c_void_p, c_void_p, c_size_t,
+                                       c_int32, c_int64, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
+                                       c_int32, ctypes.c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
-    "kvc_page_scores": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_int32, c_void_p,
-                                       c_void_p, c_int32, c_void_p, c_void_p]),
+    "kvc_page_scores": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_void_p, c_void_p,
+                                       c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "kvc_page_tokens": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_int32, c_void_p, c_void_p, c_int32,
+                                       c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p]),
     "kvc_host_commit_protect": (ctypes.c_int, [c_void_p, c_void_p, c_int32, c_int32, c_double, c_int32,
                                                c_void_p, c_void_p]),
     "kvc_host_pace_renumber": (ctypes.c_int, [c_int64, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p,

@@ -107,9 +107,27 @@ struct PeArgs {
     const float *mm;
     float *o;
     int page_size, n_pages;
+    const int32_t *pfirst, *plen;   // event pages [N][n_pages], or NULL for uniform pages
     float *eff_rel, *eff_abs;
     float *opart;
 };
+
+// Token span of page e of sequence n: [first, first + len). Event pages are
+// clamped to the cache and to page_size (the longest page).
+__device__ __forceinline__ void page_span(const PeArgs &a, int n, int e, int64_t &first, int &len) {
+    if (a.pfirst) {
+        int64_t f = a.pfirst[(size_t)n * a.n_pages + e];
+        int64_t l = a.plen[(size_t)n * a.n_pages + e];
+        f = f < 0 ? 0 : (f > a.T ? a.T : f);
+        l = l < 0 ? 0 : (l > a.page_size ? a.page_size : l);
+        if (l > a.T - f) l = a.T - f;
+        first = f;
+        len = (int)l;
+    } else {
+        first = (int64_t)e * a.page_size;
+        len = a.page_size;
+    }
+}
 
 // Stages one 64-key tile: a_pi for the block's 32 query rows into sp[32][64]
 // (0 for invisible keys and padding rows) and V into sv[64][D] as fp32.
@@ -259,6 +277,117 @@ __global__ void __launch_bounds__(PE_THREADS) pe_effect(PeArgs a, int chunks_per
             if (a.eff_abs) atomic_max_nonneg(a.eff_abs + (size_t)n_seq_idx * a.n_pages + page, ba);
         }
         __syncthreads();
+    }
+}
+
+// Event pages of at most PE_TILE tokens (page_first / page_len). A workgroup
+// walks its run of PE_SPAN_CHUNK pages: it stages the 64 keys from the first
+// page's first token, takes every following page lying wholly inside them, and
+// goes on from the first page that does not (pages in token order cover each
+// staged tile with at least 64 - page_size + 1 tokens of whole pages).
+static constexpr int PE_SPAN_CHUNK = 256;
+
+template <int D>
+__global__ void __launch_bounds__(PE_THREADS) pe_effect_spans(PeArgs a, int chunks_per_row) {
+    constexpr int DP = D / 2, STRIPES = PE_THREADS / DP, QPS = 32 / STRIPES;
+    __shared__ float sp[32][PE_TILE + 1];
+    __shared__ float sv[PE_TILE][D];
+    __shared__ float s_alpha[32][PE_TILE];
+    __shared__ float s_best[2][STRIPES][PE_TILE];
+    __shared__ int64_t s_first[PE_SPAN_CHUNK];
+    __shared__ int s_len[PE_SPAN_CHUNK];
+    const int nb = (a.G * a.W + 31) / 32;
+    const int64_t rr = blockIdx.x / (nb * chunks_per_row);
+    const int b = (int)((blockIdx.x / chunks_per_row) % nb);
+    const int pc = (int)(blockIdx.x % chunks_per_row);
+    bf16x8 qf[D / 16];
+    float mmq[1];
+    int64_t qposq[1];
+    const uint16_t *Kr, *Vr;
+    pe_load_queries<D>(a, rr, b, qf, mmq, qposq, &Kr, &Vr);
+    const int tid = threadIdx.x, dp = tid % DP, stripe = tid / DP;
+    const int QR = a.G * a.W, QRP = nb * 32;
+    const int n_seq_idx = (int)(rr / a.Hkv);
+    const int e_begin = pc * PE_SPAN_CHUNK;
+    const int e_end = e_begin + PE_SPAN_CHUNK < a.n_pages ? e_begin + PE_SPAN_CHUNK : a.n_pages;
+    for (int e = e_begin + tid; e < e_end; e += PE_THREADS) {
+        int64_t f;
+        int l;
+        page_span(a, n_seq_idx, e, f, l);
+        s_first[e - e_begin] = f;
+        s_len[e - e_begin] = l;
+    }
+    float o0[QPS], o1[QPS], onorm[QPS];
+#pragma unroll
+    for (int q = 0; q < QPS; ++q) {
+        const float *o = a.o + ((size_t)rr * QRP + b * 32 + stripe * QPS + q) * D;
+        o0[q] = o[2 * dp];
+        o1[q] = o[2 * dp + 1];
+        float n2 = o0[q] * o0[q] + o1[q] * o1[q];
+        for (int m = DP / 2; m >= 1; m >>= 1) n2 += __shfl_xor(n2, m);
+        onorm[q] = sqrtf(n2);
+    }
+    __syncthreads();
+    int e = e_begin;
+    while (e < e_end) {   // the same sequence of pages for every thread
+        const int64_t j0 = s_first[e - e_begin];
+        int e1 = e + 1;
+        while (e1 < e_end && e1 - e < PE_TILE && s_first[e1 - e_begin] >= j0 &&
+               s_first[e1 - e_begin] + s_len[e1 - e_begin] <= j0 + PE_TILE)
+            ++e1;
+        const int np = e1 - e;
+        pe_stage_tile<D>(a, Kr, Vr, qf, mmq, qposq, j0, sp, sv);
+        __syncthreads();
+        for (int t = tid; t < 32 * np; t += PE_THREADS) {
+            const int q = t / np, pg = t % np;
+            const int off = (int)(s_first[e - e_begin + pg] - j0), len = s_len[e - e_begin + pg];
+            float al = 0.f;
+            for (int k = 0; k < len; ++k) al += sp[q][off + k];
+            s_alpha[q][pg] = al;
+        }
+        __syncthreads();
+        for (int pg = 0; pg < np; ++pg) {
+            const int off = (int)(s_first[e - e_begin + pg] - j0), len = s_len[e - e_begin + pg];
+            float best_rel = 0.f, best_abs = 0.f;
+#pragma unroll
+            for (int q = 0; q < QPS; ++q) {
+                const int ql = stripe * QPS + q;
+                float t0 = 0.f, t1 = 0.f;
+                for (int k = 0; k < len; ++k) {
+                    const float p = sp[ql][off + k];
+                    t0 = fmaf(p, sv[off + k][2 * dp] - o0[q], t0);
+                    t1 = fmaf(p, sv[off + k][2 * dp + 1] - o1[q], t1);
+                }
+                float n2 = t0 * t0 + t1 * t1;
+                for (int m = DP / 2; m >= 1; m >>= 1) n2 += __shfl_xor(n2, m);
+                if (b * 32 + ql < QR) {
+                    const float al = s_alpha[ql][pg];
+                    const float num = sqrtf(n2);
+                    const float den = 1.f - al;
+                    float ab = den > 0.f ? num / den : INFINITY;
+                    float rel = onorm[q] > 0.f ? ab / onorm[q] : (num > 0.f ? INFINITY : 0.f);
+                    if (!(num > 0.f)) ab = rel = 0.f;
+                    best_rel = fmaxf(best_rel, rel);
+                    best_abs = fmaxf(best_abs, ab);
+                }
+            }
+            if (dp == 0) {
+                s_best[0][stripe][pg] = best_rel;
+                s_best[1][stripe][pg] = best_abs;
+            }
+        }
+        __syncthreads();
+        for (int pg = tid; pg < np; pg += PE_THREADS) {
+            float br = 0.f, ba = 0.f;
+            for (int st = 0; st < STRIPES; ++st) {
+                br = fmaxf(br, s_best[0][st][pg]);
+                ba = fmaxf(ba, s_best[1][st][pg]);
+            }
+            atomic_max_nonneg(a.eff_rel + (size_t)n_seq_idx * a.n_pages + e + pg, br);
+            if (a.eff_abs) atomic_max_nonneg(a.eff_abs + (size_t)n_seq_idx * a.n_pages + e + pg, ba);
+        }
+        __syncthreads();
+        e = e1;
     }
 }
 
@@ -508,7 +637,9 @@ __global__ void __launch_bounds__(PR_THREADS) pr_terms(PeArgs a, const int32_t *
     if (page < 0 || page >= a.n_pages) return;  // skipped by the walk
     const int tid = threadIdx.x;
     const int QR = a.G * a.W, QRP = ((QR + 31) / 32) * 32;
-    const int ps = a.page_size;
+    int64_t pf;
+    int ps;   // this page's tokens pf .. pf + ps - 1 (ps <= PR_PMAX)
+    page_span(a, n, page, pf, ps);
     const int64_t rows_local = (int64_t)gridDim.x / nc;
     const int64_t rr = (int64_t)n * a.Hkv + h;
     const int64_t gr = ((int64_t)n * a.L + a.lsel) * a.Hkv + h;
@@ -516,7 +647,7 @@ __global__ void __launch_bounds__(PR_THREADS) pr_terms(PeArgs a, const int32_t *
     const uint16_t *Vr = a.V + (size_t)gr * a.T * D;
     for (int e = tid; e < ps * D; e += PR_THREADS) {
         const int k = e / D, cc = e % D;
-        const int64_t t = (int64_t)page * ps + k;
+        const int64_t t = pf + k;
         s_k[k][cc] = bf16_to_f32(Kr[(size_t)t * D + cc]);
         s_v[k][cc] = bf16_to_f32(Vr[(size_t)t * D + cc]);
     }
@@ -545,7 +676,7 @@ __global__ void __launch_bounds__(PR_THREADS) pr_terms(PeArgs a, const int32_t *
         float al = 0.f;
 #pragma unroll
         for (int k = 0; k < PR_PMAX; ++k) {
-            const int64_t t = (int64_t)page * ps + k;
+            const int64_t t = pf + k;
             p[k] = (k < ps && t <= qpos) ? __builtin_amdgcn_exp2f(fmaf(p[k], a.c2, -mq)) : 0.f;
             al += p[k];
         }
@@ -741,7 +872,8 @@ __global__ void __launch_bounds__(PR_THREADS) pr_accum(PeArgs a, const int32_t *
 
 static int pe_common_checks(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
                             const uint16_t *Q, int32_t W, int64_t q_first, int32_t page_size,
-                            int32_t n_pages, const char *who) {
+                            const int32_t *page_first, const int32_t *page_len, int32_t n_pages,
+                            const char *who) {
     int st = check_dims(dims, who);
     if (st != KVC_OK) return st;
     if (!K || !V || !Q) return fail(KVC_ERR_ARG, "%s: NULL tensor pointer", who);
@@ -752,6 +884,14 @@ static int pe_common_checks(const kvc_dims *dims, int32_t layer, const uint16_t 
                     (long long)q_first, (long long)(q_first + W), (long long)dims->n_tokens);
     const int G = dims->n_q_heads / dims->n_kv_heads;
     if (G * W > 256) return fail(KVC_ERR_UNSUPPORTED, "%s: W*G = %d exceeds 256", who, G * W);
+    if ((page_first == nullptr) != (page_len == nullptr))
+        return fail(KVC_ERR_ARG, "%s: page_first and page_len go together", who);
+    if (page_first) {   // event pages: page_size bounds their length
+        if (page_size <= 0 || page_size > PE_TILE)
+            return fail(KVC_ERR_UNSUPPORTED, "%s: event pages of up to %d tokens, not %d", who, PE_TILE, page_size);
+        if (n_pages <= 0) return fail(KVC_ERR_ARG, "%s: n_pages %d must be positive", who, n_pages);
+        return KVC_OK;
+    }
     if (page_size <= 0 || PE_TILE % page_size)
         return fail(KVC_ERR_UNSUPPORTED, "%s: page_size %d must divide %d", who, page_size, PE_TILE);
     if (n_pages <= 0 || (int64_t)n_pages * page_size > dims->n_tokens)
@@ -760,8 +900,8 @@ static int pe_common_checks(const kvc_dims *dims, int32_t layer, const uint16_t 
 }
 
 static PeArgs pe_args(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
-                      const uint16_t *Q, int32_t W, int64_t q_first, int32_t page_size, int32_t n_pages,
-                      const PageWs &w) {
+                      const uint16_t *Q, int32_t W, int64_t q_first, int32_t page_size,
+                      const int32_t *page_first, const int32_t *page_len, int32_t n_pages, const PageWs &w) {
     PeArgs a;
     a.K = K;
     a.V = V;
@@ -780,6 +920,8 @@ static PeArgs pe_args(const kvc_dims *dims, int32_t layer, const uint16_t *K, co
     a.o = w.o;
     a.page_size = page_size;
     a.n_pages = n_pages;
+    a.pfirst = page_first;
+    a.plen = page_len;
     a.eff_rel = a.eff_abs = nullptr;
     a.opart = w.opart;
     return a;
@@ -859,6 +1001,149 @@ page_score_kernel(const float *scores, int64_t T, int64_t rows_per_seq, int page
     }
 }
 
+// Event pages (page_first / page_len): one workgroup per (sequence, run of
+// PS_RUN pages). When the run's pages lie within PS_TOK tokens, the token sums
+// are staged as in the uniform kernel; otherwise each thread sums its own page
+// token by token. Both add every token over the rows in order, then the page's
+// tokens in order, so the two give the same bits.
+static constexpr int PS_RUN = 64;
+
+__global__ void __launch_bounds__(PS_THREADS)
+page_score_spans(const float *scores, int64_t T, int64_t rows_per_seq, int page_size, int n_pages,
+                 int runs_per_seq, const int32_t *pfirst, const int32_t *plen, const int32_t *order,
+                 const uint8_t *accepted, int n_cand, float *page_score) {
+    __shared__ float s_tok[PS_TOK];
+    __shared__ int64_t s_f[PS_RUN];
+    __shared__ int s_l[PS_RUN];
+    __shared__ uint8_t s_ret[PS_RUN];
+    __shared__ int64_t s_span[2];
+    const int n = blockIdx.x / runs_per_seq;
+    const int p0 = (blockIdx.x % runs_per_seq) * PS_RUN;
+    const int np = min(PS_RUN, n_pages - p0);
+    const int tid = threadIdx.x;
+    if (tid < 64) {   // wave 0: the run's spans and their extent
+        int64_t f = 0, l = 0;
+        if (tid < np) {
+            f = pfirst[(int64_t)n * n_pages + p0 + tid];
+            l = plen[(int64_t)n * n_pages + p0 + tid];
+            f = f < 0 ? 0 : (f > T ? T : f);
+            l = l < 0 ? 0 : (l > page_size ? page_size : l);
+            if (l > T - f) l = T - f;
+            s_f[tid] = f;
+            s_l[tid] = (int)l;
+            s_ret[tid] = 0;
+        }
+        int64_t lo = l > 0 ? f : T, hi = l > 0 ? f + l : 0;
+        for (int m = 1; m < 64; m <<= 1) {
+            lo = min(lo, (int64_t)__shfl_xor(lo, m));
+            hi = max(hi, (int64_t)__shfl_xor(hi, m));
+        }
+        if (tid == 0) {
+            s_span[0] = lo;
+            s_span[1] = hi;
+        }
+    }
+    __syncthreads();
+    const int64_t lo = s_span[0], hi = s_span[1];
+    const bool staged = hi - lo <= PS_TOK;
+    if (staged && hi > lo) {
+        const float *base = scores + (int64_t)n * rows_per_seq * T + lo;
+        const int ntok = (int)(hi - lo);
+        constexpr int PER = PS_TOK / PS_THREADS;
+        float acc[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+#pragma unroll 4
+        for (int64_t r = 0; r < rows_per_seq; ++r) {
+            const float *row = base + r * T;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int t = tid + k * PS_THREADS;
+                if (t < ntok) acc[k] += row[t];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) s_tok[tid + k * PS_THREADS] = acc[k];
+    }
+    if (order && accepted) {
+        for (int c = tid; c < n_cand; c += PS_THREADS) {
+            const int e = order[(int64_t)n * n_cand + c];
+            if (accepted[(int64_t)n * n_cand + c] && e >= p0 && e < p0 + np) s_ret[e - p0] = 1;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < np; e += PS_THREADS) {
+        float sum = 0.f;
+        if (staged) {
+            for (int i = 0; i < s_l[e]; ++i) sum += s_tok[s_f[e] - lo + i];
+        } else {
+            const float *base = scores + (int64_t)n * rows_per_seq * T + s_f[e];
+            for (int i = 0; i < s_l[e]; ++i) {
+                float tok = 0.f;
+                for (int64_t r = 0; r < rows_per_seq; ++r) tok += base[r * T + i];
+                sum += tok;
+            }
+        }
+        page_score[(int64_t)n * n_pages + p0 + e] = s_ret[e] ? -INFINITY : sum;
+    }
+}
+
+// Page list -> token list, one workgroup per sequence: runs of PT_THREADS
+// listed pages, each thread placing its page's tokens after an exclusive scan
+// of the page lengths.
+static constexpr int PT_THREADS = 256;
+
+__global__ void __launch_bounds__(PT_THREADS)
+page_tokens_kernel(int64_t T, int page_size, int n_pages, const int32_t *pfirst, const int32_t *plen,
+                   const int32_t *pages, const int32_t *n_listed, int list_stride, int32_t *tokens,
+                   int32_t *n_tokens, int out_stride) {
+    __shared__ int s_wave[PT_THREADS / 64];
+    const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int listed = n_listed[n];
+    listed = listed < 0 ? 0 : (listed > list_stride ? list_stride : listed);
+    int64_t total = 0;
+    int32_t *out = tokens + (int64_t)n * out_stride;
+    for (int c0 = 0; c0 < listed; c0 += PT_THREADS) {
+        const int c = c0 + tid;
+        int64_t f = 0;
+        int len = 0;
+        if (c < listed) {
+            const int e = pages[(int64_t)n * list_stride + c];
+            if (e >= 0 && e < n_pages) {
+                if (pfirst) {
+                    int64_t ff = pfirst[(int64_t)n * n_pages + e], ll = plen[(int64_t)n * n_pages + e];
+                    ff = ff < 0 ? 0 : (ff > T ? T : ff);
+                    ll = ll < 0 ? 0 : (ll > page_size ? page_size : ll);
+                    if (ll > T - ff) ll = T - ff;
+                    f = ff;
+                    len = (int)ll;
+                } else {
+                    f = (int64_t)e * page_size;
+                    len = f + page_size <= T ? page_size : (int)(T - f > 0 ? T - f : 0);
+                }
+            }
+        }
+        int incl = len;
+        for (int m = 1; m < 64; m <<= 1) {
+            const int v = __shfl_up(incl, m);
+            if (lane >= m) incl += v;
+        }
+        if (lane == 63) s_wave[wave] = incl;
+        __syncthreads();
+        int before = 0, run = 0;
+        for (int w = 0; w < PT_THREADS / 64; ++w) {
+            if (w < wave) before += s_wave[w];
+            run += s_wave[w];
+        }
+        __syncthreads();
+        const int64_t pos0 = total + before + incl - len;
+        for (int k = 0; k < len; ++k)
+            if (pos0 + k < out_stride) out[pos0 + k] = (int32_t)(f + k);
+        total += run;
+    }
+    if (tid == 0) n_tokens[n] = (int32_t)(total < INT32_MAX ? total : INT32_MAX);
+}
+
 extern "C" size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int64_t q_first) {
     if (check_dims(dims, "kvc_page_workspace_bytes") != KVC_OK) return 0;
     if (W <= 0 || q_first < 0) {
@@ -870,9 +1155,10 @@ extern "C" size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int6
 
 extern "C" int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
                                const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
-                               int32_t n_pages, float *effect_rel, float *effect_abs, void *ws,
-                               size_t ws_bytes, void *stream) {
-    int st = pe_common_checks(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, "kvc_page_effect");
+                               const int32_t *page_first, const int32_t *page_len, int32_t n_pages,
+                               float *effect_rel, float *effect_abs, void *ws, size_t ws_bytes, void *stream) {
+    int st = pe_common_checks(dims, layer, K, V, Q_win, W, q_first, page_size, page_first, page_len, n_pages,
+                              "kvc_page_effect");
     if (st != KVC_OK) return st;
     if (!effect_rel) return fail(KVC_ERR_ARG, "kvc_page_effect: effect_rel is NULL");
     const size_t need = page_ws_layout(dims, W, q_first + W, nullptr, nullptr);
@@ -880,7 +1166,7 @@ extern "C" int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16
         return fail(KVC_ERR_WORKSPACE, "kvc_page_effect: workspace %zu < %zu bytes", ws_bytes, need);
     PageWs w;
     page_ws_layout(dims, W, q_first + W, ws, &w);
-    PeArgs a = pe_args(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, w);
+    PeArgs a = pe_args(dims, layer, K, V, Q_win, W, q_first, page_size, page_first, page_len, n_pages, w);
     a.eff_rel = effect_rel;
     a.eff_abs = effect_abs;
     hipStream_t s = as_stream(stream);
@@ -890,6 +1176,16 @@ extern "C" int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16
     if ((st = check_launch("kvc_page_effect clear")) != KVC_OK) return st;
     if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
     const PageGeom g = page_geom(dims, W, q_first + W);
+    if (page_first) {
+        const int cpr = (n_pages + PE_SPAN_CHUNK - 1) / PE_SPAN_CHUNK;
+        const int64_t blocks = g.rows_local * g.nb * cpr;
+        if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_effect: grid too large");
+        if (dims->head_dim == 128)
+            pe_effect_spans<128><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a, cpr);
+        else
+            pe_effect_spans<64><<<dim3((unsigned)blocks), dim3(PE_THREADS), 0, s>>>(a, cpr);
+        return check_launch("kvc_page_effect");
+    }
     const int64_t n_tok = (int64_t)n_pages * page_size;
     if (page_size == 8 || page_size == 16 || page_size == 32) {
         const int chunks = (int)((n_tok + PO_CHUNK - 1) / PO_CHUNK);
@@ -921,10 +1217,11 @@ extern "C" int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16
 
 extern "C" int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
                                const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
-                               int32_t n_pages, const int32_t *order, int32_t n_cand, float tau_joint,
-                               uint8_t *accepted, float *joint_rel, void *ws, size_t ws_bytes,
-                               void *stream) {
-    int st = pe_common_checks(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, "kvc_page_retire");
+                               const int32_t *page_first, const int32_t *page_len, int32_t n_pages,
+                               const int32_t *order, int32_t n_cand, float tau_joint, uint8_t *accepted,
+                               float *joint_rel, void *ws, size_t ws_bytes, void *stream) {
+    int st = pe_common_checks(dims, layer, K, V, Q_win, W, q_first, page_size, page_first, page_len, n_pages,
+                              "kvc_page_retire");
     if (st != KVC_OK) return st;
     if (!order || !accepted || n_cand <= 0)
         return fail(KVC_ERR_ARG, "kvc_page_retire: order/accepted missing or n_cand <= 0");
@@ -935,7 +1232,7 @@ extern "C" int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16
         return fail(KVC_ERR_WORKSPACE, "kvc_page_retire: workspace %zu < %zu bytes", ws_bytes, need);
     PageWs w;
     page_ws_layout(dims, W, q_first + W, ws, &w);
-    PeArgs a = pe_args(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, w);
+    PeArgs a = pe_args(dims, layer, K, V, Q_win, W, q_first, page_size, page_first, page_len, n_pages, w);
     hipStream_t s = as_stream(stream);
     if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
     const PageGeom g = page_geom(dims, W, q_first + W);
@@ -973,17 +1270,30 @@ extern "C" int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16
 }
 
 extern "C" int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_t page_size,
-                               int32_t n_pages, const int32_t *order, const uint8_t *accepted,
-                               int32_t n_cand, float *page_score, void *stream) {
+                               const int32_t *page_first, const int32_t *page_len, int32_t n_pages,
+                               const int32_t *order, const uint8_t *accepted, int32_t n_cand,
+                               float *page_score, void *stream) {
     int st = check_dims(dims, "kvc_page_scores");
     if (st != KVC_OK) return st;
     if (!scores || !page_score) return fail(KVC_ERR_ARG, "kvc_page_scores: NULL tensor pointer");
     if (page_size <= 0 || page_size > PS_TOK)
         return fail(KVC_ERR_UNSUPPORTED, "kvc_page_scores: page_size %d outside [1, %d]", page_size, PS_TOK);
-    if (n_pages <= 0 || (int64_t)n_pages * page_size > dims->n_tokens)
+    if ((page_first == nullptr) != (page_len == nullptr))
+        return fail(KVC_ERR_ARG, "kvc_page_scores: page_first and page_len go together");
+    if (n_pages <= 0 || (!page_first && (int64_t)n_pages * page_size > dims->n_tokens))
         return fail(KVC_ERR_ARG, "kvc_page_scores: %d pages of %d tokens exceed the cache", n_pages, page_size);
     if ((order == nullptr) != (accepted == nullptr) || (order && n_cand <= 0))
         return fail(KVC_ERR_ARG, "kvc_page_scores: order and accepted go together, with n_cand > 0");
+    const int64_t rows_per_seq_s = (int64_t)dims->n_layers * dims->n_kv_heads;
+    if (page_first) {
+        const int runs = (n_pages + PS_RUN - 1) / PS_RUN;
+        const int64_t blocks = (int64_t)dims->n_seq * runs;
+        if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_scores: grid too large");
+        page_score_spans<<<dim3((unsigned)blocks), dim3(PS_THREADS), 0, as_stream(stream)>>>(
+            scores, dims->n_tokens, rows_per_seq_s, page_size, n_pages, runs, page_first, page_len, order,
+            accepted, order ? n_cand : 0, page_score);
+        return check_launch("kvc_page_scores");
+    }
     const int ppb = PS_TOK / page_size;
     const int bps = (n_pages + ppb - 1) / ppb;
     const int64_t blocks = (int64_t)dims->n_seq * bps;
@@ -993,4 +1303,22 @@ extern "C" int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_
         scores, dims->n_tokens, rows_per_seq, page_size, n_pages, ppb, bps, order, accepted,
         order ? n_cand : 0, page_score);
     return check_launch("kvc_page_scores");
+}
+
+extern "C" int kvc_page_tokens(const kvc_dims *dims, int32_t page_size, const int32_t *page_first,
+                               const int32_t *page_len, int32_t n_pages, const int32_t *pages,
+                               const int32_t *n_listed, int32_t list_stride, int32_t *tokens, int32_t *n_tokens,
+                               int32_t out_stride, void *stream) {
+    int st = check_dims(dims, "kvc_page_tokens");
+    if (st != KVC_OK) return st;
+    if (!pages || !n_listed || !tokens || !n_tokens) return fail(KVC_ERR_ARG, "kvc_page_tokens: NULL pointer");
+    if ((page_first == nullptr) != (page_len == nullptr))
+        return fail(KVC_ERR_ARG, "kvc_page_tokens: page_first and page_len go together");
+    if (page_size <= 0 || page_size > (1 << 20) || n_pages <= 0 || list_stride <= 0 || out_stride <= 0)
+        return fail(KVC_ERR_ARG, "kvc_page_tokens: page_size %d (at most 2^20), n_pages %d, list_stride %d, "
+                    "out_stride %d must be positive", page_size, n_pages, list_stride, out_stride);
+    page_tokens_kernel<<<dim3((unsigned)dims->n_seq), dim3(PT_THREADS), 0, as_stream(stream)>>>(
+        dims->n_tokens, page_size, n_pages, page_first, page_len, pages, n_listed, list_stride, tokens, n_tokens,
+        out_stride);
+    return check_launch("kvc_page_tokens");
 }

@@ -241,34 +241,55 @@ def page_workspace(dims, W, q_first, device="cuda"):
                        device=device)
 
 
+def _pages(page_first, page_len):
+    """Event pages: int32 [N][n_pages] first token and length, both or neither."""
+    if (page_first is None) != (page_len is None):
+        raise ValueError("page_first and page_len go together")
+    return _ptr(page_first, torch.int32, "page_first"), _ptr(page_len, torch.int32, "page_len")
+
+
 def kvc_page_effect(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, effect_rel, ws,
-                    effect_abs=None, stream=None):
+                    effect_abs=None, stream=None, page_first=None, page_len=None):
+    pf, pl = _pages(page_first, page_len)
     st = _lib.load().kvc_page_effect(
         ctypes.byref(dims), layer, _ptr(K, torch.bfloat16, "K"), _ptr(V, torch.bfloat16, "V"),
-        _ptr(Q_win, torch.bfloat16, "Q_win"), W, q_first, page_size, n_pages,
+        _ptr(Q_win, torch.bfloat16, "Q_win"), W, q_first, page_size, pf, pl, n_pages,
         _ptr(effect_rel, torch.float32, "effect_rel"), _ptr(effect_abs, torch.float32, "effect_abs"),
         _ptr(ws, None, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     return _lib.check(st)
 
 
 def kvc_page_retire(dims, layer, K, V, Q_win, W, q_first, page_size, n_pages, order, tau_joint,
-                    accepted, ws, joint_rel=None, stream=None):
+                    accepted, ws, joint_rel=None, stream=None, page_first=None, page_len=None):
     n_cand = order.shape[-1]
+    pf, pl = _pages(page_first, page_len)
     st = _lib.load().kvc_page_retire(
         ctypes.byref(dims), layer, _ptr(K, torch.bfloat16, "K"), _ptr(V, torch.bfloat16, "V"),
-        _ptr(Q_win, torch.bfloat16, "Q_win"), W, q_first, page_size, n_pages,
+        _ptr(Q_win, torch.bfloat16, "Q_win"), W, q_first, page_size, pf, pl, n_pages,
         _ptr(order, torch.int32, "order"), n_cand, float(tau_joint), _ptr(accepted, torch.uint8, "accepted"),
         _ptr(joint_rel, torch.float32, "joint_rel"), _ptr(ws, None, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     return _lib.check(st)
 
 
-def kvc_page_scores(dims, scores, page_size, n_pages, page_score, order=None, accepted=None, stream=None):
+def kvc_page_scores(dims, scores, page_size, n_pages, page_score, order=None, accepted=None, stream=None,
+                    page_first=None, page_len=None):
     n_cand = 0 if order is None else order.shape[-1]
+    pf, pl = _pages(page_first, page_len)
     st = _lib.load().kvc_page_scores(
-        ctypes.byref(dims), _ptr(scores, torch.float32, "scores"), page_size, n_pages,
+        ctypes.byref(dims), _ptr(scores, torch.float32, "scores"), page_size, pf, pl, n_pages,
         _ptr(order, torch.int32, "order"), _ptr(accepted, torch.uint8, "accepted"), n_cand,
         _ptr(page_score, torch.float32, "page_score"), _stream(stream))
+    return _lib.check(st)
+
+
+def kvc_page_tokens(dims, page_size, n_pages, pages, n_listed, tokens, n_tokens, page_first=None,
+                    page_len=None, stream=None):
+    pf, pl = _pages(page_first, page_len)
+    st = _lib.load().kvc_page_tokens(
+        ctypes.byref(dims), page_size, pf, pl, n_pages, _ptr(pages, torch.int32, "pages"),
+        _ptr(n_listed, torch.int32, "n_listed"), pages.shape[-1], _ptr(tokens, torch.int32, "tokens"),
+        _ptr(n_tokens, torch.int32, "n_tokens"), tokens.shape[-1], _stream(stream))
     return _lib.check(st)
 
 

@@ -389,13 +389,27 @@ int kvc_decode_attn_h2o(const kvc_dims *dims, const uint16_t *q, const uint16_t 
 size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int64_t q_first);
 
 /*
+ * Pages (CommitKV §3.1, "Agent events and commit transitions": every event is
+ * partitioned into contiguous pages of at most G tokens, cut at event
+ * boundaries). The page calls below take either
+ *   uniform pages:  page_first = page_len = NULL; page e of every sequence is
+ *                   tokens [e*page_size, (e+1)*page_size); or
+ *   event pages:    page_first, page_len device int32 [N][n_pages]; page e of
+ *                   sequence n is tokens [page_first[n][e],
+ *                   page_first[n][e] + page_len[n][e]), and page_size is the
+ *                   longest a page may be (G). Entries are clamped to [0, T)
+ *                   and to page_size; a page of length 0 has effect 0 and
+ *                   score 0. Pages in token order without overlap run
+ *                   fastest; any order is correct.
+ */
+
+/*
  * CommitKV page deletion effect (CommitKV §3.2, Eq. 6 renormalisation and
  * Eq. 7 relative change; the window of Eq. 5).
  *
  * For the chosen layer, window query w of query head hq sits at position
  * q_first + w and attends to the cached tokens j <= q_first + w (attention
- * weights a_j, output o). For every page E = tokens [e*page_size,
- * (e+1)*page_size), e < n_pages, and every sequence n:
+ * weights a_j, output o). For every page E (e < n_pages) and every sequence n:
  *   effect_rel[n][e] = max over the layer's query heads and window queries of
  *                      ||o - o^{\E}|| / ||o||,  o - o^{\E} = sum_{j in E} a_j (v_j - o) / (1 - alpha_E)
  *   effect_abs[n][e] = the same maximum of ||o - o^{\E}||
@@ -404,14 +418,15 @@ size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int64_t q_first
  *
  *   K, V      bf16 [N][L][Hkv][T][d];  Q_win bf16 [N][L][Hq][W][d] (rotated)
  *   layer     0 <= layer < L;  q_first + W <= T;  W*G <= 256
- *   page_size divides 64;  n_pages*page_size <= T
+ *   pages     uniform: page_size divides 64, n_pages*page_size <= T;
+ *             event pages: 1 <= page_size <= 64
  *   effect_rel fp32 [N][n_pages];  effect_abs fp32 [N][n_pages] or NULL
  *   ws        kvc_page_workspace_bytes(dims, W, q_first) bytes
  */
 int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
                     const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
-                    int32_t n_pages, float *effect_rel, float *effect_abs, void *ws, size_t ws_bytes,
-                    void *stream);
+                    const int32_t *page_first, const int32_t *page_len, int32_t n_pages,
+                    float *effect_rel, float *effect_abs, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * CommitKV greedy joint retirement (CommitKV §3.3, Eq. 11). Per sequence n,
@@ -423,34 +438,55 @@ int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16_t *K, cons
  *
  *   accepted   u8 [N][n_cand] 1 = retired;  joint_rel fp32 [N][n_cand] or NULL
  *              (the joint effect tested for each candidate, -1 for none)
- *   Other arguments as kvc_page_effect; page_size <= 16.
+ *   Other arguments as kvc_page_effect; page_size <= 16 (either kind).
  */
 int kvc_page_retire(const kvc_dims *dims, int32_t layer, const uint16_t *K, const uint16_t *V,
                     const uint16_t *Q_win, int32_t W, int64_t q_first, int32_t page_size,
-                    int32_t n_pages, const int32_t *order, int32_t n_cand, float tau_joint,
-                    uint8_t *accepted, float *joint_rel, void *ws, size_t ws_bytes, void *stream);
+                    const int32_t *page_first, const int32_t *page_len, int32_t n_pages,
+                    const int32_t *order, int32_t n_cand, float tau_joint, uint8_t *accepted,
+                    float *joint_rel, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Page scores for the compression checkpoint (CommitKV §3.3: pages accepted
  * for retirement are excluded and the retained index set, Eq. 13, is applied
  * to keys, values and positions alike, Eq. 4, so one page set serves every
- * layer and head of a sequence). For every sequence n and page
- * e < n_pages (tokens [e*page_size, (e+1)*page_size)):
- *   page_score[n][e] = sum over layers l, KV heads h and tokens j of page e
- *                      of scores[n][l][h][j]            (fp32, fixed order)
- * and -inf for every page order[n][c] with accepted[n][c] != 0 (the outputs
- * of kvc_page_retire; entries outside [0, n_pages) are ignored). Ranking the
- * page scores with kvc_select (dims with T = n_pages, one layer, one head)
- * then keeps the best non-retired pages.
+ * layer and head of a sequence). For every sequence n and page e < n_pages:
+ *   page_score[n][e] = sum over the page's tokens j (in order) of
+ *                      sum over layers l and KV heads h (in order) of scores[n][l][h][j]
+ * in fp32, and -inf for every page order[n][c] with accepted[n][c] != 0 (the
+ * outputs of kvc_page_retire; entries outside [0, n_pages) are ignored).
+ * Ranking the page scores with kvc_select (dims with T = n_pages, one layer,
+ * one head) then keeps the best non-retired pages.
  *
  *   scores      fp32 [N][L][Hkv][T] (from kvc_score)
- *   page_size   1..1024;  n_pages*page_size <= T
+ *   page_size   1..1024;  uniform pages: n_pages*page_size <= T
  *   order, accepted  int32 / u8 [N][n_cand], both NULL for no exclusion
  *   page_score  fp32 [N][n_pages]
  */
-int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_t page_size, int32_t n_pages,
+int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_t page_size,
+                    const int32_t *page_first, const int32_t *page_len, int32_t n_pages,
                     const int32_t *order, const uint8_t *accepted, int32_t n_cand, float *page_score,
                     void *stream);
+
+/*
+ * Token list of per-sequence page lists: the retained index set of CommitKV
+ * §3.3 Eq. 13 as one set of token indices for every layer and head (Eq. 4).
+ * For sequence n the listed pages pages[n][0 .. min(n_listed[n], list_stride))
+ * (for instance kvc_select's kept list over page scores) are expanded in list
+ * order, each page's tokens in order; indices outside [0, n_pages) add
+ * nothing. kvc_compact_rerotate with out->kept_page = 1 then compacts those
+ * tokens, which is how event pages are compacted.
+ *
+ *   pages       int32 [N][list_stride];  n_listed int32 [N]
+ *   tokens      int32 [N][out_stride]: the first out_stride token indices
+ *   n_tokens    int32 [N]: the number of tokens of the listed pages (may
+ *               exceed out_stride; the rest are not written)
+ *   Page arguments as for the calls above, page_size <= 2^20 (dims: n_seq
+ *   and n_tokens only).
+ */
+int kvc_page_tokens(const kvc_dims *dims, int32_t page_size, const int32_t *page_first,
+                    const int32_t *page_len, int32_t n_pages, const int32_t *pages, const int32_t *n_listed,
+                    int32_t list_stride, int32_t *tokens, int32_t *n_tokens, int32_t out_stride, void *stream);
 
 /* ------------------------------------------------------------------------
  * Host-side serial control (plain C on host memory; no GPU work). Their

@@ -193,8 +193,8 @@ def test_compact_page_lists_reject_actions_and_negative_page():
 def test_page_scores_reject_bad_arguments():
     lib = _lib.load()
     d = _dims(n_tokens=1000)
-    call = lambda ps=16, n=62, order=None, acc=None, n_cand=0, sc=FAKE: lib.kvc_page_scores(
-        ctypes.byref(d), sc, ps, n, order, acc, n_cand, FAKE, None)
+    call = lambda ps=16, n=62, order=None, acc=None, n_cand=0, sc=FAKE, pf=None, pl=None: lib.kvc_page_scores(
+        ctypes.byref(d), sc, ps, pf, pl, n, order, acc, n_cand, FAKE, None)
     assert call(sc=None) == _lib.KVC_ERR_ARG
     assert call(ps=0) == _lib.KVC_ERR_UNSUPPORTED
     assert call(ps=2048) == _lib.KVC_ERR_UNSUPPORTED
@@ -202,6 +202,34 @@ def test_page_scores_reject_bad_arguments():
     assert call(order=FAKE) == _lib.KVC_ERR_ARG                  # order without accepted
     assert call(order=FAKE, acc=FAKE, n_cand=0) == _lib.KVC_ERR_ARG
     assert lib.kvc_last_error().decode().startswith("kvc_page_scores")
+    assert call(pf=FAKE) == _lib.KVC_ERR_ARG                     # event pages need both arrays
+    assert call(pl=FAKE) == _lib.KVC_ERR_ARG
+    assert call(pf=FAKE, pl=FAKE, n=0) == _lib.KVC_ERR_ARG
+
+
+def test_event_page_arguments_are_checked_before_any_launch():
+    lib = _lib.load()
+    d = _dims(n_tokens=1000)
+    eff = lambda ps=16, pf=FAKE, pl=FAKE, n=70: lib.kvc_page_effect(
+        ctypes.byref(d), 0, FAKE, FAKE, FAKE, 8, 992, ps, pf, pl, n, FAKE, None, FAKE, 1, None)
+    assert eff(pl=None) == _lib.KVC_ERR_ARG
+    assert eff(pf=None) == _lib.KVC_ERR_ARG
+    assert eff(ps=65) == _lib.KVC_ERR_UNSUPPORTED                # an event page must fit a 64-key tile
+    assert eff(ps=0) == _lib.KVC_ERR_UNSUPPORTED
+    assert eff(n=0) == _lib.KVC_ERR_ARG
+    assert eff(ps=24) == _lib.KVC_ERR_WORKSPACE                  # any length up to 64 passes the page checks
+    assert eff(ps=24, pf=None, pl=None) == _lib.KVC_ERR_UNSUPPORTED  # uniform pages must divide 64
+    ret = lambda ps=16: lib.kvc_page_retire(ctypes.byref(d), 0, FAKE, FAKE, FAKE, 8, 992, ps, FAKE, FAKE, 70,
+                                            FAKE, 4, ctypes.c_float(0.1), FAKE, None, FAKE, 1, None)
+    assert ret(ps=17) == _lib.KVC_ERR_UNSUPPORTED               # retire takes pages of up to 16 tokens
+    tok = lambda ps=16, pf=FAKE, pl=FAKE, pages=FAKE, ls=8, os_=64: lib.kvc_page_tokens(
+        ctypes.byref(d), ps, pf, pl, 70, pages, FAKE, ls, FAKE, FAKE, os_, None)
+    assert tok(pl=None) == _lib.KVC_ERR_ARG
+    assert tok(pages=None) == _lib.KVC_ERR_ARG
+    assert tok(ps=0) == _lib.KVC_ERR_ARG
+    assert tok(ls=0) == _lib.KVC_ERR_ARG
+    assert tok(os_=0) == _lib.KVC_ERR_ARG
+    assert lib.kvc_last_error().decode().startswith("kvc_page_tokens")
 
 
 def test_compact_reference_store_rejects_bad_combinations():
