@@ -109,6 +109,29 @@ extern "C" int kvc_host_pask_control(const kvc_pask_table *tbl, const double *co
     return KVC_OK;
 }
 
+// Per-row physical actions of the generated tokens (PASK §3.2): the group's
+// scheduled action for every layer of the group and every KV head, except the
+// last `recent` tokens, which stay bf16 until they leave the window.
+extern "C" int kvc_host_pask_row_actions(const uint8_t *actions, int32_t n_seq, int32_t n_tok, int32_t n_groups,
+                                         int32_t n_layers, int32_t n_kv_heads, int32_t recent,
+                                         uint8_t *row_actions) {
+    if (!actions || !row_actions || n_seq <= 0 || n_tok < 0 || n_groups <= 0 || n_layers <= 0 ||
+        n_kv_heads <= 0 || recent < 0)
+        return fail(KVC_ERR_ARG, "kvc_host_pask_row_actions: bad arguments");
+    const int32_t first_recent = recent < n_tok ? n_tok - recent : 0;
+    for (int32_t n = 0; n < n_seq; ++n)
+        for (int32_t l = 0; l < n_layers; ++l) {
+            const int32_t g = kvc_layer_group(l, n_layers, n_groups);
+            for (int32_t h = 0; h < n_kv_heads; ++h) {
+                uint8_t *out = row_actions + (((size_t)n * n_layers + l) * n_kv_heads + h) * n_tok;
+                const uint8_t *in = actions + (size_t)n * n_tok * n_groups + g;
+                for (int32_t t = 0; t < first_recent; ++t) out[t] = in[(size_t)t * n_groups];
+                for (int32_t t = first_recent; t < n_tok; ++t) out[t] = 2;   // H
+            }
+        }
+    return KVC_OK;
+}
+
 extern "C" int kvc_host_commit_candidates(const float *R_minus, const float *R_plus, int32_t n_pages,
                                           float tau_use, float tau_dead, float rho_use, float rho_dead,
                                           int32_t max_scan, uint8_t *state, int32_t *order, int32_t *n_order) {

@@ -332,6 +332,17 @@ def kvc_host_pask_control(a0, amin, prio, critical, costs, budget_fraction, tags
     return acts, ledger
 
 
+def kvc_host_pask_row_actions(actions, n_layers, n_kv_heads, recent):
+    """actions: uint8 [n_seq][n_tok][n_groups]. Returns uint8 [n_seq][n_layers][n_kv_heads][n_tok]."""
+    import numpy as np
+    acts = np.ascontiguousarray(actions, np.uint8)
+    n_seq, n_tok, C = acts.shape
+    out = np.zeros((n_seq, n_layers, n_kv_heads, n_tok), np.uint8)
+    _lib.check(_lib.load().kvc_host_pask_row_actions(_np_ptr(acts, np.uint8), n_seq, n_tok, C, n_layers,
+                                                     n_kv_heads, int(recent), _np_ptr(out, np.uint8)))
+    return out
+
+
 def kvc_host_commit_candidates(R_minus, R_plus, tau_use, tau_dead, rho_use, rho_dead, max_scan=64):
     """Returns (state uint8 [n_pages], order int32 [max_scan] padded with -1, n_order)."""
     import numpy as np

@@ -82,15 +82,13 @@ def run_pask(w, inp, timer=None):
     with t("kvc_compact_rerotate:prompt"):
         kvc.kvc_compact_rerotate(dims_p, inp.K, inp.V, None, kept, B, nk, -1, w.rope_base,
                                  kvc.CompactOut(S, Ko, Vo, po, nh0))
-    # controller per generated token, then each row's action from its layer group
+    # controller per generated token, then each row's action (group broadcast, recent window bf16)
     with t("host:kvc_host_pask_control"):
         grp = np.array([kvc.kvc_layer_group(l, L, w.n_groups) for l in range(L)])
         costs = kvc.kvc_host_pask_costs(np.bincount(grp, minlength=w.n_groups), Hkv, d, w.low_bits)
         acts, ledger = kvc.kvc_host_pask_control(inp.a0, inp.amin, inp.prio, inp.critical, costs,
                                                  w.budget_fraction, inp.tags)
-    act_rows = np.ascontiguousarray(np.broadcast_to(
-        acts[:, :, grp].transpose(0, 2, 1)[:, :, None, :], (N, L, Hkv, Tg)))
-    act_rows[..., Tg - w.gen_recent:] = kvc.ACT_BF16      # the recent window stays bf16
+        act_rows = kvc.kvc_host_pask_row_actions(acts, L, Hkv, w.gen_recent)
     action = torch.from_numpy(act_rows.reshape(rows, Tg)).to(dev)
     kept_g = torch.arange(Tg, dtype=torch.int32, device=dev).expand(rows, Tg).contiguous()
     pos_g = (Tp + kept_g).contiguous()

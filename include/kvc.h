@@ -527,6 +527,24 @@ int kvc_host_pask_control(const kvc_pask_table *tbl, const double *costs, double
                           double reserve, const uint8_t *tags, int32_t n_seq, int32_t n_tok,
                           uint8_t *actions, double *ledger);
 
+/*
+ * Per-row physical actions of the generated tokens (PASK §3.2: the layers of
+ * a group share the group's action but keep their own KV tensors; recent
+ * tokens remain high precision and scheduled releases happen after they
+ * leave the window; Appendix B.3 accounts for the recent window apart from
+ * the scheduled payload, so the ledger of kvc_host_pask_control still
+ * charges the scheduled action). For sequence n, layer l, KV head h and
+ * generated token t:
+ *   row_actions[n][l][h][t] = 2 (H)                          if t >= n_tok - recent
+ *                           = actions[n][t][kvc_layer_group(l, n_layers, n_groups)]  otherwise
+ * The result is the `action` argument of kvc_compact_rerotate for the
+ * generated tokens (kept list 0 .. n_tok - 1).
+ *   actions      host u8 [n_seq][n_tok][n_groups] (kvc_host_pask_control)
+ *   row_actions  host u8 [n_seq][n_layers][n_kv_heads][n_tok]
+ */
+int kvc_host_pask_row_actions(const uint8_t *actions, int32_t n_seq, int32_t n_tok, int32_t n_groups,
+                              int32_t n_layers, int32_t n_kv_heads, int32_t recent, uint8_t *row_actions);
+
 /* CommitKV lifecycle states (CommitKV §3.2 Eq. 10). */
 enum {
     KVC_LIFE_UNCERTAIN = 0,

@@ -109,3 +109,34 @@ def control_sequence(tags, table_a0, table_amin, table_prio, table_crit, costs, 
         R = R - M + b
         ledger.append(R)
     return acts, np.array(ledger)
+
+
+def row_actions(actions, n_layers, n_kv_heads, recent):
+    """Per-row physical actions of the generated tokens. PASK §3.2: the
+    layers of a group share its action but keep their own KV tensors, recent
+    tokens remain high precision and scheduled releases happen after they
+    leave the window (Appendix B.3 accounts for that window apart from the
+    scheduled payload, so the ledger still charges the scheduled action).
+
+    actions: [n_seq][n_tok][n_groups] scheduled actions (control_sequence).
+    Returns [n_seq][n_layers][n_kv_heads][n_tok]: H for the last ``recent``
+    tokens, else the action of the layer's group (oracle.policy.layer_group).
+    """
+    acts = np.asarray(actions)
+    n_seq, n_tok, _ = acts.shape
+    out = np.empty((n_seq, n_layers, n_kv_heads, n_tok), np.uint8)
+    for n in range(n_seq):
+        for l in range(n_layers):
+            row = row_action(acts[n], l, n_layers, recent)
+            for h in range(n_kv_heads):
+                out[n, l, h] = row
+    return out
+
+
+def row_action(actions_n, layer, n_layers, recent):
+    """row_actions for one sequence's [n_tok][n_groups] schedule and one layer."""
+    from oracle.policy import layer_group
+    acts = np.asarray(actions_n)
+    n_tok, n_groups = acts.shape
+    g = layer_group(layer, n_layers, n_groups)
+    return np.array([H_ACT if t >= n_tok - recent else acts[t, g] for t in range(n_tok)], np.uint8)

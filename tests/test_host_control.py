@@ -33,6 +33,15 @@ def test_pask_control_matches_oracle(seed, B_D):
         np.testing.assert_allclose(ledger[n], o_ledger, rtol=1e-12, atol=1e-6)
 
 
+@pytest.mark.parametrize("n_layers,n_groups,recent", [(32, 4, 16), (5, 2, 0), (7, 3, 40), (3, 3, 1)])
+def test_pask_row_actions_match_oracle(n_layers, n_groups, recent):
+    rng = np.random.default_rng(n_layers * 10 + recent)
+    n_seq, n_tok, Hkv = 2, 37, 3
+    acts = rng.integers(0, 3, (n_seq, n_tok, n_groups)).astype(np.uint8)
+    got = kvc.kvc_host_pask_row_actions(acts, n_layers, Hkv, recent)
+    np.testing.assert_array_equal(got, o_pask.row_actions(acts, n_layers, Hkv, recent))
+
+
 def test_commit_candidates_match_oracle():
     rng = np.random.default_rng(5)
     n = 500
@@ -59,6 +68,10 @@ def test_host_helpers_reject_bad_arguments():
         z = np.zeros((8, 2), np.uint8)
         kvc.kvc_host_pask_control(z, z, np.zeros((8, 2, 2), np.float32), np.zeros(8, np.uint8),
                                   np.zeros((2, 3)), 0.5, tags)
+    with pytest.raises(_lib.KvcError):
+        kvc.kvc_host_pask_row_actions(np.zeros((1, 4, 2), np.uint8), 0, 8, 2)   # no layers
+    with pytest.raises(_lib.KvcError):
+        kvc.kvc_host_pask_row_actions(np.zeros((1, 4, 2), np.uint8), 4, 8, -1)  # negative window
 
 
 def test_commit_protection_matches_oracle_and_the_page_budget():

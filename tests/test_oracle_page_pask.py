@@ -386,3 +386,19 @@ def test_controller_matches_the_order_derived_by_search_over_all_step_orders():
         R_t = float(rng.uniform(-0.1, 1.1) * costs[:, 2].sum())
         a, _ = pask.control_token(a0, amin, prio, crit, R_t, costs)
         assert a == _brute_force_token(a0, amin, prio, crit, R_t, costs), (trial, a0, amin, prio, crit, R_t)
+
+
+def test_row_actions_broadcast_groups_and_keep_the_recent_window_high():
+    # 5 layers in 2 groups (layers 0-2 -> group 0, 3-4 -> group 1 by the
+    # ceil(c*L/n_groups) boundaries), 2 KV heads, 6 generated tokens, recent 2
+    from oracle.policy import layer_group
+    assert [layer_group(l, 5, 2) for l in range(5)] == [0, 0, 0, 1, 1]
+    acts = np.array([[[0, 1], [1, 2], [2, 0], [0, 0], [1, 1], [0, 2]]], np.uint8)
+    ra = pask.row_actions(acts, 5, 2, 2)
+    assert ra.shape == (1, 5, 2, 6)
+    np.testing.assert_array_equal(ra[0, 0, 0], [0, 1, 2, 0, 2, 2])
+    np.testing.assert_array_equal(ra[0, 4, 1], [1, 2, 0, 0, 2, 2])
+    assert (ra[0, :3] == ra[0, 0, 0]).all() and (ra[0, 3:] == ra[0, 4, 1]).all()
+    # recent 0 leaves the schedule as it is; a window longer than the stream makes all H
+    np.testing.assert_array_equal(pask.row_actions(acts, 5, 2, 0)[0, 3, 0], acts[0, :, 1])
+    assert (pask.row_actions(acts, 5, 2, 9) == pask.H_ACT).all()

@@ -69,8 +69,7 @@ def _check_row(w, inp, res, o_acts, r):
     Ko_b, Vo_b, po = tl.bits(res["Ko"][r]), tl.bits(res["Vo"][r]), res["pos"][r].cpu().numpy()
     tl.check_compaction(Ko_b[:nk], Vo_b[:nk], po[:nk], Kb, Vb, np.arange(Tp), g_kept, -1, w.rope_base)
     # generated tokens: the oracle's action for the row's layer group, recent ones bf16
-    a = o_acts[n, :, o_policy.layer_group(l, L, w.n_groups)].copy()
-    a[Tg - w.gen_recent:] = o_pask.H_ACT
+    a = o_pask.row_action(o_acts[n], l, L, w.gen_recent)
     H, Lw = np.flatnonzero(a == o_pask.H_ACT), np.flatnonzero(a == o_pask.L_ACT)
     assert res["n_h"][r] == nk + H.size and res["n_l"][r] == Lw.size
     Kgb, Vgb = tl.bits(inp.K_gen[n, l, h]), tl.bits(inp.V_gen[n, l, h])
@@ -132,9 +131,8 @@ def test_pask_full_size_sampled_rows(name):
     swaps = sum(_check_row(w, inp, res, o_acts, (n * L + l) * Hkv + h) for n, l, h in sample)
     assert swaps <= 4
     # every row: the bf16 pool holds the kept prompt plus the bf16-tier generated tokens
-    grp = np.array([o_policy.layer_group(l, L, w.n_groups) for l in range(L)])
-    a = o_acts[:, :, grp].transpose(0, 2, 1).copy()         # [N][L][n_gen]
-    a[..., w.n_gen - w.gen_recent:] = o_pask.H_ACT
+    a = np.stack([[o_pask.row_action(o_acts[n], l, L, w.gen_recent) for l in range(L)]
+                  for n in range(w.n_seq)])                   # [N][L][n_gen]
     n_H = np.repeat((a == o_pask.H_ACT).sum(-1)[:, :, None], Hkv, axis=2).reshape(-1)
     n_L = np.repeat((a == o_pask.L_ACT).sum(-1)[:, :, None], Hkv, axis=2).reshape(-1)
     np.testing.assert_array_equal(res["n_h"], w.budget + n_H)
