@@ -4,7 +4,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvc.so")
+# KVC_LIBRARY selects another build of the same library (the AddressSanitizer
+# build, libkvc_asan.so, for host-side checks); by default the in-tree libkvc.so.
+LIB_PATH = os.environ.get("KVC_LIBRARY") or os.path.join(_PKG, "libkvc.so")
 
 KVC_OK = 0
 KVC_WARN_FLOOR_EXCESS = 1

@@ -42,8 +42,14 @@ EXTRA_FLAGS = {
 }
 
 
-def _compile(src, obj, verbose):
-    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+# AddressSanitizer on the host code only (device code is never instrumented):
+# the argument checks, workspace sizing and host control routines run under it.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+ASAN_LIB_PATH = os.path.join(PKG, "libkvc_asan.so")
+
+
+def _compile(src, obj, verbose, extra=()):
+    cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,23 +58,42 @@ def _compile(src, obj, verbose):
     return obj
 
 
-def build(verbose=False, jobs=8):
-    """Compile every csrc/*.hip and link libkvc.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose=False, jobs=8, asan=False):
+    """Compile every csrc/*.hip and link libkvc.so; returns the library path.
+    asan=True builds libkvc_asan.so instead, the host code under AddressSanitizer
+    (load it with the sanitizer runtime preloaded; see asan_runtime())."""
+    bdir = BUILD_DIR + ("_asan" if asan else "")
+    out = ASAN_LIB_PATH if asan else LIB_PATH
+    extra = ASAN_FLAGS if asan else []
+    os.makedirs(bdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    objs = [os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
+    objs = [os.path.join(bdir, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        list(ex.map(lambda so: _compile(so[0], so[1], verbose, extra), zip(srcs, objs)))
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def asan_runtime():
+    """The AddressSanitizer runtime of hipcc's compiler, to preload into Python."""
+    res = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime of hipcc's compiler was not found")
+    return path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    if "--asan" in sys.argv:
+        print(build(verbose=True, asan=True))
+        print(asan_runtime())
+    else:
+        print(build(verbose=True))
