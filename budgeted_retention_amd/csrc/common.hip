@@ -46,7 +46,7 @@ int check_dims(const kvc_dims *d, const char *who) {
 
 // Defined in score.hip and select.hip.
 size_t score_workspace_bytes(const kvc_dims *d, int32_t W);
-size_t select_workspace_bytes(const kvc_dims *d);
+size_t select_workspace_bytes(const kvc_dims *d, int32_t B);
 
 }  // namespace kvc
 
@@ -67,7 +67,7 @@ extern "C" size_t kvc_workspace_bytes(int op, const kvc_dims *dims, int32_t W, i
         }
         return score_workspace_bytes(dims, W);
     case KVC_OP_SELECT:
-        return select_workspace_bytes(dims);
+        return select_workspace_bytes(dims, B);
     default:
         fail(KVC_ERR_ARG, "kvc_workspace_bytes: unknown op %d", op);
         return 0;

@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
                   const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int64_t T,
                   int L, int Hkv, int n_groups, int layer_base, int n_layers_model, int n_tags,
                   int tag_rows, int n_sink, int n_recent, int B, int32_t *__restrict__ kept, int kept_stride,
-                  int32_t *__restrict__ n_kept) {
+                  int32_t *__restrict__ n_kept, const uint32_t *__restrict__ only) {
     __shared__ float s_bonus[256];
     __shared__ uint8_t s_floor[256];
     __shared__ uint32_t hist[SEL_BINS];
@@ -150,6 +150,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
     __shared__ uint32_t s_pick[2];
 
     const int64_t r = blockIdx.x;
+    if (only && !only[r]) return;   // a row mask: only the flagged rows
     const RowIdx ri = split_row(r, L, Hkv);
     const int tid = threadIdx.x;
     const int grp = device_layer_group(layer_base + ri.l, n_layers_model, n_groups);
@@ -1011,6 +1012,497 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
     if (lane == 0) n_kept[r] = gt_run + (eq_run < need ? eq_run : need);
 }
 
+// ---------------------------------------------------------------- sampled threshold
+//
+// Rows of more than 8192 tokens, when the protected tokens (sinks and recent
+// window; no floor table) fit in the budget and B <= min(2048, T/5):
+//   cand_sample   one wave per row draws 8192 keys (2048 evenly spaced groups
+//                 of four tokens) and takes the r_s-th largest, r_s chosen so
+//                 that about 2.5 B of the row's keys should be at or above it:
+//                 that key is the row's threshold k_lo;
+//   cand_filter   segments of 16384 tokens, one 1024-thread workgroup each,
+//                 append every token whose key is at least k_lo, with its
+//                 key, in index order to the segment's own region of the
+//                 workspace, and count them;
+//   cand_resolve  one workgroup per row gathers the segments' candidates in
+//                 order (if there are at least B and at most CAND_CAP of them;
+//                 every kept token is then a candidate, since the row's top B
+//                 are all at or above its B-th key, which is at least k_lo),
+//                 finds the budget-th key among them and writes the kept
+//                 indices in order; otherwise it flags the row, and the exact
+//                 one-workgroup kernel then runs for the flagged rows only.
+// The decisions are those of the other kernels: same keys, ties to the lower
+// index.
+static constexpr int CS_SAMPLE_GROUPS = 2048;            // 8192 sampled keys per row
+static constexpr int CF_THREADS = 1024;
+static constexpr int CF_SEG = CF_THREADS * 4 * 4;        // 16384 tokens per filter workgroup
+static constexpr int CR_THREADS = 512;
+static constexpr int CAND_CAP = 8192;
+
+template <int WAVES>
+__device__ __forceinline__ uint32_t blk_excl_scan(uint32_t v, uint32_t &total, uint32_t *s_w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0u, tot = 0u;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        const uint32_t x = s_w[w];
+        before += w < wave ? x : 0u;
+        tot += x;
+    }
+    __syncthreads();
+    total = tot;
+    return before + incl - v;
+}
+
+struct CandArgs {
+    const float *scores;
+    const uint8_t *tags;
+    const float *bonus;
+    int64_t T, rows;
+    int L, Hkv, n_groups, layer_base, n_layers_model, n_tags, tag_rows, n_sink, n_recent, B, nseg;
+    uint32_t *k_lo;     // [rows]
+    uint32_t *flag;     // [rows] 1 = resolve by the exact kernel
+    uint32_t *cnt;      // [rows][nseg]
+    uint32_t *c_key;    // [rows][T]: segment s's candidates from s*CF_SEG
+    int32_t *c_idx;
+    int32_t *kept;
+    int kept_stride;
+    int32_t *n_kept;
+};
+
+// The row's bonus per tag (tags beyond the table read tag 0), into tab[256].
+__device__ __forceinline__ void cand_table(const CandArgs &a, int64_t r, float *tab, int tid, int nthreads) {
+    const RowIdx ri = split_row(r, a.L, a.Hkv);
+    const int grp = device_layer_group(a.layer_base + ri.l, a.n_layers_model, a.n_groups);
+    for (int t = tid; t < 256; t += nthreads) {
+        const int u = t < a.n_tags ? t : 0;
+        tab[t] = (a.bonus && u < a.n_tags) ? a.bonus[u * a.n_groups + grp] : 0.f;
+    }
+}
+
+__device__ __forceinline__ uint32_t cand_key_of(int64_t j, float x, float bt, int64_t lo, int64_t hi) {
+    return (j < lo || j >= hi) ? KEY_PROTECTED : order_key(x + bt);
+}
+
+// hist[digit] += 1 for every active lane; the lanes that share the first
+// active lane's digit add together (one atomic instead of a same-address
+// conflict), which is where skewed totals put most of them.
+__device__ __forceinline__ void hist_add_agg(uint32_t *hist, bool active, uint32_t digit) {
+    const uint64_t act = __ballot(active);
+    if (!act) return;
+    const int first = __ffsll((unsigned long long)act) - 1;
+    const uint32_t d0 = __builtin_amdgcn_readlane(digit, first);
+    const uint64_t same = __ballot(active && digit == d0);
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+    if (active && digit != d0) atomicAdd(&hist[digit], 1u);
+}
+
+// Block-level radix pick helpers of the sampled-threshold kernels (one shared
+// LDS histogram; thread t owns the bins t*PER .. t*PER + PER - 1 from the top).
+template <int THREADS>
+struct BlkRadix {
+    static constexpr int WAVES = THREADS / 64, PER = SEL_BINS / THREADS;
+    uint32_t *hist, *s_w, *s_pick;
+    __device__ void clear() {
+        for (int t = threadIdx.x; t < SEL_BINS; t += THREADS) hist[t] = 0u;
+        __syncthreads();
+    }
+    __device__ void pick(uint32_t kr, uint32_t &bin, uint32_t &rank) {
+        const int tid = threadIdx.x;
+        uint32_t c[PER], sum = 0u;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            c[i] = hist[SEL_BINS - 1 - tid * PER - i];
+            sum += c[i];
+        }
+        uint32_t tot;
+        const uint32_t ex = blk_excl_scan<WAVES>(sum, tot, s_w);
+        if (ex < kr && kr <= ex + sum) {
+            uint32_t acc = ex;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                if (acc < kr && kr <= acc + c[i]) {
+                    s_pick[0] = (uint32_t)(SEL_BINS - 1 - tid * PER - i);
+                    s_pick[1] = kr - acc;
+                }
+                acc += c[i];
+            }
+        }
+        __syncthreads();
+        bin = s_pick[0];
+        rank = s_pick[1];
+        __syncthreads();
+    }
+};
+
+static constexpr int CS_THREADS = 256;
+
+__global__ void __launch_bounds__(CS_THREADS) cand_sample(CandArgs a) {
+    constexpr int NG = CS_SAMPLE_GROUPS / CS_THREADS;   // 8 groups of four per thread
+    constexpr int WAVES = CS_THREADS / 64;
+    __shared__ __align__(16) uint32_t hist[SEL_BINS];
+    __shared__ float s_tab[256];
+    __shared__ uint32_t s_w[WAVES];
+    __shared__ uint32_t s_r[3][WAVES];
+    __shared__ uint32_t s_pick[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = blockIdx.x;
+    cand_table(a, r, s_tab, tid, CS_THREADS);
+    const RowIdx ri = split_row(r, a.L, a.Hkv);
+    const float *sr = a.scores + (size_t)r * a.T;
+    const uint8_t *tr = a.tags ? a.tags + (size_t)(a.tag_rows ? r : ri.n) * a.T : nullptr;
+    const int64_t groups = a.T / 4, lo = a.n_sink, hi = a.T - a.n_recent;
+    uint32_t key[NG][4], tg[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        const int64_t j0 = 4 * ((int64_t)(k * CS_THREADS + tid) * groups / CS_SAMPLE_GROUPS);
+        const uint4 v = *reinterpret_cast<const uint4 *>(sr + j0);
+        tg[k] = tr ? *reinterpret_cast<const uint32_t *>(tr + j0) : 0u;
+        key[k][0] = v.x;
+        key[k][1] = v.y;
+        key[k][2] = v.z;
+        key[k][3] = v.w;
+    }
+    __syncthreads();   // s_tab
+    uint32_t nprot = 0u, kmin = 0xFFFFFFFFu, kmax1 = 0u;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        const int64_t j0 = 4 * ((int64_t)(k * CS_THREADS + tid) * groups / CS_SAMPLE_GROUPS);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t kk =
+                cand_key_of(j0 + e, __uint_as_float(key[k][e]), s_tab[(tg[k] >> (8 * e)) & 0xFF], lo, hi);
+            key[k][e] = kk;
+            nprot += kk == KEY_PROTECTED ? 1u : 0u;
+            kmin = min(kmin, kk);             // a protected key never lowers kmin
+            kmax1 = max(kmax1, kk + 1u);      // and wraps to 0 here
+        }
+    }
+    nprot = __builtin_amdgcn_readlane(wave_incl_scan(nprot), 63);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax1 = max(kmax1, (uint32_t)__shfl_xor((int)kmax1, o));
+    }
+    if (lane == 0) {
+        s_r[0][wave] = nprot;
+        s_r[1][wave] = kmin;
+        s_r[2][wave] = kmax1;
+    }
+    __syncthreads();
+    nprot = 0u;
+    kmin = 0xFFFFFFFFu;
+    kmax1 = 0u;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        nprot += s_r[0][w];
+        kmin = min(kmin, s_r[1][w]);
+        kmax1 = max(kmax1, s_r[2][w]);
+    }
+    const int ns = CS_SAMPLE_GROUPS * 4;
+    int64_t rs = (int64_t)(((double)a.B * 2.5 * ns + (double)a.T - 1) / (double)a.T) + 4;
+    rs = rs > ns ? ns : rs;
+    uint32_t k_lo;
+    if (nprot >= (uint32_t)rs) {
+        k_lo = KEY_PROTECTED;
+    } else {
+        BlkRadix<CS_THREADS> rx{hist, s_w, s_pick};
+        auto count = [&](auto match, auto digit) {
+            rx.clear();
+#pragma unroll
+            for (int k = 0; k < NG; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t kk = key[k][e], d = kk - kmin;
+                    hist_add_agg(hist, kk != KEY_PROTECTED && match(d), digit(d));
+                }
+            __syncthreads();
+        };
+        const uint32_t range = kmax1 - 1u - kmin;
+        const int bl = range ? 32 - __clz(range) : 0;
+        const int s0 = bl > 11 ? bl - 11 : 0;
+        const int w1 = s0 < 11 ? s0 : 11, s1 = s0 - w1;
+        uint32_t kr = (uint32_t)rs - nprot, dt;
+        count([](uint32_t) { return true; }, [&](uint32_t d) { return d >> s0; });
+        rx.pick(kr, dt, kr);
+        if (w1) {
+            count([&](uint32_t d) { return (d >> s0) == dt; }, [&](uint32_t d) { return (d >> s1) & ((1u << w1) - 1u); });
+            uint32_t b1;
+            rx.pick(kr, b1, kr);
+            dt = (dt << w1) | b1;
+        }
+        if (s1) {
+            count([&](uint32_t d) { return (d >> s1) == dt; }, [&](uint32_t d) { return d & ((1u << s1) - 1u); });
+            uint32_t b2;
+            rx.pick(kr, b2, kr);
+            dt = (dt << s1) | b2;
+        }
+        k_lo = kmin + dt;
+    }
+    if (tid == 0) a.k_lo[r] = k_lo;
+}
+
+__global__ void __launch_bounds__(CF_THREADS) cand_filter(CandArgs a) {
+    constexpr int WAVES = CF_THREADS / 64;
+    __shared__ float s_tab[256];
+    __shared__ uint32_t s_w[WAVES];
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x / a.nseg;
+    const int sg = (int)(blockIdx.x % a.nseg);
+    const int64_t p0 = (int64_t)sg * CF_SEG;
+    const int nv = (int)(a.T - p0 < CF_SEG ? a.T - p0 : CF_SEG);
+    cand_table(a, r, s_tab, tid, CF_THREADS);
+    const RowIdx ri = split_row(r, a.L, a.Hkv);
+    const float *sr = a.scores + (size_t)r * a.T + p0;
+    const uint8_t *tr = a.tags ? a.tags + (size_t)(a.tag_rows ? r : ri.n) * a.T + p0 : nullptr;
+    uint4 v[4];
+    uint32_t t4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int base = k * CF_THREADS * 4 + 4 * tid;
+        v[k] = make_uint4(0u, 0u, 0u, 0u);
+        t4[k] = 0u;
+        if (base < nv) {   // T % 4 == 0: a group is wholly inside or outside
+            v[k] = *reinterpret_cast<const uint4 *>(sr + base);
+            if (tr) t4[k] = *reinterpret_cast<const uint32_t *>(tr + base);
+        }
+    }
+    const uint32_t k_lo = a.k_lo[r];
+    const int64_t lo = a.n_sink, hi = a.T - a.n_recent;
+    __syncthreads();   // s_tab
+    uint32_t *ck = a.c_key + (size_t)r * a.T + p0;
+    int32_t *ci = a.c_idx + (size_t)r * a.T + p0;
+    uint32_t run = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int base = k * CF_THREADS * 4 + 4 * tid;
+        const uint32_t x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        uint32_t kk[4], n = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kk[e] = cand_key_of(p0 + base + e, __uint_as_float(x[e]), s_tab[(t4[k] >> (8 * e)) & 0xFF], lo, hi);
+            n += (base < nv && kk[e] >= k_lo) ? 1u : 0u;
+        }
+        uint32_t tot;
+        uint32_t pos = run + blk_excl_scan<WAVES>(n, tot, s_w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (base < nv && kk[e] >= k_lo) {
+                ck[pos] = kk[e];
+                ci[pos] = (int32_t)(p0 + base + e);
+                ++pos;
+            }
+        run += tot;
+    }
+    if (tid == 0) a.cnt[(size_t)r * a.nseg + sg] = run;
+}
+
+__global__ void __launch_bounds__(CR_THREADS) cand_resolve(CandArgs a) {
+    constexpr int WAVES = CR_THREADS / 64, PER = SEL_BINS / CR_THREADS;
+    __shared__ uint32_t c_key[CAND_CAP];
+    __shared__ int32_t c_idx[CAND_CAP];
+    __shared__ __align__(16) uint32_t hist[SEL_BINS];
+    __shared__ uint32_t s_w[WAVES];
+    __shared__ uint32_t s_r[3][WAVES];
+    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_pre[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = blockIdx.x;
+    const uint32_t *cnt = a.cnt + (size_t)r * a.nseg;
+    uint32_t total = 0u;
+    for (int s0 = 0; s0 < a.nseg; s0 += CR_THREADS) {
+        uint32_t t;
+        blk_excl_scan<WAVES>(s0 + tid < a.nseg ? cnt[s0 + tid] : 0u, t, s_w);
+        total += t;
+    }
+    const int B = a.B;
+    if (total < (uint32_t)B || total > (uint32_t)CAND_CAP) {   // the sample misled: exact kernel
+        if (tid == 0) a.flag[r] = 1u;
+        return;
+    }
+    if (tid == 0) a.flag[r] = 0u;
+    // gather the segments' candidates in order
+    uint32_t base = 0u;
+    for (int sg = 0; sg < a.nseg; ++sg) {
+        const uint32_t c = cnt[sg];
+        const uint32_t *ck = a.c_key + (size_t)r * a.T + (size_t)sg * CF_SEG;
+        const int32_t *ci = a.c_idx + (size_t)r * a.T + (size_t)sg * CF_SEG;
+        for (uint32_t i = tid; i < c; i += CR_THREADS) {
+            c_key[base + i] = ck[i];
+            c_idx[base + i] = ci[i];
+        }
+        base += c;
+    }
+    __syncthreads();
+    const int n = (int)total;
+    // protected count and the range of the other keys
+    uint32_t nprot = 0u, kmin = 0xFFFFFFFFu, kmax1 = 0u;
+    for (int p = tid; p < n; p += CR_THREADS) {
+        const uint32_t kk = c_key[p];
+        nprot += kk == KEY_PROTECTED ? 1u : 0u;
+        kmin = min(kmin, kk);
+        kmax1 = max(kmax1, kk + 1u);
+    }
+    nprot = __builtin_amdgcn_readlane(wave_incl_scan(nprot), 63);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax1 = max(kmax1, (uint32_t)__shfl_xor((int)kmax1, o));
+    }
+    if (lane == 0) {
+        s_r[0][wave] = nprot;
+        s_r[1][wave] = kmin;
+        s_r[2][wave] = kmax1;
+    }
+    __syncthreads();
+    nprot = 0u;
+    kmin = 0xFFFFFFFFu;
+    kmax1 = 0u;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        nprot += s_r[0][w];
+        kmin = min(kmin, s_r[1][w]);
+        kmax1 = max(kmax1, s_r[2][w]);
+    }
+    uint32_t tau;
+    int need;
+    if (nprot >= (uint32_t)B) {   // only when exactly B: every protected token
+        tau = KEY_PROTECTED;
+        need = B;
+    } else {
+        BlkRadix<CR_THREADS> rx{hist, s_w, s_pick};
+        auto count = [&](auto match, auto digit) {
+            rx.clear();
+            for (int p0 = 0; p0 < n; p0 += CR_THREADS) {   // every lane of a wave takes the same trips
+                const int p = p0 + tid;
+                const uint32_t kk = p < n ? c_key[p] : KEY_PROTECTED, d = kk - kmin;
+                hist_add_agg(hist, kk != KEY_PROTECTED && match(d), digit(d));
+            }
+            __syncthreads();
+        };
+        auto pick = [&](uint32_t kr, uint32_t &bin, uint32_t &rank) { rx.pick(kr, bin, rank); };
+        const uint32_t range = kmax1 - 1u - kmin;
+        const int bl = range ? 32 - __clz(range) : 0;
+        const int s0 = bl > 11 ? bl - 11 : 0;
+        const int w1 = s0 < 11 ? s0 : 11, s1 = s0 - w1;
+        uint32_t kr = (uint32_t)B - nprot, dt;
+        count([](uint32_t) { return true; }, [&](uint32_t d) { return d >> s0; });
+        pick(kr, dt, kr);
+        if (w1) {
+            count([&](uint32_t d) { return (d >> s0) == dt; }, [&](uint32_t d) { return (d >> s1) & ((1u << w1) - 1u); });
+            uint32_t b1;
+            pick(kr, b1, kr);
+            dt = (dt << w1) | b1;
+        }
+        if (s1) {
+            count([&](uint32_t d) { return (d >> s1) == dt; }, [&](uint32_t d) { return d & ((1u << s1) - 1u); });
+            uint32_t b2;
+            pick(kr, b2, kr);
+            dt = (dt << s1) | b2;
+        }
+        tau = kmin + dt;
+        need = (int)kr;
+    }
+    // ordered write: key > tau, and the first `need` keys == tau in list (= index) order
+    int32_t *out = a.kept + (size_t)r * a.kept_stride;
+    uint32_t gt_run = 0u, eq_run = 0u;
+    for (int c0 = 0; c0 < n; c0 += CR_THREADS * 4) {
+        const int pb = c0 + 4 * tid;
+        uint32_t ngt = 0u, neq = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool v = pb + e < n;
+            const uint32_t kk = v ? c_key[pb + e] : 0u;
+            ngt += (v && kk > tau) ? 1u : 0u;
+            neq += (v && kk == tau) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t ex = blk_excl_scan<WAVES>(ngt | (neq << 16), tot, s_w);
+        int gt_before = (int)(gt_run + (ex & 0xFFFFu)), eq_before = (int)(eq_run + (ex >> 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool v = pb + e < n;
+            const uint32_t kk = v ? c_key[pb + e] : 0u;
+            const bool gt = v && kk > tau, eq = v && kk == tau;
+            if (gt || (eq && eq_before < need)) {
+                const int pos = gt_before + (eq_before < need ? eq_before : need);
+                if (pos < a.kept_stride) out[pos] = c_idx[pb + e];
+            }
+            gt_before += gt ? 1 : 0;
+            eq_before += eq ? 1 : 0;
+        }
+        gt_run += tot & 0xFFFFu;
+        eq_run += tot >> 16;
+    }
+    if (tid == 0) a.n_kept[r] = (int32_t)(gt_run + (eq_run < (uint32_t)need ? eq_run : (uint32_t)need));
+}
+
+static bool select_use_split(const kvc_dims *d) {
+    const int64_t T = d->n_tokens, rows = n_rows(d);
+    return T >= 262144 || (rows < 128 && T >= 32768);
+}
+
+// The sampled path serves the rows that would otherwise be split over
+// several workgroups (long rows, or few rows of at least 32,768 tokens); with
+// many rows of moderate length one workgroup per row streams as fast.
+static bool cand_eligible(const kvc_dims *d, const kvc_policy *p, bool vec) {
+    const int64_t T = d->n_tokens;
+    return vec && select_use_split(d) && !p->tag_floor && p->budget <= 2048 && 5 * (int64_t)p->budget <= T &&
+           (int64_t)p->n_sink + p->n_recent <= p->budget;
+}
+
+static size_t cand_workspace_bytes(int64_t rows, int64_t T) {
+    const int64_t nseg = (T + CF_SEG - 1) / CF_SEG;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return al(rows * 4) * 2 + al(rows * nseg * 4) + al((size_t)rows * T * 4) * 2;
+}
+
+static int launch_select_cand(const kvc_dims *dims, const kvc_policy *p, const float *scores, int32_t *kept,
+                              int kept_stride, int32_t *n_kept, void *ws, hipStream_t s) {
+    const int64_t rows = n_rows(dims), T = dims->n_tokens;
+    const int nseg = (int)((T + CF_SEG - 1) / CF_SEG);
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    char *w = reinterpret_cast<char *>(ws);
+    CandArgs a;
+    a.scores = scores;
+    a.tags = p->tags;
+    a.bonus = p->tag_bonus;
+    a.T = T;
+    a.rows = rows;
+    a.L = dims->n_layers;
+    a.Hkv = dims->n_kv_heads;
+    a.n_groups = p->n_groups;
+    a.layer_base = p->layer_base;
+    a.n_layers_model = p->n_layers_model;
+    a.n_tags = p->n_tags;
+    a.tag_rows = p->tag_rows;
+    a.n_sink = p->n_sink;
+    a.n_recent = p->n_recent;
+    a.B = p->budget;
+    a.nseg = nseg;
+    a.k_lo = reinterpret_cast<uint32_t *>(w);
+    a.flag = reinterpret_cast<uint32_t *>(w + al(rows * 4));
+    a.cnt = reinterpret_cast<uint32_t *>(w + 2 * al(rows * 4));
+    a.c_key = reinterpret_cast<uint32_t *>(w + 2 * al(rows * 4) + al(rows * nseg * 4));
+    a.c_idx = reinterpret_cast<int32_t *>(w + 2 * al(rows * 4) + al(rows * nseg * 4) + al((size_t)rows * T * 4));
+    a.kept = kept;
+    a.kept_stride = kept_stride;
+    a.n_kept = n_kept;
+    if (rows * nseg > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_select: grid too large");
+    cand_sample<<<dim3((unsigned)rows), dim3(CS_THREADS), 0, s>>>(a);
+    cand_filter<<<dim3((unsigned)(rows * nseg)), dim3(CF_THREADS), 0, s>>>(a);
+    cand_resolve<<<dim3((unsigned)rows), dim3(CR_THREADS), 0, s>>>(a);
+    // rows whose sample misled: the exact one-workgroup kernel, only for them
+    select_kernel<true><<<dim3((unsigned)rows), dim3(SEL_THREADS), 0, s>>>(
+        scores, p->tags, p->tag_bonus, nullptr, T, dims->n_layers, dims->n_kv_heads, p->n_groups, p->layer_base,
+        p->n_layers_model, p->n_tags, p->tag_rows, p->n_sink, p->n_recent, p->budget, kept, kept_stride, n_kept,
+        a.flag);
+    return check_launch("kvc_select (sampled threshold)");
+}
+
 template <int NPL4>
 static void launch_select_wave(bool vec, int64_t rows, hipStream_t s, const float *scores, const kvc_policy *p,
                                const kvc_dims *dims, int32_t *kept, int kept_stride, int32_t *n_kept) {
@@ -1027,10 +1519,6 @@ static void launch_select_wave(bool vec, int64_t rows, hipStream_t s, const floa
                                                         p->n_sink, p->n_recent, p->budget, kept, kept_stride, n_kept);
 }
 
-static bool select_use_split(const kvc_dims *d) {
-    const int64_t T = d->n_tokens, rows = n_rows(d);
-    return T >= 262144 || (rows < 128 && T >= 32768);
-}
 
 static size_t split_bytes(int64_t rows, int64_t chunks) {
     return align256s((size_t)rows * 3 * SEL_BINS * sizeof(uint32_t)) + align256s((size_t)rows * sizeof(SplitState)) +
@@ -1304,10 +1792,17 @@ static int launch_select_split(const SplitArgs &a, int64_t rows, void *ws, bool 
 
 // Workspace of kvc_select: the long-row path's histograms, per-row state and
 // per-chunk counts; 0 when the rows take the one-workgroup kernels.
-size_t select_workspace_bytes(const kvc_dims *d) {
-    if (!select_use_split(d)) return 0;
-    const int64_t chunks = (d->n_tokens + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
-    return split_bytes(n_rows(d), chunks);
+size_t select_workspace_bytes(const kvc_dims *d, int32_t B) {
+    size_t n = 0;
+    if (select_use_split(d)) {
+        const int64_t chunks = (d->n_tokens + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
+        n = split_bytes(n_rows(d), chunks);
+    }
+    if (select_use_split(d) && B > 0 && B <= 2048 && 5 * (int64_t)B <= d->n_tokens) {
+        const size_t m = cand_workspace_bytes(n_rows(d), d->n_tokens);
+        n = m > n ? m : n;
+    }
+    return n;
 }
 
 }  // namespace kvc
@@ -1358,8 +1853,10 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
             launch_select_wave<16>(vec, rows, s, scores, p, dims, kept_idx, kept_stride, n_kept);
         else
             launch_select_wave<32>(vec, rows, s, scores, p, dims, kept_idx, kept_stride, n_kept);
+    } else if (cand_eligible(dims, p, vec) && ws && ws_bytes >= cand_workspace_bytes(n_rows(dims), T)) {
+        if ((st = launch_select_cand(dims, p, scores, kept_idx, kept_stride, n_kept, ws, s)) != KVC_OK) return st;
     } else if (select_use_split(dims)) {
-        const size_t need = select_workspace_bytes(dims);
+        const size_t need = select_workspace_bytes(dims, 0);
         if (!ws || ws_bytes < need)
             return fail(KVC_ERR_WORKSPACE, "kvc_select: workspace %zu < %zu bytes (long rows)", ws_bytes, need);
         SplitArgs a{scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers, dims->n_kv_heads, p->n_groups,
@@ -1382,12 +1879,12 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
         select_kernel<true><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                     dims->n_kv_heads, p->n_groups, p->layer_base,
                                                     p->n_layers_model, p->n_tags, p->tag_rows, p->n_sink,
-                                                    p->n_recent, p->budget, kept_idx, kept_stride, n_kept);
+                                                    p->n_recent, p->budget, kept_idx, kept_stride, n_kept, nullptr);
     } else {
         select_kernel<false><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                      dims->n_kv_heads, p->n_groups, p->layer_base,
                                                      p->n_layers_model, p->n_tags, p->tag_rows, p->n_sink,
-                                                     p->n_recent, p->budget, kept_idx, kept_stride, n_kept);
+                                                     p->n_recent, p->budget, kept_idx, kept_stride, n_kept, nullptr);
     }
     if ((st = check_launch("kvc_select")) != KVC_OK) return st;
     const int64_t sink_recent = (int64_t)p->n_sink + p->n_recent;

@@ -22,7 +22,7 @@ from oracle import select as o_select
 pytestmark = pytest.mark.gpu
 
 
-def _run_select(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=None):
+def _run_select(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=None, ws=None):
     from budgeted_retention_amd import kvc
     rows, T = scores.shape
     dims = kvc.make_dims(1, 1, rows, rows, 64, T)
@@ -34,7 +34,7 @@ def _run_select(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=Non
                      None if floor is None else torch.from_numpy(floor.astype(np.uint8)).to(dev))
     kept = torch.full((rows, ks), -1, dtype=torch.int32, device=dev)
     n_kept = torch.zeros(rows, dtype=torch.int32, device=dev)
-    st = kvc.kvc_select(dims, torch.from_numpy(scores).to(dev), pol, kept, ks, n_kept)
+    st = kvc.kvc_select(dims, torch.from_numpy(scores).to(dev), pol, kept, ks, n_kept, ws)
     torch.cuda.synchronize()
     return st, kept.cpu().numpy(), n_kept.cpu().numpy()
 
@@ -52,8 +52,8 @@ def _oracle(score_row, tags, bonus, floor, n_sink, n_recent, B):
     return kept
 
 
-def _check(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=None, check_rows=None):
-    st, kept, n_kept = _run_select(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride)
+def _check(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride=None, check_rows=None, ws=None):
+    st, kept, n_kept = _run_select(scores, tags, bonus, floor, n_sink, n_recent, B, kept_stride, ws)
     for r in (range(scores.shape[0]) if check_rows is None else check_rows):
         ref = _oracle(scores[r], tags, bonus, floor, n_sink, n_recent, B)
         assert n_kept[r] == ref.size, (r, n_kept[r], ref.size)
@@ -275,3 +275,40 @@ def test_short_rows_protection_at_and_beyond_the_budget(T, B, n_sink, n_recent, 
     bonus = np.zeros((2, 1))
     floor = np.array([[0], [1]], np.uint8)
     _check(scores, tags, bonus, floor if floored else None, n_sink, n_recent, B, kept_stride=T)
+
+
+@pytest.mark.parametrize("T,B", [(10_004, 2048), (32_768, 8192), (32_772, 2048), (100_000, 2048),
+                                 (300_000, 2048), (1_048_576, 2048), (65_536, 1)])
+@pytest.mark.parametrize("dist", ["gamma_spans", "ties", "signs_nans"])
+def test_long_rows_sampled_threshold(T, B, dist):
+    """Rows of more than 8192 tokens without floors (B <= min(2048, T/5)):
+    a threshold from an 8192-key sample, candidates at or above it appended
+    per 16,384-token segment, the exact budget-th key among them; quantised
+    scores put so many tokens on the threshold key that the candidates
+    overflow and the exact kernel takes those rows; larger budgets take the
+    other kernels."""
+    rng = np.random.default_rng(T + B + len(dist))
+    rows = 3
+    if dist == "gamma_spans":
+        scores = rng.gamma(0.5, 1.0 / T, (rows, T)).astype(np.float32)
+    elif dist == "ties":
+        scores = (rng.integers(0, 7, (rows, T)) / 8.0).astype(np.float32)
+    else:
+        scores = (np.sign(rng.random((rows, T)) - 0.4) * 10.0 ** rng.uniform(-20, 20, (rows, T))).astype(np.float32)
+        scores[:, ::101] = np.nan
+    tags = np.zeros(T, np.uint8)
+    for k, start in enumerate(rng.choice(np.arange(200, T - 1000, 600), 8, replace=False)):
+        tags[start:start + int(rng.integers(16, 513))] = k + 1
+    bonus = np.array([[0.0]] + [[1000.0 - 50.0 * k] for k in range(8)])
+    _check(scores, tags, bonus, None, 4 if B >= 4 else 0, 128 if B >= 132 else 0, B)
+
+
+def test_candidate_kernel_without_the_level_workspace():
+    """With too small a workspace the same rows take the one-workgroup
+    candidate kernel, with the same result."""
+    rng = np.random.default_rng(21)
+    T, B = 100_000, 2048
+    scores = rng.gamma(0.5, 1.0 / T, (130, T)).astype(np.float32)   # 128 rows and more: no split path
+    scores[:, ::9] = scores[:, 4:5]
+    _check(scores, None, np.zeros((1, 1)), None, 4, 128, B, check_rows=[0, 64, 129],
+           ws=torch.empty(1, dtype=torch.uint8, device="cuda"))
