@@ -12,7 +12,7 @@ Decode attention over the compacted cache is timed beside the step (not in
 
 Other workloads (parity cases, measured the same way call by call):
   tiny            1 layer, T=4096, B=512, renumbered
-  qwen3_8b_1m     T=1,048,576, one layer per call (154.6 GB of K+V resident)
+  qwen3_8b_1m     T=1,048,576, all 36 layers per call (154.6 GB of K+V resident)
   pask_llama3_8b  64 x 32 layers: prompt compaction, int8/bf16/release tiers, decode
   pask_llama3_8b_int4  the same with the pages' INT4 low tier (two nibbles per byte)
   commitkv_28l    16 x 28 layers: page effects, retirement, checkpoint, paged decode
@@ -52,10 +52,10 @@ def parse():
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="scratch written before every timed step so no step starts from cached data "
                          "(the 256 MB memory-side cache); 0 disables it")
-    ap.add_argument("--layers-per-call", type=int, default=36,
-                    help="layers per kvc_score / kvc_select / kvc_compact_rerotate call of the 100K "
-                         "session (a divisor of 36); one group is selected and compacted on a second "
-                         "stream while the next is scored")
+    ap.add_argument("--layers-per-call", type=int, default=0,
+                    help="layers per kvc_score / kvc_select / kvc_compact_rerotate call (a divisor of 36; "
+                         "default all of them); with several groups one is selected and compacted on a "
+                         "second stream while the next is scored")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (three times), so that HBM "
                          "counters can be scaled against a transfer of known size")
@@ -278,8 +278,7 @@ def oracle_bonus(steps_ahead):
 def bench_compaction(args, w, dev):
     """score -> select -> compact over every row, then decode over the
     compacted cache. The layers go in groups of --layers-per-call (all 36 in
-    one call by default for the 100K session, one layer per call for the
-    1M-token session). With several groups the scores of group g+1 are
+    one call by default). With several groups the scores of group g+1 are
     computed on one stream while group g is selected and compacted on a
     second stream (both at the default priority). The step is timed from the
     first launch to the last compaction's end event."""
@@ -289,7 +288,7 @@ def bench_compaction(args, w, dev):
     N, L, Hkv, Hq, d, T, W, B = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
                                  w.n_tokens, w.window, w.budget)
     per_layer = w.n_tokens > (1 << 20) - 1
-    Lc = 1 if per_layer else (args.layers_per_call or L)
+    Lc = args.layers_per_call or L
     if L % Lc:
         raise SystemExit(f"--layers-per-call {Lc} must divide {L} layers")
     chunks = [(l, l + Lc) for l in range(0, L, Lc)]
