@@ -774,7 +774,8 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
                 int32_t *__restrict__ n_kept) {
     __shared__ __align__(16) uint32_t s_hist[SW_WAVES][SEL_BINS];
     __shared__ float s_tab[SW_WAVES][256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: row pointers stay scalar
     const int64_t r = (int64_t)blockIdx.x * SW_WAVES + wave;
     if (r >= rows) return;
     const RowIdx ri = split_row(r, L, Hkv);
@@ -963,6 +964,10 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
     }
     // ordered write: key > tau, and the first `need` keys == tau by index
     int32_t *out = kept + (size_t)r * kept_stride;
+    // stores through a buffer resource: the row base stays scalar, a store
+    // takes a 32-bit byte offset (no 64-bit address arithmetic per token)
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        out, (short)0, (kept_stride < (1 << 20) ? kept_stride : (1 << 20)) * 4, 0x00020000);
     int gt_run = 0, eq_run = 0;
     int lane4 = 4 * lane;
     asm volatile("" : "+v"(lane4));   // token indices are recomputed here, not kept live from the loads
@@ -983,7 +988,7 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
             for (int e = 0; e < SEL_VEC; ++e)
                 if (key[k][e] > tau) {
-                    if (pos < kept_stride) out[pos] = base + e;
+                    if (pos < kept_stride) __builtin_amdgcn_raw_buffer_store_b32(base + e, orsrc, pos * 4, 0, 0);
                     ++pos;
                 }
             gt_run += tot;
@@ -999,7 +1004,7 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
                 const bool eq = key[k][e] == tau;
                 if (gt || (eq && eq_before < need)) {
                     const int pos = gt_before + (eq_before < need ? eq_before : need);
-                    if (pos < kept_stride) out[pos] = base + e;
+                    if (pos < kept_stride) __builtin_amdgcn_raw_buffer_store_b32(base + e, orsrc, pos * 4, 0, 0);
                 }
                 gt_before += gt;
                 eq_before += eq;
