@@ -140,6 +140,13 @@ def run_metadata(dev):
                                      text=True, timeout=10).stdout.strip() or None
     except Exception:
         meta["git"] = None
+    if meta["git"] is None:   # a tree without its history: the commit the library was built from
+        try:
+            info = json.load(open(os.path.join(ROOT, "budgeted_retention_amd", "build_info.json")))
+            meta["git"] = info.get("git")
+            meta["git_dirty_at_build"] = info.get("dirty")
+        except (OSError, ValueError):
+            pass
     try:
         meta["rocm"] = open("/opt/rocm/.info/version").read().strip()
     except OSError:

@@ -78,7 +78,28 @@ def build(verbose=False, jobs=8, asan=False):
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, out)
+    _write_build_info()
     return out
+
+
+BUILD_INFO = os.path.join(PKG, "build_info.json")
+
+
+def _write_build_info():
+    """The commit the library was built from (for run records on machines
+    that get the tree without its history)."""
+    import json
+    info = {"git": None, "dirty": None}
+    try:
+        info["git"] = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True,
+                                     text=True, timeout=10).stdout.strip() or None
+        st = subprocess.run(["git", "status", "--porcelain", "--untracked-files=no"], cwd=ROOT,
+                            capture_output=True, text=True, timeout=10).stdout
+        info["dirty"] = bool(st.strip()) if info["git"] else None
+    except Exception:
+        pass
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
 
 
 def asan_runtime():
