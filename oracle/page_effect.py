@@ -28,6 +28,8 @@ Readings where the page is silent:
 Checkpoint retention (§3.3, Eq. 13, with Eq. 4's single index set): a page's
 score pools the window score of its tokens over every layer and KV head of
 the sequence; retired pages are excluded; the best n_keep pages are kept.
+With event pages of unequal length the budget counts tokens instead
+(retained_pages_budget).
 
 Parity status: the effect itself is pinned (Eq. 6 identity, brute force,
 closed forms); the page score and the retained set by hand-built cases and
@@ -192,6 +194,30 @@ def retained_pages(score, retired, n_keep, protected=()):
     rest = np.setdiff1d(np.arange(score.size), prot)
     order = rest[np.lexsort((rest, -score[rest]))]
     return np.sort(np.concatenate([prot, order[: n_keep - prot.size]])).astype(np.int64)
+
+
+def retained_pages_budget(score, length, retired, budget):
+    """Pages kept at the checkpoint when pages differ in length (event pages,
+    CommitKV §3.1) and the budget counts tokens (§3.3, Eq. 13: |I| <= B).
+
+    Reading: retired pages are scored -inf, as in retained_pages; pages are
+    ranked by (score descending, page index ascending), a NaN score below
+    every other; the kept pages are the longest prefix of that ranking whose
+    lengths sum to at most the budget, so the first page that does not fit
+    ends the prefix. Returns (kept pages ascending, kept token count).
+    """
+    s = np.asarray(score, np.float64).copy()
+    ln = np.asarray(length, np.int64)
+    ret = np.asarray(sorted(set(int(e) for e in retired)), dtype=np.int64)
+    s[ret] = -np.inf
+    ranked = sorted(range(s.size), key=lambda e: (1, 0.0, e) if np.isnan(s[e]) else (0, -s[e], e))
+    kept, used = [], 0
+    for e in ranked:
+        if used + ln[e] > budget:
+            break
+        used += int(ln[e])
+        kept.append(e)
+    return np.sort(np.asarray(kept, np.int64)), used
 
 
 def protect_pending(R_minus, page_tokens, budget, eta, max_pages=16):

@@ -173,6 +173,78 @@ def test_retained_pages_hand_built_and_brute_force():
                 assert (eff[a], -a) > (eff[b], -b)
 
 
+
+def test_retained_pages_budget_hand_built():
+    """Event pages under a token budget (CommitKV §3.3 Eq. 13, |I| <= B): the
+    longest prefix of the (score desc, index asc) ranking that fits."""
+    sc, ln = [5, 9, 9, 1, 7], [3, 4, 2, 5, 6]       # ranking: 1, 2, 4, 0, 3
+    k, used = pe.retained_pages_budget(sc, ln, (), 12)
+    assert list(k) == [1, 2, 4] and used == 12
+    # page 4 does not fit after 1 and 2: the prefix ends there even though page 0 would fit
+    k, used = pe.retained_pages_budget(sc, ln, (), 9)
+    assert list(k) == [1, 2] and used == 6
+    # equal scores go to the lower index first: page 1 (4 tokens) fits, page 2 then does not
+    k, used = pe.retained_pages_budget(sc, ln, (), 5)
+    assert list(k) == [1] and used == 4
+    assert list(pe.retained_pages_budget(sc, ln, (), 100)[0]) == [0, 1, 2, 3, 4]
+    assert pe.retained_pages_budget(sc, ln, (), 0)[0].size == 0
+    # a retired page ranks last
+    k, used = pe.retained_pages_budget(sc, ln, {1}, 9)
+    assert list(k) == [2, 4] and used == 8
+    k, used = pe.retained_pages_budget(sc, ln, {1}, 20)
+    assert list(k) == [0, 1, 2, 3, 4] and used == 20
+    # NaN below -inf; a zero-length page after the first misfit stays out
+    assert list(pe.retained_pages_budget([np.nan, 1.0, -np.inf], [1, 1, 1], (), 2)[0]) == [1, 2]
+    assert list(pe.retained_pages_budget([3.0, 2.0, 1.0], [2, 5, 0], (), 4)[0]) == [0]
+    assert list(pe.retained_pages_budget([3.0, 2.0, 1.0], [2, 0, 5], (), 4)[0]) == [0, 1]
+
+
+def test_retained_pages_budget_reduces_to_page_count_and_matches_subset_search():
+    """Equal lengths G and a budget of k*G keep retained_pages' k pages; on
+    tiny cases the kept set is the only subset that fits, contains every page
+    ranked above any of its members, and cannot take the best page left."""
+    rng = np.random.default_rng(31)
+    for _ in range(100):
+        n = int(rng.integers(2, 14))
+        sc = rng.integers(0, 5, n).astype(float)
+        ret = set(rng.choice(n, int(rng.integers(0, n)), replace=False).tolist())
+        k, G = int(rng.integers(1, n)), int(rng.integers(1, 17))
+        got, used = pe.retained_pages_budget(sc, np.full(n, G), ret, k * G + int(rng.integers(0, G)))
+        assert list(got) == list(pe.retained_pages(sc, ret, k)) and used == k * G
+
+    def above(s, a, b):          # page a ranks above page b
+        if np.isnan(s[b]):
+            return not np.isnan(s[a]) or a < b
+        if np.isnan(s[a]):
+            return False
+        return s[a] > s[b] or (s[a] == s[b] and a < b)
+
+    for _ in range(300):
+        n = int(rng.integers(1, 8))
+        sc = rng.integers(0, 4, n).astype(float)
+        sc[rng.random(n) < 0.15] = np.nan
+        ln = rng.integers(0, 6, n)
+        ret = set(rng.choice(n, int(rng.integers(0, n + 1)), replace=False).tolist())
+        B = int(rng.integers(0, ln.sum() + 2))
+        eff = sc.copy()
+        eff[list(ret)] = -np.inf
+        fits = []
+        for mask in range(1 << n):
+            S = [e for e in range(n) if mask >> e & 1]
+            rest = [e for e in range(n) if not mask >> e & 1]
+            if ln[S].sum() > B:
+                continue
+            if any(above(eff, a, b) for b in S for a in rest):
+                continue
+            best = [e for e in rest if not any(above(eff, a, e) for a in rest if a != e)]
+            if best and ln[S].sum() + ln[best[0]] <= B:
+                continue
+            fits.append(S)
+        assert len(fits) == 1
+        got, used = pe.retained_pages_budget(sc, ln, ret, B)
+        assert list(got) == fits[0] and used == ln[fits[0]].sum()
+
+
 # ---------------------------------------------------------------- PASK controller
 
 def _rand_table(rng, n_tags, C):
