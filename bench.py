@@ -16,6 +16,8 @@ Other workloads (parity cases, measured the same way call by call):
   pask_llama3_8b  64 x 32 layers: prompt compaction, int8/bf16/release tiers, decode
   pask_llama3_8b_int4  the same with the pages' INT4 low tier (two nibbles per byte)
   commitkv_28l    16 x 28 layers: page effects, retirement, checkpoint, paged decode
+  commitkv_events the same commit on event pages (events of 1..40 tokens, pages of at most
+                  16): pages kept under the token budget, compacted by token list
   commitkv_multi  16 x 28 layers: four successive commits (pre/post effects, pending-page
                   protection, checkpoint, retirement); one step = the four commits
   pace_h2o_decode 36 layers x 8 KV heads of 2048 + 32 resident slots: one step is one
@@ -546,19 +548,36 @@ def bench_pipeline(args, w, dev, kind):
                                  + w.n_seq * w.n_layers * w.n_q_heads * d * 2 * 2}
         path_calls = ["kvc_score", "kvc_select", "kvc_compact_rerotate:prompt", "kvc_compact_rerotate:tiered"]
     else:
-        T, B, P, ps = w.n_tokens, w.budget, w.n_pages_all, w.page_size
+        T, B, ps = w.n_tokens, w.budget, w.page_size
         lrows = w.n_seq * Hkv          # rows of the deciding layer
         ab = {"kvc_page_effect:pre": lrows * (2 * T * d * 2 + G * W * d * 2),
               "kvc_page_effect:post": lrows * (2 * T * d * 2 + G * W * d * 2),
               "kvc_page_retire": lrows * (2 * T * d * 2 + G * W * d * 2),
-              "kvc_score": rows * (T * d * 2 + G * W * d * 2 + T * 4),
-              "kvc_page_scores": rows * T * 4 + w.n_seq * P * 4,
-              "kvc_select": w.n_seq * (P * 4 + (B // ps) * 4),
-              "kvc_compact_rerotate": rows * (2 * B * d * 2 * 2 + B * 4),
-              "kvc_decode_attn:pool": rows * 2 * B * d * 2,
-              "kvc_decode_attn:paged": rows * 2 * B * d * 2}
-        path_calls = ["kvc_page_effect:pre", "kvc_page_effect:post", "kvc_page_retire", "kvc_score",
-                      "kvc_page_scores", "kvc_select", "kvc_compact_rerotate"]
+              "kvc_score": rows * (T * d * 2 + G * W * d * 2 + T * 4)}
+        if w.event_max:
+            # event pages: (first, length) read wherever pages are read; the kept token count
+            # per trajectory is what the budget admitted
+            P = int(res["page_first"].shape[1])
+            kept_pages = int(res["n_kept"].sum().item())
+            kept_tok = res["n_tokens"].cpu().numpy().astype(np.int64)
+            per_row_tok = int(kept_tok.sum()) * w.n_layers * Hkv
+            ab.update({"kvc_page_scores": rows * T * 4 + w.n_seq * P * (4 + 8),
+                       "kvc_page_select": w.n_seq * P * (4 + 8) + kept_pages * 4,
+                       "kvc_page_tokens": kept_pages * (4 + 8) + int(kept_tok.sum()) * 4,
+                       "kvc_compact_rerotate": per_row_tok * (2 * d * 2 * 2 + 4),
+                       "kvc_decode_attn:pool": per_row_tok * 2 * d * 2,
+                       "kvc_decode_attn:paged": per_row_tok * 2 * d * 2})
+            path_calls = ["kvc_page_effect:pre", "kvc_page_effect:post", "kvc_page_retire", "kvc_score",
+                          "kvc_page_scores", "kvc_page_select", "kvc_page_tokens", "kvc_compact_rerotate"]
+        else:
+            P = w.n_pages_all
+            ab.update({"kvc_page_scores": rows * T * 4 + w.n_seq * P * 4,
+                       "kvc_select": w.n_seq * (P * 4 + (B // ps) * 4),
+                       "kvc_compact_rerotate": rows * (2 * B * d * 2 * 2 + B * 4),
+                       "kvc_decode_attn:pool": rows * 2 * B * d * 2,
+                       "kvc_decode_attn:paged": rows * 2 * B * d * 2})
+            path_calls = ["kvc_page_effect:pre", "kvc_page_effect:post", "kvc_page_retire", "kvc_score",
+                          "kvc_page_scores", "kvc_select", "kvc_compact_rerotate"]
     ms = sum(part[k] for k in path_calls)
     dom = max(path_calls, key=lambda k: part[k])
     roof = roofline(ab[dom], part[dom], dom, w.name)
@@ -594,6 +613,10 @@ def bench_pipeline(args, w, dev, kind):
         config = {"workload": w.name, "n_seq": w.n_seq, "layers": w.n_layers, "kv_heads": Hkv,
                   "q_heads": w.n_q_heads, "head_dim": d, "tokens": w.n_tokens, "page": w.page_size,
                   "window": W, "budget": w.budget, "decision_layer": w.layer, "parallelism": "none"}
+        if w.event_max:
+            config.update(pages=f"event pages: history events of 1..{w.event_max} tokens cut into pages of "
+                                f"at most {w.page_size}", n_pages=P,
+                          kept_tokens_mean=round(float(res["n_tokens"].float().mean().item()), 1))
     extra = {"breakdown_ms": {k: round(part[k], 4) for k in path_calls},
              "other_ms": {k: round(v, 4) for k, v in part.items() if k not in path_calls},
              "host_ms": host, "calls": per_call_rates(ab, part),

@@ -100,8 +100,12 @@ PROTOTYPES = {
                                        c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "kvc_page_tokens": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_int32, c_void_p, c_void_p, c_int32,
                                        c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p]),
+    "kvc_page_select": (ctypes.c_int, [ctypes.POINTER(KvcDims), c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                       c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "kvc_host_pask_row_actions": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                                  c_void_p]),
+    "kvc_host_event_pages": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_void_p, c_int32,
+                                            c_void_p]),
     "kvc_host_commit_protect": (ctypes.c_int, [c_void_p, c_void_p, c_int32, c_int32, c_double, c_int32,
                                                c_void_p, c_void_p]),
     "kvc_host_pace_renumber": (ctypes.c_int, [c_int64, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p,

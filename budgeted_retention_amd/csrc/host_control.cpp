@@ -3,6 +3,7 @@
 // small sequential loops whose outputs (per-token tier actions, candidate
 // order) feed the GPU calls.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <numeric>
@@ -129,6 +130,28 @@ extern "C" int kvc_host_pask_row_actions(const uint8_t *actions, int32_t n_seq, 
                 for (int32_t t = first_recent; t < n_tok; ++t) out[t] = 2;   // H
             }
         }
+    return KVC_OK;
+}
+
+extern "C" int kvc_host_event_pages(const int32_t *event_len, int32_t n_events, int32_t G, int64_t start,
+                                    int32_t *first, int32_t *len, int32_t cap, int32_t *n_pages) {
+    if (!event_len || !first || !len || !n_pages || n_events < 0 || G <= 0 || start < 0 || cap < 0)
+        return fail(KVC_ERR_ARG, "kvc_host_event_pages: bad arguments");
+    int64_t t = start, count = 0;
+    for (int32_t i = 0; i < n_events; ++i) {
+        const int64_t n_ev = event_len[i];
+        if (n_ev <= 0) return fail(KVC_ERR_ARG, "kvc_host_event_pages: event %d has %lld tokens", i, (long long)n_ev);
+        if (t + n_ev > INT32_MAX) return fail(KVC_ERR_ARG, "kvc_host_event_pages: tokens beyond 2^31 - 1");
+        // cut from the event's first token: pages of G tokens, the last one shorter
+        for (int64_t off = 0; off < n_ev; off += G, ++count)
+            if (count < cap) {
+                first[count] = (int32_t)(t + off);
+                len[count] = (int32_t)(n_ev - off < G ? n_ev - off : G);
+            }
+        t += n_ev;
+    }
+    *n_pages = (int32_t)count;
+    if (count > cap) return fail(KVC_ERR_ARG, "kvc_host_event_pages: %lld pages exceed cap %d", (long long)count, cap);
     return KVC_OK;
 }
 

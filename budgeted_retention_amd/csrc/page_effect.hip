@@ -1144,6 +1144,133 @@ page_tokens_kernel(int64_t T, int page_size, int n_pages, const int32_t *pfirst,
     if (tid == 0) n_tokens[n] = (int32_t)(total < INT32_MAX ? total : INT32_MAX);
 }
 
+// Pages kept under a token budget, one workgroup per sequence. The ranking
+// is (score descending, index ascending), a NaN below every other score; the
+// kept pages are the longest prefix of it whose lengths fit the budget. A
+// three-digit radix select on the score's order key, whose histograms add
+// page lengths instead of counts, finds the key k* of the first page that
+// does not fit and the budget left for the pages of key k*; an ordered pass
+// keeps every page of a larger key and the pages of key k* while their
+// running length (in index order) stays within what is left.
+static constexpr int PK_THREADS = 1024;
+static constexpr int PK_BINS = 2048;
+
+__device__ __forceinline__ uint32_t pk_order_key(float x) {
+    if (x != x) return 0u;
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan over the workgroup; `total` gets the sum. Ends with a barrier.
+__device__ __forceinline__ uint32_t pk_excl_scan(uint32_t v, uint32_t *s_w, uint32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+    for (int m = 1; m < 64; m <<= 1) {
+        const uint32_t u = __shfl_up(incl, m);
+        if (lane >= m) incl += u;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+    for (int w = 0; w < PK_THREADS / 64; ++w) {
+        const uint32_t x = s_w[w];
+        if (w < wave) before += x;
+        total += x;
+    }
+    __syncthreads();
+    return before + incl - v;
+}
+
+__global__ void __launch_bounds__(PK_THREADS)
+page_select_kernel(const float *page_score, int64_t T, int page_size, int n_pages, const int32_t *pfirst,
+                   const int32_t *plen, uint32_t budget, int32_t *kept, int kept_stride, int32_t *n_kept,
+                   int32_t *n_tokens) {
+    __shared__ uint32_t hist[PK_BINS];
+    __shared__ uint32_t s_w[PK_THREADS / 64];
+    __shared__ uint32_t s_sel[2];
+    __shared__ uint32_t s_tie_max;
+    const int n = blockIdx.x, tid = threadIdx.x;
+    const float *sc = page_score + (int64_t)n * n_pages;
+    // page length as the other page calls clamp it (at most 4096 tokens)
+    auto length = [&](int e) -> uint32_t {
+        if (!pfirst) return (uint32_t)page_size;
+        int64_t f = pfirst[(int64_t)n * n_pages + e], l = plen[(int64_t)n * n_pages + e];
+        f = f < 0 ? 0 : (f > T ? T : f);
+        l = l < 0 ? 0 : (l > page_size ? page_size : l);
+        if (l > T - f) l = T - f;
+        return (uint32_t)l;
+    };
+    uint32_t mine = 0;
+    for (int e = tid; e < n_pages; e += PK_THREADS) mine += length(e);
+    uint32_t total;
+    pk_excl_scan(mine, s_w, total);
+    const bool keep_all = total <= budget;
+    uint32_t prefix = 0, mask = 0, rem = budget;
+    if (!keep_all) {
+        // the scope (pages whose key matches the prefix) always outweighs rem
+        const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = shifts[pass];
+            const uint32_t bmask = (1u << widths[pass]) - 1u;
+            for (int i = tid; i < PK_BINS; i += PK_THREADS) hist[i] = 0;
+            __syncthreads();
+            for (int e = tid; e < n_pages; e += PK_THREADS) {
+                const uint32_t k = pk_order_key(sc[e]);
+                if ((k & mask) != prefix) continue;
+                const uint32_t w = length(e);
+                if (w) atomicAdd(&hist[(k >> shift) & bmask], w);
+            }
+            __syncthreads();
+            // bins in descending order, two per thread: thread t has 2047 - 2t, 2046 - 2t
+            const int b0 = PK_BINS - 1 - 2 * tid;
+            const uint32_t h0 = hist[b0], h1 = hist[b0 - 1];
+            uint32_t dummy;
+            const uint32_t before = pk_excl_scan(h0 + h1, s_w, dummy);
+            if (before <= rem && rem - before < h0) {
+                s_sel[0] = (uint32_t)b0;
+                s_sel[1] = rem - before;
+            } else if (before + h0 <= rem && rem - before - h0 < h1) {
+                s_sel[0] = (uint32_t)(b0 - 1);
+                s_sel[1] = rem - before - h0;
+            }
+            __syncthreads();
+            prefix |= s_sel[0] << shift;
+            mask |= bmask << shift;
+            rem = s_sel[1];
+            __syncthreads();
+        }
+    }
+    // prefix = k*, rem = the budget left for the pages of key k*
+    if (tid == 0) s_tie_max = 0;
+    __syncthreads();
+    int32_t *out = kept + (int64_t)n * kept_stride;
+    uint32_t tie_run = 0, count = 0;
+    for (int e0 = 0; e0 < n_pages; e0 += PK_THREADS) {
+        const int e = e0 + tid;
+        uint32_t key = 0, w = 0;
+        if (e < n_pages) {
+            key = pk_order_key(sc[e]);
+            w = length(e);
+        }
+        const bool tie = !keep_all && e < n_pages && key == prefix;
+        uint32_t tie_sum;
+        const uint32_t tie_incl = tie_run + pk_excl_scan(tie ? w : 0u, s_w, tie_sum) + (tie ? w : 0u);
+        const bool keep = e < n_pages && (keep_all || key > prefix || (tie && tie_incl <= rem));
+        if (keep && tie) atomicMax(&s_tie_max, tie_incl);
+        uint32_t n_chunk;
+        const uint32_t slot = count + pk_excl_scan(keep ? 1u : 0u, s_w, n_chunk);
+        if (keep && slot < (uint32_t)kept_stride) out[slot] = e;
+        tie_run += tie_sum;
+        count += n_chunk;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        n_kept[n] = (int32_t)count;
+        if (n_tokens) n_tokens[n] = (int32_t)(keep_all ? total : budget - rem + s_tie_max);
+    }
+}
+
 extern "C" size_t kvc_page_workspace_bytes(const kvc_dims *dims, int32_t W, int64_t q_first) {
     if (check_dims(dims, "kvc_page_workspace_bytes") != KVC_OK) return 0;
     if (W <= 0 || q_first < 0) {
@@ -1303,6 +1430,29 @@ extern "C" int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_
         scores, dims->n_tokens, rows_per_seq, page_size, n_pages, ppb, bps, order, accepted,
         order ? n_cand : 0, page_score);
     return check_launch("kvc_page_scores");
+}
+
+extern "C" int kvc_page_select(const kvc_dims *dims, const float *page_score, int32_t page_size,
+                               const int32_t *page_first, const int32_t *page_len, int32_t n_pages, int32_t budget,
+                               int32_t *kept, int32_t kept_stride, int32_t *n_kept, int32_t *n_tokens,
+                               void *stream) {
+    int st = check_dims(dims, "kvc_page_select");
+    if (st != KVC_OK) return st;
+    if (!page_score || !kept || !n_kept) return fail(KVC_ERR_ARG, "kvc_page_select: NULL pointer");
+    if ((page_first == nullptr) != (page_len == nullptr))
+        return fail(KVC_ERR_ARG, "kvc_page_select: page_first and page_len go together");
+    if (page_size <= 0 || page_size > 4096)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_page_select: page_size %d outside [1, 4096]", page_size);
+    if (n_pages <= 0 || n_pages >= (1 << 20))
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_page_select: n_pages %d outside [1, 2^20)", n_pages);
+    if (!page_first && (int64_t)n_pages * page_size > dims->n_tokens)
+        return fail(KVC_ERR_ARG, "kvc_page_select: %d pages of %d tokens exceed the cache", n_pages, page_size);
+    if (budget < 0 || kept_stride <= 0)
+        return fail(KVC_ERR_ARG, "kvc_page_select: budget %d and kept_stride %d", budget, kept_stride);
+    page_select_kernel<<<dim3((unsigned)dims->n_seq), dim3(PK_THREADS), 0, as_stream(stream)>>>(
+        page_score, dims->n_tokens, page_size, n_pages, page_first, page_len, (uint32_t)budget, kept, kept_stride,
+        n_kept, n_tokens);
+    return check_launch("kvc_page_select");
 }
 
 extern "C" int kvc_page_tokens(const kvc_dims *dims, int32_t page_size, const int32_t *page_first,

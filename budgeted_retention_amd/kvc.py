@@ -283,6 +283,16 @@ def kvc_page_scores(dims, scores, page_size, n_pages, page_score, order=None, ac
     return _lib.check(st)
 
 
+def kvc_page_select(dims, page_score, page_size, n_pages, budget, kept, n_kept, n_tokens=None,
+                    page_first=None, page_len=None, stream=None):
+    pf, pl = _pages(page_first, page_len)
+    st = _lib.load().kvc_page_select(
+        ctypes.byref(dims), _ptr(page_score, torch.float32, "page_score"), page_size, pf, pl, n_pages,
+        int(budget), _ptr(kept, torch.int32, "kept"), kept.shape[-1], _ptr(n_kept, torch.int32, "n_kept"),
+        _ptr(n_tokens, torch.int32, "n_tokens"), _stream(stream))
+    return _lib.check(st)
+
+
 def kvc_page_tokens(dims, page_size, n_pages, pages, n_listed, tokens, n_tokens, page_first=None,
                     page_len=None, stream=None):
     pf, pl = _pages(page_first, page_len)
@@ -341,6 +351,20 @@ def kvc_host_pask_row_actions(actions, n_layers, n_kv_heads, recent):
     _lib.check(_lib.load().kvc_host_pask_row_actions(_np_ptr(acts, np.uint8), n_seq, n_tok, C, n_layers,
                                                      n_kv_heads, int(recent), _np_ptr(out, np.uint8)))
     return out
+
+
+def kvc_host_event_pages(event_len, G, start=0):
+    """event_len: int event lengths of one sequence, in order from token
+    `start`. Returns (first, length), int32 [n_pages] in token order."""
+    import numpy as np
+    ev = np.ascontiguousarray(event_len, np.int32)
+    cap = max(1, int(ev.astype(np.int64).clip(min=0).sum()))     # a page holds at least one token
+    first, length = np.zeros(cap, np.int32), np.zeros(cap, np.int32)
+    n = ctypes.c_int32(0)
+    _lib.check(_lib.load().kvc_host_event_pages(_np_ptr(ev, np.int32), ev.size, int(G), int(start),
+                                                _np_ptr(first, np.int32), _np_ptr(length, np.int32), cap,
+                                                ctypes.byref(n)))
+    return first[: n.value].copy(), length[: n.value].copy()
 
 
 def kvc_host_commit_candidates(R_minus, R_plus, tau_use, tau_dead, rho_use, rho_dead, max_scan=64):

@@ -116,6 +116,22 @@ def run_pask(w, inp, timer=None):
                 pos=po, n_h=nh, Kq=Kq, Vq=Vq, Ks=Ks, Vs=Vs, pos_q=pq, n_l=nl, o=o, lse=lse)
 
 
+def _event_page_arrays(w, inp, dev):
+    """Event pages of every trajectory (kvc_host_event_pages over its event
+    lengths): int32 [N][P] first/length of all pages and the count of
+    eligible ones (pages lying wholly before the pre-commit window: a prefix,
+    pages being in token order). The batched page calls take one page count,
+    so every trajectory must cut into the same number of pages."""
+    cut = [kvc.kvc_host_event_pages(inp.events[n], w.page_size) for n in range(w.n_seq)]
+    counts = {(f.size, int(np.count_nonzero(f + ln <= w.q_first_pre))) for f, ln in cut}
+    if len(counts) != 1:
+        raise ValueError(f"trajectories cut into different page counts {sorted(counts)}")
+    P, n_elig = counts.pop()
+    first = torch.from_numpy(np.stack([f for f, _ in cut])).to(dev)
+    length = torch.from_numpy(np.stack([ln for _, ln in cut])).to(dev)
+    return first, length, P, n_elig
+
+
 def run_commit(w, inp, taus, timer=None):
     """The page-lifecycle workload at one commit: page deletion effects in the
     pre- and post-commit windows, lifecycle labels and candidate order (host),
@@ -123,19 +139,36 @@ def run_commit(w, inp, taus, timer=None):
     checkpoint), checkpoint page scores from the post-commit window, the
     retained page set, the compaction of keys, values and positions by that
     one page set, and decode attention at the next position over the
-    compacted pool and over a paged view of the original storage."""
+    compacted pool and over a paged view of the original storage.
+
+    Uniform pages keep budget / page_size pages (kvc_select over the page
+    scores) and compact by page list. Event pages (w.event_max > 0) are cut
+    on the host, keep the longest prefix of the page ranking that fits the
+    token budget (kvc_page_select), expand it into one token list per
+    trajectory (kvc_page_tokens), compact by that list and decode the
+    original storage through it as a block table of one-token pages."""
     t = timer or _null_timer
     N, L, Hkv, Hq, d, T, W, ps = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
                                   w.n_tokens, w.window, w.page_size)
     dev = inp.K.device
+    events = bool(w.event_max)
     dims = kvc.make_dims(N, L, Hkv, Hq, d, T)
     ws = kvc.page_workspace(dims, W, w.q_first_post, dev)
-    Rm = torch.empty((N, w.n_eligible), dtype=torch.float32, device=dev)
+    if events:
+        with t("host:kvc_host_event_pages"):
+            pf_all, pl_all, P, n_elig = _event_page_arrays(w, inp, dev)
+        pf, pl = pf_all[:, :n_elig].contiguous(), pl_all[:, :n_elig].contiguous()
+    else:
+        pf_all = pl_all = pf = pl = None
+        P, n_elig = w.n_pages_all, w.n_eligible
+    Rm = torch.empty((N, n_elig), dtype=torch.float32, device=dev)
     Rp = torch.empty_like(Rm)
     with t("kvc_page_effect:pre"):
-        kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_pre, W, w.q_first_pre, ps, w.n_eligible, Rm, ws)
+        kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_pre, W, w.q_first_pre, ps, n_elig, Rm, ws,
+                            page_first=pf, page_len=pl)
     with t("kvc_page_effect:post"):
-        kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible, Rp, ws)
+        kvc.kvc_page_effect(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, n_elig, Rp, ws,
+                            page_first=pf, page_len=pl)
     with t("host:kvc_host_commit_candidates"):
         Rm_h, Rp_h = Rm.cpu().numpy(), Rp.cpu().numpy()
         states, orders, n_orders = [], [], []
@@ -151,8 +184,8 @@ def run_commit(w, inp, taus, timer=None):
         acc = torch.zeros((N, w.max_scan), dtype=torch.uint8, device=dev)
         jr = torch.zeros((N, w.max_scan), dtype=torch.float32, device=dev)
         with t("kvc_page_retire" if k == 0 else f"kvc_page_retire:{k}"):
-            kvc.kvc_page_retire(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, w.n_eligible,
-                                order, tau, acc, ws, jr)
+            kvc.kvc_page_retire(dims, w.layer, inp.K, inp.V, inp.Q_post, W, w.q_first_post, ps, n_elig,
+                                order, tau, acc, ws, jr, page_first=pf, page_len=pl)
         retire.append((acc, jr))
     acc = retire[0][0]
     # checkpoint: page scores from the post-commit window, best pages kept for every row
@@ -160,23 +193,36 @@ def run_commit(w, inp, taus, timer=None):
     wss = kvc.workspace(kvc.KVC_OP_SCORE, dims, W, 0, dev)
     with t("kvc_score"):
         kvc.kvc_score(dims, inp.K, inp.Q_post, W, scores, wss)
-    P, Bp, B = w.n_pages_all, w.budget // ps, w.budget
+    B = w.budget
     pscore = torch.empty((N, P), dtype=torch.float32, device=dev)
     with t("kvc_page_scores"):
-        kvc.kvc_page_scores(dims, scores, ps, P, pscore, order, acc)
-    pol = kvc.Policy(0, 0, Bp, 1, 1, 0, 1, None, torch.zeros((1, 1), dtype=torch.float32, device=dev))
-    kept = torch.full((N, Bp), -1, dtype=torch.int32, device=dev)
-    nk = torch.zeros(N, dtype=torch.int32, device=dev)
-    with t("kvc_select"):
-        kvc.kvc_select(kvc.make_dims(N, 1, 1, 1, 64, P), pscore, pol, kept, Bp, nk)
+        kvc.kvc_page_scores(dims, scores, ps, P, pscore, order, acc, page_first=pf_all, page_len=pl_all)
     rows = N * L * Hkv
+    if events:
+        kept = torch.full((N, min(P, B)), -1, dtype=torch.int32, device=dev)
+        nk = torch.zeros(N, dtype=torch.int32, device=dev)
+        n_tok = torch.zeros(N, dtype=torch.int32, device=dev)
+        with t("kvc_page_select"):
+            kvc.kvc_page_select(dims, pscore, ps, P, B, kept, nk, n_tok, page_first=pf_all, page_len=pl_all)
+        tokens = torch.full((N, B), -1, dtype=torch.int32, device=dev)
+        with t("kvc_page_tokens"):
+            kvc.kvc_page_tokens(dims, ps, P, kept, nk, tokens, n_tok, page_first=pf_all, page_len=pl_all)
+        kept_list, kept_stride, kept_page, n_list = tokens, B, 1, n_tok
+    else:
+        Bp = B // ps
+        pol = kvc.Policy(0, 0, Bp, 1, 1, 0, 1, None, torch.zeros((1, 1), dtype=torch.float32, device=dev))
+        kept = torch.full((N, Bp), -1, dtype=torch.int32, device=dev)
+        nk = torch.zeros(N, dtype=torch.int32, device=dev)
+        with t("kvc_select"):
+            kvc.kvc_select(kvc.make_dims(N, 1, 1, 1, 64, P), pscore, pol, kept, Bp, nk)
+        kept_list, kept_stride, kept_page, n_list = kept, Bp, ps, nk
     Ko = torch.zeros((rows, B, d), dtype=torch.bfloat16, device=dev)
     Vo = torch.zeros_like(Ko)
     po = torch.full((rows, B), -1, dtype=torch.int32, device=dev)
     nh = torch.zeros(rows, dtype=torch.int32, device=dev)
     with t("kvc_compact_rerotate"):
-        kvc.kvc_compact_rerotate(dims, inp.K, inp.V, None, kept, Bp, nk, -1, 1e6,
-                                 kvc.CompactOut(B, Ko, Vo, po, nh, kept_page=ps))
+        kvc.kvc_compact_rerotate(dims, inp.K, inp.V, None, kept_list, kept_stride, n_list, -1, 1e6,
+                                 kvc.CompactOut(B, Ko, Vo, po, nh, kept_page=kept_page))
     # decode at position T: over the compacted pool, and through a block table of the kept pages
     dims_c = kvc.make_dims(N, L, Hkv, Hq, d, B)
     o1 = torch.empty((N, L, Hq, d), dtype=torch.bfloat16, device=dev)
@@ -186,13 +232,19 @@ def run_commit(w, inp, taus, timer=None):
     ws1 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_c, B, 0)), dtype=torch.uint8, device=dev)
     with t("kvc_decode_attn:pool"):
         kvc.kvc_decode_attn(dims_c, inp.q_dec, Ko, Vo, nh, B, o1, ws1, lse1)
-    ws2 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims, Bp * ps, 0)), dtype=torch.uint8, device=dev)
-    n_all = torch.full((rows,), B, dtype=torch.int32, device=dev)
+    ws2 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims, kept_stride * kept_page, 0)),
+                      dtype=torch.uint8, device=dev)
+    # every row of a trajectory holds its kept tokens (uniform pages: exactly the budget)
+    n_all = nh if events else torch.full((rows,), B, dtype=torch.int32, device=dev)
     with t("kvc_decode_attn:paged"):
-        kvc.kvc_decode_attn(dims, inp.q_dec, inp.K, inp.V, n_all, T, o2, ws2, lse2, kept, ps, Bp)
-    return dict(Rm=Rm, Rp=Rp, states=np.stack(states), order=np.stack(orders), n_order=np.array(n_orders),
-                retire=retire, scores=scores, pscore=pscore, kept=kept, n_kept=nk, Ko=Ko, Vo=Vo, pos=po, n_h=nh,
-                o1=o1, o2=o2, lse1=lse1, lse2=lse2)
+        kvc.kvc_decode_attn(dims, inp.q_dec, inp.K, inp.V, n_all, T, o2, ws2, lse2, kept_list, kept_page,
+                            kept_stride)
+    out = dict(Rm=Rm, Rp=Rp, states=np.stack(states), order=np.stack(orders), n_order=np.array(n_orders),
+               retire=retire, scores=scores, pscore=pscore, kept=kept, n_kept=nk, Ko=Ko, Vo=Vo, pos=po, n_h=nh,
+               o1=o1, o2=o2, lse1=lse1, lse2=lse2)
+    if events:
+        out.update(page_first=pf_all, page_len=pl_all, n_eligible=n_elig, tokens=tokens, n_tokens=n_tok)
+    return out
 
 
 # PACE §3.1: the foresight bonus scale. Its floor sigma/2 must stay above every

@@ -371,6 +371,7 @@ class CommitWorkload:
     tau_joint: float = 1e-2
     max_scan: int = 64
     seed: int = 20261205
+    event_max: int = 0           # > 0: the history is a run of events of 1..event_max tokens (event pages)
 
     @property
     def n_tokens(self):
@@ -386,11 +387,12 @@ class CommitWorkload:
 
     @property
     def n_eligible(self):
-        """Complete pages lying wholly before the pre-commit window."""
+        """Complete pages lying wholly before the pre-commit window (uniform pages)."""
         return self.q_first_pre // self.page_size
 
     @property
     def n_pages_all(self):
+        """Pages of the whole cache (uniform pages)."""
         return self.n_tokens // self.page_size
 
     @property
@@ -403,6 +405,11 @@ COMMIT_WORKLOADS = {
     "commitkv_small": CommitWorkload("commitkv_small", n_seq=2, n_layers=3, n_kv_heads=2, n_q_heads=6,
                                      n_pre=1024, n_obs=96, window=16, n_planted=6, budget=320, layer=2,
                                      max_scan=8, seed=20261215),
+    # the same commits on event pages: history events of 1..40 tokens, pages of at most 16
+    "commitkv_events": CommitWorkload("commitkv_events", event_max=40, seed=20261235),
+    "commitkv_events_small": CommitWorkload("commitkv_events_small", n_seq=2, n_layers=3, n_kv_heads=2,
+                                            n_q_heads=6, n_pre=1024, n_obs=96, window=16, n_planted=6,
+                                            budget=320, layer=2, max_scan=8, seed=20261247, event_max=40),
 }
 
 
@@ -414,10 +421,33 @@ class CommitInputs:
     Q_pre: torch.Tensor    # bf16 [N][L][Hq][W][d] at positions n_pre-W .. n_pre-1
     Q_post: torch.Tensor   # bf16 [N][L][Hq][W][d] at positions n_pre+n_obs .. T-1
     q_dec: torch.Tensor    # bf16 [N][L][Hq][d] at position T
-    planted: np.ndarray    # int64 [N][n_planted] ascending page indices
+    planted: np.ndarray    # uniform pages: int64 [N][n_planted] ascending page indices;
+                           # events: int64 [N][n_planted][2] (first token, length) of the planted events
+    events: Optional[np.ndarray] = None   # events: int32 [N][n_events] event lengths from token 0 to T
+
+
+def _history_events(w: CommitWorkload):
+    """Event lengths of every trajectory's history (tokens 0 .. q_first_pre):
+    one draw of lengths U[1, event_max] (the last one cut to end at the
+    pre-commit window), shuffled per trajectory, so that every trajectory
+    has the same events in its own order (and the same page count). Then
+    the pre-commit window (the end of the tool call), the observation and
+    the post-commit window as one event each."""
+    rng = np.random.default_rng(w.seed + 41)
+    base, total = [], 0
+    while total < w.q_first_pre:
+        base.append(int(rng.integers(1, w.event_max + 1)))
+        total += base[-1]
+    base[-1] -= total - w.q_first_pre
+    hist = [np.asarray(base)] + [rng.permutation(base) for _ in range(w.n_seq - 1)]
+    tail = [w.window, w.n_obs, w.window]
+    return np.stack([np.concatenate([h, tail]) for h in hist]).astype(np.int32), len(base)
 
 
 def make_commit_inputs(w: CommitWorkload, device="cpu") -> CommitInputs:
+    """Uniform pages: n_planted of the eligible pages are completion pages.
+    Event pages (w.event_max > 0): n_planted history events of page_size/2 ..
+    page_size tokens (one page each) are completion events."""
     N, L, Hkv, Hq, d, T, W = (w.n_seq, w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim,
                               w.n_tokens, w.window)
     G = Hq // Hkv
@@ -428,21 +458,41 @@ def make_commit_inputs(w: CommitWorkload, device="cpu") -> CommitInputs:
     Qp = normal_bf16((N, L, Hq, W, d), s + 4, device)
     qd = normal_bf16((N, L, Hq, d), s + 5, device)
     rng = np.random.default_rng(w.seed + 31)
-    planted = np.stack([np.sort(rng.choice(w.n_eligible, w.n_planted, replace=False)) for _ in range(N)])
+    ps = w.page_size
+    events = None
+    if w.event_max:
+        events, n_hist = _history_events(w)
+        spans = []
+        for n in range(N):
+            start = np.concatenate([[0], np.cumsum(events[n][:n_hist])[:-1]])
+            ok = np.flatnonzero((events[n][:n_hist] >= (ps + 1) // 2) & (events[n][:n_hist] <= ps))
+            if ok.size < w.n_planted:
+                raise ValueError(f"{w.name}: {ok.size} events of {(ps + 1) // 2}..{ps} tokens, "
+                                 f"{w.n_planted} to plant")
+            pick = np.sort(rng.choice(ok, w.n_planted, replace=False))
+            spans.append(np.stack([start[pick], events[n][pick]], axis=1))
+        planted = np.stack(spans).astype(np.int64)
+    else:
+        planted = np.stack([np.sort(rng.choice(w.n_eligible, w.n_planted, replace=False)) for _ in range(N)])
     u = rng.standard_normal((N, L, Hkv, d))
     u /= np.linalg.norm(u, axis=-1, keepdims=True)
     c = float(np.sqrt(w.plant_logit * np.sqrt(d)))
     cu = torch.from_numpy(c * u).to(device=device, dtype=torch.float32)        # [N][L][Hkv][d]
-    ps = w.page_size
     for n in range(N):
-        Kn = K[n].view(L, Hkv, T // ps, ps, d)
-        idx = torch.from_numpy(planted[n]).to(device)
-        sel = Kn.index_select(2, idx).float() + cu[n][:, :, None, None, :]
-        Kn.index_copy_(2, idx, sel.to(torch.bfloat16))
+        if w.event_max:
+            tok = np.concatenate([np.arange(f, f + ln) for f, ln in planted[n]])
+            idx = torch.from_numpy(tok).to(device)
+            sel = K[n].index_select(2, idx).float() + cu[n][:, :, None, :]
+            K[n].index_copy_(2, idx, sel.to(torch.bfloat16))
+        else:
+            Kn = K[n].view(L, Hkv, T // ps, ps, d)
+            idx = torch.from_numpy(planted[n]).to(device)
+            sel = Kn.index_select(2, idx).float() + cu[n][:, :, None, None, :]
+            Kn.index_copy_(2, idx, sel.to(torch.bfloat16))
     cq = cu.repeat_interleave(G, dim=2)[:, :, :, None, :]                        # [N][L][Hq][1][d]
     Qm = (Qm.float() + cq).to(torch.bfloat16)
     Qp = (Qp.float() - cq).to(torch.bfloat16)
-    return CommitInputs(w, K, V, Qm, Qp, qd, planted)
+    return CommitInputs(w, K, V, Qm, Qp, qd, planted, events)
 
 
 # ---------------------------------------------------------------- PACE-style H2O decode with eviction

@@ -469,6 +469,33 @@ int kvc_page_scores(const kvc_dims *dims, const float *scores, int32_t page_size
                     void *stream);
 
 /*
+ * Pages kept under a token budget (CommitKV §3.3, Eq. 13: the retained index
+ * set holds at most B tokens; with event pages, §3.1, pages differ in
+ * length). For every sequence n the pages are ranked by (page_score
+ * descending, page index ascending), a NaN score below every other (-inf,
+ * the score of a retired page, ranks below every finite one); the kept pages
+ * are the longest prefix of that ranking whose lengths sum to at most
+ * `budget`: the first page that does not fit ends it.
+ *
+ *   page_score   fp32 [N][n_pages] (from kvc_page_scores)
+ *   pages        uniform or event pages as for the calls above (lengths
+ *                clamped the same way); 1 <= page_size <= 4096,
+ *                1 <= n_pages < 2^20
+ *   budget       tokens, >= 0
+ *   kept         int32 [N][kept_stride]: the first kept_stride kept pages in
+ *                ascending order
+ *   n_kept       int32 [N]: the number of kept pages (may exceed kept_stride;
+ *                the rest are not written)
+ *   n_tokens     int32 [N] or NULL: their total length (<= budget), which
+ *                kvc_page_tokens then expands
+ * With uniform pages of page_size tokens and a budget of k*page_size this is
+ * kvc_select's top-k over the page scores.
+ */
+int kvc_page_select(const kvc_dims *dims, const float *page_score, int32_t page_size,
+                    const int32_t *page_first, const int32_t *page_len, int32_t n_pages, int32_t budget,
+                    int32_t *kept, int32_t kept_stride, int32_t *n_kept, int32_t *n_tokens, void *stream);
+
+/*
  * Token list of per-sequence page lists: the retained index set of CommitKV
  * §3.3 Eq. 13 as one set of token indices for every layer and head (Eq. 4).
  * For sequence n the listed pages pages[n][0 .. min(n_listed[n], list_stride))
@@ -526,6 +553,25 @@ typedef struct kvc_pask_table {
 int kvc_host_pask_control(const kvc_pask_table *tbl, const double *costs, double budget_fraction,
                           double reserve, const uint8_t *tags, int32_t n_seq, int32_t n_tok,
                           uint8_t *actions, double *ledger);
+
+/*
+ * Event pages of one sequence (CommitKV §3.1, "Agent events and commit
+ * transitions": every completed event is partitioned into contiguous pages
+ * of at most G tokens, so no page spans two events). Events follow one
+ * another from token `start`; event i has event_len[i] >= 1 tokens and is
+ * cut from its first token into pages of G tokens, the last one shorter.
+ * Page p is tokens [first[p], first[p] + len[p]), in token order: the
+ * page_first / page_len of the page calls (sequences whose page counts agree
+ * are stacked as [N][n_pages]).
+ *   event_len   host int32 [n_events]
+ *   G           >= 1 (the page calls' page_size)
+ *   first, len  host int32 [cap]
+ *   n_pages     out: the number of pages. When it exceeds cap the call
+ *               returns KVC_ERR_ARG after writing the first cap pages, with
+ *               the full count in *n_pages. Tokens must stay below 2^31.
+ */
+int kvc_host_event_pages(const int32_t *event_len, int32_t n_events, int32_t G, int64_t start,
+                         int32_t *first, int32_t *len, int32_t cap, int32_t *n_pages);
 
 /*
  * Per-row physical actions of the generated tokens (PASK §3.2: the layers of

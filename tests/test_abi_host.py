@@ -230,6 +230,17 @@ def test_event_page_arguments_are_checked_before_any_launch():
     assert tok(ls=0) == _lib.KVC_ERR_ARG
     assert tok(os_=0) == _lib.KVC_ERR_ARG
     assert lib.kvc_last_error().decode().startswith("kvc_page_tokens")
+    sel = lambda ps=16, pf=FAKE, pl=FAKE, n=70, b=512, ks=64, kept=FAKE: lib.kvc_page_select(
+        ctypes.byref(d), FAKE, ps, pf, pl, n, b, kept, ks, FAKE, None, None)
+    assert sel(pl=None) == _lib.KVC_ERR_ARG
+    assert sel(kept=None) == _lib.KVC_ERR_ARG
+    assert sel(ps=4097) == _lib.KVC_ERR_UNSUPPORTED                 # lengths up to 4096 keep the sums in 32 bits
+    assert sel(n=1 << 20) == _lib.KVC_ERR_UNSUPPORTED
+    assert sel(n=0) == _lib.KVC_ERR_UNSUPPORTED
+    assert sel(b=-1) == _lib.KVC_ERR_ARG
+    assert sel(ks=0) == _lib.KVC_ERR_ARG
+    assert sel(pf=None, pl=None, n=63) == _lib.KVC_ERR_ARG          # 63 uniform pages of 16 pass 1000 tokens
+    assert lib.kvc_last_error().decode().startswith("kvc_page_select")
 
 
 def test_compact_reference_store_rejects_bad_combinations():

@@ -59,6 +59,29 @@ def test_commit_candidates_match_oracle():
     assert np.all(order[n_order:] == -1)
 
 
+@pytest.mark.parametrize("G,start,max_ev", [(16, 0, 40), (1, 7, 5), (64, 100, 300), (9, 0, 9)])
+def test_event_pages_match_oracle(G, start, max_ev):
+    rng = np.random.default_rng(G * 1000 + max_ev)
+    ev = rng.integers(1, max_ev + 1, 400)
+    first, length = kvc.kvc_host_event_pages(ev, G, start)
+    o_first, o_len = o_pe.event_pages(ev, G, start)
+    np.testing.assert_array_equal(first, o_first)
+    np.testing.assert_array_equal(length, o_len)
+
+
+def test_event_pages_beyond_the_cap_report_the_count_and_write_only_cap():
+    import ctypes
+    from budgeted_retention_amd import _lib
+    ev = np.array([5, 3, 9], np.int32)                  # pages of 4: [4, 1], [3], [4, 4, 1]
+    first = np.full(4, -7, np.int32)
+    length = np.full(4, -7, np.int32)
+    n = ctypes.c_int32(0)
+    st = _lib.load().kvc_host_event_pages(ev.ctypes.data, 3, 4, 0, first.ctypes.data, length.ctypes.data, 2,
+                                          ctypes.byref(n))
+    assert st != 0 and n.value == 6
+    assert list(first) == [0, 4, -7, -7] and list(length) == [4, 1, -7, -7]
+
+
 def test_host_helpers_reject_bad_arguments():
     from budgeted_retention_amd import _lib
     with pytest.raises(_lib.KvcError):
@@ -72,6 +95,12 @@ def test_host_helpers_reject_bad_arguments():
         kvc.kvc_host_pask_row_actions(np.zeros((1, 4, 2), np.uint8), 0, 8, 2)   # no layers
     with pytest.raises(_lib.KvcError):
         kvc.kvc_host_pask_row_actions(np.zeros((1, 4, 2), np.uint8), 4, 8, -1)  # negative window
+    with pytest.raises(_lib.KvcError):
+        kvc.kvc_host_event_pages([3, 0, 2], 4)                                   # an empty event
+    with pytest.raises(_lib.KvcError):
+        kvc.kvc_host_event_pages([3, 2], 0)                                      # G = 0
+    with pytest.raises(_lib.KvcError):
+        kvc.kvc_host_event_pages([2 ** 30, 2 ** 30], 64, 2 ** 30)                 # tokens past 2^31 - 1
 
 
 def test_commit_protection_matches_oracle_and_the_page_budget():

@@ -235,3 +235,97 @@ def test_page_tokens_skips_bad_entries_and_truncates():
         got = tokens[n].cpu().numpy()
         np.testing.assert_array_equal(got[: min(12, want.size)], want[:12].astype(np.int32))
         assert np.all(got[want.size:] == -7)
+
+
+def _page_select(n_seq, T, G, scores, first=None, length=None, budget=0, stride=None):
+    from budgeted_retention_amd import kvc
+    n_pages = scores.shape[1]
+    dims = kvc.make_dims(n_seq, 1, 1, 1, 64, T)
+    stride = stride or n_pages
+    kept = torch.full((n_seq, stride), -1, dtype=torch.int32, device="cuda")
+    nk = torch.full((n_seq,), -1, dtype=torch.int32, device="cuda")
+    ntok = torch.full((n_seq,), -1, dtype=torch.int32, device="cuda")
+    pf = None if first is None else torch.from_numpy(first).cuda()
+    pl = None if length is None else torch.from_numpy(length).cuda()
+    kvc.kvc_page_select(dims, torch.from_numpy(scores).cuda(), G, n_pages, budget, kept, nk, ntok,
+                        page_first=pf, page_len=pl)
+    torch.cuda.synchronize()
+    return kept.cpu().numpy(), nk.cpu().numpy(), ntok.cpu().numpy()
+
+
+@pytest.mark.parametrize("n_pages", [1, 700, 1023, 1024, 1025, 3000])
+@pytest.mark.parametrize("dist", ["ties", "gamma_inf_nan"])
+def test_page_select_under_a_token_budget_matches_the_oracle(n_pages, dist):
+    """kvc_page_select against oracle.page_effect.retained_pages_budget: the
+    longest prefix of the (score desc, index asc) ranking whose page lengths
+    fit the budget. Index work: exact."""
+    rng = np.random.default_rng(n_pages * 7 + len(dist))
+    N, G = 3, 16
+    first, length, P = _event_pages(rng, N, 60 * n_pages, G, max_event=30)
+    first, length = first[:, :n_pages].copy(), length[:, :n_pages].copy()
+    T = int((first + length).max())
+    if dist == "ties":
+        sc = rng.integers(0, 4, (N, n_pages)).astype(np.float32)
+    else:
+        sc = rng.gamma(0.5, 1.0, (N, n_pages)).astype(np.float32)
+        sc[rng.random((N, n_pages)) < 0.05] = -np.inf
+        sc[rng.random((N, n_pages)) < 0.02] = np.nan
+    tot = length.astype(np.int64).sum(axis=1)
+    for budget in sorted({0, 1, int(tot.min()) // 3, int(tot.min()) - 1, int(tot.min()), int(tot.max()) + 5}):
+        budget = max(budget, 0)
+        kept, nk, ntok = _page_select(N, T, G, sc, first, length, budget)
+        for n in range(N):
+            want, used = o_pe.retained_pages_budget(sc[n].astype(np.float64), length[n], (), budget)
+            assert nk[n] == want.size and ntok[n] == used, (n, budget)
+            np.testing.assert_array_equal(kept[n][: want.size], want.astype(np.int32))
+
+
+def test_page_select_uniform_pages_equal_the_top_k_select():
+    """Uniform pages and a budget of k pages' tokens: kvc_select's top-k."""
+    from budgeted_retention_amd import kvc
+    rng = np.random.default_rng(4)
+    N, G, P, k = 4, 16, 2500, 300
+    sc = rng.integers(0, 50, (N, P)).astype(np.float32)                 # many ties
+    sc[:, ::97] = -np.inf
+    kept, nk, ntok = _page_select(N, P * G, G, sc, budget=k * G + G - 1)
+    pol = kvc.Policy(0, 0, k, 1, 1, 0, 1, None, torch.zeros((1, 1), dtype=torch.float32, device="cuda"))
+    kept2 = torch.full((N, k), -1, dtype=torch.int32, device="cuda")
+    nk2 = torch.zeros(N, dtype=torch.int32, device="cuda")
+    kvc.kvc_select(kvc.make_dims(N, 1, 1, 1, 64, P), torch.from_numpy(sc).cuda(), pol, kept2, k, nk2)
+    torch.cuda.synchronize()
+    assert np.all(nk == k) and np.all(ntok == k * G)
+    np.testing.assert_array_equal(kept[:, :k], kept2.cpu().numpy())
+    for n in range(N):
+        np.testing.assert_array_equal(kept[n][:k], o_pe.retained_pages(sc[n].astype(np.float64), (), k))
+
+
+def test_page_select_short_list_clamped_pages_and_the_largest_size():
+    """A kept list shorter than the kept count holds its first entries;
+    clamped page spans (past the cache, negative, longer than page_size) count
+    their clamped lengths; 2^20 - 1 pages of 4096 tokens stay within 32-bit
+    sums."""
+    rng = np.random.default_rng(9)
+    N, G, P, T = 2, 16, 2000, 20000
+    first = np.sort(rng.integers(-40, T + 40, (N, P))).astype(np.int32)
+    length = rng.integers(-3, 24, (N, P)).astype(np.int32)
+    sc = rng.gamma(1.0, 1.0, (N, P)).astype(np.float32)
+    clamped = np.clip(length, 0, G)
+    f = np.clip(first, 0, T)
+    clamped = np.minimum(clamped, T - f)
+    kept, nk, ntok = _page_select(N, T, G, sc, first, length, 5000, stride=64)
+    for n in range(N):
+        want, used = o_pe.retained_pages_budget(sc[n].astype(np.float64), clamped[n], (), 5000)
+        assert nk[n] == want.size > 64 and ntok[n] == used
+        np.testing.assert_array_equal(kept[n], want[:64].astype(np.int32))
+    # the largest call: every page 4096 tokens, a budget just under the 2^31 limit
+    P = (1 << 20) - 1
+    G = 4096
+    sc = rng.random((1, P)).astype(np.float32)
+    first = np.zeros((1, P), np.int32)
+    length = np.full((1, P), G, np.int32)
+    budget = (1 << 31) - 1
+    kept, nk, ntok = _page_select(1, G, G, sc, first, length, budget)
+    n_fit = budget // G
+    want = np.sort(np.lexsort((np.arange(P), -sc[0].astype(np.float64)))[:n_fit])
+    assert nk[0] == n_fit and ntok[0] == n_fit * G
+    np.testing.assert_array_equal(kept[0][:n_fit], want.astype(np.int32))
