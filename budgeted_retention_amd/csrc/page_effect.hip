@@ -467,6 +467,20 @@ __device__ __forceinline__ void pm_pv(const uint16_t *sv, const float (&w)[16], 
     }
 }
 
+// As pm_pv, with the weights of keys outside [lo, hi) of the tile taken as 0.
+template <int D>
+__device__ __forceinline__ void pm_pv_span(const uint16_t *sv, const float (&w)[16], int db, int j_lo, int j_hi,
+                                           int lo, int hi, f32x16 &c) {
+    const int lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j < j_lo || j >= j_hi) continue;
+        const int k = acc_row(j, hf);
+        const float v = bf16_to_f32(sv[k * D + db * 32 + col]);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(v, (k >= lo && k < hi) ? w[j] : 0.f, c, 0, 0, 0);
+    }
+}
+
 // Window outputs o_q = sum_k a_qk v_k: each workgroup covers PO_CHUNK keys for one
 // query block, its four waves summed in LDS, one partial per chunk.
 template <int D>
@@ -603,6 +617,119 @@ __global__ void __launch_bounds__(PM_THREADS) pe_effect_mfma(PeArgs a, int chunk
                 if (a.eff_abs) atomic_max_nonneg(a.eff_abs + (size_t)n_seq_idx * a.n_pages + page, ab);
             }
         }
+    }
+}
+
+// Event pages of at most 32 tokens on the matrix cores. Each wave walks its
+// own run of PSM_PAGES pages: it forms the logits, weights and V tile of the
+// 32 keys from a page's first token (pm_tile), takes every following page
+// lying wholly inside them, and for each page masks the weights of the other
+// keys and forms S = sum_{k in page} a_qk v_k over the key groups the page
+// touches; the norm and the reduction to the page's maximum are as in
+// pe_effect_mfma. Pages in token order share tiles; any order is correct.
+static constexpr int PSM_PAGES = 64;   // pages per wave: lane i holds page i's span
+
+template <int D>
+__global__ void __launch_bounds__(PM_THREADS) pe_effect_spans_mfma(PeArgs a, int chunks) {
+    constexpr int NDB = D / 32;
+    __shared__ uint16_t s_v[PM_THREADS / 64][32 * D];
+    __shared__ float s_o[32][D + 4];
+    const int nb = (a.G * a.W + 31) / 32;
+    const int64_t rr = blockIdx.x / (nb * chunks);
+    const int b = (int)((blockIdx.x / chunks) % nb);
+    const int ch = (int)(blockIdx.x % chunks);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+    bf16x8 qf[D / 16];
+    float mmq;
+    int64_t qpos;
+    bool qvalid;
+    const uint16_t *Kr, *Vr;
+    pm_setup<D>(a, rr, b, qf, mmq, qpos, qvalid, &Kr, &Vr);
+    const int QRP = nb * 32;
+    // the block's window outputs o_q, shared by the four waves (rows padded against bank conflicts)
+    const float *ob = a.o + ((size_t)rr * QRP + b * 32) * D;
+    for (int e = threadIdx.x; e < 32 * D; e += PM_THREADS) s_o[e / D][e % D] = ob[e];
+    __syncthreads();
+    float o2 = 0.f;
+    for (int e = hf * 4; e < D; e += 8) {   // the lane's elements in pe_effect_mfma's order
+        const float4 ov = *reinterpret_cast<const float4 *>(&s_o[col][e]);
+        o2 = fmaf(ov.x, ov.x, o2);
+        o2 = fmaf(ov.y, ov.y, o2);
+        o2 = fmaf(ov.z, ov.z, o2);
+        o2 = fmaf(ov.w, ov.w, o2);
+    }
+    o2 += __shfl_xor(o2, 32);
+    const float onorm = sqrtf(o2);
+    const int n_seq_idx = (int)(rr / a.Hkv);
+    const int e_begin = (ch * (PM_THREADS / 64) + wave) * PSM_PAGES;
+    const int n_here = a.n_pages - e_begin < PSM_PAGES ? a.n_pages - e_begin : PSM_PAGES;
+    int my_first = 0, my_len = 0;
+    if (lane < n_here) {
+        int64_t f;
+        int l;
+        page_span(a, n_seq_idx, e_begin + lane, f, l);
+        my_first = (int)f;
+        my_len = l;
+    }
+    int i = 0;
+    while (i < n_here) {   // i, i1 and p are the same for every lane
+        const int j0 = __builtin_amdgcn_readlane(my_first, i);
+        int i1 = i + 1;
+        while (i1 < n_here) {
+            const int f = __builtin_amdgcn_readlane(my_first, i1), l = __builtin_amdgcn_readlane(my_len, i1);
+            if (f < j0 || f + l > j0 + 32) break;
+            ++i1;
+        }
+        float w[16];
+        pm_tile<D>(a, Kr, Vr, j0, qf, mmq, qpos, s_v[wave], w);
+        for (int p = i; p < i1; ++p) {
+            const int lo = __builtin_amdgcn_readlane(my_first, p) - j0;
+            const int hi = lo + __builtin_amdgcn_readlane(my_len, p);
+            float al = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int k = acc_row(j, hf);
+                al += (k >= lo && k < hi) ? w[j] : 0.f;
+            }
+            al += __shfl_xor(al, 32);
+            // key k is in MFMA step 4 * (k / 8) + k % 4 (lane half (k / 4) % 2)
+            const int j_lo = 4 * (lo >> 3), j_hi = hi > lo ? 4 * ((hi - 1) >> 3) + 4 : 0;
+            float n2 = 0.f;
+#pragma unroll 1
+            for (int db = 0; db < NDB; ++db) {   // one accumulator live at a time
+                f32x16 c = {};
+                pm_pv_span<D>(s_v[wave], w, db, j_lo, j_hi, lo, hi, c);
+#pragma unroll
+                for (int r = 0; r < 16; r += 4) {
+                    const float4 ov = *reinterpret_cast<const float4 *>(&s_o[col][db * 32 + acc_row(r, hf)]);
+                    const float ovs[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float t = fmaf(-al, ovs[u], c[r + u]);
+                        n2 = fmaf(t, t, n2);
+                    }
+                }
+            }
+            n2 += __shfl_xor(n2, 32);
+            float rel = 0.f, ab = 0.f;
+            if (qvalid) {
+                const float num = sqrtf(n2);
+                const float den = 1.f - al;
+                ab = den > 0.f ? num / den : INFINITY;
+                rel = onorm > 0.f ? ab / onorm : (num > 0.f ? INFINITY : 0.f);
+                if (!(num > 0.f)) ab = rel = 0.f;
+            }
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                rel = fmaxf(rel, __shfl_xor(rel, off));
+                ab = fmaxf(ab, __shfl_xor(ab, off));
+            }
+            if (lane == 0) {
+                atomic_max_nonneg(a.eff_rel + (size_t)n_seq_idx * a.n_pages + e_begin + p, rel);
+                if (a.eff_abs) atomic_max_nonneg(a.eff_abs + (size_t)n_seq_idx * a.n_pages + e_begin + p, ab);
+            }
+        }
+        i = i1;
     }
 }
 
@@ -1303,7 +1430,18 @@ extern "C" int kvc_page_effect(const kvc_dims *dims, int32_t layer, const uint16
     if ((st = check_launch("kvc_page_effect clear")) != KVC_OK) return st;
     if ((st = pe_prepare(dims, a, w, s)) != KVC_OK) return st;
     const PageGeom g = page_geom(dims, W, q_first + W);
-    if (page_first) {
+    if (page_first && page_size <= 32) {
+        const int per_wg = PSM_PAGES * (PM_THREADS / 64);
+        const int chunks = (n_pages + per_wg - 1) / per_wg;
+        const int64_t blocks = g.rows_local * g.nb * chunks;
+        if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_effect: grid too large");
+        if (dims->head_dim == 128)
+            pe_effect_spans_mfma<128><<<dim3((unsigned)blocks), dim3(PM_THREADS), 0, s>>>(a, chunks);
+        else
+            pe_effect_spans_mfma<64><<<dim3((unsigned)blocks), dim3(PM_THREADS), 0, s>>>(a, chunks);
+        return check_launch("kvc_page_effect");
+    }
+    if (page_first) {   // event pages of 33 .. 64 tokens
         const int cpr = (n_pages + PE_SPAN_CHUNK - 1) / PE_SPAN_CHUNK;
         const int64_t blocks = g.rows_local * g.nb * cpr;
         if (blocks > (int64_t)INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "kvc_page_effect: grid too large");
