@@ -402,13 +402,18 @@ __global__ void fill_f32(float *p, int64_t n, float v) {
 // A wave owns one block of 32 query rows of one row and walks 32-key tiles.
 // Logits come from v_mfma_f32_32x32x16_bf16 as C[key][q] (lane (col, hf) holds
 // query row col and keys acc_row(i, hf)); the weights a = exp2(logit*c - mm)
-// stay in those registers. P·V is then formed as C[d][q] = sum_k V[k][d] P[q][k]
-// with v_mfma_f32_32x32x2_f32, two keys per instruction: in instruction j the
-// lane half hf contributes key acc_row(j, hf), the lane supplying V[that key][d]
-// (d = its column of the 32-dimension block, staged in LDS) and its own weight.
-// Every lane then holds query row col over 16 dimensions of each block, so a
-// row's squared norm is an in-lane sum plus one shuffle. fp32 operands: the
-// weights are not rounded.
+// stay in those registers. P·V is then C[d][q] = sum_k V[k][d] P[q][k], again
+// on v_mfma_f32_32x32x16_bf16 over 16 keys at a time: lane (col, g) supplies
+// A[col][8g .. 8g+7] and B[8g .. 8g+7][col]. The instruction's k index is
+// mapped to keys so that B is the lane's own weights: in key block beta (keys
+// 16*beta .. 16*beta + 15 of the tile) k = 8g + t stands for key
+// acc_row(8*beta + t, g), which is where the logits left that key's weight
+// for query row col; A is then V of those keys at dimension col of the
+// dimension block, gathered from the wave's V tile in LDS. Each fp32 weight
+// is split into hi = bf16(w) and lo = bf16(w - hi) (w - hi is exact in fp32),
+// so hi + lo carries about 16 significant bits; V is bf16 already. Every
+// lane then holds query row col over 16 dimensions of each block, so a row's
+// squared norm is an in-lane sum plus one shuffle.
 
 template <int D>
 __device__ __forceinline__ void pm_setup(const PeArgs &a, int64_t rr, int b, bf16x8 (&qf)[D / 16], float &mmq,
@@ -454,31 +459,58 @@ __device__ __forceinline__ void pm_tile(const PeArgs &a, const uint16_t *Kr, con
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // the V tile is written before it is read
 }
 
-// C[d][q] of dimension block db over the tile's keys acc_row(j, hf), j in [j_lo, j_hi).
-template <int D>
-__device__ __forceinline__ void pm_pv(const uint16_t *sv, const float (&w)[16], int db, int j_lo, int j_hi,
-                                      f32x16 &c) {
-    const int lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+// The split weights of one tile: hi[beta], lo[beta] are the B operands of key block beta.
+struct PvWeights {
+    bf16x8 hi[2], lo[2];
+};
+
+__device__ __forceinline__ PvWeights pv_split(const float (&w)[16]) {
+    PvWeights p;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j < j_lo || j >= j_hi) continue;
-        const float v = bf16_to_f32(sv[acc_row(j, hf) * D + db * 32 + col]);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(v, w[j], c, 0, 0, 0);
-    }
+    for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float x = w[8 * beta + t];
+            const __bf16 h = (__bf16)x;
+            p.hi[beta][t] = h;
+            p.lo[beta][t] = (__bf16)(x - (float)h);
+        }
+    return p;
 }
 
-// As pm_pv, with the weights of keys outside [lo, hi) of the tile taken as 0.
+// The A operand of key block beta and dimension block db: V[acc_row(8*beta + t, g)][db*32 + col].
 template <int D>
-__device__ __forceinline__ void pm_pv_span(const uint16_t *sv, const float (&w)[16], int db, int j_lo, int j_hi,
-                                           int lo, int hi, f32x16 &c) {
-    const int lane = threadIdx.x & 63, col = lane & 31, hf = lane >> 5;
+__device__ __forceinline__ bf16x8 pv_v(const uint16_t *sv, int db, int beta) {
+    const int lane = threadIdx.x & 63, col = lane & 31, g = lane >> 5;
+    uint16_t e[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j < j_lo || j >= j_hi) continue;
-        const int k = acc_row(j, hf);
-        const float v = bf16_to_f32(sv[k * D + db * 32 + col]);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(v, (k >= lo && k < hi) ? w[j] : 0.f, c, 0, 0, 0);
+    for (int t = 0; t < 8; ++t) e[t] = sv[acc_row(8 * beta + t, g) * D + db * 32 + col];
+    const uint4 u = make_uint4(e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                               e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// c += V^T P over key block beta with split weights (hi, then lo).
+__device__ __forceinline__ void pv_block(const bf16x8 &va, const bf16x8 &hi, const bf16x8 &lo, f32x16 &c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, lo, c, 0, 0, 0);
+}
+
+// The weights of one key block with those of keys outside [lo, hi) of the tile set to 0.
+__device__ __forceinline__ bf16x8 pv_mask(const bf16x8 &x, int beta, int lo, int hi) {
+    const int g = (threadIdx.x & 63) >> 5;
+    uint4 u = __builtin_bit_cast(uint4, x);
+    uint32_t m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k0 = acc_row(8 * beta + 2 * q, g), k1 = acc_row(8 * beta + 2 * q + 1, g);
+        m[q] = (k0 >= lo && k0 < hi ? 0xFFFFu : 0u) | (k1 >= lo && k1 < hi ? 0xFFFF0000u : 0u);
     }
+    u.x &= m[0];
+    u.y &= m[1];
+    u.z &= m[2];
+    u.w &= m[3];
+    return __builtin_bit_cast(bf16x8, u);
 }
 
 // Window outputs o_q = sum_k a_qk v_k: each workgroup covers PO_CHUNK keys for one
@@ -507,8 +539,12 @@ __global__ void __launch_bounds__(PM_THREADS) pe_out_mfma(PeArgs a, int chunks) 
     for (int64_t j0 = c0 + 32 * wave; j0 < c1; j0 += 32 * (PM_THREADS / 64)) {
         float w[16];
         pm_tile<D>(a, Kr, Vr, j0, qf, mmq, qpos, s_v[wave], w);
+        const PvWeights pw = pv_split(w);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) pm_pv<D>(s_v[wave], w, db, 0, 16, co[db]);
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int beta = 0; beta < 2; ++beta)
+                pv_block(pv_v<D>(s_v[wave], db, beta), pw.hi[beta], pw.lo[beta], co[db]);
     }
     // waves in turn add their partial into s_o
     for (int wv = 0; wv < PM_THREADS / 64; ++wv) {
@@ -544,7 +580,7 @@ __global__ void pe_out_reduce(const float *opart, float *o, int64_t n, int chunk
 template <int D, int PS>
 __global__ void __launch_bounds__(PM_THREADS) pe_effect_mfma(PeArgs a, int chunks) {
     constexpr int NDB = D / 32;
-    constexpr int JP = PS / 2;  // MFMA key pairs per page
+    constexpr int JP = PS / 2;  // a page's weights among a lane's 16
     __shared__ uint16_t s_v[PM_THREADS / 64][32 * D];
     const int nb = (a.G * a.W + 31) / 32;
     const int64_t rr = blockIdx.x / (nb * chunks);
@@ -580,17 +616,30 @@ __global__ void __launch_bounds__(PM_THREADS) pe_effect_mfma(PeArgs a, int chunk
     for (int64_t j0 = c0 + 32 * wave; j0 < c1; j0 += 32 * (PM_THREADS / 64)) {
         float w[16];
         pm_tile<D>(a, Kr, Vr, j0, qf, mmq, qpos, s_v[wave], w);
+        const PvWeights pw = pv_split(w);
 #pragma unroll
         for (int pg = 0; pg < 32 / PS; ++pg) {
             float al = 0.f;
 #pragma unroll
             for (int j = pg * JP; j < (pg + 1) * JP; ++j) al += w[j];
             al += __shfl_xor(al, 32);
+            // key blocks of the page: both (32 tokens), block pg (16), or half of block pg / 2 (8)
+            const int beta = PS == 16 ? pg : pg / 2;
+            bf16x8 mh = pw.hi[beta], ml = pw.lo[beta];
+            if (PS == 8) {
+                mh = pv_mask(mh, beta, 8 * pg, 8 * pg + 8);
+                ml = pv_mask(ml, beta, 8 * pg, 8 * pg + 8);
+            }
             float n2 = 0.f;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 f32x16 c = {};
-                pm_pv<D>(s_v[wave], w, db, pg * JP, (pg + 1) * JP, c);
+                if (PS == 32) {
+                    pv_block(pv_v<D>(s_v[wave], db, 0), pw.hi[0], pw.lo[0], c);
+                    pv_block(pv_v<D>(s_v[wave], db, 1), pw.hi[1], pw.lo[1], c);
+                } else {
+                    pv_block(pv_v<D>(s_v[wave], db, beta), mh, ml, c);
+                }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float t = fmaf(-al, ov[db][i], c[i]);
@@ -682,6 +731,7 @@ __global__ void __launch_bounds__(PM_THREADS) pe_effect_spans_mfma(PeArgs a, int
         }
         float w[16];
         pm_tile<D>(a, Kr, Vr, j0, qf, mmq, qpos, s_v[wave], w);
+        const PvWeights pw = pv_split(w);
         for (int p = i; p < i1; ++p) {
             const int lo = __builtin_amdgcn_readlane(my_first, p) - j0;
             const int hi = lo + __builtin_amdgcn_readlane(my_len, p);
@@ -692,13 +742,16 @@ __global__ void __launch_bounds__(PM_THREADS) pe_effect_spans_mfma(PeArgs a, int
                 al += (k >= lo && k < hi) ? w[j] : 0.f;
             }
             al += __shfl_xor(al, 32);
-            // key k is in MFMA step 4 * (k / 8) + k % 4 (lane half (k / 4) % 2)
-            const int j_lo = 4 * (lo >> 3), j_hi = hi > lo ? 4 * ((hi - 1) >> 3) + 4 : 0;
+            // the key blocks (tile keys 0..15, 16..31) the page touches, other keys' weights masked
+            const bool in0 = hi > lo && lo < 16, in1 = hi > lo && hi > 16;
+            const bf16x8 mh0 = pv_mask(pw.hi[0], 0, lo, hi), ml0 = pv_mask(pw.lo[0], 0, lo, hi);
+            const bf16x8 mh1 = pv_mask(pw.hi[1], 1, lo, hi), ml1 = pv_mask(pw.lo[1], 1, lo, hi);
             float n2 = 0.f;
 #pragma unroll 1
             for (int db = 0; db < NDB; ++db) {   // one accumulator live at a time
                 f32x16 c = {};
-                pm_pv_span<D>(s_v[wave], w, db, j_lo, j_hi, lo, hi, c);
+                if (in0) pv_block(pv_v<D>(s_v[wave], db, 0), mh0, ml0, c);
+                if (in1) pv_block(pv_v<D>(s_v[wave], db, 1), mh1, ml1, c);
 #pragma unroll
                 for (int r = 0; r < 16; r += 4) {
                     const float4 ov = *reinterpret_cast<const float4 *>(&s_o[col][db * 32 + acc_row(r, hf)]);
