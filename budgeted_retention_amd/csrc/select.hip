@@ -281,8 +281,15 @@ __global__ void __launch_bounds__(SEL_THREADS)
 //   D. each wave scans its contiguous bitmap words and expands the non-zero
 //      ones with 32 lanes per word: every "above" token and the first `need`
 //      "equal" tokens in index order, ascending.
+// Instances: CAP candidates, U float4 loads per thread per trip (two trips in
+// flight), WPE waves per SIMD the registers must allow. With budgets up to
+// 2048 and rows up to ~110,000 tokens the small instance's LDS (under 80 KB)
+// and registers (64) let two workgroups share a CU, so a call of a few more
+// rows than CUs runs in one round instead of two.
 static constexpr int SEL_CAND = 8192;
-static constexpr int SEL_U = 4;  // float4 loads per thread per trip (two trips in flight)
+static constexpr int SEL_CAND_SMALL = 5632;
+static constexpr size_t SEL_CAND_SMALL_LDS = 80 * 1024;   // per workgroup, static LDS included
+static constexpr size_t SEL_CAND_STATIC_LDS = 9472;        // the kernel's static LDS (9364 bytes), rounded up
 
 // ORs this lane's 4-bit nibble (tokens 4*lane .. 4*lane+3 of the wave's 256)
 // with those of its 8-lane group; lane 8g ends with the group's 32-bit word.
@@ -322,7 +329,8 @@ __device__ __forceinline__ void pick_bin(const uint32_t *hist, int nbins, uint32
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(SEL_THREADS)
+template <int CAP, int U, int WPE>
+__global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(WPE)))
     select_cand(const float *__restrict__ scores, const uint8_t *__restrict__ tags,
                 const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int64_t T, int L, int Hkv,
                 int n_groups, int layer_base, int n_layers_model, int n_tags, int tag_rows, int n_sink,
@@ -335,9 +343,9 @@ __global__ void __launch_bounds__(SEL_THREADS)
     __shared__ uint32_t s_tab[256];  // per tag: all ones = protected, else the bonus's float bits
     extern __shared__ uint32_t s_dyn[];
     const int Ti = (int)T, mwords = (Ti + 31) >> 5;
-    uint32_t *c_key = s_dyn;                    // [SEL_CAND]
-    uint32_t *c_idx = s_dyn + SEL_CAND;         // [SEL_CAND]
-    uint32_t *m_gt = s_dyn + 2 * SEL_CAND;      // [mwords] kept: above tau
+    uint32_t *c_key = s_dyn;                    // [CAP]
+    uint32_t *c_idx = s_dyn + CAP;         // [CAP]
+    uint32_t *m_gt = s_dyn + 2 * CAP;      // [mwords] kept: above tau
     uint32_t *m_eq = m_gt + mwords;             // [mwords] tie: equal to tau
 
     const int64_t r = blockIdx.x;
@@ -384,31 +392,31 @@ __global__ void __launch_bounds__(SEL_THREADS)
         }
     };
     const int stride = SEL_THREADS * SEL_VEC;  // tokens per block step
-    // Streams the row: fn(base[SEL_U], keys[SEL_U][4]) once per trip of SEL_U
+    // Streams the row: fn(base[U], keys[U][4]) once per trip of U
     // 4-token groups per thread (groups with base >= T are padding); the next trip's scores and tags are loaded
     // before this trip is processed (always issued, re-reading the last group
     // past the end, so the loads in flight per wait are the same on every path).
     // Every lane of a wave runs the same number of trips (fn may use wave-wide
     // operations).
-    const int trips = (Ti + SEL_U * stride - 1) / (SEL_U * stride);
+    const int trips = (Ti + U * stride - 1) / (U * stride);
     auto stream = [&](auto fn) {
-        float4 sa[SEL_U], sb[SEL_U];
-        uint32_t ta[SEL_U], tb[SEL_U];
-        auto fetch = [&](int it, float4 (&sv)[SEL_U], uint32_t (&tv)[SEL_U]) {
+        float4 sa[U], sb[U];
+        uint32_t ta[U], tb[U];
+        auto fetch = [&](int it, float4 (&sv)[U], uint32_t (&tv)[U]) {
 #pragma unroll
-            for (int u = 0; u < SEL_U; ++u) {
-                int b = it * SEL_U * stride + u * stride + tid * SEL_VEC;
+            for (int u = 0; u < U; ++u) {
+                int b = it * U * stride + u * stride + tid * SEL_VEC;
                 if (b >= Ti) b = Ti - SEL_VEC;
                 sv[u] = *reinterpret_cast<const float4 *>(sr + b);
                 tv[u] = tr ? *reinterpret_cast<const uint32_t *>(tr + b) : 0u;
             }
         };
-        auto consume = [&](int it, const float4 (&sv)[SEL_U], const uint32_t (&tv)[SEL_U]) {
-            int base[SEL_U];
+        auto consume = [&](int it, const float4 (&sv)[U], const uint32_t (&tv)[U]) {
+            int base[U];
 #pragma unroll
-            for (int u = 0; u < SEL_U; ++u) base[u] = it * SEL_U * stride + u * stride + tid * SEL_VEC;
-            uint32_t k[SEL_U][SEL_VEC];
-            keys_of(std::integral_constant<int, SEL_U>(), sv, tv, base, k);
+            for (int u = 0; u < U; ++u) base[u] = it * U * stride + u * stride + tid * SEL_VEC;
+            uint32_t k[U][SEL_VEC];
+            keys_of(std::integral_constant<int, U>(), sv, tv, base, k);
             fn(base, k);
         };
         fetch(0, sa, ta);
@@ -424,7 +432,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
     auto per_group = [&](auto fn) {
         return [=](const int *base, uint32_t (*k)[SEL_VEC]) {
 #pragma unroll
-            for (int u = 0; u < SEL_U; ++u) fn(base[u], base[u] < Ti, k[u]);
+            for (int u = 0; u < U; ++u) fn(base[u], base[u] < Ti, k[u]);
         };
     };
     // Appends a trip's flagged tokens (bit 4u+e of cmask) to the candidate
@@ -439,11 +447,11 @@ __global__ void __launch_bounds__(SEL_THREADS)
         slot0 = __builtin_amdgcn_readlane(slot0, 63);
         uint32_t slot = slot0 + incl - n;
 #pragma unroll
-        for (int u = 0; u < SEL_U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < SEL_VEC; ++e)
                 if ((cmask >> (SEL_VEC * u + e)) & 1u) {
-                    if (slot < SEL_CAND) {
+                    if (slot < CAP) {
                         c_key[slot] = k[u][e];
                         c_idx[slot] = (uint32_t)(base[u] + e);
                     }
@@ -498,22 +506,22 @@ __global__ void __launch_bounds__(SEL_THREADS)
         uint32_t d_lo = 0u;
         {
             const int lines = (Ti + 255) / 256;  // sampled lines start at 256*i
-            for (int g0 = 0; g0 < lines * 8; g0 += SEL_U * SEL_THREADS) {
-                float4 sv[SEL_U];
-                uint32_t tv[SEL_U];
-                int base[SEL_U];
+            for (int g0 = 0; g0 < lines * 8; g0 += U * SEL_THREADS) {
+                float4 sv[U];
+                uint32_t tv[U];
+                int base[U];
 #pragma unroll
-                for (int u = 0; u < SEL_U; ++u) {
+                for (int u = 0; u < U; ++u) {
                     const int g = g0 + u * SEL_THREADS + tid;
                     base[u] = (g >> 3) * 256 + (g & 7) * SEL_VEC;
                     const int b = base[u] < Ti ? base[u] : Ti - SEL_VEC;
                     sv[u] = *reinterpret_cast<const float4 *>(sr + b);
                     tv[u] = tr ? *reinterpret_cast<const uint32_t *>(tr + b) : 0u;
                 }
-                uint32_t k[SEL_U][SEL_VEC];
-                keys_of(std::integral_constant<int, SEL_U>(), sv, tv, base, k);
+                uint32_t k[U][SEL_VEC];
+                keys_of(std::integral_constant<int, U>(), sv, tv, base, k);
 #pragma unroll
-                for (int u = 0; u < SEL_U; ++u) {
+                for (int u = 0; u < U; ++u) {
                     if (base[u] >= Ti) continue;
                     uint32_t c0 = 1;
 #pragma unroll
@@ -536,7 +544,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
         stream([&](const int *base, uint32_t (*k)[SEL_VEC]) {
             uint32_t cmask = 0;
 #pragma unroll
-            for (int u = 0; u < SEL_U; ++u)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int e = 0; e < SEL_VEC; ++e) {
                     const uint32_t d = k[u][e] >> 21;
@@ -549,7 +557,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
         });
         __syncthreads();
         const uint32_t ncand = s_ncand;
-        fast = ncand >= (uint32_t)B && ncand <= (uint32_t)SEL_CAND;
+        fast = ncand >= (uint32_t)B && ncand <= (uint32_t)CAP;
         if (fast) {
             // R: every kept token is a candidate
             const bool all_protected = hist[SEL_BINS - 1] >= (uint32_t)B;
@@ -597,7 +605,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
             stream([&](const int *base, uint32_t (*k)[SEL_VEC]) {
                 uint32_t cmask = 0;
 #pragma unroll
-                for (int u = 0; u < SEL_U; ++u) {
+                for (int u = 0; u < U; ++u) {
                     const bool ok = base[u] < Ti;
                     uint32_t nib = 0;
                     if (ok) {
@@ -625,7 +633,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
                 tau = KEY_PROTECTED;
             } else {
                 const uint32_t nc = s_ncand;
-                const bool fits = nc <= (uint32_t)SEL_CAND;
+                const bool fits = nc <= (uint32_t)CAP;
                 low_digits(pick0, krank, fits, nc, tau, need);
                 if (fits) {
                     for (uint32_t c = tid; c < nc; c += SEL_THREADS) {
@@ -1869,17 +1877,25 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
                     kept_idx, kept_stride, n_kept, (T + SPLIT_CHUNK - 1) / SPLIT_CHUNK};
         if ((st = launch_select_split(a, n_rows(dims), ws, vec, s)) != KVC_OK) return st;
     } else if (vec && cand_lds <= 144 * 1024) {
-        static bool lds_set = false;
-        if (!lds_set) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(&select_cand),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 144 * 1024) != hipSuccess)
-                return fail(KVC_ERR_HIP, "kvc_select: cannot raise the LDS limit");
-            lds_set = true;
-        }
-        select_cand<<<grid, block, cand_lds, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
-                                                  dims->n_kv_heads, p->n_groups, p->layer_base, p->n_layers_model,
-                                                  p->n_tags, p->tag_rows, p->n_sink, p->n_recent, p->budget,
-                                                  kept_idx, kept_stride, n_kept);
+        const size_t small_lds = (size_t)2 * SEL_CAND_SMALL * sizeof(uint32_t) +
+                                 (size_t)2 * ((T + 31) / 32) * sizeof(uint32_t);
+        const bool small = p->budget <= 2048 && small_lds + SEL_CAND_STATIC_LDS <= SEL_CAND_SMALL_LDS;
+        auto launch = [&](auto kern, size_t lds) -> int {
+            static bool lds_set[2] = {false, false};
+            if (!lds_set[small]) {
+                if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, 144 * 1024) != hipSuccess)
+                    return fail(KVC_ERR_HIP, "kvc_select: cannot raise the LDS limit");
+                lds_set[small] = true;
+            }
+            kern<<<grid, block, lds, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
+                                          dims->n_kv_heads, p->n_groups, p->layer_base, p->n_layers_model,
+                                          p->n_tags, p->tag_rows, p->n_sink, p->n_recent, p->budget, kept_idx,
+                                          kept_stride, n_kept);
+            return KVC_OK;
+        };
+        st = small ? launch(select_cand<SEL_CAND_SMALL, 2, 8>, small_lds) : launch(select_cand<SEL_CAND, 4, 4>, cand_lds);
+        if (st != KVC_OK) return st;
     } else if (vec) {
         select_kernel<true><<<grid, block, 0, s>>>(scores, p->tags, p->tag_bonus, p->tag_floor, T, dims->n_layers,
                                                     dims->n_kv_heads, p->n_groups, p->layer_base,
