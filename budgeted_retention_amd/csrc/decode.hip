@@ -29,6 +29,8 @@ static constexpr int DEC_CHUNK = 256;
 static constexpr int DEC_THREADS = 256;
 static constexpr int DEC_MAX_G = 16;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 struct DecodeArgs {
     const uint16_t *q;
     const uint16_t *K, *V;
@@ -128,7 +130,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         return;
     }
     const uint16_t *qrow = a.q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * G) * D;
-    for (int i = tid; i < GM * D; i += DEC_THREADS) s_q[i / D][i % D] = i / D < G ? bf16_to_f32(qrow[i]) : 0.f;
+    if (LOW)
+        for (int i = tid; i < GM * D; i += DEC_THREADS) s_q[i / D][i % D] = i / D < G ? bf16_to_f32(qrow[i]) : 0.f;
 
     // Storage row of every key this thread touches (-1: none), then all loads.
     int32_t srow[ITER];   // storage slots fit int32: the caller checks the strides
@@ -159,39 +162,61 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         }
     }
     __syncthreads();  // s_q ready
-    float q[GM][8];
+    // bf16 keys: the query's bf16 pairs as stored (dot2 on packed bf16, fp32
+    // accumulation); dequantised keys: the query in fp32
+    float q[LOW ? GM : 1][8];
+    uint32_t qp[LOW ? 1 : GM][4];
+    if (LOW) {
 #pragma unroll
-    for (int g = 0; g < GM; ++g)
+        for (int g = 0; g < GM; ++g)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) q[g][c] = s_q[g][8 * sub + c];
+            for (int c = 0; c < 8; ++c) q[LOW ? g : 0][c] = s_q[g][8 * sub + c];
+    } else {
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (g < G) w = *reinterpret_cast<const uint4 *>(qrow + (size_t)g * D + 8 * sub);
+            qp[LOW ? 0 : g][0] = w.x;
+            qp[LOW ? 0 : g][1] = w.y;
+            qp[LOW ? 0 : g][2] = w.z;
+            qp[LOW ? 0 : g][3] = w.w;
+        }
+    }
 
     // Logits: partial dot products over this thread's 8 dimensions, summed
     // over the key's TPK threads (lanes kin*TPK .. kin*TPK + TPK-1 of the wave).
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-        float x[8];
+        float dot[GM];
         if (!low) {
             const uint32_t w[4] = {kv[it].x, kv[it].y, kv[it].z, kv[it].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xFFFF));
-                x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+            for (int g = 0; g < GM; ++g) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
+                                                          __builtin_bit_cast(bf16x2, qp[LOW ? 0 : g][e]), acc, false);
+                dot[g] = acc;
             }
-        } else if (LOWB == 4) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (float)((int32_t)(kv[it].x << (28 - 4 * e)) >> 28) * ks[LOW ? it : 0];
         } else {
-            const uint32_t w[2] = {kv[it].x, kv[it].y};
+            float x[8];
+            if (LOWB == 4) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFF) * ks[LOW ? it : 0];
-        }
-        float dot[GM];
+                for (int e = 0; e < 8; ++e) x[e] = (float)((int32_t)(kv[it].x << (28 - 4 * e)) >> 28) * ks[LOW ? it : 0];
+            } else {
+                const uint32_t w[2] = {kv[it].x, kv[it].y};
 #pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            float acc = 0.f;
+                for (int e = 0; e < 8; ++e)
+                    x[e] = (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xFF) * ks[LOW ? it : 0];
+            }
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc = fmaf(x[c], q[g][c], acc);
-            dot[g] = acc;
+            for (int g = 0; g < GM; ++g) {
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc = fmaf(x[c], q[LOW ? g : 0][c], acc);
+                dot[g] = acc;
+            }
         }
 #pragma unroll
         for (int g = 0; g < GM; ++g) dot[g] = group_sum<TPK>(dot[g]);

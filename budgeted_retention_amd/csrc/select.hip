@@ -289,7 +289,6 @@ __global__ void __launch_bounds__(SEL_THREADS)
 static constexpr int SEL_CAND = 8192;
 static constexpr int SEL_CAND_SMALL = 5632;
 static constexpr size_t SEL_CAND_SMALL_LDS = 80 * 1024;   // per workgroup, static LDS included
-static constexpr size_t SEL_CAND_STATIC_LDS = 9472;        // the kernel's static LDS (9364 bytes), rounded up
 
 // ORs this lane's 4-bit nibble (tokens 4*lane .. 4*lane+3 of the wave's 256)
 // with those of its 8-lane group; lane 8g ends with the group's 32-bit word.
@@ -1879,7 +1878,15 @@ extern "C" int kvc_select(const kvc_dims *dims, const float *scores, const kvc_p
     } else if (vec && cand_lds <= 144 * 1024) {
         const size_t small_lds = (size_t)2 * SEL_CAND_SMALL * sizeof(uint32_t) +
                                  (size_t)2 * ((T + 31) / 32) * sizeof(uint32_t);
-        const bool small = p->budget <= 2048 && small_lds + SEL_CAND_STATIC_LDS <= SEL_CAND_SMALL_LDS;
+        static size_t small_static = 0;   // the small instance's static LDS, asked once
+        if (!small_static) {
+            hipFuncAttributes fa;
+            if (hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(&select_cand<SEL_CAND_SMALL, 2, 8>)) !=
+                hipSuccess)
+                return fail(KVC_ERR_HIP, "kvc_select: cannot read the candidate kernel's attributes");
+            small_static = fa.sharedSizeBytes > 0 ? fa.sharedSizeBytes : 1;
+        }
+        const bool small = p->budget <= 2048 && small_lds + small_static <= SEL_CAND_SMALL_LDS;
         auto launch = [&](auto kern, size_t lds) -> int {
             static bool lds_set[2] = {false, false};
             if (!lds_set[small]) {
