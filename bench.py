@@ -527,7 +527,7 @@ def bench_pipeline(args, w, dev, kind):
         res = run(timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part = {k: v / args.steps for k, v in timer.totals_ms().items()}
+    part = timer.median_step_ms(args.steps)
     host = {k: round(v * 1e3 / args.steps, 3) for k, v in timer.host.items()}
     d, Hkv, G, W = w.head_dim, w.n_kv_heads, w.n_q_heads // w.n_kv_heads, w.window
     rows = w.rows
@@ -617,7 +617,9 @@ def bench_pipeline(args, w, dev, kind):
             config.update(pages=f"event pages: history events of 1..{w.event_max} tokens cut into pages of "
                                 f"at most {w.page_size}", n_pages=P,
                           kept_tokens_mean=round(float(res["n_tokens"].float().mean().item()), 1))
-    extra = {"breakdown_ms": {k: round(part[k], 4) for k in path_calls},
+    extra = {"timing": f"per call, the median over {args.steps} runs of its HIP-event time; ms_per_step "
+                       f"sums the path's calls",
+             "breakdown_ms": {k: round(part[k], 4) for k in path_calls},
              "other_ms": {k: round(v, 4) for k, v in part.items() if k not in path_calls},
              "host_ms": host, "calls": per_call_rates(ab, part),
              "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}
@@ -723,7 +725,7 @@ def bench_commit_multi(args, w, dev):
         pipelines.run_commit_multi(w, inp, timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part = {k: v / args.steps for k, v in timer.totals_ms().items()}
+    part = timer.median_step_ms(args.steps)
     host = {k: round(v * 1e3 / args.steps, 3) for k, v in timer.host.items()}
     C, N, L, Hkv, d, W, ps = w.commits, w.n_seq, w.n_layers, w.n_kv_heads, w.head_dim, w.window, w.page_size
     G = w.n_q_heads // Hkv
@@ -745,7 +747,9 @@ def bench_commit_multi(args, w, dev):
     config = {"workload": w.name, "n_seq": N, "layers": L, "kv_heads": Hkv, "q_heads": w.n_q_heads,
               "head_dim": d, "commits": C, "turn": w.n_call, "observation": w.n_obs, "window": W,
               "page": ps, "budget": B, "eta": w.eta, "decision_layer": w.layer, "parallelism": "none"}
-    extra = {"breakdown_ms": {k: round(part[k], 4) for k in path_calls},
+    extra = {"timing": f"per call, the median over {args.steps} runs of its HIP-event time; ms_per_step "
+                       f"sums the path's calls",
+             "breakdown_ms": {k: round(part[k], 4) for k in path_calls},
              "other_ms": {k: round(v, 4) for k, v in part.items() if k not in path_calls},
              "host_ms": host, "calls": per_call_rates(ab, part),
              "wall_ms_per_step": round(wall * 1e3 / args.steps, 4)}

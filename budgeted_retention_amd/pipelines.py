@@ -7,6 +7,7 @@ the current stream and every host step with the wall clock; the parity tests
 pass none. Argument marshalling only: every step runs in libkvc.
 """
 import contextlib
+import statistics
 import time
 
 import numpy as np
@@ -49,6 +50,26 @@ class CallTimer:
         for name, a, b in self.events:
             out[name] = out.get(name, 0.0) + a.elapsed_time(b)
         return out
+
+    def median_step_ms(self, steps):
+        """Per call name, the median over `steps` equal runs of that run's summed
+        milliseconds (the events split into `steps` groups of the same calls), so
+        that one run delayed on the host does not move the figures."""
+        torch.cuda.synchronize()
+        n = len(self.events)
+        if steps < 1 or n % steps:
+            raise ValueError(f"{n} timed calls do not split into {steps} equal runs")
+        per = n // steps
+        runs = []
+        for i in range(steps):
+            tot = {}
+            for name, a, b in self.events[i * per:(i + 1) * per]:
+                tot[name] = tot.get(name, 0.0) + a.elapsed_time(b)
+            runs.append(tot)
+        names = runs[0].keys()
+        if any(r.keys() != names for r in runs):
+            raise ValueError("the timed runs made different calls")
+        return {k: statistics.median(r[k] for r in runs) for k in names}
 
 
 def run_pask(w, inp, timer=None):

@@ -37,3 +37,28 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_pipeline_call_times_are_medians_over_the_runs(monkeypatch):
+    """One run delayed on the host (here the second call of the first run) does
+    not move a call's figure: each call takes the median over the runs."""
+    import torch
+    from budgeted_retention_amd import pipelines
+
+    class Ev:
+        def __init__(self, t):
+            self.t = t
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+    timer = pipelines.CallTimer()
+    runs = [{"score": 3.0, "select": 9.0}, {"score": 3.2, "select": 0.1}, {"score": 2.8, "select": 0.12}]
+    for r in runs:
+        for name in ("score", "select"):
+            timer.events.append((name, Ev(0.0), Ev(r[name])))
+    med = timer.median_step_ms(3)
+    assert med == {"score": 3.0, "select": 0.12}
+    with pytest.raises(ValueError):
+        timer.median_step_ms(4)
