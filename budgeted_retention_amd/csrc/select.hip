@@ -642,6 +642,9 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
                     }
                 } else {
                     stream(per_group([&](int base, bool ok, const uint32_t *k) {
+                        // an opaque base keeps the compiler from hoisting every
+                        // group's bitmap addresses out of the stream (registers)
+                        asm volatile("" : "+v"(base));
 #pragma unroll
                         for (int e = 0; e < SEL_VEC; ++e) {
                             const int j = base + e;
@@ -772,8 +775,11 @@ __device__ __forceinline__ uint32_t sw_key(int j, float score, float bt, int lo,
     return order_key(score + bt);
 }
 
+// Rows that are not float4-aligned load their keys one by one, which takes a
+// few more registers: their instances allow one wave fewer per SIMD rather
+// than spill (a kernel with scratch pays for it at every launch).
 template <int NPL4, bool VEC>
-__global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per_eu(NPL4 <= 16 ? 4 : 2)))
+__global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per_eu(NPL4 <= 16 ? (VEC ? 4 : 3) : 2)))
     select_wave(const float *__restrict__ scores, const uint8_t *__restrict__ tags,
                 const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int Ti, int64_t rows,
                 int L, int Hkv, int n_groups, int layer_base, int n_layers_model, int n_tags, int tag_rows,
