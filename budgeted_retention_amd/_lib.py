@@ -5,7 +5,8 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # KVC_LIBRARY selects another build of the same library (the AddressSanitizer
-# build, libkvc_asan.so, for host-side checks); by default the in-tree libkvc.so.
+# build, libkvc_asan.so, for host-side checks; the bounds-checked build,
+# libkvc_check.so); by default the in-tree libkvc.so.
 LIB_PATH = os.environ.get("KVC_LIBRARY") or os.path.join(_PKG, "libkvc.so")
 
 KVC_OK = 0
@@ -14,6 +15,18 @@ KVC_ERR_ARG = -1
 KVC_ERR_UNSUPPORTED = -2
 KVC_ERR_WORKSPACE = -3
 KVC_ERR_HIP = -4
+
+# kvc_check_read bits (bounds-checked builds)
+KVC_CHK_SCORE = 1 << 0
+KVC_CHK_SELECT = 1 << 1
+KVC_CHK_COMPACT = 1 << 2
+KVC_CHK_DECODE = 1 << 3
+KVC_CHK_POOL = 1 << 4
+KVC_CHK_PAGE = 1 << 5
+KVC_CHK_KEPT = 1 << 8
+KVC_CHK_COUNT = 1 << 9
+KVC_CHK_SPAN = 1 << 10
+KVC_CHK_BLOCK = 1 << 11
 
 KVC_OP_SCORE = 1
 KVC_OP_SELECT = 2
@@ -64,6 +77,7 @@ class KvcPaskTable(ctypes.Structure):
 PROTOTYPES = {
     "kvc_version": (ctypes.c_int, []),
     "kvc_last_error": (ctypes.c_char_p, []),
+    "kvc_check_read": (ctypes.c_int, [c_void_p, c_void_p]),
     "kvc_workspace_bytes": (c_size_t, [ctypes.c_int, ctypes.POINTER(KvcDims), c_int32, c_int32]),
     "kvc_layer_group": (c_int32, [c_int32, c_int32, c_int32]),
     "kvc_foresight_bonus": (c_double, [c_double, c_double, c_double]),

@@ -47,6 +47,11 @@ EXTRA_FLAGS = {
 ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
 ASAN_LIB_PATH = os.path.join(PKG, "libkvc_asan.so")
 
+# Bounds-checked kernels: every index wrapped in KVC_IDX is checked against its
+# range and caller data the kernels clamp is noted (kvc_check_read reports both).
+CHECK_FLAGS = ["-DKVC_CHECK"]
+CHECK_LIB_PATH = os.path.join(PKG, "libkvc_check.so")
+
 
 def _compile(src, obj, verbose, extra=()):
     cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
@@ -58,13 +63,16 @@ def _compile(src, obj, verbose, extra=()):
     return obj
 
 
-def build(verbose=False, jobs=8, asan=False):
+def build(verbose=False, jobs=8, asan=False, check=False):
     """Compile every csrc/*.hip and link libkvc.so; returns the library path.
     asan=True builds libkvc_asan.so instead, the host code under AddressSanitizer
-    (load it with the sanitizer runtime preloaded; see asan_runtime())."""
-    bdir = BUILD_DIR + ("_asan" if asan else "")
-    out = ASAN_LIB_PATH if asan else LIB_PATH
-    extra = ASAN_FLAGS if asan else []
+    (load it with the sanitizer runtime preloaded; see asan_runtime());
+    check=True builds libkvc_check.so, the kernels with their bounds checks."""
+    if asan and check:
+        raise ValueError("one variant per build")
+    bdir = BUILD_DIR + ("_asan" if asan else "_check" if check else "")
+    out = ASAN_LIB_PATH if asan else CHECK_LIB_PATH if check else LIB_PATH
+    extra = ASAN_FLAGS if asan else CHECK_FLAGS if check else []
     os.makedirs(bdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     objs = [os.path.join(bdir, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
@@ -116,5 +124,7 @@ if __name__ == "__main__":
     if "--asan" in sys.argv:
         print(build(verbose=True, asan=True))
         print(asan_runtime())
+    elif "--check" in sys.argv:
+        print(build(verbose=True, check=True))
     else:
         print(build(verbose=True))

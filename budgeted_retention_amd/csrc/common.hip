@@ -48,6 +48,14 @@ int check_dims(const kvc_dims *d, const char *who) {
 size_t score_workspace_bytes(const kvc_dims *d, int32_t W);
 size_t select_workspace_bytes(const kvc_dims *d, int32_t B);
 
+// The check words of the kernel sources (bounds-checked builds).
+unsigned check_read_score();
+unsigned check_read_select();
+unsigned check_read_compact();
+unsigned check_read_decode();
+unsigned check_read_pool();
+unsigned check_read_page();
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -55,6 +63,24 @@ using namespace kvc;
 extern "C" int kvc_version(void) { return 0 * 10000 + 1 * 100 + 0; }
 
 extern "C" const char *kvc_last_error(void) { return g_last_error; }
+
+extern "C" int kvc_check_read(void *stream, uint32_t *sites) {
+    if (!sites) return fail(KVC_ERR_ARG, "kvc_check_read: sites is NULL");
+    *sites = 0u;
+#ifdef KVC_CHECK
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return fail(KVC_ERR_HIP, "kvc_check_read: stream");
+    const unsigned words[] = {check_read_score(), check_read_select(), check_read_compact(),
+                              check_read_decode(), check_read_pool(), check_read_page()};
+    for (unsigned w : words) {
+        if (w == ~0u) return fail(KVC_ERR_HIP, "kvc_check_read: copy of a check word failed");
+        *sites |= w;
+    }
+    return KVC_OK;
+#else
+    (void)stream;
+    return fail(KVC_ERR_UNSUPPORTED, "kvc_check_read: the library was built without KVC_CHECK");
+#endif
+}
 
 extern "C" size_t kvc_workspace_bytes(int op, const kvc_dims *dims, int32_t W, int32_t B) {
     (void)B;

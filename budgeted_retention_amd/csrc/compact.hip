@@ -198,12 +198,14 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
     const int kp = a.kept_page;
     const int64_t kr = kp ? r / a.rows_per_seq : r;  // row of the kept list
     int n = a.n_kept[kr];
+    KVC_NOTE(n > a.kept_stride, KVC_CHK_COUNT);
     if (n > a.kept_stride) n = a.kept_stride;
     if (n < 0) n = 0;
     if (kp) n *= kp;
     int base = a.h_base ? a.h_base[r] : 0;
     if (base < 0) base = 0;
     const int room = a.out_stride - base > 0 ? a.out_stride - base : 0;
+    KVC_NOTE(n > room, KVC_CHK_COUNT);
     if (n > room) n = room;
     if (cb == 0 && threadIdx.x == 0 && a.nh) a.nh[r] = base + n;
     const int sub = threadIdx.x % TPT, tin = threadIdx.x / TPT;
@@ -234,6 +236,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
             j = e < 0 ? -1 : e * kp + rho % kp;
         } else {
             j = a.kept[(size_t)kr * a.kept_stride + rho];
+            KVC_NOTE(j >= a.T, KVC_CHK_KEPT);
         }
         return j < a.T ? j : -1;
     };
@@ -241,7 +244,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
     auto fetch = [&](int64_t j) -> Tok {
         Tok t;
         t.j = j;
-        const int64_t jj = j < 0 ? 0 : j;
+        const int64_t jj = KVC_IDX(j < 0 ? 0 : j, a.T, KVC_CHK_COMPACT);
         const size_t src = ((size_t)r * a.T + jj) * D;
         t.lo = *reinterpret_cast<const uint2 *>(a.K + src + 4 * sub);
         t.hi = *reinterpret_cast<const uint2 *>(a.K + src + D / 2 + 4 * sub);
@@ -262,7 +265,8 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
     auto put = [&](Tok &t, int u) {
         if (t.j < 0) return;  // the same for the token's TPT threads
         const int rho = rho0 + u * TOK;
-        const size_t dst = ((size_t)r * a.out_stride + base + rho) * D;
+        const int slot = KVC_IDX(base + rho, a.out_stride, KVC_CHK_COMPACT);
+        const size_t dst = ((size_t)r * a.out_stride + slot) * D;
         int64_t psrc = t.p;
         if (REF) {
             // the check before use; the token's TPT adjacent lanes agree on it
@@ -284,7 +288,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
             }
             *reinterpret_cast<uint2 *>(a.Kref_out + dst + 4 * sub) = t.rlo;
             *reinterpret_cast<uint2 *>(a.Kref_out + dst + D / 2 + 4 * sub) = t.rhi;
-            if (sub == 0) a.pref_out[(size_t)r * a.out_stride + base + rho] = (int32_t)psrc;
+            if (sub == 0) a.pref_out[(size_t)r * a.out_stride + slot] = (int32_t)psrc;
         }
         int64_t pn = t.p;
         if (rot) {
@@ -298,9 +302,9 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_plain(CompactArgs a, int 
         *reinterpret_cast<uint2 *>(a.Ko + dst + 4 * sub) = t.lo;
         *reinterpret_cast<uint2 *>(a.Ko + dst + D / 2 + 4 * sub) = t.hi;
         *reinterpret_cast<uint4 *>(a.Vo + dst + 8 * sub) = t.v;
-        if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + base + rho] = (int32_t)pn;
-        if (sub == 0 && a.score_out) a.score_out[(size_t)r * a.out_stride + base + rho] = t.sc;
-        if (sub == 0 && a.tag_out) a.tag_out[(size_t)r * a.out_stride + base + rho] = (uint8_t)t.tg;
+        if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + slot] = (int32_t)pn;
+        if (sub == 0 && a.score_out) a.score_out[(size_t)r * a.out_stride + slot] = t.sc;
+        if (sub == 0 && a.tag_out) a.tag_out[(size_t)r * a.out_stride + slot] = (uint8_t)t.tg;
     };
     static_assert(U == 4, "the token batch below is written out for four tokens");
     const int64_t j0 = index(0), j1 = index(1), j2 = index(2), j3 = index(3);
@@ -323,6 +327,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int n = a.n_kept[r];
+    KVC_NOTE(n > a.kept_stride, KVC_CHK_COUNT);
     if (n > a.kept_stride) n = a.kept_stride;
     if (n < 0) n = 0;
     const int sub = tid % TPT, tin = tid / TPT;
@@ -363,8 +368,10 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
         int slot = -1;
         if (act == 2) slot = carry_h + (int)(ex & 0xFFFFu);
         if (act == 1) slot = carry_l + (int)(ex >> 16);
+        KVC_NOTE(slot >= a.out_stride, KVC_CHK_COUNT);
         if (slot >= a.out_stride) slot = -1;
         s_j[tid] = rho < n ? a.kept[(size_t)r * a.kept_stride + rho] : -1;
+        KVC_NOTE(s_j[tid] >= a.T, KVC_CHK_KEPT);
         s_slot[tid] = slot;
         s_tier[tid] = (uint8_t)act;
         __syncthreads();
@@ -374,8 +381,9 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
             const int tier = s_tier[e];
             // Uniform across the TPT-thread group: all of it reads the same entry.
             if (sl < 0 || j < 0 || j >= a.T || (tier != 1 && tier != 2)) continue;
+            const int slc = KVC_IDX(sl, a.out_stride, KVC_CHK_COMPACT);
             const int rho_e = base + e;
-            const size_t src = ((size_t)r * a.T + j) * D;
+            const size_t src = ((size_t)r * a.T + KVC_IDX(j, a.T, KVC_CHK_COMPACT)) * D;
             uint32_t lo = *reinterpret_cast<const uint32_t *>(a.K + src + 2 * sub);
             uint32_t hi = *reinterpret_cast<const uint32_t *>(a.K + src + D / 2 + 2 * sub);
             const uint2 vv = *reinterpret_cast<const uint2 *>(a.V + src + 4 * sub);
@@ -385,12 +393,12 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
                 pn = (int64_t)a.renumber_base + rho_e;
                 rotate_pairs(lo, hi, (double)(pn - p), th0, th1);
             }
-            const size_t dst = ((size_t)r * a.out_stride + sl) * D;
+            const size_t dst = ((size_t)r * a.out_stride + slc) * D;
             if (tier == 2) {
                 *reinterpret_cast<uint32_t *>(a.Ko + dst + 2 * sub) = lo;
                 *reinterpret_cast<uint32_t *>(a.Ko + dst + D / 2 + 2 * sub) = hi;
                 *reinterpret_cast<uint2 *>(a.Vo + dst + 4 * sub) = vv;
-                if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + sl] = (int32_t)pn;
+                if (sub == 0 && a.po) a.po[(size_t)r * a.out_stride + slc] = (int32_t)pn;
             } else {
                 const float k0 = bf16_to_f32((uint16_t)(lo & 0xFFFF)), k1 = bf16_to_f32((uint16_t)(lo >> 16));
                 const float k2 = bf16_to_f32((uint16_t)(hi & 0xFFFF)), k3 = bf16_to_f32((uint16_t)(hi >> 16));
@@ -409,7 +417,7 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
                 if (q4) {
                     // dimensions 2sub, 2sub+1 -> byte sub; D/2+2sub, +1 -> byte D/4+sub;
                     // values 4sub..4sub+3 -> bytes 2sub, 2sub+1
-                    const size_t dq = ((size_t)r * a.out_stride + sl) * (D / 2);
+                    const size_t dq = ((size_t)r * a.out_stride + slc) * (D / 2);
                     uint8_t *kq = reinterpret_cast<uint8_t *>(a.Kq) + dq;
                     uint8_t *vq = reinterpret_cast<uint8_t *>(a.Vq) + dq;
                     kq[sub] = (uint8_t)nibble_pair(c0, c1);
@@ -427,9 +435,9 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
                                                                  ((uint32_t)(uint8_t)w3 << 24);
                 }
                 if (sub == 0) {
-                    a.Ks[(size_t)r * a.out_stride + sl] = ksb;
-                    a.Vs[(size_t)r * a.out_stride + sl] = vsb;
-                    if (a.pq) a.pq[(size_t)r * a.out_stride + sl] = (int32_t)pn;
+                    a.Ks[(size_t)r * a.out_stride + slc] = ksb;
+                    a.Vs[(size_t)r * a.out_stride + slc] = vsb;
+                    if (a.pq) a.pq[(size_t)r * a.out_stride + slc] = (int32_t)pn;
                 }
             }
         }
@@ -442,6 +450,8 @@ __global__ void __launch_bounds__(CMP_THREADS) compact_tiered(CompactArgs a) {
         if (a.nl) a.nl[r] = carry_l < a.out_stride ? carry_l : a.out_stride;
     }
 }
+
+KVC_CHECK_READER(check_read_compact)
 
 }  // namespace kvc
 

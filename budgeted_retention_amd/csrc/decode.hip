@@ -80,6 +80,7 @@ __device__ __forceinline__ int64_t bf16_slot(const DecodeArgs &a, int n, int t) 
     if (!a.block_table) return t;
     const int blk = a.block_table[(size_t)n * a.blocks_per_seq + t / a.page_size];
     const int64_t s = (int64_t)blk * a.page_size + t % a.page_size;
+    KVC_NOTE(blk < 0 || s >= a.stride_h, KVC_CHK_BLOCK);
     return (blk < 0 || s >= a.stride_h) ? -1 : s;
 }
 
@@ -122,6 +123,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
     int64_t n = low ? (a.n_l ? a.n_l[r] : 0) : a.n_h[r];
     const int64_t cap = low ? a.stride_l
                             : (a.block_table ? (int64_t)a.blocks_per_seq * a.page_size : a.stride_h);
+    KVC_NOTE(n > cap, KVC_CHK_COUNT);
     if (n > cap) n = cap;
     const int64_t k0 = (int64_t)chunk * DEC_CHUNK;
     const int cnt = n - k0 < DEC_CHUNK ? (int)(n - k0) : DEC_CHUNK;
@@ -140,6 +142,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
         const int e = it * KPI + kin;
         int64_t sl = -1;
         if (e < cnt) sl = low ? k0 + e : bf16_slot(a, ri.n, (int)(k0 + e));
+        if (sl >= 0) sl = KVC_IDX(sl, low ? a.stride_l : a.stride_h, KVC_CHK_DECODE);
         srow[it] = (int32_t)sl;
     }
     uint4 kv[ITER];   // bf16: 8 values; int8: codes in .x/.y
@@ -392,6 +395,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_mass(DecodeArgs a, float *
         m += __builtin_amdgcn_exp2f(a.logit[((size_t)r * a.G + g) * lstride + t] - a.lse2[(size_t)r * a.G + g]);
     acc[(size_t)r * a.stride_h + t] += m;
 }
+
+KVC_CHECK_READER(check_read_decode)
 
 size_t decode_workspace_bytes(const kvc_dims *d, int64_t stride_h, int64_t stride_l) {
     const int G = d->n_q_heads / d->n_kv_heads;

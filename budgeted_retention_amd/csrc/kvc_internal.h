@@ -26,6 +26,59 @@ inline int64_t n_rows(const kvc_dims *d) {
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// ---------------------------------------------------------------- bounds-checked builds
+//
+// Built with -DKVC_CHECK, an index wrapped in KVC_IDX(i, n, site) is checked
+// against [0, n): one outside records `site` in this source file's device
+// check word and is replaced by 0, an index that exists, so the access is
+// reported instead of made. KVC_NOTE(cond, site) records caller data that the
+// kernels clamp (kept indices past the cache, counts above their buffers, page
+// spans, block-table entries). Normal builds compile both away: KVC_IDX(i, n,
+// site) is i. kvc_check_read collects the words of every source and clears them.
+enum : unsigned {
+    KVC_CHK_SCORE = 1u << 0,     // score: key, query and score indices
+    KVC_CHK_SELECT = 1u << 1,    // select: token, candidate and output indices
+    KVC_CHK_COMPACT = 1u << 2,   // compaction: source tokens and destination slots
+    KVC_CHK_DECODE = 1u << 3,    // decode: pool slots and partial slots
+    KVC_CHK_POOL = 1u << 4,      // score pooling: tokens
+    KVC_CHK_PAGE = 1u << 5,      // page effects and page scores: tokens and pages
+    KVC_CHK_KEPT = 1u << 8,      // caller data: a kept index at or past the cache
+    KVC_CHK_COUNT = 1u << 9,     // caller data: a count above its buffer
+    KVC_CHK_SPAN = 1u << 10,     // caller data: a page span outside the cache or above the page size
+    KVC_CHK_BLOCK = 1u << 11,    // caller data: a block-table entry outside the storage
+};
+
+#ifdef KVC_CHECK
+static __device__ unsigned kvc_check_word;   // this source file's copy
+
+template <class I>
+__device__ __forceinline__ I kvc_idx(I i, int64_t n, unsigned site) {
+    if ((int64_t)i >= 0 && (int64_t)i < n) return i;
+    atomicOr(&kvc_check_word, site);
+    return I(0);
+}
+#define KVC_IDX(i, n, site) ::kvc::kvc_idx((i), (int64_t)(n), (site))
+#define KVC_NOTE(cond, site)                                          \
+    do {                                                              \
+        if (cond) atomicOr(&::kvc::kvc_check_word, (unsigned)(site)); \
+    } while (0)
+// Host: this source file's check word, read and cleared.
+#define KVC_CHECK_READER(fn)                                                                        \
+    unsigned fn() {                                                                                 \
+        unsigned v = 0u, z = 0u;                                                                    \
+        if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(kvc_check_word), sizeof v) != hipSuccess) return ~0u; \
+        if (hipMemcpyToSymbol(HIP_SYMBOL(kvc_check_word), &z, sizeof z) != hipSuccess) return ~0u;   \
+        return v;                                                                                   \
+    }
+#else
+#define KVC_IDX(i, n, site) (i)
+#define KVC_NOTE(cond, site) \
+    do {                     \
+    } while (0)
+#define KVC_CHECK_READER(fn) \
+    unsigned fn() { return 0u; }
+#endif
+
 // ---------------------------------------------------------------- device side
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -118,6 +118,7 @@ __device__ __forceinline__ void page_span(const PeArgs &a, int n, int e, int64_t
     if (a.pfirst) {
         int64_t f = a.pfirst[(size_t)n * a.n_pages + e];
         int64_t l = a.plen[(size_t)n * a.n_pages + e];
+        KVC_NOTE(f < 0 || l < 0 || l > a.page_size || f + l > a.T, KVC_CHK_SPAN);
         f = f < 0 ? 0 : (f > a.T ? a.T : f);
         l = l < 0 ? 0 : (l > a.page_size ? a.page_size : l);
         if (l > a.T - f) l = a.T - f;
@@ -1126,6 +1127,8 @@ static int pe_prepare(const kvc_dims *dims, const PeArgs &a, const PageWs &w, hi
     return check_launch("page effect outputs (sum)");
 }
 
+KVC_CHECK_READER(check_read_page)
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -1206,6 +1209,7 @@ page_score_spans(const float *scores, int64_t T, int64_t rows_per_seq, int page_
         if (tid < np) {
             f = pfirst[(int64_t)n * n_pages + p0 + tid];
             l = plen[(int64_t)n * n_pages + p0 + tid];
+            KVC_NOTE(f < 0 || l < 0 || l > page_size || f + l > T, KVC_CHK_SPAN);
             f = f < 0 ? 0 : (f > T ? T : f);
             l = l < 0 ? 0 : (l > page_size ? page_size : l);
             if (l > T - f) l = T - f;
@@ -1280,6 +1284,7 @@ page_tokens_kernel(int64_t T, int page_size, int n_pages, const int32_t *pfirst,
     __shared__ int s_wave[PT_THREADS / 64];
     const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int listed = n_listed[n];
+    KVC_NOTE(listed > list_stride, KVC_CHK_COUNT);
     listed = listed < 0 ? 0 : (listed > list_stride ? list_stride : listed);
     int64_t total = 0;
     int32_t *out = tokens + (int64_t)n * out_stride;
@@ -1292,6 +1297,7 @@ page_tokens_kernel(int64_t T, int page_size, int n_pages, const int32_t *pfirst,
             if (e >= 0 && e < n_pages) {
                 if (pfirst) {
                     int64_t ff = pfirst[(int64_t)n * n_pages + e], ll = plen[(int64_t)n * n_pages + e];
+                    KVC_NOTE(ff < 0 || ll < 0 || ll > page_size || ff + ll > T, KVC_CHK_SPAN);
                     ff = ff < 0 ? 0 : (ff > T ? T : ff);
                     ll = ll < 0 ? 0 : (ll > page_size ? page_size : ll);
                     if (ll > T - ff) ll = T - ff;
@@ -1318,7 +1324,7 @@ page_tokens_kernel(int64_t T, int page_size, int n_pages, const int32_t *pfirst,
         __syncthreads();
         const int64_t pos0 = total + before + incl - len;
         for (int k = 0; k < len; ++k)
-            if (pos0 + k < out_stride) out[pos0 + k] = (int32_t)(f + k);
+            if (pos0 + k < out_stride) out[KVC_IDX(pos0 + k, out_stride, KVC_CHK_PAGE)] = (int32_t)(f + k);
         total += run;
     }
     if (tid == 0) n_tokens[n] = (int32_t)(total < INT32_MAX ? total : INT32_MAX);

@@ -43,9 +43,11 @@ __global__ void __launch_bounds__(POOL_THREADS)
             for (int q = lo; q <= hi; ++q) v += s[q];
             v = __fdiv_rn(v, (float)(hi - lo + 1));
         }
-        out[(size_t)r * T + j] = v;
+        out[(size_t)r * T + KVC_IDX(j, T, KVC_CHK_POOL)] = v;
     }
 }
+
+KVC_CHECK_READER(check_read_pool)
 
 }  // namespace kvc
 

@@ -98,6 +98,7 @@ __device__ __forceinline__ void load_tile_clamped(const uint16_t *Kr, int64_t j0
     constexpr int D = S * 16;
     int64_t key = j0 + (lane & 31);
     if (key >= kend) key = kend - 1;
+    key = KVC_IDX(key, kend, KVC_CHK_SCORE);
     const uint16_t *p = Kr + (size_t)key * D + 8 * (lane >> 5);
 #pragma unroll
     for (int s = 0; s < S; ++s) kf[s] = load8(p + 16 * s);
@@ -343,7 +344,7 @@ __device__ __forceinline__ void p2_tile(const bf16x8 (&kf)[D / 16], int64_t j0, 
         }
     }
     p = xor32_sum(p);  // + the other half-wave's query rows (all lanes active here)
-    if (hf == 0 && key < kend) out[key] = p;
+    if (hf == 0 && key < kend) out[KVC_IDX(key, kend, KVC_CHK_SCORE)] = p;
 }
 
 // Pass 2 over keys [k0, k1): each wave walks its tiles (wave, wave+4, ...)
@@ -499,6 +500,8 @@ int launch_window_stats(const kvc_dims *d, const uint16_t *K, const uint16_t *Q,
 }  // namespace kvc
 
 namespace kvc {
+
+KVC_CHECK_READER(check_read_score)
 
 // Argument checks shared by both score entry points; on success `need` holds
 // the workspace bytes the call uses.

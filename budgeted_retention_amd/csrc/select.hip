@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(SEL_THREADS)
             const bool eq = valid[e] && kk[e] == tau;
             if (gt || (eq && eq_before < need)) {
                 const int64_t pos = gt_before + (eq_before < need ? eq_before : need);
-                if (pos < kept_stride) kr[pos] = (int32_t)(base + e);
+                if (pos < kept_stride) kr[KVC_IDX(pos, kept_stride, KVC_CHK_SELECT)] = (int32_t)(base + e);
             }
             gt_before += gt;
             eq_before += eq;
@@ -406,6 +406,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
             for (int u = 0; u < U; ++u) {
                 int b = it * U * stride + u * stride + tid * SEL_VEC;
                 if (b >= Ti) b = Ti - SEL_VEC;
+                b = KVC_IDX(b, Ti - SEL_VEC + 1, KVC_CHK_SELECT);
                 sv[u] = *reinterpret_cast<const float4 *>(sr + b);
                 tv[u] = tr ? *reinterpret_cast<const uint32_t *>(tr + b) : 0u;
             }
@@ -513,7 +514,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
                 for (int u = 0; u < U; ++u) {
                     const int g = g0 + u * SEL_THREADS + tid;
                     base[u] = (g >> 3) * 256 + (g & 7) * SEL_VEC;
-                    const int b = base[u] < Ti ? base[u] : Ti - SEL_VEC;
+                    const int b = KVC_IDX(base[u] < Ti ? base[u] : Ti - SEL_VEC, Ti - SEL_VEC + 1, KVC_CHK_SELECT);
                     sv[u] = *reinterpret_cast<const float4 *>(sr + b);
                     tv[u] = tr ? *reinterpret_cast<const uint32_t *>(tr + b) : 0u;
                 }
@@ -706,10 +707,10 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
                 const int gpos = GB + __popc(G & below), erank = EB + __popc(E & below);
                 if (G & bit) {
                     const int pos = gpos + (erank < need ? erank : need);
-                    if (pos < kept_stride) kr[pos] = 32 * W + lane;
+                    if (pos < kept_stride) kr[KVC_IDX(pos, kept_stride, KVC_CHK_SELECT)] = 32 * W + lane;
                 } else if ((E & bit) && erank < need) {
                     const int pos = gpos + erank;
-                    if (pos < kept_stride) kr[pos] = 32 * W + lane;
+                    if (pos < kept_stride) kr[KVC_IDX(pos, kept_stride, KVC_CHK_SELECT)] = 32 * W + lane;
                 }
             }
         }
@@ -779,7 +780,7 @@ __device__ __forceinline__ uint32_t sw_key(int j, float score, float bt, int lo,
 // few more registers: their instances allow one wave fewer per SIMD rather
 // than spill (a kernel with scratch pays for it at every launch).
 template <int NPL4, bool VEC>
-__global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per_eu(NPL4 <= 16 ? (VEC ? 4 : 3) : 2)))
+__global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per_eu(NPL4 <= 16 ? (VEC ? 4 : 3) : (VEC ? 2 : 1))))
     select_wave(const float *__restrict__ scores, const uint8_t *__restrict__ tags,
                 const float *__restrict__ bonus, const uint8_t *__restrict__ floor_tbl, int Ti, int64_t rows,
                 int L, int Hkv, int n_groups, int layer_base, int n_layers_model, int n_tags, int tag_rows,
@@ -1447,7 +1448,7 @@ __global__ void __launch_bounds__(CR_THREADS) cand_resolve(CandArgs a) {
             const bool gt = v && kk > tau, eq = v && kk == tau;
             if (gt || (eq && eq_before < need)) {
                 const int pos = gt_before + (eq_before < need ? eq_before : need);
-                if (pos < a.kept_stride) out[pos] = c_idx[pb + e];
+                if (pos < a.kept_stride) out[KVC_IDX(pos, a.kept_stride, KVC_CHK_SELECT)] = c_idx[pb + e];
             }
             gt_before += gt ? 1 : 0;
             eq_before += eq ? 1 : 0;
@@ -1457,6 +1458,8 @@ __global__ void __launch_bounds__(CR_THREADS) cand_resolve(CandArgs a) {
     }
     if (tid == 0) a.n_kept[r] = (int32_t)(gt_run + (eq_run < (uint32_t)need ? eq_run : (uint32_t)need));
 }
+
+KVC_CHECK_READER(check_read_select)
 
 static bool select_use_split(const kvc_dims *d) {
     const int64_t T = d->n_tokens, rows = n_rows(d);
@@ -1771,7 +1774,7 @@ __global__ void __launch_bounds__(SEL_THREADS) split_write(SplitArgs a, SplitWs 
                 // slot0 already counts the ties taken before the chunk
                 const int64_t taken = (eq_before < need ? eq_before : need) - (eq0 < need ? eq0 : need);
                 const int64_t pos = slot0 + gt_before + taken;
-                if (pos < a.kept_stride) kr[pos] = (int32_t)(base + e);
+                if (pos < a.kept_stride) kr[KVC_IDX(pos, a.kept_stride, KVC_CHK_SELECT)] = (int32_t)(base + e);
             }
             gt_before += gt;
             eq_before += eq;

@@ -53,6 +53,15 @@ def kvc_version():
     return _lib.load().kvc_version()
 
 
+def kvc_check_read(stream=None):
+    """Bounds-checked builds: the kvc_check_read bits reported since the last
+    read (0 when none), after synchronising the stream; raises KvcError
+    (KVC_ERR_UNSUPPORTED) in other builds."""
+    sites = ctypes.c_uint32(0)
+    _lib.check(_lib.load().kvc_check_read(_stream(stream), ctypes.byref(sites)))
+    return sites.value
+
+
 def kvc_layer_group(layer, n_layers, n_groups):
     return _lib.load().kvc_layer_group(layer, n_layers, n_groups)
 

@@ -62,6 +62,23 @@ int kvc_version(void);
 /* Thread-local text for the last non-OK status returned on this thread. */
 const char *kvc_last_error(void);
 
+/*
+ * Bounds-checked builds (the library compiled with -DKVC_CHECK, built as
+ * libkvc_check.so beside libkvc.so; kernels otherwise the same). The global
+ * indices the kernels compute from data (key and token indices of the gathers,
+ * kept slots and output positions of the scatters, pool slots) are checked
+ * against their ranges, and caller data the kernels clamp (kept indices at or
+ * past the cache, counts above their buffers, page spans, block-table
+ * entries) is noted; an index out of range is reported and replaced by one in
+ * range instead of being used.
+ * kvc_check_read synchronises `stream`, stores in *sites the bits of every
+ * kind of access reported since the last read (0: none; bits 0-5: score,
+ * select, compaction, decode, pooling, page kernels; bits 8-11: kept index,
+ * count, page span, block-table entry) and clears them. In other builds it
+ * returns KVC_ERR_UNSUPPORTED and stores 0.
+ */
+int kvc_check_read(void *stream, uint32_t *sites);
+
 /* Operation ids for kvc_workspace_bytes(). */
 enum { KVC_OP_SCORE = 1, KVC_OP_SELECT = 2 };
 
@@ -313,7 +330,8 @@ typedef struct kvc_compact_out {
  *             [N] page counts shared by the sequence's rows: rank rho is token
  *             kept_idx[n][rho / p] * p + rho % p
  *   Entries beyond min(n_kept, kept_stride) or past out_stride are ignored;
- *   indices outside [0, T) are skipped. n_h / n_l report base + rows written.
+ *   an index outside [0, T) is skipped and leaves its slot as it was. n_h /
+ *   n_l report base + the entries taken (skipped ones included).
  */
 int kvc_compact_rerotate(const kvc_dims *dims, const uint16_t *K, const uint16_t *V,
                          const int32_t *pos_in, const int32_t *kept_idx, int32_t kept_stride,
