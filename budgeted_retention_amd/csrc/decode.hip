@@ -120,18 +120,32 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
     const int sub = tid % TPK, kin = tid / TPK;  // dimension group, key within a pass
     float *out = a.part + ((size_t)r * slots + slot) * G * (D + 2);
 
+    const int64_t k0 = (int64_t)chunk * DEC_CHUNK;
+    const uint16_t *qrow = a.q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * G) * D;
+    // bf16 keys: the query's bf16 pairs as stored (dot2 on packed bf16, fp32
+    // accumulation), loaded before the row's count arrives. Heads past G
+    // repeat head G-1; nothing of theirs is written.
+    uint32_t qp[LOW ? 1 : GM][4];
+    if (!LOW) {
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(qrow + (size_t)(g < G ? g : G - 1) * D + 8 * sub);
+            qp[LOW ? 0 : g][0] = w.x;
+            qp[LOW ? 0 : g][1] = w.y;
+            qp[LOW ? 0 : g][2] = w.z;
+            qp[LOW ? 0 : g][3] = w.w;
+        }
+    }
     int64_t n = low ? (a.n_l ? a.n_l[r] : 0) : a.n_h[r];
     const int64_t cap = low ? a.stride_l
                             : (a.block_table ? (int64_t)a.blocks_per_seq * a.page_size : a.stride_h);
     KVC_NOTE(n > cap, KVC_CHK_COUNT);
     if (n > cap) n = cap;
-    const int64_t k0 = (int64_t)chunk * DEC_CHUNK;
     const int cnt = n - k0 < DEC_CHUNK ? (int)(n - k0) : DEC_CHUNK;
     if (cnt <= 0) {  // empty chunk: contributes nothing
         for (int i = tid; i < G * (D + 2); i += DEC_THREADS) out[i] = (i % (D + 2)) == 0 ? -INFINITY : 0.f;
         return;
     }
-    const uint16_t *qrow = a.q + ((size_t)(ri.n * a.L + ri.l) * a.Hq + (size_t)ri.h * G) * D;
     if (LOW)
         for (int i = tid; i < GM * D; i += DEC_THREADS) s_q[i / D][i % D] = i / D < G ? bf16_to_f32(qrow[i]) : 0.f;
 
@@ -164,26 +178,14 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_partial(DecodeArgs a) {
             ks[LOW ? it : 0] = half_bits_to_f32(a.Ks[(size_t)r * a.stride_l + srow[it]]);
         }
     }
-    __syncthreads();  // s_q ready
-    // bf16 keys: the query's bf16 pairs as stored (dot2 on packed bf16, fp32
-    // accumulation); dequantised keys: the query in fp32
+    if (LOW) __syncthreads();  // s_q ready
+    // dequantised keys: the query in fp32
     float q[LOW ? GM : 1][8];
-    uint32_t qp[LOW ? 1 : GM][4];
     if (LOW) {
 #pragma unroll
         for (int g = 0; g < GM; ++g)
 #pragma unroll
             for (int c = 0; c < 8; ++c) q[LOW ? g : 0][c] = s_q[g][8 * sub + c];
-    } else {
-#pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (g < G) w = *reinterpret_cast<const uint4 *>(qrow + (size_t)g * D + 8 * sub);
-            qp[LOW ? 0 : g][0] = w.x;
-            qp[LOW ? 0 : g][1] = w.y;
-            qp[LOW ? 0 : g][2] = w.z;
-            qp[LOW ? 0 : g][3] = w.w;
-        }
     }
 
     // Logits: partial dot products over this thread's 8 dimensions, summed

@@ -101,12 +101,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 struct RowIdx {
     int n, l, h;
 };
+// Row indices fit 32 bits (the argument checks cap the row count at
+// INT32_MAX), so the divisions are 32-bit ones.
 __device__ __forceinline__ RowIdx split_row(int64_t r, int L, int Hkv) {
     RowIdx o;
-    o.h = (int)(r % Hkv);
-    int64_t nl = r / Hkv;
-    o.l = (int)(nl % L);
-    o.n = (int)(nl / L);
+    const uint32_t rr = (uint32_t)r, nl = rr / (uint32_t)Hkv;
+    o.h = (int)(rr - nl * (uint32_t)Hkv);
+    o.l = (int)(nl % (uint32_t)L);
+    o.n = (int)(nl / (uint32_t)L);
     return o;
 }
 
