@@ -136,12 +136,13 @@ def run_metadata(dev):
     and the GPU's current and maximum shader clock."""
     import subprocess
     import torch
-    meta = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
-    try:
-        meta["git"] = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True,
-                                     text=True, timeout=10).stdout.strip() or None
-    except Exception:
-        meta["git"] = None
+    meta = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "git": None}
+    if os.path.isdir(os.path.join(ROOT, ".git")):
+        try:
+            meta["git"] = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True,
+                                         text=True, timeout=10).stdout.strip() or None
+        except Exception:
+            pass
     if meta["git"] is None:   # a tree without its history: the commit the library was built from
         try:
             info = json.load(open(os.path.join(ROOT, "budgeted_retention_amd", "build_info.json")))
@@ -155,14 +156,30 @@ def run_metadata(dev):
         meta["rocm"] = None
     p = torch.cuda.get_device_properties(dev)
     meta["gpu"] = f"{p.name} ({getattr(p, 'gcnArchName', '')}, {p.multi_processor_count} CUs)"
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                             timeout=20).stdout
-        card = next(iter(json.loads(out).values()))
-        meta["sclk"] = card.get("sclk clock speed:")
-    except Exception:
-        meta["sclk"] = None
+    meta["sclk"] = shader_clock(p)
     return meta
+
+
+def shader_clock(props):
+    """The GPU's current shader clock level from the driver's sysfs table
+    (the line marked '*' of pp_dpm_sclk), read directly rather than through a
+    helper program; the device's own PCI address when torch reports it."""
+    import glob
+    paths = []
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is not None:
+        dom, dev = getattr(props, "pci_domain_id", 0), getattr(props, "pci_device_id", 0)
+        paths.append(f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{dev:02x}.0/pp_dpm_sclk")
+    paths += sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    for path in paths:
+        try:
+            lines = open(path).read().splitlines()
+        except OSError:
+            continue
+        for line in lines:
+            if line.rstrip().endswith("*") and ":" in line:
+                return line.split(":", 1)[1].replace("*", "").strip()
+    return None
 
 
 # ---------------------------------------------------------------- algorithmic bytes
