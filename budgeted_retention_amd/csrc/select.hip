@@ -958,22 +958,54 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
             uint32_t dt;
             count([](uint32_t) { return true; }, [&](uint32_t d) { return d >> s0; });
             pick(SEL_BINS, kr, dt, kr);
-            if (w1) {
-                count([&](uint32_t d) { return (d >> s0) == dt; },
-                      [&](uint32_t d) { return (d >> s1) & ((1u << w1) - 1u); });
-                uint32_t b1;
-                pick(w1 >= 8 ? 1 << w1 : 256, kr, b1, kr);
-                dt = (dt << w1) | b1;
+            const uint32_t nbin = hist[dt];   // real keys in the top digit's bin
+            if (w1 && nbin <= 64u) {
+                // At most one of the bin's keys per lane: gather them into
+                // hist[0..nbin) and take the kr-th largest directly (lane l
+                // counts the keys above and at its own), instead of two more
+                // histogram passes over the row.
+                wave_lds_order();
+                if (lane == 0) hist[64] = 0u;
+                wave_lds_order();
+#pragma unroll
+                for (int k = 0; k < NPL4; ++k)
+#pragma unroll
+                    for (int e = 0; e < SEL_VEC; ++e) {
+                        const uint32_t kk = key[k][e];
+                        const bool real = plain(k) || (kk != KEY_PROTECTED && k * 256 + 4 * lane + e < Ti);
+                        if (real && ((kk - kmin) >> s0) == dt) hist[atomicAdd(&hist[64], 1u)] = kk;
+                    }
+                wave_lds_order();
+                const uint32_t x = (uint32_t)lane < nbin ? hist[lane] : 0u;
+                uint32_t gt = 0u, ge = 0u;
+                for (uint32_t j = 0; j < nbin; ++j) {
+                    const uint32_t y = hist[j];
+                    gt += y > x ? 1u : 0u;
+                    ge += y >= x ? 1u : 0u;
+                }
+                const uint64_t hit = __ballot((uint32_t)lane < nbin && gt < kr && kr <= ge);
+                const int at = __ffsll((unsigned long long)hit) - 1;
+                tau = __builtin_amdgcn_readlane(x, at);
+                need = (int)(kr - __builtin_amdgcn_readlane(gt, at));
+                wave_lds_order();
+            } else {
+                if (w1) {
+                    count([&](uint32_t d) { return (d >> s0) == dt; },
+                          [&](uint32_t d) { return (d >> s1) & ((1u << w1) - 1u); });
+                    uint32_t b1;
+                    pick(w1 >= 8 ? 1 << w1 : 256, kr, b1, kr);
+                    dt = (dt << w1) | b1;
+                }
+                if (s1) {
+                    count([&](uint32_t d) { return (d >> s1) == dt; },
+                          [&](uint32_t d) { return d & ((1u << s1) - 1u); });
+                    uint32_t b2;
+                    pick(s1 >= 8 ? 1 << s1 : 256, kr, b2, kr);
+                    dt = (dt << s1) | b2;
+                }
+                tau = kmin + dt;
+                need = (int)kr;
             }
-            if (s1) {
-                count([&](uint32_t d) { return (d >> s1) == dt; },
-                      [&](uint32_t d) { return d & ((1u << s1) - 1u); });
-                uint32_t b2;
-                pick(s1 >= 8 ? 1 << s1 : 256, kr, b2, kr);
-                dt = (dt << s1) | b2;
-            }
-            tau = kmin + dt;
-            need = (int)kr;
         }
     }
     // ordered write: key > tau, and the first `need` keys == tau by index
@@ -982,6 +1014,9 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
     // takes a 32-bit byte offset (no 64-bit address arithmetic per token)
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         out, (short)0, (kept_stride < (1 << 20) ? kept_stride : (1 << 20)) * 4, 0x00020000);
+    auto put = [&](int pos, int j) {
+        if (pos < kept_stride) __builtin_amdgcn_raw_buffer_store_b32(j, orsrc, pos * 4, 0, 0);
+    };
     int gt_run = 0, eq_run = 0;
     int lane4 = 4 * lane;
     asm volatile("" : "+v"(lane4));   // token indices are recomputed here, not kept live from the loads
@@ -1002,7 +1037,7 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
             for (int e = 0; e < SEL_VEC; ++e)
                 if (key[k][e] > tau) {
-                    if (pos < kept_stride) __builtin_amdgcn_raw_buffer_store_b32(base + e, orsrc, pos * 4, 0, 0);
+                    put(pos, base + e);
                     ++pos;
                 }
             gt_run += tot;
@@ -1016,10 +1051,7 @@ __global__ void __launch_bounds__(SW_WAVES * 64) __attribute__((amdgpu_waves_per
             for (int e = 0; e < SEL_VEC; ++e) {
                 const bool gt = key[k][e] > tau;
                 const bool eq = key[k][e] == tau;
-                if (gt || (eq && eq_before < need)) {
-                    const int pos = gt_before + (eq_before < need ? eq_before : need);
-                    if (pos < kept_stride) __builtin_amdgcn_raw_buffer_store_b32(base + e, orsrc, pos * 4, 0, 0);
-                }
+                if (gt || (eq && eq_before < need)) put(gt_before + (eq_before < need ? eq_before : need), base + e);
                 gt_before += gt;
                 eq_before += eq;
             }

@@ -233,19 +233,38 @@ def _short_scores(rng, dist, rows, T):
         s = 1.0 + rng.integers(0, 64, (rows, T)) * 2.0 ** -23
     elif dist == "equal":
         s = np.full((rows, T), 0.25)
+    elif dist in ("tied_cut", "dense_cut"):
+        # log-uniform totals over six decades; around the (T//3)-th largest,
+        # either 20 tokens share its total exactly (the budget cuts through a
+        # tie inside a small top-digit bin) or 500 tokens sit within 2^-16 of
+        # it (a top-digit bin of more than 64 distinct totals)
+        s = 10.0 ** rng.uniform(-3, 3, (rows, T))
+        b = max(1, T // 3)
+        for r in range(rows):
+            order = np.argsort(-s[r], kind="stable")
+            cut = s[r, order[b - 1]]
+            if dist == "tied_cut":
+                near = order[max(0, b - 10):b + 10]
+                s[r, near] = cut
+            else:
+                near = order[max(0, b - 250):b + 250]
+                s[r, near] = cut * (1.0 + rng.uniform(-2.0 ** -16, 2.0 ** -16, near.size))
     else:                   # softmax-sum-like: a few heavy tokens over a small floor
         s = rng.gamma(0.3, 1.0 / max(T, 1), (rows, T))
     return s.astype(np.float32)
 
 
 @pytest.mark.parametrize("T", [1, 5, 63, 256, 257, 1000, 1024, 1025, 2047, 2048, 3001, 4096, 4099, 6000, 8192])
-@pytest.mark.parametrize("dist", ["wide", "narrow", "equal", "gamma"])
+@pytest.mark.parametrize("dist", ["wide", "narrow", "equal", "gamma", "tied_cut", "dense_cut"])
 def test_short_rows_one_wave_per_row(T, dist):
     """Rows of at most 8192 tokens are selected one wave per row (four rows
     per workgroup, six rows here so the last workgroup is partial): every
     register-block count, ragged lengths (scalar loads), totals of both signs
     with NaNs and ties, totals a few float32 steps apart, all-equal totals,
-    and per-token tags with a negative bonus and a floored tag."""
+    the budget cutting through a tie inside a small top-digit bin (resolved
+    from the bin's keys directly) or through a bin of hundreds of distinct
+    totals (resolved by two more digit passes), and per-token tags with a
+    negative bonus and a floored tag."""
     rng = np.random.default_rng(T * 7 + len(dist))
     rows = 6
     scores = _short_scores(rng, dist, rows, T)
