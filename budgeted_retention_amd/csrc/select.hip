@@ -1352,14 +1352,13 @@ __global__ void __launch_bounds__(CF_THREADS) cand_filter(CandArgs a) {
 }
 
 __global__ void __launch_bounds__(CR_THREADS) cand_resolve(CandArgs a) {
-    constexpr int WAVES = CR_THREADS / 64, PER = SEL_BINS / CR_THREADS;
+    constexpr int WAVES = CR_THREADS / 64;
     __shared__ uint32_t c_key[CAND_CAP];
     __shared__ int32_t c_idx[CAND_CAP];
     __shared__ __align__(16) uint32_t hist[SEL_BINS];
     __shared__ uint32_t s_w[WAVES];
     __shared__ uint32_t s_r[3][WAVES];
     __shared__ uint32_t s_pick[2];
-    __shared__ uint32_t s_pre[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t r = blockIdx.x;
     const uint32_t *cnt = a.cnt + (size_t)r * a.nseg;
