@@ -1,8 +1,9 @@
 """The calls the bounds-checked build is run on: every kernel family once on
 valid seeded inputs (score, select in its short-row and candidate forms,
-compaction, decode, pooling, page lists), then compaction and decode given
-caller data that the kernels clamp (a kept index past the cache, counts above
-their buffers). Imported by the test with the default library; run as a
+compaction, decode, pooling, page lists), then compaction, decode and page
+scores given caller data that the kernels clamp (a kept index past the cache,
+counts above their buffers, a block-table entry outside the storage, a page
+span past the cache). Imported by the test with the default library; run as a
 script in a child process with KVC_LIBRARY naming libkvc_check.so, it saves
 the same outputs and the check bits read after each group of calls."""
 import os
@@ -74,7 +75,9 @@ def valid_calls(kvc):
 
 def clamped_calls(kvc):
     """Caller data the kernels clamp: one kept list holds an index past the
-    cache and a count above its stride; one decode count exceeds its pool."""
+    cache and a count above its stride; one decode count exceeds its pool; a
+    block-table entry points outside the storage; a page span runs past the
+    cache."""
     out = {}
     rng = np.random.default_rng(6)
     N, L, Hkv, Hq, d, T, ks = 1, 1, 2, 4, 64, 300, 40
@@ -103,6 +106,24 @@ def clamped_calls(kvc):
     Vf = torch.from_numpy(out["cmp_V"].view(np.int16)).view(torch.bfloat16).reshape(rows, ks, d).cuda()
     kvc.kvc_decode_attn(dims_b, q, Kf, Vf, n_h, ks, o, ws)
     out["dec_o"] = tl.bits(o)
+    # paged decode whose block table points one used page outside the storage
+    # (that page's tokens are skipped)
+    ps, bps = 8, 5
+    tbl = torch.tensor([[0, 2, 1, 4, 3]], dtype=torch.int32, device="cuda")
+    tbl[0, 2] = -1
+    n_p = torch.tensor([bps * ps - 3, bps * ps - 3], dtype=torch.int32, device="cuda")
+    o2 = torch.empty_like(o)
+    dims_p = kvc.make_dims(N, L, Hkv, Hq, d, ks)
+    ws2 = torch.empty(max(1, kvc.kvc_decode_workspace_bytes(dims_p, bps * ps, 0)), dtype=torch.uint8, device="cuda")
+    kvc.kvc_decode_attn(dims_p, q, Kf, Vf, n_p, ks, o2, ws2, block_table=tbl, page_size=ps, blocks_per_seq=bps)
+    out["dec_paged_o"] = tl.bits(o2)
+    # page scores over event pages, one span running past the cache (clamped)
+    sc = torch.from_numpy(rng.gamma(0.5, 1.0, (N, L, Hkv, T)).astype(np.float32)).cuda()
+    first = torch.tensor([[0, 16, 40, T - 10]], dtype=torch.int32, device="cuda")
+    length = torch.tensor([[16, 16, 12, 16]], dtype=torch.int32, device="cuda")
+    pscore = torch.empty((N, 4), dtype=torch.float32, device="cuda")
+    kvc.kvc_page_scores(dims, sc, 16, 4, pscore, page_first=first, page_len=length)
+    out["page_scores"] = pscore.cpu().numpy()
     torch.cuda.synchronize()
     return out
 

@@ -3,8 +3,8 @@
 answers kvc_check_read with KVC_ERR_UNSUPPORTED. On the GPU: a child process
 with the checked library runs every kernel family on valid inputs (no check
 bit may be set) and then on caller data that the kernels clamp (exactly the
-bits for that data, no index bit); every output equals the default build's
-bit for bit."""
+kept-index, count, block-table and page-span bits, no index bit); every
+output equals the default build's bit for bit."""
 import ctypes
 import os
 import subprocess
@@ -55,7 +55,7 @@ def test_checked_build_runs_clean_and_matches_the_default_build(tmp_path):
     assert int(got.pop("bits_valid")) == 0
     clamped = int(got.pop("bits_clamped"))
     assert clamped & INDEX_BITS == 0, hex(clamped)
-    assert clamped == _lib.KVC_CHK_KEPT | _lib.KVC_CHK_COUNT, hex(clamped)
+    assert clamped == _lib.KVC_CHK_KEPT | _lib.KVC_CHK_COUNT | _lib.KVC_CHK_BLOCK | _lib.KVC_CHK_SPAN, hex(clamped)
     assert int(got.pop("bits_after_read")) == 0
     want = cases.valid_calls(kvc)
     want.update(cases.clamped_calls(kvc))
