@@ -62,3 +62,21 @@ def test_pipeline_call_times_are_medians_over_the_runs(monkeypatch):
     assert med == {"score": 3.0, "select": 0.12}
     with pytest.raises(ValueError):
         timer.median_step_ms(4)
+
+
+def test_shader_clock_reads_the_current_level(tmp_path, monkeypatch):
+    """The clock comes from the driver's table: the level marked '*'; the
+    device's own PCI path is tried first, then every card; None when absent."""
+    import glob as _glob
+
+    class Props:
+        pci_domain_id, pci_bus_id, pci_device_id = 0xfff0, 0x75, 0   # a PCI path no machine has
+
+    table = tmp_path / "pp_dpm_sclk"
+    table.write_text("0: 500Mhz \n1: 1800Mhz \n2: 2400Mhz *\n")
+    monkeypatch.setattr(_glob, "glob", lambda pattern: [str(table)] if "drm" in pattern else [])
+    assert bench.shader_clock(Props()) == "2400Mhz"
+    table.write_text("0: 500Mhz \n1: 1800Mhz \n")
+    assert bench.shader_clock(Props()) is None
+    monkeypatch.setattr(_glob, "glob", lambda pattern: [])
+    assert bench.shader_clock(Props()) is None
